@@ -1,0 +1,229 @@
+/*
+ * ech.h - C ABI of the MI355X (gfx950) indexer -> exact top-k -> KV-recall path
+ * of ECHO-style lossless KV-cache offloading for native-sparse-attention models.
+ *
+ * The path, per layer and step (ECHO explainer page, sections "The top-k
+ * dependency", "Decode: fetch above a predicted threshold", "Prefill: one-round
+ * histogram", "One layer, one step: free -> allocate -> recall", "Five
+ * fixed-size integer tensors on the GPU"):
+ *   1. ech_index_logits / ech_index_logits_causal: indexer score of every
+ *      cached token, logit[r,t] = sum_h w[r,h] * ReLU(q[r,h,:] . k[g,:]).
+ *   2. ech_topk: exact top-k of each row (ties to the lower token index) found
+ *      with a 256-bin histogram of the top 8 bits of (score - theta), theta
+ *      being an EMA (alpha = 0.5) of the previous step's k-th score.
+ *   3. ech_cache_step: GPU-resident per-layer slot map. EARLY (decode): fetch
+ *      tokens scoring above theta, up to a cap, before the top-k is known.
+ *      FINAL: pin the selected resident tokens, give every selected miss a
+ *      slot in ring order (evicting lazily freed tokens, no write-back).
+ *      PREFILL: FINAL over the union of a query block's selections.
+ *   4. ech_recall: copy the missed KV rows from pinned host memory into their
+ *      device-cache slots.
+ *
+ * Conventions
+ *  - Ownership: the caller owns every buffer (device memory, the pinned host
+ *    pool, workspaces) and the stream. The library allocates nothing, keeps no
+ *    global state and is re-entrant; per-layer state is a set of caller
+ *    buffers, so L layers are L buffer sets.
+ *  - Pointers are device pointers unless stated. bf16 = uint16 bit patterns;
+ *    fp8 = OCP e4m3fn bytes. Row-major throughout.
+ *  - Asynchrony: every call only enqueues kernels on `stream` (a hipStream_t,
+ *    NULL = the default stream). It never synchronises, never allocates,
+ *    never prints and never issues hipMemset, so a whole step can be captured
+ *    in a hipGraph. Grids are sized from host-known maxima; data-dependent
+ *    counts stay in device memory (the `ctr` tensor).
+ *  - Errors: calls return ECH_OK or a negative code. Arguments are checked on
+ *    the host before any launch; on an error nothing is enqueued. Problems only
+ *    the device can see (a token index out of range, a miss list that would
+ *    overflow) set sticky bits in ctr[ECH_CTR_STATUS], which the caller reads
+ *    after its own synchronisation.
+ */
+#ifndef ECH_H
+#define ECH_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- return codes */
+#define ECH_OK            0
+#define ECH_EINVAL       -1   /* bad sizes, NULL pointer, misalignment, unsupported H/D/k */
+#define ECH_ENOSPC       -2   /* host-known FINAL demand exceeds the cache size C */
+#define ECH_EUNSUPPORTED -3   /* key dtype or device architecture not supported */
+#define ECH_EHIP         -4   /* a HIP call or kernel launch failed */
+
+/* ---- key dtypes */
+#define ECH_KEY_BF16 0        /* keys [P, D] bf16, no scale */
+#define ECH_KEY_FP8  1        /* keys [P, D] OCP e4m3fn, one fp32 scale per token */
+
+/* ---- cache-step phases */
+#define ECH_EARLY   0         /* decode: fetch tokens scoring above theta, up to cap */
+#define ECH_FINAL   1         /* decode: make every selected token resident */
+#define ECH_PREFILL 2         /* prefill: FINAL over the union of R rows of one sequence */
+
+/* ---- the control tensor ctr[ECH_CTR_LEN] (int32, device), one per layer */
+#define ECH_CTR_HEAD      0   /* ring head: next slot the allocator looks at */
+#define ECH_CTR_EPOCH     1   /* phase counter; slot s is pinned in a phase iff slot_pin[s] == epoch */
+#define ECH_CTR_NMISS     2   /* entries written to the miss list by the last phase */
+#define ECH_CTR_NEVICT    3   /* resident tokens evicted by the last phase */
+#define ECH_CTR_RECALLED  4   /* rows copied by ech_recall since reset (wraps at 2^31) */
+#define ECH_CTR_STATUS    5   /* sticky ECH_ST_* bits */
+#define ECH_CTR_NWANT     6   /* misses the last phase wanted (before cap / slot limits) */
+#define ECH_CTR_NPINNED   7   /* slots pinned by the last phase */
+#define ECH_CTR_LEN      16
+
+/* ---- sticky status bits in ctr[ECH_CTR_STATUS] */
+#define ECH_ST_OVERFLOW   1   /* a FINAL/PREFILL phase found fewer unpinned slots than misses */
+#define ECH_ST_BADTOK     2   /* a selected token offset was outside [0, len) */
+#define ECH_ST_BADMISS    4   /* ech_recall saw a miss entry with g >= P or slot >= C */
+
+/* Human-readable name of a return code. */
+const char* ech_status_str(int code);
+
+/* Library ABI version (major*100 + minor). */
+int ech_version(void);
+
+/*
+ * ech_index_logits - decode indexer scores (one query row per sequence).
+ *
+ * Computes, for r < R and t < row_len[r],
+ *     logits[r*ld + t] = sum_h w[r*H+h] * ReLU( sum_d q[(r*H+h)*D+d] * k(g, d) ),
+ *     g = row_tok0[r] + t,
+ * with k(g,d) = bf16 key, or e4m3fn key * kscale[g] (the scale multiplies the
+ * whole key; any sign is allowed). Indexer scores of every cached token:
+ * ECHO explainer, "Decode: fetch above a predicted threshold" and "Fused
+ * indexer kernel (extends DeepGEMM)"; the formula is the lightning-indexer form.
+ *
+ *  q         [R, H, D] bf16, device.        w       [R, H] fp32, device.
+ *  kcache    [P, D] bf16 or e4m3fn, device, token-major (row g = token g).
+ *  kdtype    ECH_KEY_BF16 or ECH_KEY_FP8.   kscale  [P] fp32 (FP8) or NULL (BF16).
+ *  row_tok0  [R] int64, row_len [R] int32 (0 <= row_len[r] <= max_len), device.
+ *  logits    [R, ld] fp32, device, ld >= max_len; entries t >= row_len[r] are
+ *            not written.
+ *  Requires H == 64, D == 128, R >= 1, max_len >= 0, 16-byte aligned q/kcache.
+ *  Arithmetic: bf16 x bf16 products (fp8 keys widen exactly to bf16) summed in
+ *  fp32 on the matrix cores; ReLU, head weights and the per-token scale in fp32.
+ */
+int ech_index_logits(const void* q, const float* w, const void* kcache, int kdtype,
+                     const float* kscale, const int64_t* row_tok0, const int32_t* row_len,
+                     int R, int H, int D, int max_len, float* logits, int64_t ld, void* stream);
+
+/*
+ * ech_index_logits_causal - prefill indexer scores for a block of R query rows
+ * of one sequence (ECHO explainer, "Prefill: one-round histogram": query
+ * blocks are scored one after another). Row r is the query at position
+ * row0 + r and sees tokens t = 0 .. row0 + r (inclusive) of the sequence
+ * whose first token is tok0:
+ *     logits[r*ld + t] = sum_h w[r*H+h] * ReLU(q[r,h,:] . k(tok0 + t, :)).
+ * Entries t > row0 + r are not written. ld >= row0 + R. Same dtypes and
+ * limits as ech_index_logits.
+ */
+int ech_index_logits_causal(const void* q, const float* w, const void* kcache, int kdtype,
+                            const float* kscale, int64_t tok0, int64_t row0, int R, int H, int D,
+                            float* logits, int64_t ld, void* stream);
+
+/*
+ * ech_topk - exact top-k of each score row, ascending token order.
+ *
+ * For each row r (its first row_len[r] scores), idx[r*k + j] lists the tokens
+ * t whose (score, -t) is among the k largest, in ascending t, padded with -1
+ * when row_len[r] < k; ties go to the lower token index. kth[r] is the
+ * smallest selected score (NaN for an empty row). ECHO explainer: ECHO
+ * "guarantees an exact top-k"; the selection is found with 256 bins over the
+ * top 8 bits of each score shifted by the predicted threshold ("Prefill:
+ * one-round histogram"), then the boundary bin is resolved exactly.
+ *
+ *  theta_in  [R] fp32 or NULL: predicted threshold per row; NaN or NULL means
+ *            no prediction (the histogram is unshifted). It only steers speed:
+ *            the result is the same for any theta.
+ *  theta_out [R] fp32 or NULL: receives the EMA update (ECHO explainer,
+ *            "Decode: fetch above a predicted threshold", alpha = 0.5):
+ *            kth if theta_in is NaN/NULL, else fl32(fl32(kth + theta_in) * 0.5);
+ *            unchanged copy of theta_in for an empty row. May alias theta_in
+ *            only when nothing else reads theta_in concurrently.
+ *  Scores must be finite; -0.0 and +0.0 are equal.
+ *  Requires 1 <= k <= 4096, R >= 1, ld >= max_len, 0 <= row_len[r] <= max_len.
+ *  ws: device workspace of ech_topk_ws_bytes(R, max_len, k) bytes, 256-byte
+ *  aligned; contents need not be initialised.
+ */
+size_t ech_topk_ws_bytes(int R, int max_len, int k);
+int ech_topk(const float* logits, int64_t ld, const int32_t* row_len, int R, int max_len, int k,
+             const float* theta_in, float* theta_out, int32_t* idx, float* kth,
+             void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * ech_cache_reset - clear one layer's slot-map state: tok2slot[0..P) = -1,
+ * slot2tok[0..C) = -1, slot_pin[0..C) = 0, ctr[0..ECH_CTR_LEN) = 0. Uses fill
+ * kernels (no hipMemset), so it may be captured. The cache starts empty; every
+ * row lives in the host pool.
+ */
+int ech_cache_reset(int32_t* tok2slot, int64_t P, int32_t* slot2tok, int32_t* slot_pin, int32_t C,
+                    int32_t* ctr, void* stream);
+
+/*
+ * ech_cache_step - one phase of the per-layer slot map (ECHO explainer, "One
+ * layer, one step: free -> allocate -> recall"; "Five fixed-size integer
+ * tensors on the GPU"). The five tensors, all int32 on the device:
+ *   tok2slot [P]        slot of global token g, or -1
+ *   slot2tok [C]        token held by slot s, or -1
+ *   slot_pin [C]        epoch stamp; slot s is pinned in a phase iff it equals
+ *                       that phase's epoch (no clearing pass)
+ *   miss     [M_max,2]  (g, slot) pairs allocated by the last phase, in
+ *                       allocation order; consumed by ech_recall
+ *   ctr      [ECH_CTR_LEN] ring head, epoch, counts, status (ECH_CTR_*)
+ *
+ * Free is lazy: unselected resident tokens keep their slot until it is reused.
+ * Allocation: misses, in ascending (sequence, token) order, take the unpinned
+ * slots in ring order from ctr[HEAD] (head, head+1, ... mod C); a slot's old
+ * token is unmapped (tok2slot = -1) and nothing is written back, the host
+ * pool holding every row. Afterwards head = last allocated slot + 1 mod C.
+ *
+ * phase ECH_EARLY (decode, B sequences): for each b with theta[b] not NaN,
+ *   pin the slots of resident tokens t < seq_len[b] with logits[b*ld+t] >
+ *   theta[b] (strict) and allocate the first `cap` non-resident ones in
+ *   ascending t; when slots run out, later misses are dropped. idx unused.
+ * phase ECH_FINAL (decode): idx [B, k] ascending token offsets (-1 padded, as
+ *   ech_topk writes them); pin selected resident tokens, allocate every
+ *   selected miss; sel_slot[b*k+j] = slot of token idx[b*k+j] (-1 for pads).
+ *   The sequences' token ranges [seq_tok0, seq_tok0+seq_len) must not overlap.
+ * phase ECH_PREFILL: B must be 1; idx [R, k] rows of one sequence; the union
+ *   of their tokens is made resident (misses in ascending token order);
+ *   sel_slot [R, k].
+ *
+ *  stats [B, 4] int32 (PREFILL: [1, 4]) receives, for this phase and
+ *   sequence, {hits, fetched, dropped, evictions}: selection tokens already
+ *   resident, misses given a slot, misses not given one, tokens evicted.
+ *  Host-checked: FINAL demand B*min(k, max_len) (PREFILL: min(max_len, R*k))
+ *   must be <= C (else ECH_ENOSPC); M_max must be >= that demand (EARLY:
+ *   B*cap); P < 2^31; C >= 1.
+ *  ws: ech_cache_step_ws_bytes(...) bytes, 256-byte aligned, uninitialised OK.
+ *  Calls on the same layer state must be ordered (same stream or events).
+ */
+size_t ech_cache_step_ws_bytes(int phase, int B, int R, int k, int max_len, int32_t C, int32_t M_max);
+int ech_cache_step(int phase, int32_t* tok2slot, int64_t P, int32_t* slot2tok, int32_t* slot_pin,
+                   int32_t C, int32_t* miss, int32_t M_max, int32_t* ctr,
+                   const int64_t* seq_tok0, const int32_t* seq_len, int B, int max_len,
+                   const int32_t* idx, int R, int k,
+                   const float* logits, int64_t ld, const float* theta, int cap,
+                   int32_t* sel_slot, int32_t* stats, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * ech_recall - copy missed KV rows host -> device (ECHO explainer, "One layer,
+ * one step: free -> allocate -> recall"; the host pool holds every row).
+ * For m < ctr[ECH_CTR_NMISS]: dev_cache[miss[2m+1]] = host_pool[miss[2m]],
+ * row_bytes each, read directly over PCIe by a gather kernel (zero-copy).
+ *  host_pool  [P, row_bytes] pinned host memory (hipHostMalloc / torch
+ *             pin_memory), host pointer; ECH_EINVAL if it is not device-mapped.
+ *  dev_cache  [C, row_bytes] device memory.
+ *  row_bytes  multiple of 16 (1152 for 576 bf16 values); both buffers 16-byte
+ *             aligned. Adds the rows copied to ctr[ECH_CTR_RECALLED].
+ */
+int ech_recall(const void* host_pool, int64_t P, int64_t row_bytes, void* dev_cache, int32_t C,
+               const int32_t* miss, int32_t* ctr, int32_t M_max, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* ECH_H */

@@ -1,0 +1,379 @@
+// Lightning-indexer scores on gfx950 matrix cores.
+//
+// logit[r,t] = sum_h w[r,h] * ReLU(q[r,h,:] . k[g,:]), g = tok0 + t, over every
+// cached token (ECHO explainer: "Fused indexer kernel (extends DeepGEMM)",
+// "Decode: fetch above a predicted threshold"; the lightning-indexer form).
+//
+// Per token the work is a [64 heads x 128] x [128] product: a dense
+// contraction, so it runs on MFMA v_mfma_f32_16x16x32_bf16 with heads as the
+// M dimension (4 tiles of 16) and tokens as N (tiles of 16). fp8 e4m3fn keys
+// widen exactly to bf16 (v_cvt_scalef32_pk_bf16_fp8 with scale 1), so every
+// product is exact and only the fp32 accumulation rounds. The epilogue folds
+// ReLU, the head weights and the per-token scale:
+//   ReLU(s * x) = s * med3(x, 0, s >= 0 ? +inf : -inf),
+// then reduces the 64 heads (16 per lane in registers, 4 lane groups by
+// cross-lane adds).
+//
+// MFMA operand layout used (16x16x32 bf16, wave64): lane l holds A[row l%16]
+// and B[col l%16], 8 contraction elements each in lane group l/16; the
+// result C[4*(l/16)+v][l%16] is in accumulator register v. Which physical
+// dims a lane group holds is free as long as A and B agree, so each lane's
+// key loads are 16-byte contiguous pieces of one token row.
+
+#include "common.hpp"
+
+namespace {
+
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8_t;
+typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2_t;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4_t;
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+constexpr int kH = 64;
+constexpr int kD = 128;
+constexpr int kWaves = 4;
+constexpr int kThreads = kWaves * 64;
+
+__device__ __forceinline__ uint32_t cvt_lo(uint32_t x) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x, 1.0f, false));
+}
+__device__ __forceinline__ uint32_t cvt_hi(uint32_t x) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x, 1.0f, true));
+}
+
+// 8 fp8 bytes (two dwords) -> 8 bf16 in byte order.
+__device__ __forceinline__ bf16x8_t fp8x8_to_bf16(uint32_t a, uint32_t b) {
+  u32x4_t v = {cvt_lo(a), cvt_hi(a), cvt_lo(b), cvt_hi(b)};
+  return __builtin_bit_cast(bf16x8_t, v);
+}
+
+__device__ __forceinline__ bf16x8_t as_bf16x8(uint4 v) {
+  u32x4_t u = {v.x, v.y, v.z, v.w};
+  return __builtin_bit_cast(bf16x8_t, u);
+}
+
+__device__ __forceinline__ f32x4_t mfma(bf16x8_t a, bf16x8_t b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// Contraction dims held by lane group grp in MFMA step s (8 contiguous dims).
+//  fp8 keys: a lane loads bytes [64i + 16grp, +16) of the 128-byte key
+//            (i = 0, 1); step s = 2i + h uses the h-th 8 of them.
+//  bf16 keys: a lane loads bytes [64i + 16grp, +16) of the 256-byte key
+//            (i = 0..3) = dims 32i + 8grp .. +8; step s = i.
+template <int KDT>
+__device__ __forceinline__ int dim0_of(int grp, int s) {
+  if (KDT == ECH_KEY_FP8) return 64 * (s >> 1) + 16 * grp + 8 * (s & 1);
+  return 32 * s + 8 * grp;
+}
+
+template <int KDT>
+struct KeyFrag;
+template <>
+struct KeyFrag<ECH_KEY_FP8> {
+  uint4 c[2];
+};
+template <>
+struct KeyFrag<ECH_KEY_BF16> {
+  uint4 c[4];
+};
+
+template <int KDT>
+__device__ __forceinline__ void load_key(KeyFrag<KDT>& f, const uint8_t* row, int grp) {
+  if constexpr (KDT == ECH_KEY_FP8) {
+    f.c[0] = *reinterpret_cast<const uint4*>(row + 16 * grp);
+    f.c[1] = *reinterpret_cast<const uint4*>(row + 64 + 16 * grp);
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) f.c[i] = *reinterpret_cast<const uint4*>(row + 64 * i + 16 * grp);
+  }
+}
+
+template <int KDT>
+__device__ __forceinline__ bf16x8_t key_step(const KeyFrag<KDT>& f, int s) {
+  if constexpr (KDT == ECH_KEY_FP8) {
+    const uint4 c = f.c[s >> 1];
+    return (s & 1) ? fp8x8_to_bf16(c.z, c.w) : fp8x8_to_bf16(c.x, c.y);
+  } else {
+    return as_bf16x8(f.c[s]);
+  }
+}
+
+// Reduce one 16-token tile: 16 MFMA, then ReLU/weights/scale and head sum.
+// Returns the score for token column (lane & 15), valid in every lane.
+__device__ __forceinline__ float tile_score(const bf16x8_t (&a)[4][4], const float (&wv)[4][4],
+                                            const bf16x8_t (&b)[4], float sc) {
+  f32x4_t acc[4];
+#pragma unroll
+  for (int ht = 0; ht < 4; ++ht) acc[ht] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+#pragma unroll
+    for (int ht = 0; ht < 4; ++ht) acc[ht] = mfma(a[ht][s], b[s], acc[ht]);
+  }
+  const float bound = sc >= 0.f ? __builtin_inff() : -__builtin_inff();
+  float part = 0.f;
+#pragma unroll
+  for (int ht = 0; ht < 4; ++ht) {
+#pragma unroll
+    for (int v = 0; v < 4; ++v) part = fmaf(wv[ht][v], __builtin_amdgcn_fmed3f(acc[ht][v], 0.f, bound), part);
+  }
+  part += __shfl_xor(part, 16, 64);
+  part += __shfl_xor(part, 32, 64);
+  return part * sc;
+}
+
+// Load one query row [64][128] bf16 (16 KiB) into LDS, then each wave picks
+// up its A fragments and head weights into registers.
+template <int KDT>
+__device__ __forceinline__ void load_query(const uint16_t* __restrict__ qrow, const float* __restrict__ wrow,
+                                           uint4* qs, bf16x8_t (&a)[4][4], float (&wv)[4][4], int col, int grp) {
+  const uint4* qg = reinterpret_cast<const uint4*>(qrow);
+  for (int i = threadIdx.x; i < kH * kD * 2 / 16; i += blockDim.x) qs[i] = qg[i];
+  __syncthreads();
+  const uint8_t* qb = reinterpret_cast<const uint8_t*>(qs);
+#pragma unroll
+  for (int ht = 0; ht < 4; ++ht) {
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const int off = (16 * ht + col) * (kD * 2) + 2 * dim0_of<KDT>(grp, s);
+      a[ht][s] = as_bf16x8(*reinterpret_cast<const uint4*>(qb + off));
+    }
+#pragma unroll
+    for (int v = 0; v < 4; ++v) wv[ht][v] = wrow[16 * ht + 4 * grp + v];
+  }
+}
+
+// ------------------------------------------------------------------ decode
+// grid (ceil(max_len / (kWaves*tpw*16)), R). Each wave walks tpw tiles of 16
+// tokens, the WG's waves interleaved so they stream adjacent 2-4 KiB pieces.
+template <int KDT>
+__global__ __launch_bounds__(kThreads) void logits_decode_kernel(
+    const uint16_t* __restrict__ q, const float* __restrict__ w, const uint8_t* __restrict__ kc,
+    const float* __restrict__ ksc, const int64_t* __restrict__ tok0, const int32_t* __restrict__ lens,
+    float* __restrict__ out, int64_t ld, int tpw) {
+  constexpr int kRowB = (KDT == ECH_KEY_FP8) ? kD : 2 * kD;
+  const int r = blockIdx.y;
+  const int len = lens[r];
+  const int wg_t0 = blockIdx.x * (kWaves * tpw * 16);
+  if (wg_t0 >= len) return;
+  __shared__ uint4 qs[kH * kD * 2 / 16];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int col = lane & 15, grp = lane >> 4;
+  bf16x8_t a[4][4];
+  float wv[4][4];
+  load_query<KDT>(q + (size_t)r * kH * kD, w + (size_t)r * kH, qs, a, wv, col, grp);
+
+  const int64_t g0 = tok0[r];
+  const uint8_t* kbase = kc + (size_t)g0 * kRowB;
+  const float* sbase = (KDT == ECH_KEY_FP8) ? ksc + g0 : nullptr;
+  float* orow = out + (size_t)r * ld;
+
+  int tb = wg_t0 + wave * 16;
+  if (tb >= len) return;
+  KeyFrag<KDT> cur;
+  int tc = min(tb + col, len - 1);
+  load_key<KDT>(cur, kbase + (size_t)tc * kRowB, grp);
+  float sc = (KDT == ECH_KEY_FP8) ? sbase[tc] : 1.f;
+#pragma unroll 1
+  for (int it = 0; it < tpw; ++it) {
+    const int tn = tb + kWaves * 16;
+    const bool more = (it + 1 < tpw) && (tn < len);
+    KeyFrag<KDT> nxt;
+    float scn = 1.f;
+    if (more) {
+      const int tcn = min(tn + col, len - 1);
+      load_key<KDT>(nxt, kbase + (size_t)tcn * kRowB, grp);
+      if (KDT == ECH_KEY_FP8) scn = sbase[tcn];
+    }
+    bf16x8_t b[4];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) b[s] = key_step<KDT>(cur, s);
+    const float v = tile_score(a, wv, b, sc);
+    const int t = tb + col;
+    if (grp == 0 && t < len) orow[t] = v;
+    if (!more) break;
+    cur = nxt;
+    sc = scn;
+    tb = tn;
+  }
+}
+
+// ------------------------------------------------------------------ causal prefill
+// One WG = kWaves query rows (one per wave) x a span of kSpan tokens. Key
+// tiles of 64 tokens are widened to bf16 once and staged in LDS (rows padded
+// to 272 B so the 16-lane column reads hit distinct banks), double-buffered;
+// every wave multiplies its row's q against them. Row r sees t <= row0 + r.
+constexpr int kPTile = 64;                  // tokens per LDS stage
+constexpr int kPStride = 2 * kD + 16;       // padded bf16 key row in LDS (bytes)
+constexpr int kSpan = 4096;                 // tokens per WG
+
+template <int KDT>
+__device__ __forceinline__ void stage_keys(uint8_t* dst, float* sdst, const uint8_t* __restrict__ kbase,
+                                           const float* __restrict__ sbase, int t0, int nvalid) {
+  // 256 threads; fp8: thread -> token tid/4, bytes 32*(tid%4) .. +32 -> 64 B bf16.
+  // bf16: thread -> token tid/4, bytes 64*(tid%4) .. +64.
+  const int tid = threadIdx.x;
+  const int tok = tid >> 2, part = tid & 3;
+  const int tsrc = t0 + min(tok, max(nvalid - 1, 0));
+  uint8_t* d = dst + tok * kPStride;
+  if constexpr (KDT == ECH_KEY_FP8) {
+    const uint4* s = reinterpret_cast<const uint4*>(kbase + (size_t)tsrc * kD + 32 * part);
+    const uint4 x = s[0], y = s[1];
+    u32x4_t o0 = {cvt_lo(x.x), cvt_hi(x.x), cvt_lo(x.y), cvt_hi(x.y)};
+    u32x4_t o1 = {cvt_lo(x.z), cvt_hi(x.z), cvt_lo(x.w), cvt_hi(x.w)};
+    u32x4_t o2 = {cvt_lo(y.x), cvt_hi(y.x), cvt_lo(y.y), cvt_hi(y.y)};
+    u32x4_t o3 = {cvt_lo(y.z), cvt_hi(y.z), cvt_lo(y.w), cvt_hi(y.w)};
+    u32x4_t* dd = reinterpret_cast<u32x4_t*>(d + 64 * part);
+    dd[0] = o0;
+    dd[1] = o1;
+    dd[2] = o2;
+    dd[3] = o3;
+    if (part == 0) sdst[tok] = sbase[tsrc];
+  } else {
+    const uint4* s = reinterpret_cast<const uint4*>(kbase + (size_t)tsrc * 2 * kD + 64 * part);
+    uint4* dd = reinterpret_cast<uint4*>(d + 64 * part);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) dd[i] = s[i];
+    if (part == 0) sdst[tok] = 1.f;
+  }
+}
+
+template <int KDT>
+__global__ __launch_bounds__(kThreads) void logits_causal_kernel(
+    const uint16_t* __restrict__ q, const float* __restrict__ w, const uint8_t* __restrict__ kc,
+    const float* __restrict__ ksc, int64_t tok0, int64_t row0, int R, float* __restrict__ out, int64_t ld) {
+  constexpr int kRowB = (KDT == ECH_KEY_FP8) ? kD : 2 * kD;
+  const int rg = blockIdx.x;                       // row group
+  const int span0 = blockIdx.y * kSpan;
+  const int r_first = rg * kWaves;
+  const int r_last = min(R - 1, r_first + kWaves - 1);
+  const int64_t vis_max = row0 + r_last + 1;       // tokens visible to the last row
+  if ((int64_t)span0 >= vis_max) return;
+  const int span_end = (int)min<int64_t>(vis_max, (int64_t)span0 + kSpan);
+
+  __shared__ uint4 qs[kH * kD * 2 / 16];           // 16 KiB, one row at a time
+  __shared__ __attribute__((aligned(16))) uint8_t kt[2][kPTile * kPStride];
+  __shared__ float st[2][kPTile];
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int col = lane & 15, grp = lane >> 4;
+  const int r = r_first + wave;
+  const bool row_ok = r <= r_last;
+  const int64_t vis = row_ok ? row0 + r + 1 : 0;   // tokens t < vis are visible
+
+  // A fragments: rows are staged through LDS one at a time.
+  bf16x8_t a[4][4];
+  float wv[4][4];
+  for (int i = 0; i < kWaves; ++i) {
+    const int rr = min(r_first + i, r_last);
+    const uint4* qg = reinterpret_cast<const uint4*>(q + (size_t)rr * kH * kD);
+    for (int j = threadIdx.x; j < kH * kD * 2 / 16; j += blockDim.x) qs[j] = qg[j];
+    __syncthreads();
+    if (wave == i) {
+      const uint8_t* qb = reinterpret_cast<const uint8_t*>(qs);
+#pragma unroll
+      for (int ht = 0; ht < 4; ++ht) {
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          const int off = (16 * ht + col) * (kD * 2) + 2 * dim0_of<ECH_KEY_BF16>(grp, s);
+          a[ht][s] = as_bf16x8(*reinterpret_cast<const uint4*>(qb + off));
+        }
+#pragma unroll
+        for (int v = 0; v < 4; ++v) wv[ht][v] = w[(size_t)rr * kH + 16 * ht + 4 * grp + v];
+      }
+    }
+    __syncthreads();
+  }
+
+  const uint8_t* kbase = kc + (size_t)tok0 * kRowB;
+  const float* sbase = (KDT == ECH_KEY_FP8) ? ksc + tok0 : nullptr;
+  float* orow = out + (size_t)min(r, R - 1) * ld;
+  const int ntiles = (span_end - span0 + kPTile - 1) / kPTile;
+
+  stage_keys<KDT>(kt[0], st[0], kbase, sbase, span0, span_end - span0);
+  __syncthreads();
+#pragma unroll 1
+  for (int it = 0; it < ntiles; ++it) {
+    const int cb = it & 1;
+    const int t0 = span0 + it * kPTile;
+    if (it + 1 < ntiles) {
+      const int t1 = t0 + kPTile;
+      stage_keys<KDT>(kt[cb ^ 1], st[cb ^ 1], kbase, sbase, t1, span_end - t1);
+    }
+    if (row_ok && t0 < vis) {
+#pragma unroll
+      for (int sub = 0; sub < kPTile / 16; ++sub) {
+        const int tb = t0 + sub * 16;
+        if (tb < vis) {
+          const uint8_t* kr = kt[cb] + (sub * 16 + col) * kPStride;
+          bf16x8_t b[4];
+#pragma unroll
+          for (int s = 0; s < 4; ++s)
+            b[s] = as_bf16x8(*reinterpret_cast<const uint4*>(kr + 2 * dim0_of<ECH_KEY_BF16>(grp, s)));
+          const float v = tile_score(a, wv, b, st[cb][sub * 16 + col]);
+          const int t = tb + col;
+          if (grp == 0 && t < vis) orow[t] = v;
+        }
+      }
+    }
+    __syncthreads();
+  }
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+}  // namespace
+
+extern "C" int ech_index_logits(const void* q, const float* w, const void* kcache, int kdtype,
+                                const float* kscale, const int64_t* row_tok0, const int32_t* row_len,
+                                int R, int H, int D, int max_len, float* logits, int64_t ld, void* stream) {
+  if (!q || !w || !kcache || !row_tok0 || !row_len || !logits) return ECH_EINVAL;
+  if (H != kH || D != kD || R < 1 || R > 65535 || max_len < 0 || ld < max_len) return ECH_EINVAL;
+  if (kdtype != ECH_KEY_BF16 && kdtype != ECH_KEY_FP8) return ECH_EUNSUPPORTED;
+  if (kdtype == ECH_KEY_FP8 && !kscale) return ECH_EINVAL;
+  if (!aligned16(q) || !aligned16(kcache)) return ECH_EINVAL;
+  if (max_len == 0) return ECH_OK;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  // Enough WGs to fill 256 CUs; long rows give each wave up to 32 tiles so the
+  // per-WG query staging (16 KiB) stays small next to the key stream.
+  const int64_t total = (int64_t)R * max_len;
+  int tpw = (int)std::min<int64_t>(32, std::max<int64_t>(1, total / (2048 * kWaves * 16)));
+  const int per_wg = kWaves * tpw * 16;
+  dim3 grid((max_len + per_wg - 1) / per_wg, R);
+  const uint16_t* qq = static_cast<const uint16_t*>(q);
+  const uint8_t* kk = static_cast<const uint8_t*>(kcache);
+  if (kdtype == ECH_KEY_FP8)
+    hipLaunchKernelGGL(logits_decode_kernel<ECH_KEY_FP8>, grid, dim3(kThreads), 0, s, qq, w, kk, kscale,
+                       row_tok0, row_len, logits, ld, tpw);
+  else
+    hipLaunchKernelGGL(logits_decode_kernel<ECH_KEY_BF16>, grid, dim3(kThreads), 0, s, qq, w, kk, kscale,
+                       row_tok0, row_len, logits, ld, tpw);
+  ECH_LAUNCH_CHECK();
+  return ECH_OK;
+}
+
+extern "C" int ech_index_logits_causal(const void* q, const float* w, const void* kcache, int kdtype,
+                                       const float* kscale, int64_t tok0, int64_t row0, int R, int H, int D,
+                                       float* logits, int64_t ld, void* stream) {
+  if (!q || !w || !kcache || !logits) return ECH_EINVAL;
+  if (H != kH || D != kD || R < 1 || tok0 < 0 || row0 < 0) return ECH_EINVAL;
+  if (kdtype != ECH_KEY_BF16 && kdtype != ECH_KEY_FP8) return ECH_EUNSUPPORTED;
+  if (kdtype == ECH_KEY_FP8 && !kscale) return ECH_EINVAL;
+  if (!aligned16(q) || !aligned16(kcache)) return ECH_EINVAL;
+  if (ld < row0 + R || row0 + R > (int64_t)INT32_MAX) return ECH_EINVAL;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const int64_t vis_max = row0 + R;
+  dim3 grid((R + kWaves - 1) / kWaves, (unsigned)((vis_max + kSpan - 1) / kSpan));
+  if (grid.y > 65535) return ECH_EINVAL;
+  const uint16_t* qq = static_cast<const uint16_t*>(q);
+  const uint8_t* kk = static_cast<const uint8_t*>(kcache);
+  if (kdtype == ECH_KEY_FP8)
+    hipLaunchKernelGGL(logits_causal_kernel<ECH_KEY_FP8>, grid, dim3(kThreads), 0, s, qq, w, kk, kscale, tok0,
+                       row0, R, logits, ld);
+  else
+    hipLaunchKernelGGL(logits_causal_kernel<ECH_KEY_BF16>, grid, dim3(kThreads), 0, s, qq, w, kk, kscale, tok0,
+                       row0, R, logits, ld);
+  ECH_LAUNCH_CHECK();
+  return ECH_OK;
+}

@@ -1,0 +1,471 @@
+// Exact top-k per score row on gfx950.
+//
+// ECHO explainer, "Prefill: one-round histogram": 256 bins over the top 8
+// bits of each score shifted by the predicted threshold theta; ECHO
+// "guarantees an exact top-k". The k-th element (s*, t*) of the order
+// (score descending, token ascending) defines the set exactly:
+//     t selected  <=>  s_t > s*  or  (s_t == s* and t among the first
+//                      need_eq tokens with score s*)
+// so the kernels find s* and need_eq, then compact in ascending t.
+//
+//   T1 hist     grid (chunks, R): LDS histogram of bin(t) = top 8 bits of
+//               ord(fl32(s_t - theta)) per 8192-token chunk. fl32(s - theta)
+//               is monotone in s and ord() is order preserving, so higher bins
+//               hold strictly larger scores.
+//   T2 rowsel   grid (R): sum the chunk histograms, boundary bin b* where the
+//               count from the top reaches k, need = k - count above b*.
+//   T3 gather   grid (chunks, R): count tokens above b* per chunk; append the
+//               b* tokens (score, t) to a per-row candidate list.
+//   T4 resolve  grid (R): radix-select need-th largest score among the
+//               candidates in LDS (4 rounds of 8 bits of ord(s)); per-chunk
+//               counts of ">" and "==" tokens give output offsets. If the
+//               boundary bin overflowed the list (no or poor theta), the same
+//               radix rounds run over the whole row instead. Writes kth and
+//               the EMA update of theta.
+//   T5 compact  grid (chunks, R): each chunk writes its selected tokens in
+//               ascending order at its offset; rows shorter than k are padded
+//               with -1.
+// A good theta puts only a few hundred tokens in b* (bins are logarithmic
+// around the threshold), so T4 works in LDS and the row is read three times.
+
+#include <algorithm>
+
+#include "common.hpp"
+
+namespace {
+
+constexpr int kChunk = 8192;        // tokens per chunk (T1, T3, T5)
+constexpr int kT = 256;             // threads for chunk kernels
+constexpr int kRT = 1024;           // threads for the per-row resolve kernel
+constexpr int kMaxK = 4096;
+constexpr int kMaxChunks = 1024;    // max_len <= 8M
+
+enum RowMode : int { kNormal = 0, kAll = 1, kEmpty = 2 };
+
+struct RowState {
+  int mode;
+  int bstar;
+  int need;
+  int cand;      // candidates appended (may exceed the list capacity)
+  float spred;   // scores > spred are selected (-inf in kAll mode)
+  int pad[3];
+};
+
+struct Ws {
+  RowState* rs;
+  int* hist;     // [R][nch][256]
+  int* above;    // [R][nch]
+  int* off;      // [R][nch]
+  int* take;     // [R][nch]
+  int2* cand;    // [R][cap]
+  int cap;
+  int nch;
+};
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+int cand_cap(int R) { return R <= 256 ? 16384 : 4096; }
+
+size_t layout(int R, int max_len, Ws* w, char* base) {
+  const int nch = std::max(1, (max_len + kChunk - 1) / kChunk);
+  const int cap = cand_cap(R);
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    size_t at = o;
+    o = align256(o + bytes);
+    return at;
+  };
+  size_t o_rs = take(sizeof(RowState) * R);
+  size_t o_hist = take(sizeof(int) * (size_t)R * nch * 256);
+  size_t o_above = take(sizeof(int) * (size_t)R * nch);
+  size_t o_off = take(sizeof(int) * (size_t)R * nch);
+  size_t o_take = take(sizeof(int) * (size_t)R * nch);
+  size_t o_cand = take(sizeof(int2) * (size_t)R * cap);
+  if (w && base) {
+    w->rs = reinterpret_cast<RowState*>(base + o_rs);
+    w->hist = reinterpret_cast<int*>(base + o_hist);
+    w->above = reinterpret_cast<int*>(base + o_above);
+    w->off = reinterpret_cast<int*>(base + o_off);
+    w->take = reinterpret_cast<int*>(base + o_take);
+    w->cand = reinterpret_cast<int2*>(base + o_cand);
+    w->cap = cap;
+    w->nch = nch;
+  }
+  return o;
+}
+
+__device__ __forceinline__ uint32_t shifted_bin(float x, float th) {
+  const float d = (th == th) ? (x - th) : x;   // NaN theta: unshifted
+  return ech::ord_key(d) >> 24;
+}
+
+__device__ __forceinline__ float row_theta(const float* th, int r) {
+  return th ? th[r] : __builtin_nanf("");
+}
+
+// ------------------------------------------------------------------ T1
+__global__ __launch_bounds__(kT) void topk_hist_kernel(const float* __restrict__ logits, int64_t ld,
+                                                       const int32_t* __restrict__ lens, int k,
+                                                       const float* __restrict__ theta, Ws ws) {
+  const int r = blockIdx.y, c = blockIdx.x;
+  const int len = lens[r];
+  const int lo = c * kChunk;
+  if (len <= k || lo >= len) return;
+  const int hi = min(lo + kChunk, len);
+  __shared__ int h[256];
+  h[threadIdx.x] = 0;
+  __syncthreads();
+  const float th = row_theta(theta, r);
+  const float* row = logits + (size_t)r * ld;
+#pragma unroll 2
+  for (int i = 0; i < kChunk / (4 * kT); ++i) {
+    const int t = lo + (i * kT + threadIdx.x) * 4;
+    float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (t + 3 < hi) {
+      v = *reinterpret_cast<const float4*>(row + t);
+    } else if (t < hi) {
+      v.x = row[t];
+      if (t + 1 < hi) v.y = row[t + 1];
+      if (t + 2 < hi) v.z = row[t + 2];
+    }
+    ech::lds_hist_add(h, shifted_bin(v.x, th), t < hi);
+    ech::lds_hist_add(h, shifted_bin(v.y, th), t + 1 < hi);
+    ech::lds_hist_add(h, shifted_bin(v.z, th), t + 2 < hi);
+    ech::lds_hist_add(h, shifted_bin(v.w, th), t + 3 < hi);
+  }
+  __syncthreads();
+  ws.hist[((size_t)r * ws.nch + c) * 256 + threadIdx.x] = h[threadIdx.x];
+}
+
+// ------------------------------------------------------------------ T2
+__global__ __launch_bounds__(kT) void topk_rowsel_kernel(const int32_t* __restrict__ lens, int k, Ws ws) {
+  const int r = blockIdx.x;
+  const int len = lens[r];
+  RowState& st = ws.rs[r];
+  if (len <= k) {
+    if (threadIdx.x == 0) {
+      st.mode = len == 0 ? kEmpty : kAll;
+      st.bstar = 0;
+      st.need = 0;
+      st.cand = 0;
+    }
+    return;
+  }
+  const int nch = (len + kChunk - 1) / kChunk;
+  __shared__ int scratch[kT / 64];
+  // thread b owns bin (255 - b) so an exclusive scan counts the bins above it
+  const int bin = 255 - threadIdx.x;
+  int cnt = 0;
+  for (int c = 0; c < nch; ++c) cnt += ws.hist[((size_t)r * ws.nch + c) * 256 + bin];
+  int tot;
+  const int above = ech::block_excl_scan<kT>(cnt, scratch, &tot);
+  if (above < k && above + cnt >= k) {
+    st.mode = kNormal;
+    st.bstar = bin;
+    st.need = k - above;
+    st.cand = 0;
+  }
+}
+
+// ------------------------------------------------------------------ T3
+__global__ __launch_bounds__(kT) void topk_gather_kernel(const float* __restrict__ logits, int64_t ld,
+                                                         const int32_t* __restrict__ lens,
+                                                         const float* __restrict__ theta, Ws ws) {
+  const int r = blockIdx.y, c = blockIdx.x;
+  const int len = lens[r];
+  const int lo = c * kChunk;
+  const RowState st = ws.rs[r];
+  if (st.mode != kNormal || lo >= len) return;
+  const int hi = min(lo + kChunk, len);
+  const float th = row_theta(theta, r);
+  const uint32_t bstar = (uint32_t)st.bstar;
+  const float* row = logits + (size_t)r * ld;
+  int2* cand = ws.cand + (size_t)r * ws.cap;
+  int* cnt = &ws.rs[r].cand;
+  const int lane = ech::lane_id();
+  __shared__ int scratch[kT / 64];
+  int above = 0;
+  for (int i = 0; i < kChunk / kT; ++i) {
+    const int t = lo + i * kT + threadIdx.x;
+    const bool ok = t < hi;
+    const float x = ok ? row[t] : 0.f;
+    const uint32_t b = shifted_bin(x, th);
+    above += (ok && b > bstar) ? 1 : 0;
+    const bool is_c = ok && b == bstar;
+    const uint64_t m = __ballot(is_c);
+    if (m) {
+      int base = 0;
+      const int leader = __ffsll((unsigned long long)m) - 1;
+      if (lane == leader) base = atomicAdd(cnt, __popcll(m));
+      base = __shfl(base, leader, 64);
+      if (is_c) {
+        const int pos = base + __popcll(m & ((1ull << lane) - 1ull));
+        if (pos < ws.cap) cand[pos] = make_int2(__float_as_int(x), t);
+      }
+    }
+  }
+  const int tot = ech::block_sum<kT>(above, scratch);
+  if (threadIdx.x == 0) ws.above[(size_t)r * ws.nch + c] = tot;
+}
+
+// ------------------------------------------------------------------ T4
+// Radix-select helpers over a key set; `hist` is 256 ints of LDS.
+// Finds the digit d (bits [shift, shift+8) of ord) at which the count from
+// the top reaches `need`; updates need to the rank within that digit.
+__device__ __forceinline__ void pick_digit(int* hist, int* sh, int need, int* out_digit, int* out_need) {
+  // thread i < 256 owns digit 255 - i
+  int cnt = 0, above = 0, tot = 0;
+  if (threadIdx.x < 256) cnt = hist[255 - threadIdx.x];
+  // block-wide exclusive scan over the first 256 threads (4 waves)
+  const int lane = ech::lane_id(), wave = threadIdx.x / 64;
+  int incl = ech::wave_incl_scan(cnt);
+  if (threadIdx.x < 256 && lane == 63) sh[wave] = incl;
+  __syncthreads();
+  if (threadIdx.x < 256) {
+    int wb = 0;
+    for (int i = 0; i < wave; ++i) wb += sh[i];
+    above = wb + incl - cnt;
+    if (above < need && above + cnt >= need) {
+      *out_digit = 255 - threadIdx.x;
+      *out_need = need - above;
+    }
+  }
+  (void)tot;
+  __syncthreads();
+}
+
+__global__ __launch_bounds__(kRT) void topk_resolve_kernel(const float* __restrict__ logits, int64_t ld,
+                                                           const int32_t* __restrict__ lens, int k,
+                                                           const float* __restrict__ theta_in,
+                                                           float* __restrict__ theta_out, float* __restrict__ kth,
+                                                           Ws ws) {
+  extern __shared__ int2 cl[];                     // candidate list [cap]
+  __shared__ int hist[256];
+  __shared__ int sh[16];
+  __shared__ int gt_c[kMaxChunks];
+  __shared__ int eq_c[kMaxChunks];
+  __shared__ int s_digit, s_need;
+  __shared__ float s_min;
+
+  const int r = blockIdx.x;
+  const int len = lens[r];
+  RowState& st = ws.rs[r];
+  const int mode = st.mode;
+  const float th_in = row_theta(theta_in, r);
+  const float* row = logits + (size_t)r * ld;
+  const int nch = (len + kChunk - 1) / kChunk;
+
+  if (mode == kEmpty) {
+    if (threadIdx.x == 0) {
+      kth[r] = __builtin_nanf("");
+      if (theta_out) theta_out[r] = th_in;
+    }
+    return;
+  }
+  for (int c = threadIdx.x; c < nch; c += kRT) {
+    gt_c[c] = 0;
+    eq_c[c] = 0;
+  }
+  float sstar, spred;
+  int need_eq;
+  if (mode == kAll) {
+    // every visible token is selected; kth is the row minimum
+    float m = __builtin_inff();
+    for (int t = threadIdx.x; t < len; t += kRT) m = fminf(m, row[t]);
+    for (int d = 32; d > 0; d >>= 1) m = fminf(m, __shfl_xor(m, d, 64));
+    float* wmin = reinterpret_cast<float*>(hist);
+    if (ech::lane_id() == 0) wmin[threadIdx.x / 64] = m;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      float mm = __builtin_inff();
+      for (int i = 0; i < kRT / 64; ++i) mm = fminf(mm, wmin[i]);
+      s_min = mm;
+    }
+    __syncthreads();
+    sstar = s_min;
+    spred = -__builtin_inff();
+    need_eq = 0;
+    for (int c = threadIdx.x; c < nch; c += kRT) gt_c[c] = min(kChunk, len - c * kChunk);
+    __syncthreads();
+  } else {
+    const int cnt = st.cand;
+    int need = st.need;
+    uint32_t prefix = 0, mask = 0;
+    const bool in_lds = cnt <= ws.cap;
+    const float th = th_in;
+    const uint32_t bstar = (uint32_t)st.bstar;
+    if (in_lds) {
+      const int2* src = ws.cand + (size_t)r * ws.cap;
+      for (int i = threadIdx.x; i < cnt; i += kRT) cl[i] = src[i];
+    }
+    __syncthreads();
+#pragma unroll 1
+    for (int round = 0; round < 4; ++round) {
+      const int shift = 24 - 8 * round;
+      for (int i = threadIdx.x; i < 256; i += kRT) hist[i] = 0;
+      __syncthreads();
+      if (in_lds) {
+        for (int i0 = 0; i0 < cnt; i0 += kRT) {
+          const int i = i0 + threadIdx.x;
+          uint32_t key = 0;
+          bool act = false;
+          if (i < cnt) {
+            key = ech::ord_key(__int_as_float(cl[i].x));
+            act = (key & mask) == prefix;
+          }
+          ech::lds_hist_add(hist, (key >> shift) & 255u, act);
+        }
+      } else {
+        for (int t0 = 0; t0 < len; t0 += kRT) {
+          const int t = t0 + threadIdx.x;
+          uint32_t key = 0;
+          bool act = false;
+          if (t < len) {
+            const float x = row[t];
+            key = ech::ord_key(x);
+            act = shifted_bin(x, th) == bstar && (key & mask) == prefix;
+          }
+          ech::lds_hist_add(hist, (key >> shift) & 255u, act);
+        }
+      }
+      __syncthreads();
+      pick_digit(hist, sh, need, &s_digit, &s_need);
+      prefix |= (uint32_t)s_digit << shift;
+      mask |= 255u << shift;
+      need = s_need;
+      __syncthreads();
+    }
+    sstar = ech::ord_to_float(prefix);
+    spred = sstar;
+    need_eq = need;
+    // per-chunk counts of tokens strictly above s* and equal to s*
+    if (in_lds) {
+      for (int c = threadIdx.x; c < nch; c += kRT) gt_c[c] = ws.above[(size_t)r * ws.nch + c];
+      __syncthreads();
+      for (int i = threadIdx.x; i < cnt; i += kRT) {
+        const float x = __int_as_float(cl[i].x);
+        const int c = cl[i].y / kChunk;
+        if (x > sstar) atomicAdd(&gt_c[c], 1);
+        else if (x == sstar) atomicAdd(&eq_c[c], 1);
+      }
+    } else {
+      for (int t = threadIdx.x; t < len; t += kRT) {
+        const float x = row[t];
+        if (x > sstar) atomicAdd(&gt_c[t / kChunk], 1);
+        else if (x == sstar) atomicAdd(&eq_c[t / kChunk], 1);
+      }
+    }
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) {
+    int run = 0, eq_before = 0;
+    int* off = ws.off + (size_t)r * ws.nch;
+    int* tk = ws.take + (size_t)r * ws.nch;
+    for (int c = 0; c < nch; ++c) {
+      const int tkc = max(0, min(eq_c[c], need_eq - eq_before));
+      off[c] = run;
+      tk[c] = tkc;
+      run += gt_c[c] + tkc;
+      eq_before += eq_c[c];
+    }
+    st.spred = spred;
+    kth[r] = sstar;
+    if (theta_out) theta_out[r] = (th_in == th_in) ? (sstar + th_in) * 0.5f : sstar;
+  }
+}
+
+// ------------------------------------------------------------------ T5
+__global__ __launch_bounds__(kT) void topk_compact_kernel(const float* __restrict__ logits, int64_t ld,
+                                                          const int32_t* __restrict__ lens, int k,
+                                                          int32_t* __restrict__ idx, Ws ws) {
+  const int r = blockIdx.y, c = blockIdx.x;
+  const int len = lens[r];
+  int32_t* orow = idx + (size_t)r * k;
+  if (c == 0) {
+    for (int j = min(k, len) + threadIdx.x; j < k; j += kT) orow[j] = -1;
+  }
+  const int lo = c * kChunk;
+  if (lo >= len) return;
+  const RowState st = ws.rs[r];
+  if (st.mode == kEmpty) return;
+  const int hi = min(lo + kChunk, len);
+  const float sp = st.spred;
+  const int base = ws.off[(size_t)r * ws.nch + c];
+  const int te = ws.take[(size_t)r * ws.nch + c];
+  const float* row = logits + (size_t)r * ld;
+  __shared__ int scratch[kT / 64];
+  int gt_run = 0, eq_run = 0;   // block-uniform running counts
+#pragma unroll 1
+  for (int i = 0; i < kChunk / (4 * kT); ++i) {
+    const int t = lo + (i * kT + threadIdx.x) * 4;
+    float v[4];
+    bool ok[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      ok[j] = t + j < hi;
+      v[j] = ok[j] ? row[t + j] : 0.f;
+    }
+    int ngt = 0, neq = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      ngt += (ok[j] && v[j] > sp) ? 1 : 0;
+      neq += (ok[j] && v[j] == sp) ? 1 : 0;
+    }
+    int tot;
+    const int pre = ech::block_excl_scan<kT>(ngt | (neq << 16), scratch, &tot);
+    int gt_b = gt_run + (pre & 0xffff);
+    int eq_b = eq_run + (pre >> 16);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      if (!ok[j]) continue;
+      bool sel = false;
+      if (v[j] > sp) {
+        sel = true;
+      } else if (v[j] == sp) {
+        sel = eq_b < te;
+      }
+      const int pos = base + gt_b + min(eq_b, te);
+      if (sel && pos < k) orow[pos] = t + j;
+      if (v[j] > sp) ++gt_b;
+      else if (v[j] == sp) ++eq_b;
+    }
+    gt_run += tot & 0xffff;
+    eq_run += tot >> 16;
+  }
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+}  // namespace
+
+extern "C" size_t ech_topk_ws_bytes(int R, int max_len, int k) {
+  (void)k;
+  if (R < 1 || max_len < 0) return 0;
+  return layout(R, max_len, nullptr, nullptr);
+}
+
+extern "C" int ech_topk(const float* logits, int64_t ld, const int32_t* row_len, int R, int max_len, int k,
+                        const float* theta_in, float* theta_out, int32_t* idx, float* kth, void* ws,
+                        size_t ws_bytes, void* stream) {
+  if (!logits || !row_len || !idx || !kth || !ws) return ECH_EINVAL;
+  if (R < 1 || R > 65535 || k < 1 || k > kMaxK || max_len < 0 || ld < max_len) return ECH_EINVAL;
+  if ((int64_t)max_len > (int64_t)kChunk * kMaxChunks) return ECH_EINVAL;
+  if (ld % 4 != 0 || !aligned16(logits) || (reinterpret_cast<uintptr_t>(ws) & 255u)) return ECH_EINVAL;
+  if (ws_bytes < ech_topk_ws_bytes(R, max_len, k)) return ECH_EINVAL;
+  Ws w;
+  layout(R, max_len, &w, static_cast<char*>(ws));
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const dim3 gch(w.nch, R);
+  hipLaunchKernelGGL(topk_hist_kernel, gch, dim3(kT), 0, s, logits, ld, row_len, k, theta_in, w);
+  ECH_LAUNCH_CHECK();
+  hipLaunchKernelGGL(topk_rowsel_kernel, dim3(R), dim3(kT), 0, s, row_len, k, w);
+  ECH_LAUNCH_CHECK();
+  hipLaunchKernelGGL(topk_gather_kernel, gch, dim3(kT), 0, s, logits, ld, row_len, theta_in, w);
+  ECH_LAUNCH_CHECK();
+  hipLaunchKernelGGL(topk_resolve_kernel, dim3(R), dim3(kRT), sizeof(int2) * w.cap, s, logits, ld, row_len, k,
+                     theta_in, theta_out, kth, w);
+  ECH_LAUNCH_CHECK();
+  hipLaunchKernelGGL(topk_compact_kernel, gch, dim3(kT), 0, s, logits, ld, row_len, k, idx, w);
+  ECH_LAUNCH_CHECK();
+  return ECH_OK;
+}

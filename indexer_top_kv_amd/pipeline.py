@@ -1,0 +1,204 @@
+"""One layer of the path, launched in order on two streams.
+
+Decode step (ECHO explainer, "The top-k dependency" and "Decode: fetch above
+a predicted threshold"): the recall of a step depends on its top-k; the early
+fetch of tokens scoring above the predicted threshold overlaps the top-k.
+
+    S0: ech_index_logits ------------------> ech_topk(theta -> theta')
+         \\-> S1: EARLY(theta) + recall --/ (join) FINAL + recall
+
+theta is double-buffered (EARLY reads the prediction while the top-k writes
+its update). When the batch's selections do not fit the cache at once (sum of
+min(k, len_b) > C), sequences are processed in host-computed chunks, each
+EARLY then FINAL; every selected token is resident at the end of its chunk.
+
+Prefill (ECHO explainer, "Prefill: one-round histogram"): query blocks are
+scored one after another; the recall of block i runs on S1 while S0 scores
+block i+1.
+
+Nothing here computes: this module sizes buffers with torch, chooses the
+order of the C-ABI calls and the stream events between them.
+"""
+from __future__ import annotations
+
+from typing import List, Optional, Tuple
+
+import numpy as np
+import torch
+
+from . import (ECH_EARLY, ECH_FINAL, ECH_PREFILL, LayerState, ech_cache_reset, ech_cache_step,
+               ech_cache_step_ws_bytes, ech_index_logits, ech_index_logits_causal, ech_recall, ech_topk,
+               ech_topk_ws_bytes)
+
+
+def round_up(x: int, m: int) -> int:
+    return (x + m - 1) // m * m
+
+
+def sequence_chunks(lens: np.ndarray, k: int, C: int) -> List[Tuple[int, int]]:
+    """Split sequences into consecutive chunks, each the longest prefix of the
+    remaining ones with sum(min(k, len_b)) <= C."""
+    out, b0, acc = [], 0, 0
+    for b, n in enumerate(np.asarray(lens).tolist()):
+        d = min(k, int(n))
+        if d > C:
+            raise ValueError(f'one sequence needs {d} slots, the cache has {C}')
+        if acc + d > C:
+            out.append((b0, b))
+            b0, acc = b, 0
+        acc += d
+    out.append((b0, len(lens)))
+    return out
+
+
+class DecodeLayer:
+    """Buffers and launch order of one layer's decode step."""
+
+    def __init__(self, kcache: torch.Tensor, kscale: Optional[torch.Tensor], w: torch.Tensor,
+                 tok0: np.ndarray, lens: np.ndarray, C: int, k: int = 2048, cap: int = 512,
+                 host_pool: Optional[torch.Tensor] = None, early: bool = True, device='cuda'):
+        self.kcache, self.kscale, self.w = kcache, kscale, w
+        self.B = len(lens)
+        self.lens_np = np.asarray(lens, np.int32)
+        self.tok0_np = np.asarray(tok0, np.int64)
+        self.max_len = int(self.lens_np.max())
+        self.k, self.cap, self.C = k, cap, C
+        self.early = early
+        self.P = kcache.shape[0]
+        dev = dict(device=device)
+        self.tok0 = torch.from_numpy(self.tok0_np).to(**dev)
+        self.lens = torch.from_numpy(self.lens_np).to(**dev)
+        self.ld = round_up(max(self.max_len, 4), 64)
+        self.logits = torch.empty((self.B, self.ld), dtype=torch.float32, **dev)
+        self.idx = torch.empty((self.B, k), dtype=torch.int32, **dev)
+        self.kth = torch.empty(self.B, dtype=torch.float32, **dev)
+        self.theta = [torch.full((self.B,), float('nan'), dtype=torch.float32, **dev) for _ in range(2)]
+        self.parity = 0
+        self.sel_slot = torch.empty((self.B, k), dtype=torch.int32, **dev)
+        self.stats_early = torch.zeros((self.B, 4), dtype=torch.int32, **dev)
+        self.stats_final = torch.zeros((self.B, 4), dtype=torch.int32, **dev)
+        self.chunks = sequence_chunks(self.lens_np, k, C)
+        cb = max(e - s for s, e in self.chunks)
+        m_max = max(cb * min(k, self.max_len), cb * min(cap, self.max_len), 1)
+        self.state = LayerState.allocate(self.P, C, m_max, device)
+        self.ws_topk = torch.empty(ech_topk_ws_bytes(self.B, self.max_len, k), dtype=torch.uint8, **dev)
+        self.ws_early = torch.empty(ech_cache_step_ws_bytes(ECH_EARLY, cb, cb, k, self.max_len, C, m_max),
+                                    dtype=torch.uint8, **dev)
+        self.ws_final = torch.empty(ech_cache_step_ws_bytes(ECH_FINAL, cb, cb, k, self.max_len, C, m_max),
+                                    dtype=torch.uint8, **dev)
+        self.host_pool = host_pool
+        if host_pool is not None:
+            self.dev_cache = torch.empty((C, host_pool.shape[1]), dtype=host_pool.dtype, **dev)
+        else:
+            self.dev_cache = None
+        self.s1 = torch.cuda.Stream(device=device)
+        self.ev_logits = torch.cuda.Event()
+        self.ev_early = torch.cuda.Event()
+        ech_cache_reset(self.state)
+
+    def reset(self) -> None:
+        ech_cache_reset(self.state)
+        for t in self.theta:
+            t.fill_(float('nan'))
+        self.parity = 0
+
+    def _phase(self, phase: int, b0: int, b1: int, theta: torch.Tensor, stream) -> None:
+        stats = self.stats_early if phase == ECH_EARLY else self.stats_final
+        ech_cache_step(phase, self.state, self.tok0[b0:b1], self.lens[b0:b1], self.max_len,
+                       idx=self.idx[b0:b1] if phase == ECH_FINAL else None, k=self.k,
+                       logits=self.logits[b0:b1], theta=theta[b0:b1], cap=self.cap,
+                       sel_slot=self.sel_slot[b0:b1] if phase == ECH_FINAL else None, stats=stats[b0:b1],
+                       ws=self.ws_early if phase == ECH_EARLY else self.ws_final, stream=stream)
+        if self.host_pool is not None:
+            ech_recall(self.host_pool, self.dev_cache, self.state, stream=stream)
+
+    def logits_only(self, q: torch.Tensor, stream=None) -> None:
+        ech_index_logits(q, self.w, self.kcache, self.kscale, self.tok0, self.lens, self.max_len, self.logits,
+                         stream=stream)
+
+    def step(self, q: torch.Tensor) -> None:
+        """Enqueue one decode step for query q [B, 64, 128] (bf16 bits) on the
+        current stream (with S1 forked and joined inside)."""
+        s0 = torch.cuda.current_stream()
+        th, th_next = self.theta[self.parity], self.theta[1 - self.parity]
+        self.logits_only(q, stream=s0)
+        first_b0, first_b1 = self.chunks[0]
+        if self.early:
+            self.ev_logits.record(s0)
+            self.s1.wait_stream(s0)
+            self._phase(ECH_EARLY, first_b0, first_b1, th, self.s1)
+            self.ev_early.record(self.s1)
+        ech_topk(self.logits, self.lens, self.max_len, self.k, th, th_next, self.idx, self.kth, self.ws_topk,
+                 stream=s0)
+        if self.early:
+            s0.wait_event(self.ev_early)
+        self._phase(ECH_FINAL, first_b0, first_b1, th, s0)
+        for b0, b1 in self.chunks[1:]:
+            if self.early:
+                self._phase(ECH_EARLY, b0, b1, th, s0)
+            self._phase(ECH_FINAL, b0, b1, th, s0)
+        self.parity ^= 1
+
+    @property
+    def theta_current(self) -> torch.Tensor:
+        return self.theta[self.parity]
+
+
+class PrefillLayer:
+    """Causal prefill of one sequence in query blocks: logits -> per-row top-k
+    -> PREFILL cache step (union) -> recall of block i on S1 while S0 scores
+    block i+1."""
+
+    def __init__(self, kcache: torch.Tensor, kscale: Optional[torch.Tensor], N: int, C: int, k: int = 2048,
+                 block_rows: int = 4096, host_pool: Optional[torch.Tensor] = None, tok0: int = 0, device='cuda'):
+        self.kcache, self.kscale = kcache, kscale
+        self.N, self.C, self.k, self.block_rows, self.tok0 = N, C, k, block_rows, tok0
+        dev = dict(device=device)
+        self.ld = round_up(N, 64)
+        self.logits = torch.empty((block_rows, self.ld), dtype=torch.float32, **dev)
+        self.idx = torch.empty((block_rows, k), dtype=torch.int32, **dev)
+        self.kth = torch.empty(block_rows, dtype=torch.float32, **dev)
+        self.theta = torch.full((block_rows,), float('nan'), dtype=torch.float32, **dev)
+        self.sel_slot = torch.empty((block_rows, k), dtype=torch.int32, **dev)
+        self.stats = torch.zeros((1, 4), dtype=torch.int32, **dev)
+        self.m_max = min(N, block_rows * k)
+        self.state = LayerState.allocate(N + tok0, C, self.m_max, device)
+        self.ws_topk = torch.empty(ech_topk_ws_bytes(block_rows, N, k), dtype=torch.uint8, **dev)
+        self.ws_cache = torch.empty(ech_cache_step_ws_bytes(ECH_PREFILL, 1, block_rows, k, N, C, self.m_max),
+                                    dtype=torch.uint8, **dev)
+        self.seq_tok0 = torch.tensor([tok0], dtype=torch.int64, **dev)
+        self.seq_len = torch.tensor([N], dtype=torch.int32, **dev)
+        self.row_len = torch.arange(1, block_rows + 1, dtype=torch.int32, **dev)
+        self.host_pool = host_pool
+        self.dev_cache = (torch.empty((C, host_pool.shape[1]), dtype=host_pool.dtype, **dev)
+                          if host_pool is not None else None)
+        self.s1 = torch.cuda.Stream(device=device)
+        self.ev_recall = torch.cuda.Event()
+        ech_cache_reset(self.state)
+
+    def blocks(self):
+        return [(r0, min(self.block_rows, self.N - r0)) for r0 in range(0, self.N, self.block_rows)]
+
+    def run_block(self, row0: int, q: torch.Tensor, w: torch.Tensor, first: bool) -> None:
+        """q [R,64,128], w [R,64] for rows row0 .. row0+R-1, on the current stream."""
+        s0 = torch.cuda.current_stream()
+        R = q.shape[0]
+        logits = self.logits[:R]
+        ech_index_logits_causal(q, w, self.kcache, self.kscale, self.tok0, row0, logits, stream=s0)
+        row_len = self.row_len[:R] + row0
+        # rows' thresholds: the EMA of the same row position in earlier blocks
+        ech_topk(logits, row_len, row0 + R, self.k, self.theta[:R], self.theta[:R], self.idx[:R], self.kth[:R],
+                 self.ws_topk, stream=s0)
+        if not first:
+            s0.wait_event(self.ev_recall)
+        ech_cache_step(ECH_PREFILL, self.state, self.seq_tok0, self.seq_len, self.N, idx=self.idx[:R], k=self.k,
+                       sel_slot=self.sel_slot[:R], stats=self.stats, ws=self.ws_cache, stream=s0)
+        if self.host_pool is not None:
+            self.s1.wait_stream(s0)
+            ech_recall(self.host_pool, self.dev_cache, self.state, stream=self.s1)
+            self.ev_recall.record(self.s1)
+        else:
+            self.ev_recall.record(s0)
+
+    def finish(self) -> None:
+        torch.cuda.current_stream().wait_event(self.ev_recall)

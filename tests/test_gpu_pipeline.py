@@ -1,0 +1,152 @@
+"""Whole decode steps on the GPU (two streams, early fetch overlapping the
+top-k, chunked when the batch does not fit the cache) against the same steps
+run by the oracle.
+
+Dyadic inputs (small integers, power-of-two scales, head weights m/64) make
+every score exact in float32 whatever the summation order, so the GPU and the
+oracle see identical scores and every later stage must agree bit for bit:
+idx, kth, theta, maps, head, sel_slot, stats and the recalled rows. With
+normal inputs the scores agree within tolerance only, so the selections are
+checked for validity against the oracle scores and the cache for its
+invariants.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as wk
+from gpu_util import dev, host, need_gpu, TOL_BF16, TOL_FP8
+from indexer_top_kv_amd.pipeline import DecodeLayer
+
+pytestmark = pytest.mark.gpu
+
+
+def oracle_chunks(lens, k, C):
+    """Sequence chunks: longest prefixes with sum(min(k, len)) <= C (reading
+    of the capacity-constrained decode)."""
+    out, start, acc = [], 0, 0
+    for b, n in enumerate(lens):
+        d = min(k, int(n))
+        if acc + d > C:
+            out.append((start, b))
+            start, acc = b, 0
+        acc += d
+    out.append((start, len(lens)))
+    return out
+
+
+class OracleDecode:
+    def __init__(self, wl, keys, scale, w, pool):
+        self.wl, self.keys, self.scale, self.w = wl, keys, scale, w
+        self.sm = oracle.SlotMap(wl.P, wl.C)
+        self.theta = np.full(wl.B, np.nan, np.float32)
+        self.pool = pool
+        self.cache = np.zeros((wl.C, pool.shape[1]), pool.dtype)
+        self.chunks = oracle_chunks(wl.lens, wl.k, wl.C)
+
+    def step(self, q):
+        wl = self.wl
+        L = [x.astype(np.float32) for x in oracle.index_logits(q, self.w, self.keys, wl.kdtype, self.scale,
+                                                                 wl.tok0, wl.lens)]
+        idx, kth = oracle.topk_rows(L, wl.k)
+        early_stats = np.zeros((wl.B, 4), np.int64)
+        final_stats = np.zeros((wl.B, 4), np.int64)
+        sel = np.zeros((wl.B, wl.k), np.int64)
+        for b0, b1 in self.chunks:
+            a, st = self.sm.early(wl.tok0[b0:b1], L[b0:b1], self.theta[b0:b1], wl.cap)
+            oracle.recall_rows(self.pool, self.cache, a)
+            early_stats[b0:b1] = st
+            a, s, st = self.sm.final(wl.tok0[b0:b1], idx[b0:b1])
+            oracle.recall_rows(self.pool, self.cache, a)
+            final_stats[b0:b1] = st
+            sel[b0:b1] = s
+        self.theta = oracle.theta_rows(self.theta, kth)
+        return L, idx, kth, sel, early_stats, final_stats
+
+
+def _setup(wl):
+    keys, scale = wk.keys(wl)
+    w = wk.head_weights(wl)
+    rows = wk.host_rows(wl)
+    pool = torch.empty((wl.P, 576), dtype=torch.int16, pin_memory=True)
+    pool.numpy()[:] = rows.view(np.int16)
+    layer = DecodeLayer(dev(keys), None if scale is None else dev(scale), dev(w), wl.tok0, wl.lens, wl.C,
+                        k=wl.k, cap=wl.cap, host_pool=pool)
+    return keys, scale, w, pool, layer
+
+
+def _run_bit_exact(wl, steps):
+    keys, scale, w, pool, layer = _setup(wl)
+    ref = OracleDecode(wl, keys, scale, w, pool.numpy().copy())
+    for s, q in enumerate(wk.decode_queries(wl, steps)):
+        layer.step(dev(q))
+        torch.cuda.synchronize()
+        L, idx, kth, sel, est, fst = ref.step(q)
+        for b in range(wl.B):
+            np.testing.assert_array_equal(host(layer.logits)[b, :wl.lens[b]], L[b], err_msg=f'step {s} row {b}')
+        np.testing.assert_array_equal(host(layer.idx), idx, err_msg=f'step {s}')
+        np.testing.assert_array_equal(host(layer.kth), kth)
+        np.testing.assert_array_equal(host(layer.theta_current), ref.theta)
+        np.testing.assert_array_equal(host(layer.sel_slot), sel)
+        np.testing.assert_array_equal(host(layer.stats_final), fst)
+        np.testing.assert_array_equal(host(layer.stats_early), est)
+        np.testing.assert_array_equal(host(layer.state.tok2slot), ref.sm.tok2slot)
+        np.testing.assert_array_equal(host(layer.state.slot2tok), ref.sm.slot2tok)
+        assert int(host(layer.state.ctr)[0]) == ref.sm.head
+        assert int(host(layer.state.ctr)[5]) == 0
+        np.testing.assert_array_equal(host(layer.dev_cache), ref.cache)
+    np.testing.assert_array_equal(pool.numpy(), ref.pool)   # no write-back
+
+
+def test_dyadic_decode_fp8_batch():
+    need_gpu()
+    wl = wk.CONFIGS['decode-32x128k-fp8'].scaled(B=4, N=9000, C=20000, steps=5, variant='dyadic')
+    _run_bit_exact(wl, 5)
+
+
+def test_dyadic_decode_bf16_small_cache():
+    need_gpu()
+    wl = wk.CONFIGS['decode-1x16k-bf16'].scaled(N=6000, C=2100, variant='dyadic')
+    _run_bit_exact(wl, 4)
+
+
+def test_dyadic_decode_chunked_capacity():
+    """Batch demand above the cache: sequences run in chunks, later chunks
+    evict earlier ones' tokens; topic shifts force misses."""
+    need_gpu()
+    wl = wk.CONFIGS['decode-64x110k-fp8-capacity'].scaled(B=6, N=5000, len_lo=3000, C=5000, k=1024, cap=128,
+                                                          steps=5, variant='dyadic')
+    assert len(oracle_chunks(wl.lens, wl.k, wl.C)) > 1
+    _run_bit_exact(wl, 5)
+
+
+def test_normal_decode_full_size_single_sequence():
+    """The bf16 single-sequence workload at its full size and step count:
+    scores within tolerance of the oracle, selections valid against the oracle
+    scores, and the cache invariants after every step."""
+    need_gpu()
+    wl = wk.CONFIGS['decode-1x16k-bf16']
+    keys, scale, w, pool, layer = _setup(wl)
+    for s, q in enumerate(wk.decode_queries(wl)):
+        layer.step(dev(q))
+        torch.cuda.synchronize()
+        ref = oracle.index_logits(q, w, keys, 'bf16', scale, wl.tok0, wl.lens)[0]
+        got = host(layer.logits)[0, :wl.N]
+        scale_row = np.abs(ref).max()
+        err = np.abs(got - ref) / np.maximum(np.abs(ref), 1e-2 * scale_row)
+        assert err.max() <= TOL_BF16
+        idx = host(layer.idx)[0]
+        kth_ref = np.sort(ref)[-wl.k]
+        mask = np.zeros(wl.N, bool)
+        mask[idx] = True
+        tol = TOL_BF16 * max(abs(kth_ref), 1e-2 * scale_row)
+        assert ref[mask].min() >= kth_ref - tol
+        assert ref[~mask].max() <= kth_ref + tol
+        t2s = host(layer.state.tok2slot)
+        s2t = host(layer.state.slot2tok)
+        assert np.all(t2s[idx] >= 0)
+        occ = np.nonzero(s2t >= 0)[0]
+        assert np.all(t2s[s2t[occ]] == occ)
+        np.testing.assert_array_equal(host(layer.dev_cache)[occ], pool.numpy()[s2t[occ]])
+        np.testing.assert_array_equal(host(layer.sel_slot)[0], t2s[idx])

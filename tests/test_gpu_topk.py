@@ -1,0 +1,110 @@
+"""Exact top-k on the GPU against the oracle's stable sort, bit for bit.
+
+Both sides get the same float32 score rows (drawn by the generator or computed
+by the oracle), so idx, kth and the EMA threshold must match exactly. The
+threshold only steers speed; every theta (none, exact, off by a little, far
+off so the boundary bin overflows its list) must give the same set.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import workloads as wk
+from gpu_util import need_gpu, run_topk
+
+pytestmark = pytest.mark.gpu
+
+
+def _check(scores, lens, k, theta=None):
+    idx, kth, th_out = run_topk(scores, lens, k, theta)
+    for r, n in enumerate(lens):
+        ref_idx, ref_kth = oracle.topk_row(scores[r, :n], k)
+        np.testing.assert_array_equal(idx[r], ref_idx, err_msg=f'row {r} len {n}')
+        if np.isnan(ref_kth):
+            assert np.isnan(kth[r])
+        else:
+            assert kth[r] == ref_kth, (r, kth[r], ref_kth)
+        th_in = np.float32(np.nan) if theta is None else np.float32(theta[r])
+        want = oracle.theta_next(th_in, ref_kth)
+        if np.isnan(want):
+            assert np.isnan(th_out[r])
+        else:
+            assert th_out[r] == want, (r, th_out[r], want)
+    return idx, kth
+
+
+def _pad(x, ld):
+    out = np.zeros((x.shape[0], ld), np.float32)
+    out[:, :x.shape[1]] = x
+    return out
+
+
+@pytest.mark.parametrize('kind', ['normal', 'ties', 'const', 'signed'])
+def test_kinds_ragged_lengths(kind):
+    need_gpu()
+    n = 20000
+    x = wk.random_logits(1, 6, n, kind)
+    lens = [20000, 2048, 2049, 1, 0, 12345]
+    _check(_pad(x, 20000), lens, 2048)
+
+
+@pytest.mark.parametrize('k', [1, 7, 2048, 4096])
+def test_various_k(k):
+    need_gpu()
+    x = wk.random_logits(2, 3, 30001, 'normal')
+    _check(_pad(x, 30004), [30001, 9000, 4100], k)
+
+
+def test_theta_exact_and_offsets():
+    need_gpu()
+    x = wk.random_logits(3, 8, 65536, 'normal')
+    lens = [65536] * 8
+    kth = np.array([oracle.topk_row(x[r], 2048)[1] for r in range(8)], np.float32)
+    offs = np.array([0.0, 1e-6, -1e-6, 0.01, -0.01, 0.3, -0.3, np.nan], np.float32)
+    _check(x, lens, 2048, kth + offs)
+
+
+def test_theta_far_off_overflows_candidate_list():
+    need_gpu()
+    x = wk.random_logits(4, 4, 200000, 'normal')
+    theta = np.array([-100.0, 100.0, 18.0, 1e30], np.float32)
+    _check(_pad(x, 200000), [200000] * 4, 2048, theta)
+
+
+def test_ties_at_the_boundary_with_theta():
+    need_gpu()
+    x = wk.random_logits(5, 4, 50000, 'ties')   # integers 0..63: huge tie groups
+    theta = np.array([np.nan, 62.0, 61.5, 63.0], np.float32)
+    _check(x, [50000] * 4, 2048, theta)
+
+
+def test_oracle_scores_full_row_decode_shape():
+    """fp32 casts of oracle scores for a 32 x 131072 fp8 decode batch, with
+    the previous step's k-th scores as theta."""
+    need_gpu()
+    wl = wk.CONFIGS['decode-32x128k-fp8'].scaled(B=4)
+    keys, scale = wk.keys(wl)
+    qs = wk.decode_queries(wl, 2)
+    w = wk.head_weights(wl)
+    q0, q1 = next(qs), next(qs)
+    s0 = np.stack(oracle.index_logits(q0, w, keys, 'fp8', scale, wl.tok0, wl.lens)).astype(np.float32)
+    s1 = np.stack(oracle.index_logits(q1, w, keys, 'fp8', scale, wl.tok0, wl.lens)).astype(np.float32)
+    _, kth0 = _check(s0, list(wl.lens), 2048)
+    _check(s1, list(wl.lens), 2048, kth0)
+
+
+def test_long_rows():
+    need_gpu()
+    x = wk.random_logits(6, 2, 1 << 20, 'normal')
+    kth = np.array([oracle.topk_row(x[0], 2048)[1], np.nan], np.float32)
+    _check(x, [1 << 20, (1 << 20) - 3], 2048, kth + np.float32(0.05))
+
+
+def test_many_rows_prefill_shape():
+    """4096 rows with causal lengths (row r sees r + 1 + offset tokens)."""
+    need_gpu()
+    R, off = 512, 3000
+    x = wk.random_logits(7, R, off + R, 'normal')
+    lens = [off + r + 1 for r in range(R)]
+    ld = ((off + R + 3) // 4) * 4
+    _check(_pad(x, ld), lens, 2048)
