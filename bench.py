@@ -1,0 +1,289 @@
+#!/usr/bin/env python3
+"""Benchmark of one layer of the indexer -> exact top-k -> KV-recall path on
+one MI355X.
+
+Default workload: decode, 32 sequences x 131072 tokens, fp8 indexer keys
+(64 heads x 128) with per-token scales, k = 2048, early-fetch cap 512, device
+cache 260000 slots, host pool of 4.19M rows x 1152 B in pinned memory, q from
+an AR(1) process (rho 0.9). A step is one full pass of the path for the
+batch: indexer scores, exact top-k + threshold update, early fetch (second
+stream), final slot-map step and recall. Inputs are resident in HBM (and the
+pinned pool) before the timed region; W warm-up steps (the cold first step
+included) are untimed, then exactly K steps are timed between two device
+synchronisations.
+
+Prints one JSON line (stdout). Progress goes to stderr.
+
+  python bench.py [--steps K] [--warmup W] [--config NAME] [--no-cpu-baseline]
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0           # MI355X HBM3E, vendor figure
+PEAK_BF16_TFLOPS = 2500.0       # MI355X dense bf16 MFMA, vendor figure
+
+
+def log(*a):
+    print('[bench]', *a, file=sys.stderr, flush=True)
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument('--gpus', type=int, default=1)
+    p.add_argument('--steps', type=int, default=30)
+    p.add_argument('--warmup', type=int, default=2)
+    p.add_argument('--config', default='decode-32x128k-fp8')
+    p.add_argument('--no-cpu-baseline', action='store_true')
+    p.add_argument('--no-early', action='store_true', help='disable the early fetch (ablation)')
+    p.add_argument('--cpu-seqs', type=int, default=4, help='sequences in the oracle sample')
+    p.add_argument('--cpu-steps', type=int, default=2, help='decode steps in the oracle sample')
+    return p.parse_args()
+
+
+def source_hash(*names):
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, 'indexer_top_kv_amd', 'csrc', n), 'rb') as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel_key, src_hash):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if
+    it was taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, 'profiles', 'hbm_traffic.json')
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        d = json.load(f)
+    e = d.get(kernel_key)
+    if not e or e.get('source_hash') != src_hash:
+        return None
+    return e.get('bytes_per_launch')
+
+
+def cpu_cores():
+    try:
+        from threadpoolctl import threadpool_info
+        n = max([i.get('num_threads', 1) for i in threadpool_info()] or [1])
+    except Exception:
+        n = 1
+    return int(n)
+
+
+# ---------------------------------------------------------------------------- decode
+def bench_decode(args, wl):
+    import numpy as np
+    import torch
+    import workloads as wk
+    from indexer_top_kv_amd.pipeline import DecodeLayer
+
+    dev = lambda x: torch.from_numpy(np.ascontiguousarray(x.view(np.int16) if x.dtype == np.uint16 else x)).cuda()
+    t = time.time()
+    keys, scale = wk.keys(wl)
+    w = wk.head_weights(wl)
+    log(f'keys {keys.shape} generated in {time.time() - t:.1f}s')
+    t = time.time()
+    pool = torch.empty((wl.P, wk.ROW_ELEMS), dtype=torch.int16, pin_memory=True)
+    wk.host_rows(wl, out=pool.numpy().view(np.uint16))
+    log(f'host pool {wl.P} rows x {wk.ROW_BYTES} B pinned in {time.time() - t:.1f}s')
+    total_steps = args.warmup + args.steps
+    qs = np.stack(list(wk.decode_queries(wl, total_steps)))
+    kc, ks, wd = dev(keys), (dev(scale) if scale is not None else None), dev(w)
+    qd = dev(qs)
+    layer = DecodeLayer(kc, ks, wd, wl.tok0, wl.lens, wl.C, k=wl.k, cap=wl.cap, host_pool=pool,
+                        early=not args.no_early)
+    torch.cuda.synchronize()
+    log(f'chunks {layer.chunks}; warm-up {args.warmup} steps')
+    for s in range(args.warmup):
+        layer.step(qd[s])
+    torch.cuda.synchronize()
+    recalled0 = int(layer.state.ctr[4].item())
+    marks = {}
+    log(f'timing {args.steps} steps')
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        layer.step(qd[args.warmup + s], marks)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    recalled = int(layer.state.ctr[4].item()) - recalled0
+    stats_final = layer.stats_final.cpu().numpy()
+    stats_early = layer.stats_early.cpu().numpy()
+
+    def avg_ms(name):
+        ev = marks.get(name, [])
+        if not ev:
+            return None
+        d = [ev[i].elapsed_time(ev[i + 1]) for i in range(0, len(ev), 2)]
+        return float(np.mean(d))
+
+    wall = t1 - t0
+    tokens = int(wl.lens.astype(np.int64).sum())
+    value = tokens * args.steps / wall
+    logits_ms = avg_ms('logits')
+    kbytes = 128 + 4 if wl.kdtype == 'fp8' else 256
+    per_token = kbytes + 4                                   # key (+scale) read, score written
+    per_launch = tokens * per_token + wl.B * (64 * 128 * 2 + 64 * 4)
+    achieved = per_launch / (logits_ms * 1e-3) / 1e9
+    flops = tokens * 2 * 64 * 128
+    src = source_hash('logits.hip')
+    traffic = measured_traffic('logits_decode_' + wl.name, src)
+    out = {
+        'metric': 'decode tokens scored/s (indexer logits + exact top-k + early/final slot-map step + recall), '
+                  '1 layer',
+        'value': value,
+        'unit': 'tokens/s',
+        'n_gpus': 1,
+        'steps': args.steps,
+        'warmup': args.warmup,
+        'ms_per_step': wall / args.steps * 1e3,
+        'higher_is_better': True,
+        'scaling': 'weak',
+        'vs_baseline': None,
+        'dtype': 'fp8-e4m3 keys, bf16 q, bf16 MFMA with fp32 accumulation',
+        'data': 'synthetic, seeded',
+        'config': {'workload': wl.name, 'B': wl.B, 'context': wl.N, 'k': wl.k, 'heads': 64, 'head_dim': 128,
+                   'key_dtype': wl.kdtype, 'cache_slots': wl.C, 'early_fetch_cap': wl.cap,
+                   'early_fetch': not args.no_early, 'row_bytes': 1152},
+        'roofline': {'bound': 'hbm', 'kernel': 'logits_decode_kernel', 'achieved': achieved,
+                     'peak': PEAK_HBM_GBS, 'unit': 'GB/s', 'frac': achieved / PEAK_HBM_GBS,
+                     'traffic': traffic, 'algorithmic_bytes_per_launch': per_launch,
+                     'avg_launch_us': logits_ms * 1e3,
+                     'mfma_bf16_frac': flops / (logits_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS},
+        'stages_us': {k: (avg_ms(k) or 0.0) * 1e3 for k in ('logits', 'topk', 'early', 'final')},
+        'recall': {'rows_per_step': recalled / args.steps, 'bytes_per_step': recalled * 1152 / args.steps},
+        'last_step': {'final_hits': int(stats_final[:, 0].sum()), 'final_misses': int(stats_final[:, 1].sum()),
+                      'early_fetched': int(stats_early[:, 1].sum()), 'evictions':
+                      int(stats_final[:, 3].sum() + stats_early[:, 3].sum())},
+        'logits_source': src,
+    }
+    return out, dict(wl=wl, pool=pool, qs=qs, w=w, keys=keys, scale=scale)
+
+
+def cpu_baseline_decode(args, wl, ctx):
+    """The oracle as it stands, on a bounded sample of the same workload: the
+    first `cpu_seqs` sequences for `cpu_steps` decode steps (scores, top-k,
+    threshold, early and final slot-map phases, recall)."""
+    import numpy as np
+    import oracle
+    import workloads as wk
+
+    S, T = min(args.cpu_seqs, wl.B), args.cpu_steps
+    sub = wl.scaled(B=S)
+    if wl.len_lo is not None:
+        raise SystemExit('cpu sample needs equal lengths')
+    keys = ctx['keys'][:sub.P]
+    scale = None if ctx['scale'] is None else ctx['scale'][:sub.P]
+    w = ctx['w'][:S]
+    pool = ctx['pool'].numpy()
+    sm = oracle.SlotMap(sub.P, wl.C)
+    cache = np.zeros((wl.C, pool.shape[1]), pool.dtype)
+    theta = np.full(S, np.nan, np.float32)
+    t0 = time.perf_counter()
+    for s in range(T):
+        q = ctx['qs'][s][:S]
+        L = [x.astype(np.float32) for x in oracle.index_logits(q, w, keys, wl.kdtype, scale, sub.tok0, sub.lens)]
+        idx, kth = oracle.topk_rows(L, wl.k)
+        a, _ = sm.early(sub.tok0, L, theta, wl.cap)
+        oracle.recall_rows(pool, cache, a)
+        a, _, _ = sm.final(sub.tok0, idx)
+        oracle.recall_rows(pool, cache, a)
+        theta = oracle.theta_rows(theta, kth)
+    dt = time.perf_counter() - t0
+    tokens = int(sub.lens.astype(np.int64).sum()) * T
+    return {'value': tokens / dt, 'unit': 'tokens/s', 'cores': cpu_cores(), 'kind': 'oracle',
+            'sample': f'first {S} of {wl.B} sequences x {T} decode steps ({tokens} tokens scored), '
+                      f'{dt:.1f} s; label: CPU oracle - reported baseline',
+            'seconds': dt, 'host_cpus': len(os.sched_getaffinity(0))}
+
+
+# ---------------------------------------------------------------------------- prefill
+def bench_prefill(args, wl):
+    import numpy as np
+    import torch
+    import workloads as wk
+    from indexer_top_kv_amd.pipeline import PrefillLayer
+
+    dev = lambda x: torch.from_numpy(np.ascontiguousarray(x.view(np.int16) if x.dtype == np.uint16 else x)).cuda()
+    keys, scale = wk.keys(wl)
+    pool = torch.empty((wl.P, wk.ROW_ELEMS), dtype=torch.int16, pin_memory=True)
+    wk.host_rows(wl, out=pool.numpy().view(np.uint16))
+    layer = PrefillLayer(dev(keys), dev(scale), wl.N, wl.C, k=wl.k, block_rows=wl.block_rows, host_pool=pool)
+    blocks = layer.blocks()
+    q = [dev(wk.prefill_queries(wl, r0, R)) for r0, R in blocks]
+    w = [dev(wk.head_weights(wl, rows=R, row0=r0)) for r0, R in blocks]
+    log(f'{len(blocks)} query blocks staged')
+    marks = []
+
+    def one_pass(timed):
+        layer.reset_state()
+        for i, (r0, R) in enumerate(blocks):
+            layer.run_block(r0, q[i], w[i], first=(i == 0), mark=marks if timed else None)
+        layer.finish()
+
+    for _ in range(args.warmup):
+        one_pass(False)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        one_pass(True)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    pairs = sum(sum(r0 + i + 1 for i in range(R)) for r0, R in blocks)
+    lg = [marks[i].elapsed_time(marks[i + 1]) for i in range(0, len(marks), 2)]
+    logits_ms_total = float(np.sum(lg)) / args.steps
+    flops = pairs * 2 * 64 * 128
+    tflops = flops / (logits_ms_total * 1e-3) / 1e12
+    return {
+        'metric': 'prefill (row, token) pairs scored/s (causal indexer logits + per-row exact top-k + '
+                  'union slot-map step + overlapped recall), 1 layer',
+        'value': pairs * args.steps / wall, 'unit': 'pairs/s', 'n_gpus': 1, 'steps': args.steps,
+        'warmup': args.warmup, 'ms_per_step': wall / args.steps * 1e3, 'higher_is_better': True,
+        'scaling': 'weak', 'vs_baseline': None, 'dtype': 'fp8-e4m3 keys, bf16 q, bf16 MFMA fp32 accumulation',
+        'data': 'synthetic, seeded',
+        'config': {'workload': wl.name, 'N': wl.N, 'block_rows': wl.block_rows, 'k': wl.k, 'cache_slots': wl.C},
+        'roofline': {'bound': 'mfma', 'kernel': 'logits_causal_kernel', 'achieved': tflops,
+                     'peak': PEAK_BF16_TFLOPS, 'unit': 'TFLOP/s', 'frac': tflops / PEAK_BF16_TFLOPS,
+                     'traffic': None, 'algorithmic_flops_per_pass': flops, 'logits_ms_per_pass': logits_ms_total},
+    }
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get('WORLD_SIZE', '1'))
+    if args.gpus != 1 or world != 1:
+        print('bench.py runs on one GPU only: this path is a per-layer, per-GPU kernel pipeline with no '
+              'inter-GPU exchange (sequences shard across GPUs with no communication); run with --gpus 1.',
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import workloads as wk
+    import indexer_top_kv_amd as ech
+    ech.lib()
+    assert torch.cuda.is_available(), 'no GPU'
+    torch.cuda.set_device(0)
+    wl = wk.CONFIGS[args.config]
+    log(f'{wl.name} on {torch.cuda.get_device_name(0)}')
+    if wl.mode == 'decode':
+        out, ctx = bench_decode(args, wl)
+        if not args.no_cpu_baseline:
+            log('timing the CPU oracle on a sample')
+            out['cpu_baseline'] = cpu_baseline_decode(args, wl, ctx)
+        else:
+            out['cpu_baseline'] = None
+    else:
+        out = bench_prefill(args, wl)
+        out['cpu_baseline'] = None
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == '__main__':
+    main()

@@ -88,7 +88,7 @@ class DecodeLayer:
                                     dtype=torch.uint8, **dev)
         self.host_pool = host_pool
         if host_pool is not None:
-            self.dev_cache = torch.empty((C, host_pool.shape[1]), dtype=host_pool.dtype, **dev)
+            self.dev_cache = torch.zeros((C, host_pool.shape[1]), dtype=host_pool.dtype, **dev)
         else:
             self.dev_cache = None
         self.s1 = torch.cuda.Stream(device=device)
@@ -116,27 +116,46 @@ class DecodeLayer:
         ech_index_logits(q, self.w, self.kcache, self.kscale, self.tok0, self.lens, self.max_len, self.logits,
                          stream=stream)
 
-    def step(self, q: torch.Tensor) -> None:
+    def step(self, q: torch.Tensor, marks: Optional[dict] = None) -> None:
         """Enqueue one decode step for query q [B, 64, 128] (bf16 bits) on the
-        current stream (with S1 forked and joined inside)."""
+        current stream (with S1 forked and joined inside). `marks`, when given,
+        receives timing events recorded on the stream of each stage:
+        logits, topk, final (S0) and early (S1), as (start, end) pairs."""
         s0 = torch.cuda.current_stream()
+
+        def mark(name, stream):
+            if marks is None:
+                return None
+            ev = torch.cuda.Event(enable_timing=True)
+            ev.record(stream)
+            marks.setdefault(name, []).append(ev)
+            return ev
+
         th, th_next = self.theta[self.parity], self.theta[1 - self.parity]
+        mark('logits', s0)
         self.logits_only(q, stream=s0)
+        mark('logits', s0)
         first_b0, first_b1 = self.chunks[0]
         if self.early:
             self.ev_logits.record(s0)
-            self.s1.wait_stream(s0)
+            self.s1.wait_event(self.ev_logits)
+            mark('early', self.s1)
             self._phase(ECH_EARLY, first_b0, first_b1, th, self.s1)
+            mark('early', self.s1)
             self.ev_early.record(self.s1)
+        mark('topk', s0)
         ech_topk(self.logits, self.lens, self.max_len, self.k, th, th_next, self.idx, self.kth, self.ws_topk,
                  stream=s0)
+        mark('topk', s0)
         if self.early:
             s0.wait_event(self.ev_early)
+        mark('final', s0)
         self._phase(ECH_FINAL, first_b0, first_b1, th, s0)
         for b0, b1 in self.chunks[1:]:
             if self.early:
                 self._phase(ECH_EARLY, b0, b1, th, s0)
             self._phase(ECH_FINAL, b0, b1, th, s0)
+        mark('final', s0)
         self.parity ^= 1
 
     @property
@@ -169,8 +188,9 @@ class PrefillLayer:
         self.seq_tok0 = torch.tensor([tok0], dtype=torch.int64, **dev)
         self.seq_len = torch.tensor([N], dtype=torch.int32, **dev)
         self.row_len = torch.arange(1, block_rows + 1, dtype=torch.int32, **dev)
+        self._row_lens = {}
         self.host_pool = host_pool
-        self.dev_cache = (torch.empty((C, host_pool.shape[1]), dtype=host_pool.dtype, **dev)
+        self.dev_cache = (torch.zeros((C, host_pool.shape[1]), dtype=host_pool.dtype, **dev)
                           if host_pool is not None else None)
         self.s1 = torch.cuda.Stream(device=device)
         self.ev_recall = torch.cuda.Event()
@@ -179,13 +199,34 @@ class PrefillLayer:
     def blocks(self):
         return [(r0, min(self.block_rows, self.N - r0)) for r0 in range(0, self.N, self.block_rows)]
 
-    def run_block(self, row0: int, q: torch.Tensor, w: torch.Tensor, first: bool) -> None:
-        """q [R,64,128], w [R,64] for rows row0 .. row0+R-1, on the current stream."""
+    def reset_state(self) -> None:
+        """Start the sequence again: empty cache, no threshold predictions."""
+        ech_cache_reset(self.state)
+        self.theta.fill_(float('nan'))
+
+    def _row_len(self, row0: int, R: int) -> torch.Tensor:
+        key = (row0, R)
+        if key not in self._row_lens:
+            self._row_lens[key] = self.row_len[:R] + row0
+        return self._row_lens[key]
+
+    def run_block(self, row0: int, q: torch.Tensor, w: torch.Tensor, first: bool, mark=None) -> None:
+        """q [R,64,128], w [R,64] for rows row0 .. row0+R-1, on the current
+        stream. `mark`, when given, receives a (start, end) event pair around
+        the scoring launch."""
         s0 = torch.cuda.current_stream()
         R = q.shape[0]
         logits = self.logits[:R]
+        row_len = self._row_len(row0, R)
+        if mark is not None:
+            ev = torch.cuda.Event(enable_timing=True)
+            ev.record(s0)
+            mark.append(ev)
         ech_index_logits_causal(q, w, self.kcache, self.kscale, self.tok0, row0, logits, stream=s0)
-        row_len = self.row_len[:R] + row0
+        if mark is not None:
+            ev = torch.cuda.Event(enable_timing=True)
+            ev.record(s0)
+            mark.append(ev)
         # rows' thresholds: the EMA of the same row position in earlier blocks
         ech_topk(logits, row_len, row0 + R, self.k, self.theta[:R], self.theta[:R], self.idx[:R], self.kth[:R],
                  self.ws_topk, stream=s0)
