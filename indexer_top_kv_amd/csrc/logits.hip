@@ -169,33 +169,40 @@ __global__ __launch_bounds__(kThreads) void logits_decode_kernel(
   const float* sbase = (KDT == ECH_KEY_FP8) ? ksc + g0 : nullptr;
   float* orow = out + (size_t)r * ld;
 
-  int tb = wg_t0 + wave * 16;
-  if (tb >= len) return;
-  KeyFrag<KDT> cur;
-  int tc = min(tb + col, len - 1);
-  load_key<KDT>(cur, kbase + (size_t)tc * kRowB, grp);
-  float sc = (KDT == ECH_KEY_FP8) ? sbase[tc] : 1.f;
-#pragma unroll 1
-  for (int it = 0; it < tpw; ++it) {
-    const int tn = tb + kWaves * 16;
-    const bool more = (it + 1 < tpw) && (tn < len);
-    KeyFrag<KDT> nxt;
-    float scn = 1.f;
-    if (more) {
-      const int tcn = min(tn + col, len - 1);
-      load_key<KDT>(nxt, kbase + (size_t)tcn * kRowB, grp);
-      if (KDT == ECH_KEY_FP8) scn = sbase[tcn];
-    }
+  // This wave's tiles start at wg_t0 + (it * kWaves + wave) * 16.
+  const int first = wg_t0 + wave * 16;
+  if (first >= len) return;
+  const int n_it = min(tpw, (len - first + kWaves * 16 - 1) / (kWaves * 16));
+
+  auto load = [&](KeyFrag<KDT>& f, float& sc, int it) {
+    const int tc = min(first + it * kWaves * 16 + col, len - 1);
+    load_key<KDT>(f, kbase + (size_t)tc * kRowB, grp);
+    sc = (KDT == ECH_KEY_FP8) ? sbase[tc] : 1.f;
+  };
+  auto proc = [&](const KeyFrag<KDT>& f, float sc, int it) {
     bf16x8_t b[4];
 #pragma unroll
-    for (int s = 0; s < 4; ++s) b[s] = key_step<KDT>(cur, s);
+    for (int s = 0; s < 4; ++s) b[s] = key_step<KDT>(f, s);
     const float v = tile_score(a, wv, b, sc);
-    const int t = tb + col;
+    const int t = first + it * kWaves * 16 + col;
     if (grp == 0 && t < len) orow[t] = v;
-    if (!more) break;
-    cur = nxt;
-    sc = scn;
-    tb = tn;
+  };
+  // Four register buffers: three tiles stay in flight while one is multiplied.
+  KeyFrag<KDT> f0, f1, f2, f3;
+  float s0 = 1.f, s1 = 1.f, s2 = 1.f, s3 = 1.f;
+  load(f0, s0, 0);
+  if (n_it > 1) load(f1, s1, 1);
+  if (n_it > 2) load(f2, s2, 2);
+#pragma unroll 1
+  for (int it = 0; it < n_it; it += 4) {
+    if (it + 3 < n_it) load(f3, s3, it + 3);
+    proc(f0, s0, it);
+    if (it + 4 < n_it) load(f0, s0, it + 4);
+    if (it + 1 < n_it) proc(f1, s1, it + 1);
+    if (it + 5 < n_it) load(f1, s1, it + 5);
+    if (it + 2 < n_it) proc(f2, s2, it + 2);
+    if (it + 6 < n_it) load(f2, s2, it + 6);
+    if (it + 3 < n_it) proc(f3, s3, it + 3);
   }
 }
 

@@ -9,7 +9,7 @@
 // so the kernels find s* and need_eq, then compact in ascending t.
 //
 //   T1 hist     grid (chunks, R): LDS histogram of bin(t) = top 8 bits of
-//               ord(fl32(s_t - theta)) per 8192-token chunk. fl32(s - theta)
+//               ord(fl32(s_t - theta)) per 4096-token chunk. fl32(s - theta)
 //               is monotone in s and ord() is order preserving, so higher bins
 //               hold strictly larger scores.
 //   T2 rowsel   grid (R): sum the chunk histograms, boundary bin b* where the
@@ -34,11 +34,12 @@
 
 namespace {
 
-constexpr int kChunk = 8192;        // tokens per chunk (T1, T3, T5)
+constexpr int kChunk = 4096;        // tokens per chunk (T1, T3, T5)
+constexpr int kVec = kChunk / (4 * 256);   // float4 loads per thread
 constexpr int kT = 256;             // threads for chunk kernels
 constexpr int kRT = 1024;           // threads for the per-row resolve kernel
 constexpr int kMaxK = 4096;
-constexpr int kMaxChunks = 1024;    // max_len <= 8M
+constexpr int kMaxChunks = 1024;    // max_len <= 4M
 
 enum RowMode : int { kNormal = 0, kAll = 1, kEmpty = 2 };
 
@@ -104,6 +105,25 @@ __device__ __forceinline__ float row_theta(const float* th, int r) {
 }
 
 // ------------------------------------------------------------------ T1
+// Load a chunk's 16 scores per thread (4 float4, issued before any use);
+// element j*4 + e of thread tid is token lo + 4*(j*256 + tid) + e.
+__device__ __forceinline__ void load_chunk(const float* row, int lo, int hi, float4 (&v)[kVec]) {
+#pragma unroll
+  for (int j = 0; j < kVec; ++j) {
+    const int t = lo + 4 * (j * kT + (int)threadIdx.x);
+    if (t + 3 < hi) {
+      v[j] = *reinterpret_cast<const float4*>(row + t);
+    } else {
+      v[j] = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (t < hi) v[j].x = row[t];
+      if (t + 1 < hi) v[j].y = row[t + 1];
+      if (t + 2 < hi) v[j].z = row[t + 2];
+    }
+  }
+}
+
+__device__ __forceinline__ float f4(const float4& v, int e) { return e == 0 ? v.x : e == 1 ? v.y : e == 2 ? v.z : v.w; }
+
 __global__ __launch_bounds__(kT) void topk_hist_kernel(const float* __restrict__ logits, int64_t ld,
                                                        const int32_t* __restrict__ lens, int k,
                                                        const float* __restrict__ theta, Ws ws) {
@@ -114,24 +134,15 @@ __global__ __launch_bounds__(kT) void topk_hist_kernel(const float* __restrict__
   const int hi = min(lo + kChunk, len);
   __shared__ int h[256];
   h[threadIdx.x] = 0;
-  __syncthreads();
   const float th = row_theta(theta, r);
-  const float* row = logits + (size_t)r * ld;
-#pragma unroll 2
-  for (int i = 0; i < kChunk / (4 * kT); ++i) {
-    const int t = lo + (i * kT + threadIdx.x) * 4;
-    float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (t + 3 < hi) {
-      v = *reinterpret_cast<const float4*>(row + t);
-    } else if (t < hi) {
-      v.x = row[t];
-      if (t + 1 < hi) v.y = row[t + 1];
-      if (t + 2 < hi) v.z = row[t + 2];
-    }
-    ech::lds_hist_add(h, shifted_bin(v.x, th), t < hi);
-    ech::lds_hist_add(h, shifted_bin(v.y, th), t + 1 < hi);
-    ech::lds_hist_add(h, shifted_bin(v.z, th), t + 2 < hi);
-    ech::lds_hist_add(h, shifted_bin(v.w, th), t + 3 < hi);
+  float4 v[kVec];
+  load_chunk(logits + (size_t)r * ld, lo, hi, v);
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < kVec; ++j) {
+    const int t = lo + 4 * (j * kT + (int)threadIdx.x);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) ech::lds_hist_add(h, shifted_bin(f4(v[j], e), th), t + e < hi);
   }
   __syncthreads();
   ws.hist[((size_t)r * ws.nch + c) * 256 + threadIdx.x] = h[threadIdx.x];
@@ -179,28 +190,34 @@ __global__ __launch_bounds__(kT) void topk_gather_kernel(const float* __restrict
   const int hi = min(lo + kChunk, len);
   const float th = row_theta(theta, r);
   const uint32_t bstar = (uint32_t)st.bstar;
-  const float* row = logits + (size_t)r * ld;
+  float4 v[kVec];
+  load_chunk(logits + (size_t)r * ld, lo, hi, v);
   int2* cand = ws.cand + (size_t)r * ws.cap;
   int* cnt = &ws.rs[r].cand;
   const int lane = ech::lane_id();
   __shared__ int scratch[kT / 64];
   int above = 0;
-  for (int i = 0; i < kChunk / kT; ++i) {
-    const int t = lo + i * kT + threadIdx.x;
-    const bool ok = t < hi;
-    const float x = ok ? row[t] : 0.f;
-    const uint32_t b = shifted_bin(x, th);
-    above += (ok && b > bstar) ? 1 : 0;
-    const bool is_c = ok && b == bstar;
-    const uint64_t m = __ballot(is_c);
-    if (m) {
-      int base = 0;
-      const int leader = __ffsll((unsigned long long)m) - 1;
-      if (lane == leader) base = atomicAdd(cnt, __popcll(m));
-      base = __shfl(base, leader, 64);
-      if (is_c) {
-        const int pos = base + __popcll(m & ((1ull << lane) - 1ull));
-        if (pos < ws.cap) cand[pos] = make_int2(__float_as_int(x), t);
+#pragma unroll
+  for (int j = 0; j < kVec; ++j) {
+    const int t0 = lo + 4 * (j * kT + (int)threadIdx.x);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int t = t0 + e;
+      const bool ok = t < hi;
+      const float x = f4(v[j], e);
+      const uint32_t b = shifted_bin(x, th);
+      above += (ok && b > bstar) ? 1 : 0;
+      const bool is_c = ok && b == bstar;
+      const uint64_t m = __ballot(is_c);
+      if (m) {
+        int base = 0;
+        const int leader = __ffsll((unsigned long long)m) - 1;
+        if (lane == leader) base = atomicAdd(cnt, __popcll(m));
+        base = __shfl(base, leader, 64);
+        if (is_c) {
+          const int pos = base + __popcll(m & ((1ull << lane) - 1ull));
+          if (pos < ws.cap) cand[pos] = make_int2(__float_as_int(x), t);
+        }
       }
     }
   }
@@ -389,45 +406,38 @@ __global__ __launch_bounds__(kT) void topk_compact_kernel(const float* __restric
   const RowState st = ws.rs[r];
   if (st.mode == kEmpty) return;
   const int hi = min(lo + kChunk, len);
+  float4 v[kVec];
+  load_chunk(logits + (size_t)r * ld, lo, hi, v);
   const float sp = st.spred;
   const int base = ws.off[(size_t)r * ws.nch + c];
   const int te = ws.take[(size_t)r * ws.nch + c];
-  const float* row = logits + (size_t)r * ld;
   __shared__ int scratch[kT / 64];
   int gt_run = 0, eq_run = 0;   // block-uniform running counts
-#pragma unroll 1
-  for (int i = 0; i < kChunk / (4 * kT); ++i) {
-    const int t = lo + (i * kT + threadIdx.x) * 4;
-    float v[4];
-    bool ok[4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      ok[j] = t + j < hi;
-      v[j] = ok[j] ? row[t + j] : 0.f;
-    }
+  for (int j = 0; j < kVec; ++j) {
+    const int t = lo + 4 * (j * kT + (int)threadIdx.x);
     int ngt = 0, neq = 0;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      ngt += (ok[j] && v[j] > sp) ? 1 : 0;
-      neq += (ok[j] && v[j] == sp) ? 1 : 0;
+    for (int e = 0; e < 4; ++e) {
+      const float x = f4(v[j], e);
+      const bool ok = t + e < hi;
+      ngt += (ok && x > sp) ? 1 : 0;
+      neq += (ok && x == sp) ? 1 : 0;
     }
     int tot;
     const int pre = ech::block_excl_scan<kT>(ngt | (neq << 16), scratch, &tot);
     int gt_b = gt_run + (pre & 0xffff);
     int eq_b = eq_run + (pre >> 16);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      if (!ok[j]) continue;
-      bool sel = false;
-      if (v[j] > sp) {
-        sel = true;
-      } else if (v[j] == sp) {
-        sel = eq_b < te;
-      }
+    for (int e = 0; e < 4; ++e) {
+      const float x = f4(v[j], e);
+      if (t + e >= hi) continue;
+      const bool gt = x > sp, eq = x == sp;
+      const bool sel = gt || (eq && eq_b < te);
       const int pos = base + gt_b + min(eq_b, te);
-      if (sel && pos < k) orow[pos] = t + j;
-      if (v[j] > sp) ++gt_b;
-      else if (v[j] == sp) ++eq_b;
+      if (sel && pos < k) orow[pos] = t + e;
+      gt_b += gt;
+      eq_b += eq;
     }
     gt_run += tot & 0xffff;
     eq_run += tot >> 16;
