@@ -42,6 +42,7 @@ def parse():
     p.add_argument('--config', default='decode-32x128k-fp8')
     p.add_argument('--no-cpu-baseline', action='store_true')
     p.add_argument('--no-early', action='store_true', help='disable the early fetch (ablation)')
+    p.add_argument('--eager', action='store_true', help='time eager launches instead of graph replays')
     p.add_argument('--cpu-seqs', type=int, default=4, help='sequences in the oracle sample')
     p.add_argument('--cpu-steps', type=int, default=2, help='decode steps in the oracle sample')
     return p.parse_args()
@@ -94,7 +95,8 @@ def bench_decode(args, wl):
     pool = torch.empty((wl.P, wk.ROW_ELEMS), dtype=torch.int16, pin_memory=True)
     wk.host_rows(wl, out=pool.numpy().view(np.uint16))
     log(f'host pool {wl.P} rows x {wk.ROW_BYTES} B pinned in {time.time() - t:.1f}s')
-    total_steps = args.warmup + args.steps
+    n_stage = 4                                       # extra eager steps for the stage breakdown
+    total_steps = args.warmup + args.steps + n_stage
     qs = np.stack(list(wk.decode_queries(wl, total_steps)))
     kc, ks, wd = dev(keys), (dev(scale) if scale is not None else None), dev(w)
     qd = dev(qs)
@@ -105,18 +107,40 @@ def bench_decode(args, wl):
     for s in range(args.warmup):
         layer.step(qd[s])
     torch.cuda.synchronize()
+    if not args.eager:
+        layer.capture()
+        torch.cuda.synchronize()
     recalled0 = int(layer.state.ctr[4].item())
-    marks = {}
-    log(f'timing {args.steps} steps')
+    log(f'timing {args.steps} steps ({"eager launches" if args.eager else "hipGraph replay per step"})')
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for s in range(args.steps):
-        layer.step(qd[args.warmup + s], marks)
+        if args.eager:
+            layer.step(qd[args.warmup + s])
+        else:
+            layer.replay(qd[args.warmup + s])
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     recalled = int(layer.state.ctr[4].item()) - recalled0
     stats_final = layer.stats_final.cpu().numpy()
     stats_early = layer.stats_early.cpu().numpy()
+
+    # The roofline kernel, timed with HIP events on its launch stream: the
+    # same launch (same q, keys, grid) repeated K times back to back.
+    s0 = torch.cuda.current_stream()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * args.steps)]
+    for s in range(args.steps):
+        ev[2 * s].record(s0)
+        layer.logits_only(qd[args.warmup + s], stream=s0)
+        ev[2 * s + 1].record(s0)
+    torch.cuda.synchronize()
+    logits_runs = [ev[2 * s].elapsed_time(ev[2 * s + 1]) for s in range(args.steps)]
+
+    # Stage breakdown from a few eager steps with events on each stage's stream.
+    marks = {}
+    for s in range(n_stage):
+        layer.step(qd[args.warmup + args.steps + s], marks)
+    torch.cuda.synchronize()
 
     def avg_ms(name):
         ev = marks.get(name, [])
@@ -128,7 +152,7 @@ def bench_decode(args, wl):
     wall = t1 - t0
     tokens = int(wl.lens.astype(np.int64).sum())
     value = tokens * args.steps / wall
-    logits_ms = avg_ms('logits')
+    logits_ms = float(np.mean(logits_runs))
     kbytes = 128 + 4 if wl.kdtype == 'fp8' else 256
     per_token = kbytes + 4                                   # key (+scale) read, score written
     per_launch = tokens * per_token + wl.B * (64 * 128 * 2 + 64 * 4)
@@ -152,13 +176,14 @@ def bench_decode(args, wl):
         'data': 'synthetic, seeded',
         'config': {'workload': wl.name, 'B': wl.B, 'context': wl.N, 'k': wl.k, 'heads': 64, 'head_dim': 128,
                    'key_dtype': wl.kdtype, 'cache_slots': wl.C, 'early_fetch_cap': wl.cap,
-                   'early_fetch': not args.no_early, 'row_bytes': 1152},
+                   'early_fetch': not args.no_early, 'row_bytes': 1152,
+                   'launch': 'eager' if args.eager else 'hipGraph replay per step'},
         'roofline': {'bound': 'hbm', 'kernel': 'logits_decode_kernel', 'achieved': achieved,
                      'peak': PEAK_HBM_GBS, 'unit': 'GB/s', 'frac': achieved / PEAK_HBM_GBS,
                      'traffic': traffic, 'algorithmic_bytes_per_launch': per_launch,
                      'avg_launch_us': logits_ms * 1e3,
                      'mfma_bf16_frac': flops / (logits_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS},
-        'stages_us': {k: (avg_ms(k) or 0.0) * 1e3 for k in ('logits', 'topk', 'early', 'final')},
+        'stages_us_eager': {k: (avg_ms(k) or 0.0) * 1e3 for k in ('logits', 'topk', 'early', 'final')},
         'recall': {'rows_per_step': recalled / args.steps, 'bytes_per_step': recalled * 1152 / args.steps},
         'last_step': {'final_hits': int(stats_final[:, 0].sum()), 'final_misses': int(stats_final[:, 1].sum()),
                       'early_fetched': int(stats_early[:, 1].sum()), 'evictions':
@@ -166,6 +191,49 @@ def bench_decode(args, wl):
         'logits_source': src,
     }
     return out, dict(wl=wl, pool=pool, qs=qs, w=w, keys=keys, scale=scale)
+
+
+def pcie_check(pool, C, rows=16384, reps=5):
+    """Host->device bandwidth two ways on this machine: a pinned 256 MiB
+    hipMemcpyAsync (DMA engines; the denominator) and the recall gather kernel
+    copying `rows` random rows of the pinned pool into a scratch cache through a
+    synthetic miss list (separate buffers; the layer's state is untouched)."""
+    import numpy as np
+    import torch
+    import indexer_top_kv_amd as ech
+
+    src = torch.empty(256 << 20, dtype=torch.uint8, pin_memory=True)
+    dst = torch.empty(256 << 20, dtype=torch.uint8, device='cuda')
+    best = 0.0
+    for _ in range(reps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        dst.copy_(src, non_blocking=True)
+        b.record()
+        torch.cuda.synchronize()
+        best = max(best, src.numel() / (a.elapsed_time(b) * 1e-3) / 1e9)
+    del src, dst
+    P = pool.shape[0]
+    rng = np.random.default_rng(7)
+    g = rng.choice(P, rows, replace=False).astype(np.int32)
+    p = rng.permutation(min(C, rows)).astype(np.int32)[:rows]
+    st = ech.LayerState.allocate(P, C, rows)
+    st.miss.copy_(torch.from_numpy(np.stack([g, p], 1)))
+    ctr = np.zeros(ech.CTR_LEN, np.int32)
+    ctr[ech.CTR_NMISS] = rows
+    st.ctr.copy_(torch.from_numpy(ctr))
+    cache = torch.empty((C, pool.shape[1]), dtype=pool.dtype, device='cuda')
+    t = []
+    for _ in range(reps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        ech.ech_recall(pool, cache, st)
+        b.record()
+        torch.cuda.synchronize()
+        t.append(a.elapsed_time(b))
+    gather = rows * pool.shape[1] * pool.element_size() / (min(t) * 1e-3) / 1e9
+    return {'h2d_memcpy_GBs': best, 'recall_gather_GBs': gather, 'gather_rows': rows,
+            'frac_of_memcpy': gather / best}
 
 
 def cpu_baseline_decode(args, wl, ctx):
@@ -274,6 +342,7 @@ def main():
     log(f'{wl.name} on {torch.cuda.get_device_name(0)}')
     if wl.mode == 'decode':
         out, ctx = bench_decode(args, wl)
+        out['pcie'] = pcie_check(ctx['pool'], wl.C)
         if not args.no_cpu_baseline:
             log('timing the CPU oracle on a sample')
             out['cpu_baseline'] = cpu_baseline_decode(args, wl, ctx)

@@ -9,7 +9,7 @@
  *   1. ech_index_logits / ech_index_logits_causal: indexer score of every
  *      cached token, logit[r,t] = sum_h w[r,h] * ReLU(q[r,h,:] . k[g,:]).
  *   2. ech_topk: exact top-k of each row (ties to the lower token index) found
- *      with a 256-bin histogram of the top 8 bits of (score - theta), theta
+ *      with a 256-bin histogram keyed by the high byte of (score - theta), theta
  *      being an EMA (alpha = 0.5) of the previous step's k-th score.
  *   3. ech_cache_step: GPU-resident per-layer slot map. EARLY (decode): fetch
  *      tokens scoring above theta, up to a cap, before the top-k is known.
@@ -66,12 +66,13 @@ extern "C" {
 /* ---- the control tensor ctr[ECH_CTR_LEN] (int32, device), one per layer */
 #define ECH_CTR_HEAD      0   /* ring head: next slot the allocator looks at */
 #define ECH_CTR_EPOCH     1   /* phase counter; slot s is pinned in a phase iff slot_pin[s] == epoch */
-#define ECH_CTR_NMISS     2   /* entries written to the miss list by the last phase */
+#define ECH_CTR_NMISS     2   /* entries written to the miss list by the last FINAL/PREFILL phase */
 #define ECH_CTR_NEVICT    3   /* resident tokens evicted by the last phase */
 #define ECH_CTR_RECALLED  4   /* rows copied by ech_recall since reset (wraps at 2^31) */
 #define ECH_CTR_STATUS    5   /* sticky ECH_ST_* bits */
 #define ECH_CTR_NWANT     6   /* misses the last phase wanted (before cap / slot limits) */
 #define ECH_CTR_NPINNED   7   /* slots pinned by the last phase */
+#define ECH_CTR_NMISS_EARLY 8 /* entries written to the miss list by the last EARLY phase */
 #define ECH_CTR_LEN      16
 
 /* ---- sticky status bits in ctr[ECH_CTR_STATUS] */
@@ -130,9 +131,9 @@ int ech_index_logits_causal(const void* q, const float* w, const void* kcache, i
  * For each row r (its first row_len[r] scores), idx[r*k + j] lists the tokens
  * t whose (score, -t) is among the k largest, in ascending t, padded with -1
  * when row_len[r] < k; ties go to the lower token index. kth[r] is the
- * smallest selected score (NaN for an empty row). ECHO explainer: ECHO
- * "guarantees an exact top-k"; the selection is found with 256 bins over the
- * top 8 bits of each score shifted by the predicted threshold ("Prefill:
+ * smallest selected score (NaN for an empty row). The selection is exact, as
+ * the ECHO explainer's opening summary requires; it is found with 256 bins over
+ * the high byte of each score minus the predicted threshold ("Prefill:
  * one-round histogram"), then the boundary bin is resolved exactly.
  *
  *  theta_in  [R] fp32 or NULL: predicted threshold per row; NaN or NULL means
@@ -170,8 +171,12 @@ int ech_cache_reset(int32_t* tok2slot, int64_t P, int32_t* slot2tok, int32_t* sl
  *   slot2tok [C]        token held by slot s, or -1
  *   slot_pin [C]        epoch stamp; slot s is pinned in a phase iff it equals
  *                       that phase's epoch (no clearing pass)
- *   miss     [M_max,2]  (g, slot) pairs allocated by the last phase, in
- *                       allocation order; consumed by ech_recall
+ *   miss     [M_max,2]  (g, slot) pairs allocated by the phase, in
+ *                       allocation order; consumed by ech_recall. EARLY
+ *                       phases should get their own buffer (count in
+ *                       ctr[ECH_CTR_NMISS_EARLY]) so that a FINAL phase can
+ *                       update the maps while the early rows are still being
+ *                       copied; FINAL/PREFILL counts go to ctr[ECH_CTR_NMISS].
  *   ctr      [ECH_CTR_LEN] ring head, epoch, counts, status (ECH_CTR_*)
  *
  * Free is lazy: unselected resident tokens keep their slot until it is reused.
@@ -212,15 +217,19 @@ int ech_cache_step(int phase, int32_t* tok2slot, int64_t P, int32_t* slot2tok, i
 /*
  * ech_recall - copy missed KV rows host -> device (ECHO explainer, "One layer,
  * one step: free -> allocate -> recall"; the host pool holds every row).
- * For m < ctr[ECH_CTR_NMISS]: dev_cache[miss[2m+1]] = host_pool[miss[2m]],
- * row_bytes each, read directly over PCIe by a gather kernel (zero-copy).
+ * For m < n: dev_cache[miss[2m+1]] = host_pool[miss[2m]], row_bytes each,
+ * where n = ctr[ECH_CTR_NMISS_EARLY] for phase ECH_EARLY and ctr[ECH_CTR_NMISS]
+ * otherwise; `miss` is the list that phase wrote. Rows are read directly over
+ * PCIe by a gather kernel (zero-copy). A FINAL recall must be ordered after
+ * the EARLY recall of the same step (it may reuse a slot the EARLY phase
+ * filled).
  *  host_pool  [P, row_bytes] pinned host memory (hipHostMalloc / torch
  *             pin_memory), host pointer; ECH_EINVAL if it is not device-mapped.
  *  dev_cache  [C, row_bytes] device memory.
  *  row_bytes  multiple of 16 (1152 for 576 bf16 values); both buffers 16-byte
  *             aligned. Adds the rows copied to ctr[ECH_CTR_RECALLED].
  */
-int ech_recall(const void* host_pool, int64_t P, int64_t row_bytes, void* dev_cache, int32_t C,
+int ech_recall(int phase, const void* host_pool, int64_t P, int64_t row_bytes, void* dev_cache, int32_t C,
                const int32_t* miss, int32_t* ctr, int32_t M_max, void* stream);
 
 #ifdef __cplusplus

@@ -17,7 +17,7 @@ import torch
 from . import _native
 from ._native import (ECH_EARLY, ECH_FINAL, ECH_PREFILL, ECH_KEY_BF16, ECH_KEY_FP8,  # noqa: F401
                       CTR_HEAD, CTR_EPOCH, CTR_NMISS, CTR_NEVICT, CTR_RECALLED, CTR_STATUS, CTR_NWANT,
-                      CTR_NPINNED, CTR_LEN, ST_OVERFLOW, ST_BADTOK, ST_BADMISS)
+                      CTR_NPINNED, CTR_NMISS_EARLY, CTR_LEN, ST_OVERFLOW, ST_BADTOK, ST_BADMISS)
 
 __all__ = ['ech_index_logits', 'ech_index_logits_causal', 'ech_topk', 'ech_topk_ws_bytes', 'ech_cache_reset',
            'ech_cache_step', 'ech_cache_step_ws_bytes', 'ech_recall', 'EchError', 'LayerState', 'lib']
@@ -96,12 +96,16 @@ def ech_topk(logits, row_len, max_len: int, k: int, theta_in, theta_out, idx, kt
 # ------------------------------------------------------------------ stage 3
 @dataclasses.dataclass
 class LayerState:
-    """The five fixed-size int32 tensors of one layer's slot map, on the device."""
+    """The fixed-size int32 tensors of one layer's slot map, on the device:
+    the two maps, the epoch pins, the miss list (FINAL/PREFILL; EARLY phases
+    write their own list so their rows can still be in flight while FINAL
+    updates the maps) and the control counters."""
     tok2slot: torch.Tensor   # [P]
     slot2tok: torch.Tensor   # [C]
     slot_pin: torch.Tensor   # [C]
     miss: torch.Tensor       # [M_max, 2]
     ctr: torch.Tensor        # [CTR_LEN]
+    miss_early: Optional[torch.Tensor] = None   # [M_early, 2]
 
     @property
     def P(self) -> int:
@@ -115,11 +119,16 @@ class LayerState:
     def M_max(self) -> int:
         return self.miss.shape[0]
 
+    def miss_list(self, phase: int) -> torch.Tensor:
+        return self.miss_early if phase == ECH_EARLY else self.miss
+
     @staticmethod
-    def allocate(P: int, C: int, M_max: int, device='cuda') -> 'LayerState':
+    def allocate(P: int, C: int, M_max: int, device='cuda', M_early: Optional[int] = None) -> 'LayerState':
         i32 = dict(dtype=torch.int32, device=device)
+        M_early = M_max if M_early is None else M_early
         st = LayerState(torch.empty(P, **i32), torch.empty(C, **i32), torch.empty(C, **i32),
-                        torch.empty((max(M_max, 1), 2), **i32), torch.empty(CTR_LEN, **i32))
+                        torch.empty((max(M_max, 1), 2), **i32), torch.empty(CTR_LEN, **i32),
+                        torch.empty((max(M_early, 1), 2), **i32))
         return st
 
 
@@ -140,17 +149,20 @@ def ech_cache_step(phase: int, state: LayerState, seq_tok0, seq_len, max_len: in
     B = seq_tok0.shape[0]
     R = idx.shape[0] if idx is not None else B
     ld = logits.stride(0) if logits is not None else 0
+    miss = state.miss_list(phase)
     _check('ech_cache_step', lib().ech_cache_step(
         phase, _ptr(state.tok2slot), state.P, _ptr(state.slot2tok), _ptr(state.slot_pin), state.C,
-        _ptr(state.miss), state.M_max, _ptr(state.ctr), _ptr(seq_tok0), _ptr(seq_len), B, int(max_len),
+        _ptr(miss), miss.shape[0], _ptr(state.ctr), _ptr(seq_tok0), _ptr(seq_len), B, int(max_len),
         _ptr(idx), R, int(k), _ptr(logits), ld, _ptr(theta), int(cap), _ptr(sel_slot), _ptr(stats), _ptr(ws),
         ws.numel() * ws.element_size(), _stream(stream)))
 
 
-def ech_recall(host_pool, dev_cache, state: LayerState, stream=None) -> None:
-    """Copy the last phase's missed rows: host_pool [P, row_bytes] pinned
-    (uint8/uint16), dev_cache [C, row_bytes] on the device."""
+def ech_recall(host_pool, dev_cache, state: LayerState, phase: int = ECH_FINAL, stream=None) -> None:
+    """Copy the rows missed by the last phase of this kind: host_pool
+    [P, row_bytes] pinned (uint8/uint16), dev_cache [C, row_bytes] on the
+    device."""
     row_bytes = host_pool.shape[1] * host_pool.element_size()
+    miss = state.miss_list(phase)
     _check('ech_recall', lib().ech_recall(
-        _ptr(host_pool), host_pool.shape[0], row_bytes, _ptr(dev_cache), dev_cache.shape[0], _ptr(state.miss),
-        _ptr(state.ctr), state.M_max, _stream(stream)))
+        phase, _ptr(host_pool), host_pool.shape[0], row_bytes, _ptr(dev_cache), dev_cache.shape[0], _ptr(miss),
+        _ptr(state.ctr), miss.shape[0], _stream(stream)))

@@ -268,9 +268,13 @@ __global__ __launch_bounds__(kT) void count_free_kernel(const int32_t* __restric
 }
 
 // ------------------------------------------------------------------ scan
+constexpr int kStage = 4096;   // block counts staged in LDS by the scan kernel
+
 __global__ __launch_bounds__(kST) void scan_kernel(int phase, int B, int cap, int32_t C, int32_t* ctr,
                                                    int32_t* __restrict__ stats, CWs w) {
   __shared__ int scr[kST / 64];
+  __shared__ int s_want[kStage];
+  __shared__ int s_hit[kStage];
   __shared__ int s_base;
   // free slots: exclusive scan over slot blocks (chunks of kST)
   int nfree_tot = 0;
@@ -282,14 +286,25 @@ __global__ __launch_bounds__(kST) void scan_kernel(int phase, int B, int cap, in
     if (i < w.ns) w.soff[i] = nfree_tot + ex;
     nfree_tot += tot;
   }
-  // misses: thread b sums its sequence's blocks
+  // misses: stage the block counts in LDS (coalesced), then thread b sums
+  // its sequence's blocks
   const int nseq = (phase == ECH_PREFILL) ? 1 : B;
+  const bool staged = w.ne <= kStage;
+  if (staged) {
+    for (int i = threadIdx.x; i < w.ne; i += kST) {
+      s_want[i] = w.want[i];
+      s_hit[i] = w.hit[i];
+    }
+  }
+  __syncthreads();
+  const int* want = staged ? s_want : w.want;
+  const int* hit = staged ? s_hit : w.hit;
   const int b = threadIdx.x;
   int want_b = 0, hit_b = 0;
   if (b < nseq) {
     for (int c = 0; c < w.nbr; ++c) {
-      want_b += w.want[b * w.nbr + c];
-      hit_b += w.hit[b * w.nbr + c];
+      want_b += want[b * w.nbr + c];
+      hit_b += hit[b * w.nbr + c];
     }
   }
   const int take_b = (phase == ECH_EARLY) ? min(cap, want_b) : want_b;
@@ -303,7 +318,7 @@ __global__ __launch_bounds__(kST) void scan_kernel(int phase, int B, int cap, in
     for (int c = 0; c < w.nbr; ++c) {
       w.off[b * w.nbr + c] = run;
       w.lim[b * w.nbr + c] = row_off + take_b;
-      run += w.want[b * w.nbr + c];
+      run += want[b * w.nbr + c];
     }
     const int fetched = max(0, min(n_alloc - row_off, take_b));
     int32_t* s = stats + 4 * b;
@@ -323,7 +338,7 @@ __global__ __launch_bounds__(kST) void scan_kernel(int phase, int B, int cap, in
     w.sc[S_NALLOC] = n_alloc;
     w.sc[S_HEAD] = ctr[ECH_CTR_HEAD];
     w.sc[S_NFREE] = nfree_tot;
-    ctr[ECH_CTR_NMISS] = n_alloc;
+    ctr[phase == ECH_EARLY ? ECH_CTR_NMISS_EARLY : ECH_CTR_NMISS] = n_alloc;
     ctr[ECH_CTR_NWANT] = n_want;
     ctr[ECH_CTR_NPINNED] = C - nfree_tot;
     ctr[ECH_CTR_NEVICT] = 0;
@@ -526,8 +541,9 @@ typedef uint32_t v4u __attribute__((ext_vector_type(4)));
 
 __global__ __launch_bounds__(kT) void recall_kernel(const v4u* __restrict__ host, int64_t P, int row16,
                                                     v4u* __restrict__ dev, int32_t C,
-                                                    const int32_t* __restrict__ miss, int32_t* ctr, int32_t M_max) {
-  const int n = min(ctr[ECH_CTR_NMISS], M_max);
+                                                    const int32_t* __restrict__ miss, int32_t* ctr, int cidx,
+                                                    int32_t M_max) {
+  const int n = min(ctr[cidx], M_max);
   const int64_t total = (int64_t)n * row16;
   const int64_t stride = (int64_t)gridDim.x * kT * kRecallUnroll;
   for (int64_t base = (int64_t)blockIdx.x * kT * kRecallUnroll + threadIdx.x; base < total; base += stride) {
@@ -652,8 +668,9 @@ extern "C" int ech_cache_step(int phase, int32_t* tok2slot, int64_t P, int32_t* 
   return ECH_OK;
 }
 
-extern "C" int ech_recall(const void* host_pool, int64_t P, int64_t row_bytes, void* dev_cache, int32_t C,
-                          const int32_t* miss, int32_t* ctr, int32_t M_max, void* stream) {
+extern "C" int ech_recall(int phase, const void* host_pool, int64_t P, int64_t row_bytes, void* dev_cache,
+                          int32_t C, const int32_t* miss, int32_t* ctr, int32_t M_max, void* stream) {
+  if (phase != ECH_EARLY && phase != ECH_FINAL && phase != ECH_PREFILL) return ECH_EINVAL;
   if (!host_pool || !dev_cache || !miss || !ctr || P < 1 || C < 1 || M_max < 0) return ECH_EINVAL;
   if (row_bytes <= 0 || row_bytes % 16 != 0 || row_bytes / 16 > INT32_MAX) return ECH_EINVAL;
   if ((reinterpret_cast<uintptr_t>(host_pool) & 15u) || (reinterpret_cast<uintptr_t>(dev_cache) & 15u))
@@ -673,7 +690,8 @@ extern "C" int ech_recall(const void* host_pool, int64_t P, int64_t row_bytes, v
   const int blocks = (int)std::max<int64_t>(1, std::min<int64_t>(kRecallBlocks, (work + kT * kRecallUnroll - 1) /
                                                                                     (kT * kRecallUnroll)));
   hipLaunchKernelGGL(recall_kernel, dim3(blocks), dim3(kT), 0, s, static_cast<const v4u*>(dptr), P, row16,
-                     static_cast<v4u*>(dev_cache), C, miss, ctr, M_max);
+                     static_cast<v4u*>(dev_cache), C, miss, ctr,
+                     phase == ECH_EARLY ? ECH_CTR_NMISS_EARLY : ECH_CTR_NMISS, M_max);
   ECH_LAUNCH_CHECK();
   return ECH_OK;
 }

@@ -145,19 +145,28 @@ __device__ __forceinline__ void load_query(const uint16_t* __restrict__ qrow, co
 }
 
 // ------------------------------------------------------------------ decode
-// grid (ceil(max_len / (kWaves*tpw*16)), R). Each wave walks tpw tiles of 16
-// tokens, the WG's waves interleaved so they stream adjacent 2-4 KiB pieces.
-template <int KDT>
+// grid (ceil(max_len / (kWaves*TPW*16)), R). Each wave handles TPW tiles of 16
+// tokens; the WG's waves interleave tiles so they stream adjacent 2-4 KiB
+// pieces. The tile loop is fully unrolled (TPW is a template parameter):
+// in straight-line code the compiler counts the outstanding loads exactly and
+// keeps three tiles in flight while one is multiplied, which it does not do
+// across a loop back-edge.
+template <int KDT, int TPW>
 __global__ __launch_bounds__(kThreads) void logits_decode_kernel(
     const uint16_t* __restrict__ q, const float* __restrict__ w, const uint8_t* __restrict__ kc,
     const float* __restrict__ ksc, const int64_t* __restrict__ tok0, const int32_t* __restrict__ lens,
-    float* __restrict__ out, int64_t ld, int tpw) {
+    float* __restrict__ out, int64_t ld) {
   constexpr int kRowB = (KDT == ECH_KEY_FP8) ? kD : 2 * kD;
+  constexpr int kDepth = 3;   // tiles in flight ahead of the one being multiplied
   const int r = blockIdx.y;
   const int len = lens[r];
-  const int wg_t0 = blockIdx.x * (kWaves * tpw * 16);
+  const int wg_t0 = blockIdx.x * (kWaves * TPW * 16);
   if (wg_t0 >= len) return;
   __shared__ uint4 qs[kH * kD * 2 / 16];
+  // The WG's scores are buffered here and written once at the end as full
+  // coalesced lines: per-tile 64-byte stores interleaved with the key stream
+  // cost ~15% of the bandwidth.
+  __shared__ float sbuf[kWaves * TPW * 16];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int col = lane & 15, grp = lane >> 4;
   bf16x8_t a[4][4];
@@ -168,42 +177,64 @@ __global__ __launch_bounds__(kThreads) void logits_decode_kernel(
   const uint8_t* kbase = kc + (size_t)g0 * kRowB;
   const float* sbase = (KDT == ECH_KEY_FP8) ? ksc + g0 : nullptr;
   float* orow = out + (size_t)r * ld;
-
-  // This wave's tiles start at wg_t0 + (it * kWaves + wave) * 16.
+  // This wave's tiles start at wg_t0 + (it * kWaves + wave) * 16. Tokens past
+  // the row end are clamped to len - 1 so loads stay inside the row; their
+  // scores are never written out.
   const int first = wg_t0 + wave * 16;
-  if (first >= len) return;
-  const int n_it = min(tpw, (len - first + kWaves * 16 - 1) / (kWaves * 16));
 
-  auto load = [&](KeyFrag<KDT>& f, float& sc, int it) {
+  KeyFrag<KDT> f[kDepth + 1];
+  float sc[kDepth + 1];
+  auto load = [&](int buf, int it) {
     const int tc = min(first + it * kWaves * 16 + col, len - 1);
-    load_key<KDT>(f, kbase + (size_t)tc * kRowB, grp);
-    sc = (KDT == ECH_KEY_FP8) ? sbase[tc] : 1.f;
+    load_key<KDT>(f[buf], kbase + (size_t)tc * kRowB, grp);
+    sc[buf] = (KDT == ECH_KEY_FP8) ? sbase[tc] : 1.f;
   };
-  auto proc = [&](const KeyFrag<KDT>& f, float sc, int it) {
+#pragma unroll
+  for (int it = 0; it < kDepth && it < TPW; ++it) load(it, it);
+#pragma unroll
+  for (int it = 0; it < TPW; ++it) {
+    if (it + kDepth < TPW) load((it + kDepth) % (kDepth + 1), it + kDepth);
+    // Keep the prefetch where it is: without this the scheduler sinks the
+    // loads towards their use and the tiles in flight drop to about one.
+    __builtin_amdgcn_sched_barrier(0);
+    const int buf = it % (kDepth + 1);
     bf16x8_t b[4];
 #pragma unroll
-    for (int s = 0; s < 4; ++s) b[s] = key_step<KDT>(f, s);
-    const float v = tile_score(a, wv, b, sc);
-    const int t = first + it * kWaves * 16 + col;
-    if (grp == 0 && t < len) orow[t] = v;
-  };
-  // Four register buffers: three tiles stay in flight while one is multiplied.
-  KeyFrag<KDT> f0, f1, f2, f3;
-  float s0 = 1.f, s1 = 1.f, s2 = 1.f, s3 = 1.f;
-  load(f0, s0, 0);
-  if (n_it > 1) load(f1, s1, 1);
-  if (n_it > 2) load(f2, s2, 2);
-#pragma unroll 1
-  for (int it = 0; it < n_it; it += 4) {
-    if (it + 3 < n_it) load(f3, s3, it + 3);
-    proc(f0, s0, it);
-    if (it + 4 < n_it) load(f0, s0, it + 4);
-    if (it + 1 < n_it) proc(f1, s1, it + 1);
-    if (it + 5 < n_it) load(f1, s1, it + 5);
-    if (it + 2 < n_it) proc(f2, s2, it + 2);
-    if (it + 6 < n_it) load(f2, s2, it + 6);
-    if (it + 3 < n_it) proc(f3, s3, it + 3);
+    for (int s = 0; s < 4; ++s) b[s] = key_step<KDT>(f[buf], s);
+    const float v = tile_score(a, wv, b, sc[buf]);
+    sbuf[(it * kWaves + wave) * 16 + col] = v;   // the 4 lane groups hold the same sum
   }
+  __syncthreads();
+  const int n = min(kWaves * TPW * 16, len - wg_t0);
+  float* dst = orow + wg_t0;
+  if ((ld & 3) == 0) {   // rows 16-byte aligned: float4 stores
+    for (int i = 4 * threadIdx.x; i < n; i += 4 * kThreads) {
+      if (i + 3 < n) {
+        *reinterpret_cast<float4*>(dst + i) = *reinterpret_cast<const float4*>(sbuf + i);
+      } else {
+        for (int j = i; j < n; ++j) dst[j] = sbuf[j];
+      }
+    }
+  } else {
+    for (int i = threadIdx.x; i < n; i += kThreads) dst[i] = sbuf[i];
+  }
+}
+
+template <int KDT>
+hipError_t launch_decode(int tpw, dim3 grid, hipStream_t s, const uint16_t* q, const float* w, const uint8_t* kc,
+                         const float* ksc, const int64_t* tok0, const int32_t* lens, float* out, int64_t ld) {
+  switch (tpw) {
+#define ECH_DEC(T)                                                                                          \
+  case T:                                                                                                   \
+    hipLaunchKernelGGL((logits_decode_kernel<KDT, T>), grid, dim3(kThreads), 0, s, q, w, kc, ksc, tok0, lens, \
+                       out, ld);                                                                            \
+    break;
+    ECH_DEC(1) ECH_DEC(2) ECH_DEC(4) ECH_DEC(8) ECH_DEC(16) ECH_DEC(32)
+#undef ECH_DEC
+    default:
+      return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
 }
 
 // ------------------------------------------------------------------ causal prefill
@@ -345,19 +376,19 @@ extern "C" int ech_index_logits(const void* q, const float* w, const void* kcach
   // Enough WGs to fill 256 CUs; long rows give each wave up to 32 tiles so the
   // per-WG query staging (16 KiB) stays small next to the key stream.
   const int64_t total = (int64_t)R * max_len;
-  int tpw = (int)std::min<int64_t>(32, std::max<int64_t>(1, total / (2048 * kWaves * 16)));
+  // Enough WGs to fill 256 CUs several times over; long rows give each wave up
+  // to 32 tiles so the per-WG query staging (16 KiB) stays small next to the
+  // key stream. Tiles per wave is a power of two (one kernel per value).
+  int tpw = 1;
+  while (tpw < 32 && total / ((int64_t)2048 * kWaves * 16 * (tpw * 2)) >= 1) tpw *= 2;
   const int per_wg = kWaves * tpw * 16;
   dim3 grid((max_len + per_wg - 1) / per_wg, R);
   const uint16_t* qq = static_cast<const uint16_t*>(q);
   const uint8_t* kk = static_cast<const uint8_t*>(kcache);
-  if (kdtype == ECH_KEY_FP8)
-    hipLaunchKernelGGL(logits_decode_kernel<ECH_KEY_FP8>, grid, dim3(kThreads), 0, s, qq, w, kk, kscale,
-                       row_tok0, row_len, logits, ld, tpw);
-  else
-    hipLaunchKernelGGL(logits_decode_kernel<ECH_KEY_BF16>, grid, dim3(kThreads), 0, s, qq, w, kk, kscale,
-                       row_tok0, row_len, logits, ld, tpw);
-  ECH_LAUNCH_CHECK();
-  return ECH_OK;
+  const hipError_t e = (kdtype == ECH_KEY_FP8)
+                           ? launch_decode<ECH_KEY_FP8>(tpw, grid, s, qq, w, kk, kscale, row_tok0, row_len, logits, ld)
+                           : launch_decode<ECH_KEY_BF16>(tpw, grid, s, qq, w, kk, kscale, row_tok0, row_len, logits, ld);
+  return e == hipSuccess ? ECH_OK : ECH_EHIP;
 }
 
 extern "C" int ech_index_logits_causal(const void* q, const float* w, const void* kcache, int kdtype,

@@ -1,14 +1,14 @@
 // Exact top-k per score row on gfx950.
 //
-// ECHO explainer, "Prefill: one-round histogram": 256 bins over the top 8
-// bits of each score shifted by the predicted threshold theta; ECHO
-// "guarantees an exact top-k". The k-th element (s*, t*) of the order
+// ECHO explainer, "Prefill: one-round histogram": a single 256-bin histogram
+// pass keyed by the high byte of the score minus the predicted threshold
+// theta; the selection must be exact (the explainer's opening summary). The k-th element (s*, t*) of the order
 // (score descending, token ascending) defines the set exactly:
 //     t selected  <=>  s_t > s*  or  (s_t == s* and t among the first
 //                      need_eq tokens with score s*)
 // so the kernels find s* and need_eq, then compact in ascending t.
 //
-//   T1 hist     grid (chunks, R): LDS histogram of bin(t) = top 8 bits of
+//   T1 hist     grid (chunks, R): LDS histogram of bin(t) = high byte of
 //               ord(fl32(s_t - theta)) per 4096-token chunk. fl32(s - theta)
 //               is monotone in s and ord() is order preserving, so higher bins
 //               hold strictly larger scores.
@@ -95,9 +95,30 @@ size_t layout(int R, int max_len, Ws* w, char* base) {
   return o;
 }
 
-__device__ __forceinline__ uint32_t shifted_bin(float x, float th) {
-  const float d = (th == th) ? (x - th) : x;   // NaN theta: unshifted
-  return ech::ord_key(d) >> 24;
+// Binning of a score relative to the prediction theta. Scores more than
+// |theta|/4 below theta all share bin 0: only the bins around and above the
+// boundary are needed, and lumping the bulk lets the histogram skip the
+// per-bin work for most tokens. Bin 0 is the lowest bin (a real bin 0 needs
+// |s - theta| >= 2^126, which is below the cut anyway), so the binning stays
+// monotone in s. A NaN theta means no shift and no lumping.
+struct Shift {
+  float th, cut;
+  bool on;
+};
+
+__device__ __forceinline__ Shift make_shift(float th) {
+  Shift sh;
+  sh.on = th == th;
+  sh.th = th;
+  const float a = fabsf(th);
+  sh.cut = (sh.on && a > 0.f && a < __builtin_inff()) ? -0.25f * a : -__builtin_inff();
+  return sh;
+}
+
+__device__ __forceinline__ uint32_t shifted_bin(float x, const Shift& sh) {
+  if (!sh.on) return ech::ord_key(x) >> 24;
+  const float d = x - sh.th;
+  return d < sh.cut ? 0u : ech::ord_key(d) >> 24;
 }
 
 __device__ __forceinline__ float row_theta(const float* th, int r) {
@@ -134,16 +155,26 @@ __global__ __launch_bounds__(kT) void topk_hist_kernel(const float* __restrict__
   const int hi = min(lo + kChunk, len);
   __shared__ int h[256];
   h[threadIdx.x] = 0;
-  const float th = row_theta(theta, r);
+  const Shift sh = make_shift(row_theta(theta, r));
   float4 v[kVec];
   load_chunk(logits + (size_t)r * ld, lo, hi, v);
   __syncthreads();
+  int lumped = 0;
 #pragma unroll
   for (int j = 0; j < kVec; ++j) {
     const int t = lo + 4 * (j * kT + (int)threadIdx.x);
 #pragma unroll
-    for (int e = 0; e < 4; ++e) ech::lds_hist_add(h, shifted_bin(f4(v[j], e), th), t + e < hi);
+    for (int e = 0; e < 4; ++e) {
+      const float x = f4(v[j], e);
+      const bool ok = t + e < hi;
+      const float d = sh.on ? x - sh.th : x;
+      const bool lump = ok && d < sh.cut;
+      lumped += lump;
+      ech::lds_hist_add(h, ech::ord_key(d) >> 24, ok && !lump);
+    }
   }
+  lumped = ech::wave_sum(lumped);
+  if (ech::lane_id() == 0 && lumped) atomicAdd(&h[0], lumped);
   __syncthreads();
   ws.hist[((size_t)r * ws.nch + c) * 256 + threadIdx.x] = h[threadIdx.x];
 }
@@ -188,7 +219,7 @@ __global__ __launch_bounds__(kT) void topk_gather_kernel(const float* __restrict
   const RowState st = ws.rs[r];
   if (st.mode != kNormal || lo >= len) return;
   const int hi = min(lo + kChunk, len);
-  const float th = row_theta(theta, r);
+  const Shift sh = make_shift(row_theta(theta, r));
   const uint32_t bstar = (uint32_t)st.bstar;
   float4 v[kVec];
   load_chunk(logits + (size_t)r * ld, lo, hi, v);
@@ -205,7 +236,7 @@ __global__ __launch_bounds__(kT) void topk_gather_kernel(const float* __restrict
       const int t = t0 + e;
       const bool ok = t < hi;
       const float x = f4(v[j], e);
-      const uint32_t b = shifted_bin(x, th);
+      const uint32_t b = shifted_bin(x, sh);
       above += (ok && b > bstar) ? 1 : 0;
       const bool is_c = ok && b == bstar;
       const uint64_t m = __ballot(is_c);
@@ -309,7 +340,7 @@ __global__ __launch_bounds__(kRT) void topk_resolve_kernel(const float* __restri
     int need = st.need;
     uint32_t prefix = 0, mask = 0;
     const bool in_lds = cnt <= ws.cap;
-    const float th = th_in;
+    const Shift shf = make_shift(th_in);
     const uint32_t bstar = (uint32_t)st.bstar;
     if (in_lds) {
       const int2* src = ws.cand + (size_t)r * ws.cap;
@@ -340,7 +371,7 @@ __global__ __launch_bounds__(kRT) void topk_resolve_kernel(const float* __restri
           if (t < len) {
             const float x = row[t];
             key = ech::ord_key(x);
-            act = shifted_bin(x, th) == bstar && (key & mask) == prefix;
+            act = shifted_bin(x, shf) == bstar && (key & mask) == prefix;
           }
           ech::lds_hist_add(hist, (key >> shift) & 255u, act);
         }

@@ -4,8 +4,8 @@ Decode step (ECHO explainer, "The top-k dependency" and "Decode: fetch above
 a predicted threshold"): the recall of a step depends on its top-k; the early
 fetch of tokens scoring above the predicted threshold overlaps the top-k.
 
-    S0: ech_index_logits ------------------> ech_topk(theta -> theta')
-         \\-> S1: EARLY(theta) + recall --/ (join) FINAL + recall
+    S0: ech_index_logits --------------> ech_topk(theta -> theta') -> FINAL maps -> FINAL recall
+         \\-> S1: EARLY(theta) maps --/  EARLY recall (PCIe) -----------------/
 
 theta is double-buffered (EARLY reads the prediction while the top-k writes
 its update). When the batch's selections do not fit the cache at once (sum of
@@ -69,7 +69,7 @@ class DecodeLayer:
         self.tok0 = torch.from_numpy(self.tok0_np).to(**dev)
         self.lens = torch.from_numpy(self.lens_np).to(**dev)
         self.ld = round_up(max(self.max_len, 4), 64)
-        self.logits = torch.empty((self.B, self.ld), dtype=torch.float32, **dev)
+        self.logits = torch.zeros((self.B, self.ld), dtype=torch.float32, **dev)
         self.idx = torch.empty((self.B, k), dtype=torch.int32, **dev)
         self.kth = torch.empty(self.B, dtype=torch.float32, **dev)
         self.theta = [torch.full((self.B,), float('nan'), dtype=torch.float32, **dev) for _ in range(2)]
@@ -93,6 +93,7 @@ class DecodeLayer:
             self.dev_cache = None
         self.s1 = torch.cuda.Stream(device=device)
         self.ev_logits = torch.cuda.Event()
+        self.ev_early_maps = torch.cuda.Event()
         self.ev_early = torch.cuda.Event()
         ech_cache_reset(self.state)
 
@@ -102,15 +103,21 @@ class DecodeLayer:
             t.fill_(float('nan'))
         self.parity = 0
 
-    def _phase(self, phase: int, b0: int, b1: int, theta: torch.Tensor, stream) -> None:
+    def _maps(self, phase: int, b0: int, b1: int, theta: torch.Tensor, stream) -> None:
         stats = self.stats_early if phase == ECH_EARLY else self.stats_final
         ech_cache_step(phase, self.state, self.tok0[b0:b1], self.lens[b0:b1], self.max_len,
                        idx=self.idx[b0:b1] if phase == ECH_FINAL else None, k=self.k,
                        logits=self.logits[b0:b1], theta=theta[b0:b1], cap=self.cap,
                        sel_slot=self.sel_slot[b0:b1] if phase == ECH_FINAL else None, stats=stats[b0:b1],
                        ws=self.ws_early if phase == ECH_EARLY else self.ws_final, stream=stream)
+
+    def _recall(self, phase: int, stream) -> None:
         if self.host_pool is not None:
-            ech_recall(self.host_pool, self.dev_cache, self.state, stream=stream)
+            ech_recall(self.host_pool, self.dev_cache, self.state, phase=phase, stream=stream)
+
+    def _phase(self, phase: int, b0: int, b1: int, theta: torch.Tensor, stream) -> None:
+        self._maps(phase, b0, b1, theta, stream)
+        self._recall(phase, stream)
 
     def logits_only(self, q: torch.Tensor, stream=None) -> None:
         ech_index_logits(q, self.w, self.kcache, self.kscale, self.tok0, self.lens, self.max_len, self.logits,
@@ -137,20 +144,29 @@ class DecodeLayer:
         mark('logits', s0)
         first_b0, first_b1 = self.chunks[0]
         if self.early:
+            # S1: EARLY maps, then its rows cross PCIe while S0 carries on.
             self.ev_logits.record(s0)
             self.s1.wait_event(self.ev_logits)
             mark('early', self.s1)
-            self._phase(ECH_EARLY, first_b0, first_b1, th, self.s1)
+            self._maps(ECH_EARLY, first_b0, first_b1, th, self.s1)
+            self.ev_early_maps.record(self.s1)
+            self._recall(ECH_EARLY, self.s1)
             mark('early', self.s1)
             self.ev_early.record(self.s1)
+        # The top-k is off the critical path (logits -> EARLY maps -> EARLY
+        # recall over PCIe -> FINAL recall); started after the EARLY maps it
+        # overlaps the PCIe transfer instead of competing with the maps.
+        if self.early:
+            s0.wait_event(self.ev_early_maps)      # FINAL also updates the maps EARLY left
         mark('topk', s0)
         ech_topk(self.logits, self.lens, self.max_len, self.k, th, th_next, self.idx, self.kth, self.ws_topk,
                  stream=s0)
         mark('topk', s0)
-        if self.early:
-            s0.wait_event(self.ev_early)
         mark('final', s0)
-        self._phase(ECH_FINAL, first_b0, first_b1, th, s0)
+        self._maps(ECH_FINAL, first_b0, first_b1, th, s0)
+        if self.early:
+            s0.wait_event(self.ev_early)           # ... but may reuse a slot EARLY is still filling
+        self._recall(ECH_FINAL, s0)
         for b0, b1 in self.chunks[1:]:
             if self.early:
                 self._phase(ECH_EARLY, b0, b1, th, s0)
@@ -161,6 +177,25 @@ class DecodeLayer:
     @property
     def theta_current(self) -> torch.Tensor:
         return self.theta[self.parity]
+
+    def capture(self) -> None:
+        """Capture one decode step per threshold parity as a hipGraph that
+        reads q from a static buffer (every tensor of the step has a fixed
+        size and address, so the step replays unchanged). Nothing runs."""
+        self.q_static = torch.zeros((self.B, 64, 128), dtype=torch.int16, device=self.logits.device)
+        self.graphs = [None, None]
+        for _ in range(2):
+            p = self.parity
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                self.step(self.q_static)      # flips self.parity
+            self.graphs[p] = g
+
+    def replay(self, q: torch.Tensor) -> None:
+        """One decode step through the captured graphs (on the current stream)."""
+        self.q_static.copy_(q, non_blocking=True)
+        self.graphs[self.parity].replay()
+        self.parity ^= 1
 
 
 class PrefillLayer:
@@ -236,7 +271,7 @@ class PrefillLayer:
                        sel_slot=self.sel_slot[:R], stats=self.stats, ws=self.ws_cache, stream=s0)
         if self.host_pool is not None:
             self.s1.wait_stream(s0)
-            ech_recall(self.host_pool, self.dev_cache, self.state, stream=self.s1)
+            ech_recall(self.host_pool, self.dev_cache, self.state, phase=ECH_PREFILL, stream=self.s1)
             self.ev_recall.record(self.s1)
         else:
             self.ev_recall.record(s0)

@@ -1,7 +1,7 @@
 """Exact top-k over one row of scores, and the EMA threshold.
 
-Top-k (ECHO explainer: ECHO "guarantees an exact top-k"; k = 2048 in
-"Decode: fetch above a predicted threshold"). The result has a plain
+Top-k (ECHO explainer: the selection is exact, per its opening summary;
+k = 2048 in "Decode: fetch above a predicted threshold"). The result has a plain
 definition, so the oracle is that definition: sort the row's scores in
 descending order with a stable sort (equal scores keep ascending token order,
 i.e. ties go to the lower index) and keep the first min(k, len) positions.
@@ -14,7 +14,7 @@ Rows with len <= k select every visible token. Output rows are padded with -1
 up to k. An empty row selects nothing and has kth = NaN. -0.0 and +0.0 are
 equal scores (the sort compares values). Scores must be finite.
 
-The histogram on the top 8 bits of the threshold-shifted score ("Prefill:
+The 256-bin histogram of the threshold-shifted score ("Prefill:
 one-round histogram") is how a kernel finds this set fast; it does not change
 the set, so the oracle does not model it.
 

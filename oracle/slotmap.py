@@ -1,8 +1,8 @@
 """Sequential per-layer slot map: free -> allocate -> recall, no write-back.
 
 Source: ECHO explainer, "One layer, one step: free -> allocate -> recall"
-(a per-layer GPU cache because each layer's indexer picks different tokens;
-nothing is written back on eviction because the host holds every row) and
+(the cache is kept per layer, since layers select different tokens; an
+evicted row needs no copy back, the host pool keeping all rows) and
 "Five fixed-size integer tensors on the GPU" (fixed-size state, so a decode
 step is one captured graph); "Decode: fetch above a predicted threshold"
 (early fetch of tokens scoring above theta, up to a cap); "Prefill: one-round

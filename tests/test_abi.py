@@ -111,6 +111,7 @@ def test_cache_step_rejects_bad_args():
 
 def test_recall_rejects_bad_args():
     lib = ech.lib()
-    assert lib.ech_recall(FAKE, 10, 1150, FAKE, 10, FAKE, FAKE, 4, None) == -1   # row_bytes % 16
-    assert lib.ech_recall(None, 10, 1152, FAKE, 10, FAKE, FAKE, 4, None) == -1
-    assert lib.ech_recall(FAKE, 0, 1152, FAKE, 10, FAKE, FAKE, 4, None) == -1
+    assert lib.ech_recall(1, FAKE, 10, 1150, FAKE, 10, FAKE, FAKE, 4, None) == -1   # row_bytes % 16
+    assert lib.ech_recall(1, None, 10, 1152, FAKE, 10, FAKE, FAKE, 4, None) == -1
+    assert lib.ech_recall(1, FAKE, 0, 1152, FAKE, 10, FAKE, FAKE, 4, None) == -1
+    assert lib.ech_recall(9, FAKE, 10, 1152, FAKE, 10, FAKE, FAKE, 4, None) == -1   # no such phase

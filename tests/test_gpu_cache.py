@@ -27,9 +27,10 @@ class GpuCache:
             n = ech.ech_cache_step_ws_bytes(ph, B if ph != ech.ECH_PREFILL else 1, self.R, k, max_len, C, self.M_max)
             self.ws[ph] = torch.empty(n, dtype=torch.uint8, device='cuda')
 
-    def _assigned(self):
-        n = int(host(self.st.ctr)[ech.CTR_NMISS])
-        return [tuple(x) for x in host(self.st.miss)[:n].tolist()]
+    def _assigned(self, phase=ech.ECH_FINAL):
+        early = phase == ech.ECH_EARLY
+        n = int(host(self.st.ctr)[ech.CTR_NMISS_EARLY if early else ech.CTR_NMISS])
+        return [tuple(x) for x in host(self.st.miss_list(phase))[:n].tolist()]
 
     def final(self, tok0, lens, idx):
         sel = torch.empty((self.B, self.k), dtype=torch.int32, device='cuda')
@@ -46,7 +47,7 @@ class GpuCache:
                            self.max_len, k=self.k, logits=dev(scores), theta=dev(np.asarray(theta, np.float32)),
                            cap=self.cap, stats=stats, ws=self.ws[ech.ECH_EARLY])
         torch.cuda.synchronize()
-        return self._assigned(), host(stats)
+        return self._assigned(ech.ECH_EARLY), host(stats)
 
     def prefill(self, tok0, length, idx):
         sel = torch.empty(idx.shape, dtype=torch.int32, device='cuda')

@@ -1,0 +1,53 @@
+"""The decode step captured as hipGraphs (one per threshold parity, q read
+from a static buffer) replays to exactly the eager results, step after step,
+with unrelated eager work and synchronisations between the replays."""
+import numpy as np
+import pytest
+import torch
+
+import workloads as wk
+from gpu_util import dev, host, need_gpu
+from indexer_top_kv_amd.pipeline import DecodeLayer
+
+pytestmark = pytest.mark.gpu
+
+
+def _layer(wl, keys, scale, w, pool):
+    return DecodeLayer(dev(keys), dev(scale), dev(w), wl.tok0, wl.lens, wl.C, k=wl.k, cap=wl.cap, host_pool=pool)
+
+
+def _snap(layer):
+    return [host(t).copy() for t in (layer.logits, layer.idx, layer.kth, layer.theta_current, layer.sel_slot,
+                                     layer.stats_early, layer.stats_final, layer.state.tok2slot,
+                                     layer.state.slot2tok, layer.state.ctr, layer.dev_cache)]
+
+
+@pytest.mark.parametrize('variant', ['dyadic', 'normal'])
+def test_graph_replay_matches_eager(variant):
+    need_gpu()
+    wl = wk.CONFIGS['decode-32x128k-fp8'].scaled(B=3, N=7000, C=9000, k=1024, cap=200, variant=variant)
+    keys, scale = wk.keys(wl)
+    w = wk.head_weights(wl)
+    rows = wk.host_rows(wl)
+    pool = torch.empty((wl.P, 576), dtype=torch.int16, pin_memory=True)
+    pool.numpy()[:] = rows.view(np.int16)
+    qs = [dev(q) for q in wk.decode_queries(wl, 6)]
+
+    eager = _layer(wl, keys, scale, w, pool)
+    ref = []
+    for q in qs:
+        eager.step(q)
+        torch.cuda.synchronize()
+        ref.append(_snap(eager))
+
+    g = _layer(wl, keys, scale, w, pool)
+    g.capture()
+    for s, q in enumerate(qs):
+        g.replay(q)
+        torch.cuda.synchronize()
+        got = _snap(g)
+        for a, b in zip(got, ref[s]):
+            np.testing.assert_array_equal(a, b, err_msg=f'step {s}')
+        x = torch.arange(4096, device='cuda', dtype=torch.float32)   # unrelated eager work
+        assert float((x * 2).sum().item()) == 4096 * 4095
+        torch.cuda.synchronize()
