@@ -43,8 +43,11 @@ def parse():
     p.add_argument('--no-cpu-baseline', action='store_true')
     p.add_argument('--no-early', action='store_true', help='disable the early fetch (ablation)')
     p.add_argument('--eager', action='store_true', help='time eager launches instead of graph replays')
+    p.add_argument('--topk-after-early', action='store_true', help='start the top-k after the EARLY maps')
     p.add_argument('--cpu-seqs', type=int, default=4, help='sequences in the oracle sample')
     p.add_argument('--cpu-steps', type=int, default=2, help='decode steps in the oracle sample')
+    p.add_argument('--calibrate-copy', action='store_true',
+                   help='only run a plain 1 GiB device copy 5 times (reference for HBM byte counters)')
     return p.parse_args()
 
 
@@ -101,7 +104,7 @@ def bench_decode(args, wl):
     kc, ks, wd = dev(keys), (dev(scale) if scale is not None else None), dev(w)
     qd = dev(qs)
     layer = DecodeLayer(kc, ks, wd, wl.tok0, wl.lens, wl.C, k=wl.k, cap=wl.cap, host_pool=pool,
-                        early=not args.no_early)
+                        early=not args.no_early, topk_after_early=args.topk_after_early)
     torch.cuda.synchronize()
     log(f'chunks {layer.chunks}; warm-up {args.warmup} steps')
     for s in range(args.warmup):
@@ -214,9 +217,10 @@ def pcie_check(pool, C, rows=16384, reps=5):
         best = max(best, src.numel() / (a.elapsed_time(b) * 1e-3) / 1e9)
     del src, dst
     P = pool.shape[0]
+    rows = min(rows, C, P)
     rng = np.random.default_rng(7)
     g = rng.choice(P, rows, replace=False).astype(np.int32)
-    p = rng.permutation(min(C, rows)).astype(np.int32)[:rows]
+    p = rng.permutation(C).astype(np.int32)[:rows]
     st = ech.LayerState.allocate(P, C, rows)
     st.miss.copy_(torch.from_numpy(np.stack([g, p], 1)))
     ctr = np.zeros(ech.CTR_LEN, np.int32)
@@ -245,28 +249,28 @@ def cpu_baseline_decode(args, wl, ctx):
     import workloads as wk
 
     S, T = min(args.cpu_seqs, wl.B), args.cpu_steps
-    sub = wl.scaled(B=S)
-    if wl.len_lo is not None:
-        raise SystemExit('cpu sample needs equal lengths')
-    keys = ctx['keys'][:sub.P]
-    scale = None if ctx['scale'] is None else ctx['scale'][:sub.P]
+    lens, tok0 = wl.lens[:S], wl.tok0[:S]
+    P = int(tok0[-1] + lens[-1])
+    keys = ctx['keys'][:P]
+    scale = None if ctx['scale'] is None else ctx['scale'][:P]
     w = ctx['w'][:S]
     pool = ctx['pool'].numpy()
-    sm = oracle.SlotMap(sub.P, wl.C)
-    cache = np.zeros((wl.C, pool.shape[1]), pool.dtype)
+    C = min(wl.C, P)
+    sm = oracle.SlotMap(P, C)
+    cache = np.zeros((C, pool.shape[1]), pool.dtype)
     theta = np.full(S, np.nan, np.float32)
     t0 = time.perf_counter()
     for s in range(T):
         q = ctx['qs'][s][:S]
-        L = [x.astype(np.float32) for x in oracle.index_logits(q, w, keys, wl.kdtype, scale, sub.tok0, sub.lens)]
+        L = [x.astype(np.float32) for x in oracle.index_logits(q, w, keys, wl.kdtype, scale, tok0, lens)]
         idx, kth = oracle.topk_rows(L, wl.k)
-        a, _ = sm.early(sub.tok0, L, theta, wl.cap)
+        a, _ = sm.early(tok0, L, theta, wl.cap)
         oracle.recall_rows(pool, cache, a)
-        a, _, _ = sm.final(sub.tok0, idx)
+        a, _, _ = sm.final(tok0, idx)
         oracle.recall_rows(pool, cache, a)
         theta = oracle.theta_rows(theta, kth)
     dt = time.perf_counter() - t0
-    tokens = int(sub.lens.astype(np.int64).sum()) * T
+    tokens = int(lens.astype(np.int64).sum()) * T
     return {'value': tokens / dt, 'unit': 'tokens/s', 'cores': cpu_cores(), 'kind': 'oracle',
             'sample': f'first {S} of {wl.B} sequences x {T} decode steps ({tokens} tokens scored), '
                       f'{dt:.1f} s; label: CPU oracle - reported baseline',
@@ -338,6 +342,15 @@ def main():
     ech.lib()
     assert torch.cuda.is_available(), 'no GPU'
     torch.cuda.set_device(0)
+    if args.calibrate_copy:
+        src = torch.ones(1 << 30, dtype=torch.uint8, device='cuda')
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({'copy_bytes_read_per_launch': src.numel(), 'copy_bytes_written_per_launch': src.numel(),
+                          'launches': 5}), flush=True)
+        return
     wl = wk.CONFIGS[args.config]
     log(f'{wl.name} on {torch.cuda.get_device_name(0)}')
     if wl.mode == 'decode':

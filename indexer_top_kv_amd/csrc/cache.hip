@@ -536,7 +536,7 @@ __global__ void reset_kernel(int32_t* tok2slot, int64_t P, int32_t* slot2tok, in
 }
 
 constexpr int kRecallUnroll = 4;
-constexpr int kRecallBlocks = 128;
+constexpr int kRecallBlocks = 64;
 typedef uint32_t v4u __attribute__((ext_vector_type(4)));
 
 __global__ __launch_bounds__(kT) void recall_kernel(const v4u* __restrict__ host, int64_t P, int row16,

@@ -99,11 +99,8 @@ __device__ __forceinline__ bf16x8_t key_step(const KeyFrag<KDT>& f, int s) {
   }
 }
 
-// Reduce one 16-token tile: 16 MFMA, then ReLU/weights/scale and head sum.
-// Returns the score for token column (lane & 15), valid in every lane.
-__device__ __forceinline__ float tile_score(const bf16x8_t (&a)[4][4], const float (&wv)[4][4],
-                                            const bf16x8_t (&b)[4], float sc) {
-  f32x4_t acc[4];
+// One 16-token tile on the matrix cores: acc[ht][v] = q[16ht + 4grp + v] . k[col].
+__device__ __forceinline__ void tile_mfma(const bf16x8_t (&a)[4][4], const bf16x8_t (&b)[4], f32x4_t (&acc)[4]) {
 #pragma unroll
   for (int ht = 0; ht < 4; ++ht) acc[ht] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -111,6 +108,11 @@ __device__ __forceinline__ float tile_score(const bf16x8_t (&a)[4][4], const flo
 #pragma unroll
     for (int ht = 0; ht < 4; ++ht) acc[ht] = mfma(a[ht][s], b[s], acc[ht]);
   }
+}
+
+// Epilogue of a tile: ReLU (with the per-token scale's sign), head weights,
+// head sum. Returns the score of token column (lane & 15) in every lane.
+__device__ __forceinline__ float tile_epilogue(const f32x4_t (&acc)[4], const float (&wv)[4][4], float sc) {
   const float bound = sc >= 0.f ? __builtin_inff() : -__builtin_inff();
   float part = 0.f;
 #pragma unroll
@@ -121,6 +123,13 @@ __device__ __forceinline__ float tile_score(const bf16x8_t (&a)[4][4], const flo
   part += __shfl_xor(part, 16, 64);
   part += __shfl_xor(part, 32, 64);
   return part * sc;
+}
+
+__device__ __forceinline__ float tile_score(const bf16x8_t (&a)[4][4], const float (&wv)[4][4],
+                                            const bf16x8_t (&b)[4], float sc) {
+  f32x4_t acc[4];
+  tile_mfma(a, b, acc);
+  return tile_epilogue(acc, wv, sc);
 }
 
 // Load one query row [64][128] bf16 (16 KiB) into LDS, then each wave picks
@@ -240,24 +249,51 @@ hipError_t launch_decode(int tpw, dim3 grid, hipStream_t s, const uint16_t* q, c
 // ------------------------------------------------------------------ causal prefill
 // One WG = kWaves query rows (one per wave) x a span of kSpan tokens. Key
 // tiles of 64 tokens are widened to bf16 once and staged in LDS (rows padded
-// to 272 B so the 16-lane column reads hit distinct banks), double-buffered;
-// every wave multiplies its row's q against them. Row r sees t <= row0 + r.
+// to 272 B so the 16-lane column reads hit distinct banks), double-buffered,
+// with the next tile's global loads in flight during the current tile's
+// MFMAs; every wave multiplies its row's q against them. Row r sees
+// t <= row0 + r.
 constexpr int kPTile = 64;                  // tokens per LDS stage
 constexpr int kPStride = 2 * kD + 16;       // padded bf16 key row in LDS (bytes)
 constexpr int kSpan = 4096;                 // tokens per WG
 
+// Staging of one 64-token key tile, split in two so the global loads of
+// tile i+1 are in flight while tile i is multiplied: fetch() issues them into
+// registers, commit() widens fp8 to bf16 and writes the LDS tile.
+// 256 threads; thread -> token tid/4; fp8: bytes 32*(tid%4) .. +32 (-> 64 B
+// bf16); bf16: bytes 64*(tid%4) .. +64.
 template <int KDT>
-__device__ __forceinline__ void stage_keys(uint8_t* dst, float* sdst, const uint8_t* __restrict__ kbase,
-                                           const float* __restrict__ sbase, int t0, int nvalid) {
-  // 256 threads; fp8: thread -> token tid/4, bytes 32*(tid%4) .. +32 -> 64 B bf16.
-  // bf16: thread -> token tid/4, bytes 64*(tid%4) .. +64.
+struct Staged {
+  uint4 v[KDT == ECH_KEY_FP8 ? 2 : 4];
+  float sc;
+};
+
+template <int KDT>
+__device__ __forceinline__ void stage_fetch(Staged<KDT>& r, const uint8_t* __restrict__ kbase,
+                                            const float* __restrict__ sbase, int t0, int nvalid) {
   const int tid = threadIdx.x;
   const int tok = tid >> 2, part = tid & 3;
   const int tsrc = t0 + min(tok, max(nvalid - 1, 0));
-  uint8_t* d = dst + tok * kPStride;
   if constexpr (KDT == ECH_KEY_FP8) {
     const uint4* s = reinterpret_cast<const uint4*>(kbase + (size_t)tsrc * kD + 32 * part);
-    const uint4 x = s[0], y = s[1];
+    r.v[0] = s[0];
+    r.v[1] = s[1];
+    r.sc = sbase[tsrc];
+  } else {
+    const uint4* s = reinterpret_cast<const uint4*>(kbase + (size_t)tsrc * 2 * kD + 64 * part);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) r.v[i] = s[i];
+    r.sc = 1.f;
+  }
+}
+
+template <int KDT>
+__device__ __forceinline__ void stage_commit(const Staged<KDT>& r, uint8_t* dst, float* sdst) {
+  const int tid = threadIdx.x;
+  const int tok = tid >> 2, part = tid & 3;
+  uint8_t* d = dst + tok * kPStride;
+  if constexpr (KDT == ECH_KEY_FP8) {
+    const uint4 x = r.v[0], y = r.v[1];
     u32x4_t o0 = {cvt_lo(x.x), cvt_hi(x.x), cvt_lo(x.y), cvt_hi(x.y)};
     u32x4_t o1 = {cvt_lo(x.z), cvt_hi(x.z), cvt_lo(x.w), cvt_hi(x.w)};
     u32x4_t o2 = {cvt_lo(y.x), cvt_hi(y.x), cvt_lo(y.y), cvt_hi(y.y)};
@@ -267,14 +303,12 @@ __device__ __forceinline__ void stage_keys(uint8_t* dst, float* sdst, const uint
     dd[1] = o1;
     dd[2] = o2;
     dd[3] = o3;
-    if (part == 0) sdst[tok] = sbase[tsrc];
   } else {
-    const uint4* s = reinterpret_cast<const uint4*>(kbase + (size_t)tsrc * 2 * kD + 64 * part);
     uint4* dd = reinterpret_cast<uint4*>(d + 64 * part);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) dd[i] = s[i];
-    if (part == 0) sdst[tok] = 1.f;
+    for (int i = 0; i < 4; ++i) dd[i] = r.v[i];
   }
+  if (part == 0) sdst[tok] = r.sc;
 }
 
 template <int KDT>
@@ -293,6 +327,7 @@ __global__ __launch_bounds__(kThreads) void logits_causal_kernel(
   __shared__ uint4 qs[kH * kD * 2 / 16];           // 16 KiB, one row at a time
   __shared__ __attribute__((aligned(16))) uint8_t kt[2][kPTile * kPStride];
   __shared__ float st[2][kPTile];
+  __shared__ float sres[kWaves][kPTile];
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int col = lane & 15, grp = lane >> 4;
@@ -329,33 +364,38 @@ __global__ __launch_bounds__(kThreads) void logits_causal_kernel(
   float* orow = out + (size_t)min(r, R - 1) * ld;
   const int ntiles = (span_end - span0 + kPTile - 1) / kPTile;
 
-  stage_keys<KDT>(kt[0], st[0], kbase, sbase, span0, span_end - span0);
+  Staged<KDT> nxt;
+  stage_fetch<KDT>(nxt, kbase, sbase, span0, span_end - span0);
+  stage_commit<KDT>(nxt, kt[0], st[0]);
   __syncthreads();
 #pragma unroll 1
   for (int it = 0; it < ntiles; ++it) {
     const int cb = it & 1;
     const int t0 = span0 + it * kPTile;
-    if (it + 1 < ntiles) {
-      const int t1 = t0 + kPTile;
-      stage_keys<KDT>(kt[cb ^ 1], st[cb ^ 1], kbase, sbase, t1, span_end - t1);
-    }
-    if (row_ok && t0 < vis) {
+    const bool more = it + 1 < ntiles;
+    // fp8 tiles stay in registers (8 VGPRs) while this tile is multiplied;
+    // bf16 tiles are twice as large and are committed at once instead.
+    if (more) stage_fetch<KDT>(nxt, kbase, sbase, t0 + kPTile, span_end - (t0 + kPTile));
+    if (KDT == ECH_KEY_BF16 && more) stage_commit<KDT>(nxt, kt[cb ^ 1], st[cb ^ 1]);
+    const bool live = row_ok && t0 < vis;
+    if (live) {
+      // All four sub-tiles unconditionally; scores past the causal edge are
+      // computed but never stored.
 #pragma unroll
       for (int sub = 0; sub < kPTile / 16; ++sub) {
-        const int tb = t0 + sub * 16;
-        if (tb < vis) {
-          const uint8_t* kr = kt[cb] + (sub * 16 + col) * kPStride;
-          bf16x8_t b[4];
+        const uint8_t* kr = kt[cb] + (sub * 16 + col) * kPStride;
+        bf16x8_t b[4];
 #pragma unroll
-          for (int s = 0; s < 4; ++s)
-            b[s] = as_bf16x8(*reinterpret_cast<const uint4*>(kr + 2 * dim0_of<ECH_KEY_BF16>(grp, s)));
-          const float v = tile_score(a, wv, b, st[cb][sub * 16 + col]);
-          const int t = tb + col;
-          if (grp == 0 && t < vis) orow[t] = v;
-        }
+        for (int s = 0; s < 4; ++s)
+          b[s] = as_bf16x8(*reinterpret_cast<const uint4*>(kr + 2 * dim0_of<ECH_KEY_BF16>(grp, s)));
+        sres[wave][sub * 16 + col] = tile_score(a, wv, b, st[cb][sub * 16 + col]);
       }
     }
+    if (KDT == ECH_KEY_FP8 && more) stage_commit<KDT>(nxt, kt[cb ^ 1], st[cb ^ 1]);
     __syncthreads();
+    // One coalesced 256-byte store of the wave's 64 scores per tile (four
+    // 64-byte partial-line stores cost write bandwidth).
+    if (live && t0 + lane < vis) orow[t0 + lane] = sres[wave][lane];
   }
 }
 

@@ -9,9 +9,9 @@
 // so the kernels find s* and need_eq, then compact in ascending t.
 //
 //   T1 hist     grid (chunks, R): LDS histogram of bin(t) = high byte of
-//               ord(fl32(s_t - theta)) per 4096-token chunk. fl32(s - theta)
-//               is monotone in s and ord() is order preserving, so higher bins
-//               hold strictly larger scores.
+//               the order key of fp16(fl32(s_t - theta)) per 4096-token chunk.
+//               Every step is monotone in s, so higher bins hold strictly
+//               larger scores.
 //   T2 rowsel   grid (R): sum the chunk histograms, boundary bin b* where the
 //               count from the top reaches k, need = k - count above b*.
 //   T3 gather   grid (chunks, R): count tokens above b* per chunk; append the
@@ -98,9 +98,8 @@ size_t layout(int R, int max_len, Ws* w, char* base) {
 // Binning of a score relative to the prediction theta. Scores more than
 // |theta|/4 below theta all share bin 0: only the bins around and above the
 // boundary are needed, and lumping the bulk lets the histogram skip the
-// per-bin work for most tokens. Bin 0 is the lowest bin (a real bin 0 needs
-// |s - theta| >= 2^126, which is below the cut anyway), so the binning stays
-// monotone in s. A NaN theta means no shift and no lumping.
+// per-bin work for most tokens. Bin 0 is below every real bin, so the binning
+// stays monotone in s. A NaN theta means no shift and no lumping.
 struct Shift {
   float th, cut;
   bool on;
@@ -115,10 +114,24 @@ __device__ __forceinline__ Shift make_shift(float th) {
   return sh;
 }
 
+// The 256 bins are the high byte of the order key of fp16(d): sign, 5
+// exponent bits and 2 mantissa bits, i.e. four bins per binade of |d| (the
+// high byte of the fp32 key would give one bin per two binades). fp32 -> fp16
+// rounding is monotone, so the binning stays monotone in s; overflow goes to
+// the infinities, the outermost bins. Finite negative d never reaches bin 0
+// (its order key is at least 0x0400), so bin 0 is free for the lumped scores.
+__device__ __forceinline__ uint32_t bin16(float d) {
+  const _Float16 h = (_Float16)d;
+  uint32_t u = __builtin_bit_cast(uint16_t, h);
+  if ((u & 0x7fffu) == 0u) u = 0u;               // -0 -> +0
+  const uint32_t key = (u & 0x8000u) ? (~u & 0xffffu) : (u | 0x8000u);
+  return key >> 8;
+}
+
 __device__ __forceinline__ uint32_t shifted_bin(float x, const Shift& sh) {
-  if (!sh.on) return ech::ord_key(x) >> 24;
+  if (!sh.on) return bin16(x);
   const float d = x - sh.th;
-  return d < sh.cut ? 0u : ech::ord_key(d) >> 24;
+  return d < sh.cut ? 0u : bin16(d);
 }
 
 __device__ __forceinline__ float row_theta(const float* th, int r) {
@@ -170,7 +183,7 @@ __global__ __launch_bounds__(kT) void topk_hist_kernel(const float* __restrict__
       const float d = sh.on ? x - sh.th : x;
       const bool lump = ok && d < sh.cut;
       lumped += lump;
-      ech::lds_hist_add(h, ech::ord_key(d) >> 24, ok && !lump);
+      ech::lds_hist_add(h, bin16(d), ok && !lump);
     }
   }
   lumped = ech::wave_sum(lumped);

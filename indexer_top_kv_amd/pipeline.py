@@ -4,8 +4,8 @@ Decode step (ECHO explainer, "The top-k dependency" and "Decode: fetch above
 a predicted threshold"): the recall of a step depends on its top-k; the early
 fetch of tokens scoring above the predicted threshold overlaps the top-k.
 
-    S0: ech_index_logits --------------> ech_topk(theta -> theta') -> FINAL maps -> FINAL recall
-         \\-> S1: EARLY(theta) maps --/  EARLY recall (PCIe) -----------------/
+    S0: ech_index_logits --> ech_topk(theta -> theta') --> FINAL maps --> FINAL recall
+         \\-> S1: EARLY(theta) maps -----/--> EARLY recall (PCIe) ----/
 
 theta is double-buffered (EARLY reads the prediction while the top-k writes
 its update). When the batch's selections do not fit the cache at once (sum of
@@ -56,8 +56,10 @@ class DecodeLayer:
 
     def __init__(self, kcache: torch.Tensor, kscale: Optional[torch.Tensor], w: torch.Tensor,
                  tok0: np.ndarray, lens: np.ndarray, C: int, k: int = 2048, cap: int = 512,
-                 host_pool: Optional[torch.Tensor] = None, early: bool = True, device='cuda'):
+                 host_pool: Optional[torch.Tensor] = None, early: bool = True, topk_after_early: bool = False,
+                 device='cuda'):
         self.kcache, self.kscale, self.w = kcache, kscale, w
+        self.topk_after_early = topk_after_early
         self.B = len(lens)
         self.lens_np = np.asarray(lens, np.int32)
         self.tok0_np = np.asarray(tok0, np.int64)
@@ -153,16 +155,18 @@ class DecodeLayer:
             self._recall(ECH_EARLY, self.s1)
             mark('early', self.s1)
             self.ev_early.record(self.s1)
-        # The top-k is off the critical path (logits -> EARLY maps -> EARLY
-        # recall over PCIe -> FINAL recall); started after the EARLY maps it
-        # overlaps the PCIe transfer instead of competing with the maps.
-        if self.early:
-            s0.wait_event(self.ev_early_maps)      # FINAL also updates the maps EARLY left
+        # The top-k runs beside the EARLY maps; kernels that overlap the PCIe
+        # gather of the EARLY recall slow down several-fold (its host reads
+        # hold the shared memory queues), so only the small FINAL maps do.
+        if self.early and self.topk_after_early:
+            s0.wait_event(self.ev_early_maps)
         mark('topk', s0)
         ech_topk(self.logits, self.lens, self.max_len, self.k, th, th_next, self.idx, self.kth, self.ws_topk,
                  stream=s0)
         mark('topk', s0)
         mark('final', s0)
+        if self.early and not self.topk_after_early:
+            s0.wait_event(self.ev_early_maps)      # FINAL updates the maps EARLY left ...
         self._maps(ECH_FINAL, first_b0, first_b1, th, s0)
         if self.early:
             s0.wait_event(self.ev_early)           # ... but may reuse a slot EARLY is still filling
