@@ -30,23 +30,12 @@ __device__ __forceinline__ float ord_to_float(uint32_t k) {
   return __uint_as_float(u);
 }
 
-// Add one to hist[bin] for every active lane, merging lanes that share a bin
-// so that a wave whose lanes mostly hit a few bins (the common case for the
-// threshold-shifted scores) issues one LDS atomic per distinct bin instead of
-// 64 conflicting ones. After kMaxRounds distinct bins the rest add directly.
-template <int kMaxRounds = 8>
+// Add one to hist[bin] for every active lane with a plain LDS atomic. Merging
+// lanes that share a bin first (leader election with ballots) was measured
+// slower on gfx950 for every distribution here: the LDS serialises
+// same-address atomics cheaply, the ballot loop costs more.
 __device__ __forceinline__ void lds_hist_add(int* hist, uint32_t bin, bool active) {
-  uint64_t pending = __ballot(active);
-  const int lane = lane_id();
-#pragma unroll 1
-  for (int it = 0; it < kMaxRounds && pending; ++it) {
-    const int leader = __ffsll((unsigned long long)pending) - 1;
-    const uint32_t lb = __builtin_amdgcn_readlane(bin, leader);
-    const uint64_t same = __ballot(active && bin == lb) & pending;
-    if (lane == leader) atomicAdd(&hist[lb], __popcll(same));
-    pending &= ~same;
-  }
-  if ((pending >> lane) & 1ull) atomicAdd(&hist[bin], 1);
+  if (active) atomicAdd(&hist[bin], 1);
 }
 
 // Inclusive prefix sum across the wave.
