@@ -193,7 +193,12 @@ __global__ __launch_bounds__(kT) void topk_hist_kernel(const float* __restrict__
 }
 
 // ------------------------------------------------------------------ T2
-__global__ __launch_bounds__(kT) void topk_rowsel_kernel(const int32_t* __restrict__ lens, int k, Ws ws) {
+// 1024 threads: thread (part, b) sums bin (255 - b) over the chunks
+// c = part, part + 4, ..., eight independent loads in flight (a loop with one
+// load per iteration waits a full memory round trip per chunk).
+constexpr int kRowselT = 1024;
+
+__global__ __launch_bounds__(kRowselT) void topk_rowsel_kernel(const int32_t* __restrict__ lens, int k, Ws ws) {
   const int r = blockIdx.x;
   const int len = lens[r];
   RowState& st = ws.rs[r];
@@ -207,14 +212,25 @@ __global__ __launch_bounds__(kT) void topk_rowsel_kernel(const int32_t* __restri
     return;
   }
   const int nch = (len + kChunk - 1) / kChunk;
-  __shared__ int scratch[kT / 64];
-  // thread b owns bin (255 - b) so an exclusive scan counts the bins above it
-  const int bin = 255 - threadIdx.x;
-  int cnt = 0;
-  for (int c = 0; c < nch; ++c) cnt += ws.hist[((size_t)r * ws.nch + c) * 256 + bin];
+  __shared__ int part_sum[4][256];
+  __shared__ int scratch[kRowselT / 64];
+  const int b = threadIdx.x & 255, part = threadIdx.x >> 8;
+  const int bin = 255 - b;
+  const int* h = ws.hist + (size_t)r * ws.nch * 256 + bin;
+  int acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  int c = part;
+  for (; c + 28 < nch; c += 32) {
+#pragma unroll
+    for (int u = 0; u < 8; ++u) acc[u] += h[(size_t)(c + 4 * u) * 256];
+  }
+  for (; c < nch; c += 4) acc[0] += h[(size_t)c * 256];
+  part_sum[part][b] = acc[0] + acc[1] + acc[2] + acc[3] + acc[4] + acc[5] + acc[6] + acc[7];
+  __syncthreads();
+  // threads 0..255 hold bins 255..0 in order; the rest add zeros after them
+  const int cnt = (threadIdx.x < 256) ? part_sum[0][b] + part_sum[1][b] + part_sum[2][b] + part_sum[3][b] : 0;
   int tot;
-  const int above = ech::block_excl_scan<kT>(cnt, scratch, &tot);
-  if (above < k && above + cnt >= k) {
+  const int above = ech::block_excl_scan<kRowselT>(cnt, scratch, &tot);
+  if (threadIdx.x < 256 && above < k && above + cnt >= k) {
     st.mode = kNormal;
     st.bstar = bin;
     st.need = k - above;
@@ -512,7 +528,7 @@ extern "C" int ech_topk(const float* logits, int64_t ld, const int32_t* row_len,
   const dim3 gch(w.nch, R);
   hipLaunchKernelGGL(topk_hist_kernel, gch, dim3(kT), 0, s, logits, ld, row_len, k, theta_in, w);
   ECH_LAUNCH_CHECK();
-  hipLaunchKernelGGL(topk_rowsel_kernel, dim3(R), dim3(kT), 0, s, row_len, k, w);
+  hipLaunchKernelGGL(topk_rowsel_kernel, dim3(R), dim3(kRowselT), 0, s, row_len, k, w);
   ECH_LAUNCH_CHECK();
   hipLaunchKernelGGL(topk_gather_kernel, gch, dim3(kT), 0, s, logits, ld, row_len, theta_in, w);
   ECH_LAUNCH_CHECK();
