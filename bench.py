@@ -44,8 +44,10 @@ def parse():
     p.add_argument('--no-early', action='store_true', help='disable the early fetch (ablation)')
     p.add_argument('--eager', action='store_true', help='time eager launches instead of graph replays')
     p.add_argument('--topk-after-early', action='store_true', help='start the top-k after the EARLY maps')
-    p.add_argument('--cpu-seqs', type=int, default=4, help='sequences in the oracle sample')
-    p.add_argument('--cpu-steps', type=int, default=2, help='decode steps in the oracle sample')
+    p.add_argument('--early-groups', type=int, default=0,
+                   help='sequence groups of the early fetch (0: one EARLY phase after all scores)')
+    p.add_argument('--cpu-seqs', type=int, default=32, help='sequences in the oracle sample')
+    p.add_argument('--cpu-steps', type=int, default=3, help='decode steps in the oracle sample')
     p.add_argument('--calibrate-copy', action='store_true',
                    help='only run a plain 1 GiB device copy 5 times (reference for HBM byte counters)')
     return p.parse_args()
@@ -104,7 +106,8 @@ def bench_decode(args, wl):
     kc, ks, wd = dev(keys), (dev(scale) if scale is not None else None), dev(w)
     qd = dev(qs)
     layer = DecodeLayer(kc, ks, wd, wl.tok0, wl.lens, wl.C, k=wl.k, cap=wl.cap, host_pool=pool,
-                        early=not args.no_early, topk_after_early=args.topk_after_early)
+                        early=not args.no_early, topk_after_early=args.topk_after_early,
+                        early_groups=args.early_groups)
     torch.cuda.synchronize()
     log(f'chunks {layer.chunks}; warm-up {args.warmup} steps')
     for s in range(args.warmup):
@@ -161,7 +164,7 @@ def bench_decode(args, wl):
     per_launch = tokens * per_token + wl.B * (64 * 128 * 2 + 64 * 4)
     achieved = per_launch / (logits_ms * 1e-3) / 1e9
     flops = tokens * 2 * 64 * 128
-    src = source_hash('logits.hip')
+    src = source_hash('logits.hip', 'score.hpp')
     traffic = measured_traffic('logits_decode_' + wl.name, src)
     out = {
         'metric': 'decode tokens scored/s (indexer logits + exact top-k + early/final slot-map step + recall), '
@@ -179,19 +182,37 @@ def bench_decode(args, wl):
         'data': 'synthetic, seeded',
         'config': {'workload': wl.name, 'B': wl.B, 'context': wl.N, 'k': wl.k, 'heads': 64, 'head_dim': 128,
                    'key_dtype': wl.kdtype, 'cache_slots': wl.C, 'early_fetch_cap': wl.cap,
-                   'early_fetch': not args.no_early, 'row_bytes': 1152,
+                   'early_fetch': not args.no_early, 'early_groups': len(layer.groups), 'row_bytes': 1152,
                    'launch': 'eager' if args.eager else 'hipGraph replay per step'},
         'roofline': {'bound': 'hbm', 'kernel': 'logits_decode_kernel', 'achieved': achieved,
                      'peak': PEAK_HBM_GBS, 'unit': 'GB/s', 'frac': achieved / PEAK_HBM_GBS,
                      'traffic': traffic, 'algorithmic_bytes_per_launch': per_launch,
                      'avg_launch_us': logits_ms * 1e3,
                      'mfma_bf16_frac': flops / (logits_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS},
-        'stages_us_eager': {k: (avg_ms(k) or 0.0) * 1e3 for k in ('logits', 'topk', 'early', 'final')},
+        'stages_us_eager': {k: (avg_ms(k) or 0.0) * 1e3
+                            for k in ('logits', 'topk', 'early', 'early_maps', 'recall_early', 'final',
+                                      'final_maps', 'recall_final')},
         'recall': {'rows_per_step': recalled / args.steps, 'bytes_per_step': recalled * 1152 / args.steps},
         'last_step': {'final_hits': int(stats_final[:, 0].sum()), 'final_misses': int(stats_final[:, 1].sum()),
                       'early_fetched': int(stats_early[:, 1].sum()), 'evictions':
                       int(stats_final[:, 3].sum() + stats_early[:, 3].sum())},
         'logits_source': src,
+    }
+    st = out['stages_us_eager']
+    topk_bytes = tokens * 4 + wl.B * wl.k * 4
+    rec_us = st['recall_early'] + st['recall_final']
+    out['stage_rooflines'] = {
+        'topk': {'bound': 'hbm', 'algorithmic_bytes': topk_bytes, 'us': st['topk'],
+                 'achieved_GBs': topk_bytes / (st['topk'] * 1e-6) / 1e9 if st['topk'] else None,
+                 'peak_GBs': PEAK_HBM_GBS,
+                 'frac': topk_bytes / (st['topk'] * 1e-6) / 1e9 / PEAK_HBM_GBS if st['topk'] else None,
+                 'note': 'one read of the scores plus the index output, over the five top-k launches'},
+        'recall': {'bound': 'pcie', 'bytes_per_step': out['recall']['bytes_per_step'], 'us': rec_us,
+                   'achieved_GBs': out['recall']['bytes_per_step'] / (rec_us * 1e-6) / 1e9 if rec_us else None,
+                   'note': 'EARLY + FINAL recall kernels of eager steps; denominator: pcie.h2d_memcpy_GBs'},
+        'allocator': {'early_maps_us': st['early_maps'], 'final_maps_us': st['final_maps'],
+                      'note': 'slot-map phases in eager steps (pin, free, scan, emit, apply), run beside '
+                              'the top-k (EARLY) and beside the EARLY recall (FINAL)'},
     }
     return out, dict(wl=wl, pool=pool, qs=qs, w=w, keys=keys, scale=scale)
 
@@ -356,6 +377,9 @@ def main():
     if wl.mode == 'decode':
         out, ctx = bench_decode(args, wl)
         out['pcie'] = pcie_check(ctx['pool'], wl.C)
+        r = out['stage_rooflines']['recall']
+        if r['achieved_GBs']:
+            r['frac_of_memcpy'] = r['achieved_GBs'] / out['pcie']['h2d_memcpy_GBs']
         if not args.no_cpu_baseline:
             log('timing the CPU oracle on a sample')
             out['cpu_baseline'] = cpu_baseline_decode(args, wl, ctx)

@@ -73,6 +73,7 @@ extern "C" {
 #define ECH_CTR_NWANT     6   /* misses the last phase wanted (before cap / slot limits) */
 #define ECH_CTR_NPINNED   7   /* slots pinned by the last phase */
 #define ECH_CTR_NMISS_EARLY 8 /* entries written to the miss list by the last EARLY phase */
+#define ECH_CTR_TICKET    9   /* allocator scratch counter (0 between calls; never write it) */
 #define ECH_CTR_LEN      16
 
 /* ---- sticky status bits in ctr[ECH_CTR_STATUS] */
@@ -231,6 +232,57 @@ int ech_cache_step(int phase, int32_t* tok2slot, int64_t P, int32_t* slot2tok, i
  */
 int ech_recall(int phase, const void* host_pool, int64_t P, int64_t row_bytes, void* dev_cache, int32_t C,
                const int32_t* miss, int32_t* ctr, int32_t M_max, void* stream);
+
+/*
+ * Early fetch in sequence groups (decode) - the ECH_EARLY phase of
+ * ech_cache_step, computed so that the early rows of the first sequences can
+ * cross PCIe while the scores of later sequences are still being computed
+ * (ECHO explainer, "Decode: fetch above a predicted threshold": the early
+ * fetch hides the dependency of the recall on the top-k). The maps, the miss
+ * list, ctr and stats end up exactly as after one ECH_EARLY phase over all B
+ * sequences with the same scores, whatever the grouping:
+ *
+ *   ech_early_begin   once per step, before any group; needs no scores. It
+ *                     scores the tokens resident at the start of the step with
+ *                     the arithmetic of ech_index_logits (the same bit
+ *                     patterns), pins those above theta (strict; none for a
+ *                     NaN theta), writes stats[b*4+0] (hits; the other three
+ *                     fields are zeroed) and ranks the unpinned slots in ring
+ *                     order from the head.
+ *   ech_early_group   for consecutive groups [b0, b1) in ascending order,
+ *                     group = 0, 1, ...; each after its rows of `logits` are
+ *                     written (ech_index_logits on those rows). Allocates the
+ *                     group's misses (the first `cap` non-resident tokens above
+ *                     theta per sequence, ascending), continuing the ring
+ *                     order; writes stats[b*4+1..3] of its sequences, the miss
+ *                     list entries of its rank range, ctr[ECH_CTR_NMISS_EARLY]
+ *                     (entries so far), head and evictions.
+ *   ech_recall_group  copies the rows of one group's rank range (after that
+ *                     group's ech_early_group; groups' recalls may overlap each
+ *                     other and later groups' allocation).
+ *
+ * All calls of one step use the same ws (ech_early_ws_bytes(B, max_len, C,
+ * M_early) bytes, 256-byte aligned, uninitialised OK) and the same B,
+ * max_len, C, M_early; the calls of one step must be ordered (stream or
+ * events) except as stated for the recalls, and the FINAL phase of the step
+ * must follow every group (ech_early_group) and, before its own recall, every
+ * group's recall. M_early >= B * min(cap, max_len); group < 96; B <= 1024.
+ * Arguments have the meaning they have for ech_index_logits and
+ * ech_cache_step(ECH_EARLY); miss_early is the EARLY miss list [M_early, 2].
+ */
+size_t ech_early_ws_bytes(int B, int max_len, int32_t C, int32_t M_early);
+int ech_early_begin(const void* q, const float* w, const void* kcache, int kdtype, const float* kscale,
+                    const int64_t* seq_tok0, const int32_t* seq_len, int B, int max_len, const float* theta,
+                    const int32_t* tok2slot, int64_t P, int32_t* slot_pin, int32_t C, int32_t* ctr,
+                    int32_t M_early, int32_t* stats, void* ws, size_t ws_bytes, void* stream);
+int ech_early_group(int group, int b0, int b1, const float* logits, int64_t ld, const float* theta, int cap,
+                    const int64_t* seq_tok0, const int32_t* seq_len, int B, int max_len,
+                    int32_t* tok2slot, int64_t P, int32_t* slot2tok, int32_t* slot_pin, int32_t C,
+                    int32_t* miss_early, int32_t M_early, int32_t* ctr, int32_t* stats,
+                    void* ws, size_t ws_bytes, void* stream);
+int ech_recall_group(int group, const void* host_pool, int64_t P, int64_t row_bytes, void* dev_cache,
+                     int32_t C, const int32_t* miss_early, int32_t M_early, int32_t* ctr, const void* ws,
+                     void* stream);
 
 #ifdef __cplusplus
 }

@@ -22,7 +22,8 @@ ECH_EARLY = 0
 ECH_FINAL = 1
 ECH_PREFILL = 2
 
-CTR_HEAD, CTR_EPOCH, CTR_NMISS, CTR_NEVICT, CTR_RECALLED, CTR_STATUS, CTR_NWANT, CTR_NPINNED, CTR_NMISS_EARLY = range(9)
+(CTR_HEAD, CTR_EPOCH, CTR_NMISS, CTR_NEVICT, CTR_RECALLED, CTR_STATUS, CTR_NWANT, CTR_NPINNED,
+ CTR_NMISS_EARLY, CTR_TICKET) = range(10)
 CTR_LEN = 16
 
 ST_OVERFLOW = 1
@@ -51,6 +52,13 @@ SIGNATURES = {
                                       ctypes.c_int, _p, ctypes.c_int, ctypes.c_int, _p, _i64, _p, ctypes.c_int, _p,
                                       _p, _p, _sz, _p]),
     'ech_recall': (ctypes.c_int, [ctypes.c_int, _p, _i64, _i64, _p, _i32, _p, _p, _i32, _p]),
+    'ech_early_ws_bytes': (_sz, [ctypes.c_int, ctypes.c_int, _i32, _i32]),
+    'ech_early_begin': (ctypes.c_int, [_p, _p, _p, ctypes.c_int, _p, _p, _p, ctypes.c_int, ctypes.c_int, _p,
+                                       _p, _i64, _p, _i32, _p, _i32, _p, _p, _sz, _p]),
+    'ech_early_group': (ctypes.c_int, [ctypes.c_int, ctypes.c_int, ctypes.c_int, _p, _i64, _p, ctypes.c_int, _p,
+                                       _p, ctypes.c_int, ctypes.c_int, _p, _i64, _p, _p, _i32, _p, _i32, _p, _p,
+                                       _p, _sz, _p]),
+    'ech_recall_group': (ctypes.c_int, [ctypes.c_int, _p, _i64, _i64, _p, _i32, _p, _i32, _p, _p, _p]),
 }
 
 _lib = None

@@ -5,7 +5,9 @@
 Compiles every csrc/*.hip into one shared library next to this file. Packed
 FP32 instructions are disabled for device code (their generation by the
 compiler is turned off; the host pass warns that it does not know the
-feature, which is harmless).
+feature, which is harmless). MFMA results are kept in ordinary VGPRs rather
+than accumulation registers, which saves the copies out of them (one VALU
+instruction per result register) in the scoring kernels.
 """
 import glob
 import os
@@ -28,6 +30,7 @@ def build(verbose: bool = False) -> str:
     cmd = [hipcc, f'--offload-arch={ARCH}', '-O3', '-std=c++17', '-shared', '-fPIC',
            '-Wall', '-Wno-unused-function',
            '-Xclang', '-target-feature', '-Xclang', '-packed-fp32-ops',
+           '-mllvm', '-amdgpu-mfma-vgpr-form',
            '-I', os.path.join(ROOT, 'include'), '-I', os.path.join(HERE, 'csrc'),
            *sources(), '-o', tmp]
     if verbose:

@@ -1,16 +1,28 @@
-"""One layer of the path, launched in order on two streams.
+"""One layer of the path, launched in order on up to three streams.
 
 Decode step (ECHO explainer, "The top-k dependency" and "Decode: fetch above
 a predicted threshold"): the recall of a step depends on its top-k; the early
-fetch of tokens scoring above the predicted threshold overlaps the top-k.
+fetch of tokens scoring above the predicted threshold starts before it:
 
     S0: ech_index_logits --> ech_topk(theta -> theta') --> FINAL maps --> FINAL recall
-         \\-> S1: EARLY(theta) maps -----/--> EARLY recall (PCIe) ----/
+         \-> S1: EARLY(theta) maps -----/--> EARLY recall (PCIe) ----/
 
-theta is double-buffered (EARLY reads the prediction while the top-k writes
-its update). When the batch's selections do not fit the cache at once (sum of
-min(k, len_b) > C), sequences are processed in host-computed chunks, each
-EARLY then FINAL; every selected token is resident at the end of its chunk.
+Optionally (early_groups >= 1) the batch's sequences are scored in G groups
+and each group's early rows start crossing PCIe as soon as its scores exist:
+
+    S1: early_begin (pins)     group 0 maps        group 1 maps  ...
+    S0: logits group 0 ---------> logits group 1 --------> ... --> ech_topk --+-> FINAL maps --+-> FINAL recall
+    S2:                              recall group 0 --> recall group 1 ... ---/----------------/
+
+The grouping changes only the order of the work, not its result (see
+ech_early_begin in include/ech.h). On MI355X it is slower: kernels running
+beside the saturating key stream and beside the PCIe gather slow down
+several-fold, so one EARLY phase after all scores is the default. theta is
+double-buffered (the early fetch
+reads the prediction while the top-k writes its update). When the batch's
+selections do not fit the cache at once (sum of min(k, len_b) > C),
+sequences are processed in host-computed chunks, each an ECH_EARLY phase
+then a FINAL phase; every selected token is resident at the end of its chunk.
 
 Prefill (ECHO explainer, "Prefill: one-round histogram"): query blocks are
 scored one after another; the recall of block i runs on S1 while S0 scores
@@ -27,12 +39,20 @@ import numpy as np
 import torch
 
 from . import (ECH_EARLY, ECH_FINAL, ECH_PREFILL, LayerState, ech_cache_reset, ech_cache_step,
-               ech_cache_step_ws_bytes, ech_index_logits, ech_index_logits_causal, ech_recall, ech_topk,
-               ech_topk_ws_bytes)
+               ech_cache_step_ws_bytes, ech_early_begin, ech_early_group, ech_early_ws_bytes, ech_index_logits,
+               ech_index_logits_causal, ech_recall, ech_recall_group, ech_topk, ech_topk_ws_bytes)
 
 
 def round_up(x: int, m: int) -> int:
     return (x + m - 1) // m * m
+
+
+def sequence_groups(B: int, groups: int) -> List[Tuple[int, int]]:
+    """Split sequences 0..B-1 into at most `groups` consecutive ranges of
+    nearly equal size."""
+    g = max(1, min(int(groups), B))
+    bounds = [round(i * B / g) for i in range(g + 1)]
+    return [(bounds[i], bounds[i + 1]) for i in range(g) if bounds[i + 1] > bounds[i]]
 
 
 def sequence_chunks(lens: np.ndarray, k: int, C: int) -> List[Tuple[int, int]]:
@@ -57,7 +77,7 @@ class DecodeLayer:
     def __init__(self, kcache: torch.Tensor, kscale: Optional[torch.Tensor], w: torch.Tensor,
                  tok0: np.ndarray, lens: np.ndarray, C: int, k: int = 2048, cap: int = 512,
                  host_pool: Optional[torch.Tensor] = None, early: bool = True, topk_after_early: bool = False,
-                 device='cuda'):
+                 early_groups: int = 0, device='cuda'):
         self.kcache, self.kscale, self.w = kcache, kscale, w
         self.topk_after_early = topk_after_early
         self.B = len(lens)
@@ -88,6 +108,17 @@ class DecodeLayer:
                                     dtype=torch.uint8, **dev)
         self.ws_final = torch.empty(ech_cache_step_ws_bytes(ECH_FINAL, cb, cb, k, self.max_len, C, m_max),
                                     dtype=torch.uint8, **dev)
+        # Early fetch in sequence groups: only when the whole batch is one chunk.
+        self.groups = (sequence_groups(self.B, early_groups)
+                       if early and early_groups >= 1 and len(self.chunks) == 1 else [])
+        if self.groups:
+            self.ws_group = torch.empty(ech_early_ws_bytes(self.B, self.max_len, C, m_max), dtype=torch.uint8,
+                                        **dev)
+            self.s2 = torch.cuda.Stream(device=device)
+            self.ev_start = torch.cuda.Event()
+            self.ev_lg = [torch.cuda.Event() for _ in self.groups]
+            self.ev_mg = [torch.cuda.Event() for _ in self.groups]
+            self.ev_rg = torch.cuda.Event()
         self.host_pool = host_pool
         if host_pool is not None:
             self.dev_cache = torch.zeros((C, host_pool.shape[1]), dtype=host_pool.dtype, **dev)
@@ -128,8 +159,10 @@ class DecodeLayer:
     def step(self, q: torch.Tensor, marks: Optional[dict] = None) -> None:
         """Enqueue one decode step for query q [B, 64, 128] (bf16 bits) on the
         current stream (with S1 forked and joined inside). `marks`, when given,
-        receives timing events recorded on the stream of each stage:
-        logits, topk, final (S0) and early (S1), as (start, end) pairs."""
+        receives timing events recorded on the stream of each stage, as
+        (start, end) pairs: logits, topk, final (S0: FINAL maps to the end of
+        its recall), early (S1: EARLY maps and recall), and inside those
+        early_maps, recall_early, final_maps, recall_final."""
         s0 = torch.cuda.current_stream()
 
         def mark(name, stream):
@@ -141,6 +174,10 @@ class DecodeLayer:
             return ev
 
         th, th_next = self.theta[self.parity], self.theta[1 - self.parity]
+        if self.groups:
+            self._step_grouped(q, th, th_next, s0, mark)
+            self.parity ^= 1
+            return
         mark('logits', s0)
         self.logits_only(q, stream=s0)
         mark('logits', s0)
@@ -150,9 +187,13 @@ class DecodeLayer:
             self.ev_logits.record(s0)
             self.s1.wait_event(self.ev_logits)
             mark('early', self.s1)
+            mark('early_maps', self.s1)
             self._maps(ECH_EARLY, first_b0, first_b1, th, self.s1)
+            mark('early_maps', self.s1)
             self.ev_early_maps.record(self.s1)
+            mark('recall_early', self.s1)
             self._recall(ECH_EARLY, self.s1)
+            mark('recall_early', self.s1)
             mark('early', self.s1)
             self.ev_early.record(self.s1)
         # The top-k runs beside the EARLY maps; kernels that overlap the PCIe
@@ -167,16 +208,57 @@ class DecodeLayer:
         mark('final', s0)
         if self.early and not self.topk_after_early:
             s0.wait_event(self.ev_early_maps)      # FINAL updates the maps EARLY left ...
+        mark('final_maps', s0)
         self._maps(ECH_FINAL, first_b0, first_b1, th, s0)
+        mark('final_maps', s0)
         if self.early:
             s0.wait_event(self.ev_early)           # ... but may reuse a slot EARLY is still filling
+        mark('recall_final', s0)
         self._recall(ECH_FINAL, s0)
+        mark('recall_final', s0)
         for b0, b1 in self.chunks[1:]:
             if self.early:
                 self._phase(ECH_EARLY, b0, b1, th, s0)
             self._phase(ECH_FINAL, b0, b1, th, s0)
         mark('final', s0)
         self.parity ^= 1
+
+    def _step_grouped(self, q, th, th_next, s0, mark) -> None:
+        """Decode step with the early fetch in sequence groups (one chunk)."""
+        s1, s2 = self.s1, self.s2
+        self.ev_start.record(s0)
+        s1.wait_event(self.ev_start)
+        s2.wait_event(self.ev_start)
+        mark('early', s1)
+        ech_early_begin(q, self.w, self.kcache, self.kscale, self.tok0, self.lens, self.max_len, th, self.state,
+                        self.stats_early, self.ws_group, stream=s1)
+        mark('logits', s0)
+        mark('recall_early', s2)
+        for g, (b0, b1) in enumerate(self.groups):
+            ech_index_logits(q[b0:b1], self.w[b0:b1], self.kcache, self.kscale, self.tok0[b0:b1],
+                             self.lens[b0:b1], self.max_len, self.logits[b0:b1], stream=s0)
+            self.ev_lg[g].record(s0)
+            s1.wait_event(self.ev_lg[g])
+            ech_early_group(g, b0, b1, self.logits, th, self.cap, self.tok0, self.lens, self.max_len, self.state,
+                            self.stats_early, self.ws_group, stream=s1)
+            self.ev_mg[g].record(s1)
+            if self.host_pool is not None:
+                s2.wait_event(self.ev_mg[g])
+                ech_recall_group(g, self.host_pool, self.dev_cache, self.state, self.ws_group, stream=s2)
+        mark('logits', s0)
+        mark('early', s1)
+        mark('recall_early', s2)
+        self.ev_rg.record(s2)
+        mark('topk', s0)
+        ech_topk(self.logits, self.lens, self.max_len, self.k, th, th_next, self.idx, self.kth, self.ws_topk,
+                 stream=s0)
+        mark('topk', s0)
+        mark('final', s0)
+        s0.wait_event(self.ev_mg[-1])      # FINAL updates the maps the groups left ...
+        self._maps(ECH_FINAL, 0, self.B, th, s0)
+        s0.wait_event(self.ev_rg)          # ... but may reuse a slot an early recall is still filling
+        self._recall(ECH_FINAL, s0)
+        mark('final', s0)
 
     @property
     def theta_current(self) -> torch.Tensor:

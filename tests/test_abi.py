@@ -14,7 +14,8 @@ HEADER = os.path.join(ROOT, 'include', 'ech.h')
 
 
 def declared_symbols():
-    text = open(HEADER).read()
+    with open(HEADER) as f:
+        text = f.read()
     text = re.sub(r'/\*.*?\*/', '', text, flags=re.S)
     return sorted(set(re.findall(r'\b(ech_[a-z_0-9]+)\s*\(', text)))
 
@@ -23,6 +24,7 @@ def test_header_declares_entry_points():
     syms = declared_symbols()
     for name in ['ech_index_logits', 'ech_index_logits_causal', 'ech_topk', 'ech_topk_ws_bytes',
                  'ech_cache_step', 'ech_cache_step_ws_bytes', 'ech_cache_reset', 'ech_recall',
+                 'ech_early_ws_bytes', 'ech_early_begin', 'ech_early_group', 'ech_recall_group',
                  'ech_status_str', 'ech_version']:
         assert name in syms
 
@@ -115,3 +117,38 @@ def test_recall_rejects_bad_args():
     assert lib.ech_recall(1, None, 10, 1152, FAKE, 10, FAKE, FAKE, 4, None) == -1
     assert lib.ech_recall(1, FAKE, 0, 1152, FAKE, 10, FAKE, FAKE, 4, None) == -1
     assert lib.ech_recall(9, FAKE, 10, 1152, FAKE, 10, FAKE, FAKE, 4, None) == -1   # no such phase
+
+
+def test_early_group_calls_reject_bad_args():
+    lib = ech.lib()
+    assert lib.ech_early_ws_bytes(0, 10, 10, 10) == 0
+    a = lib.ech_early_ws_bytes(4, 131072, 260000, 2048)
+    b = lib.ech_early_ws_bytes(32, 131072, 260000, 16384)
+    assert 0 < a < b
+    ws = lib.ech_early_ws_bytes(2, 1000, 500, 64)
+
+    def begin(q=FAKE, dt=1, sc=FAKE, B=2, ml=1000, C=500, M=64, wsb=ws, wsp=FAKE):
+        return lib.ech_early_begin(q, FAKE, FAKE, dt, sc, FAKE, FAKE, B, ml, FAKE, FAKE, 4000, FAKE, C, FAKE, M,
+                                   FAKE, wsp, wsb, None)
+    assert begin(q=None) == -1
+    assert begin(dt=5) == -3
+    assert begin(sc=None) == -1
+    assert begin(q=FAKE + 8) == -1
+    assert begin(B=2000) == -1
+    assert begin(wsb=ws - 1) == -1
+    assert begin(wsp=FAKE + 64) == -1
+
+    def group(g=0, b0=0, b1=2, B=2, cap=32, M=64, ld=1000, lg=FAKE, wsb=ws):
+        return lib.ech_early_group(g, b0, b1, lg, ld, FAKE, cap, FAKE, FAKE, B, 1000, FAKE, 4000, FAKE, FAKE, 500,
+                                   FAKE, M, FAKE, FAKE, FAKE, wsb, None)
+    assert group(g=-1) == -1
+    assert group(g=96) == -1
+    assert group(b0=1, b1=1) == -1
+    assert group(b1=3) == -1
+    assert group(cap=33) == -1            # early miss list smaller than B * cap
+    assert group(ld=999) == -1
+    assert group(lg=FAKE + 4) == -1
+    assert group(wsb=16) == -1
+    assert lib.ech_recall_group(0, FAKE, 10, 1150, FAKE, 10, FAKE, 4, FAKE, FAKE, None) == -1   # row_bytes % 16
+    assert lib.ech_recall_group(99, FAKE, 10, 1152, FAKE, 10, FAKE, 4, FAKE, FAKE, None) == -1
+    assert lib.ech_recall_group(0, FAKE, 10, 1152, FAKE, 10, FAKE, 4, FAKE, FAKE + 16, None) == -1

@@ -65,19 +65,20 @@ class OracleDecode:
         return L, idx, kth, sel, early_stats, final_stats
 
 
-def _setup(wl):
+def _setup(wl, early_groups=0):
     keys, scale = wk.keys(wl)
     w = wk.head_weights(wl)
     rows = wk.host_rows(wl)
     pool = torch.empty((wl.P, 576), dtype=torch.int16, pin_memory=True)
     pool.numpy()[:] = rows.view(np.int16)
     layer = DecodeLayer(dev(keys), None if scale is None else dev(scale), dev(w), wl.tok0, wl.lens, wl.C,
-                        k=wl.k, cap=wl.cap, host_pool=pool)
+                        k=wl.k, cap=wl.cap, host_pool=pool, early_groups=early_groups)
     return keys, scale, w, pool, layer
 
 
-def _run_bit_exact(wl, steps):
-    keys, scale, w, pool, layer = _setup(wl)
+def _run_bit_exact(wl, steps, early_groups=0):
+    keys, scale, w, pool, layer = _setup(wl, early_groups)
+    assert len(layer.groups) == (min(early_groups, wl.B) if early_groups and len(layer.chunks) == 1 else 0)
     ref = OracleDecode(wl, keys, scale, w, pool.numpy().copy())
     for s, q in enumerate(wk.decode_queries(wl, steps)):
         layer.step(dev(q))
@@ -103,6 +104,15 @@ def test_dyadic_decode_fp8_batch():
     need_gpu()
     wl = wk.CONFIGS['decode-32x128k-fp8'].scaled(B=4, N=9000, C=20000, steps=5, variant='dyadic')
     _run_bit_exact(wl, 5)
+
+
+def test_dyadic_decode_fp8_batch_grouped_early():
+    """The same steps with the early fetch in three sequence groups (pins
+    from the resident tokens' own scores, groups' rows recalled on a third
+    stream): bit-identical to the oracle's single early phase."""
+    need_gpu()
+    wl = wk.CONFIGS['decode-32x128k-fp8'].scaled(B=5, N=9000, C=20000, steps=5, variant='dyadic')
+    _run_bit_exact(wl, 5, early_groups=3)
 
 
 def test_dyadic_decode_bf16_small_cache():
