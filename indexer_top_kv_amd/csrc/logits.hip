@@ -170,57 +170,62 @@ __device__ __forceinline__ void stage_commit(const Staged<KDT>& r, uint8_t* dst,
   if (part == 0) sdst[tok] = r.sc;
 }
 
-template <int KDT>
+template <int KDT, int RPW>
 __global__ __launch_bounds__(kThreads) void logits_causal_kernel(
     const uint16_t* __restrict__ q, const float* __restrict__ w, const uint8_t* __restrict__ kc,
     const float* __restrict__ ksc, int64_t tok0, int64_t row0, int R, float* __restrict__ out, int64_t ld) {
   constexpr int kRowB = (KDT == ECH_KEY_FP8) ? kD : 2 * kD;
+  constexpr int kRows = kWaves * RPW;              // query rows per WG
   const int rg = blockIdx.x;                       // row group
   const int span0 = blockIdx.y * kSpan;
-  const int r_first = rg * kWaves;
-  const int r_last = min(R - 1, r_first + kWaves - 1);
+  const int r_first = rg * kRows;
+  const int r_last = min(R - 1, r_first + kRows - 1);
   const int64_t vis_max = row0 + r_last + 1;       // tokens visible to the last row
   if ((int64_t)span0 >= vis_max) return;
   const int span_end = (int)min<int64_t>(vis_max, (int64_t)span0 + kSpan);
 
-  __shared__ uint4 qs[kH * kD * 2 / 16];           // 16 KiB, one row at a time
   __shared__ __attribute__((aligned(16))) uint8_t kt[2][kPTile * kPStride];
   __shared__ float st[2][kPTile];
-  __shared__ float sres[kWaves][kPTile];
+  __shared__ float sres[kRows][kPTile];
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int col = lane & 15, grp = lane >> 4;
-  const int r = r_first + wave;
-  const bool row_ok = r <= r_last;
-  const int64_t vis = row_ok ? row0 + r + 1 : 0;   // tokens t < vis are visible
+  // wave w scores rows r_first + w*RPW + j, j < RPW: every key fragment read
+  // from LDS feeds RPW rows' MFMAs
+  bool row_ok[RPW];
+  int64_t vis[RPW];                                // tokens t < vis are visible
+  float* orow[RPW];
+#pragma unroll
+  for (int j = 0; j < RPW; ++j) {
+    const int r = r_first + wave * RPW + j;
+    row_ok[j] = r <= r_last;
+    vis[j] = row_ok[j] ? row0 + r + 1 : 0;
+    orow[j] = out + (size_t)min(r, R - 1) * ld;
+  }
 
-  // A fragments: rows are staged through LDS one at a time.
-  bf16x8_t a[4][4];
-  float wv[4][4];
-  for (int i = 0; i < kWaves; ++i) {
-    const int rr = min(r_first + i, r_last);
-    const uint4* qg = reinterpret_cast<const uint4*>(q + (size_t)rr * kH * kD);
-    for (int j = threadIdx.x; j < kH * kD * 2 / 16; j += blockDim.x) qs[j] = qg[j];
-    __syncthreads();
-    if (wave == i) {
-      const uint8_t* qb = reinterpret_cast<const uint8_t*>(qs);
+  // A fragments and head weights straight from global memory (q rows are
+  // shared by every span of the row group and stay in L2): 16-byte pieces,
+  // all loads in flight at once, no staging barrier.
+  bf16x8_t a[RPW][4][4];
+  float wv[RPW][4][4];
 #pragma unroll
-      for (int ht = 0; ht < 4; ++ht) {
+  for (int j = 0; j < RPW; ++j) {
+    const int rr = min(r_first + wave * RPW + j, r_last);
+    const uint8_t* qb = reinterpret_cast<const uint8_t*>(q + (size_t)rr * kH * kD);
 #pragma unroll
-        for (int s = 0; s < 4; ++s) {
-          const int off = (16 * ht + col) * (kD * 2) + 2 * dim0_of<ECH_KEY_BF16>(grp, s);
-          a[ht][s] = as_bf16x8(*reinterpret_cast<const uint4*>(qb + off));
-        }
+    for (int ht = 0; ht < 4; ++ht) {
 #pragma unroll
-        for (int v = 0; v < 4; ++v) wv[ht][v] = w[(size_t)rr * kH + 16 * ht + 4 * grp + v];
+      for (int s = 0; s < 4; ++s) {
+        const int off = (16 * ht + col) * (kD * 2) + 2 * dim0_of<ECH_KEY_BF16>(grp, s);
+        a[j][ht][s] = as_bf16x8(*reinterpret_cast<const uint4*>(qb + off));
       }
+#pragma unroll
+      for (int v = 0; v < 4; ++v) wv[j][ht][v] = w[(size_t)rr * kH + 16 * ht + 4 * grp + v];
     }
-    __syncthreads();
   }
 
   const uint8_t* kbase = kc + (size_t)tok0 * kRowB;
   const float* sbase = (KDT == ECH_KEY_FP8) ? ksc + tok0 : nullptr;
-  float* orow = out + (size_t)min(r, R - 1) * ld;
   const int ntiles = (span_end - span0 + kPTile - 1) / kPTile;
 
   Staged<KDT> nxt;
@@ -236,10 +241,12 @@ __global__ __launch_bounds__(kThreads) void logits_causal_kernel(
     // bf16 tiles are twice as large and are committed at once instead.
     if (more) stage_fetch<KDT>(nxt, kbase, sbase, t0 + kPTile, span_end - (t0 + kPTile));
     if (KDT == ECH_KEY_BF16 && more) stage_commit<KDT>(nxt, kt[cb ^ 1], st[cb ^ 1]);
-    const bool live = row_ok && t0 < vis;
+    bool live = false;
+#pragma unroll
+    for (int j = 0; j < RPW; ++j) live |= row_ok[j] && t0 < vis[j];
     if (live) {
-      // All four sub-tiles unconditionally; scores past the causal edge are
-      // computed but never stored.
+      // All four sub-tiles for every row of the wave; scores past a row's
+      // causal edge are computed but never stored.
 #pragma unroll
       for (int sub = 0; sub < kPTile / 16; ++sub) {
         const uint8_t* kr = kt[cb] + (sub * 16 + col) * kPStride;
@@ -247,14 +254,18 @@ __global__ __launch_bounds__(kThreads) void logits_causal_kernel(
 #pragma unroll
         for (int s = 0; s < 4; ++s)
           b[s] = as_bf16x8(*reinterpret_cast<const uint4*>(kr + 2 * dim0_of<ECH_KEY_BF16>(grp, s)));
-        sres[wave][sub * 16 + col] = tile_score(a, wv, b, st[cb][sub * 16 + col]);
+        const float sc = st[cb][sub * 16 + col];
+#pragma unroll
+        for (int j = 0; j < RPW; ++j) sres[wave * RPW + j][sub * 16 + col] = tile_score(a[j], wv[j], b, sc);
       }
     }
     if (KDT == ECH_KEY_FP8 && more) stage_commit<KDT>(nxt, kt[cb ^ 1], st[cb ^ 1]);
     __syncthreads();
-    // One coalesced 256-byte store of the wave's 64 scores per tile (four
+    // One coalesced 256-byte store of each row's 64 scores per tile (four
     // 64-byte partial-line stores cost write bandwidth).
-    if (live && t0 + lane < vis) orow[t0 + lane] = sres[wave][lane];
+#pragma unroll
+    for (int j = 0; j < RPW; ++j)
+      if (row_ok[j] && t0 + lane < vis[j]) orow[j][t0 + lane] = sres[wave * RPW + j][lane];
   }
 }
 
@@ -301,16 +312,17 @@ extern "C" int ech_index_logits_causal(const void* q, const float* w, const void
   if (ld < row0 + R || row0 + R > (int64_t)INT32_MAX) return ECH_EINVAL;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   const int64_t vis_max = row0 + R;
-  dim3 grid((R + kWaves - 1) / kWaves, (unsigned)((vis_max + kSpan - 1) / kSpan));
+  constexpr int kRPW = 2;   // query rows per wave
+  dim3 grid((R + kWaves * kRPW - 1) / (kWaves * kRPW), (unsigned)((vis_max + kSpan - 1) / kSpan));
   if (grid.y > 65535) return ECH_EINVAL;
   const uint16_t* qq = static_cast<const uint16_t*>(q);
   const uint8_t* kk = static_cast<const uint8_t*>(kcache);
   if (kdtype == ECH_KEY_FP8)
-    hipLaunchKernelGGL(logits_causal_kernel<ECH_KEY_FP8>, grid, dim3(kThreads), 0, s, qq, w, kk, kscale, tok0,
-                       row0, R, logits, ld);
+    hipLaunchKernelGGL((logits_causal_kernel<ECH_KEY_FP8, kRPW>), grid, dim3(kThreads), 0, s, qq, w, kk, kscale,
+                       tok0, row0, R, logits, ld);
   else
-    hipLaunchKernelGGL(logits_causal_kernel<ECH_KEY_BF16>, grid, dim3(kThreads), 0, s, qq, w, kk, kscale, tok0,
-                       row0, R, logits, ld);
+    hipLaunchKernelGGL((logits_causal_kernel<ECH_KEY_BF16, kRPW>), grid, dim3(kThreads), 0, s, qq, w, kk, kscale,
+                       tok0, row0, R, logits, ld);
   ECH_LAUNCH_CHECK();
   return ECH_OK;
 }
