@@ -46,6 +46,8 @@ def parse():
     p.add_argument('--topk-after-early', action='store_true', help='start the top-k after the EARLY maps')
     p.add_argument('--early-groups', type=int, default=0,
                    help='sequence groups of the early fetch (0: one EARLY phase after all scores)')
+    p.add_argument('--prefill-serial', action='store_true',
+                   help='prefill: one score buffer, top-k after each block on the same stream (ablation)')
     p.add_argument('--cpu-seqs', type=int, default=32, help='sequences in the oracle sample')
     p.add_argument('--cpu-steps', type=int, default=3, help='decode steps in the oracle sample')
     p.add_argument('--calibrate-copy', action='store_true',
@@ -309,7 +311,8 @@ def bench_prefill(args, wl):
     keys, scale = wk.keys(wl)
     pool = torch.empty((wl.P, wk.ROW_ELEMS), dtype=torch.int16, pin_memory=True)
     wk.host_rows(wl, out=pool.numpy().view(np.uint16))
-    layer = PrefillLayer(dev(keys), dev(scale), wl.N, wl.C, k=wl.k, block_rows=wl.block_rows, host_pool=pool)
+    layer = PrefillLayer(dev(keys), dev(scale), wl.N, wl.C, k=wl.k, block_rows=wl.block_rows, host_pool=pool,
+                         overlap=not args.prefill_serial)
     blocks = layer.blocks()
     q = [dev(wk.prefill_queries(wl, r0, R)) for r0, R in blocks]
     w = [dev(wk.head_weights(wl, rows=R, row0=r0)) for r0, R in blocks]
@@ -342,7 +345,8 @@ def bench_prefill(args, wl):
         'warmup': args.warmup, 'ms_per_step': wall / args.steps * 1e3, 'higher_is_better': True,
         'scaling': 'weak', 'vs_baseline': None, 'dtype': 'fp8-e4m3 keys, bf16 q, bf16 MFMA fp32 accumulation',
         'data': 'synthetic, seeded',
-        'config': {'workload': wl.name, 'N': wl.N, 'block_rows': wl.block_rows, 'k': wl.k, 'cache_slots': wl.C},
+        'config': {'workload': wl.name, 'N': wl.N, 'block_rows': wl.block_rows, 'k': wl.k, 'cache_slots': wl.C,
+                   'selection_beside_next_block': not args.prefill_serial},
         'roofline': {'bound': 'mfma', 'kernel': 'logits_causal_kernel', 'achieved': tflops,
                      'peak': PEAK_BF16_TFLOPS, 'unit': 'TFLOP/s', 'frac': tflops / PEAK_BF16_TFLOPS,
                      'traffic': None, 'algorithmic_flops_per_pass': flops, 'logits_ms_per_pass': logits_ms_total},

@@ -33,7 +33,6 @@ namespace {
 constexpr int kT = 256;
 constexpr int kPer = 16;
 constexpr int kBlk = kT * kPer;   // tokens or slots per block in ordered kernels
-constexpr int kST = 1024;         // scan kernel threads
 constexpr int kMaxK = 4096;
 constexpr int kMaxB = 1024;
 
@@ -270,19 +269,20 @@ __global__ __launch_bounds__(kT) void count_free_kernel(const int32_t* __restric
 // ------------------------------------------------------------------ scan
 constexpr int kStage = 4096;   // block counts staged in LDS by the scan kernel
 
-__global__ __launch_bounds__(kST) void scan_kernel(int phase, int B, int cap, int32_t C, int32_t* ctr,
+template <int NT>
+__global__ __launch_bounds__(NT) void scan_kernel(int phase, int B, int cap, int32_t C, int32_t* ctr,
                                                    int32_t* __restrict__ stats, CWs w) {
-  __shared__ int scr[kST / 64];
+  __shared__ int scr[NT / 64];
   __shared__ int s_want[kStage];
   __shared__ int s_hit[kStage];
   __shared__ int s_base;
-  // free slots: exclusive scan over slot blocks (chunks of kST)
+  // free slots: exclusive scan over slot blocks (chunks of NT)
   int nfree_tot = 0;
-  for (int b0 = 0; b0 < w.ns; b0 += kST) {
+  for (int b0 = 0; b0 < w.ns; b0 += NT) {
     const int i = b0 + threadIdx.x;
     const int v = i < w.ns ? w.nfree[i] : 0;
     int tot;
-    const int ex = ech::block_excl_scan<kST>(v, scr, &tot);
+    const int ex = ech::block_excl_scan<NT>(v, scr, &tot);
     if (i < w.ns) w.soff[i] = nfree_tot + ex;
     nfree_tot += tot;
   }
@@ -291,7 +291,7 @@ __global__ __launch_bounds__(kST) void scan_kernel(int phase, int B, int cap, in
   const int nseq = (phase == ECH_PREFILL) ? 1 : B;
   const bool staged = w.ne <= kStage;
   if (staged) {
-    for (int i = threadIdx.x; i < w.ne; i += kST) {
+    for (int i = threadIdx.x; i < w.ne; i += NT) {
       s_want[i] = w.want[i];
       s_hit[i] = w.hit[i];
     }
@@ -309,7 +309,7 @@ __global__ __launch_bounds__(kST) void scan_kernel(int phase, int B, int cap, in
   }
   const int take_b = (phase == ECH_EARLY) ? min(cap, want_b) : want_b;
   int n_want;
-  const int row_off = ech::block_excl_scan<kST>(b < nseq ? take_b : 0, scr, &n_want);
+  const int row_off = ech::block_excl_scan<NT>(b < nseq ? take_b : 0, scr, &n_want);
   const bool clamped = n_want > w.M_max;   // only when a caller contract is broken
   if (clamped) n_want = w.M_max;
   const int n_alloc = min(n_want, nfree_tot);
@@ -638,7 +638,12 @@ extern "C" int ech_cache_step(int phase, int32_t* tok2slot, int64_t P, int32_t* 
   ECH_LAUNCH_CHECK();
   hipLaunchKernelGGL(count_free_kernel, dim3(w.ns), dim3(kT), 0, s, slot_pin, C, ctr, w);
   ECH_LAUNCH_CHECK();
-  hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(kST), 0, s, phase, B, cap, C, ctr, stats, w);
+  // one thread per sequence: 1024 for decode batches, 256 for the single
+  // prefill sequence (fits beside other work on a CU)
+  if (phase == ECH_PREFILL)
+    hipLaunchKernelGGL(scan_kernel<256>, dim3(1), dim3(256), 0, s, phase, B, cap, C, ctr, stats, w);
+  else
+    hipLaunchKernelGGL(scan_kernel<1024>, dim3(1), dim3(1024), 0, s, phase, B, cap, C, ctr, stats, w);
   ECH_LAUNCH_CHECK();
   EmitArgs ea;
   ea.phase = phase;

@@ -37,7 +37,6 @@ namespace {
 constexpr int kChunk = 4096;        // tokens per chunk (T1, T3, T5)
 constexpr int kVec = kChunk / (4 * 256);   // float4 loads per thread
 constexpr int kT = 256;             // threads for chunk kernels
-constexpr int kRT = 1024;           // threads for the per-row resolve kernel
 constexpr int kMaxK = 4096;
 constexpr int kMaxChunks = 1024;    // max_len <= 4M
 
@@ -193,12 +192,13 @@ __global__ __launch_bounds__(kT) void topk_hist_kernel(const float* __restrict__
 }
 
 // ------------------------------------------------------------------ T2
-// 1024 threads: thread (part, b) sums bin (255 - b) over the chunks
-// c = part, part + 4, ..., eight independent loads in flight (a loop with one
-// load per iteration waits a full memory round trip per chunk).
-constexpr int kRowselT = 1024;
-
-__global__ __launch_bounds__(kRowselT) void topk_rowsel_kernel(const int32_t* __restrict__ lens, int k, Ws ws) {
+// NT threads (1024 for a few long rows, 256 for many rows): thread
+// (part, b) sums bin (255 - b) over the chunks c = part, part + NT/256, ...,
+// eight independent loads in flight (a loop with one load per iteration
+// waits a full memory round trip per chunk).
+template <int NT>
+__global__ __launch_bounds__(NT) void topk_rowsel_kernel(const int32_t* __restrict__ lens, int k, Ws ws) {
+  constexpr int kParts = NT / 256;
   const int r = blockIdx.x;
   const int len = lens[r];
   RowState& st = ws.rs[r];
@@ -212,24 +212,28 @@ __global__ __launch_bounds__(kRowselT) void topk_rowsel_kernel(const int32_t* __
     return;
   }
   const int nch = (len + kChunk - 1) / kChunk;
-  __shared__ int part_sum[4][256];
-  __shared__ int scratch[kRowselT / 64];
+  __shared__ int part_sum[kParts][256];
+  __shared__ int scratch[NT / 64];
   const int b = threadIdx.x & 255, part = threadIdx.x >> 8;
   const int bin = 255 - b;
   const int* h = ws.hist + (size_t)r * ws.nch * 256 + bin;
   int acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
   int c = part;
-  for (; c + 28 < nch; c += 32) {
+  for (; c + 7 * kParts < nch; c += 8 * kParts) {
 #pragma unroll
-    for (int u = 0; u < 8; ++u) acc[u] += h[(size_t)(c + 4 * u) * 256];
+    for (int u = 0; u < 8; ++u) acc[u] += h[(size_t)(c + kParts * u) * 256];
   }
-  for (; c < nch; c += 4) acc[0] += h[(size_t)c * 256];
+  for (; c < nch; c += kParts) acc[0] += h[(size_t)c * 256];
   part_sum[part][b] = acc[0] + acc[1] + acc[2] + acc[3] + acc[4] + acc[5] + acc[6] + acc[7];
   __syncthreads();
   // threads 0..255 hold bins 255..0 in order; the rest add zeros after them
-  const int cnt = (threadIdx.x < 256) ? part_sum[0][b] + part_sum[1][b] + part_sum[2][b] + part_sum[3][b] : 0;
+  int cnt = 0;
+  if (threadIdx.x < 256) {
+#pragma unroll
+    for (int pp = 0; pp < kParts; ++pp) cnt += part_sum[pp][b];
+  }
   int tot;
-  const int above = ech::block_excl_scan<kRowselT>(cnt, scratch, &tot);
+  const int above = ech::block_excl_scan<NT>(cnt, scratch, &tot);
   if (threadIdx.x < 256 && above < k && above + cnt >= k) {
     st.mode = kNormal;
     st.bstar = bin;
@@ -311,7 +315,8 @@ __device__ __forceinline__ void pick_digit(int* hist, int* sh, int need, int* ou
   __syncthreads();
 }
 
-__global__ __launch_bounds__(kRT) void topk_resolve_kernel(const float* __restrict__ logits, int64_t ld,
+template <int NT>
+__global__ __launch_bounds__(NT) void topk_resolve_kernel(const float* __restrict__ logits, int64_t ld,
                                                            const int32_t* __restrict__ lens, int k,
                                                            const float* __restrict__ theta_in,
                                                            float* __restrict__ theta_out, float* __restrict__ kth,
@@ -339,7 +344,7 @@ __global__ __launch_bounds__(kRT) void topk_resolve_kernel(const float* __restri
     }
     return;
   }
-  for (int c = threadIdx.x; c < nch; c += kRT) {
+  for (int c = threadIdx.x; c < nch; c += NT) {
     gt_c[c] = 0;
     eq_c[c] = 0;
   }
@@ -348,21 +353,21 @@ __global__ __launch_bounds__(kRT) void topk_resolve_kernel(const float* __restri
   if (mode == kAll) {
     // every visible token is selected; kth is the row minimum
     float m = __builtin_inff();
-    for (int t = threadIdx.x; t < len; t += kRT) m = fminf(m, row[t]);
+    for (int t = threadIdx.x; t < len; t += NT) m = fminf(m, row[t]);
     for (int d = 32; d > 0; d >>= 1) m = fminf(m, __shfl_xor(m, d, 64));
     float* wmin = reinterpret_cast<float*>(hist);
     if (ech::lane_id() == 0) wmin[threadIdx.x / 64] = m;
     __syncthreads();
     if (threadIdx.x == 0) {
       float mm = __builtin_inff();
-      for (int i = 0; i < kRT / 64; ++i) mm = fminf(mm, wmin[i]);
+      for (int i = 0; i < NT / 64; ++i) mm = fminf(mm, wmin[i]);
       s_min = mm;
     }
     __syncthreads();
     sstar = s_min;
     spred = -__builtin_inff();
     need_eq = 0;
-    for (int c = threadIdx.x; c < nch; c += kRT) gt_c[c] = min(kChunk, len - c * kChunk);
+    for (int c = threadIdx.x; c < nch; c += NT) gt_c[c] = min(kChunk, len - c * kChunk);
     __syncthreads();
   } else {
     const int cnt = st.cand;
@@ -373,16 +378,16 @@ __global__ __launch_bounds__(kRT) void topk_resolve_kernel(const float* __restri
     const uint32_t bstar = (uint32_t)st.bstar;
     if (in_lds) {
       const int2* src = ws.cand + (size_t)r * ws.cap;
-      for (int i = threadIdx.x; i < cnt; i += kRT) cl[i] = src[i];
+      for (int i = threadIdx.x; i < cnt; i += NT) cl[i] = src[i];
     }
     __syncthreads();
 #pragma unroll 1
     for (int round = 0; round < 4; ++round) {
       const int shift = 24 - 8 * round;
-      for (int i = threadIdx.x; i < 256; i += kRT) hist[i] = 0;
+      for (int i = threadIdx.x; i < 256; i += NT) hist[i] = 0;
       __syncthreads();
       if (in_lds) {
-        for (int i0 = 0; i0 < cnt; i0 += kRT) {
+        for (int i0 = 0; i0 < cnt; i0 += NT) {
           const int i = i0 + threadIdx.x;
           uint32_t key = 0;
           bool act = false;
@@ -393,7 +398,7 @@ __global__ __launch_bounds__(kRT) void topk_resolve_kernel(const float* __restri
           ech::lds_hist_add(hist, (key >> shift) & 255u, act);
         }
       } else {
-        for (int t0 = 0; t0 < len; t0 += kRT) {
+        for (int t0 = 0; t0 < len; t0 += NT) {
           const int t = t0 + threadIdx.x;
           uint32_t key = 0;
           bool act = false;
@@ -417,16 +422,16 @@ __global__ __launch_bounds__(kRT) void topk_resolve_kernel(const float* __restri
     need_eq = need;
     // per-chunk counts of tokens strictly above s* and equal to s*
     if (in_lds) {
-      for (int c = threadIdx.x; c < nch; c += kRT) gt_c[c] = ws.above[(size_t)r * ws.nch + c];
+      for (int c = threadIdx.x; c < nch; c += NT) gt_c[c] = ws.above[(size_t)r * ws.nch + c];
       __syncthreads();
-      for (int i = threadIdx.x; i < cnt; i += kRT) {
+      for (int i = threadIdx.x; i < cnt; i += NT) {
         const float x = __int_as_float(cl[i].x);
         const int c = cl[i].y / kChunk;
         if (x > sstar) atomicAdd(&gt_c[c], 1);
         else if (x == sstar) atomicAdd(&eq_c[c], 1);
       }
     } else {
-      for (int t = threadIdx.x; t < len; t += kRT) {
+      for (int t = threadIdx.x; t < len; t += NT) {
         const float x = row[t];
         if (x > sstar) atomicAdd(&gt_c[t / kChunk], 1);
         else if (x == sstar) atomicAdd(&eq_c[t / kChunk], 1);
@@ -528,12 +533,22 @@ extern "C" int ech_topk(const float* logits, int64_t ld, const int32_t* row_len,
   const dim3 gch(w.nch, R);
   hipLaunchKernelGGL(topk_hist_kernel, gch, dim3(kT), 0, s, logits, ld, row_len, k, theta_in, w);
   ECH_LAUNCH_CHECK();
-  hipLaunchKernelGGL(topk_rowsel_kernel, dim3(R), dim3(kRowselT), 0, s, row_len, k, w);
+  // A few long rows (decode) get 1024 threads per row; many rows (a prefill
+  // block) get 256, so the per-row kernels fit beside other work on a CU.
+  const bool wide = R <= 256;
+  if (wide)
+    hipLaunchKernelGGL(topk_rowsel_kernel<1024>, dim3(R), dim3(1024), 0, s, row_len, k, w);
+  else
+    hipLaunchKernelGGL(topk_rowsel_kernel<256>, dim3(R), dim3(256), 0, s, row_len, k, w);
   ECH_LAUNCH_CHECK();
   hipLaunchKernelGGL(topk_gather_kernel, gch, dim3(kT), 0, s, logits, ld, row_len, theta_in, w);
   ECH_LAUNCH_CHECK();
-  hipLaunchKernelGGL(topk_resolve_kernel, dim3(R), dim3(kRT), sizeof(int2) * w.cap, s, logits, ld, row_len, k,
-                     theta_in, theta_out, kth, w);
+  if (wide)
+    hipLaunchKernelGGL(topk_resolve_kernel<1024>, dim3(R), dim3(1024), sizeof(int2) * w.cap, s, logits, ld,
+                       row_len, k, theta_in, theta_out, kth, w);
+  else
+    hipLaunchKernelGGL(topk_resolve_kernel<256>, dim3(R), dim3(256), sizeof(int2) * w.cap, s, logits, ld, row_len,
+                       k, theta_in, theta_out, kth, w);
   ECH_LAUNCH_CHECK();
   hipLaunchKernelGGL(topk_compact_kernel, gch, dim3(kT), 0, s, logits, ld, row_len, k, idx, w);
   ECH_LAUNCH_CHECK();

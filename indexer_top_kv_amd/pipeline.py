@@ -287,15 +287,24 @@ class DecodeLayer:
 class PrefillLayer:
     """Causal prefill of one sequence in query blocks: logits -> per-row top-k
     -> PREFILL cache step (union) -> recall of block i on S1 while S0 scores
-    block i+1."""
+    block i+1.
+
+    With overlap=True the score buffer is doubled: S0 scores block i+1 into
+    one buffer while S1 runs block i's top-k and cache step on the other
+    (recalls on S2), so the selection work hides under the next block's
+    matrix-core work."""
 
     def __init__(self, kcache: torch.Tensor, kscale: Optional[torch.Tensor], N: int, C: int, k: int = 2048,
-                 block_rows: int = 4096, host_pool: Optional[torch.Tensor] = None, tok0: int = 0, device='cuda'):
+                 block_rows: int = 4096, host_pool: Optional[torch.Tensor] = None, tok0: int = 0,
+                 overlap: bool = False, device='cuda'):
         self.kcache, self.kscale = kcache, kscale
         self.N, self.C, self.k, self.block_rows, self.tok0 = N, C, k, block_rows, tok0
+        self.overlap = overlap
         dev = dict(device=device)
         self.ld = round_up(N, 64)
-        self.logits = torch.empty((block_rows, self.ld), dtype=torch.float32, **dev)
+        nbuf = 2 if overlap else 1
+        self.logits_buf = [torch.empty((block_rows, self.ld), dtype=torch.float32, **dev) for _ in range(nbuf)]
+        self.logits = self.logits_buf[0]
         self.idx = torch.empty((block_rows, k), dtype=torch.int32, **dev)
         self.kth = torch.empty(block_rows, dtype=torch.float32, **dev)
         self.theta = torch.full((block_rows,), float('nan'), dtype=torch.float32, **dev)
@@ -314,7 +323,11 @@ class PrefillLayer:
         self.dev_cache = (torch.zeros((C, host_pool.shape[1]), dtype=host_pool.dtype, **dev)
                           if host_pool is not None else None)
         self.s1 = torch.cuda.Stream(device=device)
+        self.s2 = torch.cuda.Stream(device=device) if overlap else None
         self.ev_recall = torch.cuda.Event()
+        self.ev_scored = [torch.cuda.Event() for _ in range(nbuf)]
+        self.ev_used = [torch.cuda.Event() for _ in range(nbuf)]
+        self.nblock = 0
         ech_cache_reset(self.state)
 
     def blocks(self):
@@ -324,6 +337,7 @@ class PrefillLayer:
         """Start the sequence again: empty cache, no threshold predictions."""
         ech_cache_reset(self.state)
         self.theta.fill_(float('nan'))
+        self.nblock = 0
 
     def _row_len(self, row0: int, R: int) -> torch.Tensor:
         key = (row0, R)
@@ -337,8 +351,12 @@ class PrefillLayer:
         the scoring launch."""
         s0 = torch.cuda.current_stream()
         R = q.shape[0]
-        logits = self.logits[:R]
+        buf = self.nblock % len(self.logits_buf) if self.overlap else 0
+        logits = self.logits_buf[buf][:R]
+        self.logits = self.logits_buf[buf]
         row_len = self._row_len(row0, R)
+        if self.overlap and self.nblock >= 2:
+            s0.wait_event(self.ev_used[buf])      # the top-k two blocks back has read this buffer
         if mark is not None:
             ev = torch.cuda.Event(enable_timing=True)
             ev.record(s0)
@@ -348,19 +366,32 @@ class PrefillLayer:
             ev = torch.cuda.Event(enable_timing=True)
             ev.record(s0)
             mark.append(ev)
+        self.nblock += 1
+        if self.overlap:
+            self.ev_scored[buf].record(s0)
+            sel = self.s1
+            sel.wait_event(self.ev_scored[buf])
+        else:
+            sel = s0
         # rows' thresholds: the EMA of the same row position in earlier blocks
         ech_topk(logits, row_len, row0 + R, self.k, self.theta[:R], self.theta[:R], self.idx[:R], self.kth[:R],
-                 self.ws_topk, stream=s0)
+                 self.ws_topk, stream=sel)
+        if self.overlap:
+            self.ev_used[buf].record(sel)
         if not first:
-            s0.wait_event(self.ev_recall)
+            sel.wait_event(self.ev_recall)
         ech_cache_step(ECH_PREFILL, self.state, self.seq_tok0, self.seq_len, self.N, idx=self.idx[:R], k=self.k,
-                       sel_slot=self.sel_slot[:R], stats=self.stats, ws=self.ws_cache, stream=s0)
+                       sel_slot=self.sel_slot[:R], stats=self.stats, ws=self.ws_cache, stream=sel)
         if self.host_pool is not None:
-            self.s1.wait_stream(s0)
-            ech_recall(self.host_pool, self.dev_cache, self.state, phase=ECH_PREFILL, stream=self.s1)
-            self.ev_recall.record(self.s1)
+            rs = self.s2 if self.overlap else self.s1
+            rs.wait_stream(sel)
+            ech_recall(self.host_pool, self.dev_cache, self.state, phase=ECH_PREFILL, stream=rs)
+            self.ev_recall.record(rs)
         else:
-            self.ev_recall.record(s0)
+            self.ev_recall.record(sel)
 
     def finish(self) -> None:
-        torch.cuda.current_stream().wait_event(self.ev_recall)
+        s0 = torch.cuda.current_stream()
+        s0.wait_event(self.ev_recall)
+        if self.overlap:
+            s0.wait_stream(self.s1)

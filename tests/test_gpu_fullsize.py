@@ -140,3 +140,43 @@ def test_prefill_full_size_all_blocks():
         assert np.all(t2s[~touched] == -1)
         np.testing.assert_array_equal(host(layer.sel_slot[:R]), np.where(idx >= 0, t2s[np.maximum(idx, 0)], -1))
         assert int(host(layer.state.ctr)[ech.CTR_STATUS]) == 0
+
+
+def test_prefill_overlapped_matches_serial():
+    """The double-buffered prefill (block i's top-k and slot-map step on a
+    second stream while block i+1 is scored, recalls on a third) against the
+    serial one, with no synchronisation between blocks: every block's
+    selection, the final maps and the device cache are identical."""
+    need_gpu()
+    wl = wk.CONFIGS['prefill-110k-fp8']
+    keys, scale = wk.keys(wl)
+    rows = torch.from_numpy(np.random.default_rng(5).integers(-30000, 30000, (wl.N, 64), dtype=np.int16))
+    pool = torch.empty((wl.N, 64), dtype=torch.int16, pin_memory=True)
+    pool.copy_(rows)
+    kd, sd = dev(keys), dev(scale)
+    blocks = None
+    results = []
+    for overlap in (False, True):
+        layer = PrefillLayer(kd, sd, wl.N, wl.C, k=wl.k, block_rows=wl.block_rows, host_pool=pool, overlap=overlap)
+        blocks = layer.blocks()
+        qs = [dev(wk.prefill_queries(wl, r0, R)) for r0, R in blocks]
+        ws = [dev(wk.head_weights(wl, rows=R, row0=r0)) for r0, R in blocks]
+        torch.cuda.synchronize()
+        saved = []
+        for bi, (r0, R) in enumerate(blocks):
+            layer.run_block(r0, qs[bi], ws[bi], first=(bi == 0))
+            sel_stream = layer.s1 if overlap else torch.cuda.current_stream()
+            with torch.cuda.stream(sel_stream):
+                saved.append(layer.idx[:R].clone())
+        layer.finish()
+        torch.cuda.synchronize()
+        results.append((saved, layer.state.tok2slot.clone(), layer.state.slot2tok.clone(), layer.dev_cache.clone(),
+                        int(host(layer.state.ctr)[ech.CTR_STATUS])))
+    (sa, t2a, s2a, ca, sta), (sb, t2b, s2b, cb, stb) = results
+    for bi in range(len(blocks)):
+        assert torch.equal(sa[bi], sb[bi]), f'block {bi}'
+    assert torch.equal(t2a, t2b) and torch.equal(s2a, s2b) and torch.equal(ca, cb)
+    assert sta == 0 and stb == 0
+    occ = host(s2b)
+    occ_slots = np.nonzero(occ >= 0)[0]
+    np.testing.assert_array_equal(host(cb)[occ_slots], pool.numpy()[occ[occ_slots]])
