@@ -102,22 +102,6 @@ size_t early_layout(int B, int max_len, int32_t C, int32_t M_early, EWs* w, char
   return o;
 }
 
-// True in exactly one block of the grid: the last to arrive. Call from every
-// thread after the block's results are stored; contains __syncthreads().
-__device__ __forceinline__ bool last_block(int32_t* ctr, int nblocks) {
-  __shared__ int s_last;
-  __threadfence();
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    const unsigned t = atomicInc(reinterpret_cast<unsigned*>(&ctr[ECH_CTR_TICKET]), (unsigned)(nblocks - 1));
-    s_last = (t == (unsigned)(nblocks - 1));
-  }
-  __syncthreads();
-  const bool last = s_last;
-  if (last) __threadfence();
-  return last;
-}
-
 // ------------------------------------------------------------------ begin: pin
 // grid (nch, B), 4 waves. Chunk c of sequence b covers tokens [c*kBlk, +kBlk).
 template <int KDT>
@@ -220,7 +204,7 @@ __global__ __launch_bounds__(kT) void early_free_kernel(const int32_t* __restric
   free_flags(slot_pin, C, head, ep, blockIdx.x * kBlk + threadIdx.x * kPer, fr, &n);
   const int tot = ech::block_sum<kT>(n, scr);
   if (threadIdx.x == 0) ws.nfree[blockIdx.x] = tot;
-  if (!last_block(ctr, gridDim.x)) return;
+  if (!ech::last_block(ctr, gridDim.x)) return;
   // free-slot rank of every block (ring order), total
   int run = 0;
   for (int b0 = 0; b0 < ws.ns; b0 += kT) {
@@ -326,7 +310,7 @@ __global__ __launch_bounds__(kT) void early_want_kernel(int group, int b0, const
   }
   const int tot = ech::block_sum<kT>(n, scr);
   if (threadIdx.x == 0) ws.want[(size_t)b * ws.nch + c] = tot;
-  if (!last_block(ctr, gridDim.x * gridDim.y)) return;
+  if (!ech::last_block(ctr, gridDim.x * gridDim.y)) return;
   // Rank ranges of the group's sequences, continuing earlier groups.
   // (a) exclusive prefix of the want counts over the group's blocks in
   //     (sequence, chunk) order, stored in off[]
