@@ -49,7 +49,7 @@ def parse():
     p.add_argument('--prefill-serial', action='store_true',
                    help='prefill: one score buffer, top-k after each block on the same stream (ablation)')
     p.add_argument('--cpu-seqs', type=int, default=32, help='sequences in the oracle sample')
-    p.add_argument('--cpu-steps', type=int, default=3, help='decode steps in the oracle sample')
+    p.add_argument('--cpu-steps', type=int, default=5, help='decode steps in the oracle sample')
     p.add_argument('--calibrate-copy', action='store_true',
                    help='only run a plain 1 GiB device copy 5 times (reference for HBM byte counters)')
     return p.parse_args()
@@ -63,9 +63,9 @@ def source_hash(*names):
     return h.hexdigest()[:16]
 
 
-def measured_traffic(kernel_key, src_hash):
-    """HBM bytes per launch from the committed rocprofv3 counter summary, if
-    it was taken on the current kernel source; else None."""
+def measured_traffic(kernel_key, src_hash, field='bytes_per_launch'):
+    """HBM bytes per launch (or per pass) from the committed rocprofv3 counter
+    summary, if it was taken on the current kernel source; else None."""
     path = os.path.join(ROOT, 'profiles', 'hbm_traffic.json')
     if not os.path.exists(path):
         return None
@@ -74,7 +74,7 @@ def measured_traffic(kernel_key, src_hash):
     e = d.get(kernel_key)
     if not e or e.get('source_hash') != src_hash:
         return None
-    return e.get('bytes_per_launch')
+    return e.get(field)
 
 
 def cpu_cores():
@@ -349,7 +349,10 @@ def bench_prefill(args, wl):
                    'selection_beside_next_block': not args.prefill_serial},
         'roofline': {'bound': 'mfma', 'kernel': 'logits_causal_kernel', 'achieved': tflops,
                      'peak': PEAK_BF16_TFLOPS, 'unit': 'TFLOP/s', 'frac': tflops / PEAK_BF16_TFLOPS,
-                     'traffic': None, 'algorithmic_flops_per_pass': flops, 'logits_ms_per_pass': logits_ms_total},
+                     'traffic': measured_traffic('logits_causal_' + wl.name, source_hash('logits.hip', 'score.hpp'),
+                                                 'bytes_per_pass'),
+                     'traffic_unit': 'bytes per pass (27 launches)',
+                     'algorithmic_flops_per_pass': flops, 'logits_ms_per_pass': logits_ms_total},
     }
 
 
