@@ -115,6 +115,17 @@ def test_dyadic_decode_fp8_batch_grouped_early():
     _run_bit_exact(wl, 5, early_groups=3)
 
 
+@pytest.mark.parametrize('early_groups', [0, 3])
+def test_dyadic_decode_short_and_long_sequences(early_groups):
+    """Ragged lengths from 1 token up, several no longer than k (those rows
+    select every token and cannot miss the top-k), in one chunk."""
+    need_gpu()
+    wl = wk.CONFIGS['decode-64x110k-fp8-capacity'].scaled(B=6, N=3000, len_lo=1, C=7000, k=1024, cap=128,
+                                                          steps=4, resample_p=0.0, variant='dyadic')
+    assert (wl.lens <= wl.k).any() and (wl.lens > wl.k).any()
+    _run_bit_exact(wl, 4, early_groups=early_groups)
+
+
 def test_dyadic_decode_bf16_small_cache():
     need_gpu()
     wl = wk.CONFIGS['decode-1x16k-bf16'].scaled(N=6000, C=2100, variant='dyadic')
