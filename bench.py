@@ -151,11 +151,12 @@ def bench_decode(args, wl):
     torch.cuda.synchronize()
 
     def avg_ms(name):
+        """Time per step of a stage (summed over the chunks of a step)."""
         ev = marks.get(name, [])
         if not ev:
             return None
         d = [ev[i].elapsed_time(ev[i + 1]) for i in range(0, len(ev), 2)]
-        return float(np.mean(d))
+        return float(np.sum(d)) / n_stage
 
     wall = t1 - t0
     tokens = int(wl.lens.astype(np.int64).sum())

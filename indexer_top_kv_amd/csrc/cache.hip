@@ -535,8 +535,8 @@ __global__ void reset_kernel(int32_t* tok2slot, int64_t P, int32_t* slot2tok, in
   if (blockIdx.x == 0 && threadIdx.x < ECH_CTR_LEN) ctr[threadIdx.x] = 0;
 }
 
-constexpr int kRecallUnroll = 4;
-constexpr int kRecallBlocks = 64;
+constexpr int kRecallUnroll = 8;
+constexpr int kRecallBlocks = 48;
 typedef uint32_t v4u __attribute__((ext_vector_type(4)));
 
 __global__ __launch_bounds__(kT) void recall_kernel(const v4u* __restrict__ host, int64_t P, int row16,
@@ -689,9 +689,10 @@ extern "C" int ech_recall(int phase, const void* host_pool, int64_t P, int64_t r
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   const int row16 = (int)(row_bytes / 16);
   const int64_t work = (int64_t)M_max * row16;
-  // A PCIe-bound gather needs only ~1-2 MB of loads in flight (128 blocks x
-  // 256 threads x 4 x 16 B = 2 MB); more blocks would just park waves on
-  // host loads and keep the kernels of the other stream off the CUs.
+  // A PCIe-bound gather needs only ~1-2 MB of loads in flight (48 blocks x
+  // 256 threads x 8 x 16 B = 1.5 MB, the best of the shapes measured in the
+  // decode step); more blocks would just park waves on host loads and keep
+  // the kernels of the other stream off the CUs.
   const int blocks = (int)std::max<int64_t>(1, std::min<int64_t>(kRecallBlocks, (work + kT * kRecallUnroll - 1) /
                                                                                     (kT * kRecallUnroll)));
   hipLaunchKernelGGL(recall_kernel, dim3(blocks), dim3(kT), 0, s, static_cast<const v4u*>(dptr), P, row16,

@@ -422,8 +422,8 @@ __global__ __launch_bounds__(kT) void early_apply_kernel(int group, int b0, cons
 }
 
 // ------------------------------------------------------------------ recall of a group
-constexpr int kRecallUnroll = 4;
-constexpr int kRecallBlocks = 64;
+constexpr int kRecallUnroll = 8;
+constexpr int kRecallBlocks = 48;
 typedef uint32_t v4u __attribute__((ext_vector_type(4)));
 
 __global__ __launch_bounds__(kT) void recall_range_kernel(const v4u* __restrict__ host, int64_t P, int row16,

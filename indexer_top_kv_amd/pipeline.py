@@ -148,10 +148,6 @@ class DecodeLayer:
         if self.host_pool is not None:
             ech_recall(self.host_pool, self.dev_cache, self.state, phase=phase, stream=stream)
 
-    def _phase(self, phase: int, b0: int, b1: int, theta: torch.Tensor, stream) -> None:
-        self._maps(phase, b0, b1, theta, stream)
-        self._recall(phase, stream)
-
     def logits_only(self, q: torch.Tensor, stream=None) -> None:
         ech_index_logits(q, self.w, self.kcache, self.kscale, self.tok0, self.lens, self.max_len, self.logits,
                          stream=stream)
@@ -161,8 +157,9 @@ class DecodeLayer:
         current stream (with S1 forked and joined inside). `marks`, when given,
         receives timing events recorded on the stream of each stage, as
         (start, end) pairs: logits, topk, final (S0: FINAL maps to the end of
-        its recall), early (S1: EARLY maps and recall), and inside those
-        early_maps, recall_early, final_maps, recall_final."""
+        the step), early (S1: EARLY maps and recall of the first chunk), and
+        early_maps, recall_early, final_maps, recall_final (one pair per
+        chunk)."""
         s0 = torch.cuda.current_stream()
 
         def mark(name, stream):
@@ -217,9 +214,14 @@ class DecodeLayer:
         self._recall(ECH_FINAL, s0)
         mark('recall_final', s0)
         for b0, b1 in self.chunks[1:]:
-            if self.early:
-                self._phase(ECH_EARLY, b0, b1, th, s0)
-            self._phase(ECH_FINAL, b0, b1, th, s0)
+            for phase in ((ECH_EARLY, ECH_FINAL) if self.early else (ECH_FINAL,)):
+                name = 'early' if phase == ECH_EARLY else 'final'
+                mark(name + '_maps', s0)
+                self._maps(phase, b0, b1, th, s0)
+                mark(name + '_maps', s0)
+                mark('recall_' + name, s0)
+                self._recall(phase, s0)
+                mark('recall_' + name, s0)
         mark('final', s0)
         self.parity ^= 1
 
