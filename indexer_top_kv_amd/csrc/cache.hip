@@ -10,7 +10,7 @@
 //            epoch (slot_pin[s] = epoch) and count hits / wanted misses per
 //            block. EARLY: tokens with score > theta; FINAL: idx entries;
 //            PREFILL: idx entries of all rows, misses claimed once per token
-//            with an atomic CAS tok2slot -1 -> -2 (union), then counted by a
+//            by marking tok2slot -1 -> -2 (union), then counted by a
 //            token scan.
 //   free     count unpinned slots per block in ring order from the head.
 //   scan     one workgroup: exclusive scans of the block counts give every
@@ -204,8 +204,11 @@ __global__ __launch_bounds__(kT) void pin_early_kernel(const float* __restrict__
   }
 }
 
-// PREFILL: grid (nbj, R). Pins resident tokens of every row; claims each
-// missing token once (tok2slot -1 -> -2) so the union has no duplicates.
+// PREFILL: grid (nbj, R). Pins resident tokens of every row; marks each
+// missing token as claimed (tok2slot -1 -> -2) so the union has no
+// duplicates. Many rows select the same tokens; a plain store suffices since
+// every claimer stores the same value and nothing else writes these entries
+// during the kernel (an atomic compare-and-swap serialised the duplicates).
 __global__ __launch_bounds__(kT) void pin_prefill_kernel(const int32_t* __restrict__ idx, int k,
                                                          const int64_t* __restrict__ tok0p,
                                                          const int32_t* __restrict__ lenp,
@@ -225,7 +228,7 @@ __global__ __launch_bounds__(kT) void pin_prefill_kernel(const int32_t* __restri
   const int ep = ctr[ECH_CTR_EPOCH] + 1;
   const int sl = tok2slot[g];
   if (sl >= 0 && sl < w.C) slot_pin[sl] = ep;
-  else if (sl == -1) atomicCAS(&tok2slot[g], -1, -2);
+  else if (sl == -1) tok2slot[g] = -2;   // every claimer writes the same value: no atomic needed
 }
 
 // PREFILL: grid (nch), count claimed tokens per block of the token range.
