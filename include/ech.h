@@ -84,7 +84,7 @@ extern "C" {
 /* Human-readable name of a return code. */
 const char* ech_status_str(int code);
 
-/* Library ABI version (major*100 + minor). */
+/* Library ABI version (major*100 + minor); 101 adds the grouped early-fetch calls. */
 int ech_version(void);
 
 /*

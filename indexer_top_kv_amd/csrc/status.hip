@@ -12,4 +12,4 @@ extern "C" const char* ech_status_str(int code) {
   }
 }
 
-extern "C" int ech_version(void) { return 100; }
+extern "C" int ech_version(void) { return 101; }   // 1.1: grouped early-fetch entry points
