@@ -187,7 +187,8 @@ def bench_decode(args, wl):
                    'key_dtype': wl.kdtype, 'cache_slots': wl.C, 'early_fetch_cap': wl.cap,
                    'early_fetch': not args.no_early, 'early_groups': len(layer.groups), 'row_bytes': 1152,
                    'launch': 'eager' if args.eager else 'hipGraph replay per step'},
-        'roofline': {'bound': 'hbm', 'kernel': 'logits_decode_kernel', 'achieved': achieved,
+        'roofline': {'bound': 'hbm', 'kernel': 'logits_decode_fp8_kernel' if wl.kdtype == 'fp8' else 'logits_decode_kernel',
+                     'achieved': achieved,
                      'peak': PEAK_HBM_GBS, 'unit': 'GB/s', 'frac': achieved / PEAK_HBM_GBS,
                      'traffic': traffic, 'algorithmic_bytes_per_launch': per_launch,
                      'avg_launch_us': logits_ms * 1e3,

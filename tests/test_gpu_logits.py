@@ -115,6 +115,37 @@ def test_fp8_full_size_decode_sampled():
         assert e.max() <= min(TOL_FP8, ARITH_BOUND), (r, float(e.max()))
 
 
+def test_fp8_ragged_at_full_launch_shape():
+    """32 rows of the 32 x 131072 launch shape (2048 tokens per workgroup,
+    512 per wave) with ragged lengths ending inside a tile, on tile, wave and
+    workgroup edges and after one token, and key offsets that are not
+    multiples of 8 rows: every row's first and last 64 scores, the scores
+    around each 512-token wave edge and 2048 sampled ones against the
+    oracle; nothing past a row's end is written."""
+    need_gpu()
+    wl = wk.CONFIGS['decode-32x128k-fp8']
+    keys, scale = wk.keys(wl)
+    q = next(wk.decode_queries(wl))
+    w = wk.head_weights(wl)
+    rng = np.random.default_rng(17)
+    edge = [1, 15, 16, 17, 511, 512, 513, 2047, 2048, 2049, 4095, 131072, 131071, 100003]
+    lens = np.concatenate([edge, rng.integers(1, wl.N + 1, wl.B - len(edge))]).astype(np.int32)
+    lens[wl.B - 1] = wl.N                          # keeps max_len (and so the launch shape) at 131072
+    P = keys.shape[0]
+    tok0 = np.array([min(int(wl.tok0[r]) + 37 * r + 3, P - int(lens[r])) for r in range(wl.B)], np.int64)
+    got = run_logits(q, w, keys, scale, tok0, lens)
+    for r in range(wl.B):
+        n = int(lens[r])
+        assert np.all(np.isnan(got[r, n:])), r
+        sel = np.unique(np.concatenate([np.arange(min(n, 64)), np.arange(max(0, n - 64), n),
+                                        np.array([t for e in range(512, n, 512) for t in (e - 1, e) if t < n], np.int64),
+                                        rng.integers(0, n, 64)]).astype(np.int64))
+        ref = oracle.index_logit_at(q[r], w[r], keys, 'fp8', scale, tok0[r] + sel)
+        scale_r = max(np.abs(ref).max(), np.abs(got[r, :n]).max())
+        e = np.abs(got[r, sel] - ref) / np.maximum(np.abs(ref), 1e-2 * scale_r)
+        assert e.max() <= min(TOL_FP8, ARITH_BOUND), (r, n, float(e.max()))
+
+
 def _causal(wl, keys, scale, row0, R):
     q = wk.prefill_queries(wl, row0, R)
     w = wk.head_weights(wl, rows=R, row0=row0)
