@@ -307,6 +307,7 @@ def bench_prefill(args, wl):
     import numpy as np
     import torch
     import workloads as wk
+    import indexer_top_kv_amd as ech
     from indexer_top_kv_amd.pipeline import PrefillLayer
 
     dev = lambda x: torch.from_numpy(np.ascontiguousarray(x.view(np.int16) if x.dtype == np.uint16 else x)).cuda()
@@ -320,11 +321,13 @@ def bench_prefill(args, wl):
     w = [dev(wk.head_weights(wl, rows=R, row0=r0)) for r0, R in blocks]
     log(f'{len(blocks)} query blocks staged')
     marks = []
+    stage_marks = {}
 
     def one_pass(timed):
         layer.reset_state()
         for i, (r0, R) in enumerate(blocks):
-            layer.run_block(r0, q[i], w[i], first=(i == 0), mark=marks if timed else None)
+            layer.run_block(r0, q[i], w[i], first=(i == 0), mark=marks if timed else None,
+                            stage_marks=stage_marks if timed else None)
         layer.finish()
 
     for _ in range(args.warmup):
@@ -340,6 +343,31 @@ def bench_prefill(args, wl):
     logits_ms_total = float(np.sum(lg)) / args.steps
     flops = pairs * 2 * 64 * 128
     tflops = flops / (logits_ms_total * 1e-3) / 1e12
+
+    def stage_ms(name):
+        ev = stage_marks.get(name, [])
+        return float(np.sum([ev[i].elapsed_time(ev[i + 1]) for i in range(0, len(ev), 2)])) / args.steps
+
+    # top-k: one read of every visible score plus the index output, per pass
+    topk_bytes = pairs * 4 + sum(R for _, R in blocks) * wl.k * 4
+    topk_ms = stage_ms('topk')
+    recalled = int(layer.state.ctr[ech.CTR_RECALLED].item())   # counted since the pass's reset
+    recall_ms = stage_ms('recall')
+    h2d = pcie_check(pool, wl.C)['h2d_memcpy_GBs']
+    stages = {
+        'topk': {'bound': 'hbm', 'algorithmic_bytes_per_pass': topk_bytes, 'ms_per_pass': topk_ms,
+                 'achieved_GBs': topk_bytes / (topk_ms * 1e-3) / 1e9 if topk_ms else None, 'peak_GBs': PEAK_HBM_GBS,
+                 'frac': topk_bytes / (topk_ms * 1e-3) / 1e9 / PEAK_HBM_GBS if topk_ms else None,
+                 'note': 'one read of the visible scores plus the index output; the five top-k launches of each '
+                         'block, timed on their stream' + ('' if args.prefill_serial else
+                                                           ' (beside the next block\'s scoring)')},
+        'cache_step_ms_per_pass': stage_ms('cache'),
+        'recall': {'bound': 'pcie', 'ms_per_pass': recall_ms, 'h2d_memcpy_GBs': h2d,
+                   'rows_per_pass': recalled,
+                   'achieved_GBs': recalled * 1152 / (recall_ms * 1e-3) / 1e9 if recalled and recall_ms else None,
+                   'frac_of_memcpy': recalled * 1152 / (recall_ms * 1e-3) / 1e9 / h2d if recalled and recall_ms
+                   else None},
+    }
     return {
         'metric': 'prefill (row, token) pairs scored/s (causal indexer logits + per-row exact top-k + '
                   'union slot-map step + overlapped recall), 1 layer',
@@ -355,6 +383,7 @@ def bench_prefill(args, wl):
                                                  'bytes_per_pass'),
                      'traffic_unit': 'bytes per pass (27 launches)',
                      'algorithmic_flops_per_pass': flops, 'logits_ms_per_pass': logits_ms_total},
+        'stage_rooflines': stages,
     }
 
 

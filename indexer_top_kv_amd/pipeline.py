@@ -347,10 +347,20 @@ class PrefillLayer:
             self._row_lens[key] = self.row_len[:R] + row0
         return self._row_lens[key]
 
-    def run_block(self, row0: int, q: torch.Tensor, w: torch.Tensor, first: bool, mark=None) -> None:
+    def run_block(self, row0: int, q: torch.Tensor, w: torch.Tensor, first: bool, mark=None,
+                  stage_marks: Optional[dict] = None) -> None:
         """q [R,64,128], w [R,64] for rows row0 .. row0+R-1, on the current
         stream. `mark`, when given, receives a (start, end) event pair around
-        the scoring launch."""
+        the scoring launch; `stage_marks`, when given, receives (start, end)
+        pairs recorded on each stage's own stream under 'topk', 'cache' and
+        'recall'."""
+
+        def smark(name, stream):
+            if stage_marks is not None:
+                ev = torch.cuda.Event(enable_timing=True)
+                ev.record(stream)
+                stage_marks.setdefault(name, []).append(ev)
+
         s0 = torch.cuda.current_stream()
         R = q.shape[0]
         buf = self.nblock % len(self.logits_buf) if self.overlap else 0
@@ -376,18 +386,24 @@ class PrefillLayer:
         else:
             sel = s0
         # rows' thresholds: the EMA of the same row position in earlier blocks
+        smark('topk', sel)
         ech_topk(logits, row_len, row0 + R, self.k, self.theta[:R], self.theta[:R], self.idx[:R], self.kth[:R],
                  self.ws_topk, stream=sel)
+        smark('topk', sel)
         if self.overlap:
             self.ev_used[buf].record(sel)
         if not first:
             sel.wait_event(self.ev_recall)
+        smark('cache', sel)
         ech_cache_step(ECH_PREFILL, self.state, self.seq_tok0, self.seq_len, self.N, idx=self.idx[:R], k=self.k,
                        sel_slot=self.sel_slot[:R], stats=self.stats, ws=self.ws_cache, stream=sel)
+        smark('cache', sel)
         if self.host_pool is not None:
             rs = self.s2 if self.overlap else self.s1
             rs.wait_stream(sel)
+            smark('recall', rs)
             ech_recall(self.host_pool, self.dev_cache, self.state, phase=ECH_PREFILL, stream=rs)
+            smark('recall', rs)
             self.ev_recall.record(rs)
         else:
             self.ev_recall.record(sel)
