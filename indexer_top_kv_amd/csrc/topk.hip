@@ -14,19 +14,23 @@
 //               larger scores.
 //   T2 rowsel   grid (R): sum the chunk histograms, boundary bin b* where the
 //               count from the top reaches k, need = k - count above b*.
-//   T3 gather   grid (chunks, R): count tokens above b* per chunk; append the
-//               b* tokens (score, t) to a per-row candidate list.
-//   T4 resolve  grid (R): radix-select need-th largest score among the
-//               candidates in LDS (4 rounds of 8 bits of ord(s)); per-chunk
-//               counts of ">" and "==" tokens give output offsets. If the
-//               boundary bin overflowed the list (no or poor theta), the same
-//               radix rounds run over the whole row instead. Writes kth and
-//               the EMA update of theta.
-//   T5 compact  grid (chunks, R): each chunk writes its selected tokens in
-//               ascending order at its offset; rows shorter than k are padded
-//               with -1.
+//               The chunk histograms also give, per chunk, the number of
+//               tokens in bins >= b*, hence each chunk's offset in T3's list.
+//   T3 list     grid (chunks, R): every token in a bin >= b* is written, in
+//               token order, to the row's list at its chunk's offset (block
+//               scans, no atomics): the tokens certainly selected and the
+//               boundary-bin tokens, at most k + cap entries.
+//   T4 resolve  grid (R): radix-select the need-th largest score among the
+//               list's b* entries in LDS (4 rounds of 8 bits of ord(s)), then
+//               write the selection in token order by one ordered pass over
+//               the list. Writes kth and the EMA update of theta.
+//   T5 compact  grid (chunks, R): only for rows the list does not serve:
+//               rows no longer than k (all tokens; padded with -1) and rows
+//               whose boundary bin holds more than cap tokens (no or poor
+//               theta), for which T4 ran the radix rounds over the whole row
+//               and left per-chunk offsets.
 // A good theta puts only a few hundred tokens in b* (bins are logarithmic
-// around the threshold), so T4 works in LDS and the row is read three times.
+// around the threshold), so the row is read twice (T1, T3).
 
 #include <algorithm>
 
@@ -35,30 +39,33 @@
 namespace {
 
 constexpr int kChunk = 4096;        // tokens per chunk (T1, T3, T5)
+static_assert(kChunk == 4 * 4 * 256, "four float4 loads per thread per chunk");
 constexpr int kVec = kChunk / (4 * 256);   // float4 loads per thread
 constexpr int kT = 256;             // threads for chunk kernels
 constexpr int kMaxK = 4096;
 constexpr int kMaxChunks = 1024;    // max_len <= 4M
 
-enum RowMode : int { kNormal = 0, kAll = 1, kEmpty = 2 };
+// kNormal: resolved from T3's list. kWide: the boundary bin holds more than
+// cap tokens; resolved over the whole row, compacted by T5.
+enum RowMode : int { kNormal = 0, kAll = 1, kEmpty = 2, kWide = 3 };
 
 struct RowState {
   int mode;
   int bstar;
-  int need;
-  int cand;      // candidates appended (may exceed the list capacity)
-  float spred;   // scores > spred are selected (-inf in kAll mode)
+  int need;      // rank of the k-th token within b*
+  int nlist;     // list entries (tokens in bins >= b*)
+  float spred;   // T5: scores > spred are selected (-inf in kAll mode)
   int pad[3];
 };
 
 struct Ws {
   RowState* rs;
   int* hist;     // [R][nch][256]
-  int* above;    // [R][nch]
-  int* off;      // [R][nch]
+  int* off;      // [R][nch] list offsets (kNormal) or output offsets (T5 rows)
   int* take;     // [R][nch]
-  int2* cand;    // [R][cap]
-  int cap;
+  int2* list;    // [R][lcap] (score bits, token)
+  int cap;       // largest boundary bin served by the list
+  int lcap;      // k + cap, rounded up to 8 entries
   int nch;
 };
 
@@ -66,9 +73,10 @@ size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 int cand_cap(int R) { return R <= 256 ? 16384 : 4096; }
 
-size_t layout(int R, int max_len, Ws* w, char* base) {
+size_t layout(int R, int max_len, int k, Ws* w, char* base) {
   const int nch = std::max(1, (max_len + kChunk - 1) / kChunk);
   const int cap = cand_cap(R);
+  const int lcap = (k + cap + 7) & ~7;   // rows of the list stay 64-byte aligned
   size_t o = 0;
   auto take = [&](size_t bytes) {
     size_t at = o;
@@ -77,18 +85,17 @@ size_t layout(int R, int max_len, Ws* w, char* base) {
   };
   size_t o_rs = take(sizeof(RowState) * R);
   size_t o_hist = take(sizeof(int) * (size_t)R * nch * 256);
-  size_t o_above = take(sizeof(int) * (size_t)R * nch);
   size_t o_off = take(sizeof(int) * (size_t)R * nch);
   size_t o_take = take(sizeof(int) * (size_t)R * nch);
-  size_t o_cand = take(sizeof(int2) * (size_t)R * cap);
+  size_t o_list = take(sizeof(int2) * (size_t)R * lcap);
   if (w && base) {
     w->rs = reinterpret_cast<RowState*>(base + o_rs);
     w->hist = reinterpret_cast<int*>(base + o_hist);
-    w->above = reinterpret_cast<int*>(base + o_above);
     w->off = reinterpret_cast<int*>(base + o_off);
     w->take = reinterpret_cast<int*>(base + o_take);
-    w->cand = reinterpret_cast<int2*>(base + o_cand);
+    w->list = reinterpret_cast<int2*>(base + o_list);
     w->cap = cap;
+    w->lcap = lcap;
     w->nch = nch;
   }
   return o;
@@ -211,13 +218,14 @@ __global__ __launch_bounds__(NT) void topk_rowsel_kernel(const int32_t* __restri
       st.mode = len == 0 ? kEmpty : kAll;
       st.bstar = 0;
       st.need = 0;
-      st.cand = 0;
+      st.nlist = 0;
     }
     return;
   }
   const int nch = (len + kChunk - 1) / kChunk;
   __shared__ int part_sum[kParts][256];
   __shared__ int scratch[NT / 64];
+  __shared__ int s_bstar, s_nbin;
   const int b = threadIdx.x & 255, part = threadIdx.x >> 8;
   const int bin = 255 - b;
   const int* h = ws.hist + (size_t)r * ws.nch * 256 + bin;
@@ -239,60 +247,134 @@ __global__ __launch_bounds__(NT) void topk_rowsel_kernel(const int32_t* __restri
   int tot;
   const int above = ech::block_excl_scan<NT>(cnt, scratch, &tot);
   if (threadIdx.x < 256 && above < k && above + cnt >= k) {
-    st.mode = kNormal;
+    s_bstar = bin;
+    s_nbin = cnt;
     st.bstar = bin;
     st.need = k - above;
-    st.cand = 0;
   }
+  __syncthreads();
+  const int bstar = s_bstar;
+  const bool wide = s_nbin > ws.cap;
+  if (threadIdx.x == 0) st.mode = wide ? kWide : kNormal;
+  if (wide) return;
+  // List offsets: chunk c holds sum over bins >= b* of its histogram. Four
+  // adjacent threads share a chunk (16 int4 loads each, all in flight).
+  int run = 0;
+  const int sub = threadIdx.x & 3;
+  for (int c0 = 0; c0 < nch; c0 += NT / 4) {
+    const int c = c0 + (int)threadIdx.x / 4;
+    int n = 0;
+    if (c < nch) {
+      const int4* hc = reinterpret_cast<const int4*>(ws.hist + ((size_t)r * ws.nch + c) * 256) + 16 * sub;
+      int4 q[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) q[i] = hc[i];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int b0 = 64 * sub + 4 * i;
+        n += (b0 >= bstar ? q[i].x : 0) + (b0 + 1 >= bstar ? q[i].y : 0) + (b0 + 2 >= bstar ? q[i].z : 0) +
+             (b0 + 3 >= bstar ? q[i].w : 0);
+      }
+    }
+    n += __shfl_xor(n, 1, 64);
+    n += __shfl_xor(n, 2, 64);
+    int t;
+    const int pre = ech::block_excl_scan<NT>(sub == 0 ? n : 0, scratch, &t);
+    if (c < nch && sub == 0) ws.off[(size_t)r * ws.nch + c] = run + pre;
+    run += t;
+  }
+  if (threadIdx.x == 0) st.nlist = run;
 }
 
 // ------------------------------------------------------------------ T3
-__global__ __launch_bounds__(kT) void topk_gather_kernel(const float* __restrict__ logits, int64_t ld,
-                                                         const int32_t* __restrict__ lens,
-                                                         const float* __restrict__ theta, Ws ws) {
+// Wave w of the block takes tokens [lo + 1024w, +1024) of the chunk: load j
+// of lane l covers tokens +256j + 4l .. +3 (each instruction still reads a
+// contiguous 1 KiB). The listing order (wave, j, lane, element) is the token
+// order, so ranks come from wave scans and one exchange of wave totals.
+__global__ __launch_bounds__(kT) void topk_list_kernel(const float* __restrict__ logits, int64_t ld,
+                                                       const int32_t* __restrict__ lens,
+                                                       const float* __restrict__ theta, Ws ws) {
   const int r = blockIdx.y, c = blockIdx.x;
   const int len = lens[r];
   const int lo = c * kChunk;
   if (lo >= len) return;
   const int hi = min(lo + kChunk, len);
+  const int lane = ech::lane_id(), wave = threadIdx.x >> 6;
+  const float* row = logits + (size_t)r * ld;
+  const int wlo = lo + 1024 * wave;
   // scores first, so their latency overlaps that of the row state
-  float4 v[kVec];
-  load_chunk(logits + (size_t)r * ld, lo, hi, v);
+  float4 v[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int t = wlo + 256 * j + 4 * lane;
+    if (t + 3 < hi) {
+      typedef float f4v __attribute__((ext_vector_type(4)));
+      const f4v x = __builtin_nontemporal_load(reinterpret_cast<const f4v*>(row + t));
+      v[j] = make_float4(x.x, x.y, x.z, x.w);
+    } else {
+      v[j] = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (t < hi) v[j].x = row[t];
+      if (t + 1 < hi) v[j].y = row[t + 1];
+      if (t + 2 < hi) v[j].z = row[t + 2];
+    }
+  }
   const RowState st = ws.rs[r];
+  const int o = ws.off[(size_t)r * ws.nch + c];   // loaded beside the row state
   if (st.mode != kNormal) return;
   const Shift sh = make_shift(row_theta(theta, r));
   const uint32_t bstar = (uint32_t)st.bstar;
-  int2* cand = ws.cand + (size_t)r * ws.cap;
-  int* cnt = &ws.rs[r].cand;
-  const int lane = ech::lane_id();
-  __shared__ int scratch[kT / 64];
-  int above = 0;
+  __shared__ int wtot[kT / 64];
+  // The chunk's entries are gathered in LDS and leave as consecutive 8-byte
+  // stores: written one by one from the lanes that hold them they cost more
+  // than the whole read of the chunk. Chunks with more entries than the
+  // buffer (rows barely longer than k) write directly.
+  constexpr int kStage = 1024;
+  __shared__ int2 stage[kStage];
+  uint32_t in = 0;   // bit 4j + e: element e of load j is in a bin >= b*
 #pragma unroll
-  for (int j = 0; j < kVec; ++j) {
-    const int t0 = lo + 4 * (j * kT + (int)threadIdx.x);
+  for (int j = 0; j < 4; ++j) {
+    const int t = wlo + 256 * j + 4 * lane;
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      in |= (t + e < hi && shifted_bin(f4(v[j], e), sh) >= bstar) ? 1u << (4 * j + e) : 0u;
+  }
+  int n[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) n[j] = __popc((in >> (4 * j)) & 15u);
+  const int i01 = ech::wave_incl_scan(n[0] | (n[1] << 16));
+  const int i23 = ech::wave_incl_scan(n[2] | (n[3] << 16));
+  const int t01 = __shfl(i01, 63, 64), t23 = __shfl(i23, 63, 64);
+  const int p01 = i01 - (n[0] | (n[1] << 16)), p23 = i23 - (n[2] | (n[3] << 16));
+  const int tj[4] = {t01 & 0xffff, t01 >> 16, t23 & 0xffff, t23 >> 16};
+  const int pj[4] = {p01 & 0xffff, p01 >> 16, p23 & 0xffff, p23 >> 16};
+  if (lane == 0) wtot[wave] = tj[0] + tj[1] + tj[2] + tj[3];
+  __syncthreads();
+  int base = 0;   // this wave's first entry within the chunk
+  for (int w = 0; w < wave; ++w) base += wtot[w];
+  const int total = wtot[0] + wtot[1] + wtot[2] + wtot[3];
+  const bool staged = total <= kStage;
+  const int room = ws.lcap - o;   // the offsets bound the list by k + cap; guard only
+  int2* dst = ws.list + (size_t)r * ws.lcap + o;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    int pos = base + pj[j];
+    const int t = wlo + 256 * j + 4 * lane;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const int t = t0 + e;
-      const bool ok = t < hi;
-      const float x = f4(v[j], e);
-      const uint32_t b = shifted_bin(x, sh);
-      above += (ok && b > bstar) ? 1 : 0;
-      const bool is_c = ok && b == bstar;
-      const uint64_t m = __ballot(is_c);
-      if (m) {
-        int base = 0;
-        const int leader = __ffsll((unsigned long long)m) - 1;
-        if (lane == leader) base = atomicAdd(cnt, __popcll(m));
-        base = __shfl(base, leader, 64);
-        if (is_c) {
-          const int pos = base + __popcll(m & ((1ull << lane) - 1ull));
-          if (pos < ws.cap) cand[pos] = make_int2(__float_as_int(x), t);
-        }
+      if ((in >> (4 * j + e)) & 1u) {
+        const int2 entry = make_int2(__float_as_int(f4(v[j], e)), t + e);
+        if (staged) stage[pos] = entry;
+        else if (pos < room) dst[pos] = entry;
+        ++pos;
       }
     }
+    base += tj[j];
   }
-  const int tot = ech::block_sum<kT>(above, scratch);
-  if (threadIdx.x == 0) ws.above[(size_t)r * ws.nch + c] = tot;
+  if (staged) {
+    __syncthreads();
+    const int n_out = min(total, room);
+    for (int i = threadIdx.x; i < n_out; i += kT) dst[i] = stage[i];
+  }
 }
 
 // ------------------------------------------------------------------ T4
@@ -351,18 +433,67 @@ __device__ __forceinline__ void pick_digit(int* hist, int* sh, int need, int* ou
   __syncthreads();
 }
 
+// The need-th largest of the first n scores of cl, by wave 0 alone (4
+// rounds of 8 bits of the order key, histogram in LDS). One wave's LDS
+// operations execute in order, so the rounds need no block barrier; the
+// wavefront fences keep the compiler from moving LDS accesses across phases.
+// Returns the order key of the score; *need_out = its rank among equals.
+__device__ __forceinline__ uint32_t wave_select(const int2* cl, int n, int need, int* hist, int* need_out) {
+  const int lane = ech::lane_id();
+  uint32_t prefix = 0, mask = 0;
+#pragma unroll 1
+  for (int round = 0; round < 4; ++round) {
+    const int shift = 24 - 8 * round;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) hist[4 * lane + q] = 0;
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    for (int i = lane; i < n; i += 64) {
+      const uint32_t key = ech::ord_key(__int_as_float(cl[i].x));
+      if ((key & mask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    // lane l owns digits 255 - 4l - q, q = 0..3 (descending)
+    int cnt[4], sum = 0;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      cnt[q] = hist[255 - 4 * lane - q];
+      sum += cnt[q];
+    }
+    int above = ech::wave_incl_scan(sum) - sum;
+    int digit = -1, nneed = 0;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      if (above < need && above + cnt[q] >= need) {
+        digit = 255 - 4 * lane - q;
+        nneed = need - above;
+      }
+      above += cnt[q];
+    }
+    const uint64_t m = __ballot(digit >= 0);
+    const int src = __ffsll((unsigned long long)m) - 1;
+    digit = __shfl(digit, src, 64);
+    need = __shfl(nneed, src, 64);
+    prefix |= (uint32_t)digit << shift;
+    mask |= 255u << shift;
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  }
+  *need_out = need;
+  return prefix;
+}
+
 template <int NT>
 __global__ __launch_bounds__(NT) void topk_resolve_kernel(const float* __restrict__ logits, int64_t ld,
                                                            const int32_t* __restrict__ lens, int k,
                                                            const float* __restrict__ theta_in,
                                                            float* __restrict__ theta_out, float* __restrict__ kth,
-                                                           Ws ws) {
+                                                           int32_t* __restrict__ idx, Ws ws) {
   extern __shared__ int2 cl[];                     // candidate list [cap]
   __shared__ int hist[256];
   __shared__ int sh[16];
   __shared__ int gt_c[kMaxChunks];
   __shared__ int eq_c[kMaxChunks];
-  __shared__ int s_digit, s_need;
+  __shared__ int s_digit, s_need, s_nb;
+  __shared__ uint32_t s_prefix;
   __shared__ float s_min;
 
   const int r = blockIdx.x;
@@ -406,40 +537,58 @@ __global__ __launch_bounds__(NT) void topk_resolve_kernel(const float* __restric
     for (int c = threadIdx.x; c < nch; c += NT) gt_c[c] = min(kChunk, len - c * kChunk);
     __syncthreads();
   } else {
-    const int cnt = st.cand;
     int need = st.need;
     uint32_t prefix = 0, mask = 0;
-    const bool in_lds = cnt <= ws.cap;
+    const bool in_lds = mode == kNormal;
     const Shift shf = make_shift(th_in);
     const uint32_t bstar = (uint32_t)st.bstar;
+    const int nlist = in_lds ? st.nlist : 0;
+    const int2* lst = ws.list + (size_t)r * ws.lcap;
+    int cnt = 0;
     if (in_lds) {
-      const int2* src = ws.cand + (size_t)r * ws.cap;
-      for (int i = threadIdx.x; i < cnt; i += NT) cl[i] = src[i];
+      // the list's b* entries (at most cap) into LDS, in any order
+      if (threadIdx.x == 0) s_nb = 0;
+      __syncthreads();
+      for (int i0 = 0; i0 < nlist; i0 += 8 * NT) {
+        int2 e[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const int i = i0 + u * NT + (int)threadIdx.x;
+          e[u] = i < nlist ? lst[i] : make_int2(0, -1);
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          if (e[u].y >= 0 && shifted_bin(__int_as_float(e[u].x), shf) == bstar) {
+            const int p = atomicAdd(&s_nb, 1);
+            if (p < ws.cap) cl[p] = e[u];   // the histogram bounds b* by cap; guard only
+          }
+        }
+      }
+      __syncthreads();
+      cnt = min(s_nb, ws.cap);
+      if (threadIdx.x < 64) {
+        int nq;
+        const uint32_t pf = wave_select(cl, cnt, need, hist, &nq);
+        if (threadIdx.x == 0) {
+          s_prefix = pf;
+          s_need = nq;
+        }
+      }
+      __syncthreads();
+      prefix = s_prefix;
+      need = s_need;
     }
     __syncthreads();
 #pragma unroll 1
-    for (int round = 0; round < 4; ++round) {
+    for (int round = 0; round < 4 && !in_lds; ++round) {   // wide rows: the same rounds over the whole row
       const int shift = 24 - 8 * round;
       for (int i = threadIdx.x; i < 256; i += NT) hist[i] = 0;
       __syncthreads();
-      if (in_lds) {
-        for (int i0 = 0; i0 < cnt; i0 += NT) {
-          const int i = i0 + threadIdx.x;
-          uint32_t key = 0;
-          bool act = false;
-          if (i < cnt) {
-            key = ech::ord_key(__int_as_float(cl[i].x));
-            act = (key & mask) == prefix;
-          }
-          ech::lds_hist_add(hist, (key >> shift) & 255u, act);
-        }
-      } else {
-        for_each_score<NT>(row, len, [&](int, float x) {
-          const uint32_t key = ech::ord_key(x);
-          const bool act = shifted_bin(x, shf) == bstar && (key & mask) == prefix;
-          ech::lds_hist_add(hist, (key >> shift) & 255u, act);
-        });
-      }
+      for_each_score<NT>(row, len, [&](int, float x) {
+        const uint32_t key = ech::ord_key(x);
+        const bool act = shifted_bin(x, shf) == bstar && (key & mask) == prefix;
+        ech::lds_hist_add(hist, (key >> shift) & 255u, act);
+      });
       __syncthreads();
       pick_digit(hist, sh, need, &s_digit, &s_need);
       prefix |= (uint32_t)s_digit << shift;
@@ -450,16 +599,58 @@ __global__ __launch_bounds__(NT) void topk_resolve_kernel(const float* __restric
     sstar = ech::ord_to_float(prefix);
     spred = sstar;
     need_eq = need;
-    // per-chunk counts of tokens strictly above s* and equal to s*
     if (in_lds) {
-      for (int c = threadIdx.x; c < nch; c += NT) gt_c[c] = ws.above[(size_t)r * ws.nch + c];
-      __syncthreads();
-      for (int i = threadIdx.x; i < cnt; i += NT) {
-        const float x = __int_as_float(cl[i].x);
-        const int c = cl[i].y / kChunk;
-        if (x > sstar) atomicAdd(&gt_c[c], 1);
-        else if (x == sstar) atomicAdd(&eq_c[c], 1);
+      // The selection in token order, by one ordered pass over the list:
+      // every entry above b*, and the b* entries above s* or among the first
+      // need_eq equal to it.
+      // Thread i holds 8 consecutive entries per round, so one block scan
+      // serves 8 * NT entries.
+      int32_t* orow = idx + (size_t)r * k;
+      int gt_run = 0, eq_run = 0;
+      for (int i0 = 0; i0 < nlist; i0 += 8 * NT) {
+        const int ib = i0 + 8 * (int)threadIdx.x;
+        int2 e[8];
+        if (ib + 7 < nlist) {
+          const int4* q = reinterpret_cast<const int4*>(lst + ib);   // 64-byte aligned (lcap and ib multiples of 8)
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            const int4 x = q[u];
+            e[2 * u] = make_int2(x.x, x.y);
+            e[2 * u + 1] = make_int2(x.z, x.w);
+          }
+        } else {
+#pragma unroll
+          for (int u = 0; u < 8; ++u) e[u] = ib + u < nlist ? lst[ib + u] : make_int2(0, -1);
+        }
+        uint32_t gtm = 0, eqm = 0;
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          if (e[u].y < 0) continue;
+          const float x = __int_as_float(e[u].x);
+          const bool gt = shifted_bin(x, shf) > bstar || x > sstar;
+          gtm |= gt ? 1u << u : 0u;
+          eqm |= (!gt && x == sstar) ? 1u << u : 0u;
+        }
+        int tot;
+        const int pre = ech::block_excl_scan<NT>(__popc(gtm) | (__popc(eqm) << 16), sh, &tot);
+        int gt_b = gt_run + (pre & 0xffff), eq_b = eq_run + (pre >> 16);
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const bool gt = (gtm >> u) & 1u, eq = (eqm >> u) & 1u;
+          const int pos = gt_b + min(eq_b, need_eq);
+          if ((gt || (eq && eq_b < need_eq)) && pos < k) orow[pos] = e[u].y;
+          gt_b += gt;
+          eq_b += eq;
+        }
+        gt_run += tot & 0xffff;
+        eq_run += tot >> 16;
       }
+      if (threadIdx.x == 0) {
+        st.spred = spred;
+        kth[r] = sstar;
+        if (theta_out) theta_out[r] = (th_in == th_in) ? (sstar + th_in) * 0.5f : sstar;
+      }
+      return;
     } else {
       for_each_score<NT>(row, len, [&](int t, float x) {
         if (x > sstar) atomicAdd(&gt_c[t / kChunk], 1);
@@ -497,11 +688,12 @@ __global__ __launch_bounds__(kT) void topk_compact_kernel(const float* __restric
   }
   const int lo = c * kChunk;
   if (lo >= len) return;
+  // Most rows were written by T4 from the list: check before reading scores.
+  const RowState st = ws.rs[r];
+  if (st.mode == kEmpty || st.mode == kNormal) return;
   const int hi = min(lo + kChunk, len);
   float4 v[kVec];
-  load_chunk(logits + (size_t)r * ld, lo, hi, v);   // before the row state: the latencies overlap
-  const RowState st = ws.rs[r];
-  if (st.mode == kEmpty) return;
+  load_chunk(logits + (size_t)r * ld, lo, hi, v);
   const float sp = st.spred;
   const int base = ws.off[(size_t)r * ws.nch + c];
   const int te = ws.take[(size_t)r * ws.nch + c];
@@ -543,9 +735,9 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 }  // namespace
 
 extern "C" size_t ech_topk_ws_bytes(int R, int max_len, int k) {
-  (void)k;
   if (R < 1 || max_len < 0) return 0;
-  return layout(R, max_len, nullptr, nullptr);
+  if (k < 1 || k > kMaxK) return 0;
+  return layout(R, max_len, k, nullptr, nullptr);
 }
 
 extern "C" int ech_topk(const float* logits, int64_t ld, const int32_t* row_len, int R, int max_len, int k,
@@ -557,7 +749,7 @@ extern "C" int ech_topk(const float* logits, int64_t ld, const int32_t* row_len,
   if (ld % 4 != 0 || !aligned16(logits) || (reinterpret_cast<uintptr_t>(ws) & 255u)) return ECH_EINVAL;
   if (ws_bytes < ech_topk_ws_bytes(R, max_len, k)) return ECH_EINVAL;
   Ws w;
-  layout(R, max_len, &w, static_cast<char*>(ws));
+  layout(R, max_len, k, &w, static_cast<char*>(ws));
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   const dim3 gch(w.nch, R);
   hipLaunchKernelGGL(topk_hist_kernel, gch, dim3(kT), 0, s, logits, ld, row_len, k, theta_in, w);
@@ -570,14 +762,14 @@ extern "C" int ech_topk(const float* logits, int64_t ld, const int32_t* row_len,
   else
     hipLaunchKernelGGL(topk_rowsel_kernel<256>, dim3(R), dim3(256), 0, s, row_len, k, w);
   ECH_LAUNCH_CHECK();
-  hipLaunchKernelGGL(topk_gather_kernel, gch, dim3(kT), 0, s, logits, ld, row_len, theta_in, w);
+  hipLaunchKernelGGL(topk_list_kernel, gch, dim3(kT), 0, s, logits, ld, row_len, theta_in, w);
   ECH_LAUNCH_CHECK();
   if (wide)
     hipLaunchKernelGGL(topk_resolve_kernel<1024>, dim3(R), dim3(1024), sizeof(int2) * w.cap, s, logits, ld,
-                       row_len, k, theta_in, theta_out, kth, w);
+                       row_len, k, theta_in, theta_out, kth, idx, w);
   else
     hipLaunchKernelGGL(topk_resolve_kernel<256>, dim3(R), dim3(256), sizeof(int2) * w.cap, s, logits, ld, row_len,
-                       k, theta_in, theta_out, kth, w);
+                       k, theta_in, theta_out, kth, idx, w);
   ECH_LAUNCH_CHECK();
   hipLaunchKernelGGL(topk_compact_kernel, gch, dim3(kT), 0, s, logits, ld, row_len, k, idx, w);
   ECH_LAUNCH_CHECK();
