@@ -46,7 +46,10 @@ constexpr int kMaxK = 4096;
 constexpr int kMaxChunks = 1024;    // max_len <= 4M
 
 // kNormal: resolved from T3's list. kWide: the boundary bin holds more than
-// cap tokens; resolved over the whole row, compacted by T5.
+// cap tokens; resolved over the whole row, compacted by T5. With many rows a
+// wide row whose boundary is the lumped bin 0 is first refined (T2b): its
+// lumped tokens are binned again without lumping, and if the boundary
+// sub-bin d0 fits, the row is served by the list after all (refine = 1).
 enum RowMode : int { kNormal = 0, kAll = 1, kEmpty = 2, kWide = 3 };
 
 struct RowState {
@@ -55,7 +58,9 @@ struct RowState {
   int need;      // rank of the k-th token within b*
   int nlist;     // list entries (tokens in bins >= b*)
   float spred;   // T5: scores > spred are selected (-inf in kAll mode)
-  int pad[3];
+  int refine;    // boundary = lumped tokens whose unlumped bin is d0
+  int d0;
+  int pad;
 };
 
 struct Ws {
@@ -219,6 +224,7 @@ __global__ __launch_bounds__(NT) void topk_rowsel_kernel(const int32_t* __restri
       st.bstar = 0;
       st.need = 0;
       st.nlist = 0;
+      st.refine = 0;
     }
     return;
   }
@@ -255,10 +261,15 @@ __global__ __launch_bounds__(NT) void topk_rowsel_kernel(const int32_t* __restri
   __syncthreads();
   const int bstar = s_bstar;
   const bool wide = s_nbin > ws.cap;
-  if (threadIdx.x == 0) st.mode = wide ? kWide : kNormal;
-  if (wide) return;
-  // List offsets: chunk c holds sum over bins >= b* of its histogram. Four
-  // adjacent threads share a chunk (16 int4 loads each, all in flight).
+  if (threadIdx.x == 0) {
+    st.mode = wide ? kWide : kNormal;
+    st.refine = 0;
+  }
+  // List offsets: chunk c holds the sum over bins >= b* of its histogram.
+  // Wide rows keep instead, per chunk, the count of bins > b* (in take), for
+  // the refinement. Four adjacent threads share a chunk (16 int4 loads each,
+  // all in flight).
+  const int tb = wide ? bstar + 1 : bstar;
   int run = 0;
   const int sub = threadIdx.x & 3;
   for (int c0 = 0; c0 < nch; c0 += NT / 4) {
@@ -272,9 +283,112 @@ __global__ __launch_bounds__(NT) void topk_rowsel_kernel(const int32_t* __restri
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const int b0 = 64 * sub + 4 * i;
-        n += (b0 >= bstar ? q[i].x : 0) + (b0 + 1 >= bstar ? q[i].y : 0) + (b0 + 2 >= bstar ? q[i].z : 0) +
-             (b0 + 3 >= bstar ? q[i].w : 0);
+        n += (b0 >= tb ? q[i].x : 0) + (b0 + 1 >= tb ? q[i].y : 0) + (b0 + 2 >= tb ? q[i].z : 0) +
+             (b0 + 3 >= tb ? q[i].w : 0);
       }
+    }
+    n += __shfl_xor(n, 1, 64);
+    n += __shfl_xor(n, 2, 64);
+    int t;
+    const int pre = ech::block_excl_scan<NT>(sub == 0 ? n : 0, scratch, &t);
+    if (c < nch && sub == 0) {
+      if (wide) ws.take[(size_t)r * ws.nch + c] = n;
+      else ws.off[(size_t)r * ws.nch + c] = run + pre;
+    }
+    run += t;
+  }
+  if (threadIdx.x == 0 && !wide) st.nlist = run;
+}
+
+// ------------------------------------------------------------------ T2b
+// Refinement of wide rows whose boundary is the lumped bin 0 (a prediction
+// far above the k-th score), for calls with many rows. Histogram, per chunk,
+// of the lumped tokens by bin16(d) without lumping, into the row's T1
+// histogram space (no longer read).
+__global__ __launch_bounds__(kT) void topk_refine_hist_kernel(const float* __restrict__ logits, int64_t ld,
+                                                              const int32_t* __restrict__ lens,
+                                                              const float* __restrict__ theta, Ws ws) {
+  const int r = blockIdx.y, c = blockIdx.x;
+  const int len = lens[r];
+  const int lo = c * kChunk;
+  if (lo >= len) return;
+  const RowState st = ws.rs[r];
+  if (st.mode != kWide || st.bstar != 0) return;
+  const Shift sh = make_shift(row_theta(theta, r));
+  if (!sh.on) return;
+  const int hi = min(lo + kChunk, len);
+  __shared__ int h[256];
+  h[threadIdx.x] = 0;
+  float4 v[kVec];
+  load_chunk(logits + (size_t)r * ld, lo, hi, v);
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < kVec; ++j) {
+    const int t = lo + 4 * (j * kT + (int)threadIdx.x);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float d = f4(v[j], e) - sh.th;
+      ech::lds_hist_add(h, bin16(d), t + e < hi && d < sh.cut);
+    }
+  }
+  __syncthreads();
+  ws.hist[((size_t)r * ws.nch + c) * 256 + threadIdx.x] = h[threadIdx.x];
+}
+
+// The boundary sub-bin d0 of a refined row and, if it holds at most cap
+// tokens, the row's list offsets: per chunk, the tokens above the lumped bin
+// (take) plus the lumped ones with unlumped bin >= d0.
+template <int NT>
+__global__ __launch_bounds__(NT) void topk_refine_sel_kernel(const int32_t* __restrict__ lens,
+                                                             const float* __restrict__ theta, Ws ws) {
+  constexpr int kParts = NT / 256;
+  const int r = blockIdx.x;
+  const int len = lens[r];
+  RowState& st = ws.rs[r];
+  if (st.mode != kWide || st.bstar != 0 || !make_shift(row_theta(theta, r)).on) return;
+  const int nch = (len + kChunk - 1) / kChunk;
+  __shared__ int part_sum[kParts][256];
+  __shared__ int scratch[NT / 64];
+  __shared__ int s_d0, s_n2, s_need;
+  const int b = threadIdx.x & 255, part = threadIdx.x >> 8;
+  const int* h = ws.hist + (size_t)r * ws.nch * 256 + (255 - b);
+  int acc = 0;
+  for (int c = part; c < nch; c += kParts) acc += h[(size_t)c * 256];
+  part_sum[part][b] = acc;
+  __syncthreads();
+  int cnt = 0;
+  if (threadIdx.x < 256) {
+#pragma unroll
+    for (int pp = 0; pp < kParts; ++pp) cnt += part_sum[pp][b];
+  }
+  int tot;
+  const int above = ech::block_excl_scan<NT>(cnt, scratch, &tot);
+  const int need = st.need;
+  if (threadIdx.x < 256 && above < need && above + cnt >= need) {
+    s_d0 = 255 - b;
+    s_n2 = cnt;
+    s_need = need - above;
+  }
+  __syncthreads();
+  if (s_n2 > ws.cap) return;   // still wider than the list: resolved over the whole row
+  const int d0 = s_d0;
+  int run = 0;
+  const int sub = threadIdx.x & 3;
+  for (int c0 = 0; c0 < nch; c0 += NT / 4) {
+    const int c = c0 + (int)threadIdx.x / 4;
+    int n = 0;
+    if (c < nch) {
+      const int4* hc = reinterpret_cast<const int4*>(ws.hist + ((size_t)r * ws.nch + c) * 256) + 16 * sub;
+      int4 q[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) q[i] = hc[i];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int b0 = 64 * sub + 4 * i;
+        n += (b0 >= d0 ? q[i].x : 0) + (b0 + 1 >= d0 ? q[i].y : 0) + (b0 + 2 >= d0 ? q[i].z : 0) +
+             (b0 + 3 >= d0 ? q[i].w : 0);
+      }
+      if (sub == 0) n += ws.take[(size_t)r * ws.nch + c];
     }
     n += __shfl_xor(n, 1, 64);
     n += __shfl_xor(n, 2, 64);
@@ -283,7 +397,13 @@ __global__ __launch_bounds__(NT) void topk_rowsel_kernel(const int32_t* __restri
     if (c < nch && sub == 0) ws.off[(size_t)r * ws.nch + c] = run + pre;
     run += t;
   }
-  if (threadIdx.x == 0) st.nlist = run;
+  if (threadIdx.x == 0) {
+    st.need = s_need;
+    st.refine = 1;
+    st.d0 = d0;
+    st.nlist = run;
+    st.mode = kNormal;
+  }
 }
 
 // ------------------------------------------------------------------ T3
@@ -323,6 +443,8 @@ __global__ __launch_bounds__(kT) void topk_list_kernel(const float* __restrict__
   if (st.mode != kNormal) return;
   const Shift sh = make_shift(row_theta(theta, r));
   const uint32_t bstar = (uint32_t)st.bstar;
+  const bool refine = st.refine;
+  const uint32_t d0 = (uint32_t)st.d0;
   __shared__ int wtot[kT / 64];
   // The chunk's entries are gathered in LDS and leave as consecutive 8-byte
   // stores: written one by one from the lanes that hold them they cost more
@@ -335,8 +457,12 @@ __global__ __launch_bounds__(kT) void topk_list_kernel(const float* __restrict__
   for (int j = 0; j < 4; ++j) {
     const int t = wlo + 256 * j + 4 * lane;
 #pragma unroll
-    for (int e = 0; e < 4; ++e)
-      in |= (t + e < hi && shifted_bin(f4(v[j], e), sh) >= bstar) ? 1u << (4 * j + e) : 0u;
+    for (int e = 0; e < 4; ++e) {
+      const float x = f4(v[j], e);
+      const uint32_t b = shifted_bin(x, sh);
+      const bool listed = b > bstar || (b == bstar && (!refine || bin16(x - sh.th) >= d0));
+      in |= (t + e < hi && listed) ? 1u << (4 * j + e) : 0u;
+    }
   }
   int n[4];
 #pragma unroll
@@ -543,6 +669,8 @@ __global__ __launch_bounds__(NT) void topk_resolve_kernel(const float* __restric
     const Shift shf = make_shift(th_in);
     const uint32_t bstar = (uint32_t)st.bstar;
     const int nlist = in_lds ? st.nlist : 0;
+    const bool refine = st.refine;
+    const uint32_t d0 = (uint32_t)st.d0;
     const int2* lst = ws.list + (size_t)r * ws.lcap;
     int cnt = 0;
     if (in_lds) {
@@ -558,7 +686,8 @@ __global__ __launch_bounds__(NT) void topk_resolve_kernel(const float* __restric
         }
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
-          if (e[u].y >= 0 && shifted_bin(__int_as_float(e[u].x), shf) == bstar) {
+          const float x = __int_as_float(e[u].x);
+          if (e[u].y >= 0 && shifted_bin(x, shf) == bstar && (!refine || bin16(x - shf.th) == d0)) {
             const int p = atomicAdd(&s_nb, 1);
             if (p < ws.cap) cl[p] = e[u];   // the histogram bounds b* by cap; guard only
           }
@@ -626,10 +755,10 @@ __global__ __launch_bounds__(NT) void topk_resolve_kernel(const float* __restric
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
           if (e[u].y < 0) continue;
+          // every list entry outside the boundary set scores above it
           const float x = __int_as_float(e[u].x);
-          const bool gt = shifted_bin(x, shf) > bstar || x > sstar;
-          gtm |= gt ? 1u << u : 0u;
-          eqm |= (!gt && x == sstar) ? 1u << u : 0u;
+          gtm |= x > sstar ? 1u << u : 0u;
+          eqm |= x == sstar ? 1u << u : 0u;
         }
         int tot;
         const int pre = ech::block_excl_scan<NT>(__popc(gtm) | (__popc(eqm) << 16), sh, &tot);
@@ -756,15 +885,22 @@ extern "C" int ech_topk(const float* logits, int64_t ld, const int32_t* row_len,
   ECH_LAUNCH_CHECK();
   // A few long rows (decode) get 1024 threads per row; many rows (a prefill
   // block) get 256, so the per-row kernels fit beside other work on a CU.
-  const bool wide = R <= 256;
-  if (wide)
+  const bool few_rows = R <= 256;
+  if (few_rows)
     hipLaunchKernelGGL(topk_rowsel_kernel<1024>, dim3(R), dim3(1024), 0, s, row_len, k, w);
   else
     hipLaunchKernelGGL(topk_rowsel_kernel<256>, dim3(R), dim3(256), 0, s, row_len, k, w);
   ECH_LAUNCH_CHECK();
+  if (!few_rows) {
+    // many rows: refine rows with a lumped boundary in parallel over chunks
+    hipLaunchKernelGGL(topk_refine_hist_kernel, gch, dim3(kT), 0, s, logits, ld, row_len, theta_in, w);
+    ECH_LAUNCH_CHECK();
+    hipLaunchKernelGGL(topk_refine_sel_kernel<256>, dim3(R), dim3(256), 0, s, row_len, theta_in, w);
+    ECH_LAUNCH_CHECK();
+  }
   hipLaunchKernelGGL(topk_list_kernel, gch, dim3(kT), 0, s, logits, ld, row_len, theta_in, w);
   ECH_LAUNCH_CHECK();
-  if (wide)
+  if (few_rows)
     hipLaunchKernelGGL(topk_resolve_kernel<1024>, dim3(R), dim3(1024), sizeof(int2) * w.cap, s, logits, ld,
                        row_len, k, theta_in, theta_out, kth, idx, w);
   else

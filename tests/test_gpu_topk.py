@@ -108,3 +108,27 @@ def test_many_rows_prefill_shape():
     lens = [off + r + 1 for r in range(R)]
     ld = ((off + R + 3) // 4) * 4
     _check(_pad(x, ld), lens, 2048)
+
+
+def test_many_rows_theta_far_above_refined():
+    """More than 256 rows (the many-rows path) with predictions far above the
+    true k-th score, so the boundary is the lumped bin: rows whose refined
+    boundary fits the list (theta = 1.5 x kth) and rows where it does not
+    (2 x kth on N(18, 4) scores, constant rows, tied integers) must all give
+    the oracle's set; the others take no, exact or near predictions."""
+    need_gpu()
+    R, k = 320, 2048
+    lens = [12000 + (r * 877) % 28000 for r in range(R)]
+    ld = ((max(lens) + 3) // 4) * 4
+    x = wk.random_logits(8, R, ld, 'normal')
+    ties = wk.random_logits(9, R, ld, 'ties')
+    for r in range(R):
+        if r % 16 == 3:
+            x[r] = 3.5
+        elif r % 16 == 11:
+            x[r] = ties[r]
+    kth = np.array([oracle.topk_row(x[r, :lens[r]], k)[1] for r in range(R)], np.float32)
+    factor = np.array([1.5, 2.0, 1.1, np.nan, 1.0], np.float32)[np.arange(R) % 5]
+    theta = (kth * factor).astype(np.float32)
+    theta[np.arange(R) % 16 == 3] = np.float32(14.0)       # constant rows: 4 x the score
+    _check(x, lens, k, theta)
