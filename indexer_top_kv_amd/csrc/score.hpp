@@ -11,7 +11,7 @@
 // weights and the per-token scale:
 //   ReLU(s * x) = s * med3(x, 0, s >= 0 ? +inf : -inf),
 // then reduces the 64 heads (16 per lane in registers, 4 lane groups by
-// cross-lane adds).
+// lane swaps and adds).
 //
 // MFMA operand layout used (16x16x32 bf16, wave64): lane l holds A[row l%16]
 // and B[col l%16], 8 contraction elements each in lane group l/16; the
@@ -108,6 +108,19 @@ __device__ __forceinline__ void tile_mfma(const bf16x8_t (&a)[4][4], const bf16x
   }
 }
 
+// x[l] + x[l^16] + x[l^32] + x[l^48] (the 4 lane groups) in every lane, with
+// the same additions in the same order as x + xor16(x), then + xor32 of that.
+// v_permlane16/32_swap of a register with itself leaves, in each lane, the
+// lane's own value and its partner's in the two outputs, so their sum is the
+// pair sum; unlike a shuffle (ds_bpermute) this stays in the VALU and does not
+// wait on the LDS crossbar.
+__device__ __forceinline__ float lane_group_sum(float x) {
+  const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  const float y = __uint_as_float(p[0]) + __uint_as_float(p[1]);
+  const auto q = __builtin_amdgcn_permlane32_swap(__float_as_uint(y), __float_as_uint(y), false, false);
+  return __uint_as_float(q[0]) + __uint_as_float(q[1]);
+}
+
 // Epilogue of a tile: ReLU (with the per-token scale's sign), head weights,
 // head sum. Returns the score of token column (lane & 15) in every lane.
 __device__ __forceinline__ float tile_epilogue(const f32x4_t (&acc)[4], const float (&wv)[4][4], float sc) {
@@ -118,9 +131,7 @@ __device__ __forceinline__ float tile_epilogue(const f32x4_t (&acc)[4], const fl
 #pragma unroll
     for (int v = 0; v < 4; ++v) part = fmaf(wv[ht][v], __builtin_amdgcn_fmed3f(acc[ht][v], 0.f, bound), part);
   }
-  part += __shfl_xor(part, 16, 64);
-  part += __shfl_xor(part, 32, 64);
-  return part * sc;
+  return lane_group_sum(part) * sc;
 }
 
 __device__ __forceinline__ float tile_score(const bf16x8_t (&a)[4][4], const float (&wv)[4][4],
