@@ -270,15 +270,12 @@ __global__ __launch_bounds__(kT) void count_free_kernel(const int32_t* __restric
 }
 
 // ------------------------------------------------------------------ scan
-constexpr int kStage = 4096;   // block counts staged in LDS by the scan kernel
 
 template <int NT>
 __global__ __launch_bounds__(NT) void scan_kernel(int phase, int B, int cap, int32_t C, int32_t* ctr,
                                                    int32_t* __restrict__ stats, CWs w) {
   __shared__ int scr[NT / 64];
-  __shared__ int s_want[kStage];
-  __shared__ int s_hit[kStage];
-  __shared__ int s_base;
+  __shared__ int s_rowoff[NT], s_take[NT], s_seg[NT];
   // free slots: exclusive scan over slot blocks (chunks of NT)
   int nfree_tot = 0;
   for (int b0 = 0; b0 < w.ns; b0 += NT) {
@@ -289,26 +286,33 @@ __global__ __launch_bounds__(NT) void scan_kernel(int phase, int B, int cap, int
     if (i < w.ns) w.soff[i] = nfree_tot + ex;
     nfree_tot += tot;
   }
-  // misses: stage the block counts in LDS (coalesced), then thread b sums
-  // its sequence's blocks
+  // misses: the entry blocks are sequence-major (b * nbr + c). One flat
+  // exclusive scan of the want counts gives every block's prefix (kept in off
+  // for now) and, at the segment boundaries, every sequence's total; the hit
+  // counts get the same scan (prefixes kept in lim for now). All threads
+  // take part, however many blocks a sequence has.
   const int nseq = (phase == ECH_PREFILL) ? 1 : B;
-  const bool staged = w.ne <= kStage;
-  if (staged) {
-    for (int i = threadIdx.x; i < w.ne; i += NT) {
-      s_want[i] = w.want[i];
-      s_hit[i] = w.hit[i];
+  const int n = nseq * w.nbr;
+  int want_all = 0, hit_all = 0;
+  for (int i0 = 0; i0 < n; i0 += NT) {
+    const int i = i0 + threadIdx.x;
+    int tw, th;
+    const int ew = ech::block_excl_scan<NT>(i < n ? w.want[i] : 0, scr, &tw);
+    const int eh = ech::block_excl_scan<NT>(i < n ? w.hit[i] : 0, scr, &th);
+    if (i < n) {
+      w.off[i] = want_all + ew;
+      w.lim[i] = hit_all + eh;
     }
+    want_all += tw;
+    hit_all += th;
   }
-  __syncthreads();
-  const int* want = staged ? s_want : w.want;
-  const int* hit = staged ? s_hit : w.hit;
+  __syncthreads();   // the prefixes in off and lim are read across threads below
   const int b = threadIdx.x;
-  int want_b = 0, hit_b = 0;
+  int want_b = 0, hit_b = 0, seg = 0;
   if (b < nseq) {
-    for (int c = 0; c < w.nbr; ++c) {
-      want_b += want[b * w.nbr + c];
-      hit_b += hit[b * w.nbr + c];
-    }
+    seg = w.off[b * w.nbr];
+    want_b = (b + 1 < nseq ? w.off[(b + 1) * w.nbr] : want_all) - seg;
+    hit_b = (b + 1 < nseq ? w.lim[(b + 1) * w.nbr] : hit_all) - w.lim[b * w.nbr];
   }
   const int take_b = (phase == ECH_EARLY) ? min(cap, want_b) : want_b;
   int n_want;
@@ -317,12 +321,18 @@ __global__ __launch_bounds__(NT) void scan_kernel(int phase, int B, int cap, int
   if (clamped) n_want = w.M_max;
   const int n_alloc = min(n_want, nfree_tot);
   if (b < nseq) {
-    int run = row_off;
-    for (int c = 0; c < w.nbr; ++c) {
-      w.off[b * w.nbr + c] = run;
-      w.lim[b * w.nbr + c] = row_off + take_b;
-      run += want[b * w.nbr + c];
-    }
+    s_rowoff[b] = row_off;
+    s_take[b] = take_b;
+    s_seg[b] = seg;
+  }
+  __syncthreads();
+  // every block: its first miss's rank and its sequence's rank limit
+  for (int i = threadIdx.x; i < n; i += NT) {
+    const int bi = i / w.nbr;
+    w.off[i] = s_rowoff[bi] + (w.off[i] - s_seg[bi]);
+    w.lim[i] = s_rowoff[bi] + s_take[bi];
+  }
+  if (b < nseq) {
     const int fetched = max(0, min(n_alloc - row_off, take_b));
     int32_t* s = stats + 4 * b;
     if (phase == ECH_PREFILL) {
@@ -347,7 +357,6 @@ __global__ __launch_bounds__(NT) void scan_kernel(int phase, int B, int cap, int
     ctr[ECH_CTR_NEVICT] = 0;
     if ((phase != ECH_EARLY && n_want > nfree_tot) || clamped) ctr[ECH_CTR_STATUS] |= ECH_ST_OVERFLOW;
   }
-  (void)s_base;
 }
 
 // ------------------------------------------------------------------ emit
