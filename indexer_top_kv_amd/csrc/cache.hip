@@ -6,21 +6,21 @@
 // maxima; every data-dependent count lives in device memory, so the phase can
 // be captured in a hipGraph and replayed.
 //
-//   pin      mark the slots of the phase's resident selection with the new
-//            epoch (slot_pin[s] = epoch) and count hits / wanted misses per
-//            block. EARLY: tokens with score > theta; FINAL: idx entries;
-//            PREFILL: idx entries of all rows, misses claimed once per token
-//            by marking tok2slot -1 -> -2 (union), then counted by a
-//            token scan.
-//   free     count unpinned slots per block in ring order from the head.
-//   scan     one workgroup: exclusive scans of the block counts give every
-//            miss its rank (ascending sequence, token; EARLY keeps the first
-//            `cap` per sequence) and every free slot its rank in ring order;
-//            n_alloc = min(wanted, free). Writes stats and counters.
-//   emit     recompute the same flags in order: miss of rank m -> mcand[m],
-//            free slot of rank m -> freelist[m].
-//   apply    miss m takes freelist[m]: the slot's old token is unmapped (no
-//            write-back), the maps point at each other, miss[m] = (g, slot).
+//   count    each block marks the slots of its part of the phase's resident
+//            selection with the new epoch (slot_pin[s] = epoch), counts hits
+//            and misses, and lists its misses in order. EARLY: tokens with
+//            score > theta; FINAL: idx entries; PREFILL: idx entries of all
+//            rows, misses claimed once per token by marking tok2slot -1 -> -2
+//            (union), then listed by a token scan.
+//   allocate one workgroup: scans of the block counts give every miss its
+//            rank (ascending sequence,
+//            token; EARLY keeps the first `cap` per sequence); unpinned slots
+//            are ranked in ring order from the head, window by window, only
+//            as far as the misses need; n_alloc = min(wanted, free). Writes
+//            stats, counters, head and epoch.
+//   apply    miss m takes the free slot of rank m: the slot's old token is
+//            unmapped (no write-back), the maps point at each other,
+//            miss[m] = (g, slot).
 // Ranks come from scans, not from atomics, so the maps are a deterministic
 // function of the inputs: bit-identical run to run.
 
@@ -36,44 +36,43 @@ constexpr int kBlk = kT * kPer;   // tokens or slots per block in ordered kernel
 constexpr int kMaxK = 4096;
 constexpr int kMaxB = 1024;
 
-enum { S_EP = 0, S_NWANT = 1, S_NALLOC = 2, S_HEAD = 3, S_NFREE = 4, S_N = 16 };
+enum { S_EP = 0, S_NWANT = 1, S_NALLOC = 2, S_N = 16 };
 
 struct CWs {
-  int* want;     // [ne] wanted misses per entry block
-  int* hit;      // [ne] hits per entry block
+  int* want;     // [ne] misses per entry block (all of them)
+  int* hit;      // [ne] hits (pinned slots) per entry block
   int* off;      // [ne] rank of the block's first miss
   int* lim;      // [ne] rank limit of the block's sequence (EARLY cap)
-  int* nfree;    // [ns] unpinned slots per slot block
-  int* soff;     // [ns] rank of the block's first free slot
-  int* freelist; // [M_max]
-  int2* mcand;   // [M_max] (g, aux): aux = entry index (FINAL), sequence (EARLY), 0 (PREFILL)
+  int* freelist; // [M_max] free slot of each rank, in ring order from the head
+  int2* lmiss;   // [ne][lcap] the block's misses in order: (g, aux), aux = entry index (FINAL)
   int* sc;       // [S_N] scalars
-  int ne, ns, nbr;  // entry blocks, slot blocks, entry blocks per sequence
-  int P, C, M_max;  // bounds every index is checked against
+  int ne, nbr, lcap;  // entry blocks, entry blocks per sequence, list capacity per block
+  int P, C, M_max;    // bounds every index is checked against
 };
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
-void block_counts(int phase, int B, int R, int k, int max_len, int32_t C, int* ne, int* ns, int* nbr) {
+void block_counts(int phase, int B, int k, int max_len, int* ne, int* nbr, int* lcap) {
   const int nbj = (k + kT - 1) / kT;
   const int nch = std::max(1, (max_len + kBlk - 1) / kBlk);
   if (phase == ECH_FINAL) {
     *nbr = nbj;
     *ne = B * nbj;
+    *lcap = kT;
   } else if (phase == ECH_EARLY) {
     *nbr = nch;
     *ne = B * nch;
+    *lcap = kBlk;
   } else {
     *nbr = nch;
     *ne = nch;
+    *lcap = kBlk;
   }
-  (void)R;
-  *ns = (int)((C + kBlk - 1) / kBlk);
 }
 
-size_t layout(int phase, int B, int R, int k, int max_len, int32_t C, int32_t M_max, CWs* w, char* base) {
-  int ne, ns, nbr;
-  block_counts(phase, B, R, k, max_len, C, &ne, &ns, &nbr);
+size_t layout(int phase, int B, int k, int max_len, int32_t M_max, CWs* w, char* base) {
+  int ne, nbr, lcap;
+  block_counts(phase, B, k, max_len, &ne, &nbr, &lcap);
   size_t o = 0;
   auto take = [&](size_t bytes) {
     size_t at = o;
@@ -81,28 +80,216 @@ size_t layout(int phase, int B, int R, int k, int max_len, int32_t C, int32_t M_
     return at;
   };
   size_t o_want = take(4 * (size_t)ne), o_hit = take(4 * (size_t)ne), o_off = take(4 * (size_t)ne),
-         o_lim = take(4 * (size_t)ne), o_nf = take(4 * (size_t)ns), o_so = take(4 * (size_t)ns),
-         o_fl = take(4 * (size_t)M_max), o_mc = take(8 * (size_t)M_max), o_sc = take(4 * S_N);
+         o_lim = take(4 * (size_t)ne), o_fl = take(4 * (size_t)M_max), o_lm = take(8 * (size_t)ne * lcap),
+         o_sc = take(4 * S_N);
   if (w && base) {
     w->want = reinterpret_cast<int*>(base + o_want);
     w->hit = reinterpret_cast<int*>(base + o_hit);
     w->off = reinterpret_cast<int*>(base + o_off);
     w->lim = reinterpret_cast<int*>(base + o_lim);
-    w->nfree = reinterpret_cast<int*>(base + o_nf);
-    w->soff = reinterpret_cast<int*>(base + o_so);
     w->freelist = reinterpret_cast<int*>(base + o_fl);
-    w->mcand = reinterpret_cast<int2*>(base + o_mc);
+    w->lmiss = reinterpret_cast<int2*>(base + o_lm);
     w->sc = reinterpret_cast<int*>(base + o_sc);
     w->ne = ne;
-    w->ns = ns;
     w->nbr = nbr;
+    w->lcap = lcap;
   }
   return o;
 }
 
 __device__ __forceinline__ void set_status(int32_t* ctr, int bit) { atomicOr(&ctr[ECH_CTR_STATUS], bit); }
 
+// ------------------------------------------------------------------ allocate
+// One workgroup of kA threads, after the counting kernel.
+//   1. ranks: exclusive scans of the per-block counts (sequence-major) give
+//      every block its first miss's rank; EARLY keeps the first `cap` misses
+//      of each sequence; n_want = the misses taken.
+//   2. free slots: ring positions from the head, a window of kWin at a time,
+//      until n_want unpinned slots are found or the ring is exhausted; the
+//      slot of rank m goes to freelist[m]. n_alloc = min(n_want, found).
+//   3. statistics, counters, the new head and epoch.
+constexpr int kA = 1024;        // threads of the allocating workgroup
+constexpr int kWin = kA * 16;   // ring positions per window
+
+__global__ __launch_bounds__(kA) void allocate_kernel(int phase, int nseq, int cap, int32_t* ctr,
+                                                     const int32_t* __restrict__ slot_pin,
+                                                     int32_t* __restrict__ stats, CWs w) {
+  __shared__ int scr[kA / 64];
+  __shared__ int s_rowoff[kMaxB], s_take[kMaxB], s_seg[kMaxB + 1], s_hseg[kMaxB + 1];
+  __shared__ __align__(16) uint8_t s_fr[kWin];
+  __shared__ int s_last, s_lastw;
+  const int tid = threadIdx.x;
+  const int C = w.C;
+  const int ep = ctr[ECH_CTR_EPOCH] + 1;
+  int head = ctr[ECH_CTR_HEAD];
+  if (head < 0 || head >= C) head = 0;   // only a corrupted state; keeps every slot index in range
+  // ---- 1. ranks. Flat exclusive scans of want and hit over the n entry
+  // blocks (sequence-major), four consecutive blocks per thread; each
+  // sequence's first block leaves its prefixes in s_seg / s_hseg.
+  const int n = nseq * w.nbr;
+  int wv[4], ew[4];   // one pass (n <= 4 kA): the prefixes stay here for step 1b
+  int want_all = 0, hit_all = 0;
+  for (int i0 = 0; i0 < n; i0 += 4 * kA) {
+    const int i = i0 + 4 * tid;
+    int hv[4], ws = 0, hs = 0;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int iu = min(i + u, n - 1);   // clamped: every load issued at once
+      wv[u] = w.want[iu];
+      hv[u] = w.hit[iu];
+      if (i + u >= n) wv[u] = hv[u] = 0;
+      ws += wv[u];
+      hs += hv[u];
+    }
+    int tw, th;
+    int pw = want_all + ech::block_excl_scan<kA>(ws, scr, &tw);
+    int ph = hit_all + ech::block_excl_scan<kA>(hs, scr, &th);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      ew[u] = pw;
+      if (i + u < n && (i + u) % w.nbr == 0) {
+        s_seg[(i + u) / w.nbr] = pw;
+        s_hseg[(i + u) / w.nbr] = ph;
+      }
+      pw += wv[u];
+      ph += hv[u];
+    }
+    want_all += tw;
+    hit_all += th;
+  }
+  if (tid == 0) {
+    s_seg[nseq] = want_all;
+    s_hseg[nseq] = hit_all;
+  }
+  __syncthreads();
+  // per sequence: the misses it takes (EARLY: at most cap) and the rank of its first
+  int n_want = 0;
+  for (int b0 = 0; b0 < nseq; b0 += kA) {
+    const int b = b0 + tid;
+    int take_b = 0;
+    if (b < nseq) {
+      const int want_b = s_seg[b + 1] - s_seg[b];
+      take_b = (phase == ECH_EARLY) ? min(cap, want_b) : want_b;
+      s_take[b] = take_b;
+    }
+    int tot;
+    const int ex = ech::block_excl_scan<kA>(take_b, scr, &tot);
+    if (b < nseq) s_rowoff[b] = n_want + ex;
+    n_want += tot;
+  }
+  const bool clamped = n_want > w.M_max;   // only when a caller contract is broken
+  if (clamped) n_want = w.M_max;
+  __syncthreads();
+  // ---- 1b. every block: the rank of its first miss and its sequence's limit
+  if (n <= 4 * kA) {
+    const int i = 4 * tid;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      if (i + u < n) {
+        const int bi = (i + u) / w.nbr;
+        w.off[i + u] = s_rowoff[bi] + (ew[u] - s_seg[bi]);
+        w.lim[i + u] = s_rowoff[bi] + s_take[bi];
+      }
+    }
+  } else {
+    int run = 0;   // the same scan again
+    for (int i0 = 0; i0 < n; i0 += 4 * kA) {
+      const int i = i0 + 4 * tid;
+      int ws = 0;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        wv[u] = w.want[min(i + u, n - 1)];
+        if (i + u >= n) wv[u] = 0;
+        ws += wv[u];
+      }
+      int tw;
+      int pw = run + ech::block_excl_scan<kA>(ws, scr, &tw);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        if (i + u < n) {
+          const int bi = (i + u) / w.nbr;
+          w.off[i + u] = s_rowoff[bi] + (pw - s_seg[bi]);
+          w.lim[i + u] = s_rowoff[bi] + s_take[bi];
+        }
+        pw += wv[u];
+      }
+      run += tw;
+    }
+  }
+  // ---- 2. free slots in ring order from the head
+  int found = 0;
+  for (int i0 = 0; i0 < C && found < n_want; i0 += kWin) {   // block-uniform
+#pragma unroll
+    for (int j = 0; j < kWin / kA; ++j) {   // coalesced loads, all in flight
+      const int pos = i0 + j * kA + tid;
+      int p = head + min(pos, C - 1);   // clamped: every load issued at once
+      if (p >= C) p -= C;
+      const int pv = slot_pin[p];
+      s_fr[j * kA + tid] = (pos < C && pv != ep) ? 1 : 0;
+    }
+    __syncthreads();
+    // thread t ranks positions i0 + 16t .. +15 (one 16-byte LDS read)
+    const uint4 f0 = reinterpret_cast<const uint4*>(s_fr)[tid];
+    const uint32_t fw[4] = {f0.x, f0.y, f0.z, f0.w};
+    int cnt = 0;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) cnt += __popc(fw[q]);   // flags are 0/1 bytes
+    int tot;
+    int rank = found + ech::block_excl_scan<kA>(cnt, scr, &tot);
+    const int wlast = found + tot - 1;   // rank of the window's last free slot
+    if (rank < n_want) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          if ((fw[q] >> (8 * e)) & 1u) {
+            if (rank < n_want) {
+              int p = head + i0 + 16 * tid + 4 * q + e;
+              if (p >= C) p -= C;
+              w.freelist[rank] = p;
+              if (rank == n_want - 1) s_last = p;
+              if (rank == wlast) s_lastw = p;
+            }
+            ++rank;
+          }
+        }
+      }
+    }
+    found += tot;
+    __syncthreads();   // s_fr is rewritten by the next window
+  }
+  const int n_alloc = min(n_want, found);
+  // ---- 3. statistics and counters
+  for (int b = tid; b < nseq; b += kA) {
+    const int fetched = max(0, min(n_alloc - s_rowoff[b], s_take[b]));
+    int32_t* st = stats + 4 * b;
+    st[0] = s_hseg[b + 1] - s_hseg[b];
+    st[1] = fetched;
+    st[2] = (s_seg[b + 1] - s_seg[b]) - fetched;   // wanted (before the cap) and not fetched
+    st[3] = 0;
+  }
+  if (tid == 0) {
+    w.sc[S_EP] = ep;
+    w.sc[S_NWANT] = n_want;
+    w.sc[S_NALLOC] = n_alloc;
+    ctr[phase == ECH_EARLY ? ECH_CTR_NMISS_EARLY : ECH_CTR_NMISS] = n_alloc;
+    ctr[ECH_CTR_NWANT] = n_want;
+    ctr[ECH_CTR_NPINNED] = hit_all;
+    ctr[ECH_CTR_NEVICT] = 0;
+    ctr[ECH_CTR_EPOCH] = ep;
+    if (n_alloc > 0) {
+      const int last = (n_alloc == n_want) ? s_last : s_lastw;
+      ctr[ECH_CTR_HEAD] = (last + 1 == C) ? 0 : last + 1;
+    }
+    if ((phase != ECH_EARLY && n_want > found) || clamped) ctr[ECH_CTR_STATUS] |= ECH_ST_OVERFLOW;
+  }
+}
+
 // ------------------------------------------------------------------ pin / count
+// Each block pins the slots of its resident selection with the new epoch
+// (slot_pin[s] = epoch), counts hits and misses and lists its misses in
+// order.
+
 // FINAL: grid (nbj, B), one idx entry per thread.
 __global__ __launch_bounds__(kT) void pin_final_kernel(const int32_t* __restrict__ idx, int k,
                                                        const int64_t* __restrict__ tok0,
@@ -112,20 +299,23 @@ __global__ __launch_bounds__(kT) void pin_final_kernel(const int32_t* __restrict
                                                        int32_t* ctr, CWs w) {
   __shared__ int scr[kT / 64];
   const int b = blockIdx.y, j = blockIdx.x * kT + threadIdx.x;
+  const int blk = b * gridDim.x + blockIdx.x;
   const int ep = ctr[ECH_CTR_EPOCH] + 1;
-  int hit = 0, miss = 0;
+  int hit = 0, miss = 0, g = -1;
+  size_t e = 0;
   if (j < k) {
-    const size_t e = (size_t)b * k + j;
+    e = (size_t)b * k + j;
     const int t = idx[e];
     int sl = -1;
     if (t >= 0) {
       if (t >= lens[b]) {
         set_status(ctr, ECH_ST_BADTOK);
       } else {
-        const int64_t g = tok0[b] + t;
-        if (g < 0 || g >= w.P) {
+        const int64_t gg = tok0[b] + t;
+        if (gg < 0 || gg >= w.P) {
           set_status(ctr, ECH_ST_BADTOK);
         } else {
+          g = (int)gg;
           sl = tok2slot[g];
           if (sl >= 0 && sl < w.C) {
             slot_pin[sl] = ep;
@@ -139,10 +329,11 @@ __global__ __launch_bounds__(kT) void pin_final_kernel(const int32_t* __restrict
     }
     sel_slot[e] = sl;
   }
+  int nm;
+  const int r = ech::block_excl_scan<kT>(miss, scr, &nm);
+  if (miss) w.lmiss[(size_t)blk * w.lcap + r] = make_int2(g, (int)e);
   const int nh = ech::block_sum<kT>(hit, scr);
-  const int nm = ech::block_sum<kT>(miss, scr);
   if (threadIdx.x == 0) {
-    const int blk = b * gridDim.x + blockIdx.x;
     w.hit[blk] = nh;
     w.want[blk] = nm;
   }
@@ -173,32 +364,47 @@ __global__ __launch_bounds__(kT) void pin_early_kernel(const float* __restrict__
                                                        int32_t* __restrict__ slot_pin, int32_t* ctr, CWs w) {
   __shared__ int scr[kT / 64];
   const int b = blockIdx.y;
+  const int blk = b * gridDim.x + blockIdx.x;
   const int len = lens[b];
   const float th = theta[b];
   const int ep = ctr[ECH_CTR_EPOCH] + 1;
   const int t = blockIdx.x * kBlk + threadIdx.x * kPer;
+  const int64_t g0 = tok0[b] + t;
   int hit = 0, want = 0;
+  uint32_t miss_mask = 0;   // bit i: token t + i is a miss
   if (th == th && t < len) {
     float v[kPer];
     load16(logits + (size_t)b * ld, t, len, v);
-    const int64_t g0 = tok0[b] + t;
+    uint32_t above = 0;
 #pragma unroll
-    for (int i = 0; i < kPer; ++i) {
-      if (t + i < len && v[i] > th && g0 + i < w.P) {
-        const int sl = tok2slot[g0 + i];
-        if (sl >= 0 && sl < w.C) {
-          slot_pin[sl] = ep;
-          ++hit;
-        } else {
-          ++want;
+    for (int i = 0; i < kPer; ++i)
+      above |= (t + i < len && v[i] > th && g0 + i < w.P) ? 1u << i : 0u;
+    if (above) {
+      // all sixteen lookups in flight at once (addresses clamped into the
+      // map; only the flagged ones are used)
+      int sl[kPer];
+#pragma unroll
+      for (int i = 0; i < kPer; ++i) sl[i] = tok2slot[min(max(g0 + i, (int64_t)0), (int64_t)w.P - 1)];
+#pragma unroll
+      for (int i = 0; i < kPer; ++i) {
+        if ((above >> i) & 1u) {
+          if (sl[i] >= 0 && sl[i] < w.C) {
+            slot_pin[sl[i]] = ep;
+            ++hit;
+          } else {
+            miss_mask |= 1u << i;
+            ++want;
+          }
         }
       }
     }
   }
+  int nw;
+  int r = ech::block_excl_scan<kT>(want, scr, &nw);
+  for (uint32_t mm = miss_mask; mm != 0u && r < w.lcap; mm &= mm - 1u, ++r)
+    w.lmiss[(size_t)blk * w.lcap + r] = make_int2((int)(g0 + __builtin_ctz(mm)), b);
   const int nh = ech::block_sum<kT>(hit, scr);
-  const int nw = ech::block_sum<kT>(want, scr);
   if (threadIdx.x == 0) {
-    const int blk = b * gridDim.x + blockIdx.x;
     w.hit[blk] = nh;
     w.want[blk] = nw;
   }
@@ -231,292 +437,103 @@ __global__ __launch_bounds__(kT) void pin_prefill_kernel(const int32_t* __restri
   else if (sl == -1) tok2slot[g] = -2;   // every claimer writes the same value: no atomic needed
 }
 
-// PREFILL: grid (nch), count claimed tokens per block of the token range.
+// PREFILL: grid (nch), 16 consecutive tokens per thread: the claimed tokens
+// of each block of the token range (its misses, in order) and its pinned
+// resident tokens (one per pinned slot: a slot holds one token).
 __global__ __launch_bounds__(kT) void count_claimed_kernel(const int64_t* __restrict__ tok0p,
                                                            const int32_t* __restrict__ lenp,
-                                                           const int32_t* __restrict__ tok2slot, CWs w) {
+                                                           const int32_t* __restrict__ tok2slot,
+                                                           const int32_t* __restrict__ slot_pin, const int32_t* ctr,
+                                                           CWs w) {
   __shared__ int scr[kT / 64];
   const int64_t tok0 = tok0p[0];
   const int len = lenp[0];
-  const int t = blockIdx.x * kBlk + threadIdx.x * kPer;
-  int n = 0;
-  for (int i = 0; i < kPer; ++i)
-    if (t + i < len && tok0 + t + i < w.P && tok2slot[tok0 + t + i] == -2) ++n;
-  const int tot = ech::block_sum<kT>(n, scr);
-  if (threadIdx.x == 0) {
-    w.want[blockIdx.x] = tot;
-    w.hit[blockIdx.x] = 0;
-  }
-}
-
-// grid (ns): unpinned slots per block, ring positions i -> slot (head + i) % C.
-__global__ __launch_bounds__(kT) void count_free_kernel(const int32_t* __restrict__ slot_pin, int32_t C,
-                                                        const int32_t* ctr, CWs w) {
-  __shared__ int scr[kT / 64];
-  const int head = ctr[ECH_CTR_HEAD];
   const int ep = ctr[ECH_CTR_EPOCH] + 1;
-  const int i0 = blockIdx.x * kBlk + threadIdx.x * kPer;
-  int n = 0;
-  for (int i = 0; i < kPer; ++i) {
-    const int pos = i0 + i;
-    if (pos < C) {
-      int p = head + pos;
-      if (p >= C) p -= C;
-      n += slot_pin[p] != ep;
+  const int t = blockIdx.x * kBlk + threadIdx.x * kPer;
+  const int64_t g0 = tok0 + t;
+  int want = 0, pinned = 0;
+  uint32_t miss_mask = 0;   // bit i: token t + i is claimed
+  if (t < len && g0 < w.P) {
+    int sl[kPer];
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) sl[i] = tok2slot[min(max(g0 + i, (int64_t)0), (int64_t)w.P - 1)];   // all in flight
+    int pe[kPer];
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) pe[i] = slot_pin[min(max(sl[i], 0), w.C - 1)];   // clamped, used only for slots in range
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      if (t + i < len && g0 + i < w.P) {
+        if (sl[i] == -2) {
+          miss_mask |= 1u << i;
+          ++want;
+        } else if (sl[i] >= 0 && sl[i] < w.C && pe[i] == ep) {
+          ++pinned;
+        }
+      }
     }
   }
-  const int tot = ech::block_sum<kT>(n, scr);
-  if (threadIdx.x == 0) w.nfree[blockIdx.x] = tot;
-}
-
-// ------------------------------------------------------------------ scan
-
-template <int NT>
-__global__ __launch_bounds__(NT) void scan_kernel(int phase, int B, int cap, int32_t C, int32_t* ctr,
-                                                   int32_t* __restrict__ stats, CWs w) {
-  __shared__ int scr[NT / 64];
-  __shared__ int s_rowoff[NT], s_take[NT], s_seg[NT];
-  // free slots: exclusive scan over slot blocks (chunks of NT)
-  int nfree_tot = 0;
-  for (int b0 = 0; b0 < w.ns; b0 += NT) {
-    const int i = b0 + threadIdx.x;
-    const int v = i < w.ns ? w.nfree[i] : 0;
-    int tot;
-    const int ex = ech::block_excl_scan<NT>(v, scr, &tot);
-    if (i < w.ns) w.soff[i] = nfree_tot + ex;
-    nfree_tot += tot;
-  }
-  // misses: the entry blocks are sequence-major (b * nbr + c). One flat
-  // exclusive scan of the want counts gives every block's prefix (kept in off
-  // for now) and, at the segment boundaries, every sequence's total; the hit
-  // counts get the same scan (prefixes kept in lim for now). All threads
-  // take part, however many blocks a sequence has.
-  const int nseq = (phase == ECH_PREFILL) ? 1 : B;
-  const int n = nseq * w.nbr;
-  int want_all = 0, hit_all = 0;
-  for (int i0 = 0; i0 < n; i0 += NT) {
-    const int i = i0 + threadIdx.x;
-    int tw, th;
-    const int ew = ech::block_excl_scan<NT>(i < n ? w.want[i] : 0, scr, &tw);
-    const int eh = ech::block_excl_scan<NT>(i < n ? w.hit[i] : 0, scr, &th);
-    if (i < n) {
-      w.off[i] = want_all + ew;
-      w.lim[i] = hit_all + eh;
-    }
-    want_all += tw;
-    hit_all += th;
-  }
-  __syncthreads();   // the prefixes in off and lim are read across threads below
-  const int b = threadIdx.x;
-  int want_b = 0, hit_b = 0, seg = 0;
-  if (b < nseq) {
-    seg = w.off[b * w.nbr];
-    want_b = (b + 1 < nseq ? w.off[(b + 1) * w.nbr] : want_all) - seg;
-    hit_b = (b + 1 < nseq ? w.lim[(b + 1) * w.nbr] : hit_all) - w.lim[b * w.nbr];
-  }
-  const int take_b = (phase == ECH_EARLY) ? min(cap, want_b) : want_b;
-  int n_want;
-  const int row_off = ech::block_excl_scan<NT>(b < nseq ? take_b : 0, scr, &n_want);
-  const bool clamped = n_want > w.M_max;   // only when a caller contract is broken
-  if (clamped) n_want = w.M_max;
-  const int n_alloc = min(n_want, nfree_tot);
-  if (b < nseq) {
-    s_rowoff[b] = row_off;
-    s_take[b] = take_b;
-    s_seg[b] = seg;
-  }
-  __syncthreads();
-  // every block: its first miss's rank and its sequence's rank limit
-  for (int i = threadIdx.x; i < n; i += NT) {
-    const int bi = i / w.nbr;
-    w.off[i] = s_rowoff[bi] + (w.off[i] - s_seg[bi]);
-    w.lim[i] = s_rowoff[bi] + s_take[bi];
-  }
-  if (b < nseq) {
-    const int fetched = max(0, min(n_alloc - row_off, take_b));
-    int32_t* s = stats + 4 * b;
-    if (phase == ECH_PREFILL) {
-      s[0] = C - nfree_tot;          // resident union tokens = pinned slots
-    } else {
-      s[0] = hit_b;
-    }
-    s[1] = fetched;
-    s[2] = want_b - fetched;
-    s[3] = 0;
-  }
+  int nw;
+  int r = ech::block_excl_scan<kT>(want, scr, &nw);
+  for (uint32_t mm = miss_mask; mm != 0u; mm &= mm - 1u, ++r)
+    w.lmiss[(size_t)blockIdx.x * w.lcap + r] = make_int2((int)(g0 + __builtin_ctz(mm)), 0);
+  const int np = ech::block_sum<kT>(pinned, scr);
   if (threadIdx.x == 0) {
-    const int ep = ctr[ECH_CTR_EPOCH] + 1;
-    w.sc[S_EP] = ep;
-    w.sc[S_NWANT] = n_want;
-    w.sc[S_NALLOC] = n_alloc;
-    w.sc[S_HEAD] = ctr[ECH_CTR_HEAD];
-    w.sc[S_NFREE] = nfree_tot;
-    ctr[phase == ECH_EARLY ? ECH_CTR_NMISS_EARLY : ECH_CTR_NMISS] = n_alloc;
-    ctr[ECH_CTR_NWANT] = n_want;
-    ctr[ECH_CTR_NPINNED] = C - nfree_tot;
-    ctr[ECH_CTR_NEVICT] = 0;
-    if ((phase != ECH_EARLY && n_want > nfree_tot) || clamped) ctr[ECH_CTR_STATUS] |= ECH_ST_OVERFLOW;
-  }
-}
-
-// ------------------------------------------------------------------ emit
-// Blocks [0, ne) are entry blocks, [ne, ne + ns) slot blocks.
-struct EmitArgs {
-  int phase;
-  const int32_t* idx;
-  int k;
-  const int64_t* tok0;
-  const int32_t* lens;
-  const float* logits;
-  int64_t ld;
-  const float* theta;
-  const int32_t* tok2slot;
-  const int32_t* slot_pin;
-  int32_t C;
-  int nbj;
-};
-
-__global__ __launch_bounds__(kT) void emit_kernel(EmitArgs a, CWs w) {
-  __shared__ int scr[kT / 64];
-  const int n_want = w.sc[S_NWANT];
-  const int n_alloc = w.sc[S_NALLOC];
-  if ((int)blockIdx.x >= w.ne) {
-    // ---- slot role
-    const int sb = blockIdx.x - w.ne;
-    const int head = w.sc[S_HEAD], ep = w.sc[S_EP];
-    const int i0 = sb * kBlk + threadIdx.x * kPer;
-    bool fr[kPer];
-    int n = 0;
-#pragma unroll
-    for (int i = 0; i < kPer; ++i) {
-      const int pos = i0 + i;
-      fr[i] = false;
-      if (pos < a.C) {
-        int p = head + pos;
-        if (p >= a.C) p -= a.C;
-        fr[i] = a.slot_pin[p] != ep;
-      }
-      n += fr[i];
-    }
-    int tot;
-    int rank = w.soff[sb] + ech::block_excl_scan<kT>(n, scr, &tot);
-    if (w.soff[sb] >= n_alloc) return;
-#pragma unroll
-    for (int i = 0; i < kPer; ++i) {
-      if (!fr[i]) continue;
-      if (rank < n_alloc) {
-        int p = head + i0 + i;
-        if (p >= a.C) p -= a.C;
-        w.freelist[rank] = p;
-        if (rank == n_alloc - 1) w.sc[S_HEAD] = (p + 1 == a.C) ? 0 : p + 1;
-      }
-      ++rank;
-    }
-    return;
-  }
-  // ---- entry role
-  const int blk = blockIdx.x;
-  const int base = w.off[blk], lim = w.lim[blk];
-  if (a.phase == ECH_FINAL) {
-    const int b = blk / a.nbj, jb = blk % a.nbj;
-    const int j = jb * kT + threadIdx.x;
-    int g = -1;
-    bool m = false;
-    size_t e = 0;
-    if (j < a.k) {
-      e = (size_t)b * a.k + j;
-      const int t = a.idx[e];
-      if (t >= 0 && t < a.lens[b] && a.tok0[b] + t < w.P) {
-        g = (int)(a.tok0[b] + t);
-        m = a.tok2slot[g] < 0;
-      }
-    }
-    int tot;
-    const int rank = base + ech::block_excl_scan<kT>(m ? 1 : 0, scr, &tot);
-    if (m && rank < lim && rank < w.M_max) w.mcand[rank] = make_int2(g, (int)e);
-    (void)n_want;
-    return;
-  }
-  // EARLY / PREFILL: 16 consecutive tokens per thread
-  const int b = (a.phase == ECH_EARLY) ? blk / w.nbr : 0;
-  const int c = (a.phase == ECH_EARLY) ? blk % w.nbr : blk;
-  const int t = c * kBlk + threadIdx.x * kPer;
-  bool m[kPer];
-  int n = 0;
-  int64_t g0;
-  if (a.phase == ECH_EARLY) {
-    const int len = a.lens[b];
-    const float th = a.theta[b];
-    g0 = a.tok0[b] + t;
-    float v[kPer];
-    const bool live = th == th && t < len;
-    if (live) load16(a.logits + (size_t)b * a.ld, t, len, v);
-#pragma unroll
-    for (int i = 0; i < kPer; ++i) {
-      m[i] = live && t + i < len && v[i] > th && g0 + i < w.P && a.tok2slot[g0 + i] < 0;
-      n += m[i];
-    }
-  } else {
-    const int plen = a.lens[0];
-    g0 = a.tok0[0] + t;
-#pragma unroll
-    for (int i = 0; i < kPer; ++i) {
-      m[i] = t + i < plen && g0 + i < w.P && a.tok2slot[g0 + i] == -2;
-      n += m[i];
-    }
-  }
-  int tot;
-  int rank = base + ech::block_excl_scan<kT>(n, scr, &tot);
-#pragma unroll
-  for (int i = 0; i < kPer; ++i) {
-    if (!m[i]) continue;
-    if (rank < lim && rank < w.M_max) w.mcand[rank] = make_int2((int)(g0 + i), b);
-    ++rank;
+    w.want[blockIdx.x] = nw;
+    w.hit[blockIdx.x] = np;
   }
 }
 
 // ------------------------------------------------------------------ apply
-__global__ __launch_bounds__(kT) void apply_kernel(int phase, int k, int nseq, int32_t* __restrict__ tok2slot,
+// grid (ne, S): block (i, y) takes the slices y, y + S, ... (kT misses each)
+// of block i's miss list; S > 1 for the long lists of PREFILL token blocks.
+// Miss m (rank off[i] + j) takes freelist[m]: the slot's old token is
+// unmapped (no write-back), the maps point at each other, miss[m] = (g, slot).
+// The owner sequence of a block is fixed, so eviction counts are merged per
+// wave.
+__global__ __launch_bounds__(kT) void apply_kernel(int phase, int32_t* __restrict__ tok2slot,
                                                    int32_t* __restrict__ slot2tok, int32_t* __restrict__ slot_pin,
                                                    int32_t* __restrict__ miss, int32_t* ctr,
                                                    int32_t* __restrict__ sel_slot, int32_t* __restrict__ stats,
                                                    CWs w) {
-  const int n_want = w.sc[S_NWANT];
+  const int blk = blockIdx.x;
+  const int cnt = min(w.want[blk], w.lcap);
+  if ((int)blockIdx.y * kT >= cnt) return;   // block-uniform
   const int n_alloc = w.sc[S_NALLOC];
   const int ep = w.sc[S_EP];
-  if (blockIdx.x == 0 && threadIdx.x == 0) {
-    ctr[ECH_CTR_EPOCH] = ep;
-    if (n_alloc > 0) ctr[ECH_CTR_HEAD] = w.sc[S_HEAD];
-  }
-  for (int m = blockIdx.x * kT + threadIdx.x; m < n_want; m += gridDim.x * kT) {
-    const int2 mc = w.mcand[m];
-    const int g = mc.x;
-    const int owner = (phase == ECH_FINAL) ? mc.y / k : (phase == ECH_EARLY ? mc.y : 0);
-    if (g < 0 || g >= w.P || owner < 0 || owner >= nseq || (phase == ECH_FINAL && mc.y >= nseq * k)) {
-      set_status(ctr, ECH_ST_OVERFLOW);   // unreachable unless counts and ranks disagree
-      continue;
-    }
-    if (m < n_alloc) {
-      const int p = w.freelist[m];
-      if (p < 0 || p >= w.C) {
-        set_status(ctr, ECH_ST_OVERFLOW);
-        continue;
+  const int base = w.off[blk];
+  const int lim = min(w.lim[blk], w.sc[S_NWANT]);
+  const int owner = (phase == ECH_PREFILL) ? 0 : blk / w.nbr;
+  for (int i = blockIdx.y * kT + threadIdx.x; i < cnt; i += kT * gridDim.y) {   // trips differ only in the last pass
+    const int m = base + i;
+    bool evicted = false;
+    if (m < lim) {
+      const int2 mc = w.lmiss[(size_t)blk * w.lcap + i];
+      const int g = mc.x;
+      if (g < 0 || g >= w.P) {
+        set_status(ctr, ECH_ST_OVERFLOW);   // unreachable unless counts and lists disagree
+      } else if (m < n_alloc) {
+        const int p = w.freelist[m];
+        if (p < 0 || p >= w.C) {
+          set_status(ctr, ECH_ST_OVERFLOW);
+        } else {
+          const int u = slot2tok[p];
+          if (u >= 0 && u < w.P) {
+            tok2slot[u] = -1;   // evict; the host row stays where it is
+            evicted = true;
+          }
+          slot2tok[p] = g;
+          tok2slot[g] = p;
+          slot_pin[p] = ep;
+          miss[2 * m] = g;
+          miss[2 * m + 1] = p;
+          if (phase == ECH_FINAL) sel_slot[mc.y] = p;
+        }
+      } else if (phase == ECH_PREFILL) {
+        tok2slot[g] = -1;     // release the claim of a miss that got no slot
       }
-      const int u = slot2tok[p];
-      if (u >= 0 && u < w.P) {
-        tok2slot[u] = -1;   // evict; the host row stays where it is
-        atomicAdd(&ctr[ECH_CTR_NEVICT], 1);
-        atomicAdd(&stats[4 * owner + 3], 1);
-      }
-      slot2tok[p] = g;
-      tok2slot[g] = p;
-      slot_pin[p] = ep;
-      miss[2 * m] = g;
-      miss[2 * m + 1] = p;
-      if (phase == ECH_FINAL) sel_slot[mc.y] = p;
-    } else if (phase == ECH_PREFILL) {
-      tok2slot[g] = -1;     // release the claim of a miss that got no slot
     }
+    ech::wave_count(&ctr[ECH_CTR_NEVICT], evicted);
+    ech::wave_count(&stats[4 * owner + 3], evicted);
   }
 }
 
@@ -599,7 +616,8 @@ extern "C" int ech_cache_reset(int32_t* tok2slot, int64_t P, int32_t* slot2tok, 
 
 extern "C" size_t ech_cache_step_ws_bytes(int phase, int B, int R, int k, int max_len, int32_t C, int32_t M_max) {
   if (phase < ECH_EARLY || phase > ECH_PREFILL || B < 1 || k < 1 || max_len < 0 || C < 1 || M_max < 0) return 0;
-  return layout(phase, B, R, k, max_len, C, M_max, nullptr, nullptr);
+  (void)R;
+  return layout(phase, B, k, max_len, M_max, nullptr, nullptr);
 }
 
 extern "C" int ech_cache_step(int phase, int32_t* tok2slot, int64_t P, int32_t* slot2tok, int32_t* slot_pin,
@@ -629,15 +647,16 @@ extern "C" int ech_cache_step(int phase, int32_t* tok2slot, int64_t P, int32_t* 
   if ((int64_t)M_max < demand) return ECH_EINVAL;
   if (ws_bytes < ech_cache_step_ws_bytes(phase, B, R, k, max_len, C, M_max)) return ECH_EINVAL;
   CWs w;
-  layout(phase, B, R, k, max_len, C, M_max, &w, static_cast<char*>(ws));
+  layout(phase, B, k, max_len, M_max, &w, static_cast<char*>(ws));
   w.P = (int)P;
   w.C = C;
   w.M_max = M_max;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   const int nbj = (k + kT - 1) / kT;
+  // count, allocate, apply
   if (phase == ECH_FINAL) {
-    hipLaunchKernelGGL(pin_final_kernel, dim3(nbj, B), dim3(kT), 0, s, idx, k, seq_tok0, seq_len, tok2slot, slot_pin,
-                       sel_slot, ctr, w);
+    hipLaunchKernelGGL(pin_final_kernel, dim3(nbj, B), dim3(kT), 0, s, idx, k, seq_tok0, seq_len, tok2slot,
+                       slot_pin, sel_slot, ctr, w);
   } else if (phase == ECH_EARLY) {
     hipLaunchKernelGGL(pin_early_kernel, dim3(w.nbr, B), dim3(kT), 0, s, logits, ld, theta, seq_tok0, seq_len,
                        tok2slot, slot_pin, ctr, w);
@@ -645,36 +664,15 @@ extern "C" int ech_cache_step(int phase, int32_t* tok2slot, int64_t P, int32_t* 
     hipLaunchKernelGGL(pin_prefill_kernel, dim3(nbj, R), dim3(kT), 0, s, idx, k, seq_tok0, seq_len, tok2slot,
                        slot_pin, ctr, w);
     ECH_LAUNCH_CHECK();
-    hipLaunchKernelGGL(count_claimed_kernel, dim3(w.ne), dim3(kT), 0, s, seq_tok0, seq_len, tok2slot, w);
+    hipLaunchKernelGGL(count_claimed_kernel, dim3(w.ne), dim3(kT), 0, s, seq_tok0, seq_len, tok2slot, slot_pin, ctr,
+                       w);
   }
   ECH_LAUNCH_CHECK();
-  hipLaunchKernelGGL(count_free_kernel, dim3(w.ns), dim3(kT), 0, s, slot_pin, C, ctr, w);
+  hipLaunchKernelGGL(allocate_kernel, dim3(1), dim3(kA), 0, s, phase, phase == ECH_PREFILL ? 1 : B, cap, ctr,
+                     slot_pin, stats, w);
   ECH_LAUNCH_CHECK();
-  // one thread per sequence: 1024 for decode batches, 256 for the single
-  // prefill sequence (fits beside other work on a CU)
-  if (phase == ECH_PREFILL)
-    hipLaunchKernelGGL(scan_kernel<256>, dim3(1), dim3(256), 0, s, phase, B, cap, C, ctr, stats, w);
-  else
-    hipLaunchKernelGGL(scan_kernel<1024>, dim3(1), dim3(1024), 0, s, phase, B, cap, C, ctr, stats, w);
-  ECH_LAUNCH_CHECK();
-  EmitArgs ea;
-  ea.phase = phase;
-  ea.idx = idx;
-  ea.k = k;
-  ea.tok0 = seq_tok0;
-  ea.lens = seq_len;
-  ea.logits = logits;
-  ea.ld = ld;
-  ea.theta = theta;
-  ea.tok2slot = tok2slot;
-  ea.slot_pin = slot_pin;
-  ea.C = C;
-  ea.nbj = nbj;
-  hipLaunchKernelGGL(emit_kernel, dim3(w.ne + w.ns), dim3(kT), 0, s, ea, w);
-  ECH_LAUNCH_CHECK();
-  const int apply_blocks = (int)std::max<int64_t>(1, std::min<int64_t>(1024, (demand + kT - 1) / kT));
-  hipLaunchKernelGGL(apply_kernel, dim3(apply_blocks), dim3(kT), 0, s, phase, k, phase == ECH_PREFILL ? 1 : B,
-                     tok2slot, slot2tok, slot_pin, miss,
+  const int slices = (phase == ECH_PREFILL) ? w.lcap / kT : 1;
+  hipLaunchKernelGGL(apply_kernel, dim3(w.ne, slices), dim3(kT), 0, s, phase, tok2slot, slot2tok, slot_pin, miss,
                      ctr, sel_slot, stats, w);
   ECH_LAUNCH_CHECK();
   if (phase == ECH_PREFILL) {

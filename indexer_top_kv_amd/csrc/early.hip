@@ -394,10 +394,10 @@ __global__ __launch_bounds__(kT) void early_apply_kernel(int group, int b0, cons
   int rank = base + ech::block_excl_scan<kT>(n, scr, &tot);
   const int ep = ws.sc[E_EP];
   const int last = ws.grp[2 * group + 1] - 1;
+  int nev = 0;
 #pragma unroll
   for (int i = 0; i < kPer; ++i) {
-    if (!m[i]) continue;
-    if (rank < lim) {
+    if (m[i] && rank < lim) {
       const int g = (int)(g0 + t + i);
       const int p = ws.freelist[rank];
       if (p < 0 || p >= C) {
@@ -406,8 +406,7 @@ __global__ __launch_bounds__(kT) void early_apply_kernel(int group, int b0, cons
         const int u = slot2tok[p];
         if (u >= 0 && u < P) {
           tok2slot[u] = -1;   // evict; the host row stays where it is
-          atomicAdd(&ctr[ECH_CTR_NEVICT], 1);
-          atomicAdd(&stats[4 * b + 3], 1);
+          ++nev;
         }
         slot2tok[p] = g;
         tok2slot[g] = p;
@@ -417,7 +416,13 @@ __global__ __launch_bounds__(kT) void early_apply_kernel(int group, int b0, cons
         if (rank == last) ctr[ECH_CTR_HEAD] = (p + 1 == C) ? 0 : p + 1;
       }
     }
-    ++rank;
+    rank += m[i] ? 1 : 0;
+  }
+  // One eviction count per wave (the block serves one sequence b).
+  const int wev = ech::wave_sum(nev);
+  if (wev > 0 && ech::lane_id() == 0) {
+    atomicAdd(&ctr[ECH_CTR_NEVICT], wev);
+    atomicAdd(&stats[4 * b + 3], wev);
   }
 }
 

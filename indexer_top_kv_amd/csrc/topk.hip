@@ -208,13 +208,16 @@ __global__ __launch_bounds__(kT) void topk_hist_kernel(const float* __restrict__
 }
 
 // ------------------------------------------------------------------ T2
-// NT threads (1024 for a few long rows, 256 for many rows): thread
-// (part, b) sums bin (255 - b) over the chunks c = part, part + NT/256, ...,
-// eight independent loads in flight (a loop with one load per iteration
-// waits a full memory round trip per chunk).
+// NT threads (1024 for a few long rows, 256 for many rows). Wave w reads the
+// chunk histograms w, w + kW, ... with lane l holding bins 4l..4l+3 (one int4
+// per lane, a whole histogram per wave instruction, sixteen loads in flight).
+// Their sum is the row histogram, which fixes b*; the same registers then give
+// each chunk's count over bins >= b* (a row of at most 16 kW chunks is read
+// once).
 template <int NT>
 __global__ __launch_bounds__(NT) void topk_rowsel_kernel(const int32_t* __restrict__ lens, int k, Ws ws) {
-  constexpr int kParts = NT / 256;
+  constexpr int kW = NT / 64;
+  constexpr int kPass = 16 * kW;   // chunks per pass
   const int r = blockIdx.x;
   const int len = lens[r];
   RowState& st = ws.rs[r];
@@ -229,34 +232,51 @@ __global__ __launch_bounds__(NT) void topk_rowsel_kernel(const int32_t* __restri
     return;
   }
   const int nch = (len + kChunk - 1) / kChunk;
-  __shared__ int part_sum[kParts][256];
+  __shared__ int4 part_sum[kW][64];
+  __shared__ int s_cnt[kMaxChunks];
   __shared__ int scratch[NT / 64];
   __shared__ int s_bstar, s_nbin;
-  const int b = threadIdx.x & 255, part = threadIdx.x >> 8;
-  const int bin = 255 - b;
-  const int* h = ws.hist + (size_t)r * ws.nch * 256 + bin;
-  int acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-  int c = part;
-  for (; c + 7 * kParts < nch; c += 8 * kParts) {
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int4* h4 = reinterpret_cast<const int4*>(ws.hist + (size_t)r * ws.nch * 256) + lane;
+  int4 q[16];
+  auto load_pass = [&](int c0) {
 #pragma unroll
-    for (int u = 0; u < 8; ++u) acc[u] += h[(size_t)(c + kParts * u) * 256];
+    for (int u = 0; u < 16; ++u) {
+      const int cc = c0 + wv + kW * u;
+      q[u] = cc < nch ? h4[(size_t)cc * 64] : int4{0, 0, 0, 0};
+    }
+  };
+  {
+    int4 acc = {0, 0, 0, 0};
+    for (int c0 = 0; c0 < nch; c0 += kPass) {
+      load_pass(c0);
+#pragma unroll
+      for (int u = 0; u < 16; ++u) {
+        acc.x += q[u].x;
+        acc.y += q[u].y;
+        acc.z += q[u].z;
+        acc.w += q[u].w;
+      }
+    }
+    part_sum[wv][lane] = acc;
   }
-  for (; c < nch; c += kParts) acc[0] += h[(size_t)c * 256];
-  part_sum[part][b] = acc[0] + acc[1] + acc[2] + acc[3] + acc[4] + acc[5] + acc[6] + acc[7];
   __syncthreads();
   // threads 0..255 hold bins 255..0 in order; the rest add zeros after them
-  int cnt = 0;
-  if (threadIdx.x < 256) {
+  {
+    const int bin = 255 - (int)(threadIdx.x & 255);
+    int cnt = 0;
+    if (threadIdx.x < 256) {
 #pragma unroll
-    for (int pp = 0; pp < kParts; ++pp) cnt += part_sum[pp][b];
-  }
-  int tot;
-  const int above = ech::block_excl_scan<NT>(cnt, scratch, &tot);
-  if (threadIdx.x < 256 && above < k && above + cnt >= k) {
-    s_bstar = bin;
-    s_nbin = cnt;
-    st.bstar = bin;
-    st.need = k - above;
+      for (int w = 0; w < kW; ++w) cnt += reinterpret_cast<const int*>(part_sum[w])[bin];
+    }
+    int tot;
+    const int above = ech::block_excl_scan<NT>(cnt, scratch, &tot);
+    if (threadIdx.x < 256 && above < k && above + cnt >= k) {
+      s_bstar = bin;
+      s_nbin = cnt;
+      st.bstar = bin;
+      st.need = k - above;
+    }
   }
   __syncthreads();
   const int bstar = s_bstar;
@@ -265,33 +285,44 @@ __global__ __launch_bounds__(NT) void topk_rowsel_kernel(const int32_t* __restri
     st.mode = wide ? kWide : kNormal;
     st.refine = 0;
   }
-  // List offsets: chunk c holds the sum over bins >= b* of its histogram.
-  // Wide rows keep instead, per chunk, the count of bins > b* (in take), for
-  // the refinement. Four adjacent threads share a chunk (16 int4 loads each,
-  // all in flight).
+  // Per chunk, the count over bins >= tb: list sizes for normal rows (their
+  // exclusive scan gives the list offsets); for wide rows the count of bins
+  // above b* (kept in take, for the refinement).
   const int tb = wide ? bstar + 1 : bstar;
-  int run = 0;
-  const int sub = threadIdx.x & 3;
-  for (int c0 = 0; c0 < nch; c0 += NT / 4) {
-    const int c = c0 + (int)threadIdx.x / 4;
-    int n = 0;
-    if (c < nch) {
-      const int4* hc = reinterpret_cast<const int4*>(ws.hist + ((size_t)r * ws.nch + c) * 256) + 16 * sub;
-      int4 q[16];
+  for (int c0 = 0; c0 < nch; c0 += kPass) {
+    if (nch > kPass) load_pass(c0);   // one pass: q still holds it
+    int p[16];
+    const int b0 = 4 * lane;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) q[i] = hc[i];
+    for (int u = 0; u < 16; ++u)
+      p[u] = (b0 >= tb ? q[u].x : 0) + (b0 + 1 >= tb ? q[u].y : 0) + (b0 + 2 >= tb ? q[u].z : 0) +
+             (b0 + 3 >= tb ? q[u].w : 0);
+    // Sum each p[u] over the wave, halving the values per lane at each step:
+    // lane l ends with the total of u = (l >> 2) & 15.
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int b0 = 64 * sub + 4 * i;
-        n += (b0 >= tb ? q[i].x : 0) + (b0 + 1 >= tb ? q[i].y : 0) + (b0 + 2 >= tb ? q[i].z : 0) +
-             (b0 + 3 >= tb ? q[i].w : 0);
+    for (int m = 32, n = 16; m >= 4; m >>= 1, n >>= 1) {
+      const bool hi = (lane & m) != 0;
+#pragma unroll
+      for (int j = 0; j < n / 2; ++j) {
+        const int keep = hi ? p[j + n / 2] : p[j];
+        const int give = hi ? p[j] : p[j + n / 2];
+        p[j] = keep + __shfl_xor(give, m, 64);
       }
     }
-    n += __shfl_xor(n, 1, 64);
+    int n = p[0];
     n += __shfl_xor(n, 2, 64);
+    n += __shfl_xor(n, 1, 64);
+    const int cc = c0 + wv + kW * ((lane >> 2) & 15);
+    if ((lane & 3) == 0 && cc < nch) s_cnt[cc] = n;
+  }
+  __syncthreads();
+  int run = 0;
+  for (int c0 = 0; c0 < nch; c0 += NT) {
+    const int c = c0 + (int)threadIdx.x;
+    const int n = c < nch ? s_cnt[c] : 0;
     int t;
-    const int pre = ech::block_excl_scan<NT>(sub == 0 ? n : 0, scratch, &t);
-    if (c < nch && sub == 0) {
+    const int pre = ech::block_excl_scan<NT>(n, scratch, &t);
+    if (c < nch) {
       if (wide) ws.take[(size_t)r * ws.nch + c] = n;
       else ws.off[(size_t)r * ws.nch + c] = run + pre;
     }
@@ -806,56 +837,60 @@ __global__ __launch_bounds__(NT) void topk_resolve_kernel(const float* __restric
 }
 
 // ------------------------------------------------------------------ T5
+// grid (gx, R): block x takes the chunks x, x + gx, ... of row r. Rows
+// written from the list leave at once, so gx stays small: with long rows a
+// block per chunk would be hundreds of workgroups that only read the mode.
 __global__ __launch_bounds__(kT) void topk_compact_kernel(const float* __restrict__ logits, int64_t ld,
                                                           const int32_t* __restrict__ lens, int k,
                                                           int32_t* __restrict__ idx, Ws ws) {
-  const int r = blockIdx.y, c = blockIdx.x;
+  const int r = blockIdx.y;
   const int len = lens[r];
   int32_t* orow = idx + (size_t)r * k;
-  if (c == 0) {
+  if (blockIdx.x == 0) {
     for (int j = min(k, len) + threadIdx.x; j < k; j += kT) orow[j] = -1;
   }
-  const int lo = c * kChunk;
-  if (lo >= len) return;
   // Most rows were written by T4 from the list: check before reading scores.
   const RowState st = ws.rs[r];
   if (st.mode == kEmpty || st.mode == kNormal) return;
-  const int hi = min(lo + kChunk, len);
-  float4 v[kVec];
-  load_chunk(logits + (size_t)r * ld, lo, hi, v);
   const float sp = st.spred;
-  const int base = ws.off[(size_t)r * ws.nch + c];
-  const int te = ws.take[(size_t)r * ws.nch + c];
   __shared__ int scratch[kT / 64];
-  int gt_run = 0, eq_run = 0;   // block-uniform running counts
+  for (int c = blockIdx.x; c * kChunk < len; c += gridDim.x) {   // block-uniform trip count
+    const int lo = c * kChunk;
+    const int hi = min(lo + kChunk, len);
+    float4 v[kVec];
+    load_chunk(logits + (size_t)r * ld, lo, hi, v);
+    const int base = ws.off[(size_t)r * ws.nch + c];
+    const int te = ws.take[(size_t)r * ws.nch + c];
+    int gt_run = 0, eq_run = 0;   // block-uniform running counts
 #pragma unroll
-  for (int j = 0; j < kVec; ++j) {
-    const int t = lo + 4 * (j * kT + (int)threadIdx.x);
-    int ngt = 0, neq = 0;
+    for (int j = 0; j < kVec; ++j) {
+      const int t = lo + 4 * (j * kT + (int)threadIdx.x);
+      int ngt = 0, neq = 0;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const float x = f4(v[j], e);
-      const bool ok = t + e < hi;
-      ngt += (ok && x > sp) ? 1 : 0;
-      neq += (ok && x == sp) ? 1 : 0;
+      for (int e = 0; e < 4; ++e) {
+        const float x = f4(v[j], e);
+        const bool ok = t + e < hi;
+        ngt += (ok && x > sp) ? 1 : 0;
+        neq += (ok && x == sp) ? 1 : 0;
+      }
+      int tot;
+      const int pre = ech::block_excl_scan<kT>(ngt | (neq << 16), scratch, &tot);
+      int gt_b = gt_run + (pre & 0xffff);
+      int eq_b = eq_run + (pre >> 16);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float x = f4(v[j], e);
+        if (t + e >= hi) continue;
+        const bool gt = x > sp, eq = x == sp;
+        const bool sel = gt || (eq && eq_b < te);
+        const int pos = base + gt_b + min(eq_b, te);
+        if (sel && pos < k) orow[pos] = t + e;
+        gt_b += gt;
+        eq_b += eq;
+      }
+      gt_run += tot & 0xffff;
+      eq_run += tot >> 16;
     }
-    int tot;
-    const int pre = ech::block_excl_scan<kT>(ngt | (neq << 16), scratch, &tot);
-    int gt_b = gt_run + (pre & 0xffff);
-    int eq_b = eq_run + (pre >> 16);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const float x = f4(v[j], e);
-      if (t + e >= hi) continue;
-      const bool gt = x > sp, eq = x == sp;
-      const bool sel = gt || (eq && eq_b < te);
-      const int pos = base + gt_b + min(eq_b, te);
-      if (sel && pos < k) orow[pos] = t + e;
-      gt_b += gt;
-      eq_b += eq;
-    }
-    gt_run += tot & 0xffff;
-    eq_run += tot >> 16;
   }
 }
 
@@ -907,7 +942,8 @@ extern "C" int ech_topk(const float* logits, int64_t ld, const int32_t* row_len,
     hipLaunchKernelGGL(topk_resolve_kernel<256>, dim3(R), dim3(256), sizeof(int2) * w.cap, s, logits, ld, row_len,
                        k, theta_in, theta_out, kth, idx, w);
   ECH_LAUNCH_CHECK();
-  hipLaunchKernelGGL(topk_compact_kernel, gch, dim3(kT), 0, s, logits, ld, row_len, k, idx, w);
+  const int gx = std::max(1, std::min(w.nch, std::max(8, 256 / R)));
+  hipLaunchKernelGGL(topk_compact_kernel, dim3(gx, R), dim3(kT), 0, s, logits, ld, row_len, k, idx, w);
   ECH_LAUNCH_CHECK();
   return ECH_OK;
 }

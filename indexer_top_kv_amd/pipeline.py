@@ -1,4 +1,4 @@
-"""One layer of the path, launched in order on up to three streams.
+r"""One layer of the path, launched in order on up to three streams.
 
 Decode step (ECHO explainer, "The top-k dependency" and "Decode: fetch above
 a predicted threshold"): the recall of a step depends on its top-k; the early

@@ -223,3 +223,84 @@ def test_deterministic_replay():
                      host(gc.st.ctr).copy()))
     for a, b in zip(*outs):
         np.testing.assert_array_equal(a, b)
+
+
+def test_final_large_ring_many_windows():
+    """A ring of 40000 slots: the cold phase ranks 16384 free slots (several
+    windows of ring positions), later phases find their free slots between
+    pinned ones while the head wraps round the ring."""
+    need_gpu()
+    B, k = 8, 2048
+    lens = np.array([30000, 21000, 30000, 9000, 30000, 25001, 30000, 17777], np.int32)
+    tok0 = np.concatenate([[0], np.cumsum(lens)[:-1]]).astype(np.int64)
+    P, C = int(lens.sum()), 40000
+    gc = GpuCache(P, C, B, k, int(lens.max()))
+    sm = oracle.SlotMap(P, C)
+    base = _scores(17, B, int(lens.max()), 0)
+    wrapped = False
+    for step in range(10):
+        scores = base + (0.2 + 0.1 * step) * _scores(17, B, int(lens.max()), step + 1)
+        idx = _topk_idx(scores, lens, k)
+        head0 = sm.head
+        a_g, sel_g, st_g = gc.final(tok0, lens, idx)
+        a_o, sel_o, st_o = sm.final(tok0, idx)
+        assert a_g == a_o, step
+        np.testing.assert_array_equal(sel_g, sel_o)
+        np.testing.assert_array_equal(st_g, st_o)
+        gc.compare(sm)
+        wrapped |= sm.head < head0
+    assert wrapped
+
+
+def test_early_final_large_cap_many_windows():
+    """EARLY phases that want more than one window of free slots (cap 4000,
+    a low theta) on a 30000-slot ring, then FINAL, over several steps."""
+    need_gpu()
+    B, k, cap = 4, 2048, 4000
+    lens = np.array([40000, 40000, 23000, 40000], np.int32)
+    tok0 = np.concatenate([[0], np.cumsum(lens)[:-1]]).astype(np.int64)
+    P, C, ld = int(lens.sum()), 30000, 40000
+    gc = GpuCache(P, C, B, k, ld, cap=cap)
+    sm = oracle.SlotMap(P, C)
+    base = _scores(18, B, ld, 0)
+    n_early = []
+    for step in range(4):
+        scores = (base + 0.5 * _scores(18, B, ld, step + 1)).astype(np.float32)
+        theta = np.array([np.quantile(scores[b, :lens[b]], 0.85) for b in range(B)], np.float32)
+        theta[2] = np.nan if step == 1 else theta[2]
+        a_g, st_g = gc.early(tok0, lens, scores, theta)
+        a_o, st_o = sm.early(tok0, [scores[b, :lens[b]] for b in range(B)], theta, cap)
+        assert a_g == a_o, ('early', step)
+        np.testing.assert_array_equal(st_g, st_o)
+        gc.compare(sm)
+        n_early.append(len(a_o))
+        idx = _topk_idx(scores, lens, k)
+        a_g, sel_g, st_g = gc.final(tok0, lens, idx)
+        a_o, sel_o, st_o = sm.final(tok0, idx)
+        assert a_g == a_o, ('final', step)
+        np.testing.assert_array_equal(sel_g, sel_o)
+        np.testing.assert_array_equal(st_g, st_o)
+        gc.compare(sm)
+    assert n_early[0] > 8192   # the cold phase ranks free slots over several windows
+
+
+def test_prefill_large_union_many_windows():
+    """Prefill blocks whose union misses span several windows of ring
+    positions (64 rows x 2048 of a 60000-token sequence, 60000 slots)."""
+    need_gpu()
+    N, k, Rb, C = 60000, 2048, 64, 60000
+    gc = GpuCache(N, C, 1, k, N, R=Rb)
+    sm = oracle.SlotMap(N, C)
+    r = np.random.default_rng(19)
+    for blk in range(3):
+        row0 = 12000 + blk * 16000
+        idx = np.full((Rb, k), -1, np.int64)
+        for i in range(Rb):
+            vis = row0 + 211 * i + 1
+            idx[i] = np.sort(r.choice(vis, k, replace=False))
+        a_g, sel_g, st_g = gc.prefill(0, N, idx)
+        a_o, sel_o, st_o = sm.prefill_block(0, idx)
+        assert a_g == a_o, blk
+        np.testing.assert_array_equal(sel_g, sel_o)
+        np.testing.assert_array_equal(st_g, st_o)
+        gc.compare(sm)

@@ -132,3 +132,26 @@ def test_many_rows_theta_far_above_refined():
     theta = (kth * factor).astype(np.float32)
     theta[np.arange(R) % 16 == 3] = np.float32(14.0)       # constant rows: 4 x the score
     _check(x, lens, k, theta)
+
+
+def test_rows_longer_than_one_rowsel_pass():
+    """Rows whose chunk histograms take the row select more than one pass:
+    over 256 chunks of 4096 (1M tokens) with a few rows, over 64 chunks
+    (262144 tokens) with more than 256 rows. Predictions exact, absent and far
+    above the k-th score (a wide boundary bin)."""
+    need_gpu()
+    k = 2048
+    lens = [1_500_007, 1_100_000, 1_300_000]
+    x = wk.random_logits(12, 3, 1_500_008, 'normal')
+    kth = np.array([oracle.topk_row(x[r, :lens[r]], k)[1] for r in range(3)], np.float32)
+    theta = np.array([kth[0], np.nan, 3.0 * kth[2]], np.float32)
+    _check(x, lens, k, theta)
+
+    R = 260
+    lens = [3000 + 7 * r for r in range(R)]
+    lens[0], lens[100], lens[259] = 300_000, 400_003, 270_001
+    ld = ((max(lens) + 3) // 4) * 4
+    x = wk.random_logits(13, R, ld, 'normal')
+    kth = np.array([oracle.topk_row(x[r, :lens[r]], k)[1] for r in range(R)], np.float32)
+    factor = np.array([1.0, np.nan, 1.5, 3.0], np.float32)[np.arange(R) % 4]
+    _check(x, lens, k, (kth * factor).astype(np.float32))
