@@ -73,7 +73,7 @@ extern "C" {
 #define ECH_CTR_NWANT     6   /* misses the last phase wanted (before cap / slot limits) */
 #define ECH_CTR_NPINNED   7   /* slots pinned by the last phase */
 #define ECH_CTR_NMISS_EARLY 8 /* entries written to the miss list by the last EARLY phase */
-#define ECH_CTR_TICKET    9   /* allocator scratch counter (0 between calls; never write it) */
+#define ECH_CTR_TICKET    9   /* reserved: stays 0 */
 #define ECH_CTR_LEN      16
 
 /* ---- sticky status bits in ctr[ECH_CTR_STATUS] */

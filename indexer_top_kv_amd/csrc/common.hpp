@@ -101,26 +101,6 @@ __device__ __forceinline__ int block_excl_scan(int v, int* scratch, int* total) 
   return wbase + incl - v;
 }
 
-// True in exactly one block of the grid: the last to finish its stores. Each
-// block takes one ticket from ctr[ECH_CTR_TICKET] with atomicInc after a
-// release fence; the block drawing the last ticket wraps the counter back to
-// 0 (ready for the next launch) and may read every other block's results.
-// No block waits for another. Call from every thread of every block (it
-// contains __syncthreads()).
-__device__ __forceinline__ bool last_block(int32_t* ctr, int nblocks) {
-  __shared__ int s_last;
-  __threadfence();
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    const unsigned t = atomicInc(reinterpret_cast<unsigned*>(&ctr[ECH_CTR_TICKET]), (unsigned)(nblocks - 1));
-    s_last = (t == (unsigned)(nblocks - 1));
-  }
-  __syncthreads();
-  const bool last = s_last;
-  if (last) __threadfence();
-  return last;
-}
-
 template <int NT>
 __device__ __forceinline__ int block_sum(int v, int* scratch) {
   int tot;

@@ -15,18 +15,18 @@
 //     pin       grid (chunks, B): compact the chunk's resident tokens, score
 //               them with the same MFMA tile and epilogue as the scores kernel
 //               (bit-identical values), pin those above theta, count hits.
-//     free      grid (slot blocks): unpinned slots per block in ring order;
-//               the last block to finish scans the counts (free-slot rank of
-//               every block), sums the hits per sequence and advances the epoch.
-//     freelist  grid (slot blocks): slot of every free rank below the early
-//               demand bound, in ring order from the head.
+//     alloc     one workgroup: hits per sequence; the unpinned slots in ring
+//               order from the head, as far as the early demand bound needs
+//               (window by window), into the free list; advances the epoch.
 //   group [b0, b1), in ascending b0, once that group's scores are written
-//     want      grid (chunks, b1-b0): non-resident tokens above theta per
-//               block; the last block gives every sequence its rank range
-//               (continuing the ranks of earlier groups, capped per sequence).
-//     apply     grid (chunks, b1-b0): recompute the same flags in order; miss
-//               of rank m takes freelist[m] (evicting its old token, no
-//               write-back) and is written to the miss list at m.
+//     want      grid (chunks, b1-b0): each block lists its non-resident tokens
+//               above theta, in order.
+//     rank      one workgroup: every sequence's rank range (continuing the
+//               ranks of earlier groups, capped per sequence) and every
+//               block's first rank.
+//     apply     grid (chunks, b1-b0): a listed miss of rank m takes
+//               freelist[m] (evicting its old token, no write-back) and is
+//               written to the miss list at m.
 //   recall per group: the rows of the group's rank range.
 //
 // Only the pins depend on the whole batch, and they involve resident tokens
@@ -35,11 +35,6 @@
 // (an earlier group evicts only unpinned slots, i.e. resident tokens at or
 // below theta, and maps only its own tokens). So any grouping gives the same
 // maps, miss list and statistics as the single phase.
-//
-// "Last block" steps use a ticket counter in ctr[ECH_CTR_TICKET]: every block
-// takes one ticket with atomicInc after a release fence; the block that draws
-// the last one wraps the counter back to 0 and runs the step. No block waits
-// for another.
 
 #include <algorithm>
 
@@ -59,21 +54,20 @@ struct EWs {
   int* sc;        // [E_NSC] scalars
   int* grp;       // [2 * kMaxGroups] (begin, end) rank range of each group's allocations
   int* hitblk;    // [B * nch]
-  int* want;      // [B * nch]
+  int* want;      // [B * nch] misses per block (all of them)
   int* off;       // [B * nch] rank of the block's first miss
   int* lim;       // [B] rank limit of the sequence (cap)
-  int* seqd;      // [B] rank of a sequence's first miss minus its raw want prefix
-  int* nfree;     // [ns]
-  int* soff;      // [ns]
   int* freelist;  // [M_early]
-  int nch, ns;
+  int* lmiss;     // [B * nch][kBlk] the block's missed token ids, in order
+  int nch;
 };
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
+// sc and grp come first: ech_recall_group finds them without the sizes.
 size_t early_layout(int B, int max_len, int32_t C, int32_t M_early, EWs* w, char* base) {
+  (void)C;
   const int nch = std::max(1, (max_len + kBlk - 1) / kBlk);
-  const int ns = (int)((C + kBlk - 1) / kBlk);
   size_t o = 0;
   auto take = [&](size_t bytes) {
     size_t at = o;
@@ -82,9 +76,8 @@ size_t early_layout(int B, int max_len, int32_t C, int32_t M_early, EWs* w, char
   };
   const size_t o_sc = take(4 * E_NSC), o_grp = take(4 * 2 * kMaxGroups);
   const size_t o_hit = take(4 * (size_t)B * nch), o_want = take(4 * (size_t)B * nch),
-               o_off = take(4 * (size_t)B * nch), o_lim = take(4 * (size_t)B), o_sd = take(4 * (size_t)B),
-               o_nf = take(4 * (size_t)ns),
-               o_so = take(4 * (size_t)ns), o_fl = take(4 * (size_t)std::max(M_early, 1));
+               o_off = take(4 * (size_t)B * nch), o_lim = take(4 * (size_t)B),
+               o_fl = take(4 * (size_t)std::max(M_early, 1)), o_lm = take(4 * (size_t)B * nch * kBlk);
   if (w && base) {
     w->sc = reinterpret_cast<int*>(base + o_sc);
     w->grp = reinterpret_cast<int*>(base + o_grp);
@@ -92,12 +85,9 @@ size_t early_layout(int B, int max_len, int32_t C, int32_t M_early, EWs* w, char
     w->want = reinterpret_cast<int*>(base + o_want);
     w->off = reinterpret_cast<int*>(base + o_off);
     w->lim = reinterpret_cast<int*>(base + o_lim);
-    w->seqd = reinterpret_cast<int*>(base + o_sd);
-    w->nfree = reinterpret_cast<int*>(base + o_nf);
-    w->soff = reinterpret_cast<int*>(base + o_so);
     w->freelist = reinterpret_cast<int*>(base + o_fl);
+    w->lmiss = reinterpret_cast<int*>(base + o_lm);
     w->nch = nch;
-    w->ns = ns;
   }
   return o;
 }
@@ -131,14 +121,13 @@ __global__ __launch_bounds__(kT) void early_pin_kernel(const uint16_t* __restric
   const int t_first = lo + threadIdx.x * kPer;
   bool res[kPer];
   int n = 0;
+  int sl[kPer];   // all sixteen lookups in flight (clamped addresses; only tokens in the row used)
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) sl[i] = tok2slot[min(max(g0 + t_first + i, (int64_t)0), P - 1)];
 #pragma unroll
   for (int i = 0; i < kPer; ++i) {
     const int t = t_first + i;
-    res[i] = false;
-    if (t < len && g0 + t < P) {
-      const int sl = tok2slot[g0 + t];
-      res[i] = sl >= 0 && sl < C;
-    }
+    res[i] = t < len && g0 + t < P && sl[i] >= 0 && sl[i] < C;
     n += res[i];
   }
   int nres;
@@ -176,187 +165,233 @@ __global__ __launch_bounds__(kT) void early_pin_kernel(const uint16_t* __restric
   if (threadIdx.x == 0) *out = tot;
 }
 
-// ------------------------------------------------------------------ begin: free
-__device__ __forceinline__ void free_flags(const int32_t* __restrict__ slot_pin, int32_t C, int head, int ep,
-                                           int i0, bool (&fr)[kPer], int* n) {
-  int cnt = 0;
-#pragma unroll
-  for (int i = 0; i < kPer; ++i) {
-    const int pos = i0 + i;
-    fr[i] = false;
-    if (pos < C) {
-      int p = head + pos;
-      if (p >= C) p -= C;
-      fr[i] = slot_pin[p] != ep;
-    }
-    cnt += fr[i];
-  }
-  *n = cnt;
-}
+// ------------------------------------------------------------------ begin: alloc
+constexpr int kA = 1024;        // threads of the one-workgroup steps
+constexpr int kWin = kA * 16;   // ring positions per window
 
-__global__ __launch_bounds__(kT) void early_free_kernel(const int32_t* __restrict__ slot_pin, int32_t C, int B,
-                                                        int32_t* ctr, int32_t* __restrict__ stats, EWs ws) {
-  __shared__ int scr[kT / 64];
-  const int head = ctr[ECH_CTR_HEAD];
+__global__ __launch_bounds__(kA) void early_alloc_kernel(const int32_t* __restrict__ slot_pin, int32_t C, int B,
+                                                         int32_t M_early, int32_t* ctr,
+                                                         int32_t* __restrict__ stats, EWs ws) {
+  __shared__ int scr[kA / 64];
+  __shared__ __align__(16) uint8_t s_fr[kWin];
+  const int tid = threadIdx.x;
   const int ep = ctr[ECH_CTR_EPOCH] + 1;
-  bool fr[kPer];
-  int n;
-  free_flags(slot_pin, C, head, ep, blockIdx.x * kBlk + threadIdx.x * kPer, fr, &n);
-  const int tot = ech::block_sum<kT>(n, scr);
-  if (threadIdx.x == 0) ws.nfree[blockIdx.x] = tot;
-  if (!ech::last_block(ctr, gridDim.x)) return;
-  // free-slot rank of every block (ring order), total
-  int run = 0;
-  for (int b0 = 0; b0 < ws.ns; b0 += kT) {
-    const int i = b0 + threadIdx.x;
-    const int v = i < ws.ns ? ws.nfree[i] : 0;
-    int t;
-    const int ex = ech::block_excl_scan<kT>(v, scr, &t);
-    if (i < ws.ns) ws.soff[i] = run + ex;
-    run += t;
-  }
-  for (int b = threadIdx.x; b < B; b += kT) {
+  int head = ctr[ECH_CTR_HEAD];
+  if (head < 0 || head >= C) head = 0;   // only a corrupted state; keeps every slot index in range
+  // hits per sequence (the pinned slots: one per resident token above theta)
+  int hit_all = 0;
+  for (int b0 = 0; b0 < B; b0 += kA) {
+    const int b = b0 + tid;
     int h = 0;
-    for (int c = 0; c < ws.nch; ++c) h += ws.hitblk[(size_t)b * ws.nch + c];
-    int32_t* s = stats + 4 * b;
-    s[0] = h;
-    s[1] = 0;
-    s[2] = 0;
-    s[3] = 0;
+    if (b < B) {
+      const int* hb = ws.hitblk + (size_t)b * ws.nch;
+      int c = 0;
+      for (; c + 8 <= ws.nch; c += 8) {
+        int v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) v[u] = hb[c + u];   // all in flight
+#pragma unroll
+        for (int u = 0; u < 8; ++u) h += v[u];
+      }
+      for (; c < ws.nch; ++c) h += hb[c];
+      int32_t* st = stats + 4 * b;
+      st[0] = h;
+      st[1] = 0;
+      st[2] = 0;
+      st[3] = 0;
+    }
+    hit_all += ech::block_sum<kA>(h, scr);
   }
-  if (threadIdx.x == 0) {
+  // free slots in ring order from the head, up to the early demand bound
+  int found = 0;
+  for (int i0 = 0; i0 < C && found < M_early; i0 += kWin) {   // block-uniform
+#pragma unroll
+    for (int j = 0; j < kWin / kA; ++j) {   // coalesced loads, all in flight
+      const int pos = i0 + j * kA + tid;
+      int p = head + min(pos, C - 1);
+      if (p >= C) p -= C;
+      const int pv = slot_pin[p];
+      s_fr[j * kA + tid] = (pos < C && pv != ep) ? 1 : 0;
+    }
+    __syncthreads();
+    const uint4 f0 = reinterpret_cast<const uint4*>(s_fr)[tid];   // positions i0 + 16 tid .. +15
+    const uint32_t fw[4] = {f0.x, f0.y, f0.z, f0.w};
+    int cnt = 0;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) cnt += __popc(fw[q]);   // flags are 0/1 bytes
+    int tot;
+    int rank = found + ech::block_excl_scan<kA>(cnt, scr, &tot);
+    if (rank < M_early) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          if ((fw[q] >> (8 * e)) & 1u) {
+            if (rank < M_early) {
+              int p = head + i0 + 16 * tid + 4 * q + e;
+              if (p >= C) p -= C;
+              ws.freelist[rank] = p;
+            }
+            ++rank;
+          }
+        }
+      }
+    }
+    found += tot;
+    __syncthreads();   // s_fr is rewritten by the next window
+  }
+  if (tid == 0) {
     ws.sc[E_EP] = ep;
-    ws.sc[E_NFREE] = run;
+    ws.sc[E_NFREE] = min(found, M_early);   // the free slots any rank can take
     ws.sc[E_RUN] = 0;
     ws.sc[E_HEAD0] = head;
     ctr[ECH_CTR_EPOCH] = ep;
-    ctr[ECH_CTR_NPINNED] = C - run;
+    ctr[ECH_CTR_NPINNED] = hit_all;
     ctr[ECH_CTR_NEVICT] = 0;
     ctr[ECH_CTR_NWANT] = 0;
     ctr[ECH_CTR_NMISS_EARLY] = 0;
   }
 }
 
-__global__ __launch_bounds__(kT) void early_freelist_kernel(const int32_t* __restrict__ slot_pin, int32_t C,
-                                                            int32_t M_early, EWs ws) {
-  __shared__ int scr[kT / 64];
-  const int base = ws.soff[blockIdx.x];
-  const int lim = min(ws.sc[E_NFREE], M_early);
-  if (base >= lim) return;   // block-uniform
-  const int head = ws.sc[E_HEAD0], ep = ws.sc[E_EP];
-  const int i0 = blockIdx.x * kBlk + threadIdx.x * kPer;
-  bool fr[kPer];
-  int n;
-  free_flags(slot_pin, C, head, ep, i0, fr, &n);
-  int tot;
-  int rank = base + ech::block_excl_scan<kT>(n, scr, &tot);
-#pragma unroll
-  for (int i = 0; i < kPer; ++i) {
-    if (!fr[i]) continue;
-    if (rank < lim) {
-      int p = head + i0 + i;
-      if (p >= C) p -= C;
-      ws.freelist[rank] = p;
-    }
-    ++rank;
-  }
-}
-
 // ------------------------------------------------------------------ group
-// Miss flags of 16 consecutive tokens of sequence b: non-resident, score above
-// theta (strict), inside the row.
-__device__ __forceinline__ void miss_flags(const float* __restrict__ row, int t, int len, float th, int64_t g0,
-                                           int64_t P, const int32_t* __restrict__ tok2slot, bool (&m)[kPer],
-                                           int* n) {
-  int cnt = 0;
-  float v[kPer];
-  if (t + kPer <= len) {
-#pragma unroll
-    for (int i = 0; i < kPer / 4; ++i) {
-      const float4 x = reinterpret_cast<const float4*>(row + t)[i];
-      v[4 * i] = x.x;
-      v[4 * i + 1] = x.y;
-      v[4 * i + 2] = x.z;
-      v[4 * i + 3] = x.w;
-    }
-  } else {
-#pragma unroll
-    for (int i = 0; i < kPer; ++i) v[i] = (t + i < len) ? row[t + i] : 0.f;
-  }
-#pragma unroll
-  for (int i = 0; i < kPer; ++i) {
-    m[i] = t + i < len && v[i] > th && g0 + t + i < P && tok2slot[g0 + t + i] < 0;
-    cnt += m[i];
-  }
-  *n = cnt;
-}
-
-// grid (nch, b1 - b0)
-__global__ __launch_bounds__(kT) void early_want_kernel(int group, int b0, const float* __restrict__ logits,
-                                                        int64_t ld, const float* __restrict__ theta, int cap,
+// grid (nch, b1 - b0): 16 consecutive tokens per thread; a miss is a
+// non-resident token above theta (strict) inside the row. The block's
+// misses are listed in order and counted.
+__global__ __launch_bounds__(kT) void early_want_kernel(int b0, const float* __restrict__ logits, int64_t ld,
+                                                        const float* __restrict__ theta,
                                                         const int64_t* __restrict__ tok0,
                                                         const int32_t* __restrict__ lens,
-                                                        const int32_t* __restrict__ tok2slot, int64_t P,
-                                                        int32_t* ctr, int32_t* __restrict__ stats, EWs ws) {
+                                                        const int32_t* __restrict__ tok2slot, int64_t P, EWs ws) {
   __shared__ int scr[kT / 64];
   const int b = b0 + blockIdx.y, c = blockIdx.x;
+  const size_t blk = (size_t)b * ws.nch + c;
   const int len = lens[b];
   const float th = theta[b];
   const int t = c * kBlk + threadIdx.x * kPer;
+  const int64_t g0 = tok0[b] + t;
+  uint32_t mm = 0;
   int n = 0;
   if (th == th && t < len) {
-    bool m[kPer];
-    miss_flags(logits + (size_t)b * ld, t, len, th, tok0[b], P, tok2slot, m, &n);
+    const float* row = logits + (size_t)b * ld;
+    float v[kPer];
+    if (t + kPer <= len) {
+#pragma unroll
+      for (int i = 0; i < kPer / 4; ++i) {
+        const float4 x = reinterpret_cast<const float4*>(row + t)[i];
+        v[4 * i] = x.x;
+        v[4 * i + 1] = x.y;
+        v[4 * i + 2] = x.z;
+        v[4 * i + 3] = x.w;
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < kPer; ++i) v[i] = (t + i < len) ? row[t + i] : 0.f;
+    }
+    uint32_t above = 0;
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) above |= (t + i < len && v[i] > th && g0 + i < P) ? 1u << i : 0u;
+    if (above) {
+      int sl[kPer];   // all sixteen lookups in flight (clamped addresses; only flagged ones used)
+#pragma unroll
+      for (int i = 0; i < kPer; ++i) sl[i] = tok2slot[min(max(g0 + i, (int64_t)0), P - 1)];
+#pragma unroll
+      for (int i = 0; i < kPer; ++i) mm |= (((above >> i) & 1u) && sl[i] < 0) ? 1u << i : 0u;
+      n = __popc(mm);
+    }
   }
-  const int tot = ech::block_sum<kT>(n, scr);
-  if (threadIdx.x == 0) ws.want[(size_t)b * ws.nch + c] = tot;
-  if (!ech::last_block(ctr, gridDim.x * gridDim.y)) return;
-  // Rank ranges of the group's sequences, continuing earlier groups.
-  // (a) exclusive prefix of the want counts over the group's blocks in
-  //     (sequence, chunk) order, stored in off[]
-  const int nb = gridDim.y, nch = ws.nch;
-  const int E = nb * nch;
-  int* off = ws.off + (size_t)b0 * nch;
+  int tot;
+  int r = ech::block_excl_scan<kT>(n, scr, &tot);
+  for (; mm != 0u; mm &= mm - 1u, ++r) ws.lmiss[blk * kBlk + r] = (int)(g0 + __builtin_ctz(mm));
+  if (threadIdx.x == 0) ws.want[blk] = tot;
+}
+
+// One workgroup: rank ranges of the group's sequences, continuing earlier
+// groups; every block's first rank; statistics; the group's range.
+__global__ __launch_bounds__(kA) void early_rank_kernel(int group, int b0, int nb, int cap, int32_t* ctr,
+                                                        int32_t* __restrict__ stats, EWs ws) {
+  __shared__ int scr[kA / 64];
+  __shared__ int s_seg[kMaxB + 1], s_off[kMaxB];
+  const int tid = threadIdx.x;
+  const int nch = ws.nch;
+  const int n = nb * nch;
   const int* want = ws.want + (size_t)b0 * nch;
+  int* off = ws.off + (size_t)b0 * nch;
+  // flat exclusive scan of the group's block counts (sequence-major), four
+  // blocks per thread; each sequence's first block leaves its prefix in s_seg
+  int wv[4], ew[4];
   int run = 0;
-  for (int e0 = 0; e0 < E; e0 += kT) {
-    const int e = e0 + threadIdx.x;
-    const int v = e < E ? want[e] : 0;
-    int t_tot;
-    const int ex = ech::block_excl_scan<kT>(v, scr, &t_tot);
-    if (e < E) off[e] = run + ex;
-    run += t_tot;
+  for (int i0 = 0; i0 < n; i0 += 4 * kA) {
+    const int i = i0 + 4 * tid;
+    int sum = 0;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      wv[u] = want[min(i + u, n - 1)];
+      if (i + u >= n) wv[u] = 0;
+      sum += wv[u];
+    }
+    int tot;
+    int pw = run + ech::block_excl_scan<kA>(sum, scr, &tot);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      ew[u] = pw;
+      if (i + u < n && (i + u) % nch == 0) s_seg[(i + u) / nch] = pw;
+      pw += wv[u];
+    }
+    run += tot;
   }
-  const int want_all = run;
+  if (tid == 0) s_seg[nb] = run;
   __syncthreads();
-  // (b) per sequence: capped take, rank of its first miss, statistics; the
-  //     shift from the raw prefix to the rank goes to seqd[]
+  // per sequence: capped take, rank of its first miss, statistics
   const int start = ws.sc[E_RUN], nfree = ws.sc[E_NFREE];
   int rank_run = start;
-  for (int j0 = 0; j0 < nb; j0 += kT) {
-    const int j = j0 + threadIdx.x;
-    int want_b = 0, raw0 = 0;
+  for (int j0 = 0; j0 < nb; j0 += kA) {
+    const int j = j0 + tid;
+    int take = 0, want_b = 0;
     if (j < nb) {
-      raw0 = off[j * nch];
-      want_b = (j + 1 < nb ? off[(j + 1) * nch] : want_all) - raw0;
+      want_b = s_seg[j + 1] - s_seg[j];
+      take = min(cap, want_b);
     }
-    const int take = min(cap, want_b);
-    int t_tot;
-    const int seq_off = rank_run + ech::block_excl_scan<kT>(j < nb ? take : 0, scr, &t_tot);
+    int tot;
+    const int seq_off = rank_run + ech::block_excl_scan<kA>(take, scr, &tot);
     if (j < nb) {
       const int bb = b0 + j;
-      ws.seqd[bb] = seq_off - raw0;
+      s_off[j] = seq_off;
       ws.lim[bb] = seq_off + take;
       const int fetched = max(0, min(nfree - seq_off, take));
       stats[4 * bb + 1] = fetched;
       stats[4 * bb + 2] = want_b - fetched;
     }
-    rank_run += t_tot;
+    rank_run += tot;
   }
   __syncthreads();
-  // (c) ranks of the blocks' first misses
-  for (int e = threadIdx.x; e < E; e += kT) off[e] += ws.seqd[b0 + e / nch];
-  if (threadIdx.x == 0) {
+  // every block's first rank
+  if (n <= 4 * kA) {
+    const int i = 4 * tid;
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      if (i + u < n) off[i + u] = s_off[(i + u) / nch] + (ew[u] - s_seg[(i + u) / nch]);
+  } else {
+    run = 0;   // the same scan again
+    for (int i0 = 0; i0 < n; i0 += 4 * kA) {
+      const int i = i0 + 4 * tid;
+      int sum = 0;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        wv[u] = want[min(i + u, n - 1)];
+        if (i + u >= n) wv[u] = 0;
+        sum += wv[u];
+      }
+      int tot;
+      int pw = run + ech::block_excl_scan<kA>(sum, scr, &tot);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        if (i + u < n) off[i + u] = s_off[(i + u) / nch] + (pw - s_seg[(i + u) / nch]);
+        pw += wv[u];
+      }
+      run += tot;
+    }
+  }
+  if (tid == 0) {
     ws.sc[E_RUN] = rank_run;
     ws.grp[2 * group] = min(start, nfree);
     ws.grp[2 * group + 1] = min(rank_run, nfree);
@@ -365,64 +400,44 @@ __global__ __launch_bounds__(kT) void early_want_kernel(int group, int b0, const
   }
 }
 
-// grid (nch, b1 - b0)
-__global__ __launch_bounds__(kT) void early_apply_kernel(int group, int b0, const float* __restrict__ logits,
-                                                         int64_t ld, const float* __restrict__ theta,
-                                                         const int64_t* __restrict__ tok0,
-                                                         const int32_t* __restrict__ lens,
-                                                         int32_t* __restrict__ tok2slot, int64_t P,
-                                                         int32_t* __restrict__ slot2tok,
+// grid (nch, b1 - b0): block (c, j) places its listed misses by rank.
+__global__ __launch_bounds__(kT) void early_apply_kernel(int group, int b0, int32_t* __restrict__ tok2slot,
+                                                         int64_t P, int32_t* __restrict__ slot2tok,
                                                          int32_t* __restrict__ slot_pin, int32_t C,
                                                          int32_t* __restrict__ miss, int32_t M_early, int32_t* ctr,
                                                          int32_t* __restrict__ stats, EWs ws) {
-  __shared__ int scr[kT / 64];
   const int b = b0 + blockIdx.y, c = blockIdx.x;
-  const int len = lens[b];
-  const float th = theta[b];
-  const int t = c * kBlk + threadIdx.x * kPer;
-  const int base = ws.off[(size_t)b * ws.nch + c];
+  const size_t blk = (size_t)b * ws.nch + c;
+  const int cnt = min(ws.want[blk], kBlk);
+  const int base = ws.off[blk];
   const int lim = min(ws.lim[b], min(ws.grp[2 * group + 1], M_early));
-  if (!(th == th) || c * kBlk >= len || base >= lim) return;   // block-uniform
-  const int64_t g0 = tok0[b];
-  bool m[kPer];
-  int n = 0;
-  if (t < len) miss_flags(logits + (size_t)b * ld, t, len, th, g0, P, tok2slot, m, &n);
-  else
-#pragma unroll
-    for (int i = 0; i < kPer; ++i) m[i] = false;
-  int tot;
-  int rank = base + ech::block_excl_scan<kT>(n, scr, &tot);
+  if (cnt == 0 || base >= lim) return;   // block-uniform
   const int ep = ws.sc[E_EP];
   const int last = ws.grp[2 * group + 1] - 1;
-  int nev = 0;
-#pragma unroll
-  for (int i = 0; i < kPer; ++i) {
-    if (m[i] && rank < lim) {
-      const int g = (int)(g0 + t + i);
-      const int p = ws.freelist[rank];
-      if (p < 0 || p >= C) {
-        atomicOr(&ctr[ECH_CTR_STATUS], ECH_ST_OVERFLOW);   // unreachable unless counts and ranks disagree
+  for (int i = threadIdx.x; i < cnt; i += kT) {   // trips differ only in the last pass
+    const int m = base + i;
+    bool evicted = false;
+    if (m < lim) {
+      const int g = ws.lmiss[blk * kBlk + i];
+      const int p = ws.freelist[m];
+      if (g < 0 || g >= P || p < 0 || p >= C) {
+        atomicOr(&ctr[ECH_CTR_STATUS], ECH_ST_OVERFLOW);   // unreachable unless counts and lists disagree
       } else {
         const int u = slot2tok[p];
         if (u >= 0 && u < P) {
           tok2slot[u] = -1;   // evict; the host row stays where it is
-          ++nev;
+          evicted = true;
         }
         slot2tok[p] = g;
         tok2slot[g] = p;
         slot_pin[p] = ep;
-        miss[2 * rank] = g;
-        miss[2 * rank + 1] = p;
-        if (rank == last) ctr[ECH_CTR_HEAD] = (p + 1 == C) ? 0 : p + 1;
+        miss[2 * m] = g;
+        miss[2 * m + 1] = p;
+        if (m == last) ctr[ECH_CTR_HEAD] = (p + 1 == C) ? 0 : p + 1;
       }
     }
-    rank += m[i] ? 1 : 0;
-  }
-  // One eviction count per wave (the block serves one sequence b).
-  const int wev = ech::wave_sum(nev);
-  if (wev > 0 && ech::lane_id() == 0) {
-    atomicAdd(&ctr[ECH_CTR_NEVICT], wev);
-    atomicAdd(&stats[4 * b + 3], wev);
+    ech::wave_count(&ctr[ECH_CTR_NEVICT], evicted);
+    ech::wave_count(&stats[4 * b + 3], evicted);
   }
 }
 
@@ -506,9 +521,7 @@ extern "C" int ech_early_begin(const void* q, const float* w, const void* kcache
     hipLaunchKernelGGL(early_pin_kernel<ECH_KEY_BF16>, gp, dim3(kT), 0, s, qq, w, kk, kscale, seq_tok0, seq_len,
                        theta, tok2slot, P, C, slot_pin, ctr, e);
   ECH_LAUNCH_CHECK();
-  hipLaunchKernelGGL(early_free_kernel, dim3(e.ns), dim3(kT), 0, s, slot_pin, C, B, ctr, stats, e);
-  ECH_LAUNCH_CHECK();
-  hipLaunchKernelGGL(early_freelist_kernel, dim3(e.ns), dim3(kT), 0, s, slot_pin, C, M_early, e);
+  hipLaunchKernelGGL(early_alloc_kernel, dim3(1), dim3(kA), 0, s, slot_pin, C, B, M_early, ctr, stats, e);
   ECH_LAUNCH_CHECK();
   return ECH_OK;
 }
@@ -531,11 +544,13 @@ extern "C" int ech_early_group(int group, int b0, int b1, const float* logits, i
   early_layout(B, max_len, C, M_early, &e, static_cast<char*>(ws));
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   const dim3 gg(e.nch, b1 - b0);
-  hipLaunchKernelGGL(early_want_kernel, gg, dim3(kT), 0, s, group, b0, logits, ld, theta, cap, seq_tok0, seq_len,
-                     tok2slot, P, ctr, stats, e);
+  hipLaunchKernelGGL(early_want_kernel, gg, dim3(kT), 0, s, b0, logits, ld, theta, seq_tok0, seq_len, tok2slot, P,
+                     e);
   ECH_LAUNCH_CHECK();
-  hipLaunchKernelGGL(early_apply_kernel, gg, dim3(kT), 0, s, group, b0, logits, ld, theta, seq_tok0, seq_len,
-                     tok2slot, P, slot2tok, slot_pin, C, miss_early, M_early, ctr, stats, e);
+  hipLaunchKernelGGL(early_rank_kernel, dim3(1), dim3(kA), 0, s, group, b0, b1 - b0, cap, ctr, stats, e);
+  ECH_LAUNCH_CHECK();
+  hipLaunchKernelGGL(early_apply_kernel, gg, dim3(kT), 0, s, group, b0, tok2slot, P, slot2tok, slot_pin, C,
+                     miss_early, M_early, ctr, stats, e);
   ECH_LAUNCH_CHECK();
   return ECH_OK;
 }

@@ -10,15 +10,15 @@ fetch of tokens scoring above the predicted threshold starts before it:
 Optionally (early_groups >= 1) the batch's sequences are scored in G groups
 and each group's early rows start crossing PCIe as soon as its scores exist:
 
-    S1: early_begin (pins)     group 0 maps        group 1 maps  ...
-    S0: logits group 0 ---------> logits group 1 --------> ... --> ech_topk --+-> FINAL maps --+-> FINAL recall
-    S2:                              recall group 0 --> recall group 1 ... ---/----------------/
+    S0: logits g0 -> maps g0 -> logits g1 -> maps g1 ... -> ech_topk -> FINAL maps --+
+    S1: early_begin (pins) --> recall g0 ------> recall g1 ... -----------------------+-> FINAL recall
 
 The grouping changes only the order of the work, not its result (see
-ech_early_begin in include/ech.h). On MI355X it is slower: kernels running
-beside the saturating key stream and beside the PCIe gather slow down
-several-fold, so one EARLY phase after all scores is the default. theta is
-double-buffered (the early fetch
+ech_early_begin in include/ech.h). On MI355X it does not pay: beside the
+zero-copy PCIe gather the group maps slow 2-3x and the gather itself drops
+to 34-41 GB/s (55 alone), and a captured graph started the group recalls only
+when the top-k began; two groups are level with one EARLY phase after all
+scores, which stays the default. theta is double-buffered (the early fetch
 reads the prediction while the top-k writes its update). When the batch's
 selections do not fit the cache at once (sum of min(k, len_b) > C),
 sequences are processed in host-computed chunks, each an ECH_EARLY phase
@@ -102,7 +102,8 @@ class DecodeLayer:
         self.chunks = sequence_chunks(self.lens_np, k, C)
         cb = max(e - s for s, e in self.chunks)
         m_max = max(cb * min(k, self.max_len), cb * min(cap, self.max_len), 1)
-        self.state = LayerState.allocate(self.P, C, m_max, device)
+        m_early = max(cb * min(cap, self.max_len), 1)   # the EARLY demand bound: no free slot beyond it is ranked
+        self.state = LayerState.allocate(self.P, C, m_max, device, M_early=m_early)
         self.ws_topk = torch.empty(ech_topk_ws_bytes(self.B, self.max_len, k), dtype=torch.uint8, **dev)
         self.ws_early = torch.empty(ech_cache_step_ws_bytes(ECH_EARLY, cb, cb, k, self.max_len, C, m_max),
                                     dtype=torch.uint8, **dev)
@@ -112,12 +113,12 @@ class DecodeLayer:
         self.groups = (sequence_groups(self.B, early_groups)
                        if early and early_groups >= 1 and len(self.chunks) == 1 else [])
         if self.groups:
-            self.ws_group = torch.empty(ech_early_ws_bytes(self.B, self.max_len, C, m_max), dtype=torch.uint8,
+            self.ws_group = torch.empty(ech_early_ws_bytes(self.B, self.max_len, C, m_early), dtype=torch.uint8,
                                         **dev)
-            self.s2 = torch.cuda.Stream(device=device)
             self.ev_start = torch.cuda.Event()
-            self.ev_lg = [torch.cuda.Event() for _ in self.groups]
+            self.ev_begin = torch.cuda.Event()
             self.ev_mg = [torch.cuda.Event() for _ in self.groups]
+            self.ev_fm = torch.cuda.Event()
             self.ev_rg = torch.cuda.Event()
         self.host_pool = host_pool
         if host_pool is not None:
@@ -226,40 +227,56 @@ class DecodeLayer:
         self.parity ^= 1
 
     def _step_grouped(self, q, th, th_next, s0, mark) -> None:
-        """Decode step with the early fetch in sequence groups (one chunk)."""
-        s1, s2 = self.s1, self.s2
+        """Decode step with the early fetch in sequence groups (one chunk), on
+        two streams: S0 scores each group and allocates its early misses (a
+        few short kernels), then runs the top-k and the FINAL maps; S1 pins
+        (begin), recalls each group's rows as soon as they are allocated,
+        then the FINAL rows."""
+        s1 = self.s1
         self.ev_start.record(s0)
         s1.wait_event(self.ev_start)
-        s2.wait_event(self.ev_start)
         mark('early', s1)
         ech_early_begin(q, self.w, self.kcache, self.kscale, self.tok0, self.lens, self.max_len, th, self.state,
                         self.stats_early, self.ws_group, stream=s1)
+        self.ev_begin.record(s1)
         mark('logits', s0)
-        mark('recall_early', s2)
+        mark('recall_early', s1)
+
+        def recall(g):
+            if self.host_pool is not None:
+                s1.wait_event(self.ev_mg[g])
+                ech_recall_group(g, self.host_pool, self.dev_cache, self.state, self.ws_group, stream=s1)
+
+        # Group g's recall is enqueued after the next S0 launch (the next
+        # group's scores, or the top-k after the last group): a captured graph
+        # then keeps the S0 chain on one hardware queue and gives the recalls
+        # their own (its executor continues a node's queue with the child
+        # captured first).
         for g, (b0, b1) in enumerate(self.groups):
             ech_index_logits(q[b0:b1], self.w[b0:b1], self.kcache, self.kscale, self.tok0[b0:b1],
                              self.lens[b0:b1], self.max_len, self.logits[b0:b1], stream=s0)
-            self.ev_lg[g].record(s0)
-            s1.wait_event(self.ev_lg[g])
+            if g > 0:
+                recall(g - 1)
+            if g == 0:
+                s0.wait_event(self.ev_begin)
             ech_early_group(g, b0, b1, self.logits, th, self.cap, self.tok0, self.lens, self.max_len, self.state,
-                            self.stats_early, self.ws_group, stream=s1)
-            self.ev_mg[g].record(s1)
-            if self.host_pool is not None:
-                s2.wait_event(self.ev_mg[g])
-                ech_recall_group(g, self.host_pool, self.dev_cache, self.state, self.ws_group, stream=s2)
+                            self.stats_early, self.ws_group, stream=s0)
+            self.ev_mg[g].record(s0)
         mark('logits', s0)
-        mark('early', s1)
-        mark('recall_early', s2)
-        self.ev_rg.record(s2)
         mark('topk', s0)
         ech_topk(self.logits, self.lens, self.max_len, self.k, th, th_next, self.idx, self.kth, self.ws_topk,
                  stream=s0)
+        recall(len(self.groups) - 1)
+        mark('recall_early', s1)
+        mark('early', s1)
         mark('topk', s0)
         mark('final', s0)
-        s0.wait_event(self.ev_mg[-1])      # FINAL updates the maps the groups left ...
-        self._maps(ECH_FINAL, 0, self.B, th, s0)
-        s0.wait_event(self.ev_rg)          # ... but may reuse a slot an early recall is still filling
-        self._recall(ECH_FINAL, s0)
+        self._maps(ECH_FINAL, 0, self.B, th, s0)      # after every group (same stream)
+        self.ev_fm.record(s0)
+        s1.wait_event(self.ev_fm)                     # after the early recalls: it may reuse their slots
+        self._recall(ECH_FINAL, s1)
+        self.ev_rg.record(s1)
+        s0.wait_event(self.ev_rg)
         mark('final', s0)
 
     @property
