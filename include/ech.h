@@ -171,7 +171,9 @@ int ech_cache_reset(int32_t* tok2slot, int64_t P, int32_t* slot2tok, int32_t* sl
  *   tok2slot [P]        slot of global token g, or -1
  *   slot2tok [C]        token held by slot s, or -1
  *   slot_pin [C]        epoch stamp; slot s is pinned in a phase iff it equals
- *                       that phase's epoch (no clearing pass)
+ *                       that phase's epoch (no clearing pass). Pins are the
+ *                       phase's resident selection; slots it allocates are
+ *                       not stamped.
  *   miss     [M_max,2]  (g, slot) pairs allocated by the phase, in
  *                       allocation order; consumed by ech_recall. EARLY
  *                       phases should get their own buffer (count in

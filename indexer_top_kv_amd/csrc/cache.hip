@@ -12,15 +12,14 @@
 //            score > theta; FINAL: idx entries; PREFILL: idx entries of all
 //            rows, misses claimed once per token by marking tok2slot -1 -> -2
 //            (union), then listed by a token scan.
-//   allocate one workgroup: scans of the block counts give every miss its
-//            rank (ascending sequence,
-//            token; EARLY keeps the first `cap` per sequence); unpinned slots
-//            are ranked in ring order from the head, window by window, only
-//            as far as the misses need; n_alloc = min(wanted, free). Writes
-//            stats, counters, head and epoch.
-//   apply    miss m takes the free slot of rank m: the slot's old token is
-//            unmapped (no write-back), the maps point at each other,
-//            miss[m] = (g, slot).
+//   place    every block with misses takes its ranks from the counts
+//            (ascending sequence, token; EARLY keeps the first `cap` per
+//            sequence) and ranks the unpinned slots in ring order from the
+//            head, window by window, only as far as its own ranks; miss m
+//            takes the free slot of rank m: the slot's old token is unmapped
+//            (no write-back), the maps point at each other, miss[m] =
+//            (g, slot). One more block writes the statistics, counters, head
+//            and epoch; n_alloc = min(wanted, free).
 // Ranks come from scans, not from atomics, so the maps are a deterministic
 // function of the inputs: bit-identical run to run.
 
@@ -36,16 +35,13 @@ constexpr int kBlk = kT * kPer;   // tokens or slots per block in ordered kernel
 constexpr int kMaxK = 4096;
 constexpr int kMaxB = 1024;
 
-enum { S_EP = 0, S_NWANT = 1, S_NALLOC = 2, S_N = 16 };
+enum { S_EP = 0, S_HEAD = 1, S_N = 16 };
 
 struct CWs {
   int* want;     // [ne] misses per entry block (all of them)
   int* hit;      // [ne] hits (pinned slots) per entry block
-  int* off;      // [ne] rank of the block's first miss
-  int* lim;      // [ne] rank limit of the block's sequence (EARLY cap)
-  int* freelist; // [M_max] free slot of each rank, in ring order from the head
   int2* lmiss;   // [ne][lcap] the block's misses in order: (g, aux), aux = entry index (FINAL)
-  int* sc;       // [S_N] scalars
+  int* sc;       // [S_N] the phase's epoch and head, published by its counting kernel
   int ne, nbr, lcap;  // entry blocks, entry blocks per sequence, list capacity per block
   int P, C, M_max;    // bounds every index is checked against
 };
@@ -70,7 +66,7 @@ void block_counts(int phase, int B, int k, int max_len, int* ne, int* nbr, int* 
   }
 }
 
-size_t layout(int phase, int B, int k, int max_len, int32_t M_max, CWs* w, char* base) {
+size_t layout(int phase, int B, int k, int max_len, CWs* w, char* base) {
   int ne, nbr, lcap;
   block_counts(phase, B, k, max_len, &ne, &nbr, &lcap);
   size_t o = 0;
@@ -79,15 +75,11 @@ size_t layout(int phase, int B, int k, int max_len, int32_t M_max, CWs* w, char*
     o = align256(o + bytes);
     return at;
   };
-  size_t o_want = take(4 * (size_t)ne), o_hit = take(4 * (size_t)ne), o_off = take(4 * (size_t)ne),
-         o_lim = take(4 * (size_t)ne), o_fl = take(4 * (size_t)M_max), o_lm = take(8 * (size_t)ne * lcap),
+  size_t o_want = take(4 * (size_t)ne), o_hit = take(4 * (size_t)ne), o_lm = take(8 * (size_t)ne * lcap),
          o_sc = take(4 * S_N);
   if (w && base) {
     w->want = reinterpret_cast<int*>(base + o_want);
     w->hit = reinterpret_cast<int*>(base + o_hit);
-    w->off = reinterpret_cast<int*>(base + o_off);
-    w->lim = reinterpret_cast<int*>(base + o_lim);
-    w->freelist = reinterpret_cast<int*>(base + o_fl);
     w->lmiss = reinterpret_cast<int2*>(base + o_lm);
     w->sc = reinterpret_cast<int*>(base + o_sc);
     w->ne = ne;
@@ -99,157 +91,61 @@ size_t layout(int phase, int B, int k, int max_len, int32_t M_max, CWs* w, char*
 
 __device__ __forceinline__ void set_status(int32_t* ctr, int bit) { atomicOr(&ctr[ECH_CTR_STATUS], bit); }
 
-// ------------------------------------------------------------------ allocate
-// One workgroup of kA threads, after the counting kernel.
-//   1. ranks: exclusive scans of the per-block counts (sequence-major) give
-//      every block its first miss's rank; EARLY keeps the first `cap` misses
-//      of each sequence; n_want = the misses taken.
-//   2. free slots: ring positions from the head, a window of kWin at a time,
-//      until n_want unpinned slots are found or the ring is exhausted; the
-//      slot of rank m goes to freelist[m]. n_alloc = min(n_want, found).
-//   3. statistics, counters, the new head and epoch.
-constexpr int kA = 1024;        // threads of the allocating workgroup
-constexpr int kWin = kA * 16;   // ring positions per window
-
-__global__ __launch_bounds__(kA) void allocate_kernel(int phase, int nseq, int cap, int32_t* ctr,
-                                                     const int32_t* __restrict__ slot_pin,
-                                                     int32_t* __restrict__ stats, CWs w) {
-  __shared__ int scr[kA / 64];
-  __shared__ int s_rowoff[kMaxB], s_take[kMaxB], s_seg[kMaxB + 1], s_hseg[kMaxB + 1];
-  __shared__ __align__(16) uint8_t s_fr[kWin];
-  __shared__ int s_last, s_lastw;
-  const int tid = threadIdx.x;
-  const int C = w.C;
-  const int ep = ctr[ECH_CTR_EPOCH] + 1;
+// Start of a phase, by one thread of its counting kernel: publish the epoch
+// and the head (the placing kernel's blocks read them while its bookkeeping
+// block rewrites ctr) and clear the eviction count.
+__device__ __forceinline__ void publish_phase(int32_t* ctr, int ep, CWs w) {
   int head = ctr[ECH_CTR_HEAD];
-  if (head < 0 || head >= C) head = 0;   // only a corrupted state; keeps every slot index in range
-  // ---- 1. ranks. Flat exclusive scans of want and hit over the n entry
-  // blocks (sequence-major), four consecutive blocks per thread; each
-  // sequence's first block leaves its prefixes in s_seg / s_hseg.
-  const int n = nseq * w.nbr;
-  int wv[4], ew[4];   // one pass (n <= 4 kA): the prefixes stay here for step 1b
-  int want_all = 0, hit_all = 0;
-  for (int i0 = 0; i0 < n; i0 += 4 * kA) {
-    const int i = i0 + 4 * tid;
-    int hv[4], ws = 0, hs = 0;
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int iu = min(i + u, n - 1);   // clamped: every load issued at once
-      wv[u] = w.want[iu];
-      hv[u] = w.hit[iu];
-      if (i + u >= n) wv[u] = hv[u] = 0;
-      ws += wv[u];
-      hs += hv[u];
-    }
-    int tw, th;
-    int pw = want_all + ech::block_excl_scan<kA>(ws, scr, &tw);
-    int ph = hit_all + ech::block_excl_scan<kA>(hs, scr, &th);
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      ew[u] = pw;
-      if (i + u < n && (i + u) % w.nbr == 0) {
-        s_seg[(i + u) / w.nbr] = pw;
-        s_hseg[(i + u) / w.nbr] = ph;
-      }
-      pw += wv[u];
-      ph += hv[u];
-    }
-    want_all += tw;
-    hit_all += th;
-  }
-  if (tid == 0) {
-    s_seg[nseq] = want_all;
-    s_hseg[nseq] = hit_all;
-  }
-  __syncthreads();
-  // per sequence: the misses it takes (EARLY: at most cap) and the rank of its first
-  int n_want = 0;
-  for (int b0 = 0; b0 < nseq; b0 += kA) {
-    const int b = b0 + tid;
-    int take_b = 0;
-    if (b < nseq) {
-      const int want_b = s_seg[b + 1] - s_seg[b];
-      take_b = (phase == ECH_EARLY) ? min(cap, want_b) : want_b;
-      s_take[b] = take_b;
-    }
-    int tot;
-    const int ex = ech::block_excl_scan<kA>(take_b, scr, &tot);
-    if (b < nseq) s_rowoff[b] = n_want + ex;
-    n_want += tot;
-  }
-  const bool clamped = n_want > w.M_max;   // only when a caller contract is broken
-  if (clamped) n_want = w.M_max;
-  __syncthreads();
-  // ---- 1b. every block: the rank of its first miss and its sequence's limit
-  if (n <= 4 * kA) {
-    const int i = 4 * tid;
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      if (i + u < n) {
-        const int bi = (i + u) / w.nbr;
-        w.off[i + u] = s_rowoff[bi] + (ew[u] - s_seg[bi]);
-        w.lim[i + u] = s_rowoff[bi] + s_take[bi];
-      }
-    }
-  } else {
-    int run = 0;   // the same scan again
-    for (int i0 = 0; i0 < n; i0 += 4 * kA) {
-      const int i = i0 + 4 * tid;
-      int ws = 0;
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        wv[u] = w.want[min(i + u, n - 1)];
-        if (i + u >= n) wv[u] = 0;
-        ws += wv[u];
-      }
-      int tw;
-      int pw = run + ech::block_excl_scan<kA>(ws, scr, &tw);
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        if (i + u < n) {
-          const int bi = (i + u) / w.nbr;
-          w.off[i + u] = s_rowoff[bi] + (pw - s_seg[bi]);
-          w.lim[i + u] = s_rowoff[bi] + s_take[bi];
-        }
-        pw += wv[u];
-      }
-      run += tw;
-    }
-  }
-  // ---- 2. free slots in ring order from the head
+  if (head < 0 || head >= w.C) head = 0;   // only a corrupted state; keeps every slot index in range
+  w.sc[S_EP] = ep;
+  w.sc[S_HEAD] = head;
+  ctr[ECH_CTR_NEVICT] = 0;
+}
+
+// ------------------------------------------------------------------ ring scan
+// Free (unpinned) slots in ring order from the head, a window of kWin
+// positions at a time, until `need` are counted or the ring ends. For every
+// free slot whose rank r lies in [lo, hi), fn(r, slot) runs in the thread
+// that ranks it. Returns the number counted; *s_last (LDS) gets the slot of
+// the last one counted. Block-wide (kT threads, contains barriers); s_fr is
+// kWin bytes of LDS, scr kT/64 ints.
+constexpr int kWin = kT * 32;
+
+template <class Fn>
+__device__ int ring_scan(const int32_t* __restrict__ slot_pin, int C, int head, int ep, int need, int lo, int hi,
+                         uint8_t* s_fr, int* scr, int* s_last, Fn fn) {
+  const int tid = threadIdx.x;
   int found = 0;
-  for (int i0 = 0; i0 < C && found < n_want; i0 += kWin) {   // block-uniform
+  for (int i0 = 0; i0 < C && found < need; i0 += kWin) {   // block-uniform
 #pragma unroll
-    for (int j = 0; j < kWin / kA; ++j) {   // coalesced loads, all in flight
-      const int pos = i0 + j * kA + tid;
-      int p = head + min(pos, C - 1);   // clamped: every load issued at once
+    for (int j = 0; j < kWin / kT; ++j) {   // coalesced loads, all in flight
+      const int pos = i0 + j * kT + tid;
+      int p = head + min(pos, C - 1);
       if (p >= C) p -= C;
       const int pv = slot_pin[p];
-      s_fr[j * kA + tid] = (pos < C && pv != ep) ? 1 : 0;
+      s_fr[j * kT + tid] = (pos < C && pv != ep) ? 1 : 0;
     }
     __syncthreads();
-    // thread t ranks positions i0 + 16t .. +15 (one 16-byte LDS read)
-    const uint4 f0 = reinterpret_cast<const uint4*>(s_fr)[tid];
-    const uint32_t fw[4] = {f0.x, f0.y, f0.z, f0.w};
+    // thread t ranks positions i0 + 32t .. +31 (two 16-byte LDS reads)
+    const uint4 f0 = reinterpret_cast<const uint4*>(s_fr)[2 * tid];
+    const uint4 f1 = reinterpret_cast<const uint4*>(s_fr)[2 * tid + 1];
+    const uint32_t fw[8] = {f0.x, f0.y, f0.z, f0.w, f1.x, f1.y, f1.z, f1.w};
     int cnt = 0;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) cnt += __popc(fw[q]);   // flags are 0/1 bytes
+    for (int q = 0; q < 8; ++q) cnt += __popc(fw[q]);   // flags are 0/1 bytes
     int tot;
-    int rank = found + ech::block_excl_scan<kA>(cnt, scr, &tot);
-    const int wlast = found + tot - 1;   // rank of the window's last free slot
-    if (rank < n_want) {
+    int rank = found + ech::block_excl_scan<kT>(cnt, scr, &tot);
+    const int wlast = found + tot - 1;
+    if (cnt > 0 && (rank < hi || rank + cnt > wlast)) {
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
+      for (int q = 0; q < 8; ++q) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           if ((fw[q] >> (8 * e)) & 1u) {
-            if (rank < n_want) {
-              int p = head + i0 + 16 * tid + 4 * q + e;
-              if (p >= C) p -= C;
-              w.freelist[rank] = p;
-              if (rank == n_want - 1) s_last = p;
-              if (rank == wlast) s_lastw = p;
-            }
+            int p = head + i0 + 32 * tid + 4 * q + e;
+            if (p >= C) p -= C;
+            if (rank >= lo && rank < hi) fn(rank, p);
+            if (rank == wlast) *s_last = p;
             ++rank;
           }
         }
@@ -258,31 +154,7 @@ __global__ __launch_bounds__(kA) void allocate_kernel(int phase, int nseq, int c
     found += tot;
     __syncthreads();   // s_fr is rewritten by the next window
   }
-  const int n_alloc = min(n_want, found);
-  // ---- 3. statistics and counters
-  for (int b = tid; b < nseq; b += kA) {
-    const int fetched = max(0, min(n_alloc - s_rowoff[b], s_take[b]));
-    int32_t* st = stats + 4 * b;
-    st[0] = s_hseg[b + 1] - s_hseg[b];
-    st[1] = fetched;
-    st[2] = (s_seg[b + 1] - s_seg[b]) - fetched;   // wanted (before the cap) and not fetched
-    st[3] = 0;
-  }
-  if (tid == 0) {
-    w.sc[S_EP] = ep;
-    w.sc[S_NWANT] = n_want;
-    w.sc[S_NALLOC] = n_alloc;
-    ctr[phase == ECH_EARLY ? ECH_CTR_NMISS_EARLY : ECH_CTR_NMISS] = n_alloc;
-    ctr[ECH_CTR_NWANT] = n_want;
-    ctr[ECH_CTR_NPINNED] = hit_all;
-    ctr[ECH_CTR_NEVICT] = 0;
-    ctr[ECH_CTR_EPOCH] = ep;
-    if (n_alloc > 0) {
-      const int last = (n_alloc == n_want) ? s_last : s_lastw;
-      ctr[ECH_CTR_HEAD] = (last + 1 == C) ? 0 : last + 1;
-    }
-    if ((phase != ECH_EARLY && n_want > found) || clamped) ctr[ECH_CTR_STATUS] |= ECH_ST_OVERFLOW;
-  }
+  return found;
 }
 
 // ------------------------------------------------------------------ pin / count
@@ -296,7 +168,7 @@ __global__ __launch_bounds__(kT) void pin_final_kernel(const int32_t* __restrict
                                                        const int32_t* __restrict__ lens,
                                                        const int32_t* __restrict__ tok2slot,
                                                        int32_t* __restrict__ slot_pin, int32_t* __restrict__ sel_slot,
-                                                       int32_t* ctr, CWs w) {
+                                                       int32_t* ctr, int32_t* __restrict__ stats, CWs w) {
   __shared__ int scr[kT / 64];
   const int b = blockIdx.y, j = blockIdx.x * kT + threadIdx.x;
   const int blk = b * gridDim.x + blockIdx.x;
@@ -336,6 +208,10 @@ __global__ __launch_bounds__(kT) void pin_final_kernel(const int32_t* __restrict
   if (threadIdx.x == 0) {
     w.hit[blk] = nh;
     w.want[blk] = nm;
+    if (blockIdx.x == 0) {
+      stats[4 * b + 3] = 0;   // evictions, counted by the placing kernel
+      if (b == 0) publish_phase(ctr, ep, w);
+    }
   }
 }
 
@@ -361,7 +237,8 @@ __global__ __launch_bounds__(kT) void pin_early_kernel(const float* __restrict__
                                                        const int64_t* __restrict__ tok0,
                                                        const int32_t* __restrict__ lens,
                                                        const int32_t* __restrict__ tok2slot,
-                                                       int32_t* __restrict__ slot_pin, int32_t* ctr, CWs w) {
+                                                       int32_t* __restrict__ slot_pin, int32_t* ctr,
+                                                       int32_t* __restrict__ stats, CWs w) {
   __shared__ int scr[kT / 64];
   const int b = blockIdx.y;
   const int blk = b * gridDim.x + blockIdx.x;
@@ -407,6 +284,10 @@ __global__ __launch_bounds__(kT) void pin_early_kernel(const float* __restrict__
   if (threadIdx.x == 0) {
     w.hit[blk] = nh;
     w.want[blk] = nw;
+    if (blockIdx.x == 0) {
+      stats[4 * b + 3] = 0;   // evictions, counted by the placing kernel
+      if (b == 0) publish_phase(ctr, ep, w);
+    }
   }
 }
 
@@ -443,8 +324,8 @@ __global__ __launch_bounds__(kT) void pin_prefill_kernel(const int32_t* __restri
 __global__ __launch_bounds__(kT) void count_claimed_kernel(const int64_t* __restrict__ tok0p,
                                                            const int32_t* __restrict__ lenp,
                                                            const int32_t* __restrict__ tok2slot,
-                                                           const int32_t* __restrict__ slot_pin, const int32_t* ctr,
-                                                           CWs w) {
+                                                           const int32_t* __restrict__ slot_pin, int32_t* ctr,
+                                                           int32_t* __restrict__ stats, CWs w) {
   __shared__ int scr[kT / 64];
   const int64_t tok0 = tok0p[0];
   const int len = lenp[0];
@@ -480,57 +361,163 @@ __global__ __launch_bounds__(kT) void count_claimed_kernel(const int64_t* __rest
   if (threadIdx.x == 0) {
     w.want[blockIdx.x] = nw;
     w.hit[blockIdx.x] = np;
+    if (blockIdx.x == 0) {
+      stats[3] = 0;   // evictions, counted by the placing kernel
+      publish_phase(ctr, ep, w);
+    }
   }
 }
 
-// ------------------------------------------------------------------ apply
-// grid (ne, S): block (i, y) takes the slices y, y + S, ... (kT misses each)
-// of block i's miss list; S > 1 for the long lists of PREFILL token blocks.
-// Miss m (rank off[i] + j) takes freelist[m]: the slot's old token is
-// unmapped (no write-back), the maps point at each other, miss[m] = (g, slot).
-// The owner sequence of a block is fixed, so eviction counts are merged per
-// wave.
-__global__ __launch_bounds__(kT) void apply_kernel(int phase, int32_t* __restrict__ tok2slot,
-                                                   int32_t* __restrict__ slot2tok, int32_t* __restrict__ slot_pin,
-                                                   int32_t* __restrict__ miss, int32_t* ctr,
-                                                   int32_t* __restrict__ sel_slot, int32_t* __restrict__ stats,
-                                                   CWs w) {
-  const int blk = blockIdx.x;
-  const int cnt = min(w.want[blk], w.lcap);
-  if ((int)blockIdx.y * kT >= cnt) return;   // block-uniform
-  const int n_alloc = w.sc[S_NALLOC];
-  const int ep = w.sc[S_EP];
-  const int base = w.off[blk];
-  const int lim = min(w.lim[blk], w.sc[S_NWANT]);
-  const int owner = (phase == ECH_PREFILL) ? 0 : blk / w.nbr;
-  for (int i = blockIdx.y * kT + threadIdx.x; i < cnt; i += kT * gridDim.y) {   // trips differ only in the last pass
-    const int m = base + i;
+// ------------------------------------------------------------------ place
+// grid (ne + 1, S). Block (i, y), i < ne, places the misses of entry block i
+// in the slice y of its list (S > 1 splits the long lists of PREFILL token
+// blocks). Ranks come from the counts: the capped totals of the sequences
+// before i's (EARLY keeps the first `cap` misses of each sequence) plus the
+// misses of i's sequence before block i. The block then ranks the free slots
+// itself, in ring order from the head, only as far as its own ranks: miss of
+// rank m takes the m-th free slot; its old token is unmapped (no
+// write-back), the maps point at each other, miss[m] = (g, slot). Block
+// (ne, 0) does the bookkeeping: per-sequence statistics, counts, the new head
+// and epoch. Nothing in this kernel writes slot_pin, so every block ranks the
+// same free slots.
+
+__device__ __forceinline__ int sum_counts(const int* p, int n) {
+  int s = 0, c = 0;
+  for (; c + 8 <= n; c += 8) {
+    int v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = p[c + u];   // eight loads in flight
+#pragma unroll
+    for (int u = 0; u < 8; ++u) s += v[u];
+  }
+  for (; c < n; ++c) s += p[c];
+  return s;
+}
+
+__device__ void bookkeep(int phase, int nseq, int cap, const int32_t* __restrict__ slot_pin, int32_t* ctr,
+                         int32_t* __restrict__ stats, CWs w, uint8_t* smem, int* scr) {
+  int* s_take = reinterpret_cast<int*>(smem);
+  int* s_want = s_take + kMaxB;
+  int* s_hit = s_want + kMaxB;
+  int* s_row = s_hit + kMaxB;
+  uint8_t* s_fr = reinterpret_cast<uint8_t*>(s_row + kMaxB);
+  __shared__ int s_last, s_lastw;
+  const int tid = threadIdx.x;
+  const int ep = w.sc[S_EP], head = w.sc[S_HEAD];
+  int n_want = 0, hit_all = 0;
+  for (int b0 = 0; b0 < nseq; b0 += kT) {
+    const int b = b0 + tid;
+    int take = 0, h = 0;
+    if (b < nseq) {
+      const int wb = sum_counts(w.want + (size_t)b * w.nbr, w.nbr);
+      h = sum_counts(w.hit + (size_t)b * w.nbr, w.nbr);
+      take = (phase == ECH_EARLY) ? min(cap, wb) : wb;
+      s_want[b] = wb;
+      s_hit[b] = h;
+      s_take[b] = take;
+    }
+    int tot;
+    const int ex = ech::block_excl_scan<kT>(take, scr, &tot);
+    if (b < nseq) s_row[b] = n_want + ex;
+    n_want += tot;
+    hit_all += ech::block_sum<kT>(h, scr);
+  }
+  const bool clamped = n_want > w.M_max;   // only when a caller contract is broken
+  if (clamped) n_want = w.M_max;
+  const int found = ring_scan(slot_pin, w.C, head, ep, n_want, n_want - 1, n_want, s_fr, scr, &s_lastw,
+                              [&](int, int p) { s_last = p; });
+  const int n_alloc = min(n_want, found);
+  for (int b = tid; b < nseq; b += kT) {
+    const int fetched = max(0, min(n_alloc - s_row[b], s_take[b]));
+    int32_t* st = stats + 4 * b;
+    st[0] = s_hit[b];
+    st[1] = fetched;
+    st[2] = s_want[b] - fetched;   // wanted (before the cap) and not fetched
+  }
+  if (tid == 0) {
+    ctr[phase == ECH_EARLY ? ECH_CTR_NMISS_EARLY : ECH_CTR_NMISS] = n_alloc;
+    ctr[ECH_CTR_NWANT] = n_want;
+    ctr[ECH_CTR_NPINNED] = hit_all;
+    ctr[ECH_CTR_EPOCH] = ep;
+    if (n_alloc > 0) {
+      const int last = (n_alloc == n_want) ? s_last : s_lastw;
+      ctr[ECH_CTR_HEAD] = (last + 1 == w.C) ? 0 : last + 1;
+    }
+    if ((phase != ECH_EARLY && n_want > found) || clamped) ctr[ECH_CTR_STATUS] |= ECH_ST_OVERFLOW;
+  }
+}
+
+__global__ __launch_bounds__(kT) void place_kernel(int phase, int nseq, int cap, int32_t* __restrict__ tok2slot,
+                                                   int32_t* __restrict__ slot2tok,
+                                                   const int32_t* __restrict__ slot_pin, int32_t* __restrict__ miss,
+                                                   int32_t* ctr, int32_t* __restrict__ sel_slot,
+                                                   int32_t* __restrict__ stats, CWs w) {
+  __shared__ __align__(16) uint8_t smem[4 * kBlk + kWin];   // >= 4 kMaxB ints + kWin bytes
+  __shared__ int scr[kT / 64];
+  __shared__ int s_lastw;
+  static_assert(4 * kBlk >= 4 * 4 * kMaxB, "bookkeeping arrays fit");
+  const int i = blockIdx.x;
+  if (i == w.ne) {
+    if (blockIdx.y == 0) bookkeep(phase, nseq, cap, slot_pin, ctr, stats, w, smem, scr);
+    return;
+  }
+  const int cnt = min(w.want[i], w.lcap);
+  const int span = (gridDim.y == 1) ? w.lcap : kT;
+  const int j_lo = blockIdx.y * span;
+  if (j_lo >= cnt) return;   // block-uniform: most blocks have no misses
+  const int j_hi = min(cnt, j_lo + span);
+  const int tid = threadIdx.x;
+  const int b = i / w.nbr, c = i % w.nbr;
+  // ranks: capped totals of the sequences before b, then b's misses before block i
+  int prev = 0;
+  for (int bb = tid; bb < b; bb += kT) {
+    const int wb = sum_counts(w.want + (size_t)bb * w.nbr, w.nbr);
+    prev += (phase == ECH_EARLY) ? min(cap, wb) : wb;
+  }
+  int pre = 0, tot_b = 0;
+  for (int cc = tid; cc < w.nbr; cc += kT) {
+    const int v = w.want[(size_t)b * w.nbr + cc];
+    tot_b += v;
+    pre += (cc < c) ? v : 0;
+  }
+  prev = ech::block_sum<kT>(prev, scr);
+  pre = ech::block_sum<kT>(pre, scr);
+  tot_b = ech::block_sum<kT>(tot_b, scr);
+  const int take = (phase == ECH_EARLY) ? min(cap, tot_b) : tot_b;
+  const int base = prev + pre;                      // rank of list entry 0
+  const int lim = min(prev + take, w.M_max);        // ranks at or past lim are not placed
+  const int r_lo = base + j_lo, r_hi = min(base + j_hi, lim);
+  if (r_lo >= r_hi) return;                         // block-uniform: all past the cap
+  // the free slots of ranks [r_lo, r_hi)
+  int* s_slot = reinterpret_cast<int*>(smem);
+  uint8_t* s_fr = smem + 4 * kBlk;
+  for (int j = tid; j < r_hi - r_lo; j += kT) s_slot[j] = -1;
+  __syncthreads();
+  const int ep = w.sc[S_EP], head = w.sc[S_HEAD];
+  ring_scan(slot_pin, w.C, head, ep, r_hi, r_lo, r_hi, s_fr, scr, &s_lastw,
+            [&](int r, int p) { s_slot[r - r_lo] = p; });
+  const int owner = (phase == ECH_PREFILL) ? 0 : b;
+  for (int j = tid; j < r_hi - r_lo; j += kT) {   // trips differ only in the last pass
+    const int m = r_lo + j;
+    const int2 mc = w.lmiss[(size_t)i * w.lcap + j_lo + j];
+    const int g = mc.x;
+    const int p = s_slot[j];
     bool evicted = false;
-    if (m < lim) {
-      const int2 mc = w.lmiss[(size_t)blk * w.lcap + i];
-      const int g = mc.x;
-      if (g < 0 || g >= w.P) {
-        set_status(ctr, ECH_ST_OVERFLOW);   // unreachable unless counts and lists disagree
-      } else if (m < n_alloc) {
-        const int p = w.freelist[m];
-        if (p < 0 || p >= w.C) {
-          set_status(ctr, ECH_ST_OVERFLOW);
-        } else {
-          const int u = slot2tok[p];
-          if (u >= 0 && u < w.P) {
-            tok2slot[u] = -1;   // evict; the host row stays where it is
-            evicted = true;
-          }
-          slot2tok[p] = g;
-          tok2slot[g] = p;
-          slot_pin[p] = ep;
-          miss[2 * m] = g;
-          miss[2 * m + 1] = p;
-          if (phase == ECH_FINAL) sel_slot[mc.y] = p;
-        }
-      } else if (phase == ECH_PREFILL) {
-        tok2slot[g] = -1;     // release the claim of a miss that got no slot
+    if (g < 0 || g >= w.P) {
+      set_status(ctr, ECH_ST_OVERFLOW);   // unreachable unless counts and lists disagree
+    } else if (p >= 0) {
+      const int u = slot2tok[p];
+      if (u >= 0 && u < w.P) {
+        tok2slot[u] = -1;   // evict; the host row stays where it is
+        evicted = true;
       }
+      slot2tok[p] = g;
+      tok2slot[g] = p;
+      miss[2 * m] = g;
+      miss[2 * m + 1] = p;
+      if (phase == ECH_FINAL) sel_slot[mc.y] = p;
+    } else if (phase == ECH_PREFILL) {
+      tok2slot[g] = -1;     // release the claim of a miss that got no slot
     }
     ech::wave_count(&ctr[ECH_CTR_NEVICT], evicted);
     ech::wave_count(&stats[4 * owner + 3], evicted);
@@ -617,7 +604,7 @@ extern "C" int ech_cache_reset(int32_t* tok2slot, int64_t P, int32_t* slot2tok, 
 extern "C" size_t ech_cache_step_ws_bytes(int phase, int B, int R, int k, int max_len, int32_t C, int32_t M_max) {
   if (phase < ECH_EARLY || phase > ECH_PREFILL || B < 1 || k < 1 || max_len < 0 || C < 1 || M_max < 0) return 0;
   (void)R;
-  return layout(phase, B, k, max_len, M_max, nullptr, nullptr);
+  return layout(phase, B, k, max_len, nullptr, nullptr);
 }
 
 extern "C" int ech_cache_step(int phase, int32_t* tok2slot, int64_t P, int32_t* slot2tok, int32_t* slot_pin,
@@ -647,33 +634,30 @@ extern "C" int ech_cache_step(int phase, int32_t* tok2slot, int64_t P, int32_t* 
   if ((int64_t)M_max < demand) return ECH_EINVAL;
   if (ws_bytes < ech_cache_step_ws_bytes(phase, B, R, k, max_len, C, M_max)) return ECH_EINVAL;
   CWs w;
-  layout(phase, B, k, max_len, M_max, &w, static_cast<char*>(ws));
+  layout(phase, B, k, max_len, &w, static_cast<char*>(ws));
   w.P = (int)P;
   w.C = C;
   w.M_max = M_max;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   const int nbj = (k + kT - 1) / kT;
-  // count, allocate, apply
+  // count, then place (the ranks, the free slots and the maps)
   if (phase == ECH_FINAL) {
     hipLaunchKernelGGL(pin_final_kernel, dim3(nbj, B), dim3(kT), 0, s, idx, k, seq_tok0, seq_len, tok2slot,
-                       slot_pin, sel_slot, ctr, w);
+                       slot_pin, sel_slot, ctr, stats, w);
   } else if (phase == ECH_EARLY) {
     hipLaunchKernelGGL(pin_early_kernel, dim3(w.nbr, B), dim3(kT), 0, s, logits, ld, theta, seq_tok0, seq_len,
-                       tok2slot, slot_pin, ctr, w);
+                       tok2slot, slot_pin, ctr, stats, w);
   } else {
     hipLaunchKernelGGL(pin_prefill_kernel, dim3(nbj, R), dim3(kT), 0, s, idx, k, seq_tok0, seq_len, tok2slot,
                        slot_pin, ctr, w);
     ECH_LAUNCH_CHECK();
     hipLaunchKernelGGL(count_claimed_kernel, dim3(w.ne), dim3(kT), 0, s, seq_tok0, seq_len, tok2slot, slot_pin, ctr,
-                       w);
+                       stats, w);
   }
   ECH_LAUNCH_CHECK();
-  hipLaunchKernelGGL(allocate_kernel, dim3(1), dim3(kA), 0, s, phase, phase == ECH_PREFILL ? 1 : B, cap, ctr,
-                     slot_pin, stats, w);
-  ECH_LAUNCH_CHECK();
   const int slices = (phase == ECH_PREFILL) ? w.lcap / kT : 1;
-  hipLaunchKernelGGL(apply_kernel, dim3(w.ne, slices), dim3(kT), 0, s, phase, tok2slot, slot2tok, slot_pin, miss,
-                     ctr, sel_slot, stats, w);
+  hipLaunchKernelGGL(place_kernel, dim3(w.ne + 1, slices), dim3(kT), 0, s, phase, phase == ECH_PREFILL ? 1 : B, cap,
+                     tok2slot, slot2tok, slot_pin, miss, ctr, sel_slot, stats, w);
   ECH_LAUNCH_CHECK();
   if (phase == ECH_PREFILL) {
     hipLaunchKernelGGL(selfill_kernel, dim3(nbj, R), dim3(kT), 0, s, idx, k, seq_tok0, seq_len, tok2slot, P,

@@ -402,8 +402,7 @@ __global__ __launch_bounds__(kA) void early_rank_kernel(int group, int b0, int n
 
 // grid (nch, b1 - b0): block (c, j) places its listed misses by rank.
 __global__ __launch_bounds__(kT) void early_apply_kernel(int group, int b0, int32_t* __restrict__ tok2slot,
-                                                         int64_t P, int32_t* __restrict__ slot2tok,
-                                                         int32_t* __restrict__ slot_pin, int32_t C,
+                                                         int64_t P, int32_t* __restrict__ slot2tok, int32_t C,
                                                          int32_t* __restrict__ miss, int32_t M_early, int32_t* ctr,
                                                          int32_t* __restrict__ stats, EWs ws) {
   const int b = b0 + blockIdx.y, c = blockIdx.x;
@@ -412,7 +411,6 @@ __global__ __launch_bounds__(kT) void early_apply_kernel(int group, int b0, int3
   const int base = ws.off[blk];
   const int lim = min(ws.lim[b], min(ws.grp[2 * group + 1], M_early));
   if (cnt == 0 || base >= lim) return;   // block-uniform
-  const int ep = ws.sc[E_EP];
   const int last = ws.grp[2 * group + 1] - 1;
   for (int i = threadIdx.x; i < cnt; i += kT) {   // trips differ only in the last pass
     const int m = base + i;
@@ -430,7 +428,6 @@ __global__ __launch_bounds__(kT) void early_apply_kernel(int group, int b0, int3
         }
         slot2tok[p] = g;
         tok2slot[g] = p;
-        slot_pin[p] = ep;
         miss[2 * m] = g;
         miss[2 * m + 1] = p;
         if (m == last) ctr[ECH_CTR_HEAD] = (p + 1 == C) ? 0 : p + 1;
@@ -549,8 +546,8 @@ extern "C" int ech_early_group(int group, int b0, int b1, const float* logits, i
   ECH_LAUNCH_CHECK();
   hipLaunchKernelGGL(early_rank_kernel, dim3(1), dim3(kA), 0, s, group, b0, b1 - b0, cap, ctr, stats, e);
   ECH_LAUNCH_CHECK();
-  hipLaunchKernelGGL(early_apply_kernel, gg, dim3(kT), 0, s, group, b0, tok2slot, P, slot2tok, slot_pin, C,
-                     miss_early, M_early, ctr, stats, e);
+  hipLaunchKernelGGL(early_apply_kernel, gg, dim3(kT), 0, s, group, b0, tok2slot, P, slot2tok, C, miss_early,
+                     M_early, ctr, stats, e);
   ECH_LAUNCH_CHECK();
   return ECH_OK;
 }
