@@ -51,7 +51,8 @@ def test_ws_sizes_monotone():
     assert 0 < a < b
     assert lib.ech_topk_ws_bytes(0, 10, 10) == 0
     c = lib.ech_cache_step_ws_bytes(1, 32, 32, 2048, 131072, 260000, 65536)
-    assert c >= 65536 * 12
+    assert c >= 32 * 2048 * 8          # FINAL: room to list every selected token as a miss (8 B each)
+    assert lib.ech_cache_step_ws_bytes(1, 64, 64, 2048, 131072, 260000, 131072) > c
     assert lib.ech_cache_step_ws_bytes(7, 1, 1, 1, 1, 1, 1) == 0
 
 
