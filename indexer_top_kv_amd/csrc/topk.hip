@@ -894,6 +894,192 @@ __global__ __launch_bounds__(kT) void topk_compact_kernel(const float* __restric
   }
 }
 
+// ------------------------------------------------------------------ short rows
+// A few rows of at most kSmallMax tokens: one launch, one workgroup per row,
+// each thread holding 16 consecutive scores of the row in registers for the
+// whole kernel. The same steps as the multi-kernel path: histogram of the
+// shifted bins, boundary bin b*, radix rounds on the exact order keys of the
+// b* tokens (listed in LDS and selected by one wave when there are at most
+// kSmallCand of them, else block-wide over the registers, so b* may be any
+// width), then the selection written in token order by one ordered pass.
+constexpr int kSmallNT = 1024;
+constexpr int kSmallPer = 16;
+constexpr int kSmallMax = kSmallNT * kSmallPer;   // 16384 tokens
+constexpr int kSmallCand = 4096;                  // boundary tokens listed for the radix rounds
+
+__global__ __launch_bounds__(kSmallNT) void topk_small_kernel(const float* __restrict__ logits, int64_t ld,
+                                                              const int32_t* __restrict__ lens, int k,
+                                                              const float* __restrict__ theta_in,
+                                                              float* __restrict__ theta_out,
+                                                              float* __restrict__ kth, int32_t* __restrict__ idx) {
+  constexpr int NT = kSmallNT;
+  __shared__ int2 cand[kSmallCand];   // (score bits, token) of the boundary tokens
+  __shared__ int hist[256];
+  __shared__ int sh[NT / 64];
+  __shared__ int s_digit, s_need, s_nc;
+  __shared__ uint32_t s_prefix;
+  __shared__ float s_min;
+  const int r = blockIdx.x, tid = threadIdx.x;
+  const int len = min(lens[r], kSmallMax);
+  const float th_in = row_theta(theta_in, r);
+  int32_t* orow = idx + (size_t)r * k;
+  for (int j = min(k, len) + tid; j < k; j += NT) orow[j] = -1;
+  if (len == 0) {
+    if (tid == 0) {
+      kth[r] = __builtin_nanf("");
+      if (theta_out) theta_out[r] = th_in;
+    }
+    return;
+  }
+  // tokens t0 .. t0+15 of this thread (16-byte aligned rows: ld % 4 == 0)
+  const int t0 = kSmallPer * tid;
+  const float* row = logits + (size_t)r * ld;
+  float v[kSmallPer];
+  if (t0 + kSmallPer <= len) {
+#pragma unroll
+    for (int q = 0; q < kSmallPer / 4; ++q) {
+      const float4 x = reinterpret_cast<const float4*>(row + t0)[q];
+      v[4 * q] = x.x;
+      v[4 * q + 1] = x.y;
+      v[4 * q + 2] = x.z;
+      v[4 * q + 3] = x.w;
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < kSmallPer; ++e) v[e] = t0 + e < len ? row[t0 + e] : 0.f;
+  }
+  uint32_t valid = 0;   // bit e: token t0 + e is in the row
+#pragma unroll
+  for (int e = 0; e < kSmallPer; ++e) valid |= (t0 + e < len) ? 1u << e : 0u;
+  float sstar;
+  int need_eq = 0;
+  if (len <= k) {
+    // every token is selected; kth is the row minimum
+    float m = __builtin_inff();
+#pragma unroll
+    for (int e = 0; e < kSmallPer; ++e)
+      if ((valid >> e) & 1u) m = fminf(m, v[e]);
+    for (int d = 32; d > 0; d >>= 1) m = fminf(m, __shfl_xor(m, d, 64));
+    float* wmin = reinterpret_cast<float*>(hist);
+    if (ech::lane_id() == 0) wmin[tid / 64] = m;
+#pragma unroll
+    for (int e = 0; e < kSmallPer; ++e)
+      if ((valid >> e) & 1u) orow[t0 + e] = t0 + e;
+    __syncthreads();
+    if (tid == 0) {
+      float mm = __builtin_inff();
+      for (int i = 0; i < NT / 64; ++i) mm = fminf(mm, wmin[i]);
+      s_min = mm;
+    }
+    __syncthreads();
+    sstar = s_min;
+  } else {
+    // 1. histogram of the shifted bins (lumped tokens counted per wave); the
+    // thread keeps its bins
+    const Shift shf = make_shift(th_in);
+    if (tid < 256) hist[tid] = 0;
+    if (tid == 0) s_nc = 0;
+    __syncthreads();
+    uint32_t bins[kSmallPer];
+    int lumped = 0;
+#pragma unroll
+    for (int e = 0; e < kSmallPer; ++e) {
+      bins[e] = shifted_bin(v[e], shf);
+      const bool ok = (valid >> e) & 1u;
+      const bool lump = ok && shf.on && bins[e] == 0u;
+      lumped += lump;
+      ech::lds_hist_add(hist, bins[e], ok && !lump);
+    }
+    lumped = ech::wave_sum(lumped);
+    if (ech::lane_id() == 0 && lumped) atomicAdd(&hist[0], lumped);
+    __syncthreads();
+    // 2. boundary bin and the rank of the k-th token within it
+    pick_digit(hist, sh, k, &s_digit, &s_need);
+    const uint32_t bstar = (uint32_t)s_digit;
+    int need = s_need;
+    // list the boundary tokens (one LDS atomic per wave)
+    uint32_t bm = 0;
+#pragma unroll
+    for (int e = 0; e < kSmallPer; ++e) bm |= (((valid >> e) & 1u) && bins[e] == bstar) ? 1u << e : 0u;
+    const int cnt = __popc(bm);
+    const int incl = ech::wave_incl_scan(cnt);
+    int wbase = 0;
+    if (ech::lane_id() == 63 && incl > 0) wbase = atomicAdd(&s_nc, incl);
+    wbase = __shfl(wbase, 63, 64);
+    int p = wbase + incl - cnt;
+#pragma unroll
+    for (int e = 0; e < kSmallPer; ++e) {
+      if ((bm >> e) & 1u) {
+        if (p < kSmallCand) cand[p] = make_int2(__float_as_int(v[e]), t0 + e);
+        ++p;
+      }
+    }
+    __syncthreads();
+    const int nc = s_nc;
+    // 3. the need-th largest boundary score: one wave over the list, or
+    // block-wide rounds over the registers when the bin is wider than it
+    uint32_t prefix = 0;
+    if (nc <= kSmallCand) {   // block-uniform
+      if (tid < 64) {
+        int nq;
+        const uint32_t pf = wave_select(cand, nc, need, hist, &nq);
+        if (tid == 0) {
+          s_prefix = pf;
+          s_need = nq;
+        }
+      }
+      __syncthreads();
+      prefix = s_prefix;
+      need = s_need;
+    } else {
+      uint32_t mask = 0;
+#pragma unroll 1
+      for (int round = 0; round < 4; ++round) {
+        const int shift = 24 - 8 * round;
+        if (tid < 256) hist[tid] = 0;
+        __syncthreads();
+#pragma unroll
+        for (int e = 0; e < kSmallPer; ++e) {
+          const uint32_t key = ech::ord_key(v[e]);
+          ech::lds_hist_add(hist, (key >> shift) & 255u, ((bm >> e) & 1u) && (key & mask) == prefix);
+        }
+        __syncthreads();
+        pick_digit(hist, sh, need, &s_digit, &s_need);
+        prefix |= (uint32_t)s_digit << shift;
+        mask |= 255u << shift;
+        need = s_need;
+        __syncthreads();
+      }
+    }
+    sstar = ech::ord_to_float(prefix);
+    need_eq = need;
+    // 4. the selection in token order: every score above s*, and the first
+    // need_eq equal to it
+    uint32_t gtm = 0, eqm = 0;
+#pragma unroll
+    for (int e = 0; e < kSmallPer; ++e) {
+      const bool ok = (valid >> e) & 1u;
+      gtm |= (ok && v[e] > sstar) ? 1u << e : 0u;
+      eqm |= (ok && v[e] == sstar) ? 1u << e : 0u;
+    }
+    int tot;
+    const int pre = ech::block_excl_scan<NT>(__popc(gtm) | (__popc(eqm) << 16), sh, &tot);
+    int gt_b = pre & 0xffff, eq_b = pre >> 16;
+#pragma unroll
+    for (int e = 0; e < kSmallPer; ++e) {
+      const bool gt = (gtm >> e) & 1u, eq = (eqm >> e) & 1u;
+      const int pos = gt_b + min(eq_b, need_eq);
+      if ((gt || (eq && eq_b < need_eq)) && pos < k) orow[pos] = t0 + e;
+      gt_b += gt;
+      eq_b += eq;
+    }
+  }
+  if (tid == 0) {
+    kth[r] = sstar;
+    if (theta_out) theta_out[r] = (th_in == th_in) ? (sstar + th_in) * 0.5f : sstar;
+  }
+}
+
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 }  // namespace
@@ -915,6 +1101,12 @@ extern "C" int ech_topk(const float* logits, int64_t ld, const int32_t* row_len,
   Ws w;
   layout(R, max_len, k, &w, static_cast<char*>(ws));
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (R <= 256 && max_len <= kSmallMax) {   // a few short rows: one launch
+    hipLaunchKernelGGL(topk_small_kernel, dim3(R), dim3(kSmallNT), 0, s, logits, ld, row_len, k, theta_in,
+                       theta_out, kth, idx);
+    ECH_LAUNCH_CHECK();
+    return ECH_OK;
+  }
   const dim3 gch(w.nch, R);
   hipLaunchKernelGGL(topk_hist_kernel, gch, dim3(kT), 0, s, logits, ld, row_len, k, theta_in, w);
   ECH_LAUNCH_CHECK();

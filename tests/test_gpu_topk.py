@@ -155,3 +155,43 @@ def test_rows_longer_than_one_rowsel_pass():
     kth = np.array([oracle.topk_row(x[r, :lens[r]], k)[1] for r in range(R)], np.float32)
     factor = np.array([1.0, np.nan, 1.5, 3.0], np.float32)[np.arange(R) % 4]
     _check(x, lens, k, (kth * factor).astype(np.float32))
+
+
+@pytest.mark.parametrize('kind', ['normal', 'ties', 'const', 'signed'])
+def test_short_rows_one_launch(kind):
+    """A few rows of at most 16384 tokens take the one-launch path (one
+    workgroup per row, the row in LDS): ragged lengths around k, empty and
+    one-token rows, with no, exact, near, far-above and far-below predictions."""
+    need_gpu()
+    n = 16384
+    lens = [16384, 2048, 2049, 2047, 1, 0, 9999, 16383]
+    R = len(lens)
+    x = wk.random_logits(14, R, n, kind)
+    kth = np.array([oracle.topk_row(x[r, :lens[r]], 2048)[1] if lens[r] else np.nan for r in range(R)], np.float32)
+    _check(x, lens, 2048)
+    for th in (kth, kth + np.float32(1e-3), kth * np.float32(3.0) + np.float32(5.0), kth - np.float32(40.0)):
+        _check(x, lens, 2048, th)
+    mixed = kth.copy()
+    mixed[::3] = np.nan
+    _check(x, lens, 2048, mixed)
+
+
+@pytest.mark.parametrize('k', [1, 7, 2048, 4096])
+def test_short_rows_various_k(k):
+    need_gpu()
+    x = wk.random_logits(15, 5, 16384, 'normal')
+    lens = [16384, 5000, 4097, 4096, 4095]
+    kth = np.array([oracle.topk_row(x[r, :lens[r]], k)[1] for r in range(5)], np.float32)
+    _check(x, lens, k, kth * np.float32(1.01))
+
+
+def test_short_rows_most_rows_and_many_rows():
+    """256 rows of 16384 (the most the one-launch path takes) and 300 short
+    rows (more than that: the multi-kernel path)."""
+    need_gpu()
+    x = wk.random_logits(16, 256, 16384, 'normal')
+    kth = np.array([oracle.topk_row(x[r], 2048)[1] for r in range(256)], np.float32)
+    _check(x, [16384] * 256, 2048, kth)
+    lens = [100 + (r * 977) % 16285 for r in range(300)]
+    y = wk.random_logits(17, 300, 16384, 'ties')
+    _check(y, lens, 2048)
