@@ -50,6 +50,8 @@ def parse():
                    help='prefill: one score buffer, top-k after each block on the same stream (ablation)')
     p.add_argument('--cpu-seqs', type=int, default=32, help='sequences in the oracle sample')
     p.add_argument('--cpu-steps', type=int, default=5, help='decode steps in the oracle sample')
+    p.add_argument('--topk-first', choices=['auto', 'on', 'off'], default='auto',
+                   help='decode: launch the top-k before the EARLY maps (auto: batches of at most 8 sequences)')
     p.add_argument('--calibrate-copy', action='store_true',
                    help='only run a plain 1 GiB device copy 5 times (reference for HBM byte counters)')
     return p.parse_args()
@@ -109,6 +111,7 @@ def bench_decode(args, wl):
     qd = dev(qs)
     layer = DecodeLayer(kc, ks, wd, wl.tok0, wl.lens, wl.C, k=wl.k, cap=wl.cap, host_pool=pool,
                         early=not args.no_early, topk_after_early=args.topk_after_early,
+                        topk_first={'auto': None, 'on': True, 'off': False}[args.topk_first],
                         early_groups=args.early_groups)
     torch.cuda.synchronize()
     log(f'chunks {layer.chunks}; warm-up {args.warmup} steps')
@@ -186,7 +189,8 @@ def bench_decode(args, wl):
         'config': {'workload': wl.name, 'B': wl.B, 'context': wl.N, 'k': wl.k, 'heads': 64, 'head_dim': 128,
                    'key_dtype': wl.kdtype, 'cache_slots': wl.C, 'early_fetch_cap': wl.cap,
                    'early_fetch': not args.no_early, 'early_groups': len(layer.groups), 'row_bytes': 1152,
-                   'launch': 'eager' if args.eager else 'hipGraph replay per step'},
+                   'launch': 'eager' if args.eager else 'hipGraph replay per step',
+                   'topk_first': layer.topk_first},
         'roofline': {'bound': 'hbm', 'kernel': 'logits_decode_fp8_kernel' if wl.kdtype == 'fp8' else 'logits_decode_kernel',
                      'achieved': achieved,
                      'peak': PEAK_HBM_GBS, 'unit': 'GB/s', 'frac': achieved / PEAK_HBM_GBS,

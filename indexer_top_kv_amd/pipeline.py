@@ -77,9 +77,16 @@ class DecodeLayer:
     def __init__(self, kcache: torch.Tensor, kscale: Optional[torch.Tensor], w: torch.Tensor,
                  tok0: np.ndarray, lens: np.ndarray, C: int, k: int = 2048, cap: int = 512,
                  host_pool: Optional[torch.Tensor] = None, early: bool = True, topk_after_early: bool = False,
+                 topk_first: Optional[bool] = None,
                  early_groups: int = 0, device='cuda'):
         self.kcache, self.kscale, self.w = kcache, kscale, w
         self.topk_after_early = topk_after_early
+        # Launch order of the two branches after the scores. A captured graph
+        # keeps the branch launched first on the scores kernel's hardware
+        # queue; the other starts after a cross-queue wait (~10 us). With a
+        # few sequences the top-k chain is the longer branch, with many the
+        # EARLY maps and their PCIe recall are.
+        self.topk_first = (len(lens) <= 8) if topk_first is None else bool(topk_first)
         self.B = len(lens)
         self.lens_np = np.asarray(lens, np.int32)
         self.tok0_np = np.asarray(tok0, np.int64)
@@ -181,8 +188,10 @@ class DecodeLayer:
         mark('logits', s0)
         first_b0, first_b1 = self.chunks[0]
         if self.early:
-            # S1: EARLY maps, then its rows cross PCIe while S0 carries on.
             self.ev_logits.record(s0)
+
+        def early_branch():
+            # S1: EARLY maps, then its rows cross PCIe while S0 carries on.
             self.s1.wait_event(self.ev_logits)
             mark('early', self.s1)
             mark('early_maps', self.s1)
@@ -194,15 +203,23 @@ class DecodeLayer:
             mark('recall_early', self.s1)
             mark('early', self.s1)
             self.ev_early.record(self.s1)
-        # The top-k runs beside the EARLY maps; kernels that overlap the PCIe
-        # gather of the EARLY recall slow down several-fold (its host reads
-        # hold the shared memory queues), so only the small FINAL maps do.
-        if self.early and self.topk_after_early:
-            s0.wait_event(self.ev_early_maps)
-        mark('topk', s0)
-        ech_topk(self.logits, self.lens, self.max_len, self.k, th, th_next, self.idx, self.kth, self.ws_topk,
-                 stream=s0)
-        mark('topk', s0)
+
+        def topk_branch():
+            # The top-k runs beside the EARLY maps (or after them, on request).
+            if self.early and self.topk_after_early:
+                s0.wait_event(self.ev_early_maps)
+            mark('topk', s0)
+            ech_topk(self.logits, self.lens, self.max_len, self.k, th, th_next, self.idx, self.kth, self.ws_topk,
+                     stream=s0)
+            mark('topk', s0)
+
+        if self.early and not (self.topk_first and not self.topk_after_early):
+            early_branch()
+            topk_branch()
+        else:
+            topk_branch()
+            if self.early:
+                early_branch()
         mark('final', s0)
         if self.early and not self.topk_after_early:
             s0.wait_event(self.ev_early_maps)      # FINAL updates the maps EARLY left ...
