@@ -381,17 +381,36 @@ __global__ __launch_bounds__(kT) void count_claimed_kernel(const int64_t* __rest
 // and epoch. Nothing in this kernel writes slot_pin, so every block ranks the
 // same free slots.
 
-__device__ __forceinline__ int sum_counts(const int* p, int n) {
-  int s = 0, c = 0;
-  for (; c + 8 <= n; c += 8) {
+// s_tot[b] = the sum of cnt[b * nbr + c] over c, for b < nb (LDS), by the
+// whole block: thread t sums a contiguous run of the counts (all its loads
+// in flight) and adds each sequence's part with one LDS atomic.
+__device__ void seq_totals(const int* __restrict__ cnt, int nb, int nbr, int* s_tot) {
+  const int tid = threadIdx.x;
+  for (int b = tid; b < nb; b += kT) s_tot[b] = 0;
+  __syncthreads();
+  const int n = nb * nbr;
+  const int m = (n + kT - 1) / kT;
+  const int i_lo = min(n, tid * m), i_hi = min(n, i_lo + m);
+  int cur = -1, acc = 0;
+  for (int i0 = i_lo; i0 < i_hi; i0 += 8) {
     int v[8];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) v[u] = p[c + u];   // eight loads in flight
+    for (int u = 0; u < 8; ++u) v[u] = cnt[min(i0 + u, n - 1)];   // clamped: all issued at once
 #pragma unroll
-    for (int u = 0; u < 8; ++u) s += v[u];
+    for (int u = 0; u < 8; ++u) {
+      if (i0 + u < i_hi) {
+        const int sq = (i0 + u) / nbr;
+        if (sq != cur) {
+          if (acc) atomicAdd(&s_tot[cur], acc);
+          cur = sq;
+          acc = 0;
+        }
+        acc += v[u];
+      }
+    }
   }
-  for (; c < n; ++c) s += p[c];
-  return s;
+  if (acc) atomicAdd(&s_tot[cur], acc);
+  __syncthreads();
 }
 
 __device__ void bookkeep(int phase, int nseq, int cap, const int32_t* __restrict__ slot_pin, int32_t* ctr,
@@ -404,16 +423,16 @@ __device__ void bookkeep(int phase, int nseq, int cap, const int32_t* __restrict
   __shared__ int s_last, s_lastw;
   const int tid = threadIdx.x;
   const int ep = w.sc[S_EP], head = w.sc[S_HEAD];
+  seq_totals(w.want, nseq, w.nbr, s_want);
+  seq_totals(w.hit, nseq, w.nbr, s_hit);
   int n_want = 0, hit_all = 0;
   for (int b0 = 0; b0 < nseq; b0 += kT) {
     const int b = b0 + tid;
     int take = 0, h = 0;
     if (b < nseq) {
-      const int wb = sum_counts(w.want + (size_t)b * w.nbr, w.nbr);
-      h = sum_counts(w.hit + (size_t)b * w.nbr, w.nbr);
+      const int wb = s_want[b];
+      h = s_hit[b];
       take = (phase == ECH_EARLY) ? min(cap, wb) : wb;
-      s_want[b] = wb;
-      s_hit[b] = h;
       s_take[b] = take;
     }
     int tot;
@@ -452,7 +471,9 @@ __global__ __launch_bounds__(kT) void place_kernel(int phase, int nseq, int cap,
                                                    const int32_t* __restrict__ slot_pin, int32_t* __restrict__ miss,
                                                    int32_t* ctr, int32_t* __restrict__ sel_slot,
                                                    int32_t* __restrict__ stats, CWs w) {
-  __shared__ __align__(16) uint8_t smem[4 * kBlk + kWin];   // >= 4 kMaxB ints + kWin bytes
+  // placing blocks: s_slot [kBlk ints] | s_fr [kWin bytes] | s_tot [kMaxB ints];
+  // the bookkeeping block: 4 x [kMaxB ints] | s_fr [kWin bytes]
+  __shared__ __align__(16) uint8_t smem[4 * kBlk + kWin + 4 * kMaxB];
   __shared__ int scr[kT / 64];
   __shared__ int s_lastw;
   static_assert(4 * kBlk >= 4 * 4 * kMaxB, "bookkeeping arrays fit");
@@ -469,20 +490,15 @@ __global__ __launch_bounds__(kT) void place_kernel(int phase, int nseq, int cap,
   const int tid = threadIdx.x;
   const int b = i / w.nbr, c = i % w.nbr;
   // ranks: capped totals of the sequences before b, then b's misses before block i
+  int* s_tot = reinterpret_cast<int*>(smem + 4 * kBlk + kWin);
+  seq_totals(w.want, b + 1, w.nbr, s_tot);
   int prev = 0;
-  for (int bb = tid; bb < b; bb += kT) {
-    const int wb = sum_counts(w.want + (size_t)bb * w.nbr, w.nbr);
-    prev += (phase == ECH_EARLY) ? min(cap, wb) : wb;
-  }
-  int pre = 0, tot_b = 0;
-  for (int cc = tid; cc < w.nbr; cc += kT) {
-    const int v = w.want[(size_t)b * w.nbr + cc];
-    tot_b += v;
-    pre += (cc < c) ? v : 0;
-  }
+  for (int bb = tid; bb < b; bb += kT) prev += (phase == ECH_EARLY) ? min(cap, s_tot[bb]) : s_tot[bb];
+  int pre = 0;
+  for (int cc = tid; cc < c; cc += kT) pre += w.want[(size_t)b * w.nbr + cc];
   prev = ech::block_sum<kT>(prev, scr);
   pre = ech::block_sum<kT>(pre, scr);
-  tot_b = ech::block_sum<kT>(tot_b, scr);
+  const int tot_b = s_tot[b];
   const int take = (phase == ECH_EARLY) ? min(cap, tot_b) : tot_b;
   const int base = prev + pre;                      // rank of list entry 0
   const int lim = min(prev + take, w.M_max);        // ranks at or past lim are not placed
