@@ -219,7 +219,7 @@ def bench_decode(args, wl):
                    'achieved_GBs': out['recall']['bytes_per_step'] / (rec_us * 1e-6) / 1e9 if rec_us else None,
                    'note': 'EARLY + FINAL recall kernels of eager steps; denominator: pcie.h2d_memcpy_GBs'},
         'allocator': {'early_maps_us': st['early_maps'], 'final_maps_us': st['final_maps'],
-                      'note': 'slot-map phases in eager steps (count, allocate, apply), run beside '
+                      'note': 'slot-map phases in eager steps (count, place), run beside '
                               'the top-k (EARLY) and beside the EARLY recall (FINAL)'},
     }
     return out, dict(wl=wl, pool=pool, qs=qs, w=w, keys=keys, scale=scale)
