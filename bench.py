@@ -136,16 +136,18 @@ def bench_decode(args, wl):
     stats_final = layer.stats_final.cpu().numpy()
     stats_early = layer.stats_early.cpu().numpy()
 
-    # The roofline kernel, timed with HIP events on its launch stream: the
-    # same launch (same q, keys, grid) repeated K times back to back.
+    # The roofline kernel, timed with HIP events on its launch stream: K
+    # launches back to back (the step's queries) between one pair of events,
+    # so no event sits between launches; the average launch is the span / K.
     s0 = torch.cuda.current_stream()
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * args.steps)]
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    layer.logits_only(qd[args.warmup], stream=s0)
+    ev0.record(s0)
     for s in range(args.steps):
-        ev[2 * s].record(s0)
         layer.logits_only(qd[args.warmup + s], stream=s0)
-        ev[2 * s + 1].record(s0)
+    ev1.record(s0)
     torch.cuda.synchronize()
-    logits_runs = [ev[2 * s].elapsed_time(ev[2 * s + 1]) for s in range(args.steps)]
+    logits_runs = [ev0.elapsed_time(ev1) / args.steps]
 
     # Stage breakdown from a few eager steps with events on each stage's stream.
     marks = {}
