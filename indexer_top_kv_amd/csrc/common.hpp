@@ -38,27 +38,14 @@ __device__ __forceinline__ void lds_hist_add(int* hist, uint32_t bin, bool activ
   if (active) atomicAdd(&hist[bin], 1);
 }
 
-// Global counters bumped by many lanes: one atomic per wave (per distinct
-// word) with the number of flagged lanes, instead of one per lane. Atomics on
+// A global counter bumped by many lanes: one atomic per wave with the number
+// of flagged lanes, instead of one per lane. Atomics on
 // one word serialise in one L2 channel, which made per-lane counting cost tens
 // of microseconds over 10^5 entries. Call from converged code: every active
 // lane takes part in the ballots.
 __device__ __forceinline__ void wave_count(int32_t* addr, bool flag) {
   const unsigned long long m = __ballot(flag);
   if (m != 0ull && lane_id() == __builtin_ctzll(m)) atomicAdd(addr, (int)__popcll(m));
-}
-
-// base[key] += the number of flagged lanes holding that key, for each key
-// present in the wave; one pass per distinct key.
-__device__ __forceinline__ void wave_count_keyed(int32_t* base, int key, bool flag) {
-  unsigned long long todo = __ballot(flag);
-  while (todo != 0ull) {
-    const int leader = __builtin_amdgcn_readfirstlane(__builtin_ctzll(todo));
-    const int k0 = __builtin_amdgcn_readlane(key, leader);
-    const unsigned long long same = __ballot(flag && key == k0);
-    if (lane_id() == leader) atomicAdd(&base[k0], (int)__popcll(same));
-    todo &= ~same;
-  }
 }
 
 // Inclusive prefix sum across the wave.
