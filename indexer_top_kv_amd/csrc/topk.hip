@@ -208,7 +208,7 @@ __global__ __launch_bounds__(kT) void topk_hist_kernel(const float* __restrict__
 }
 
 // ------------------------------------------------------------------ T2
-// NT threads (1024 for a few long rows, 256 for many rows). Wave w reads the
+// T2 for a few long rows, NT = 1024 threads. Wave w reads the
 // chunk histograms w, w + kW, ... with lane l holding bins 4l..4l+3 (one int4
 // per lane, a whole histogram per wave instruction, sixteen loads in flight).
 // Their sum is the row histogram, which fixes b*; the same registers then give
@@ -323,6 +323,99 @@ __global__ __launch_bounds__(NT) void topk_rowsel_kernel(const int32_t* __restri
     int t;
     const int pre = ech::block_excl_scan<NT>(n, scratch, &t);
     if (c < nch) {
+      if (wide) ws.take[(size_t)r * ws.nch + c] = n;
+      else ws.off[(size_t)r * ws.nch + c] = run + pre;
+    }
+    run += t;
+  }
+  if (threadIdx.x == 0 && !wide) st.nlist = run;
+}
+
+// T2 for calls with many rows (a prefill block: rows of at most a few dozen
+// chunks), 256 threads: thread b sums bin (255 - b) over the row's chunks,
+// eight independent loads in flight; four adjacent threads then share a
+// chunk for its count over bins >= b* (16 int4 loads each). Few registers, so
+// its workgroups fit beside the matrix-core kernel of the next block.
+__global__ __launch_bounds__(256) void topk_rowsel_many_kernel(const int32_t* __restrict__ lens, int k, Ws ws) {
+  constexpr int NT = 256;
+  constexpr int kParts = NT / 256;
+  const int r = blockIdx.x;
+  const int len = lens[r];
+  RowState& st = ws.rs[r];
+  if (len <= k) {
+    if (threadIdx.x == 0) {
+      st.mode = len == 0 ? kEmpty : kAll;
+      st.bstar = 0;
+      st.need = 0;
+      st.nlist = 0;
+      st.refine = 0;
+    }
+    return;
+  }
+  const int nch = (len + kChunk - 1) / kChunk;
+  __shared__ int part_sum[kParts][256];
+  __shared__ int scratch[NT / 64];
+  __shared__ int s_bstar, s_nbin;
+  const int b = threadIdx.x & 255, part = threadIdx.x >> 8;
+  const int bin = 255 - b;
+  const int* h = ws.hist + (size_t)r * ws.nch * 256 + bin;
+  int acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  int c = part;
+  for (; c + 7 * kParts < nch; c += 8 * kParts) {
+#pragma unroll
+    for (int u = 0; u < 8; ++u) acc[u] += h[(size_t)(c + kParts * u) * 256];
+  }
+  for (; c < nch; c += kParts) acc[0] += h[(size_t)c * 256];
+  part_sum[part][b] = acc[0] + acc[1] + acc[2] + acc[3] + acc[4] + acc[5] + acc[6] + acc[7];
+  __syncthreads();
+  // threads 0..255 hold bins 255..0 in order; the rest add zeros after them
+  int cnt = 0;
+  if (threadIdx.x < 256) {
+#pragma unroll
+    for (int pp = 0; pp < kParts; ++pp) cnt += part_sum[pp][b];
+  }
+  int tot;
+  const int above = ech::block_excl_scan<NT>(cnt, scratch, &tot);
+  if (threadIdx.x < 256 && above < k && above + cnt >= k) {
+    s_bstar = bin;
+    s_nbin = cnt;
+    st.bstar = bin;
+    st.need = k - above;
+  }
+  __syncthreads();
+  const int bstar = s_bstar;
+  const bool wide = s_nbin > ws.cap;
+  if (threadIdx.x == 0) {
+    st.mode = wide ? kWide : kNormal;
+    st.refine = 0;
+  }
+  // List offsets: chunk c holds the sum over bins >= b* of its histogram.
+  // Wide rows keep instead, per chunk, the count of bins > b* (in take), for
+  // the refinement. Four adjacent threads share a chunk (16 int4 loads each,
+  // all in flight).
+  const int tb = wide ? bstar + 1 : bstar;
+  int run = 0;
+  const int sub = threadIdx.x & 3;
+  for (int c0 = 0; c0 < nch; c0 += NT / 4) {
+    const int c = c0 + (int)threadIdx.x / 4;
+    int n = 0;
+    if (c < nch) {
+      const int4* hc = reinterpret_cast<const int4*>(ws.hist + ((size_t)r * ws.nch + c) * 256) + 16 * sub;
+      int4 q[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) q[i] = hc[i];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int b0 = 64 * sub + 4 * i;
+        n += (b0 >= tb ? q[i].x : 0) + (b0 + 1 >= tb ? q[i].y : 0) + (b0 + 2 >= tb ? q[i].z : 0) +
+             (b0 + 3 >= tb ? q[i].w : 0);
+      }
+    }
+    n += __shfl_xor(n, 1, 64);
+    n += __shfl_xor(n, 2, 64);
+    int t;
+    const int pre = ech::block_excl_scan<NT>(sub == 0 ? n : 0, scratch, &t);
+    if (c < nch && sub == 0) {
       if (wide) ws.take[(size_t)r * ws.nch + c] = n;
       else ws.off[(size_t)r * ws.nch + c] = run + pre;
     }
@@ -1116,7 +1209,7 @@ extern "C" int ech_topk(const float* logits, int64_t ld, const int32_t* row_len,
   if (few_rows)
     hipLaunchKernelGGL(topk_rowsel_kernel<1024>, dim3(R), dim3(1024), 0, s, row_len, k, w);
   else
-    hipLaunchKernelGGL(topk_rowsel_kernel<256>, dim3(R), dim3(256), 0, s, row_len, k, w);
+    hipLaunchKernelGGL(topk_rowsel_many_kernel, dim3(R), dim3(256), 0, s, row_len, k, w);
   ECH_LAUNCH_CHECK();
   if (!few_rows) {
     // many rows: refine rows with a lumped boundary in parallel over chunks
