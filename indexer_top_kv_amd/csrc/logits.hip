@@ -461,8 +461,20 @@ __global__ __launch_bounds__(kThreads) void logits_causal_kernel(
         for (int s = 0; s < 4; ++s)
           b[s] = as_bf16x8(*reinterpret_cast<const uint4*>(kr + 2 * dim0_of<ECH_KEY_BF16>(grp, s)));
         const float sc = st[cb][sub * 16 + col];
+        // Every row's MFMAs first, issued at raised wave priority; the
+        // epilogues at normal priority, so the other wave on the SIMD gets its
+        // MFMAs issued while this one runs VALU work (2-3% per block).
+        f32x4_t acc[RPW][4];
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_setprio(2);
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int j = 0; j < RPW; ++j) sres[wave * RPW + j][sub * 16 + col] = tile_score(a[j], wv[j], b, sc);
+        for (int j = 0; j < RPW; ++j) tile_mfma(a[j], b, acc[j]);
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_setprio(0);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int j = 0; j < RPW; ++j) sres[wave * RPW + j][sub * 16 + col] = tile_epilogue(acc[j], wv[j], sc);
       }
     }
     if (KDT == ECH_KEY_FP8 && more) stage_commit<KDT>(nxt, kt[cb ^ 1], st[cb ^ 1]);
