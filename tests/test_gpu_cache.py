@@ -304,3 +304,36 @@ def test_prefill_large_union_many_windows():
         np.testing.assert_array_equal(sel_g, sel_o)
         np.testing.assert_array_equal(st_g, st_o)
         gc.compare(sm)
+
+
+def test_early_cap_zero_and_an_empty_sequence():
+    """EARLY with cap 0 only pins (no misses, no allocation), then FINAL, with
+    an empty sequence in the batch; maps, head and stats as the oracle's."""
+    need_gpu()
+    B, k, cap = 3, 512, 0
+    lens = np.array([5000, 0, 3001], np.int32)
+    tok0 = np.array([0, 5000, 5000], np.int64)
+    P, C, ld = 8001, 2000, 5000
+    gc = GpuCache(P, C, B, k, ld, cap=cap)
+    sm = oracle.SlotMap(P, C)
+    base = _scores(20, B, ld, 0)
+    theta = np.full(B, np.nan, np.float32)
+    for step in range(3):
+        scores = (base + 0.4 * _scores(20, B, ld, step + 1)).astype(np.float32)
+        a_g, st_g = gc.early(tok0, lens, scores, theta)
+        a_o, st_o = sm.early(tok0, [scores[b, :lens[b]] for b in range(B)], theta, cap)
+        assert a_g == a_o == [], ('early', step)
+        np.testing.assert_array_equal(st_g, st_o)
+        gc.compare(sm)
+        idx = np.full((B, k), -1, np.int64)
+        kth = np.full(B, np.nan, np.float32)
+        for b in range(B):
+            if lens[b]:
+                idx[b], kth[b] = oracle.topk_row(scores[b, :lens[b]], k)
+        a_g, sel_g, st_g = gc.final(tok0, lens, idx)
+        a_o, sel_o, st_o = sm.final(tok0, idx)
+        assert a_g == a_o, ('final', step)
+        np.testing.assert_array_equal(sel_g, sel_o)
+        np.testing.assert_array_equal(st_g, st_o)
+        gc.compare(sm)
+        theta = oracle.theta_rows(theta, kth)
