@@ -52,6 +52,10 @@ def parse():
     p.add_argument('--cpu-steps', type=int, default=5, help='decode steps in the oracle sample')
     p.add_argument('--topk-first', choices=['auto', 'on', 'off'], default='auto',
                    help='decode: launch the top-k before the EARLY maps (auto: batches of at most 8 sequences)')
+    p.add_argument('--layers', type=int, default=1,
+                   help='decode: layers per step, each with its own keys, slot maps, cache and host pool')
+    p.add_argument('--micro-batches', type=int, default=1,
+                   help='decode with --layers: micro-batches, interleaved so one recalls while another scores')
     p.add_argument('--calibrate-copy', action='store_true',
                    help='only run a plain 1 GiB device copy 5 times (reference for HBM byte counters)')
     return p.parse_args()
@@ -225,6 +229,81 @@ def bench_decode(args, wl):
                               'the top-k (EARLY) and beside the EARLY recall (FINAL)'},
     }
     return out, dict(wl=wl, pool=pool, qs=qs, w=w, keys=keys, scale=scale)
+
+
+def bench_stack(args, wl):
+    """Decode steps over `--layers` layers in `--micro-batches` micro-batches
+    (DecodeStack): every (layer, micro-batch) has its own slot map and a
+    1/M share of the layer's device cache; each layer its own keys, scales,
+    head weights, queries and host pool (seeded per layer). Times graph
+    replays of the whole L-layer step."""
+    import numpy as np
+    import torch
+    import workloads as wk
+    from indexer_top_kv_amd.pipeline import DecodeLayer, DecodeStack, sequence_groups
+
+    dev = lambda x: torch.from_numpy(np.ascontiguousarray(x.view(np.int16) if x.dtype == np.uint16 else x)).cuda()
+    L, M = args.layers, args.micro_batches
+    groups = sequence_groups(wl.B, M)
+    C_m = wl.C // len(groups)
+    total_steps = args.warmup + args.steps
+    layers, qs, pools = [], [], []
+    for l in range(L):
+        t = time.time()
+        wll = wl.scaled(layer=l)
+        keys, scale = wk.keys(wll)
+        pool = torch.empty((wll.P, wk.ROW_ELEMS), dtype=torch.int16, pin_memory=True)
+        wk.host_rows(wll, out=pool.numpy().view(np.uint16))
+        kc, ks, wd = dev(keys), (dev(scale) if scale is not None else None), dev(wk.head_weights(wll))
+        del keys, scale
+        layers.append([DecodeLayer(kc, ks, wd[b0:b1], wll.tok0[b0:b1], wll.lens[b0:b1], C_m, k=wll.k,
+                                   cap=wll.cap, host_pool=pool) for b0, b1 in groups])
+        qs.append(dev(np.stack(list(wk.decode_queries(wll, total_steps)))))
+        pools.append(pool)
+        log(f'layer {l}: keys, {wll.P} host rows and queries in {time.time() - t:.1f}s')
+    stack = DecodeStack(layers)
+    step_q = lambda s: [[qs[l][s, b0:b1] for b0, b1 in groups] for l in range(L)]
+    for s in range(args.warmup):
+        stack.step(step_q(s))
+    torch.cuda.synchronize()
+    if not args.eager:
+        stack.capture()
+    torch.cuda.synchronize()
+    rec0 = sum(int(d.state.ctr[4].item()) for r in layers for d in r)
+    launch = ('eager launches' if args.eager
+              else 'per (layer, micro-batch): scores kernel + hipGraph replay of the rest of its step')
+    log(f'timing {args.steps} steps of {L} layers x {len(groups)} micro-batches ({launch})')
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        (stack.step if args.eager else stack.replay)(step_q(args.warmup + s))
+    t_host = time.perf_counter() - t0                  # host time to enqueue the K steps
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    recalled = sum(int(d.state.ctr[4].item()) for r in layers for d in r) - rec0
+    tokens = int(wl.lens.astype(np.int64).sum())
+    step_ms = wall / args.steps * 1e3
+    rec_bytes = recalled * 1152 / args.steps
+    return {
+        'metric': f'decode tokens scored/s over a {L}-layer step (indexer logits + exact top-k + early/final '
+                  f'slot-map step + recall per layer)',
+        'value': tokens * L * args.steps / wall,
+        'unit': 'tokens/s',
+        'n_gpus': 1, 'steps': args.steps, 'warmup': args.warmup,
+        'ms_per_step': step_ms,
+        'higher_is_better': True, 'scaling': 'weak', 'vs_baseline': None,
+        'dtype': 'fp8-e4m3 keys, bf16 q, bf16 MFMA with fp32 accumulation' if wl.kdtype == 'fp8' else 'bf16',
+        'data': 'synthetic, seeded per layer',
+        'config': {'workload': wl.name, 'layers': L, 'micro_batches': len(groups),
+                   'micro_batch_sequences': [b1 - b0 for b0, b1 in groups], 'cache_slots_per_micro_batch': C_m,
+                   'B': wl.B, 'context': wl.N, 'k': wl.k, 'early_fetch_cap': wl.cap,
+                   'launch': launch},
+        'us_per_layer': step_ms * 1e3 / L,
+        'host_enqueue_ms_per_step': t_host / args.steps * 1e3,
+        'recall': {'rows_per_step': recalled / args.steps, 'bytes_per_step': rec_bytes,
+                   'GBs_over_step': rec_bytes / (step_ms * 1e-3) / 1e9},
+        'roofline': None,
+        'cpu_baseline': None,
+    }, pools
 
 
 def pcie_check(pool, C, rows=16384, reps=5):
@@ -418,7 +497,11 @@ def main():
         return
     wl = wk.CONFIGS[args.config]
     log(f'{wl.name} on {torch.cuda.get_device_name(0)}')
-    if wl.mode == 'decode':
+    if wl.mode == 'decode' and (args.layers > 1 or args.micro_batches > 1):
+        out, pools = bench_stack(args, wl)
+        out['pcie'] = pcie_check(pools[0], wl.C)
+        out['recall']['frac_of_memcpy'] = out['recall']['GBs_over_step'] / out['pcie']['h2d_memcpy_GBs']
+    elif wl.mode == 'decode':
         out, ctx = bench_decode(args, wl)
         out['pcie'] = pcie_check(ctx['pool'], wl.C)
         r = out['stage_rooflines']['recall']

@@ -24,6 +24,10 @@ selections do not fit the cache at once (sum of min(k, len_b) > C),
 sequences are processed in host-computed chunks, each an ECH_EARLY phase
 then a FINAL phase; every selected token is resident at the end of its chunk.
 
+Several layers (DecodeStack): one DecodeLayer per (layer, micro-batch), the
+layers of a micro-batch in order, two micro-batches interleaved so that one
+crosses PCIe while the other scores.
+
 Prefill (ECHO explainer, "Prefill: one-round histogram"): query blocks are
 scored one after another; the recall of block i runs on S1 while S0 scores
 block i+1.
@@ -160,15 +164,22 @@ class DecodeLayer:
         ech_index_logits(q, self.w, self.kcache, self.kscale, self.tok0, self.lens, self.max_len, self.logits,
                          stream=stream)
 
-    def step(self, q: torch.Tensor, marks: Optional[dict] = None) -> None:
+    def step(self, q: Optional[torch.Tensor], marks: Optional[dict] = None,
+             wait: Optional[torch.cuda.Event] = None, logits_done: Optional[torch.cuda.Event] = None,
+             scores: bool = True) -> None:
         """Enqueue one decode step for query q [B, 64, 128] (bf16 bits) on the
         current stream (with S1 forked and joined inside). `marks`, when given,
         receives timing events recorded on the stream of each stage, as
         (start, end) pairs: logits, topk, final (S0: FINAL maps to the end of
         the step), early (S1: EARLY maps and recall of the first chunk), and
         early_maps, recall_early, final_maps, recall_final (one pair per
-        chunk)."""
+        chunk). `wait`, when given, is an event the scores wait for;
+        `logits_done` is recorded once they are written (one group only).
+        scores=False leaves the scores out: the caller has launched them on
+        the current stream already (q is then unused)."""
         s0 = torch.cuda.current_stream()
+        if wait is not None:
+            s0.wait_event(wait)
 
         def mark(name, stream):
             if marks is None:
@@ -180,12 +191,17 @@ class DecodeLayer:
 
         th, th_next = self.theta[self.parity], self.theta[1 - self.parity]
         if self.groups:
+            if logits_done is not None or not scores:
+                raise ValueError('logits_done and scores=False need the early fetch in one group')
             self._step_grouped(q, th, th_next, s0, mark)
             self.parity ^= 1
             return
-        mark('logits', s0)
-        self.logits_only(q, stream=s0)
-        mark('logits', s0)
+        if scores:
+            mark('logits', s0)
+            self.logits_only(q, stream=s0)
+            mark('logits', s0)
+        if logits_done is not None:
+            logits_done.record(s0)
         first_b0, first_b1 = self.chunks[0]
         if self.early:
             self.ev_logits.record(s0)
@@ -300,22 +316,35 @@ class DecodeLayer:
     def theta_current(self) -> torch.Tensor:
         return self.theta[self.parity]
 
-    def capture(self) -> None:
+    def capture(self, scores: bool = True) -> None:
         """Capture one decode step per threshold parity as a hipGraph that
         reads q from a static buffer (every tensor of the step has a fixed
-        size and address, so the step replays unchanged). Nothing runs."""
+        size and address, so the step replays unchanged). Nothing runs.
+        scores=False captures the step after the scores (replay_after_scores)."""
         self.q_static = torch.zeros((self.B, 64, 128), dtype=torch.int16, device=self.logits.device)
         self.graphs = [None, None]
+        self.graph_scores = scores
         for _ in range(2):
             p = self.parity
             g = torch.cuda.CUDAGraph()
             with torch.cuda.graph(g):
-                self.step(self.q_static)      # flips self.parity
+                self.step(self.q_static if scores else None, scores=scores)      # flips self.parity
             self.graphs[p] = g
 
     def replay(self, q: torch.Tensor) -> None:
         """One decode step through the captured graphs (on the current stream)."""
+        if not self.graph_scores:
+            raise ValueError('captured without the scores: use replay_after_scores')
         self.q_static.copy_(q, non_blocking=True)
+        self.graphs[self.parity].replay()
+        self.parity ^= 1
+
+    def replay_after_scores(self) -> None:
+        """The rest of a decode step through graphs captured with
+        scores=False, after the caller's ech_index_logits on the current
+        stream."""
+        if self.graph_scores:
+            raise ValueError('captured with the scores: use replay')
         self.graphs[self.parity].replay()
         self.parity ^= 1
 
@@ -447,3 +476,99 @@ class PrefillLayer:
         s0.wait_event(self.ev_recall)
         if self.overlap:
             s0.wait_stream(self.s1)
+
+
+class DecodeStack:
+    """One decode step over L layers for M micro-batches of the batch.
+
+    Each (layer, micro-batch) pair is a DecodeLayer of its own: its slot map
+    and device cache (the layer's cache split between the micro-batches),
+    reading the layer's indexer keys and host pool at its sequences' token
+    offsets. The cache is per layer because each layer's indexer selects its
+    own tokens (ECHO explainer, "One layer, one step").
+
+    Within a micro-batch the layers run in order: layer l+1 scores only after
+    layer l's recall, because in the model the attention over the recalled
+    rows stands between them and yields the next layer's query. The
+    micro-batches are independent chains on streams of their own, started
+    one score launch apart, so while one micro-batch's rows cross PCIe the
+    other one scores:
+
+        mb0: logits L0 | maps, recall L0 ............ | logits L1 | ...
+        mb1:           | logits L0 | maps, recall L0 ............ | logits L1
+
+    The queries of every layer are inputs of the step (no attention or MLP is
+    computed between layers): qs[l][m] is DecodeLayer l, m's [B_m, 64, 128].
+    """
+
+    def __init__(self, layers: List[List[DecodeLayer]], device='cuda'):
+        self.layers = [list(r) for r in layers]
+        self.L, self.M = len(self.layers), (len(self.layers[0]) if self.layers else 0)
+        if self.L == 0 or self.M == 0 or any(len(r) != self.M for r in self.layers):
+            raise ValueError('layers must be a non-empty L x M list of DecodeLayer')
+        if any(d.groups for r in self.layers for d in r):
+            raise ValueError('the early fetch in sequence groups is not supported in a stack')
+        # Two streams per micro-batch (scores and its chain; EARLY branch),
+        # shared by its layers; micro-batch 0's chain is the caller's stream.
+        # With two micro-batches these are four streams, one per hardware
+        # queue at the runtime's default of four, so neither micro-batch
+        # waits behind the other's work in a shared queue.
+        self.streams = [None] + [torch.cuda.Stream(device=device) for _ in range(self.M - 1)]
+        self.side = [torch.cuda.Stream(device=device) for _ in range(self.M)]
+        for r in self.layers:
+            for m, d in enumerate(r):
+                d.s1 = self.side[m]
+        self.ev_start = torch.cuda.Event()
+        self.ev_end = [torch.cuda.Event() for _ in range(self.M)]
+        self.ev_logits = [[torch.cuda.Event() for _ in range(self.M)]]
+
+    def step(self, qs) -> None:
+        """Enqueue one L-layer step on the current stream (micro-batch streams
+        forked and joined inside)."""
+        self._run(qs, graphs=False)
+
+    def _run(self, qs, graphs: bool) -> None:
+        # Per layer, every micro-batch's scores are enqueued before the rest
+        # of any micro-batch's step, so each cross-stream wait is enqueued
+        # right behind the event it waits for (the runtime can otherwise
+        # resolve a wait only once later work on the recording stream has
+        # been submitted and finished). Micro-batch m > 0 starts its first
+        # scores after those of m - 1; from then on the chains run free, one
+        # score launch apart.
+        s = torch.cuda.current_stream()
+        chain = [s] + self.streams[1:]          # micro-batch 0 runs on the caller's stream
+        self.ev_start.record(s)
+        for st in chain[1:]:
+            st.wait_event(self.ev_start)
+        for l in range(self.L):
+            for m in range(self.M):
+                st, d = chain[m], self.layers[l][m]
+                if l == 0 and m > 0:
+                    st.wait_event(self.ev_logits[0][m - 1])
+                d.logits_only(qs[l][m], stream=st)
+                if l == 0:
+                    self.ev_logits[0][m].record(st)
+            for m in range(self.M):
+                with torch.cuda.stream(chain[m]):
+                    if graphs:
+                        self.layers[l][m].replay_after_scores()
+                    else:
+                        self.layers[l][m].step(None, scores=False)
+        for m in range(1, self.M):
+            self.ev_end[m].record(chain[m])
+            s.wait_event(self.ev_end[m])
+
+    def capture(self) -> None:
+        """Capture, for every (layer, micro-batch), its step after the scores
+        as hipGraphs (one per threshold parity). Nothing runs. A replay then
+        launches each pair's scores kernel and its graph on the micro-batch's
+        stream, in the order and with the events of step()."""
+        if len({d.parity for r in self.layers for d in r}) != 1:
+            raise ValueError('every layer must be at the same threshold parity')
+        for r in self.layers:
+            for d in r:
+                d.capture(scores=False)
+
+    def replay(self, qs) -> None:
+        """One L-layer step through the captured graphs (current stream)."""
+        self._run(qs, graphs=True)

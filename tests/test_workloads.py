@@ -86,3 +86,18 @@ def test_prefill_blocks_consistent():
     np.testing.assert_array_equal(whole[200:500], part)
     w = wk.head_weights(wl)
     np.testing.assert_array_equal(w[200:500], wk.head_weights(wl, rows=300, row0=200))
+
+
+def test_layers_share_lengths_and_draw_their_own_values():
+    base = wk.CONFIGS['decode-64x110k-fp8-capacity'].scaled(B=3, N=3000, len_lo=1000)
+    l0, l1, l2 = base, base.scaled(layer=1), base.scaled(layer=2)
+    np.testing.assert_array_equal(l0.lens, l1.lens)
+    np.testing.assert_array_equal(l0.tok0, l2.tok0)
+    k0, s0 = wk.keys(l0)
+    k1, s1 = wk.keys(l1)
+    k0b, _ = wk.keys(base.scaled(layer=0))
+    np.testing.assert_array_equal(k0, k0b)              # layer 0 keeps the plain seeds
+    assert not np.array_equal(k0, k1) and not np.array_equal(s0, s1)
+    assert not np.array_equal(wk.head_weights(l0), wk.head_weights(l1))
+    assert not np.array_equal(next(wk.decode_queries(l1, 1)), next(wk.decode_queries(l2, 1)))
+    assert not np.array_equal(wk.host_rows(l0)[:4], wk.host_rows(l1)[:4])

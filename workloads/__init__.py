@@ -18,7 +18,8 @@ Seeds: every array is drawn from ``numpy.random.default_rng([20261202, cfg,
 stream, *extra])``; streams are 0 keys, 1 key scales, 2 q0, 3 q innovations,
 4 head weights, 5 host rows, 6 lengths, 7 topic-shift draws. Large arrays are
 drawn in fixed-size chunks, each with its own seed, so results do not depend on
-thread count.
+thread count. Layer l > 0 of a workload appends 1000000 + l to the seed of
+every draw except the lengths, which all layers share.
 
 Casts to bf16 and to OCP e4m3fn use torch's round-to-nearest-even conversions
 (``torch.bfloat16``, ``torch.float8_e4m3fn``); fp8 inputs are clamped to
@@ -47,6 +48,15 @@ CHUNK_ROWS = 1 << 20  # rows per independently seeded chunk
 
 def rng(cfg: int, stream: int, *extra: int) -> np.random.Generator:
     return np.random.default_rng([SEED_ROOT, cfg, stream, *extra])
+
+
+def wl_rng(wl: 'Workload', stream: int, *extra: int) -> np.random.Generator:
+    """The generator of one draw of a workload's layer: layer 0 uses the plain
+    seed, layer l > 0 appends 1000000 + l (lengths are not drawn here: every
+    layer shares them)."""
+    if wl.layer == 0:
+        return rng(wl.cfg, stream, *extra)
+    return rng(wl.cfg, stream, *extra, 1000000 + wl.layer)
 
 
 def _threads() -> int:
@@ -91,6 +101,7 @@ class Workload:
     len_lo: Optional[int] = None   # lengths ~ U{len_lo..N} when set
     block_rows: int = 4096   # prefill query block
     variant: str = 'normal'  # 'normal' | 'dyadic'
+    layer: int = 0           # model layer: its own keys, scales, weights, queries and rows
 
     # ---- derived sizes
     @property
@@ -177,7 +188,7 @@ def keys(wl: Workload) -> tuple[np.ndarray, Optional[np.ndarray]]:
         out = np.empty((P, D), dtype=np.uint16)
 
         def f(c, lo, hi):
-            r = rng(wl.cfg, S_KEYS, c)
+            r = wl_rng(wl, S_KEYS, c)
             if dyadic:
                 x = r.integers(-8, 9, size=(hi - lo, D)).astype(np.float32)
             else:
@@ -187,14 +198,14 @@ def keys(wl: Workload) -> tuple[np.ndarray, Optional[np.ndarray]]:
     out = np.empty((P, D), dtype=np.uint8)
 
     def f8(c, lo, hi):
-        r = rng(wl.cfg, S_KEYS, c)
+        r = wl_rng(wl, S_KEYS, c)
         if dyadic:
             x = r.integers(-8, 9, size=(hi - lo, D)).astype(np.float32)
         else:
             x = r.standard_normal((hi - lo, D), dtype=np.float32)
         return to_e4m3_bits(x)
     _chunked(P, f8, out)
-    r = rng(wl.cfg, S_SCALE)
+    r = wl_rng(wl, S_SCALE)
     if dyadic:
         scale = np.array([0.5, 1.0, 2.0], dtype=np.float32)[r.integers(0, 3, size=P)]
     else:
@@ -206,7 +217,7 @@ def head_weights(wl: Workload, rows: Optional[int] = None, row0: int = 0) -> np.
     """Head weights w_h ~ U(0,1)/8 as fp32, one vector per decode sequence
     (fixed over steps) or per prefill query row. Dyadic: m/64, m in 0..8."""
     if wl.mode == 'decode':
-        r = rng(wl.cfg, S_W)
+        r = wl_rng(wl, S_W)
         if wl.variant == 'dyadic':
             return (r.integers(0, 9, size=(wl.B, H)) / 64.0).astype(np.float32)
         return (r.uniform(0.0, 1.0, size=(wl.B, H)) / 8.0).astype(np.float32)
@@ -216,7 +227,7 @@ def head_weights(wl: Workload, rows: Optional[int] = None, row0: int = 0) -> np.
     for blk in range(row0 // wl.block_rows, (row0 + rows + wl.block_rows - 1) // wl.block_rows):
         lo = blk * wl.block_rows
         hi = min(wl.N, lo + wl.block_rows)
-        r = rng(wl.cfg, S_W, blk)
+        r = wl_rng(wl, S_W, blk)
         if wl.variant == 'dyadic':
             wb = (r.integers(0, 9, size=(hi - lo, H)) / 64.0).astype(np.float32)
         else:
@@ -237,7 +248,7 @@ def decode_queries(wl: Workload, steps: Optional[int] = None) -> Iterator[np.nda
     """
     steps = wl.steps if steps is None else steps
     shape = (wl.B, H, D)
-    r0 = rng(wl.cfg, S_Q0)
+    r0 = wl_rng(wl, S_Q0)
     dyadic = wl.variant == 'dyadic'
     if dyadic:
         state = r0.integers(-3, 4, size=shape).astype(np.float32)
@@ -245,8 +256,8 @@ def decode_queries(wl: Workload, steps: Optional[int] = None) -> Iterator[np.nda
         state = r0.standard_normal(shape, dtype=np.float32)
     for s in range(steps):
         yield to_bf16_bits(state)
-        ri = rng(wl.cfg, S_QINNOV, s)
-        rs = rng(wl.cfg, S_SHIFT, s)
+        ri = wl_rng(wl, S_QINNOV, s)
+        rs = wl_rng(wl, S_SHIFT, s)
         if dyadic:
             fresh = ri.integers(-3, 4, size=shape).astype(np.float32)
             redraw = ri.random(shape) < (1.0 - wl.rho)
@@ -272,7 +283,7 @@ def prefill_queries(wl: Workload, row0: int, rows: int) -> np.ndarray:
     for blk in range(row0 // wl.block_rows, (row0 + rows + wl.block_rows - 1) // wl.block_rows):
         lo = blk * wl.block_rows
         hi = min(wl.N, lo + wl.block_rows)
-        r = rng(wl.cfg, S_Q0, blk)
+        r = wl_rng(wl, S_Q0, blk)
         if wl.variant == 'dyadic':
             x = r.integers(-3, 4, size=(hi - lo, H, D)).astype(np.float32)
         else:
@@ -291,7 +302,7 @@ def host_rows(wl: Workload, out: Optional[np.ndarray] = None) -> np.ndarray:
     assert out.shape == (P, ROW_ELEMS) and out.dtype == np.uint16
 
     def f(c, lo, hi):
-        r = rng(wl.cfg, S_ROWS, c)
+        r = wl_rng(wl, S_ROWS, c)
         return to_bf16_bits(r.standard_normal((hi - lo, ROW_ELEMS), dtype=np.float32))
     return _chunked(P, f, out)
 
