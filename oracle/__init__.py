@@ -14,6 +14,8 @@ against the pages:
 - ``select``    - exact top-k by full stable sort; EMA threshold.
 - ``slotmap``   - sequential per-layer slot-map simulator (free -> allocate ->
                   recall, no write-back) and the recall byte copy.
+- ``attention`` - softmax attention of each head over the rows its sequence
+                  selects through sel_slot (the consumer of the path).
 
 Sources: the ECHO explainer page ("One layer, one step: free -> allocate ->
 recall", "Decode: fetch above a predicted threshold", "Prefill: one-round
@@ -25,8 +27,9 @@ Every function is pinned by ``tests/test_oracle_*.py`` against closed forms,
 brute force on tiny inputs, library routines and invariants; none is marked
 "parity unpinned".
 """
-from . import numerics, indexer, select, slotmap  # noqa: F401
+from . import numerics, indexer, select, slotmap, attention  # noqa: F401
 from .numerics import bf16_to_f64, e4m3fn_to_f64, e4m3fn_table  # noqa: F401
 from .indexer import index_logits, index_logit_at, dequant_keys  # noqa: F401
 from .select import topk_row, topk_rows, theta_next, theta_rows  # noqa: F401
 from .slotmap import SlotMap, recall_rows  # noqa: F401
+from .attention import sparse_attention  # noqa: F401

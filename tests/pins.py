@@ -378,3 +378,101 @@ def pin_slotmap_invariants(SlotMap):
 
 SLOTMAP_PINS = [pin_slotmap_trace, pin_slotmap_early, pin_slotmap_large_cache, pin_slotmap_exact_cache,
                 pin_slotmap_fifo, pin_slotmap_prefill_first_touch, pin_slotmap_invariants]
+
+
+# ------------------------------------------------------------------ sparse attention
+
+def _attn_case(seed, B=2, H=4, C=50, k=12, pad=3):
+    import workloads as wk
+    r = np.random.default_rng(seed)
+    q = wk.to_bf16_bits(r.standard_normal((B, H, 576)).astype(np.float32))
+    cache = wk.to_bf16_bits(r.standard_normal((C, 576)).astype(np.float32))
+    sel = np.stack([r.choice(C, k, replace=False) for _ in range(B)]).astype(np.int32)
+    sel[:, k - pad:] = -1                       # padding at the end (short sequences)
+    sel[0, 1] = C + 7                           # out of range: selects nothing
+    return q, cache, sel
+
+
+def pin_attn_library(sparse_attention):
+    """Against torch's scaled_dot_product_attention in float64 on the CPU,
+    over the valid slots gathered by hand (keys = the 576-value rows, values
+    = their first 512), and torch.logsumexp for the denominator."""
+    import torch
+    from oracle.numerics import bf16_to_f64
+    for seed in range(3):
+        q, cache, sel = _attn_case(seed)
+        scale = 0.0721
+        out, lse = sparse_attention(q, cache, sel, scale)
+        for b in range(q.shape[0]):
+            ok = [s for s in sel[b] if 0 <= s < cache.shape[0]]
+            rows = torch.from_numpy(bf16_to_f64(cache[ok]))
+            qq = torch.from_numpy(bf16_to_f64(q[b]))
+            sc = float(np.float32(scale))
+            ref = torch.nn.functional.scaled_dot_product_attention(qq[None], rows[None], rows[None, :, :512],
+                                                                   scale=sc)[0]
+            np.testing.assert_allclose(out[b], ref.numpy(), rtol=1e-10, atol=1e-12)
+            np.testing.assert_allclose(lse[b], torch.logsumexp(qq @ rows.T * sc, dim=1).numpy(), rtol=1e-12)
+
+
+def pin_attn_closed_forms(sparse_attention):
+    r = np.random.default_rng(7)
+    import workloads as wk
+    from oracle.numerics import bf16_to_f64
+    C = 9
+    cache = wk.to_bf16_bits(r.standard_normal((C, 576)).astype(np.float32))
+    q = wk.to_bf16_bits(r.standard_normal((1, 3, 576)).astype(np.float32))
+    row = bf16_to_f64(cache)
+    # every selected slot holds the same row: the weights sum to one
+    same = cache.copy()
+    same[:] = cache[4]
+    out, lse = sparse_attention(q, same, np.array([[0, 2, 5, -1, 8]]), 0.05)
+    np.testing.assert_allclose(out[0], np.broadcast_to(row[4, :512], (3, 512)), rtol=1e-13, atol=1e-14)
+    s = bf16_to_f64(q[0]) @ row[4] * float(np.float32(0.05))
+    np.testing.assert_allclose(lse[0], s + np.log(4.0), rtol=1e-12)
+    # a zero query weighs every selected row equally
+    out, lse = sparse_attention(np.zeros_like(q), cache, np.array([[1, 3, 6]]), 0.3)
+    np.testing.assert_allclose(out[0], np.broadcast_to(row[[1, 3, 6], :512].mean(0), (3, 512)), rtol=1e-12,
+                               atol=1e-14)
+    np.testing.assert_allclose(lse[0], np.log(3.0), rtol=1e-14)
+    # one valid slot: its value row, unchanged
+    out, lse = sparse_attention(q, cache, np.array([[-1, 7, C, -5]]), 1.0)
+    np.testing.assert_array_equal(out[0], np.broadcast_to(row[7, :512], (3, 512)))
+    np.testing.assert_allclose(lse[0], bf16_to_f64(q[0]) @ row[7], rtol=1e-12)
+    # nothing selected
+    out, lse = sparse_attention(q, cache, np.array([[-1, -1, C]]), 1.0)
+    assert np.all(out == 0) and np.all(np.isneginf(lse))
+
+
+def pin_attn_bruteforce(sparse_attention):
+    """Pure-Python loops with math.exp, one head and token at a time."""
+    import math
+    from oracle.numerics import bf16_to_f64
+    q, cache, sel = _attn_case(11, B=1, H=2, C=10, k=5, pad=1)
+    scale = 0.11
+    out, lse = sparse_attention(q, cache, sel, scale)
+    sc = float(np.float32(scale))
+    rows = bf16_to_f64(cache)
+    qq = bf16_to_f64(q[0])
+    for h in range(2):
+        sc_list = []
+        for s in sel[0]:
+            if 0 <= s < 10:
+                sc_list.append((sum(qq[h, d] * rows[s, d] for d in range(576)) * sc, s))
+        mx = max(v for v, _ in sc_list)
+        den = sum(math.exp(v - mx) for v, _ in sc_list)
+        for c in (0, 1, 255, 511):
+            num = sum(math.exp(v - mx) * rows[s, c] for v, s in sc_list)
+            assert abs(out[0, h, c] - num / den) <= 1e-12 * max(1.0, abs(num / den))
+        assert abs(lse[0, h] - (mx + math.log(den))) <= 1e-12 * abs(mx + math.log(den))
+
+
+def pin_attn_permutation(sparse_attention):
+    q, cache, sel = _attn_case(5, B=1, k=20, pad=0)
+    out, lse = sparse_attention(q, cache, sel, 0.07)
+    perm = np.random.default_rng(1).permutation(20)
+    out2, lse2 = sparse_attention(q, cache, sel[:, perm], 0.07)
+    np.testing.assert_allclose(out2, out, rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(lse2, lse, rtol=1e-13)
+
+
+ATTN_PINS = [pin_attn_library, pin_attn_closed_forms, pin_attn_bruteforce, pin_attn_permutation]

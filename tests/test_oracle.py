@@ -81,3 +81,8 @@ def test_final_overflow_is_error():
     sm = oracle.SlotMap(10, 2)
     with pytest.raises(RuntimeError):
         sm.final([0], np.array([[0, 1, 2]], np.int64))
+
+
+@pytest.mark.parametrize('pin', pins.ATTN_PINS, ids=lambda f: f.__name__)
+def test_attention_pins(pin):
+    pin(oracle.sparse_attention)

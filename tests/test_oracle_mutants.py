@@ -272,3 +272,68 @@ def test_unmutated_oracle_passes_all():
     assert not _fails(pins.TOPK_PINS, oracle.topk_row)
     assert not _fails([pins.pin_theta], oracle.theta_next)
     assert not _fails(pins.SLOTMAP_PINS, oracle.SlotMap)
+
+
+# ------------------------------------------------------------------ sparse attention
+
+def _attn_with(core):
+    """An attention oracle whose per-sequence core (q [H,576], rows [n,576],
+    scale) -> (out, lse) is replaced; slot filtering as in the oracle unless
+    the core takes the raw slot list."""
+    def f(q_bits, cache_bits, sel_slot, sm_scale):
+        B, H, _ = q_bits.shape
+        out = np.zeros((B, H, 512))
+        lse = np.full((B, H), -np.inf)
+        C = cache_bits.shape[0]
+        for b in range(B):
+            sl = np.asarray(sel_slot[b], np.int64)
+            sl = core.get('filter', lambda s: s[(s >= 0) & (s < C)])(sl)
+            if len(sl) == 0:
+                continue
+            o, l = core['fn'](bf16_to_f64(q_bits[b]), bf16_to_f64(cache_bits[sl]), float(np.float32(sm_scale)))
+            out[b], lse[b] = o, l
+        return out, lse
+    return f
+
+
+def _softmax_core(s, v):
+    m = s.max(axis=1, keepdims=True)
+    p = np.exp(s - m)
+    den = p.sum(axis=1, keepdims=True)
+    return (p @ v) / den, (m + np.log(den))[:, 0]
+
+
+ATTN_MUTANTS = {
+    'no_scale': dict(fn=lambda q, r, sc: _softmax_core(q @ r.T, r[:, :512])),
+    'value_is_rope_end': dict(fn=lambda q, r, sc: _softmax_core(q @ r.T * sc, r[:, 64:])),
+    'key_without_rope': dict(fn=lambda q, r, sc: _softmax_core(q[:, :512] @ r[:, :512].T * sc, r[:, :512])),
+    'softmax_over_heads': dict(fn=lambda q, r, sc: (
+        (np.exp(q @ r.T * sc - (q @ r.T * sc).max(0)) / np.exp(q @ r.T * sc - (q @ r.T * sc).max(0)).sum(0)) @ r[:, :512],
+        np.log(np.exp(q @ r.T * sc).sum(1)))),
+    'lse_log2': dict(fn=lambda q, r, sc: (_softmax_core(q @ r.T * sc, r[:, :512])[0],
+                                          _softmax_core(q @ r.T * sc, r[:, :512])[1] / np.log(2.0))),
+    'unnormalised': dict(fn=lambda q, r, sc: (np.exp(q @ r.T * sc - (q @ r.T * sc).max(1, keepdims=True)) @ r[:, :512],
+                                              _softmax_core(q @ r.T * sc, r[:, :512])[1])),
+    'negative_slot_wraps': dict(filter=lambda s: s[s < 10 ** 9], fn=lambda q, r, sc: _softmax_core(q @ r.T * sc,
+                                                                                               r[:, :512])),
+    'last_slot_dropped': dict(filter=lambda s: s[(s >= 0) & (s < s.max())] if len(s) else s,
+                              fn=lambda q, r, sc: _softmax_core(q @ r.T * sc, r[:, :512])),
+}
+
+
+def _attn_negative_slot_wraps(q_bits, cache_bits, sel_slot, sm_scale):
+    # -1 indexes the last slot (numpy negative indexing) instead of selecting nothing
+    return _attn_with(ATTN_MUTANTS['negative_slot_wraps'])(q_bits, cache_bits,
+                                                           np.where(np.asarray(sel_slot) >= cache_bits.shape[0], -1,
+                                                                    sel_slot), sm_scale)
+
+
+@pytest.mark.parametrize('name', list(ATTN_MUTANTS))
+def test_attention_mutants_are_caught(name):
+    impl = (_attn_negative_slot_wraps if name == 'negative_slot_wraps' else _attn_with(ATTN_MUTANTS[name]))
+    assert _fails(pins.ATTN_PINS, impl), name
+
+
+def test_attention_unmutated_core_passes():
+    for p in pins.ATTN_PINS:
+        p(_attn_with(dict(fn=lambda q, r, sc: _softmax_core(q @ r.T * sc, r[:, :512]))))
