@@ -18,6 +18,8 @@
  *      PREFILL: FINAL over the union of a query block's selections.
  *   4. ech_recall: copy the missed KV rows from pinned host memory into their
  *      device-cache slots.
+ *   5. ech_sparse_attn (the consumer): attention of each head over the rows
+ *      its sequence selects, through sel_slot.
  *
  * Conventions
  *  - Ownership: the caller owns every buffer (device memory, the pinned host
@@ -285,6 +287,32 @@ int ech_early_group(int group, int b0, int b1, const float* logits, int64_t ld, 
 int ech_recall_group(int group, const void* host_pool, int64_t P, int64_t row_bytes, void* dev_cache,
                      int32_t C, const int32_t* miss_early, int32_t M_early, int32_t* ctr, const void* ws,
                      void* stream);
+
+/*
+ * ech_sparse_attn - the consumer of sel_slot: softmax attention of each head
+ * over the rows its sequence selects, read from the fixed device cache through
+ * the index tensor (ECHO Guide blog, "CUDA Graph Compatibility via
+ * Pre-Allocated Tensor Pointers": the attention binds no new addresses as the
+ * selection changes). Rows are absorbed-MLA rows of 576 bf16 values: all 576
+ * are the key, the first 512 the value. For sequence b and head h, over the
+ * valid entries j of sel_slot[b, :] (0 <= slot < C):
+ *   s_j = sm_scale * q[b,h,:] . dev_cache[slot_j, :]
+ *   out[b,h,:] = sum_j softmax(s)_j * dev_cache[slot_j, 0:512]
+ *   lse[b,h] = log sum_j exp(s_j)
+ * Entries < 0 or >= C select nothing (padding of short sequences); a sequence
+ * that selects nothing gets out = 0 and lse = -inf. Scores accumulate in fp32
+ * on bf16 matrix cores; the softmax weights enter the value product as bf16.
+ *  q          [B, H, 576] bf16, 16-byte aligned; H a multiple of 16, <= 128.
+ *  dev_cache  [C, 576] bf16 (the layer's device cache), 16-byte aligned.
+ *  sel_slot   [B, k] int32 (what ech_cache_step FINAL writes), 1 <= k <= 65536.
+ *  out        [B, H, 512] fp32, 16-byte aligned; lse [B, H] fp32 or NULL.
+ *  ws         ech_sparse_attn_ws_bytes(B, H, k) bytes, 256-byte aligned
+ *             (per-span partial results; uninitialised OK).
+ *  ECH_EINVAL for NULLs, bad sizes or alignment, a NaN sm_scale.
+ */
+size_t ech_sparse_attn_ws_bytes(int B, int H, int k);
+int ech_sparse_attn(const void* q, const void* dev_cache, int32_t C, const int32_t* sel_slot, int B, int H, int k,
+                    float sm_scale, float* out, float* lse, void* ws, size_t ws_bytes, void* stream);
 
 #ifdef __cplusplus
 }

@@ -19,7 +19,7 @@ from ._native import (ECH_EARLY, ECH_FINAL, ECH_PREFILL, ECH_KEY_BF16, ECH_KEY_F
                       CTR_HEAD, CTR_EPOCH, CTR_NMISS, CTR_NEVICT, CTR_RECALLED, CTR_STATUS, CTR_NWANT,
                       CTR_NPINNED, CTR_NMISS_EARLY, CTR_TICKET, CTR_LEN, ST_OVERFLOW, ST_BADTOK, ST_BADMISS)
 
-__all__ = ['ech_index_logits', 'ech_index_logits_causal', 'ech_topk', 'ech_topk_ws_bytes', 'ech_cache_reset',
+__all__ = ['ech_sparse_attn', 'ech_sparse_attn_ws_bytes', 'ech_index_logits', 'ech_index_logits_causal', 'ech_topk', 'ech_topk_ws_bytes', 'ech_cache_reset',
            'ech_cache_step', 'ech_cache_step_ws_bytes', 'ech_recall', 'ech_early_ws_bytes', 'ech_early_begin',
            'ech_early_group', 'ech_recall_group', 'EchError', 'LayerState', 'lib']
 
@@ -206,3 +206,19 @@ def ech_recall_group(group: int, host_pool, dev_cache, state: LayerState, ws, st
     _check('ech_recall_group', lib().ech_recall_group(
         int(group), _ptr(host_pool), host_pool.shape[0], row_bytes, _ptr(dev_cache), dev_cache.shape[0], _ptr(miss),
         miss.shape[0], _ptr(state.ctr), _ptr(ws), _stream(stream)))
+
+
+# ------------------------------------------------------------------ consumer: sparse attention
+def ech_sparse_attn_ws_bytes(B: int, H: int, k: int) -> int:
+    return int(lib().ech_sparse_attn_ws_bytes(B, H, k))
+
+
+def ech_sparse_attn(q, dev_cache, sel_slot, sm_scale: float, out, lse=None, ws=None, stream=None) -> None:
+    """Attention of each head over the rows its sequence selects: q [B, H, 576]
+    bf16 bits (int16/uint16), dev_cache [C, 576] bf16 bits, sel_slot [B, k]
+    int32 -> out [B, H, 512] fp32, lse [B, H] fp32 (optional)."""
+    B, H = q.shape[0], q.shape[1]
+    k = sel_slot.shape[1]
+    _check('ech_sparse_attn', lib().ech_sparse_attn(
+        _ptr(q), _ptr(dev_cache), dev_cache.shape[0], _ptr(sel_slot), B, H, k, float(sm_scale), _ptr(out),
+        _ptr(lse), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))

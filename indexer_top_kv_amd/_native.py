@@ -59,6 +59,9 @@ SIGNATURES = {
                                        _p, ctypes.c_int, ctypes.c_int, _p, _i64, _p, _p, _i32, _p, _i32, _p, _p,
                                        _p, _sz, _p]),
     'ech_recall_group': (ctypes.c_int, [ctypes.c_int, _p, _i64, _i64, _p, _i32, _p, _i32, _p, _p, _p]),
+    'ech_sparse_attn_ws_bytes': (_sz, [ctypes.c_int, ctypes.c_int, ctypes.c_int]),
+    'ech_sparse_attn': (ctypes.c_int, [_p, _p, _i32, _p, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_float,
+                                       _p, _p, _p, _sz, _p]),
 }
 
 _lib = None
