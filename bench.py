@@ -167,6 +167,26 @@ def bench_decode(args, wl):
         d = [ev[i].elapsed_time(ev[i + 1]) for i in range(0, len(ev), 2)]
         return float(np.sum(d)) / n_stage
 
+    # The consumer of sel_slot: sparse attention (128 heads, 576-value rows)
+    # over the step's selections in the device cache, K launches between one
+    # pair of events.
+    import indexer_top_kv_amd as ech
+    Ha = 128
+    qa = torch.randn((wl.B, Ha, 576), device='cuda').to(torch.bfloat16).view(torch.int16)
+    out_a = torch.empty((wl.B, Ha, 512), dtype=torch.float32, device='cuda')
+    lse_a = torch.empty((wl.B, Ha), dtype=torch.float32, device='cuda')
+    ws_a = torch.empty(ech.ech_sparse_attn_ws_bytes(wl.B, Ha, wl.k), dtype=torch.uint8, device='cuda')
+    sm = 1.0 / float(np.sqrt(192.0))
+    ech.ech_sparse_attn(qa, layer.dev_cache, layer.sel_slot, sm, out_a, lse_a, ws_a)
+    ea0, ea1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ea0.record(s0)
+    for _ in range(args.steps):
+        ech.ech_sparse_attn(qa, layer.dev_cache, layer.sel_slot, sm, out_a, lse_a, ws_a)
+    ea1.record(s0)
+    torch.cuda.synchronize()
+    attn_us = ea0.elapsed_time(ea1) / args.steps * 1e3
+    n_sel = int((layer.sel_slot >= 0).sum().item())
+
     wall = t1 - t0
     tokens = int(wl.lens.astype(np.int64).sum())
     value = tokens * args.steps / wall
@@ -224,6 +244,16 @@ def bench_decode(args, wl):
         'recall': {'bound': 'pcie', 'bytes_per_step': out['recall']['bytes_per_step'], 'us': rec_us,
                    'achieved_GBs': out['recall']['bytes_per_step'] / (rec_us * 1e-6) / 1e9 if rec_us else None,
                    'note': 'EARLY + FINAL recall kernels of eager steps; denominator: pcie.h2d_memcpy_GBs'},
+        'attention': {'kernel': 'ech_sparse_attn (span + merge launches)', 'heads': Ha, 'rows_attended': n_sel,
+                      'us': attn_us,
+                      'bound': 'hbm',
+                      'algorithmic_bytes': n_sel * 1152 + wl.B * Ha * (576 * 2 + 512 * 4 + 4),
+                      'achieved_GBs': (n_sel * 1152 + wl.B * Ha * (576 * 2 + 512 * 4 + 4)) / (attn_us * 1e-6) / 1e9,
+                      'peak_GBs': PEAK_HBM_GBS,
+                      'frac': (n_sel * 1152 + wl.B * Ha * (576 * 2 + 512 * 4 + 4)) / (attn_us * 1e-6) / 1e9
+                      / PEAK_HBM_GBS,
+                      'mfma_bf16_frac': n_sel * Ha * (576 + 512) * 2 / (attn_us * 1e-6) / 1e12 / PEAK_BF16_TFLOPS,
+                      'note': 'the consumer of sel_slot, after the timed steps; not part of the step time'},
         'allocator': {'early_maps_us': st['early_maps'], 'final_maps_us': st['final_maps'],
                       'note': 'slot-map phases in eager steps (count, place), run beside '
                               'the top-k (EARLY) and beside the EARLY recall (FINAL)'},

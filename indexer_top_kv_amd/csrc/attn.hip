@@ -50,7 +50,11 @@ __device__ __forceinline__ float lane_group_max(float x) {
 }
 
 // Gather the rows of tile tokens [t0, t0 + 32) of this span into registers
-// (invalid tokens: slot 0, flagged). Each thread takes pieces i = tid + j*nt.
+// (invalid tokens: slot 0, flagged). Each thread takes pieces i = tid + j*nt,
+// token fastest: neighbouring lanes then write neighbouring tokens of one
+// value column in the transposed tile (2-byte stores without bank conflicts;
+// token-major rows would put 16 lanes on 4 banks), and 16-byte row pieces of
+// neighbouring tokens, whose LDS rows the pitch spreads over all banks.
 template <int NT>
 __device__ __forceinline__ void tile_load(const uint4* __restrict__ cache, const int32_t* __restrict__ sel, int C,
                                           int t0, int t1, uint4 (&reg)[(kTile * kChunks + NT - 1) / NT]) {
@@ -58,7 +62,7 @@ __device__ __forceinline__ void tile_load(const uint4* __restrict__ cache, const
 #pragma unroll
   for (int j = 0; j < kP; ++j) {
     const int i = threadIdx.x + j * NT;
-    const int t = i / kChunks, ch = i - t * kChunks;
+    const int ch = i / kTile, t = i - ch * kTile;
     int slot = 0;
     if (i < kTile * kChunks && t0 + t < t1) {
       const int s = sel[t0 + t];
@@ -77,7 +81,7 @@ __device__ __forceinline__ void tile_store(uint8_t* __restrict__ lds_k, uint8_t*
   for (int j = 0; j < kP; ++j) {
     const int i = threadIdx.x + j * NT;
     if (i >= kTile * kChunks) break;
-    const int t = i / kChunks, ch = i - t * kChunks;
+    const int ch = i / kTile, t = i - ch * kTile;
     *reinterpret_cast<uint4*>(lds_k + t * kKPitch + ch * 16) = reg[j];
     if (ch < kVChunks) {
       const uint32_t w[4] = {reg[j].x, reg[j].y, reg[j].z, reg[j].w};
@@ -128,13 +132,14 @@ __global__ void __launch_bounds__(NT, 1)
   for (int c = 0; c < kCt; ++c) acc[c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   float m = -__builtin_inff(), l = 0.f;
 
-  uint4 reg[kP];
-  if (t_begin < t_end) tile_load<NT>(cache, sel, C, t_begin, t_end, reg);
   for (int t0 = t_begin; t0 < t_end; t0 += kTile) {
-    __syncthreads();                                         // the previous tile is consumed
-    tile_store<NT>(lds_k, lds_v, lds_ok, sel, C, t0, t_end, reg);
-    __syncthreads();
-    if (t0 + kTile < t_end) tile_load<NT>(cache, sel, C, t0 + kTile, t_end, reg);   // next rows in flight
+    {
+      uint4 reg[kP];
+      tile_load<NT>(cache, sel, C, t0, t_end, reg);
+      __syncthreads();                                       // the previous tile is consumed
+      tile_store<NT>(lds_k, lds_v, lds_ok, sel, C, t0, t_end, reg);
+      __syncthreads();
+    }
 
     // scores of the 32 tokens for this wave's 16 heads
     f32x4_t st[2];
@@ -155,7 +160,11 @@ __global__ void __launch_bounds__(NT, 1)
       tmax = fmaxf(tmax, sv[j]);
     }
     tmax = lane_group_max(tmax);
-    const float mn = fmaxf(m, tmax);
+    // The running max moves only when some head's tile max exceeds it by more
+    // than 8 (base 2): weights up to 2^8 stay exact enough in fp32 sums and
+    // in bf16, and most tiles then skip the rescale of the accumulators.
+    const bool grow = __any(tmax > m + 8.f);
+    const float mn = grow ? fmaxf(m, tmax) : m;
     const bool none = (mn == -__builtin_inff());
     const float alpha = none ? 1.f : exp2f(m - mn);
     float psum = 0.f;
@@ -168,10 +177,12 @@ __global__ void __launch_bounds__(NT, 1)
     }
     l = l * alpha + lane_group_sum(psum);
     m = mn;
+    if (grow) {
 #pragma unroll
-    for (int c = 0; c < kCt; ++c) {
+      for (int c = 0; c < kCt; ++c) {
 #pragma unroll
-      for (int v = 0; v < 4; ++v) acc[c][v] *= alpha;
+        for (int v = 0; v < 4; ++v) acc[c][v] *= alpha;
+      }
     }
     // O^T += V^T . P^T: A = value column (ct*16 + col) at this lane group's tokens
 #pragma unroll
@@ -200,14 +211,23 @@ __global__ void __launch_bounds__(128)
   float den = 0.f;
   f32x4_t o = f32x4_t{0.f, 0.f, 0.f, 0.f};
   if (mx != -__builtin_inff()) {
-    for (int s = 0; s < nsp; ++s) {
-      const float2 ml = part_ml[((size_t)b * nsp + s) * H + h];
-      const float wgt = exp2f(ml.x - mx);          // 0 for a span that saw nothing
-      den += wgt * ml.y;
-      const f32x4_t v = *reinterpret_cast<const f32x4_t*>(part_o + (((size_t)b * nsp + s) * H + h) * kValV +
-                                                         4 * threadIdx.x);
+    for (int s0 = 0; s0 < nsp; s0 += 8) {
+      f32x4_t v[8];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) o[e] += wgt * v[e];
+      for (int j = 0; j < 8; ++j)        // the group's loads in flight together
+        if (s0 + j < nsp)
+          v[j] = *reinterpret_cast<const f32x4_t*>(part_o + (((size_t)b * nsp + s0 + j) * H + h) * kValV +
+                                                   4 * threadIdx.x);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        if (s0 + j < nsp) {
+          const float2 ml = part_ml[((size_t)b * nsp + s0 + j) * H + h];
+          const float wgt = exp2f(ml.x - mx);      // 0 for a span that saw nothing
+          den += wgt * ml.y;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) o[e] += wgt * v[j][e];
+        }
+      }
     }
   }
   const float inv = den > 0.f ? 1.f / den : 0.f;
