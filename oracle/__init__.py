@@ -14,6 +14,8 @@ against the pages:
 - ``select``    - exact top-k by full stable sort; EMA threshold.
 - ``slotmap``   - sequential per-layer slot-map simulator (free -> allocate ->
                   recall, no write-back) and the recall byte copy.
+- ``append``    - the decoded token of each sequence joins the host pool and
+                  the key cache (growing contexts).
 - ``attention`` - softmax attention of each head over the rows its sequence
                   selects through sel_slot (the consumer of the path).
 
@@ -27,9 +29,10 @@ Every function is pinned by ``tests/test_oracle_*.py`` against closed forms,
 brute force on tiny inputs, library routines and invariants; none is marked
 "parity unpinned".
 """
-from . import numerics, indexer, select, slotmap, attention  # noqa: F401
+from . import numerics, indexer, select, slotmap, attention, append  # noqa: F401
 from .numerics import bf16_to_f64, e4m3fn_to_f64, e4m3fn_table  # noqa: F401
 from .indexer import index_logits, index_logit_at, dequant_keys  # noqa: F401
 from .select import topk_row, topk_rows, theta_next, theta_rows  # noqa: F401
 from .slotmap import SlotMap, recall_rows  # noqa: F401
 from .attention import sparse_attention  # noqa: F401
+from .append import kv_append  # noqa: F401

@@ -476,3 +476,71 @@ def pin_attn_permutation(sparse_attention):
 
 
 ATTN_PINS = [pin_attn_library, pin_attn_closed_forms, pin_attn_bruteforce, pin_attn_permutation]
+
+
+# ------------------------------------------------------------------ append
+
+def pin_append_hand(kv_append):
+    """Two sequences laid out [0, 4) and [4, 7) (capacities 4 and 3), worked
+    by hand: sequence 0 (length 2) gets token 2, sequence 1 (length 3) is
+    full."""
+    pool = np.zeros((7, 2), np.int16)
+    keys = np.zeros((7, 3), np.uint8)
+    scale = np.zeros(7, np.float32)
+    t2s = np.array([5, 1, 9, -1, 0, 2, 3], np.int32)
+    lens = np.array([2, 3], np.int32)
+    full = kv_append(pool, keys, scale, t2s, np.array([0, 4]), lens, np.array([4, 3]),
+                     np.array([[11, 12], [21, 22]], np.int16), np.array([[1, 2, 3], [4, 5, 6]], np.uint8),
+                     np.array([0.5, 2.0], np.float32))
+    assert full
+    np.testing.assert_array_equal(lens, [3, 3])
+    np.testing.assert_array_equal(pool, [[0, 0], [0, 0], [11, 12], [0, 0], [0, 0], [0, 0], [0, 0]])
+    np.testing.assert_array_equal(keys[2], [1, 2, 3])
+    assert keys[[0, 1, 3, 4, 5, 6]].sum() == 0
+    np.testing.assert_array_equal(scale, [0, 0, 0.5, 0, 0, 0, 0])
+    np.testing.assert_array_equal(t2s, [5, 1, -1, -1, 0, 2, 3])
+    # bf16 keys carry no scale; appending again fills the last free id of sequence 0
+    full = kv_append(pool, keys, None, t2s, np.array([0, 4]), lens, np.array([4, 3]),
+                     np.array([[31, 32], [41, 42]], np.int16), np.array([[7, 8, 9], [1, 1, 1]], np.uint8), None)
+    assert full
+    np.testing.assert_array_equal(lens, [4, 3])
+    np.testing.assert_array_equal(pool[3], [31, 32])
+    np.testing.assert_array_equal(keys[3], [7, 8, 9])
+
+
+def pin_append_invariants(kv_append):
+    """Random layouts: only the ids tok0 + old length change, each to its
+    sequence's new row; nothing is written for full sequences."""
+    r = np.random.default_rng(3)
+    for _ in range(20):
+        B = int(r.integers(1, 6))
+        cap = r.integers(1, 6, B)
+        tok0 = np.concatenate([[0], np.cumsum(cap)[:-1]])
+        P = int(cap.sum())
+        lens = np.array([int(r.integers(0, c + 1)) for c in cap], np.int32)
+        pool = r.integers(-100, 100, (P, 3)).astype(np.int16)
+        keys = r.integers(0, 255, (P, 2)).astype(np.uint8)
+        t2s = r.integers(-1, 9, P).astype(np.int32)
+        rows = r.integers(-100, 100, (B, 3)).astype(np.int16)
+        nk = r.integers(0, 255, (B, 2)).astype(np.uint8)
+        p0, k0, t0, l0 = pool.copy(), keys.copy(), t2s.copy(), lens.copy()
+        full = kv_append(pool, keys, None, t2s, tok0, lens, cap, rows, nk, None)
+        assert full == bool((l0 >= cap).any())
+        changed = set()
+        for b in range(B):
+            if l0[b] < cap[b]:
+                g = tok0[b] + l0[b]
+                changed.add(int(g))
+                assert lens[b] == l0[b] + 1
+                np.testing.assert_array_equal(pool[g], rows[b])
+                np.testing.assert_array_equal(keys[g], nk[b])
+                assert t2s[g] == -1
+            else:
+                assert lens[b] == l0[b]
+        rest = [i for i in range(P) if i not in changed]
+        np.testing.assert_array_equal(pool[rest], p0[rest])
+        np.testing.assert_array_equal(keys[rest], k0[rest])
+        np.testing.assert_array_equal(t2s[rest], t0[rest])
+
+
+APPEND_PINS = [pin_append_hand, pin_append_invariants]

@@ -86,3 +86,8 @@ def test_final_overflow_is_error():
 @pytest.mark.parametrize('pin', pins.ATTN_PINS, ids=lambda f: f.__name__)
 def test_attention_pins(pin):
     pin(oracle.sparse_attention)
+
+
+@pytest.mark.parametrize('pin', pins.APPEND_PINS, ids=lambda f: f.__name__)
+def test_append_pins(pin):
+    pin(oracle.kv_append)

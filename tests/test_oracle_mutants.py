@@ -337,3 +337,39 @@ def test_attention_mutants_are_caught(name):
 def test_attention_unmutated_core_passes():
     for p in pins.ATTN_PINS:
         p(_attn_with(dict(fn=lambda q, r, sc: _softmax_core(q @ r.T * sc, r[:, :512]))))
+
+
+# ------------------------------------------------------------------ append
+
+def _append_mutant(kind):
+    def f(host_pool, kcache, kscale, tok2slot, tok0, lens, cap, new_rows, new_keys, new_scales):
+        full = False
+        for b in range(len(lens)):
+            if kind != 'ignores_cap' and lens[b] >= cap[b]:
+                full = True
+                continue
+            if kind == 'ignores_cap' and lens[b] >= cap[b]:
+                full = True
+            g = int(tok0[b]) + int(lens[b]) - (1 if kind == 'off_by_one' else 0)
+            if kind == 'ignores_cap' and g >= host_pool.shape[0]:
+                continue
+            host_pool[g] = new_rows[b]
+            kcache[g] = new_keys[b]
+            if kscale is not None:
+                kscale[g if kind != 'scale_next' else min(g + 1, len(kscale) - 1)] = new_scales[b]
+            if kind != 'keeps_slot':
+                tok2slot[g] = -1
+            if kind != 'no_grow':
+                lens[b] += 1
+        return full
+    return f
+
+
+@pytest.mark.parametrize('kind', ['off_by_one', 'ignores_cap', 'scale_next', 'keeps_slot', 'no_grow'])
+def test_append_mutants_are_caught(kind):
+    assert _fails(pins.APPEND_PINS, _append_mutant(kind)), kind
+
+
+def test_append_unmutated_passes():
+    for p in pins.APPEND_PINS:
+        p(_append_mutant('none'))
