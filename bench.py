@@ -187,6 +187,32 @@ def bench_decode(args, wl):
     attn_us = ea0.elapsed_time(ea1) / args.steps * 1e3
     n_sel = int((layer.sel_slot >= 0).sum().item())
 
+    # Growing contexts: ech_kv_append of one decoded token per sequence, on a
+    # scratch layout of the same batch (B sequences with room for K tokens)
+    # so the layer's own data stays as the steps left it.
+    Ka = args.steps
+    Ps = wl.B * (Ka + 1)
+    pool_s = torch.empty((Ps, 576), dtype=torch.int16, pin_memory=True)
+    kc_s = torch.zeros((Ps, 128), dtype=torch.uint8, device='cuda')
+    ks_s = torch.zeros(Ps, dtype=torch.float32, device='cuda')
+    st_s = ech.LayerState.allocate(Ps, 16, 16)
+    ech.ech_cache_reset(st_s)
+    t0_s = torch.arange(wl.B, dtype=torch.int64, device='cuda') * (Ka + 1)
+    len_s = torch.zeros(wl.B, dtype=torch.int32, device='cuda')
+    cap_s = torch.full((wl.B,), Ka + 1, dtype=torch.int32, device='cuda')
+    rows_s = torch.zeros((wl.B, 576), dtype=torch.int16, device='cuda')
+    keys_s = torch.zeros((wl.B, 128), dtype=torch.uint8, device='cuda')
+    sc_s = torch.ones(wl.B, dtype=torch.float32, device='cuda')
+    ech.ech_kv_append(pool_s, kc_s, ks_s, st_s, t0_s, len_s, cap_s, rows_s, keys_s, sc_s)
+    eb0, eb1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    eb0.record(s0)
+    for _ in range(Ka - 1):
+        ech.ech_kv_append(pool_s, kc_s, ks_s, st_s, t0_s, len_s, cap_s, rows_s, keys_s, sc_s)
+    eb1.record(s0)
+    torch.cuda.synchronize()
+    append_us = eb0.elapsed_time(eb1) / max(Ka - 1, 1) * 1e3
+    assert int(len_s.min().item()) == Ka and int(st_s.ctr[5].item()) == 0
+
     wall = t1 - t0
     tokens = int(wl.lens.astype(np.int64).sum())
     value = tokens * args.steps / wall
@@ -254,6 +280,10 @@ def bench_decode(args, wl):
                       / PEAK_HBM_GBS,
                       'mfma_bf16_frac': n_sel * Ha * (576 + 512) * 2 / (attn_us * 1e-6) / 1e12 / PEAK_BF16_TFLOPS,
                       'note': 'the consumer of sel_slot, after the timed steps; not part of the step time'},
+        'append': {'kernel': 'ech_kv_append', 'sequences': wl.B, 'us': append_us,
+                   'bytes_per_call': wl.B * (1152 + 128 + 4),
+                   'note': 'one decoded token per sequence: its row written over PCIe into the pinned pool, '
+                           'its fp8 key and scale into the key cache; latency-bound'},
         'allocator': {'early_maps_us': st['early_maps'], 'final_maps_us': st['final_maps'],
                       'note': 'slot-map phases in eager steps (count, place), run beside '
                               'the top-k (EARLY) and beside the EARLY recall (FINAL)'},

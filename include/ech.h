@@ -20,6 +20,8 @@
  *      device-cache slots.
  *   5. ech_sparse_attn (the consumer): attention of each head over the rows
  *      its sequence selects, through sel_slot.
+ *   6. ech_kv_append: each sequence's decoded token joins the host pool and
+ *      the key cache (growing contexts).
  *
  * Conventions
  *  - Ownership: the caller owns every buffer (device memory, the pinned host
@@ -82,6 +84,7 @@ extern "C" {
 #define ECH_ST_OVERFLOW   1   /* a FINAL/PREFILL phase found fewer unpinned slots than misses */
 #define ECH_ST_BADTOK     2   /* a selected token offset was outside [0, len) */
 #define ECH_ST_BADMISS    4   /* ech_recall saw a miss entry with g >= P or slot >= C */
+#define ECH_ST_FULL       8   /* ech_kv_append found a sequence at its capacity */
 
 /* Human-readable name of a return code. */
 const char* ech_status_str(int code);
@@ -313,6 +316,28 @@ int ech_recall_group(int group, const void* host_pool, int64_t P, int64_t row_by
 size_t ech_sparse_attn_ws_bytes(int B, int H, int k);
 int ech_sparse_attn(const void* q, const void* dev_cache, int32_t C, const int32_t* sel_slot, int B, int H, int k,
                     float sm_scale, float* out, float* lse, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * ech_kv_append - each sequence's newly decoded token joins the layer's data
+ * (growing contexts). The host copy holds every KV row and is per model (ECHO
+ * explainer, "One layer, one step"), so the row is written once, here, over
+ * PCIe into the pinned host pool; the key cache gets the token's indexer key.
+ * Sequence b owns global token ids [seq_tok0[b], seq_tok0[b] + seq_cap[b]);
+ * its new token g = seq_tok0[b] + seq_len[b]:
+ *   host_pool[g] = new_rows[b]   (row_bytes)
+ *   kcache[g] = new_keys[b]      (128 B fp8 or 256 B bf16), kscale[g] = new_scales[b] (fp8)
+ *   tok2slot[g] = -1             (not resident; a later recall brings it in)
+ *   seq_len[b] += 1              (device, in place)
+ * A sequence with seq_len[b] >= seq_cap[b] (or g outside [0, P)) gets nothing
+ * written and sets ECH_ST_FULL in ctr[ECH_CTR_STATUS].
+ *  host_pool  [P, row_bytes] pinned host memory (host pointer, device-mapped).
+ *  new_rows   [B, row_bytes] and new_keys [B, key bytes] device, 16-byte aligned;
+ *             new_scales [B] fp32 (fp8 keys; NULL for bf16).
+ *  Order it after the step that scores the old length and before the next.
+ */
+int ech_kv_append(void* host_pool, int64_t P, int64_t row_bytes, void* kcache, int kdtype, float* kscale,
+                  int32_t* tok2slot, const int64_t* seq_tok0, int32_t* seq_len, const int32_t* seq_cap, int B,
+                  const void* new_rows, const void* new_keys, const float* new_scales, int32_t* ctr, void* stream);
 
 #ifdef __cplusplus
 }

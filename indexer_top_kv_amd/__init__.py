@@ -17,9 +17,9 @@ import torch
 from . import _native
 from ._native import (ECH_EARLY, ECH_FINAL, ECH_PREFILL, ECH_KEY_BF16, ECH_KEY_FP8,  # noqa: F401
                       CTR_HEAD, CTR_EPOCH, CTR_NMISS, CTR_NEVICT, CTR_RECALLED, CTR_STATUS, CTR_NWANT,
-                      CTR_NPINNED, CTR_NMISS_EARLY, CTR_TICKET, CTR_LEN, ST_OVERFLOW, ST_BADTOK, ST_BADMISS)
+                      CTR_NPINNED, CTR_NMISS_EARLY, CTR_TICKET, CTR_LEN, ST_OVERFLOW, ST_BADTOK, ST_BADMISS, ST_FULL)
 
-__all__ = ['ech_sparse_attn', 'ech_sparse_attn_ws_bytes', 'ech_index_logits', 'ech_index_logits_causal', 'ech_topk', 'ech_topk_ws_bytes', 'ech_cache_reset',
+__all__ = ['ech_kv_append', 'ech_sparse_attn', 'ech_sparse_attn_ws_bytes', 'ech_index_logits', 'ech_index_logits_causal', 'ech_topk', 'ech_topk_ws_bytes', 'ech_cache_reset',
            'ech_cache_step', 'ech_cache_step_ws_bytes', 'ech_recall', 'ech_early_ws_bytes', 'ech_early_begin',
            'ech_early_group', 'ech_recall_group', 'EchError', 'LayerState', 'lib']
 
@@ -222,3 +222,15 @@ def ech_sparse_attn(q, dev_cache, sel_slot, sm_scale: float, out, lse=None, ws=N
     _check('ech_sparse_attn', lib().ech_sparse_attn(
         _ptr(q), _ptr(dev_cache), dev_cache.shape[0], _ptr(sel_slot), B, H, k, float(sm_scale), _ptr(out),
         _ptr(lse), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
+
+
+# ------------------------------------------------------------------ growing contexts
+def ech_kv_append(host_pool, kcache, kscale, state: LayerState, seq_tok0, seq_len, seq_cap, new_rows, new_keys,
+                  new_scales=None, stream=None) -> None:
+    """Each sequence's decoded token joins the host pool (pinned [P, row])
+    and the key cache; seq_len (device int32) grows in place."""
+    row_bytes = host_pool.shape[1] * host_pool.element_size()
+    _check('ech_kv_append', lib().ech_kv_append(
+        _ptr(host_pool), host_pool.shape[0], row_bytes, _ptr(kcache), _key_dtype(kcache), _ptr(kscale),
+        _ptr(state.tok2slot), _ptr(seq_tok0), _ptr(seq_len), _ptr(seq_cap), seq_tok0.shape[0], _ptr(new_rows),
+        _ptr(new_keys), _ptr(new_scales), _ptr(state.ctr), _stream(stream)))

@@ -29,6 +29,7 @@ CTR_LEN = 16
 ST_OVERFLOW = 1
 ST_BADTOK = 2
 ST_BADMISS = 4
+ST_FULL = 8
 
 _p = ctypes.c_void_p
 _i32 = ctypes.c_int32
@@ -59,6 +60,8 @@ SIGNATURES = {
                                        _p, ctypes.c_int, ctypes.c_int, _p, _i64, _p, _p, _i32, _p, _i32, _p, _p,
                                        _p, _sz, _p]),
     'ech_recall_group': (ctypes.c_int, [ctypes.c_int, _p, _i64, _i64, _p, _i32, _p, _i32, _p, _p, _p]),
+    'ech_kv_append': (ctypes.c_int, [_p, _i64, _i64, _p, ctypes.c_int, _p, _p, _p, _p, _p, ctypes.c_int, _p, _p, _p,
+                                     _p, _p]),
     'ech_sparse_attn_ws_bytes': (_sz, [ctypes.c_int, ctypes.c_int, ctypes.c_int]),
     'ech_sparse_attn': (ctypes.c_int, [_p, _p, _i32, _p, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_float,
                                        _p, _p, _p, _sz, _p]),

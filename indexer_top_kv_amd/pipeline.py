@@ -44,7 +44,7 @@ import torch
 
 from . import (ECH_EARLY, ECH_FINAL, ECH_PREFILL, LayerState, ech_cache_reset, ech_cache_step,
                ech_cache_step_ws_bytes, ech_early_begin, ech_early_group, ech_early_ws_bytes, ech_index_logits,
-               ech_index_logits_causal, ech_recall, ech_recall_group, ech_topk, ech_topk_ws_bytes)
+               ech_index_logits_causal, ech_kv_append, ech_recall, ech_recall_group, ech_topk, ech_topk_ws_bytes)
 
 
 def round_up(x: int, m: int) -> int:
@@ -82,7 +82,7 @@ class DecodeLayer:
                  tok0: np.ndarray, lens: np.ndarray, C: int, k: int = 2048, cap: int = 512,
                  host_pool: Optional[torch.Tensor] = None, early: bool = True, topk_after_early: bool = False,
                  topk_first: Optional[bool] = None,
-                 early_groups: int = 0, device='cuda'):
+                 early_groups: int = 0, capacity: Optional[np.ndarray] = None, device='cuda'):
         self.kcache, self.kscale, self.w = kcache, kscale, w
         self.topk_after_early = topk_after_early
         # Launch order of the two branches after the scores. A captured graph
@@ -94,7 +94,12 @@ class DecodeLayer:
         self.B = len(lens)
         self.lens_np = np.asarray(lens, np.int32)
         self.tok0_np = np.asarray(tok0, np.int64)
-        self.max_len = int(self.lens_np.max())
+        # Growing contexts: sequence b may reach capacity[b] tokens (ech_kv_append
+        # grows the device lengths); grids, buffers and chunks are sized for it.
+        self.cap_np = self.lens_np.copy() if capacity is None else np.asarray(capacity, np.int32)
+        if np.any(self.cap_np < self.lens_np):
+            raise ValueError('capacity below the current length')
+        self.max_len = int(self.cap_np.max())
         self.k, self.cap, self.C = k, cap, C
         self.early = early
         self.P = kcache.shape[0]
@@ -110,7 +115,8 @@ class DecodeLayer:
         self.sel_slot = torch.empty((self.B, k), dtype=torch.int32, **dev)
         self.stats_early = torch.zeros((self.B, 4), dtype=torch.int32, **dev)
         self.stats_final = torch.zeros((self.B, 4), dtype=torch.int32, **dev)
-        self.chunks = sequence_chunks(self.lens_np, k, C)
+        self.chunks = sequence_chunks(self.cap_np, k, C)
+        self.seq_cap = torch.from_numpy(self.cap_np).to(**dev)
         cb = max(e - s for s, e in self.chunks)
         m_max = max(cb * min(k, self.max_len), cb * min(cap, self.max_len), 1)
         m_early = max(cb * min(cap, self.max_len), 1)   # the EARLY demand bound: no free slot beyond it is ranked
@@ -159,6 +165,13 @@ class DecodeLayer:
     def _recall(self, phase: int, stream) -> None:
         if self.host_pool is not None:
             ech_recall(self.host_pool, self.dev_cache, self.state, phase=phase, stream=stream)
+
+    def append(self, new_rows: torch.Tensor, new_keys: torch.Tensor, new_scales: Optional[torch.Tensor] = None,
+               stream=None) -> None:
+        """Each sequence's decoded token joins the host pool and the key cache
+        (ech_kv_append); the device lengths grow by one, up to the capacity."""
+        ech_kv_append(self.host_pool, self.kcache, self.kscale, self.state, self.tok0, self.lens, self.seq_cap,
+                      new_rows, new_keys, new_scales, stream=stream)
 
     def logits_only(self, q: torch.Tensor, stream=None) -> None:
         ech_index_logits(q, self.w, self.kcache, self.kscale, self.tok0, self.lens, self.max_len, self.logits,
