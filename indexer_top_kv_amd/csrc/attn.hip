@@ -49,33 +49,46 @@ __device__ __forceinline__ float lane_group_max(float x) {
   return fmaxf(__uint_as_float(q[0]), __uint_as_float(q[1]));
 }
 
-// Gather the rows of tile tokens [t0, t0 + 32) of this span into registers
-// (invalid tokens: slot 0, flagged). Each thread takes pieces i = tid + j*nt,
-// token fastest: neighbouring lanes then write neighbouring tokens of one
-// value column in the transposed tile (2-byte stores without bank conflicts;
-// token-major rows would put 16 lanes on 4 banks), and 16-byte row pieces of
-// neighbouring tokens, whose LDS rows the pitch spreads over all banks.
+// Gather the rows of tile tokens [t0, t0 + 32) of this span into registers.
+// Each thread takes pieces i = tid + j*NT, token fastest: neighbouring lanes
+// then write neighbouring tokens of one value column in the transposed tile
+// (2-byte stores without bank conflicts; token-major pieces would put 16
+// lanes on 4 banks), and 16-byte row pieces of neighbouring tokens, whose LDS
+// rows the pitch spreads over all banks. Every slot id is read first with a
+// clamped index and every row piece after, with no branch around a load, so
+// a tile costs two memory round trips (a guarded load waits for all loads in
+// flight before the next one issues). Invalid tokens read slot 0; the
+// result says whether piece 0's token is valid.
 template <int NT>
-__device__ __forceinline__ void tile_load(const uint4* __restrict__ cache, const int32_t* __restrict__ sel, int C,
-                                          int t0, int t1, uint4 (&reg)[(kTile * kChunks + NT - 1) / NT]) {
+__device__ __forceinline__ uint32_t tile_load(const uint4* __restrict__ cache, const int32_t* __restrict__ sel,
+                                              int C, int t0, int t1,
+                                              uint4 (&reg)[(kTile * kChunks + NT - 1) / NT]) {
   constexpr int kP = (kTile * kChunks + NT - 1) / NT;
+  int slot[kP];
 #pragma unroll
   for (int j = 0; j < kP; ++j) {
     const int i = threadIdx.x + j * NT;
-    const int ch = i / kTile, t = i - ch * kTile;
-    int slot = 0;
-    if (i < kTile * kChunks && t0 + t < t1) {
-      const int s = sel[t0 + t];
-      slot = (s >= 0 && s < C) ? s : 0;
-    }
-    reg[j] = (i < kTile * kChunks) ? cache[(size_t)slot * kChunks + ch] : make_uint4(0, 0, 0, 0);
+    const int t = i % kTile;
+    slot[j] = sel[min(t0 + t, t1 - 1)];
   }
+  uint32_t ok0 = 0;
+#pragma unroll
+  for (int j = 0; j < kP; ++j) {
+    const int i = threadIdx.x + j * NT;
+    const int ch = min(i / kTile, kChunks - 1), t = i % kTile;
+    const bool valid = (t0 + t < t1) && slot[j] >= 0 && slot[j] < C;
+    if (j == 0) ok0 = valid;
+    reg[j] = cache[(size_t)(valid ? slot[j] : 0) * kChunks + ch];
+  }
+  return ok0;
 }
 
+// Pieces beyond the tile (i >= 32 * 72) were loaded from a clamped address
+// and are dropped here. Threads 0..31 hold piece 0 of token tid (chunk 0).
 template <int NT>
 __device__ __forceinline__ void tile_store(uint8_t* __restrict__ lds_k, uint8_t* __restrict__ lds_v,
-                                           int* __restrict__ lds_ok, const int32_t* __restrict__ sel, int C, int t0,
-                                           int t1, const uint4 (&reg)[(kTile * kChunks + NT - 1) / NT]) {
+                                           int* __restrict__ lds_ok, uint32_t ok,
+                                           const uint4 (&reg)[(kTile * kChunks + NT - 1) / NT]) {
   constexpr int kP = (kTile * kChunks + NT - 1) / NT;
 #pragma unroll
   for (int j = 0; j < kP; ++j) {
@@ -92,15 +105,7 @@ __device__ __forceinline__ void tile_store(uint8_t* __restrict__ lds_k, uint8_t*
       }
     }
   }
-  if (threadIdx.x < kTile) {
-    const int t = threadIdx.x;
-    int ok = 0;
-    if (t0 + t < t1) {
-      const int s = sel[t0 + t];
-      ok = (s >= 0 && s < C);
-    }
-    lds_ok[t] = ok;
-  }
+  if (threadIdx.x < kTile) lds_ok[threadIdx.x] = (int)ok;
 }
 
 // grid (spans, B), block 64 * H/16 threads (NT fixed at compile time).
@@ -135,9 +140,9 @@ __global__ void __launch_bounds__(NT, 1)
   for (int t0 = t_begin; t0 < t_end; t0 += kTile) {
     {
       uint4 reg[kP];
-      tile_load<NT>(cache, sel, C, t0, t_end, reg);
+      const uint32_t ok = tile_load<NT>(cache, sel, C, t0, t_end, reg);
       __syncthreads();                                       // the previous tile is consumed
-      tile_store<NT>(lds_k, lds_v, lds_ok, sel, C, t0, t_end, reg);
+      tile_store<NT>(lds_k, lds_v, lds_ok, ok, reg);
       __syncthreads();
     }
 
