@@ -150,3 +150,38 @@ def test_lossless_through_the_cache():
         np.testing.assert_array_equal(o1, o2, err_msg=f'step {s}')
         np.testing.assert_array_equal(l1, l2, err_msg=f'step {s}')
         assert np.all(np.isfinite(l1))
+
+
+def test_captured_attention_follows_the_index_tensor():
+    """The attention captured once in a hipGraph keeps reading the fixed
+    pool through sel_slot: after the selection and the cache rows change in
+    place (as decode steps change them), every replay equals an eager call,
+    with unrelated eager work between the replays."""
+    need_gpu()
+    r = np.random.default_rng(21)
+    B, H, k, C = 3, 64, 512, 3000
+    q = dev(wk.to_bf16_bits(r.standard_normal((B, H, 576)).astype(np.float32)))
+    cache = dev(wk.to_bf16_bits(r.standard_normal((C, 576)).astype(np.float32)))
+    sel = dev(np.stack([r.choice(C, k, replace=False) for _ in range(B)]).astype(np.int32))
+    out = torch.zeros((B, H, 512), dtype=torch.float32, device='cuda')
+    lse = torch.zeros((B, H), dtype=torch.float32, device='cuda')
+    ws = torch.empty(ech.ech_sparse_attn_ws_bytes(B, H, k), dtype=torch.uint8, device='cuda')
+    ech.ech_sparse_attn(q, cache, sel, 0.08, out, lse, ws)     # warm-up outside the capture
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        ech.ech_sparse_attn(q, cache, sel, 0.08, out, lse, ws)
+    for step in range(4):
+        new_sel = np.stack([r.choice(C, k, replace=False) for _ in range(B)]).astype(np.int32)
+        new_sel[step % B, k - 100:] = -1
+        sel.copy_(torch.from_numpy(new_sel))
+        rows = r.choice(C, 200, replace=False)
+        cache[torch.from_numpy(rows).cuda()] = dev(wk.to_bf16_bits(r.standard_normal((200, 576)).astype(np.float32)))
+        g.replay()
+        torch.cuda.synchronize()
+        got_o, got_l = host(out).copy(), host(lse).copy()
+        ref_o, ref_l = _run(q, cache, sel, 0.08)
+        np.testing.assert_array_equal(got_o, ref_o, err_msg=f'replay {step}')
+        np.testing.assert_array_equal(got_l, ref_l, err_msg=f'replay {step}')
+        x = torch.arange(4096, device='cuda', dtype=torch.float32)    # unrelated eager work
+        assert float((x * 2).sum().item()) == 4096 * 4095
