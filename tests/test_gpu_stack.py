@@ -63,12 +63,13 @@ def _build(base, L, M, C_m, steps):
     return groups, layers, refs, qs
 
 
-@pytest.mark.parametrize('graph', [False, True], ids=['eager', 'graph'])
-def test_stack_matches_oracle_per_layer(graph):
+@pytest.mark.parametrize('graph,L,M', [(False, 3, 2), (True, 3, 2), (False, 2, 3), (True, 2, 3)],
+                         ids=['eager-3x2', 'graph-3x2', 'eager-2x3', 'graph-2x3'])
+def test_stack_matches_oracle_per_layer(graph, L, M):
     need_gpu()
     base = wk.CONFIGS['decode-64x110k-fp8-capacity'].scaled(B=5, N=7000, len_lo=3000, k=512, cap=128,
                                                             variant='dyadic', resample_p=0.3)
-    L, M, C_m, steps = 3, 2, 1700, 4
+    C_m, steps = 1700, 4
     groups, layers, refs, qs = _build(base, L, M, C_m, steps)
     stack = DecodeStack(layers)
     if graph:
