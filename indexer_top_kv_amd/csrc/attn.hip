@@ -207,31 +207,40 @@ __global__ void __launch_bounds__(NT, 1)
 }
 
 // out[b, h, :] and lse[b, h] from the spans' partials. grid (H, B), 128 threads.
+// KG = spans whose loads are in flight together (8 for up to 8 spans, else 32).
+template <int kG>
 __global__ void __launch_bounds__(128)
     attn_merge_kernel(const float* __restrict__ part_o, const float2* __restrict__ part_ml, int H, int nsp,
                       float* __restrict__ out, float* __restrict__ lse) {
   const int h = blockIdx.x, b = blockIdx.y;
+  // Every load below is clamped and unguarded, so a group's loads all issue
+  // before the first wait; spans past the end are masked in arithmetic.
   float mx = -__builtin_inff();
-  for (int s = 0; s < nsp; ++s) mx = fmaxf(mx, part_ml[((size_t)b * nsp + s) * H + h].x);
+  for (int s0 = 0; s0 < nsp; s0 += kG) {
+    float2 ml[kG];
+#pragma unroll
+    for (int j = 0; j < kG; ++j) ml[j] = part_ml[((size_t)b * nsp + min(s0 + j, nsp - 1)) * H + h];
+#pragma unroll
+    for (int j = 0; j < kG; ++j) mx = fmaxf(mx, ml[j].x);          // clamped repeats change nothing
+  }
   float den = 0.f;
   f32x4_t o = f32x4_t{0.f, 0.f, 0.f, 0.f};
   if (mx != -__builtin_inff()) {
-    for (int s0 = 0; s0 < nsp; s0 += 8) {
-      f32x4_t v[8];
+    for (int s0 = 0; s0 < nsp; s0 += kG) {
+      f32x4_t v[kG];
+      float2 ml[kG];
 #pragma unroll
-      for (int j = 0; j < 8; ++j)        // the group's loads in flight together
-        if (s0 + j < nsp)
-          v[j] = *reinterpret_cast<const f32x4_t*>(part_o + (((size_t)b * nsp + s0 + j) * H + h) * kValV +
-                                                   4 * threadIdx.x);
+      for (int j = 0; j < kG; ++j) {
+        const size_t sj = (size_t)b * nsp + min(s0 + j, nsp - 1);
+        v[j] = *reinterpret_cast<const f32x4_t*>(part_o + (sj * H + h) * kValV + 4 * threadIdx.x);
+        ml[j] = part_ml[sj * H + h];
+      }
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        if (s0 + j < nsp) {
-          const float2 ml = part_ml[((size_t)b * nsp + s0 + j) * H + h];
-          const float wgt = exp2f(ml.x - mx);      // 0 for a span that saw nothing
-          den += wgt * ml.y;
+      for (int j = 0; j < kG; ++j) {
+        const float wgt = (s0 + j < nsp) ? exp2f(ml[j].x - mx) : 0.f;   // 0 also for a span that saw nothing
+        den += wgt * ml[j].y;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) o[e] += wgt * v[j][e];
-        }
+        for (int e = 0; e < 4; ++e) o[e] += wgt * v[j][e];
       }
     }
   }
@@ -308,7 +317,10 @@ extern "C" int ech_sparse_attn(const void* q, const void* dev_cache, int32_t C, 
       return ECH_EINVAL;
   }
   ECH_LAUNCH_CHECK();
-  hipLaunchKernelGGL(attn_merge_kernel, dim3(H, B), dim3(kValV / 4), 0, s, part_o, part_ml, H, nsp, out, lse);
+  if (nsp <= 8)
+    hipLaunchKernelGGL(attn_merge_kernel<8>, dim3(H, B), dim3(kValV / 4), 0, s, part_o, part_ml, H, nsp, out, lse);
+  else
+    hipLaunchKernelGGL(attn_merge_kernel<32>, dim3(H, B), dim3(kValV / 4), 0, s, part_o, part_ml, H, nsp, out, lse);
   ECH_LAUNCH_CHECK();
   return ECH_OK;
 }
