@@ -5,8 +5,9 @@
 // changes between steps. Rows are DeepSeek-V3.2-style absorbed MLA rows: 576
 // bf16 values, all of them the key and the first 512 the value.
 //
-// Work split. A workgroup takes one (sequence, token span) and every head:
-// each of its H/16 waves owns 16 heads. The span's rows are gathered 32
+// Work split. A workgroup takes one (sequence, token span) and every head
+// (or half of 128 heads when there are fewer workgroups than CUs): each of
+// its waves owns 16 heads. The span's rows are gathered 32
 // tokens at a time from HBM into LDS once for all heads, token-major for the
 // scores and transposed (value column-major) for the output product, so each
 // row crosses HBM once. Per 32-token tile and wave, on the matrix cores
@@ -120,9 +121,11 @@ __global__ void __launch_bounds__(NT, 1)
   int* lds_ok = reinterpret_cast<int*>(lds_v + kValV * kVPitch);
   constexpr int kP = (kTile * kChunks + NT - 1) / NT;
 
-  const int b = blockIdx.y, sp = blockIdx.x, nsp = gridDim.x;
+  // blockIdx.x = span * hsplit + head group (hsplit = H / heads per workgroup)
+  const int hsplit = H / (NT / 4);
+  const int b = blockIdx.y, sp = blockIdx.x / hsplit, nsp = gridDim.x / hsplit;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, col = lane & 15, grp = lane >> 4;
-  const int h = wave * 16 + col;                 // this lane's head (S^T column, O^T column)
+  const int h = (blockIdx.x % hsplit) * (NT / 4) + wave * 16 + col;   // this lane's head (S^T, O^T column)
   const int32_t* sel = sel_slot + (size_t)b * k;
   const int t_begin = sp * span, t_end = min(k, t_begin + span);
 
@@ -295,10 +298,15 @@ extern "C" int ech_sparse_attn(const void* q, const void* dev_cache, int32_t C, 
   float2* part_ml = reinterpret_cast<float2*>(static_cast<char*>(ws) + ((o + 255) & ~(size_t)255));
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   const float scale2 = sm_scale * 1.4426950408889634f;
-  const dim3 grid(nsp, B);
+  // With fewer workgroups than CUs (a few sequences), 128 heads go to two
+  // workgroups of 64 per span: twice the workgroups, rows read twice (one
+  // sequence: 36 -> 29 us). With more, one workgroup of 128 reads each row
+  // once and its 8 waves fill a CU.
+  const int hsplit = (H == 16 * kMaxWaves && B * nsp < 256) ? 2 : 1;
+  const dim3 grid(nsp * hsplit, B);
   const auto* qq = static_cast<const uint16_t*>(q);
   const auto* cc = static_cast<const uint4*>(dev_cache);
-  switch (H / 16) {
+  switch (H / 16 / hsplit) {
 #define ECH_ATTN_CASE(W)                                                                                      \
   case W:                                                                                                     \
     hipLaunchKernelGGL(attn_span_kernel<64 * W>, grid, dim3(64 * W), kLdsBytes, s, qq, cc, C, sel_slot, H, k, \
