@@ -177,15 +177,41 @@ def bench_decode(args, wl):
     lse_a = torch.empty((wl.B, Ha), dtype=torch.float32, device='cuda')
     ws_a = torch.empty(ech.ech_sparse_attn_ws_bytes(wl.B, Ha, wl.k), dtype=torch.uint8, device='cuda')
     sm = 1.0 / float(np.sqrt(192.0))
-    ech.ech_sparse_attn(qa, layer.dev_cache, layer.sel_slot, sm, out_a, lse_a, ws_a)
-    ea0, ea1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    ea0.record(s0)
-    for _ in range(args.steps):
+    if len(layer.chunks) == 1:
         ech.ech_sparse_attn(qa, layer.dev_cache, layer.sel_slot, sm, out_a, lse_a, ws_a)
-    ea1.record(s0)
-    torch.cuda.synchronize()
-    attn_us = ea0.elapsed_time(ea1) / args.steps * 1e3
-    n_sel = int((layer.sel_slot >= 0).sum().item())
+        ea0, ea1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        ea0.record(s0)
+        for _ in range(args.steps):
+            ech.ech_sparse_attn(qa, layer.dev_cache, layer.sel_slot, sm, out_a, lse_a, ws_a)
+        ea1.record(s0)
+        torch.cuda.synchronize()
+        attn_us = ea0.elapsed_time(ea1) / args.steps * 1e3
+        n_sel = int((layer.sel_slot >= 0).sum().item())
+        attn_note = 'the consumer of sel_slot, after the timed steps; not part of the step time'
+    else:
+        # Several chunks: a later chunk may evict an earlier chunk's tokens, so
+        # each chunk's attention runs inside the step, right after that
+        # chunk's FINAL recall (on_chunk), timed with events around it.
+        att_ev, n_sel_c = [], []
+
+        def consume(b0, b1, stream):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            ech.ech_sparse_attn(qa[b0:b1], layer.dev_cache, layer.sel_slot[b0:b1], sm, out_a[b0:b1],
+                                lse_a[b0:b1], ws_a, stream=stream)
+            e1.record(stream)
+            att_ev.append((e0, e1))
+            n_sel_c.append((layer.sel_slot[b0:b1] >= 0).sum())
+
+        n_att = 2
+        for s in range(n_att):
+            layer.step(qd[args.warmup + args.steps + s], on_chunk=consume)
+        torch.cuda.synchronize()
+        attn_us = sum(a.elapsed_time(b) for a, b in att_ev) / n_att * 1e3
+        n_sel = int(sum(int(x.item()) for x in n_sel_c) / n_att)
+        attn_note = ('the consumer of sel_slot, per sequence chunk right after its FINAL recall (a later chunk '
+                     'may evict an earlier chunk\'s tokens), in eager steps after the timed ones; not part of '
+                     'the step time')
 
     # Growing contexts: ech_kv_append of one decoded token per sequence, on a
     # scratch layout of the same batch (B sequences with room for K tokens)
@@ -279,7 +305,7 @@ def bench_decode(args, wl):
                       'frac': (n_sel * 1152 + wl.B * Ha * (576 * 2 + 512 * 4 + 4)) / (attn_us * 1e-6) / 1e9
                       / PEAK_HBM_GBS,
                       'mfma_bf16_frac': n_sel * Ha * (576 + 512) * 2 / (attn_us * 1e-6) / 1e12 / PEAK_BF16_TFLOPS,
-                      'note': 'the consumer of sel_slot, after the timed steps; not part of the step time'},
+                      'note': attn_note},
         'append': {'kernel': 'ech_kv_append', 'sequences': wl.B, 'us': append_us,
                    'bytes_per_call': wl.B * (1152 + 128 + 4),
                    'note': 'one decoded token per sequence: its row written over PCIe into the pinned pool, '
@@ -447,6 +473,42 @@ def cpu_baseline_decode(args, wl, ctx):
             'seconds': dt, 'host_cpus': len(os.sched_getaffinity(0))}
 
 
+def cpu_baseline_prefill(args, wl, ctx):
+    """The oracle as it stands, on a bounded sample of the prefill pass: the
+    first 128 rows of three query blocks (early, middle, last) - scores of
+    every visible token, exact top-k of each row, one union slot-map phase per
+    sampled block, recall of its rows. Scaled to (row, token) pairs per
+    second."""
+    import numpy as np
+    import oracle
+    import workloads as wk
+
+    keys, scale, pool = ctx['keys'], ctx['scale'], ctx['pool'].numpy()
+    nblk = (wl.N + wl.block_rows - 1) // wl.block_rows
+    blocks = sorted({1 % nblk, nblk // 2, nblk - 1})
+    rows_per = min(128, wl.block_rows)
+    sm = oracle.SlotMap(wl.N, wl.C)
+    cache = np.zeros((wl.C, pool.shape[1]), pool.dtype)
+    pairs = 0
+    t0 = time.perf_counter()
+    for bi in blocks:
+        r0 = bi * wl.block_rows
+        R = min(rows_per, wl.N - r0)
+        q = wk.prefill_queries(wl, r0, R)
+        w = wk.head_weights(wl, rows=R, row0=r0)
+        vis = r0 + 1 + np.arange(R)
+        L = [x.astype(np.float32) for x in oracle.index_logits(q, w, keys, wl.kdtype, scale, [0] * R, vis)]
+        idx, _ = oracle.topk_rows(L, wl.k)
+        a, _, _ = sm.prefill_block(0, idx)
+        oracle.recall_rows(pool, cache, a)
+        pairs += int(vis.sum())
+    dt = time.perf_counter() - t0
+    return {'value': pairs / dt, 'unit': 'pairs/s', 'cores': cpu_cores(), 'kind': 'oracle',
+            'sample': f'first {rows_per} rows of query blocks {blocks} ({pairs} (row, token) pairs scored, '
+                      f'selected and made resident), {dt:.1f} s; label: CPU oracle - reported baseline',
+            'seconds': dt, 'host_cpus': len(os.sched_getaffinity(0))}
+
+
 # ---------------------------------------------------------------------------- prefill
 def bench_prefill(args, wl):
     import numpy as np
@@ -529,7 +591,7 @@ def bench_prefill(args, wl):
                      'traffic_unit': 'bytes per pass (27 launches)',
                      'algorithmic_flops_per_pass': flops, 'logits_ms_per_pass': logits_ms_total},
         'stage_rooflines': stages,
-    }
+    }, dict(keys=keys, scale=scale, pool=pool)
 
 
 def main():
@@ -573,8 +635,12 @@ def main():
         else:
             out['cpu_baseline'] = None
     else:
-        out = bench_prefill(args, wl)
-        out['cpu_baseline'] = None
+        out, ctx = bench_prefill(args, wl)
+        if not args.no_cpu_baseline:
+            log('timing the CPU oracle on a sample')
+            out['cpu_baseline'] = cpu_baseline_prefill(args, wl, ctx)
+        else:
+            out['cpu_baseline'] = None
     print(json.dumps(out), flush=True)
 
 

@@ -47,5 +47,30 @@ def build(verbose: bool = False) -> str:
     return LIB
 
 
+def build_sanitized(verbose: bool = False) -> str:
+    """The host code of every source (entry points, argument checks,
+    workspace sizing), built with AddressSanitizer and UBSan on the host side
+    only (each -fsanitize flag is passed to the host compiler; device code is
+    built as usual) into _build/libech_san.so (not tracked). Loading it needs
+    the sanitizer runtime preloaded; the checks run with it launch no kernel."""
+    hipcc = os.environ.get('HIPCC', '/opt/rocm/bin/hipcc')
+    out_dir = os.path.join(ROOT, '_build')
+    os.makedirs(out_dir, exist_ok=True)
+    out = os.path.join(out_dir, 'libech_san.so')
+    cmd = [hipcc, f'--offload-arch={ARCH}', '-O1', '-g', '-std=c++17', '-shared', '-fPIC',
+           '-Xarch_host', '-fsanitize=address', '-Xarch_host', '-fsanitize=undefined',
+           '-Xarch_host', '-fno-omit-frame-pointer', '-shared-libsan',
+           '-Xclang', '-target-feature', '-Xclang', '-packed-fp32-ops',
+           '-I', os.path.join(ROOT, 'include'), '-I', os.path.join(HERE, 'csrc'),
+           *sources(), '-o', out]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        sys.stderr.write(r.stdout + r.stderr)
+        raise RuntimeError(f'hipcc (sanitized host build) failed with exit code {r.returncode}')
+    if verbose:
+        print(' '.join(cmd))
+    return out
+
+
 if __name__ == '__main__':
     print(build(verbose=True))

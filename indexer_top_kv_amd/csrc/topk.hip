@@ -734,8 +734,8 @@ __device__ __forceinline__ uint32_t wave_select(const int2* cl, int n, int need,
 template <int NT>
 __global__ __launch_bounds__(NT) void topk_resolve_kernel(const float* __restrict__ logits, int64_t ld,
                                                            const int32_t* __restrict__ lens, int k,
-                                                           const float* __restrict__ theta_in,
-                                                           float* __restrict__ theta_out, float* __restrict__ kth,
+                                                           const float* theta_in,
+                                                           float* theta_out, float* __restrict__ kth,
                                                            int32_t* __restrict__ idx, Ws ws) {
   extern __shared__ int2 cl[];                     // candidate list [cap]
   __shared__ int hist[256];
@@ -1002,8 +1002,8 @@ constexpr int kSmallCand = 4096;                  // boundary tokens listed for 
 
 __global__ __launch_bounds__(kSmallNT) void topk_small_kernel(const float* __restrict__ logits, int64_t ld,
                                                               const int32_t* __restrict__ lens, int k,
-                                                              const float* __restrict__ theta_in,
-                                                              float* __restrict__ theta_out,
+                                                              const float* theta_in,
+                                                              float* theta_out,
                                                               float* __restrict__ kth, int32_t* __restrict__ idx) {
   constexpr int NT = kSmallNT;
   __shared__ int2 cand[kSmallCand];   // (score bits, token) of the boundary tokens

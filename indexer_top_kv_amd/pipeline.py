@@ -179,7 +179,7 @@ class DecodeLayer:
 
     def step(self, q: Optional[torch.Tensor], marks: Optional[dict] = None,
              wait: Optional[torch.cuda.Event] = None, logits_done: Optional[torch.cuda.Event] = None,
-             scores: bool = True) -> None:
+             scores: bool = True, on_chunk=None) -> None:
         """Enqueue one decode step for query q [B, 64, 128] (bf16 bits) on the
         current stream (with S1 forked and joined inside). `marks`, when given,
         receives timing events recorded on the stream of each stage, as
@@ -189,7 +189,17 @@ class DecodeLayer:
         chunk). `wait`, when given, is an event the scores wait for;
         `logits_done` is recorded once they are written (one group only).
         scores=False leaves the scores out: the caller has launched them on
-        the current stream already (q is then unused)."""
+        the current stream already (q is then unused).
+
+        on_chunk(b0, b1, stream), when given, is called once per sequence
+        chunk, right after the chunk's FINAL recall is enqueued on `stream`:
+        work the caller enqueues there (the attention over sel_slot[b0:b1])
+        sees every selected token of sequences b0..b1-1 resident in the
+        slot sel_slot names. When the batch's selections exceed the cache
+        (several chunks), a later chunk's FINAL phase may evict an earlier
+        chunk's tokens, so an earlier chunk's sel_slot rows are only valid
+        until then: read them in on_chunk. With one chunk they stay valid
+        until the next step."""
         s0 = torch.cuda.current_stream()
         if wait is not None:
             s0.wait_event(wait)
@@ -207,6 +217,8 @@ class DecodeLayer:
             if logits_done is not None or not scores:
                 raise ValueError('logits_done and scores=False need the early fetch in one group')
             self._step_grouped(q, th, th_next, s0, mark)
+            if on_chunk is not None:
+                on_chunk(0, self.B, s0)
             self.parity ^= 1
             return
         if scores:
@@ -260,6 +272,8 @@ class DecodeLayer:
         mark('recall_final', s0)
         self._recall(ECH_FINAL, s0)
         mark('recall_final', s0)
+        if on_chunk is not None:
+            on_chunk(first_b0, first_b1, s0)
         for b0, b1 in self.chunks[1:]:
             for phase in ((ECH_EARLY, ECH_FINAL) if self.early else (ECH_FINAL,)):
                 name = 'early' if phase == ECH_EARLY else 'final'
@@ -269,6 +283,8 @@ class DecodeLayer:
                 mark('recall_' + name, s0)
                 self._recall(phase, s0)
                 mark('recall_' + name, s0)
+            if on_chunk is not None:
+                on_chunk(b0, b1, s0)
         mark('final', s0)
         self.parity ^= 1
 

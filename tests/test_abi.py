@@ -9,6 +9,8 @@ import pytest
 import indexer_top_kv_amd as ech
 from indexer_top_kv_amd import _native
 
+import abi_checks
+
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, 'include', 'ech.h')
 
@@ -56,100 +58,34 @@ def test_ws_sizes_monotone():
     assert lib.ech_cache_step_ws_bytes(7, 1, 1, 1, 1, 1, 1) == 0
 
 
-FAKE = 1 << 20  # never dereferenced: validation fails before any HIP call
+def test_argument_checks():
+    for fn in abi_checks.CHECKS:
+        fn(ech.lib())
 
 
-def test_index_logits_rejects_bad_args():
-    lib = ech.lib()
-    ok = dict(q=FAKE, w=FAKE, k=FAKE, dt=1, sc=FAKE, t0=FAKE, ln=FAKE, R=2, H=64, D=128, ml=100, out=FAKE, ld=100)
-
-    def call(**kw):
-        a = dict(ok, **kw)
-        return lib.ech_index_logits(a['q'], a['w'], a['k'], a['dt'], a['sc'], a['t0'], a['ln'], a['R'], a['H'],
-                                    a['D'], a['ml'], a['out'], a['ld'], None)
-    assert call(q=None) == -1
-    assert call(H=32) == -1
-    assert call(D=64) == -1
-    assert call(R=0) == -1
-    assert call(ld=50) == -1
-    assert call(dt=7) == -3
-    assert call(sc=None) == -1          # fp8 needs scales
-    assert call(q=FAKE + 4) == -1        # misaligned
-    assert call(ml=0) == 0               # nothing to do, nothing launched
+def _clang_rt(name):
+    import glob
+    hits = sorted(glob.glob(f'/opt/rocm/llvm/lib/clang/*/lib/linux/libclang_rt.{name}-x86_64.so'))
+    return hits[-1] if hits else None
 
 
-def test_topk_rejects_bad_args():
-    lib = ech.lib()
-    ws = lib.ech_topk_ws_bytes(4, 1000, 64)
-
-    def call(k=64, ld=1000, ml=1000, wsb=ws, ptr=FAKE, wsp=FAKE):
-        return lib.ech_topk(ptr, ld, FAKE, 4, ml, k, None, None, FAKE, FAKE, wsp, wsb, None)
-    assert call(k=0) == -1
-    assert call(k=5000) == -1
-    assert call(ld=999) == -1
-    assert call(ld=1002) == -1           # rows must stay 16-byte aligned
-    assert call(wsb=ws - 1) == -1
-    assert call(ptr=FAKE + 4) == -1
-    assert call(wsp=FAKE + 16) == -1     # workspace must be 256-byte aligned
-    assert call(ml=1 << 24) == -1
-
-
-def test_cache_step_rejects_bad_args():
-    lib = ech.lib()
-
-    def call(phase=1, B=2, R=2, k=64, ml=1000, C=1000, M=128, cap=8, P=4000, wsb=None, idx=FAKE):
-        wsz = lib.ech_cache_step_ws_bytes(phase, B, R, k, ml, C, M) if wsb is None else wsb
-        return lib.ech_cache_step(phase, FAKE, P, FAKE, FAKE, C, FAKE, M, FAKE, FAKE, FAKE, B, ml, idx, R, k,
-                                  FAKE, 1000, FAKE, cap, FAKE, FAKE, FAKE, wsz, None)
-    assert call(phase=5) == -1
-    assert call(C=100) == -2             # FINAL demand 2*64 > 100
-    assert call(phase=2, B=1, R=4, C=200) == -2   # PREFILL demand min(1000, 256) > 200
-    assert call(M=100) == -1             # miss list smaller than the demand
-    assert call(P=1 << 31) == -1
-    assert call(idx=None) == -1
-    assert call(phase=2, B=2) == -1      # PREFILL is one sequence
-    assert call(wsb=16) == -1
-    assert call(phase=0, M=15) == -1     # EARLY needs B*cap entries
-
-
-def test_recall_rejects_bad_args():
-    lib = ech.lib()
-    assert lib.ech_recall(1, FAKE, 10, 1150, FAKE, 10, FAKE, FAKE, 4, None) == -1   # row_bytes % 16
-    assert lib.ech_recall(1, None, 10, 1152, FAKE, 10, FAKE, FAKE, 4, None) == -1
-    assert lib.ech_recall(1, FAKE, 0, 1152, FAKE, 10, FAKE, FAKE, 4, None) == -1
-    assert lib.ech_recall(9, FAKE, 10, 1152, FAKE, 10, FAKE, FAKE, 4, None) == -1   # no such phase
-
-
-def test_early_group_calls_reject_bad_args():
-    lib = ech.lib()
-    assert lib.ech_early_ws_bytes(0, 10, 10, 10) == 0
-    a = lib.ech_early_ws_bytes(4, 131072, 260000, 2048)
-    b = lib.ech_early_ws_bytes(32, 131072, 260000, 16384)
-    assert 0 < a < b
-    ws = lib.ech_early_ws_bytes(2, 1000, 500, 64)
-
-    def begin(q=FAKE, dt=1, sc=FAKE, B=2, ml=1000, C=500, M=64, wsb=ws, wsp=FAKE):
-        return lib.ech_early_begin(q, FAKE, FAKE, dt, sc, FAKE, FAKE, B, ml, FAKE, FAKE, 4000, FAKE, C, FAKE, M,
-                                   FAKE, wsp, wsb, None)
-    assert begin(q=None) == -1
-    assert begin(dt=5) == -3
-    assert begin(sc=None) == -1
-    assert begin(q=FAKE + 8) == -1
-    assert begin(B=2000) == -1
-    assert begin(wsb=ws - 1) == -1
-    assert begin(wsp=FAKE + 64) == -1
-
-    def group(g=0, b0=0, b1=2, B=2, cap=32, M=64, ld=1000, lg=FAKE, wsb=ws):
-        return lib.ech_early_group(g, b0, b1, lg, ld, FAKE, cap, FAKE, FAKE, B, 1000, FAKE, 4000, FAKE, FAKE, 500,
-                                   FAKE, M, FAKE, FAKE, FAKE, wsb, None)
-    assert group(g=-1) == -1
-    assert group(g=96) == -1
-    assert group(b0=1, b1=1) == -1
-    assert group(b1=3) == -1
-    assert group(cap=33) == -1            # early miss list smaller than B * cap
-    assert group(ld=999) == -1
-    assert group(lg=FAKE + 4) == -1
-    assert group(wsb=16) == -1
-    assert lib.ech_recall_group(0, FAKE, 10, 1150, FAKE, 10, FAKE, 4, FAKE, FAKE, None) == -1   # row_bytes % 16
-    assert lib.ech_recall_group(99, FAKE, 10, 1152, FAKE, 10, FAKE, 4, FAKE, FAKE, None) == -1
-    assert lib.ech_recall_group(0, FAKE, 10, 1152, FAKE, 10, FAKE, 4, FAKE, FAKE + 16, None) == -1
+def test_argument_checks_under_asan_ubsan():
+    """The host code of every entry point (argument validation, workspace
+    sizing, status strings) built with AddressSanitizer and UBSan on the host
+    side, and run through the same checks: no sanitizer report."""
+    import subprocess
+    import sys
+    from indexer_top_kv_amd import build as b
+    rt = _clang_rt('asan')
+    if rt is None or not os.path.exists(os.environ.get('HIPCC', '/opt/rocm/bin/hipcc')):
+        pytest.skip('no hipcc or sanitizer runtime')
+    lib = b.build_sanitized()
+    env = dict(os.environ, LD_PRELOAD=rt, ASAN_OPTIONS='detect_leaks=0:abort_on_error=1',
+               UBSAN_OPTIONS='halt_on_error=1:print_stacktrace=1',
+               LD_LIBRARY_PATH=os.path.dirname(rt) + ':' + os.environ.get('LD_LIBRARY_PATH', ''))
+    r = subprocess.run([sys.executable, os.path.join(ROOT, 'tests', 'abi_checks.py'), lib], env=env,
+                       capture_output=True, text=True, timeout=300)
+    out = r.stdout + r.stderr
+    assert r.returncode == 0, out[-4000:]
+    assert 'abi checks ok' in r.stdout
+    assert 'AddressSanitizer' not in out and 'runtime error' not in out, out[-4000:]

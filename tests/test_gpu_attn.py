@@ -56,7 +56,10 @@ def _case(seed, B, H, C, k, pad_max, q_scale=1.0):
 
 
 @pytest.mark.parametrize('B,H,k,pad', [(3, 16, 37, 10), (2, 48, 64, 64), (4, 128, 2048, 1500), (1, 128, 5, 0),
-                                       (5, 64, 300, 299)])
+                                       (5, 64, 300, 299),
+                                       # two workgroups of 64 heads per span (fewer workgroups than CUs),
+                                       # several spans and tiles each
+                                       (1, 128, 2048, 0), (2, 128, 1024, 100)])
 def test_random_against_oracle(B, H, k, pad):
     need_gpu()
     q, cache, sel = _case(B * 100 + H + k, B, H, 4000, k, pad)
@@ -150,6 +153,58 @@ def test_lossless_through_the_cache():
         np.testing.assert_array_equal(o1, o2, err_msg=f'step {s}')
         np.testing.assert_array_equal(l1, l2, err_msg=f'step {s}')
         assert np.all(np.isfinite(l1))
+
+
+def test_lossless_through_the_cache_chunked():
+    """A batch whose selections exceed the cache runs in sequence chunks,
+    and a later chunk may evict an earlier chunk's tokens. The consumer reads
+    each chunk's sel_slot rows right after that chunk's FINAL recall
+    (DecodeLayer.step's on_chunk): there every selected token is resident in
+    the slot sel_slot names (slot2tok[sel_slot] == the selected token), and
+    attention through the device cache equals, bit for bit, attention over
+    the selected rows held whole in HBM."""
+    need_gpu()
+    from indexer_top_kv_amd.pipeline import DecodeLayer
+    wl = wk.CONFIGS['decode-64x110k-fp8-capacity'].scaled(B=6, N=5000, len_lo=3000, C=5000, k=1024, cap=128,
+                                                          resample_p=0.4)
+    keys, scale = wk.keys(wl)
+    w = wk.head_weights(wl)
+    rows = wk.host_rows(wl)
+    pool = torch.empty((wl.P, 576), dtype=torch.int16, pin_memory=True)
+    pool.numpy()[:] = rows.view(np.int16)
+    layer = DecodeLayer(dev(keys), dev(scale), dev(w), wl.tok0, wl.lens, wl.C, k=wl.k, cap=wl.cap, host_pool=pool)
+    assert len(layer.chunks) > 1
+    full = dev(rows)
+    r = np.random.default_rng(8)
+    H = 64
+    tok0_d = dev(wl.tok0)
+    for s, qi in enumerate(wk.decode_queries(wl, 4)):
+        qa = dev(wk.to_bf16_bits(r.standard_normal((wl.B, H, 576)).astype(np.float32)))
+        outs = {}
+
+        def consume(b0, b1, stream):
+            with torch.cuda.stream(stream):
+                sel = layer.sel_slot[b0:b1]
+                n = b1 - b0
+                o = torch.empty((n, H, 512), dtype=torch.float32, device='cuda')
+                l = torch.empty((n, H), dtype=torch.float32, device='cuda')
+                ws = torch.empty(ech.ech_sparse_attn_ws_bytes(n, H, wl.k), dtype=torch.uint8, device='cuda')
+                ech.ech_sparse_attn(qa[b0:b1], layer.dev_cache, sel, 0.07, o, l, ws, stream=stream)
+                # residency of what the consumer read, at the time it read it
+                held = torch.where(sel >= 0, layer.state.slot2tok[sel.clamp(min=0).long()], -1)
+                want = torch.where(layer.idx[b0:b1] >= 0, layer.idx[b0:b1] + tok0_d[b0:b1, None], -1)
+                outs[(b0, b1)] = (o, l, held.clone(), want.clone(), layer.idx[b0:b1].clone())
+
+        layer.step(dev(qi), on_chunk=consume)
+        torch.cuda.synchronize()
+        assert sorted(outs) == layer.chunks
+        for (b0, b1), (o, l, held, want, idx_c) in outs.items():
+            np.testing.assert_array_equal(host(held), host(want), err_msg=f'step {s} chunk {b0}:{b1}')
+            idx = host(idx_c)
+            g = np.where(idx >= 0, idx + wl.tok0[b0:b1, None], -1).astype(np.int32)
+            o2, l2 = _run(qa[b0:b1], full, dev(g), 0.07)
+            np.testing.assert_array_equal(host(o), o2, err_msg=f'step {s} chunk {b0}:{b1}')
+            np.testing.assert_array_equal(host(l), l2, err_msg=f'step {s} chunk {b0}:{b1}')
 
 
 def test_captured_attention_follows_the_index_tensor():

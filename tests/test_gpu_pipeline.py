@@ -171,3 +171,48 @@ def test_normal_decode_full_size_single_sequence():
         assert np.all(t2s[s2t[occ]] == occ)
         np.testing.assert_array_equal(host(layer.dev_cache)[occ], pool.numpy()[s2t[occ]])
         np.testing.assert_array_equal(host(layer.sel_slot)[0], t2s[idx])
+
+
+def test_cache_reset_mid_run_changes_only_residency():
+    """The host pool holds every row and nothing is written back (ECHO
+    explainer, "One layer, one step"), so dropping the device maps between
+    two decode steps (ech_cache_reset, threshold kept) loses nothing: the
+    scores, selections, k-th scores and thresholds of every later step are
+    those of a run without the reset; only residency changes (the next step
+    misses what was resident). The reset run is compared bit for bit with the
+    oracle run reset at the same step (a fresh slot map)."""
+    need_gpu()
+    import indexer_top_kv_amd as ech
+    wl = wk.CONFIGS['decode-32x128k-fp8'].scaled(B=4, N=9000, C=20000, steps=5, variant='dyadic')
+    keys, scale, w, pool, plain = _setup(wl)
+    reset = DecodeLayer(dev(keys), dev(scale), dev(w), wl.tok0, wl.lens, wl.C, k=wl.k, cap=wl.cap, host_pool=pool)
+    ref = OracleDecode(wl, keys, scale, w, pool.numpy().copy())
+    RESET_AT = 2
+    for s, q in enumerate(wk.decode_queries(wl, 5)):
+        if s == RESET_AT:
+            ech.ech_cache_reset(reset.state)
+            ref.sm = oracle.SlotMap(wl.P, wl.C)
+        qd = dev(q)
+        plain.step(qd)
+        reset.step(qd)
+        torch.cuda.synchronize()
+        L, idx, kth, sel, est, fst = ref.step(q)
+        for t in ('logits', 'idx', 'kth'):
+            np.testing.assert_array_equal(host(getattr(reset, t)), host(getattr(plain, t)), err_msg=f'{t} step {s}')
+        np.testing.assert_array_equal(host(reset.theta_current), host(plain.theta_current))
+        np.testing.assert_array_equal(host(reset.idx), idx, err_msg=f'step {s}')
+        np.testing.assert_array_equal(host(reset.sel_slot), sel, err_msg=f'step {s}')
+        np.testing.assert_array_equal(host(reset.stats_early), est, err_msg=f'step {s}')
+        np.testing.assert_array_equal(host(reset.stats_final), fst, err_msg=f'step {s}')
+        np.testing.assert_array_equal(host(reset.state.tok2slot), ref.sm.tok2slot, err_msg=f'step {s}')
+        assert int(host(reset.state.ctr)[0]) == ref.sm.head
+        assert int(host(reset.state.ctr)[5]) == 0
+        occ = ref.sm.resident()
+        np.testing.assert_array_equal(host(reset.dev_cache)[occ], pool.numpy()[ref.sm.slot2tok[occ]])
+        if s == RESET_AT:
+            # nothing was resident: no early hits, and the final hits are
+            # only tokens this step's early fetch brought in
+            est_r, fst_r = host(reset.stats_early), host(reset.stats_final)
+            assert np.all(est_r[:, 0] == 0)
+            assert np.all(fst_r[:, 0] <= est_r[:, 1])
+            assert host(plain.stats_final)[:, 0].sum() > fst_r[:, 0].sum()
