@@ -27,7 +27,9 @@
  *  - Ownership: the caller owns every buffer (device memory, the pinned host
  *    pool, workspaces) and the stream. The library allocates nothing, keeps no
  *    global state and is re-entrant; per-layer state is a set of caller
- *    buffers, so L layers are L buffer sets.
+ *    buffers, so L layers are L buffer sets. The one exception is
+ *    ech_topk_noalloc, whose workspace is a static per-GPU array inside the
+ *    library (for callers that cannot allocate).
  *  - Pointers are device pointers unless stated. bf16 = uint16 bit patterns;
  *    fp8 = OCP e4m3fn bytes. Row-major throughout.
  *  - Asynchrony: every call only enqueues kernels on `stream` (a hipStream_t,
@@ -57,6 +59,7 @@ extern "C" {
 #define ECH_ENOSPC       -2   /* host-known FINAL demand exceeds the cache size C */
 #define ECH_EUNSUPPORTED -3   /* key dtype or device architecture not supported */
 #define ECH_EHIP         -4   /* a HIP call or kernel launch failed */
+#define ECH_ESCRATCH     -5   /* the call needs more than the library's static scratch array holds */
 
 /* ---- key dtypes */
 #define ECH_KEY_BF16 0        /* keys [P, D] bf16, no scale */
@@ -89,7 +92,7 @@ extern "C" {
 /* Human-readable name of a return code. */
 const char* ech_status_str(int code);
 
-/* Library ABI version (major*100 + minor); 101 adds the grouped early-fetch calls. */
+/* Library ABI version (major*100 + minor); 102 adds ech_topk_noalloc. */
 int ech_version(void);
 
 /*
@@ -159,6 +162,26 @@ size_t ech_topk_ws_bytes(int R, int max_len, int k);
 int ech_topk(const float* logits, int64_t ld, const int32_t* row_len, int R, int max_len, int k,
              const float* theta_in, float* theta_out, int32_t* idx, float* kth,
              void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * ech_topk_noalloc - ech_topk for callers that cannot allocate device memory
+ * (code under hipGraph capture, tight serving loops, harnesses that forbid
+ * allocation). Same arguments, results and errors as ech_topk, without ws:
+ * the workspace is a static device array of ECH_TOPK_SCRATCH_BYTES inside the
+ * library, one copy per GPU, held until the process ends. Its device address
+ * is looked up once per device, on the first call with that device current;
+ * no call allocates or frees memory. Contents left by earlier calls do not
+ * matter (nothing needs to start at zero).
+ *  ECH_ESCRATCH if ech_topk_ws_bytes(R, max_len, k) > ECH_TOPK_SCRATCH_BYTES
+ *  (16 MiB: enough for 64 rows of 131072 tokens or 4 rows of 1M tokens at
+ *  k = 2048; a 4096-row prefill block needs ech_topk with a workspace).
+ *  Every call on one GPU uses the same array: calls on one GPU that may
+ *  overlap in time (different streams without ordering between them) race
+ *  and give wrong results; order them.
+ */
+#define ECH_TOPK_SCRATCH_BYTES (16u << 20)
+int ech_topk_noalloc(const float* logits, int64_t ld, const int32_t* row_len, int R, int max_len, int k,
+                     const float* theta_in, float* theta_out, int32_t* idx, float* kth, void* stream);
 
 /*
  * ech_cache_reset - clear one layer's slot-map state: tok2slot[0..P) = -1,

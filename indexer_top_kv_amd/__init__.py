@@ -19,7 +19,7 @@ from ._native import (ECH_EARLY, ECH_FINAL, ECH_PREFILL, ECH_KEY_BF16, ECH_KEY_F
                       CTR_HEAD, CTR_EPOCH, CTR_NMISS, CTR_NEVICT, CTR_RECALLED, CTR_STATUS, CTR_NWANT,
                       CTR_NPINNED, CTR_NMISS_EARLY, CTR_TICKET, CTR_LEN, ST_OVERFLOW, ST_BADTOK, ST_BADMISS, ST_FULL)
 
-__all__ = ['ech_kv_append', 'ech_sparse_attn', 'ech_sparse_attn_ws_bytes', 'ech_index_logits', 'ech_index_logits_causal', 'ech_topk', 'ech_topk_ws_bytes', 'ech_cache_reset',
+__all__ = ['ech_kv_append', 'ech_sparse_attn', 'ech_sparse_attn_ws_bytes', 'ech_index_logits', 'ech_index_logits_causal', 'ech_topk', 'ech_topk_noalloc', 'ech_topk_ws_bytes', 'ech_cache_reset',
            'ech_cache_step', 'ech_cache_step_ws_bytes', 'ech_recall', 'ech_early_ws_bytes', 'ech_early_begin',
            'ech_early_group', 'ech_recall_group', 'EchError', 'LayerState', 'lib']
 
@@ -92,6 +92,15 @@ def ech_topk(logits, row_len, max_len: int, k: int, theta_in, theta_out, idx, kt
     _check('ech_topk', lib().ech_topk(
         _ptr(logits), logits.stride(0), _ptr(row_len), R, int(max_len), int(k), _ptr(theta_in), _ptr(theta_out),
         _ptr(idx), _ptr(kth), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def ech_topk_noalloc(logits, row_len, max_len: int, k: int, theta_in, theta_out, idx, kth, stream=None) -> None:
+    """ech_topk with the library's static per-GPU scratch array as its
+    workspace (allocates nothing; calls on one GPU must not overlap)."""
+    R = logits.shape[0]
+    _check('ech_topk_noalloc', lib().ech_topk_noalloc(
+        _ptr(logits), logits.stride(0), _ptr(row_len), R, int(max_len), int(k), _ptr(theta_in), _ptr(theta_out),
+        _ptr(idx), _ptr(kth), _stream(stream)))
 
 
 # ------------------------------------------------------------------ stage 3

@@ -14,6 +14,8 @@ ECH_EINVAL = -1
 ECH_ENOSPC = -2
 ECH_EUNSUPPORTED = -3
 ECH_EHIP = -4
+ECH_ESCRATCH = -5
+ECH_TOPK_SCRATCH_BYTES = 16 << 20
 
 ECH_KEY_BF16 = 0
 ECH_KEY_FP8 = 1
@@ -46,6 +48,8 @@ SIGNATURES = {
     'ech_topk_ws_bytes': (_sz, [ctypes.c_int, ctypes.c_int, ctypes.c_int]),
     'ech_topk': (ctypes.c_int, [_p, _i64, _p, ctypes.c_int, ctypes.c_int, ctypes.c_int, _p, _p, _p, _p, _p, _sz,
                                 _p]),
+    'ech_topk_noalloc': (ctypes.c_int, [_p, _i64, _p, ctypes.c_int, ctypes.c_int, ctypes.c_int, _p, _p, _p, _p,
+                                        _p]),
     'ech_cache_reset': (ctypes.c_int, [_p, _i64, _p, _p, _i32, _p, _p]),
     'ech_cache_step_ws_bytes': (_sz, [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, _i32,
                                       _i32]),

@@ -8,8 +8,9 @@ extern "C" const char* ech_status_str(int code) {
     case ECH_ENOSPC: return "selection demand exceeds the device cache size";
     case ECH_EUNSUPPORTED: return "unsupported key dtype or device";
     case ECH_EHIP: return "HIP launch or runtime error";
+    case ECH_ESCRATCH: return "the call needs more than the static scratch array holds";
     default: return "unknown error code";
   }
 }
 
-extern "C" int ech_version(void) { return 101; }   // 1.1: grouped early-fetch entry points
+extern "C" int ech_version(void) { return 102; }   // 1.2: ech_topk_noalloc

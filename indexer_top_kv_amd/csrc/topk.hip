@@ -33,6 +33,7 @@
 // around the threshold), so the row is read twice (T1, T3).
 
 #include <algorithm>
+#include <mutex>
 
 #include "common.hpp"
 
@@ -1183,14 +1184,20 @@ extern "C" size_t ech_topk_ws_bytes(int R, int max_len, int k) {
   return layout(R, max_len, k, nullptr, nullptr);
 }
 
-extern "C" int ech_topk(const float* logits, int64_t ld, const int32_t* row_len, int R, int max_len, int k,
-                        const float* theta_in, float* theta_out, int32_t* idx, float* kth, void* ws,
-                        size_t ws_bytes, void* stream) {
-  if (!logits || !row_len || !idx || !kth || !ws) return ECH_EINVAL;
-  if (R < 1 || R > 65535 || k < 1 || k > kMaxK || max_len < 0 || ld < max_len) return ECH_EINVAL;
-  if ((int64_t)max_len > (int64_t)kChunk * kMaxChunks) return ECH_EINVAL;
-  if (ld % 4 != 0 || !aligned16(logits) || (reinterpret_cast<uintptr_t>(ws) & 255u)) return ECH_EINVAL;
-  if (ws_bytes < ech_topk_ws_bytes(R, max_len, k)) return ECH_EINVAL;
+namespace {
+
+// Arguments of ech_topk other than the workspace.
+bool topk_args_ok(const float* logits, int64_t ld, const int32_t* row_len, int R, int max_len, int k,
+                  const int32_t* idx, const float* kth) {
+  if (!logits || !row_len || !idx || !kth) return false;
+  if (R < 1 || R > 65535 || k < 1 || k > kMaxK || max_len < 0 || ld < max_len) return false;
+  if ((int64_t)max_len > (int64_t)kChunk * kMaxChunks) return false;
+  return ld % 4 == 0 && aligned16(logits);
+}
+
+// The launches of one ech_topk call on a checked workspace.
+int topk_launch(const float* logits, int64_t ld, const int32_t* row_len, int R, int max_len, int k,
+                const float* theta_in, float* theta_out, int32_t* idx, float* kth, void* ws, void* stream) {
   Ws w;
   layout(R, max_len, k, &w, static_cast<char*>(ws));
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
@@ -1231,4 +1238,63 @@ extern "C" int ech_topk(const float* logits, int64_t ld, const int32_t* row_len,
   hipLaunchKernelGGL(topk_compact_kernel, dim3(gx, R), dim3(kT), 0, s, logits, ld, row_len, k, idx, w);
   ECH_LAUNCH_CHECK();
   return ECH_OK;
+}
+
+}  // namespace
+
+extern "C" int ech_topk(const float* logits, int64_t ld, const int32_t* row_len, int R, int max_len, int k,
+                        const float* theta_in, float* theta_out, int32_t* idx, float* kth, void* ws,
+                        size_t ws_bytes, void* stream) {
+  if (!topk_args_ok(logits, ld, row_len, R, max_len, k, idx, kth)) return ECH_EINVAL;
+  if (!ws || (reinterpret_cast<uintptr_t>(ws) & 255u)) return ECH_EINVAL;
+  if (ws_bytes < ech_topk_ws_bytes(R, max_len, k)) return ECH_EINVAL;
+  return topk_launch(logits, ld, row_len, R, max_len, k, theta_in, theta_out, idx, kth, ws, stream);
+}
+
+// ------------------------------------------------------------------ no allocation
+// The workspace of ech_topk_noalloc: a static device array, one per GPU the
+// library runs on (held until the process ends). In host code `scratch`
+// names a host-side stand-in, not the device address: the device address of
+// each GPU's copy is looked up once per device (hipGetSymbolAddress, with
+// that device current) and only that address is passed to kernels.
+namespace {
+
+constexpr size_t kScratchBytes = ECH_TOPK_SCRATCH_BYTES;
+__device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_dev[kMaxDevices] = {};
+
+// Device address of the current device's scratch array; ECH_EHIP if the
+// device or the symbol lookup fails.
+int scratch_of_current_device(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    (void)hipGetLastError();
+    return ECH_EHIP;
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_dev[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) {
+      (void)hipGetLastError();
+      return ECH_EHIP;
+    }
+    g_scratch_dev[dev] = p;
+  }
+  *out = g_scratch_dev[dev];
+  return ECH_OK;
+}
+
+}  // namespace
+
+extern "C" int ech_topk_noalloc(const float* logits, int64_t ld, const int32_t* row_len, int R, int max_len, int k,
+                                const float* theta_in, float* theta_out, int32_t* idx, float* kth, void* stream) {
+  if (!topk_args_ok(logits, ld, row_len, R, max_len, k, idx, kth)) return ECH_EINVAL;
+  if (ech_topk_ws_bytes(R, max_len, k) > kScratchBytes) return ECH_ESCRATCH;
+  void* ws = nullptr;
+  const int rc = scratch_of_current_device(&ws);
+  if (rc != ECH_OK) return rc;
+  return topk_launch(logits, ld, row_len, R, max_len, k, theta_in, theta_out, idx, kth, ws, stream);
 }

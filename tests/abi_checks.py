@@ -107,6 +107,20 @@ def check_early_group_calls_reject_bad_args(lib):
     assert lib.ech_recall_group(0, FAKE, 10, 1152, FAKE, 10, FAKE, 4, FAKE, FAKE + 16, None) == -1
 
 
+def check_topk_noalloc_rejects_bad_args(lib):
+    def call(R=4, ml=1000, k=64, ld=1000, ptr=FAKE):
+        return lib.ech_topk_noalloc(ptr, ld, FAKE, R, ml, k, None, None, FAKE, FAKE, None)
+    assert call(k=0) == -1
+    assert call(k=5000) == -1
+    assert call(ld=999) == -1
+    assert call(ptr=FAKE + 4) == -1
+    assert call(ptr=None) == -1
+    # a 4096-row prefill block needs more than the static array: -5, before any HIP call
+    assert lib.ech_topk_ws_bytes(4096, 110000, 2048) > (16 << 20)
+    assert call(R=4096, ml=110000, k=2048, ld=110016) == -5
+    assert lib.ech_topk_ws_bytes(64, 131072, 2048) <= (16 << 20)
+
+
 CHECKS = [v for k, v in sorted(globals().items()) if k.startswith('check_')]
 
 

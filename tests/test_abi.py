@@ -40,9 +40,9 @@ def test_library_exports_every_declared_symbol():
 
 def test_status_strings_and_version():
     lib = ech.lib()
-    assert lib.ech_version() == 101
+    assert lib.ech_version() == 102
     assert lib.ech_status_str(0) == b'ok'
-    for code in (-1, -2, -3, -4):
+    for code in (-1, -2, -3, -4, -5):
         assert b'unknown' not in lib.ech_status_str(code)
 
 
