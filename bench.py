@@ -44,8 +44,9 @@ def parse():
     p.add_argument('--no-early', action='store_true', help='disable the early fetch (ablation)')
     p.add_argument('--eager', action='store_true', help='time eager launches instead of graph replays')
     p.add_argument('--topk-after-early', action='store_true', help='start the top-k after the EARLY maps')
-    p.add_argument('--early-groups', type=int, default=0,
-                   help='sequence groups of the early fetch (0: one EARLY phase after all scores)')
+    p.add_argument('--no-fused', action='store_true',
+                   help='decode: the plain scores kernel, then the EARLY phase on a second stream (ablation of the '
+                        'fused scores + early-fetch launch)')
     p.add_argument('--prefill-serial', action='store_true',
                    help='prefill: one score buffer, top-k after each block on the same stream (ablation)')
     p.add_argument('--cpu-seqs', type=int, default=32, help='sequences in the oracle sample')
@@ -116,7 +117,7 @@ def bench_decode(args, wl):
     layer = DecodeLayer(kc, ks, wd, wl.tok0, wl.lens, wl.C, k=wl.k, cap=wl.cap, host_pool=pool,
                         early=not args.no_early, topk_after_early=args.topk_after_early,
                         topk_first={'auto': None, 'on': True, 'off': False}[args.topk_first],
-                        early_groups=args.early_groups)
+                        fused=False if (args.no_fused or args.no_early) else None)
     torch.cuda.synchronize()
     log(f'chunks {layer.chunks}; warm-up {args.warmup} steps')
     for s in range(args.warmup):
@@ -266,7 +267,7 @@ def bench_decode(args, wl):
         'data': 'synthetic, seeded',
         'config': {'workload': wl.name, 'B': wl.B, 'context': wl.N, 'k': wl.k, 'heads': 64, 'head_dim': 128,
                    'key_dtype': wl.kdtype, 'cache_slots': wl.C, 'early_fetch_cap': wl.cap,
-                   'early_fetch': not args.no_early, 'early_groups': len(layer.groups), 'row_bytes': 1152,
+                   'early_fetch': not args.no_early, 'fused_scores_early_fetch': layer.fused, 'row_bytes': 1152,
                    'launch': 'eager' if args.eager else 'hipGraph replay per step',
                    'topk_first': layer.topk_first},
         'roofline': {'bound': 'hbm', 'kernel': 'logits_decode_fp8_kernel' if wl.kdtype == 'fp8' else 'logits_decode_kernel',

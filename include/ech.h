@@ -12,7 +12,8 @@
  *      with a 256-bin histogram keyed by the high byte of (score - theta), theta
  *      being an EMA (alpha = 0.5) of the previous step's k-th score.
  *   3. ech_cache_step: GPU-resident per-layer slot map. EARLY (decode): fetch
- *      tokens scoring above theta, up to a cap, before the top-k is known.
+ *      tokens scoring above theta, up to a cap, before the top-k is known
+ *      (ech_index_logits_early: fused with the scores, for fp8 keys).
  *      FINAL: pin the selected resident tokens, give every selected miss a
  *      slot in ring order (evicting lazily freed tokens, no write-back).
  *      PREFILL: FINAL over the union of a query block's selections.
@@ -81,6 +82,7 @@ extern "C" {
 #define ECH_CTR_NPINNED   7   /* slots pinned by the last phase */
 #define ECH_CTR_NMISS_EARLY 8 /* entries written to the miss list by the last EARLY phase */
 #define ECH_CTR_TICKET    9   /* reserved: stays 0 */
+#define ECH_CTR_NCOPIED_EARLY 10 /* leading EARLY miss-list entries already copied (by ech_index_logits_early) */
 #define ECH_CTR_LEN      16
 
 /* ---- sticky status bits in ctr[ECH_CTR_STATUS] */
@@ -88,11 +90,13 @@ extern "C" {
 #define ECH_ST_BADTOK     2   /* a selected token offset was outside [0, len) */
 #define ECH_ST_BADMISS    4   /* ech_recall saw a miss entry with g >= P or slot >= C */
 #define ECH_ST_FULL       8   /* ech_kv_append found a sequence at its capacity */
+#define ECH_ST_TIMEOUT   16   /* a bounded wait inside ech_index_logits_early ran out (results invalid) */
 
 /* Human-readable name of a return code. */
 const char* ech_status_str(int code);
 
-/* Library ABI version (major*100 + minor); 102 adds ech_topk_noalloc. */
+/* Library ABI version (major*100 + minor); 200: the grouped early-fetch calls gave way to
+   ech_index_logits_early; ech_topk_noalloc. */
 int ech_version(void);
 
 /*
@@ -250,7 +254,9 @@ int ech_cache_step(int phase, int32_t* tok2slot, int64_t P, int32_t* slot2tok, i
  * one step: free -> allocate -> recall"; the host pool holds every row).
  * For m < n: dev_cache[miss[2m+1]] = host_pool[miss[2m]], row_bytes each,
  * where n = ctr[ECH_CTR_NMISS_EARLY] for phase ECH_EARLY and ctr[ECH_CTR_NMISS]
- * otherwise; `miss` is the list that phase wrote. Rows are read directly over
+ * otherwise; `miss` is the list that phase wrote. Phase ECH_EARLY starts at
+ * m = ctr[ECH_CTR_NCOPIED_EARLY] (rows ech_index_logits_early already
+ * copied; 0 after ech_cache_step). Rows are read directly over
  * PCIe by a gather kernel (zero-copy). A FINAL recall must be ordered after
  * the EARLY recall of the same step (it may reuse a slot the EARLY phase
  * filled).
@@ -264,55 +270,48 @@ int ech_recall(int phase, const void* host_pool, int64_t P, int64_t row_bytes, v
                const int32_t* miss, int32_t* ctr, int32_t M_max, void* stream);
 
 /*
- * Early fetch in sequence groups (decode) - the ECH_EARLY phase of
- * ech_cache_step, computed so that the early rows of the first sequences can
- * cross PCIe while the scores of later sequences are still being computed
- * (ECHO explainer, "Decode: fetch above a predicted threshold": the early
- * fetch hides the dependency of the recall on the top-k). The maps, the miss
- * list, ctr and stats end up exactly as after one ECH_EARLY phase over all B
- * sequences with the same scores, whatever the grouping:
+ * ech_index_logits_early - decode scores fused with the early fetch (ECHO
+ * explainer, "Decode: fetch above a predicted threshold": tokens scoring above
+ * the predicted threshold are fetched before the exact top-k is known, hiding
+ * the recall's dependency on the top-k; "Fused indexer kernel (extends
+ * DeepGEMM)": the scores and the prefetch in one kernel).
  *
- *   ech_early_begin   once per step, before any group; needs no scores. It
- *                     scores the tokens resident at the start of the step with
- *                     the arithmetic of ech_index_logits (the same bit
- *                     patterns), pins those above theta (strict; none for a
- *                     NaN theta), writes stats[b*4+0] (hits; the other three
- *                     fields are zeroed) and ranks the unpinned slots in ring
- *                     order from the head.
- *   ech_early_group   for consecutive groups [b0, b1) in ascending order,
- *                     group = 0, 1, ...; each after its rows of `logits` are
- *                     written (ech_index_logits on those rows). Allocates the
- *                     group's misses (the first `cap` non-resident tokens above
- *                     theta per sequence, ascending), continuing the ring
- *                     order; writes stats[b*4+1..3] of its sequences, the miss
- *                     list entries of its rank range, ctr[ECH_CTR_NMISS_EARLY]
- *                     (entries so far), head and evictions.
- *   ech_recall_group  copies the rows of one group's rank range (after that
- *                     group's ech_early_group; groups' recalls may overlap each
- *                     other and later groups' allocation).
+ * Results: exactly those of ech_index_logits(q, ..., logits, ld) followed by
+ * ech_cache_step(ECH_EARLY) over sequences [e0, e1) with the same scores,
+ * theta and cap (maps, pins, early miss list, ctr, stats[e0..e1)); the rows
+ * of a leading part of the early miss list are also copied into dev_cache
+ * (ctr[ECH_CTR_NCOPIED_EARLY] of them, added to ctr[ECH_CTR_RECALLED]);
+ * ech_recall(ECH_EARLY, ...) afterwards copies the rest. The allocation of a
+ * sequence's early misses and the PCIe copy of their rows start while later
+ * sequences are still being scored.
  *
- * All calls of one step use the same ws (ech_early_ws_bytes(B, max_len, C,
- * M_early) bytes, 256-byte aligned, uninitialised OK) and the same B,
- * max_len, C, M_early; the calls of one step must be ordered (stream or
- * events) except as stated for the recalls, and the FINAL phase of the step
- * must follow every group (ech_early_group) and, before its own recall, every
- * group's recall. M_early >= B * min(cap, max_len); group < 96; B <= 1024.
- * Arguments have the meaning they have for ech_index_logits and
- * ech_cache_step(ECH_EARLY); miss_early is the EARLY miss list [M_early, 2].
+ *  q, w, kcache, kscale, row_tok0, row_len, R, H, D, max_len, logits, ld:
+ *            as ech_index_logits (R sequences, one query row each); fp8 keys
+ *            only (ECH_EUNSUPPORTED otherwise); R <= 1024.
+ *  e0, e1    the sequences whose early fetch runs (0 <= e0 < e1 <= R): a
+ *            chunk of the batch when its selections do not fit the cache.
+ *  theta [R], cap (<= 4096), tok2slot, P, slot2tok, slot_pin, C, ctr, stats [R, 4]:
+ *            as ech_cache_step(ECH_EARLY), indexed by absolute sequence.
+ *  miss_early [M_early, 2], M_early >= (e1 - e0) * min(cap, max_len); 8-byte
+ *            aligned; overwritten ((-1, -1) where unused).
+ *  host_pool [P, row_bytes] pinned, device-mapped (host pointer); dev_cache
+ *            [C, row_bytes]; row_bytes a multiple of 16, at most 32768.
+ *  ws        ech_index_logits_early_ws_bytes(R, max_len, M_early) bytes,
+ *            256-byte aligned, zero-filled before the first call; the calls
+ *            keep it ready for the next one (after ECH_ST_TIMEOUT, zero it
+ *            again). Calls with the same ws must be ordered.
+ * The launch's workgroups wait on one another within the launch, with bounded
+ * waits: if one runs out, ECH_ST_TIMEOUT is set in ctr[ECH_CTR_STATUS] and the
+ * results of the call are not valid.
  */
-size_t ech_early_ws_bytes(int B, int max_len, int32_t C, int32_t M_early);
-int ech_early_begin(const void* q, const float* w, const void* kcache, int kdtype, const float* kscale,
-                    const int64_t* seq_tok0, const int32_t* seq_len, int B, int max_len, const float* theta,
-                    const int32_t* tok2slot, int64_t P, int32_t* slot_pin, int32_t C, int32_t* ctr,
-                    int32_t M_early, int32_t* stats, void* ws, size_t ws_bytes, void* stream);
-int ech_early_group(int group, int b0, int b1, const float* logits, int64_t ld, const float* theta, int cap,
-                    const int64_t* seq_tok0, const int32_t* seq_len, int B, int max_len,
-                    int32_t* tok2slot, int64_t P, int32_t* slot2tok, int32_t* slot_pin, int32_t C,
-                    int32_t* miss_early, int32_t M_early, int32_t* ctr, int32_t* stats,
-                    void* ws, size_t ws_bytes, void* stream);
-int ech_recall_group(int group, const void* host_pool, int64_t P, int64_t row_bytes, void* dev_cache,
-                     int32_t C, const int32_t* miss_early, int32_t M_early, int32_t* ctr, const void* ws,
-                     void* stream);
+size_t ech_index_logits_early_ws_bytes(int R, int max_len, int32_t M_early);
+int ech_index_logits_early(const void* q, const float* w, const void* kcache, int kdtype, const float* kscale,
+                           const int64_t* row_tok0, const int32_t* row_len, int R, int H, int D, int max_len,
+                           float* logits, int64_t ld, int e0, int e1, const float* theta, int cap,
+                           int32_t* tok2slot, int64_t P, int32_t* slot2tok, int32_t* slot_pin, int32_t C,
+                           int32_t* miss_early, int32_t M_early, int32_t* ctr, int32_t* stats,
+                           const void* host_pool, int64_t row_bytes, void* dev_cache, void* ws, size_t ws_bytes,
+                           void* stream);
 
 /*
  * ech_sparse_attn - the consumer of sel_slot: softmax attention of each head

@@ -17,11 +17,12 @@ import torch
 from . import _native
 from ._native import (ECH_EARLY, ECH_FINAL, ECH_PREFILL, ECH_KEY_BF16, ECH_KEY_FP8,  # noqa: F401
                       CTR_HEAD, CTR_EPOCH, CTR_NMISS, CTR_NEVICT, CTR_RECALLED, CTR_STATUS, CTR_NWANT,
-                      CTR_NPINNED, CTR_NMISS_EARLY, CTR_TICKET, CTR_LEN, ST_OVERFLOW, ST_BADTOK, ST_BADMISS, ST_FULL)
+                      CTR_NPINNED, CTR_NMISS_EARLY, CTR_TICKET, CTR_NCOPIED_EARLY, CTR_LEN, ST_OVERFLOW, ST_BADTOK,
+                      ST_BADMISS, ST_FULL, ST_TIMEOUT)
 
 __all__ = ['ech_kv_append', 'ech_sparse_attn', 'ech_sparse_attn_ws_bytes', 'ech_index_logits', 'ech_index_logits_causal', 'ech_topk', 'ech_topk_noalloc', 'ech_topk_ws_bytes', 'ech_cache_reset',
-           'ech_cache_step', 'ech_cache_step_ws_bytes', 'ech_recall', 'ech_early_ws_bytes', 'ech_early_begin',
-           'ech_early_group', 'ech_recall_group', 'EchError', 'LayerState', 'lib']
+           'ech_cache_step', 'ech_cache_step_ws_bytes', 'ech_recall', 'ech_index_logits_early',
+           'ech_index_logits_early_ws_bytes', 'EchError', 'LayerState', 'lib']
 
 
 class EchError(RuntimeError):
@@ -178,46 +179,28 @@ def ech_recall(host_pool, dev_cache, state: LayerState, phase: int = ECH_FINAL, 
         _ptr(state.ctr), miss.shape[0], _stream(stream)))
 
 
-# ------------------------------------------------------------------ early fetch in sequence groups
-def ech_early_ws_bytes(B: int, max_len: int, C: int, M_early: int) -> int:
-    return int(lib().ech_early_ws_bytes(B, max_len, C, M_early))
+# ------------------------------------------------------------------ stages 1 and 3 fused (decode, fp8 keys)
+def ech_index_logits_early_ws_bytes(R: int, max_len: int, M_early: int) -> int:
+    return int(lib().ech_index_logits_early_ws_bytes(R, max_len, M_early))
 
 
-def ech_early_begin(q, w, kcache, kscale, seq_tok0, seq_len, max_len: int, theta, state: LayerState, stats, ws,
-                    stream=None) -> None:
-    """Pins of the step's early fetch (resident tokens above theta) and the
-    ranking of the free slots; stats [B,4] i32 (hits; other fields zeroed)."""
-    B = seq_tok0.shape[0]
-    miss = state.miss_early
-    _check('ech_early_begin', lib().ech_early_begin(
-        _ptr(q), _ptr(w), _ptr(kcache), _key_dtype(kcache), _ptr(kscale), _ptr(seq_tok0), _ptr(seq_len), B,
-        int(max_len), _ptr(theta), _ptr(state.tok2slot), state.P, _ptr(state.slot_pin), state.C, _ptr(state.ctr),
-        miss.shape[0], _ptr(stats), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
-
-
-def ech_early_group(group: int, b0: int, b1: int, logits, theta, cap: int, seq_tok0, seq_len, max_len: int,
-                    state: LayerState, stats, ws, stream=None) -> None:
-    """Early-fetch allocation of sequences [b0, b1) (group number `group`),
-    after their rows of logits [B, ld] are written."""
-    B = seq_tok0.shape[0]
-    miss = state.miss_early
-    _check('ech_early_group', lib().ech_early_group(
-        int(group), int(b0), int(b1), _ptr(logits), logits.stride(0), _ptr(theta), int(cap), _ptr(seq_tok0),
-        _ptr(seq_len), B, int(max_len), _ptr(state.tok2slot), state.P, _ptr(state.slot2tok), _ptr(state.slot_pin),
-        state.C, _ptr(miss), miss.shape[0], _ptr(state.ctr), _ptr(stats), _ptr(ws), ws.numel() * ws.element_size(),
-        _stream(stream)))
-
-
-def ech_recall_group(group: int, host_pool, dev_cache, state: LayerState, ws, stream=None) -> None:
-    """Copy the rows of one group's early allocations into the device cache."""
+def ech_index_logits_early(q, w, kcache, kscale, row_tok0, row_len, max_len: int, logits, e0: int, e1: int, theta,
+                           cap: int, state: 'LayerState', stats, host_pool, dev_cache, ws, stream=None) -> None:
+    """Decode scores of every row fused with the early fetch of sequences
+    [e0, e1) (maps, early miss list, and the rows of a leading part of it
+    copied over PCIe; ech_recall(ECH_EARLY) copies the rest). ws: uint8,
+    zero-filled before the first call."""
+    R = q.shape[0]
     row_bytes = host_pool.shape[1] * host_pool.element_size()
-    miss = state.miss_early
-    _check('ech_recall_group', lib().ech_recall_group(
-        int(group), _ptr(host_pool), host_pool.shape[0], row_bytes, _ptr(dev_cache), dev_cache.shape[0], _ptr(miss),
-        miss.shape[0], _ptr(state.ctr), _ptr(ws), _stream(stream)))
+    _check('ech_index_logits_early', lib().ech_index_logits_early(
+        _ptr(q), _ptr(w), _ptr(kcache), _key_dtype(kcache), _ptr(kscale), _ptr(row_tok0), _ptr(row_len), R,
+        q.shape[1], q.shape[2], int(max_len), _ptr(logits), logits.stride(0), int(e0), int(e1), _ptr(theta),
+        int(cap), _ptr(state.tok2slot), state.P, _ptr(state.slot2tok), _ptr(state.slot_pin), state.C,
+        _ptr(state.miss_early), state.miss_early.shape[0], _ptr(state.ctr), _ptr(stats), _ptr(host_pool),
+        row_bytes, _ptr(dev_cache), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
 
 
-# ------------------------------------------------------------------ consumer: sparse attention
+# ------------------------------------------------------------------ consumer
 def ech_sparse_attn_ws_bytes(B: int, H: int, k: int) -> int:
     return int(lib().ech_sparse_attn_ws_bytes(B, H, k))
 

@@ -455,6 +455,7 @@ __device__ void bookkeep(int phase, int nseq, int cap, const int32_t* __restrict
   }
   if (tid == 0) {
     ctr[phase == ECH_EARLY ? ECH_CTR_NMISS_EARLY : ECH_CTR_NMISS] = n_alloc;
+    if (phase == ECH_EARLY) ctr[ECH_CTR_NCOPIED_EARLY] = 0;   // nothing of this list is copied yet
     ctr[ECH_CTR_NWANT] = n_want;
     ctr[ECH_CTR_NPINNED] = hit_all;
     ctr[ECH_CTR_EPOCH] = ep;
@@ -576,7 +577,9 @@ __global__ __launch_bounds__(kT) void recall_kernel(const v4u* __restrict__ host
                                                     const int32_t* __restrict__ miss, int32_t* ctr, int cidx,
                                                     int32_t M_max) {
   const int n = min(ctr[cidx], M_max);
-  const int64_t total = (int64_t)n * row16;
+  // EARLY: entries the fused scores + early-fetch launch already copied are skipped
+  const int n0 = (cidx == ECH_CTR_NMISS_EARLY) ? min(max(ctr[ECH_CTR_NCOPIED_EARLY], 0), n) : 0;
+  const int64_t total = (int64_t)(n - n0) * row16;
   const int64_t stride = (int64_t)gridDim.x * kT * kRecallUnroll;
   for (int64_t base = (int64_t)blockIdx.x * kT * kRecallUnroll + threadIdx.x; base < total; base += stride) {
     v4u v[kRecallUnroll];
@@ -586,8 +589,8 @@ __global__ __launch_bounds__(kT) void recall_kernel(const v4u* __restrict__ host
       const int64_t i = base + (int64_t)u * kT;
       dst[u] = -1;
       if (i < total) {
-        const int m = (int)(i / row16);
-        const int c = (int)(i - (int64_t)m * row16);
+        const int m = n0 + (int)(i / row16);
+        const int c = (int)(i % row16);
         const int g = miss[2 * m], p = miss[2 * m + 1];
         if (g >= 0 && g < P && p >= 0 && p < C) {
           v[u] = __builtin_nontemporal_load(host + (int64_t)g * row16 + c);
@@ -601,7 +604,7 @@ __global__ __launch_bounds__(kT) void recall_kernel(const v4u* __restrict__ host
     for (int u = 0; u < kRecallUnroll; ++u)
       if (dst[u] >= 0) __builtin_nontemporal_store(v[u], dev + dst[u]);
   }
-  if (blockIdx.x == 0 && threadIdx.x == 0) atomicAdd(&ctr[ECH_CTR_RECALLED], n);
+  if (blockIdx.x == 0 && threadIdx.x == 0) atomicAdd(&ctr[ECH_CTR_RECALLED], n - n0);
 }
 
 }  // namespace

@@ -13,4 +13,4 @@ extern "C" const char* ech_status_str(int code) {
   }
 }
 
-extern "C" int ech_version(void) { return 102; }   // 1.2: ech_topk_noalloc
+extern "C" int ech_version(void) { return 200; }   // 2.0: ech_index_logits_early replaces the grouped early fetch

@@ -7,19 +7,17 @@ fetch of tokens scoring above the predicted threshold starts before it:
     S0: ech_index_logits --> ech_topk(theta -> theta') --> FINAL maps --> FINAL recall
          \-> S1: EARLY(theta) maps -----/--> EARLY recall (PCIe) ----/
 
-Optionally (early_groups >= 1) the batch's sequences are scored in G groups
-and each group's early rows start crossing PCIe as soon as its scores exist:
+With fp8 keys the scores and the early fetch are one launch
+(ech_index_logits_early): the early misses of a sequence get their slots, and
+their rows start crossing PCIe, while later sequences are still being scored;
+the rows not yet copied when the scoring ends are copied on S1 beside the
+top-k:
 
-    S0: logits g0 -> maps g0 -> logits g1 -> maps g1 ... -> ech_topk -> FINAL maps --+
-    S1: early_begin (pins) --> recall g0 ------> recall g1 ... -----------------------+-> FINAL recall
+    S0: scores + EARLY maps + early rows (one launch) --> ech_topk --> FINAL maps --+--> FINAL recall
+         \-> S1: rest of the early rows (PCIe) ------------------------------------/
 
-The grouping changes only the order of the work, not its result (see
-ech_early_begin in include/ech.h). On MI355X it does not pay: beside the
-zero-copy PCIe gather the group maps slow 2-3x and the gather itself drops
-to 34-41 GB/s (55 alone), and a captured graph started the group recalls only
-when the top-k began; two groups are level with one EARLY phase after all
-scores, which stays the default. theta is double-buffered (the early fetch
-reads the prediction while the top-k writes its update). When the batch's
+theta is double-buffered (the early fetch reads the prediction while the
+top-k writes its update). When the batch's
 selections do not fit the cache at once (sum of min(k, len_b) > C),
 sequences are processed in host-computed chunks, each an ECH_EARLY phase
 then a FINAL phase; every selected token is resident at the end of its chunk.
@@ -43,8 +41,8 @@ import numpy as np
 import torch
 
 from . import (ECH_EARLY, ECH_FINAL, ECH_PREFILL, LayerState, ech_cache_reset, ech_cache_step,
-               ech_cache_step_ws_bytes, ech_early_begin, ech_early_group, ech_early_ws_bytes, ech_index_logits,
-               ech_index_logits_causal, ech_kv_append, ech_recall, ech_recall_group, ech_topk, ech_topk_ws_bytes)
+               ech_cache_step_ws_bytes, ech_index_logits, ech_index_logits_causal, ech_index_logits_early,
+               ech_index_logits_early_ws_bytes, ech_kv_append, ech_recall, ech_topk, ech_topk_ws_bytes)
 
 
 def round_up(x: int, m: int) -> int:
@@ -81,8 +79,8 @@ class DecodeLayer:
     def __init__(self, kcache: torch.Tensor, kscale: Optional[torch.Tensor], w: torch.Tensor,
                  tok0: np.ndarray, lens: np.ndarray, C: int, k: int = 2048, cap: int = 512,
                  host_pool: Optional[torch.Tensor] = None, early: bool = True, topk_after_early: bool = False,
-                 topk_first: Optional[bool] = None,
-                 early_groups: int = 0, capacity: Optional[np.ndarray] = None, device='cuda'):
+                 topk_first: Optional[bool] = None, fused: Optional[bool] = None,
+                 capacity: Optional[np.ndarray] = None, device='cuda'):
         self.kcache, self.kscale, self.w = kcache, kscale, w
         self.topk_after_early = topk_after_early
         # Launch order of the two branches after the scores. A captured graph
@@ -126,17 +124,17 @@ class DecodeLayer:
                                     dtype=torch.uint8, **dev)
         self.ws_final = torch.empty(ech_cache_step_ws_bytes(ECH_FINAL, cb, cb, k, self.max_len, C, m_max),
                                     dtype=torch.uint8, **dev)
-        # Early fetch in sequence groups: only when the whole batch is one chunk.
-        self.groups = (sequence_groups(self.B, early_groups)
-                       if early and early_groups >= 1 and len(self.chunks) == 1 else [])
-        if self.groups:
-            self.ws_group = torch.empty(ech_early_ws_bytes(self.B, self.max_len, C, m_early), dtype=torch.uint8,
-                                        **dev)
-            self.ev_start = torch.cuda.Event()
-            self.ev_begin = torch.cuda.Event()
-            self.ev_mg = [torch.cuda.Event() for _ in self.groups]
-            self.ev_fm = torch.cuda.Event()
-            self.ev_rg = torch.cuda.Event()
+        # Scores fused with the first chunk's early fetch: fp8 keys, a host
+        # pool to copy from, and the early fetch on.
+        can_fuse = early and host_pool is not None and kscale is not None and cap <= 4096
+        self.fused = can_fuse if fused is None else bool(fused)
+        if self.fused and not can_fuse:
+            raise ValueError('the fused scores + early fetch needs fp8 keys, a host pool, the early fetch and '
+                             'cap <= 4096')
+        if self.fused:
+            # zero-filled once; every call leaves it ready for the next
+            self.ws_fused = torch.zeros(ech_index_logits_early_ws_bytes(self.B, self.max_len, m_early),
+                                        dtype=torch.uint8, **dev)
         self.host_pool = host_pool
         if host_pool is not None:
             self.dev_cache = torch.zeros((C, host_pool.shape[1]), dtype=host_pool.dtype, **dev)
@@ -177,6 +175,18 @@ class DecodeLayer:
         ech_index_logits(q, self.w, self.kcache, self.kscale, self.tok0, self.lens, self.max_len, self.logits,
                          stream=stream)
 
+    def scores_launch(self, q: torch.Tensor, stream=None) -> None:
+        """The first launch of a step: the scores, and with the fused path
+        also the first chunk's early fetch (its maps, and the rows of a
+        leading part of its misses copied over PCIe)."""
+        if self.fused:
+            b0, b1 = self.chunks[0]
+            ech_index_logits_early(q, self.w, self.kcache, self.kscale, self.tok0, self.lens, self.max_len,
+                                   self.logits, b0, b1, self.theta[self.parity], self.cap, self.state,
+                                   self.stats_early, self.host_pool, self.dev_cache, self.ws_fused, stream=stream)
+        else:
+            self.logits_only(q, stream=stream)
+
     def step(self, q: Optional[torch.Tensor], marks: Optional[dict] = None,
              wait: Optional[torch.cuda.Event] = None, logits_done: Optional[torch.cuda.Event] = None,
              scores: bool = True, on_chunk=None) -> None:
@@ -188,8 +198,8 @@ class DecodeLayer:
         early_maps, recall_early, final_maps, recall_final (one pair per
         chunk). `wait`, when given, is an event the scores wait for;
         `logits_done` is recorded once they are written (one group only).
-        scores=False leaves the scores out: the caller has launched them on
-        the current stream already (q is then unused).
+        scores=False leaves the scores out: the caller has launched them
+        (scores_launch) on the current stream already (q is then unused).
 
         on_chunk(b0, b1, stream), when given, is called once per sequence
         chunk, right after the chunk's FINAL recall is enqueued on `stream`:
@@ -213,23 +223,65 @@ class DecodeLayer:
             return ev
 
         th, th_next = self.theta[self.parity], self.theta[1 - self.parity]
-        if self.groups:
-            if logits_done is not None or not scores:
-                raise ValueError('logits_done and scores=False need the early fetch in one group')
-            self._step_grouped(q, th, th_next, s0, mark)
-            if on_chunk is not None:
-                on_chunk(0, self.B, s0)
-            self.parity ^= 1
-            return
         if scores:
             mark('logits', s0)
-            self.logits_only(q, stream=s0)
+            self.scores_launch(q, stream=s0)
             mark('logits', s0)
         if logits_done is not None:
             logits_done.record(s0)
         first_b0, first_b1 = self.chunks[0]
         if self.early:
             self.ev_logits.record(s0)
+        if self.fused:
+            self._after_fused(th, th_next, s0, mark)
+        else:
+            self._after_scores(th, th_next, s0, mark)
+        mark('recall_final', s0)
+        self._recall(ECH_FINAL, s0)
+        mark('recall_final', s0)
+        if on_chunk is not None:
+            on_chunk(first_b0, first_b1, s0)
+        for b0, b1 in self.chunks[1:]:
+            for phase in ((ECH_EARLY, ECH_FINAL) if self.early else (ECH_FINAL,)):
+                name = 'early' if phase == ECH_EARLY else 'final'
+                mark(name + '_maps', s0)
+                self._maps(phase, b0, b1, th, s0)
+                mark(name + '_maps', s0)
+                mark('recall_' + name, s0)
+                self._recall(phase, s0)
+                mark('recall_' + name, s0)
+            if on_chunk is not None:
+                on_chunk(b0, b1, s0)
+        mark('final', s0)
+        self.parity ^= 1
+
+    def _after_fused(self, th, th_next, s0, mark) -> None:
+        """First chunk after the fused launch: the rest of the early rows on
+        S1, the top-k and the FINAL maps on S0; ends with S0 waiting for the
+        early rows (the FINAL recall may reuse a slot they fill)."""
+        first_b0, first_b1 = self.chunks[0]
+        mark('topk', s0)
+        ech_topk(self.logits, self.lens, self.max_len, self.k, th, th_next, self.idx, self.kth, self.ws_topk,
+                 stream=s0)
+        mark('topk', s0)
+        self.s1.wait_event(self.ev_logits)
+        mark('early', self.s1)
+        mark('recall_early', self.s1)
+        self._recall(ECH_EARLY, self.s1)
+        mark('recall_early', self.s1)
+        mark('early', self.s1)
+        self.ev_early.record(self.s1)
+        mark('final', s0)
+        mark('final_maps', s0)
+        self._maps(ECH_FINAL, first_b0, first_b1, th, s0)
+        mark('final_maps', s0)
+        s0.wait_event(self.ev_early)
+
+    def _after_scores(self, th, th_next, s0, mark) -> None:
+        """First chunk after the plain scores: the EARLY maps and recall on
+        S1 beside the top-k on S0, then the FINAL maps; ends with S0 waiting
+        for the early rows."""
+        first_b0, first_b1 = self.chunks[0]
 
         def early_branch():
             # S1: EARLY maps, then its rows cross PCIe while S0 carries on.
@@ -269,77 +321,6 @@ class DecodeLayer:
         mark('final_maps', s0)
         if self.early:
             s0.wait_event(self.ev_early)           # ... but may reuse a slot EARLY is still filling
-        mark('recall_final', s0)
-        self._recall(ECH_FINAL, s0)
-        mark('recall_final', s0)
-        if on_chunk is not None:
-            on_chunk(first_b0, first_b1, s0)
-        for b0, b1 in self.chunks[1:]:
-            for phase in ((ECH_EARLY, ECH_FINAL) if self.early else (ECH_FINAL,)):
-                name = 'early' if phase == ECH_EARLY else 'final'
-                mark(name + '_maps', s0)
-                self._maps(phase, b0, b1, th, s0)
-                mark(name + '_maps', s0)
-                mark('recall_' + name, s0)
-                self._recall(phase, s0)
-                mark('recall_' + name, s0)
-            if on_chunk is not None:
-                on_chunk(b0, b1, s0)
-        mark('final', s0)
-        self.parity ^= 1
-
-    def _step_grouped(self, q, th, th_next, s0, mark) -> None:
-        """Decode step with the early fetch in sequence groups (one chunk), on
-        two streams: S0 scores each group and allocates its early misses (a
-        few short kernels), then runs the top-k and the FINAL maps; S1 pins
-        (begin), recalls each group's rows as soon as they are allocated,
-        then the FINAL rows."""
-        s1 = self.s1
-        self.ev_start.record(s0)
-        s1.wait_event(self.ev_start)
-        mark('early', s1)
-        ech_early_begin(q, self.w, self.kcache, self.kscale, self.tok0, self.lens, self.max_len, th, self.state,
-                        self.stats_early, self.ws_group, stream=s1)
-        self.ev_begin.record(s1)
-        mark('logits', s0)
-        mark('recall_early', s1)
-
-        def recall(g):
-            if self.host_pool is not None:
-                s1.wait_event(self.ev_mg[g])
-                ech_recall_group(g, self.host_pool, self.dev_cache, self.state, self.ws_group, stream=s1)
-
-        # Group g's recall is enqueued after the next S0 launch (the next
-        # group's scores, or the top-k after the last group): a captured graph
-        # then keeps the S0 chain on one hardware queue and gives the recalls
-        # their own (its executor continues a node's queue with the child
-        # captured first).
-        for g, (b0, b1) in enumerate(self.groups):
-            ech_index_logits(q[b0:b1], self.w[b0:b1], self.kcache, self.kscale, self.tok0[b0:b1],
-                             self.lens[b0:b1], self.max_len, self.logits[b0:b1], stream=s0)
-            if g > 0:
-                recall(g - 1)
-            if g == 0:
-                s0.wait_event(self.ev_begin)
-            ech_early_group(g, b0, b1, self.logits, th, self.cap, self.tok0, self.lens, self.max_len, self.state,
-                            self.stats_early, self.ws_group, stream=s0)
-            self.ev_mg[g].record(s0)
-        mark('logits', s0)
-        mark('topk', s0)
-        ech_topk(self.logits, self.lens, self.max_len, self.k, th, th_next, self.idx, self.kth, self.ws_topk,
-                 stream=s0)
-        recall(len(self.groups) - 1)
-        mark('recall_early', s1)
-        mark('early', s1)
-        mark('topk', s0)
-        mark('final', s0)
-        self._maps(ECH_FINAL, 0, self.B, th, s0)      # after every group (same stream)
-        self.ev_fm.record(s0)
-        s1.wait_event(self.ev_fm)                     # after the early recalls: it may reuse their slots
-        self._recall(ECH_FINAL, s1)
-        self.ev_rg.record(s1)
-        s0.wait_event(self.ev_rg)
-        mark('final', s0)
 
     @property
     def theta_current(self) -> torch.Tensor:
@@ -535,8 +516,6 @@ class DecodeStack:
         self.L, self.M = len(self.layers), (len(self.layers[0]) if self.layers else 0)
         if self.L == 0 or self.M == 0 or any(len(r) != self.M for r in self.layers):
             raise ValueError('layers must be a non-empty L x M list of DecodeLayer')
-        if any(d.groups for r in self.layers for d in r):
-            raise ValueError('the early fetch in sequence groups is not supported in a stack')
         # Two streams per micro-batch (scores and its chain; EARLY branch),
         # shared by its layers; micro-batch 0's chain is the caller's stream.
         # With two micro-batches these are four streams, one per hardware
@@ -574,7 +553,7 @@ class DecodeStack:
                 st, d = chain[m], self.layers[l][m]
                 if l == 0 and m > 0:
                     st.wait_event(self.ev_logits[0][m - 1])
-                d.logits_only(qs[l][m], stream=st)
+                d.scores_launch(qs[l][m], stream=st)
                 if l == 0:
                     self.ev_logits[0][m].record(st)
             for m in range(self.M):

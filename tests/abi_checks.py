@@ -73,38 +73,35 @@ def check_recall_rejects_bad_args(lib):
     assert lib.ech_recall(9, FAKE, 10, 1152, FAKE, 10, FAKE, FAKE, 4, None) == -1   # no such phase
 
 
-def check_early_group_calls_reject_bad_args(lib):
-    assert lib.ech_early_ws_bytes(0, 10, 10, 10) == 0
-    a = lib.ech_early_ws_bytes(4, 131072, 260000, 2048)
-    b = lib.ech_early_ws_bytes(32, 131072, 260000, 16384)
+def check_index_logits_early_rejects_bad_args(lib):
+    assert lib.ech_index_logits_early_ws_bytes(0, 10, 10) == 0
+    a = lib.ech_index_logits_early_ws_bytes(4, 131072, 2048)
+    b = lib.ech_index_logits_early_ws_bytes(32, 131072, 16384)
     assert 0 < a < b
-    ws = lib.ech_early_ws_bytes(2, 1000, 500, 64)
+    ws = lib.ech_index_logits_early_ws_bytes(4, 1000, 64)
 
-    def begin(q=FAKE, dt=1, sc=FAKE, B=2, ml=1000, C=500, M=64, wsb=ws, wsp=FAKE):
-        return lib.ech_early_begin(q, FAKE, FAKE, dt, sc, FAKE, FAKE, B, ml, FAKE, FAKE, 4000, FAKE, C, FAKE, M,
-                                   FAKE, wsp, wsb, None)
-    assert begin(q=None) == -1
-    assert begin(dt=5) == -3
-    assert begin(sc=None) == -1
-    assert begin(q=FAKE + 8) == -1
-    assert begin(B=2000) == -1
-    assert begin(wsb=ws - 1) == -1
-    assert begin(wsp=FAKE + 64) == -1
-
-    def group(g=0, b0=0, b1=2, B=2, cap=32, M=64, ld=1000, lg=FAKE, wsb=ws):
-        return lib.ech_early_group(g, b0, b1, lg, ld, FAKE, cap, FAKE, FAKE, B, 1000, FAKE, 4000, FAKE, FAKE, 500,
-                                   FAKE, M, FAKE, FAKE, FAKE, wsb, None)
-    assert group(g=-1) == -1
-    assert group(g=96) == -1
-    assert group(b0=1, b1=1) == -1
-    assert group(b1=3) == -1
-    assert group(cap=33) == -1            # early miss list smaller than B * cap
-    assert group(ld=999) == -1
-    assert group(lg=FAKE + 4) == -1
-    assert group(wsb=16) == -1
-    assert lib.ech_recall_group(0, FAKE, 10, 1150, FAKE, 10, FAKE, 4, FAKE, FAKE, None) == -1   # row_bytes % 16
-    assert lib.ech_recall_group(99, FAKE, 10, 1152, FAKE, 10, FAKE, 4, FAKE, FAKE, None) == -1
-    assert lib.ech_recall_group(0, FAKE, 10, 1152, FAKE, 10, FAKE, 4, FAKE, FAKE + 16, None) == -1
+    def call(q=FAKE, dt=1, sc=FAKE, R=4, ml=1000, ld=1000, e0=0, e1=4, cap=16, P=4000, C=500, M=64, rb=1152,
+             wsb=ws, wsp=FAKE, pool=FAKE, miss=FAKE):
+        return lib.ech_index_logits_early(q, FAKE, FAKE, dt, sc, FAKE, FAKE, R, 64, 128, ml, FAKE, ld, e0, e1, FAKE,
+                                          cap, FAKE, P, FAKE, FAKE, C, miss, M, FAKE, FAKE, pool, rb, FAKE, wsp, wsb,
+                                          None)
+    assert call(q=None) == -1
+    assert call(dt=0) == -3              # bf16 keys: not fused
+    assert call(sc=None) == -1
+    assert call(R=2000) == -1
+    assert call(ld=999) == -1
+    assert call(e0=2, e1=2) == -1
+    assert call(e1=5) == -1
+    assert call(cap=5000) == -1
+    assert call(cap=17) == -1            # early miss list smaller than (e1 - e0) * cap
+    assert call(P=1 << 31) == -1
+    assert call(rb=1150) == -1
+    assert call(rb=65536) == -1
+    assert call(wsb=ws - 1) == -1
+    assert call(wsp=FAKE + 64) == -1
+    assert call(q=FAKE + 8) == -1
+    assert call(miss=FAKE + 4) == -1
+    assert call(pool=None) == -1
 
 
 def check_topk_noalloc_rejects_bad_args(lib):

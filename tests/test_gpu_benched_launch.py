@@ -3,8 +3,8 @@
 Workload decode-32x128k-fp8 at its full size: 32 sequences x 131072 tokens,
 fp8 keys with per-token scales, k = 2048, early-fetch cap 512, a device cache
 of 260000 slots, 1152-byte rows in a pinned host pool. The layer is built
-with bench.py's arguments, so with 32 sequences the EARLY branch is launched
-before the top-k. Two eager warm-up steps (the cold step included), then the
+with bench.py's arguments (the scores and the early fetch are one launch, the rest of
+the early rows cross PCIe beside the top-k). Two eager warm-up steps (the cold step included), then the
 step is captured as hipGraphs and replayed, as in the timed region.
 
 Dyadic inputs (small integers, power-of-two scales, head weights m/64) make
@@ -78,9 +78,9 @@ def test_benched_decode_step_full_size_captured_bit_exact():
     pool = torch.empty((wl.P, wk.ROW_ELEMS), dtype=torch.int16, pin_memory=True)
     wk.host_rows(wl, out=pool.numpy().view(np.uint16))
     pool_before = pool.numpy().copy()
-    # bench.py's construction (topk_first and early_groups at their defaults)
+    # bench.py's construction (launch order and fusion at their defaults)
     layer = DecodeLayer(dev(keys), dev(scale), dev(w), wl.tok0, wl.lens, wl.C, k=wl.k, cap=wl.cap, host_pool=pool)
-    assert layer.topk_first is False and not layer.groups and len(layer.chunks) == 1
+    assert layer.fused and len(layer.chunks) == 1
     ref = _Recorder(wl, keys, scale, w, pool.numpy())
     qs = list(wk.decode_queries(wl, 5))
     fetched_early = 0

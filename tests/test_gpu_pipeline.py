@@ -65,24 +65,26 @@ class OracleDecode:
         return L, idx, kth, sel, early_stats, final_stats
 
 
-def _setup(wl, early_groups=0):
+def _setup(wl, fused=None):
     keys, scale = wk.keys(wl)
     w = wk.head_weights(wl)
     rows = wk.host_rows(wl)
     pool = torch.empty((wl.P, 576), dtype=torch.int16, pin_memory=True)
     pool.numpy()[:] = rows.view(np.int16)
     layer = DecodeLayer(dev(keys), None if scale is None else dev(scale), dev(w), wl.tok0, wl.lens, wl.C,
-                        k=wl.k, cap=wl.cap, host_pool=pool, early_groups=early_groups)
+                        k=wl.k, cap=wl.cap, host_pool=pool, fused=fused)
     return keys, scale, w, pool, layer
 
 
-def _run_bit_exact(wl, steps, early_groups=0):
-    keys, scale, w, pool, layer = _setup(wl, early_groups)
-    assert len(layer.groups) == (min(early_groups, wl.B) if early_groups and len(layer.chunks) == 1 else 0)
+def _run_bit_exact(wl, steps, fused=None):
+    keys, scale, w, pool, layer = _setup(wl, fused)
+    assert layer.fused == (wl.kdtype == 'fp8' if fused is None else fused)
     ref = OracleDecode(wl, keys, scale, w, pool.numpy().copy())
+    copied_in_launch = 0
     for s, q in enumerate(wk.decode_queries(wl, steps)):
         layer.step(dev(q))
         torch.cuda.synchronize()
+        copied_in_launch += int(host(layer.state.ctr)[10])   # early rows copied by the fused launch itself
         L, idx, kth, sel, est, fst = ref.step(q)
         for b in range(wl.B):
             np.testing.assert_array_equal(host(layer.logits)[b, :wl.lens[b]], L[b], err_msg=f'step {s} row {b}')
@@ -98,32 +100,38 @@ def _run_bit_exact(wl, steps, early_groups=0):
         assert int(host(layer.state.ctr)[5]) == 0
         np.testing.assert_array_equal(host(layer.dev_cache), ref.cache)
     np.testing.assert_array_equal(pool.numpy(), ref.pool)   # no write-back
+    return layer, copied_in_launch
 
 
-def test_dyadic_decode_fp8_batch():
+@pytest.mark.parametrize('fused', [True, False])
+def test_dyadic_decode_fp8_batch(fused):
+    """fused: the scores and the early fetch in one launch (the default for
+    fp8 keys); otherwise the scores, then the EARLY phase on a second
+    stream."""
     need_gpu()
     wl = wk.CONFIGS['decode-32x128k-fp8'].scaled(B=4, N=9000, C=20000, steps=5, variant='dyadic')
-    _run_bit_exact(wl, 5)
+    _run_bit_exact(wl, 5, fused=fused)
 
 
-def test_dyadic_decode_fp8_batch_grouped_early():
-    """The same steps with the early fetch in three sequence groups (pins
-    from the resident tokens' own scores, groups' rows recalled on a third
-    stream): bit-identical to the oracle's single early phase."""
+def test_dyadic_decode_fp8_fused_slot_shortage_and_cap():
+    """The fused launch with more early misses than free slots (later misses
+    dropped) and sequences reaching the cap, over a ring that wraps."""
     need_gpu()
-    wl = wk.CONFIGS['decode-32x128k-fp8'].scaled(B=5, N=9000, C=20000, steps=5, variant='dyadic')
-    _run_bit_exact(wl, 5, early_groups=3)
+    wl = wk.CONFIGS['decode-64x110k-fp8-capacity'].scaled(B=7, N=6000, len_lo=2000, C=3600, k=512, cap=400,
+                                                          steps=6, resample_p=0.5, variant='dyadic')
+    layer, copied = _run_bit_exact(wl, 6, fused=True)
+    assert copied > 0, 'the fused launch copied no early row itself'
 
 
-@pytest.mark.parametrize('early_groups', [0, 3])
-def test_dyadic_decode_short_and_long_sequences(early_groups):
+@pytest.mark.parametrize('fused', [True, False])
+def test_dyadic_decode_short_and_long_sequences(fused):
     """Ragged lengths from 1 token up, several no longer than k (those rows
     select every token and cannot miss the top-k), in one chunk."""
     need_gpu()
     wl = wk.CONFIGS['decode-64x110k-fp8-capacity'].scaled(B=6, N=3000, len_lo=1, C=7000, k=1024, cap=128,
                                                           steps=4, resample_p=0.0, variant='dyadic')
     assert (wl.lens <= wl.k).any() and (wl.lens > wl.k).any()
-    _run_bit_exact(wl, 4, early_groups=early_groups)
+    _run_bit_exact(wl, 4, fused=fused)
 
 
 def test_dyadic_decode_bf16_small_cache():
@@ -132,14 +140,17 @@ def test_dyadic_decode_bf16_small_cache():
     _run_bit_exact(wl, 4)
 
 
-def test_dyadic_decode_chunked_capacity():
+@pytest.mark.parametrize('fused', [True, False])
+def test_dyadic_decode_chunked_capacity(fused):
     """Batch demand above the cache: sequences run in chunks, later chunks
-    evict earlier ones' tokens; topic shifts force misses."""
+    evict earlier ones' tokens; topic shifts force misses. Fused: the first
+    chunk's early fetch is in the scores launch, later chunks' phases follow
+    one by one."""
     need_gpu()
     wl = wk.CONFIGS['decode-64x110k-fp8-capacity'].scaled(B=6, N=5000, len_lo=3000, C=5000, k=1024, cap=128,
                                                           steps=5, variant='dyadic')
     assert len(oracle_chunks(wl.lens, wl.k, wl.C)) > 1
-    _run_bit_exact(wl, 5)
+    _run_bit_exact(wl, 5, fused=fused)
 
 
 def test_normal_decode_full_size_single_sequence():
