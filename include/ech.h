@@ -82,7 +82,8 @@ extern "C" {
 #define ECH_CTR_NPINNED   7   /* slots pinned by the last phase */
 #define ECH_CTR_NMISS_EARLY 8 /* entries written to the miss list by the last EARLY phase */
 #define ECH_CTR_TICKET    9   /* reserved: stays 0 */
-#define ECH_CTR_NCOPIED_EARLY 10 /* leading EARLY miss-list entries already copied (by ech_index_logits_early) */
+#define ECH_CTR_NCOPIED_EARLY 10 /* leading EARLY miss-list entries already copied (by ech_recall_early_live) */
+#define ECH_CTR_LIVE     11   /* 1 while ech_index_logits_early is writing the early list; ech_recall(EARLY) clears it */
 #define ECH_CTR_LEN      16
 
 /* ---- sticky status bits in ctr[ECH_CTR_STATUS] */
@@ -278,12 +279,11 @@ int ech_recall(int phase, const void* host_pool, int64_t P, int64_t row_bytes, v
  *
  * Results: exactly those of ech_index_logits(q, ..., logits, ld) followed by
  * ech_cache_step(ECH_EARLY) over sequences [e0, e1) with the same scores,
- * theta and cap (maps, pins, early miss list, ctr, stats[e0..e1)); the rows
- * of a leading part of the early miss list are also copied into dev_cache
- * (ctr[ECH_CTR_NCOPIED_EARLY] of them, added to ctr[ECH_CTR_RECALLED]);
- * ech_recall(ECH_EARLY, ...) afterwards copies the rest. The allocation of a
- * sequence's early misses and the PCIe copy of their rows start while later
- * sequences are still being scored.
+ * theta and cap (maps, early miss list, ctr, stats[e0..e1); ctr[NPINNED]
+ * counts the resident tokens above theta). The early misses of a sequence get
+ * their slots, and appear in the early miss list, while later sequences are
+ * still being scored, so ech_recall_early_live on another stream can copy
+ * their rows meanwhile.
  *
  *  q, w, kcache, kscale, row_tok0, row_len, R, H, D, max_len, logits, ld:
  *            as ech_index_logits (R sequences, one query row each); fp8 keys
@@ -293,10 +293,8 @@ int ech_recall(int phase, const void* host_pool, int64_t P, int64_t row_bytes, v
  *  theta [R], cap (<= 4096), tok2slot, P, slot2tok, slot_pin, C, ctr, stats [R, 4]:
  *            as ech_cache_step(ECH_EARLY), indexed by absolute sequence.
  *  miss_early [M_early, 2], M_early >= (e1 - e0) * min(cap, max_len); 8-byte
- *            aligned; overwritten ((-1, -1) where unused).
- *  host_pool [P, row_bytes] pinned, device-mapped (host pointer); dev_cache
- *            [C, row_bytes]; row_bytes a multiple of 16, at most 32768.
- *  ws        ech_index_logits_early_ws_bytes(R, max_len, M_early) bytes,
+ *            aligned; rewritten ((-1, -1) where unused).
+ *  ws        ech_index_logits_early_ws_bytes(R, max_len, C, M_early) bytes,
  *            256-byte aligned, zero-filled before the first call; the calls
  *            keep it ready for the next one (after ECH_ST_TIMEOUT, zero it
  *            again). Calls with the same ws must be ordered.
@@ -304,14 +302,33 @@ int ech_recall(int phase, const void* host_pool, int64_t P, int64_t row_bytes, v
  * waits: if one runs out, ECH_ST_TIMEOUT is set in ctr[ECH_CTR_STATUS] and the
  * results of the call are not valid.
  */
-size_t ech_index_logits_early_ws_bytes(int R, int max_len, int32_t M_early);
+size_t ech_index_logits_early_ws_bytes(int R, int max_len, int32_t C, int32_t M_early);
 int ech_index_logits_early(const void* q, const float* w, const void* kcache, int kdtype, const float* kscale,
                            const int64_t* row_tok0, const int32_t* row_len, int R, int H, int D, int max_len,
                            float* logits, int64_t ld, int e0, int e1, const float* theta, int cap,
                            int32_t* tok2slot, int64_t P, int32_t* slot2tok, int32_t* slot_pin, int32_t C,
-                           int32_t* miss_early, int32_t M_early, int32_t* ctr, int32_t* stats,
-                           const void* host_pool, int64_t row_bytes, void* dev_cache, void* ws, size_t ws_bytes,
-                           void* stream);
+                           int32_t* miss_early, int32_t M_early, int32_t* ctr, int32_t* stats, void* ws,
+                           size_t ws_bytes, void* stream);
+
+/*
+ * ech_recall_early_live - copy the early rows while ech_index_logits_early
+ * allocates them (ECHO explainer, "Decode: fetch above a predicted
+ * threshold": the early fetch's transfer overlaps the scoring). Enqueue it on
+ * a second stream right after ech_index_logits_early is enqueued (with no
+ * wait on it); it copies dev_cache[slot] = host_pool[g] for the early
+ * miss-list entries as they appear, leaving ctr[ECH_CTR_NCOPIED_EARLY] = the
+ * length of the copied prefix (added to ctr[ECH_CTR_RECALLED]). Then enqueue
+ * ech_recall(ECH_EARLY) on that stream, ordered after ech_index_logits_early
+ * (an event): it copies the rest and ends the step's early list.
+ * The copier never depends on being scheduled beside the scoring: it waits
+ * for the list to start and for each entry with a bounded patience (1 ms
+ * without progress) and otherwise leaves the rows to ech_recall(ECH_EARLY).
+ *  host_pool [P, row_bytes] pinned, device-mapped (host pointer); dev_cache
+ *  [C, row_bytes]; row_bytes a multiple of 16, at most 32768; miss_early,
+ *  M_early, ctr and ws: those of the ech_index_logits_early call.
+ */
+int ech_recall_early_live(const void* host_pool, int64_t P, int64_t row_bytes, void* dev_cache, int32_t C,
+                          const int32_t* miss_early, int32_t M_early, int32_t* ctr, void* ws, void* stream);
 
 /*
  * ech_sparse_attn - the consumer of sel_slot: softmax attention of each head

@@ -17,12 +17,12 @@ import torch
 from . import _native
 from ._native import (ECH_EARLY, ECH_FINAL, ECH_PREFILL, ECH_KEY_BF16, ECH_KEY_FP8,  # noqa: F401
                       CTR_HEAD, CTR_EPOCH, CTR_NMISS, CTR_NEVICT, CTR_RECALLED, CTR_STATUS, CTR_NWANT,
-                      CTR_NPINNED, CTR_NMISS_EARLY, CTR_TICKET, CTR_NCOPIED_EARLY, CTR_LEN, ST_OVERFLOW, ST_BADTOK,
+                      CTR_NPINNED, CTR_NMISS_EARLY, CTR_TICKET, CTR_NCOPIED_EARLY, CTR_LIVE, CTR_LEN, ST_OVERFLOW, ST_BADTOK,
                       ST_BADMISS, ST_FULL, ST_TIMEOUT)
 
 __all__ = ['ech_kv_append', 'ech_sparse_attn', 'ech_sparse_attn_ws_bytes', 'ech_index_logits', 'ech_index_logits_causal', 'ech_topk', 'ech_topk_noalloc', 'ech_topk_ws_bytes', 'ech_cache_reset',
            'ech_cache_step', 'ech_cache_step_ws_bytes', 'ech_recall', 'ech_index_logits_early',
-           'ech_index_logits_early_ws_bytes', 'EchError', 'LayerState', 'lib']
+           'ech_index_logits_early_ws_bytes', 'ech_recall_early_live', 'EchError', 'LayerState', 'lib']
 
 
 class EchError(RuntimeError):
@@ -180,24 +180,32 @@ def ech_recall(host_pool, dev_cache, state: LayerState, phase: int = ECH_FINAL, 
 
 
 # ------------------------------------------------------------------ stages 1 and 3 fused (decode, fp8 keys)
-def ech_index_logits_early_ws_bytes(R: int, max_len: int, M_early: int) -> int:
-    return int(lib().ech_index_logits_early_ws_bytes(R, max_len, M_early))
+def ech_index_logits_early_ws_bytes(R: int, max_len: int, C: int, M_early: int) -> int:
+    return int(lib().ech_index_logits_early_ws_bytes(R, max_len, C, M_early))
 
 
 def ech_index_logits_early(q, w, kcache, kscale, row_tok0, row_len, max_len: int, logits, e0: int, e1: int, theta,
-                           cap: int, state: 'LayerState', stats, host_pool, dev_cache, ws, stream=None) -> None:
+                           cap: int, state: 'LayerState', stats, ws, stream=None) -> None:
     """Decode scores of every row fused with the early fetch of sequences
-    [e0, e1) (maps, early miss list, and the rows of a leading part of it
-    copied over PCIe; ech_recall(ECH_EARLY) copies the rest). ws: uint8,
-    zero-filled before the first call."""
+    [e0, e1) (maps and early miss list, written while the scoring runs).
+    ws: uint8, zero-filled before the first call."""
     R = q.shape[0]
-    row_bytes = host_pool.shape[1] * host_pool.element_size()
     _check('ech_index_logits_early', lib().ech_index_logits_early(
         _ptr(q), _ptr(w), _ptr(kcache), _key_dtype(kcache), _ptr(kscale), _ptr(row_tok0), _ptr(row_len), R,
         q.shape[1], q.shape[2], int(max_len), _ptr(logits), logits.stride(0), int(e0), int(e1), _ptr(theta),
         int(cap), _ptr(state.tok2slot), state.P, _ptr(state.slot2tok), _ptr(state.slot_pin), state.C,
-        _ptr(state.miss_early), state.miss_early.shape[0], _ptr(state.ctr), _ptr(stats), _ptr(host_pool),
-        row_bytes, _ptr(dev_cache), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
+        _ptr(state.miss_early), state.miss_early.shape[0], _ptr(state.ctr), _ptr(stats), _ptr(ws),
+        ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def ech_recall_early_live(host_pool, dev_cache, state: 'LayerState', ws, stream=None) -> None:
+    """Copy early rows as ech_index_logits_early allocates them (enqueue on a
+    second stream right after it; ech_recall(ECH_EARLY) afterwards copies the
+    rest)."""
+    row_bytes = host_pool.shape[1] * host_pool.element_size()
+    _check('ech_recall_early_live', lib().ech_recall_early_live(
+        _ptr(host_pool), host_pool.shape[0], row_bytes, _ptr(dev_cache), dev_cache.shape[0], _ptr(state.miss_early),
+        state.miss_early.shape[0], _ptr(state.ctr), _ptr(ws), _stream(stream)))
 
 
 # ------------------------------------------------------------------ consumer

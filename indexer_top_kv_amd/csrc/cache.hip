@@ -604,7 +604,10 @@ __global__ __launch_bounds__(kT) void recall_kernel(const v4u* __restrict__ host
     for (int u = 0; u < kRecallUnroll; ++u)
       if (dst[u] >= 0) __builtin_nontemporal_store(v[u], dev + dst[u]);
   }
-  if (blockIdx.x == 0 && threadIdx.x == 0) atomicAdd(&ctr[ECH_CTR_RECALLED], n - n0);
+  if (blockIdx.x == 0 && threadIdx.x == 0) {
+    atomicAdd(&ctr[ECH_CTR_RECALLED], n - n0);
+    if (cidx == ECH_CTR_NMISS_EARLY) ctr[ECH_CTR_LIVE] = 0;   // this step's early list is complete
+  }
 }
 
 }  // namespace

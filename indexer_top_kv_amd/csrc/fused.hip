@@ -10,44 +10,57 @@
 // tokens scoring above theta; misses = per sequence the first `cap`
 // non-resident tokens above theta, ascending; misses in ascending (sequence,
 // token) order take the unpinned slots in ring order from the head. What
-// changes is when things happen: the allocation of a sequence's misses and the
-// PCIe copy of their rows start while later sequences are still being scored.
+// changes is when things happen: a sequence's early misses get their slots,
+// and appear in the early miss list, while later sequences are still being
+// scored, and a copier launch on another stream moves their rows meanwhile.
 //
-//   pin    grid (chunks, e1-e0): each 4096-token chunk lists its resident
-//          tokens, scores them with the scores kernel's own tile arithmetic
-//          (decode.hpp / score.hpp: the same bit patterns), pins those above
-//          theta (slot_pin = epoch), counts hits.
-//   rank   one workgroup: hits per sequence, the unpinned slots in ring order
-//          from the head (as many as the early demand bound needs), the
-//          epoch; clears the fused kernel's control words and the early miss
-//          list (every entry (-1, -1)).
-//   fused  one launch, three kinds of workgroups (1-D grid, in this order):
-//     alloc  (one per early sequence, at most 64, each taking every 64th)
-//            waits for the masks its sequence's scoring waves publish,
-//            lists the sequence's first `cap` misses in token order, takes its
-//            first rank from the sequences before it (decoupled look-back on
-//            one word per sequence), gives miss m the m-th ranked free slot
-//            (evicting its old token, no write-back) and writes miss m.
-//     copy   (32) claim groups of consecutive miss ranks in order, wait for
-//            their entries and copy the rows from pinned host memory over
-//            PCIe; once every alloc workgroup is done they stop claiming, so
-//            the launch ends soon after the scoring. ctr[NCOPIED_EARLY] says
-//            how many leading entries were copied; ech_recall(ECH_EARLY)
-//            copies the rest.
-//     score  the fp8 decode scores kernel's waves (256 tokens each); a wave
-//            of an early sequence then looks up the residency of its tokens
-//            above theta and publishes its misses as a 256-bit mask in 8
-//            tagged words.
+//   pins    (min(e1-e0, 64) workgroups) only slots the allocation can reach
+//           need their pin status, so the ring is taken in windows of 16384
+//           positions from the head: each workgroup finds its sequence's
+//           tokens in the window (slot2tok), scores them with the scores
+//           kernel's own tile arithmetic (decode.hpp / score.hpp: the same bit
+//           patterns) and pins those above theta (slot_pin = epoch); the
+//           workgroups then agree, through two counters, whether the windows
+//           so far hold enough unpinned slots for the early demand bound, else
+//           take the next window. Also clears the control words, the early
+//           miss list (every entry (-1, -1)) and the free list.
+//   fused   one launch, three kinds of workgroups (1-D grid, in this order):
+//     rank    (16) the unpinned slots in ring order from the head, as many as
+//             the early demand bound (ring slices with a decoupled look-back),
+//             published one by one: the free list, then its length.
+//     alloc   (one per early sequence, at most 64, each taking every 64th)
+//             waits for the masks its sequence's scoring waves publish, lists
+//             the sequence's first `cap` misses in token order, takes its
+//             first rank from the sequences before it (decoupled look-back,
+//             the predecessors' words read in parallel), gives miss m the m-th
+//             free slot (evicting its old token, no write-back) and writes miss
+//             m. The last early sequence publishes the list's length.
+//     score   the fp8 decode scores kernel's waves (256 tokens each); a wave
+//             of an early sequence then looks up the residency of its tokens
+//             above theta and publishes its misses as a 256-bit mask in 8
+//             tagged words, with the count of its resident tokens above theta
+//             (hits).
+//   copier  a separate launch on a second stream (ech_recall_early_live):
+//           claims groups of consecutive ranks in order and copies their rows
+//           from pinned host memory over PCIe as their entries appear, so the
+//           transfer runs beside the scoring and on beside the top-k.
 //
-// Workgroups of one launch communicate through words that carry their own
-// validity (a tag bit, a flag, or a (-1, -1) sentinel), read and written with
-// relaxed device-scope atomics (coherent across the chiplets' L2 caches), so
-// no release fence - which writes back a whole L2 on MI355X - is needed. The
-// scoring waves never wait; alloc workgroups wait only on scoring waves and
-// on alloc workgroups of earlier sequences; copy workgroups wait only on
-// alloc workgroups. Every wait is bounded (0.5 s of the constant-rate clock):
-// past it the workgroup sets ECH_ST_TIMEOUT and carries on, so the launch
-// always ends.
+// Workgroups communicate through words that carry their own validity (a tag
+// bit, a flag, or a (-1, -1) / 0 sentinel), read and written with relaxed
+// device-scope atomics (coherent across the chiplets' L2 caches), so no
+// release fence - which writes back a whole L2 on MI355X - is needed inside a
+// launch. Scoring waves and rank workgroups wait on nothing but rank
+// look-backs; alloc workgroups wait on scoring waves, rank workgroups and
+// earlier sequences; the pins workgroups wait on one another (64 at most, all
+// resident). Every wait is bounded (0.5 s of the constant-rate clock): past it
+// the workgroup sets ECH_ST_TIMEOUT and carries on, so every launch ends. The
+// copier only ever waits with a short patience and then leaves the rest to
+// ech_recall(ECH_EARLY), so it is correct whichever way the two streams are
+// scheduled.
+//
+// Measured on MI355X (32 x 131072 fp8, 260000 slots): PCIe reads in flight
+// slow the HBM stream and stretch every dependent memory round trip several
+// times over, so the copier is kept to 32 workgroups (1 MB in flight).
 
 #include <algorithm>
 
@@ -56,8 +69,6 @@
 namespace {
 
 constexpr int kT = 256;
-constexpr int kPer = 16;
-constexpr int kBlk = kT * kPer;          // tokens per pin block
 constexpr int kTPW = 16;                 // tiles per scoring wave
 constexpr int kNS = 4;                   // ring slots per scoring wave
 constexpr int kWavesF = 4;               // waves per scoring workgroup
@@ -66,10 +77,11 @@ constexpr int kWords = kWaveTok / 32;    // mask words per wave
 constexpr int kMaxCap = 4096;
 constexpr int kMaxB = 1024;
 constexpr int kMaxAlloc = 64;            // alloc workgroups at most
-constexpr int kCopy = 32;                // copy workgroups
-constexpr int kCopyUnroll = 8;           // 16-byte pieces per thread per group
-constexpr int kA = 1024;                 // threads of the rank workgroup
-constexpr int kWinA = kA * 16;           // ring positions per window
+constexpr int kCopyUnroll = 8;           // 16-byte pieces per thread per copied group
+constexpr int kPinWin = 16384;           // ring positions per window of the pins kernel
+constexpr int kMaxPinWg = 64;            // pins workgroups at most
+constexpr int kRankSlice = kT * 16;      // ring positions per slice of a rank workgroup
+constexpr int kRankWg = 16;              // rank workgroups
 
 typedef unsigned long long u64;
 typedef uint32_t v4u __attribute__((ext_vector_type(4)));
@@ -82,26 +94,28 @@ constexpr u64 kSpinTicks = 50000000ull;  // 0.5 s at the 100 MHz constant-rate c
 
 struct Ctl {                             // control words at the start of the workspace
   int next_group;                        // copy groups claimed
-  int a_done;                            // alloc workgroups finished
   int c_done;                            // copy workgroups finished
-  int nfree;                             // free slots ranked (<= M_early)
-  int pad[4];
+  int ep;                                // the phase's epoch
+  int head;                              // the ring head at the phase's start
+  int pin_done;                          // pins kernel: window arrivals (all workgroups, all windows)
+  int pin_total;                         // pins kernel: slots pinned so far
+  int first_incomplete;                  // live copier: the first group it gave up on
   u64 finished;                          // kFin | n_alloc
+  u64 nfree;                             // kFin | free slots ranked (<= M_early)
 };
 
 struct FWs {
   Ctl* ctl;
   u64* lb;                               // [R] look-back word per sequence
-  int* hitblk;                           // [R * nch] hits per pin block
-  int* freelist;                         // [M_early] free slots in ring order from the head
+  u64* rlb;                              // [ceil(C / kRankSlice)] look-back word per ring slice
+  int* freelist;                         // [M_early] slot + 1 of the free slot of each rank (0: not yet)
   u64* masks;                            // [R * wpr * kWords] published miss masks
-  int nch, wpr;
+  int wpr;
 };
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
-size_t fused_layout(int R, int max_len, int32_t M_early, FWs* w, char* base) {
-  const int nch = std::max(1, (max_len + kBlk - 1) / kBlk);
+size_t fused_layout(int R, int max_len, int32_t C, int32_t M_early, FWs* w, char* base) {
   const int wpr = std::max(1, (max_len + kWaveTok - 1) / kWaveTok);
   size_t o = 0;
   auto take = [&](size_t bytes) {
@@ -109,15 +123,16 @@ size_t fused_layout(int R, int max_len, int32_t M_early, FWs* w, char* base) {
     o = align256(o + bytes);
     return at;
   };
-  const size_t o_ctl = take(sizeof(Ctl)), o_lb = take(8 * (size_t)R), o_hit = take(4 * (size_t)R * nch),
-               o_fl = take(4 * (size_t)std::max(M_early, 1)), o_m = take(8 * (size_t)R * wpr * kWords);
+  const size_t o_ctl = take(sizeof(Ctl)), o_lb = take(8 * (size_t)R),
+               o_rlb = take(8 * (size_t)((std::max(C, 1) + kRankSlice - 1) / kRankSlice)),
+               o_fl = take(4 * (size_t)std::max(M_early, 1)),
+               o_m = take(8 * (size_t)R * wpr * kWords);
   if (w && base) {
     w->ctl = reinterpret_cast<Ctl*>(base + o_ctl);
     w->lb = reinterpret_cast<u64*>(base + o_lb);
-    w->hitblk = reinterpret_cast<int*>(base + o_hit);
+    w->rlb = reinterpret_cast<u64*>(base + o_rlb);
     w->freelist = reinterpret_cast<int*>(base + o_fl);
     w->masks = reinterpret_cast<u64*>(base + o_m);
-    w->nch = nch;
     w->wpr = wpr;
   }
   return o;
@@ -131,6 +146,9 @@ __device__ __forceinline__ void st_dev(u64* p, u64 v) {
 }
 __device__ __forceinline__ int ld_dev(const int* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_dev(int* p, int v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 __device__ __forceinline__ void set_status(int32_t* ctr, int bit) { atomicOr(&ctr[ECH_CTR_STATUS], bit); }
@@ -154,59 +172,54 @@ __device__ __forceinline__ bool spin_until(Load load, Pred pred, int32_t* ctr, u
   }
 }
 
-// ------------------------------------------------------------------ pin
-// grid (nch, e1 - e0). Chunk c of sequence b covers tokens [c*kBlk, +kBlk).
-// The resident tokens of the chunk are listed in order, then each wave
-// scores tiles of 16 of them, four tiles at a time with all their (gathered)
-// key rows in flight together.
+// ------------------------------------------------------------------ pins
+// grid (min(e1 - e0, kMaxPinWg)); workgroup j handles the early sequences
+// e0 + j, e0 + j + grid, ... Every workgroup takes part in every window's
+// count (two counters that only grow, so nothing is cleared between
+// windows); every workgroup reads the same totals after a window and so takes
+// the same decision.
 constexpr int kPinBatch = 4;
 
-__global__ __launch_bounds__(kT) void fused_pin_kernel(const uint16_t* __restrict__ q, const float* __restrict__ w,
-                                                       const uint8_t* __restrict__ kc, const float* __restrict__ ksc,
-                                                       const int64_t* __restrict__ tok0,
-                                                       const int32_t* __restrict__ lens,
-                                                       const float* __restrict__ theta, int e0,
-                                                       const int32_t* __restrict__ tok2slot, int64_t P, int32_t C,
-                                                       int32_t* __restrict__ slot_pin, const int32_t* ctr, FWs ws) {
-  __shared__ int rt[kBlk];          // resident token offsets of the chunk, ascending
-  __shared__ int scr[kT / 64];
-  const int b = e0 + blockIdx.y, c = blockIdx.x;
-  const int len = lens[b];
-  const float th = theta[b];
-  const int lo = c * kBlk;
-  int* out = ws.hitblk + (size_t)b * ws.nch + c;
-  if (th != th || lo >= len) {
-    if (threadIdx.x == 0) *out = 0;
-    return;
-  }
-  const int64_t g0 = tok0[b];
-  const int ep = ctr[ECH_CTR_EPOCH] + 1;
-  // ordered compaction of the chunk's resident tokens
-  const int t_first = lo + threadIdx.x * kPer;
-  bool res[kPer];
+__device__ int pin_sequence_window(const uint16_t* __restrict__ q, const float* __restrict__ w,
+                                   const uint8_t* __restrict__ kc, const float* __restrict__ ksc, int b, int64_t g0,
+                                   int len, float th, const int32_t* __restrict__ slot2tok, int32_t C, int head, int p0,
+                                   int wsz, int ep, int32_t* __restrict__ slot_pin, int* s_pos, int* scr) {
+  const int tid = threadIdx.x;
+  // the window's slots holding a token of sequence b
+  constexpr int kU = kPinWin / kT;
   int n = 0;
-  int sl[kPer];   // all sixteen lookups in flight (clamped addresses; only tokens in the row used)
+  uint32_t mine[kU / 32];
 #pragma unroll
-  for (int i = 0; i < kPer; ++i) sl[i] = tok2slot[min(max(g0 + t_first + i, (int64_t)0), P - 1)];
+  for (int k = 0; k < kU / 32; ++k) mine[k] = 0;
 #pragma unroll
-  for (int i = 0; i < kPer; ++i) {
-    const int t = t_first + i;
-    res[i] = t < len && g0 + t < P && sl[i] >= 0 && sl[i] < C;
-    n += res[i];
+  for (int u0 = 0; u0 < kU; u0 += 16) {
+    int gv[16];
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {   // coalesced, sixteen in flight
+      const int pos = p0 + (u0 + u) * kT + tid;
+      int p = head + min(pos, C - 1);
+      if (p >= C) p -= C;
+      gv[u] = slot2tok[p];
+    }
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      const bool in = (u0 + u) * kT + tid < wsz && gv[u] >= g0 && (int64_t)gv[u] < g0 + len;
+      if (in) mine[(u0 + u) >> 5] |= 1u << ((u0 + u) & 31);
+      n += in;
+    }
   }
   int nres;
   int pos = ech::block_excl_scan<kT>(n, scr, &nres);
 #pragma unroll
-  for (int i = 0; i < kPer; ++i)
-    if (res[i]) rt[pos++] = t_first + i;
+  for (int k = 0; k < kU / 32; ++k)
+    for (uint32_t m = mine[k]; m != 0u; m &= m - 1u) s_pos[pos++] = (32 * k + __builtin_ctz(m)) * kT + tid;
   __syncthreads();
-  int hits = 0;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int pinned = 0;
+  const int lane = tid & 63, wave = tid >> 6;
   const int ntile = (nres + 15) / 16;
   if (wave < ntile) {   // wave-uniform
     const int col = lane & 15, grp = lane >> 4;
-    // query fragments and head weights straight into registers, in the
-    // scores kernel's operand layout (the same products, the same sums)
+    // query fragments and head weights in the scores kernel's operand layout
     bf16x8_t a[4][4];
     float wv[4][4];
     const uint8_t* qb = reinterpret_cast<const uint8_t*>(q + (size_t)b * kH * kD);
@@ -219,17 +232,20 @@ __global__ __launch_bounds__(kT) void fused_pin_kernel(const uint16_t* __restric
 #pragma unroll
       for (int u = 0; u < 4; ++u) wv[ht][u] = w[(size_t)b * kH + 16 * ht + 4 * grp + u];
     }
-    const uint8_t* kbase = kc + (size_t)g0 * kD;
     for (int j0 = wave; j0 < ntile; j0 += kPinBatch * (kT / 64)) {
       KeyFrag<ECH_KEY_FP8> f[kPinBatch];
       float sc[kPinBatch];
-      int tt[kPinBatch];
+      int pp[kPinBatch];
+      int64_t gg[kPinBatch];
 #pragma unroll
       for (int u = 0; u < kPinBatch; ++u) {   // the batch's gathers, all in flight
         const int e = 16 * (j0 + u * (kT / 64)) + col;
-        tt[u] = rt[min(e, nres - 1)];
-        load_key<ECH_KEY_FP8>(f[u], kbase + (size_t)tt[u] * kD, grp);
-        sc[u] = ksc[g0 + tt[u]];
+        int p = head + p0 + s_pos[min(e, nres - 1)];
+        p = (int)((int64_t)p % C);
+        pp[u] = p;
+        gg[u] = slot2tok[p];
+        load_key<ECH_KEY_FP8>(f[u], kc + (size_t)gg[u] * kD, grp);
+        sc[u] = ksc[gg[u]];
       }
 #pragma unroll
       for (int u = 0; u < kPinBatch; ++u) {
@@ -241,101 +257,84 @@ __global__ __launch_bounds__(kT) void fused_pin_kernel(const uint16_t* __restric
           for (int s2 = 0; s2 < 4; ++s2) kb[s2] = key_step<ECH_KEY_FP8>(f[u], s2);
           const float v = tile_score(a, wv, kb, sc[u]);
           if (grp == 0 && e < nres && v > th) {
-            slot_pin[tok2slot[g0 + tt[u]]] = ep;
-            ++hits;
+            slot_pin[pp[u]] = ep;
+            ++pinned;
           }
         }
       }
     }
   }
-  const int tot = ech::block_sum<kT>(hits, scr);
-  if (threadIdx.x == 0) *out = tot;
+  __syncthreads();   // s_pos is rewritten by the next sequence or window
+  return pinned;
 }
 
-// ------------------------------------------------------------------ rank
-__global__ __launch_bounds__(kA) void fused_rank_kernel(const int32_t* __restrict__ slot_pin, int32_t C, int e0,
-                                                        int e1, int32_t* __restrict__ miss_early, int32_t M_early,
-                                                        int32_t* ctr, int32_t* __restrict__ stats, FWs ws) {
-  __shared__ int scr[kA / 64];
-  __shared__ __align__(16) uint8_t s_fr[kWinA];
-  const int tid = threadIdx.x;
+__global__ __launch_bounds__(kT) void fused_pins_kernel(const uint16_t* __restrict__ q, const float* __restrict__ w,
+                                                        const uint8_t* __restrict__ kc, const float* __restrict__ ksc,
+                                                        const int64_t* __restrict__ tok0,
+                                                        const int32_t* __restrict__ lens,
+                                                        const float* __restrict__ theta, int e0, int e1,
+                                                        const int32_t* __restrict__ slot2tok, int32_t C,
+                                                        int32_t* __restrict__ slot_pin, int32_t* __restrict__ miss_early,
+                                                        int32_t M_early, int32_t* ctr, FWs ws) {
+  __shared__ int s_pos[kPinWin];
+  __shared__ int scr[kT / 64];
+  __shared__ int s_tot;
+  const int tid = threadIdx.x, j = blockIdx.x, nwg = gridDim.x;
   const int ep = ctr[ECH_CTR_EPOCH] + 1;
   int head = ctr[ECH_CTR_HEAD];
   if (head < 0 || head >= C) head = 0;   // only a corrupted state; keeps every slot index in range
-  // hits per sequence (the pinned slots: one per resident token above
-  // theta): every pin block's count in flight at once, summed in LDS
-  __shared__ int s_hit[kMaxB];
-  const int nb = e1 - e0;
-  for (int i = tid; i < nb; i += kA) s_hit[i] = 0;
-  __syncthreads();
-  int hit_all = 0;
-  for (int i = tid; i < nb * ws.nch; i += kA) {
-    const int h = ws.hitblk[(size_t)e0 * ws.nch + i];
-    if (h) atomicAdd(&s_hit[i / ws.nch], h);
-    hit_all += h;
-  }
-  hit_all = ech::block_sum<kA>(hit_all, scr);   // contains the barrier s_hit needs
-  for (int i = tid; i < nb; i += kA) {
-    int32_t* st = stats + 4 * (e0 + i);
-    st[0] = s_hit[i];
-    st[1] = 0;
-    st[2] = 0;
-    st[3] = 0;
-    ws.lb[e0 + i] = 0;
-  }
-  // the early miss list starts empty: every entry (-1, -1)
-  for (int i = tid; i < 2 * M_early; i += kA) miss_early[i] = -1;
-  // free slots in ring order from the head, up to the early demand bound
-  int found = 0;
-  for (int i0 = 0; i0 < C && found < M_early; i0 += kWinA) {   // block-uniform
-#pragma unroll
-    for (int j = 0; j < kWinA / kA; ++j) {   // coalesced loads, all in flight
-      const int pos = i0 + j * kA + tid;
-      int p = head + min(pos, C - 1);
-      if (p >= C) p -= C;
-      const int pv = slot_pin[p];
-      s_fr[j * kA + tid] = (pos < C && pv != ep) ? 1 : 0;
-    }
-    __syncthreads();
-    const uint4 f0 = reinterpret_cast<const uint4*>(s_fr)[tid];   // positions i0 + 16 tid .. +15
-    const uint32_t fw[4] = {f0.x, f0.y, f0.z, f0.w};
-    int cnt = 0;
-#pragma unroll
-    for (int qq = 0; qq < 4; ++qq) cnt += __popc(fw[qq]);   // flags are 0/1 bytes
-    int tot;
-    int rank = found + ech::block_excl_scan<kA>(cnt, scr, &tot);
-    if (rank < M_early) {
-#pragma unroll
-      for (int qq = 0; qq < 4; ++qq) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          if ((fw[qq] >> (8 * e)) & 1u) {
-            if (rank < M_early) {
-              int p = head + i0 + 16 * tid + 4 * qq + e;
-              if (p >= C) p -= C;
-              ws.freelist[rank] = p;
-            }
-            ++rank;
-          }
-        }
-      }
-    }
-    found += tot;
-    __syncthreads();   // s_fr is rewritten by the next window
-  }
-  if (tid == 0) {
+  // the launch starts from empty lists and cleared control words
+  for (int i = j * kT + tid; i < 2 * M_early; i += nwg * kT) miss_early[i] = -1;
+  for (int i = j * kT + tid; i < M_early; i += nwg * kT) ws.freelist[i] = 0;
+  for (int b = e0 + j * kT + tid; b < e1; b += nwg * kT) ws.lb[b] = 0;
+  for (int i = j * kT + tid; i < (C + kRankSlice - 1) / kRankSlice; i += nwg * kT) ws.rlb[i] = 0;
+  if (j == 0 && tid == 0) {
     Ctl* cl = ws.ctl;
     cl->next_group = 0;
-    cl->a_done = 0;
     cl->c_done = 0;
-    cl->nfree = min(found, M_early);
+    cl->ep = ep;
+    cl->head = head;
     cl->finished = 0;
-    ctr[ECH_CTR_EPOCH] = ep;
-    ctr[ECH_CTR_NPINNED] = hit_all;
+    cl->nfree = 0;
+    cl->first_incomplete = INT32_MAX;
     ctr[ECH_CTR_NEVICT] = 0;
     ctr[ECH_CTR_NWANT] = 0;
     ctr[ECH_CTR_NMISS_EARLY] = 0;
     ctr[ECH_CTR_NCOPIED_EARLY] = 0;
+    ctr[ECH_CTR_NPINNED] = 0;
+  }
+  const u64 t0 = wall_clock64();
+  int covered = 0;
+  for (int win = 0;; ++win) {   // block-uniform
+    const int p0 = win * kPinWin;
+    if (p0 >= C) break;
+    const int wsz = min(kPinWin, C - p0);
+    int pinned = 0;
+    for (int b = e0 + j; b < e1; b += nwg) {
+      const float th = theta[b];
+      if (th != th) continue;
+      pinned += pin_sequence_window(q, w, kc, ksc, b, tok0[b], lens[b], th, slot2tok, C, head, p0, wsz, ep, slot_pin,
+                                    s_pos, scr);
+    }
+    pinned = ech::block_sum<kT>(pinned, scr);
+    if (tid == 0) {
+      if (pinned) atomicAdd(&ws.ctl->pin_total, pinned);
+      atomicAdd(&ws.ctl->pin_done, 1);
+      for (;;) {   // every workgroup's count of this window is in
+        if (ld_dev(&ws.ctl->pin_done) >= nwg * (win + 1)) break;
+        if (wall_clock64() - t0 > kSpinTicks) {
+          set_status(ctr, ECH_ST_TIMEOUT);
+          break;
+        }
+        __builtin_amdgcn_s_sleep(4);
+      }
+      s_tot = ld_dev(&ws.ctl->pin_total);
+    }
+    __syncthreads();
+    covered += wsz;
+    const int enough = covered - s_tot >= M_early;
+    __syncthreads();   // s_tot is rewritten after the next window
+    if (enough) break;
   }
 }
 
@@ -362,20 +361,121 @@ struct FusedArgs {
   int32_t M_early;
   int32_t* ctr;
   int32_t* stats;
-  // recall
-  const v4u* host;         // device view of the pinned pool
-  v4u* dev;
-  int row16;
-  int n_alloc_wg, n_copy_wg;
+  const int32_t* slot_pin;
+  int n_alloc_wg;
   FWs ws;
 };
 
 constexpr int kFusedLds = kWavesF * kNS * kDecTile + kWavesF * 2 * 64 * 4;
 static_assert(kFusedLds >= 4 * kMaxCap + 64, "alloc list fits");
-static_assert(kFusedLds >= 8 * (kT * kCopyUnroll), "copy entries fit");
+static_assert(kFusedLds >= kRankSlice, "rank flags fit");
+
+// The free list: unpinned slots in ring order from the head (the pins kernel
+// stamped every pinned slot of the windows it took, and those hold enough
+// unpinned ones). Rank workgroup i takes ring slices i, i + kRankWg, ... of
+// kRankSlice positions; a slice's first rank comes from the slices before it
+// (decoupled look-back); entries are published one by one as slot + 1, and
+// the slice holding the last needed rank (or the ring's end) publishes the
+// count.
+__device__ void rank_role(const FusedArgs& a, int i, uint8_t* smem) {
+  __shared__ int scr[kT / 64];
+  __shared__ u64 s_ex;
+  uint8_t* s_fr = smem;
+  const int tid = threadIdx.x;
+  const int ep = a.ws.ctl->ep, head = a.ws.ctl->head, C = a.C, M = a.M_early;
+  const int nslice = (C + kRankSlice - 1) / kRankSlice;
+  const u64 t0 = wall_clock64();
+  for (int k = i; k < nslice; k += kRankWg) {   // block-uniform
+    const int i0 = k * kRankSlice;
+#pragma unroll
+    for (int j = 0; j < kRankSlice / kT; ++j) {   // coalesced loads, all in flight
+      const int pos = i0 + j * kT + tid;
+      int p = head + min(pos, C - 1);
+      if (p >= C) p -= C;
+      const int pv = a.slot_pin[p];
+      s_fr[j * kT + tid] = (pos < C && pv != ep) ? 1 : 0;
+    }
+    __syncthreads();
+    // thread t ranks positions i0 + 16t .. +15
+    const uint4 f0 = reinterpret_cast<const uint4*>(s_fr)[tid];
+    const uint32_t fw[4] = {f0.x, f0.y, f0.z, f0.w};
+    int cnt = 0;
+#pragma unroll
+    for (int qq = 0; qq < 4; ++qq) cnt += __popc(fw[qq]);   // flags are 0/1 bytes
+    int tot;
+    int local = ech::block_excl_scan<kT>(cnt, scr, &tot);
+    if (tid == 0) {   // this slice's first rank
+      st_dev(&a.ws.rlb[k], kAgg | (u64)tot);
+      u64 ex = 0;
+      for (int kk = k - 1; kk >= 0; --kk) {
+        u64 v;
+        spin_until([&] { return ld_dev(&a.ws.rlb[kk]); }, [](u64 x) { return (x & (kAgg | kInc)) != 0ull; }, a.ctr,
+                   t0, &v);
+        ex += v & 0xffffffffull;
+        if (v & kInc) break;
+      }
+      st_dev(&a.ws.rlb[k], kInc | (ex + (u64)tot));
+      if ((ex < (u64)M && ex + (u64)tot >= (u64)M) || (k == nslice - 1 && ex < (u64)M))
+        st_dev(&a.ws.ctl->nfree, kFin | min(ex + (u64)tot, (u64)M));
+      s_ex = ex;
+    }
+    __syncthreads();
+    const int ex = (int)min(s_ex, (u64)M);
+    int rank = ex + local;
+    if (rank < M) {
+#pragma unroll
+      for (int qq = 0; qq < 4; ++qq) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          if ((fw[qq] >> (8 * e)) & 1u) {
+            if (rank < M) {
+              int p = head + i0 + 16 * tid + 4 * qq + e;
+              if (p >= C) p -= C;
+              st_dev(&a.ws.freelist[rank], p + 1);
+            }
+            ++rank;
+          }
+        }
+      }
+    }
+    const bool done = s_ex + (u64)tot >= (u64)M;
+    __syncthreads();   // s_fr and s_ex are rewritten by the next slice
+    if (done) break;
+  }
+  if (i == 0 && tid == 0) {
+    a.ctr[ECH_CTR_EPOCH] = ep;
+    a.ws.ctl->pin_done = 0;   // the pins kernel of the next call starts from zero
+    a.ws.ctl->pin_total = 0;
+  }
+}
+
+// The first rank of early sequence b: the takes of the early sequences before
+// it, read back to the nearest one that has published its inclusive prefix.
+// The words of up to kT predecessors are read at once, one per thread (a
+// walk of one dependent load per predecessor costs tens of microseconds while
+// the PCIe copy loads the memory system).
+__device__ int first_rank(const FusedArgs& a, int b, u64 t0, int* scr, int* s_min) {
+  const int tid = threadIdx.x;
+  int base = 0;
+  for (int off = 0; off < b - a.e0; off += kT) {   // block-uniform
+    const int bb = b - 1 - off - tid;
+    u64 v = 0;
+    if (bb >= a.e0)
+      spin_until([&] { return ld_dev(&a.ws.lb[bb]); }, [](u64 x) { return (x & (kAgg | kInc)) != 0ull; }, a.ctr,
+                 t0, &v);
+    if (tid == 0) *s_min = kT;
+    __syncthreads();
+    if (bb >= a.e0 && (v & kInc)) atomicMin(s_min, tid);
+    __syncthreads();
+    const int nearest = *s_min;   // the nearest inclusive prefix in this chunk, or kT
+    base += ech::block_sum<kT>((bb >= a.e0 && tid <= nearest) ? (int)(v & 0xffffffffull) : 0, scr);
+    if (nearest < kT) break;
+  }
+  return base;
+}
 
 // One early sequence: its misses in token order, its ranks, its slots.
-__device__ void alloc_sequence(const FusedArgs& a, int b, int* s_list, int* scr, u64* s_bcast) {
+__device__ void alloc_sequence(const FusedArgs& a, int b, int nfree, int* s_list, int* scr, int* s_min) {
   const int tid = threadIdx.x;
   const int len = a.lens[b];
   const float th = a.theta[b];
@@ -383,7 +483,7 @@ __device__ void alloc_sequence(const FusedArgs& a, int b, int* s_list, int* scr,
   const int64_t g0 = a.tok0[b];
   const u64* mk = a.ws.masks + (size_t)b * a.ws.wpr * kWords;
   const u64 t0 = wall_clock64();
-  int want = 0;
+  int want = 0, hits = 0;
   for (int base = 0; base < nw; base += kT) {   // block-uniform
     const int i = base + tid;
     // One thread waits for the window's last wave (the waves of a row are
@@ -392,7 +492,7 @@ __device__ void alloc_sequence(const FusedArgs& a, int b, int* s_list, int* scr,
     if (tid == 0) {
       const u64* wl = mk + (size_t)(min(base + kT, nw) - 1) * kWords;
       u64 v;
-      spin_until([&] { return ld_dev(wl); }, [](u64 x) { return (x >> 32) == 1ull; }, a.ctr, t0, &v);
+      spin_until([&] { return ld_dev(wl); }, [](u64 x) { return (x & kTag) != 0ull; }, a.ctr, t0, &v);
     }
     __syncthreads();
     u64 wd[kWords];
@@ -400,13 +500,14 @@ __device__ void alloc_sequence(const FusedArgs& a, int b, int* s_list, int* scr,
     if (i < nw) {
       u64* wp = const_cast<u64*>(mk) + (size_t)i * kWords;
       u64 v;
-      spin_until([&] { return ld_dev(wp); }, [](u64 x) { return (x >> 32) == 1ull; }, a.ctr, t0, &v);
+      spin_until([&] { return ld_dev(wp); }, [](u64 x) { return (x & kTag) != 0ull; }, a.ctr, t0, &v);
       wd[0] = v;
 #pragma unroll
       for (int k = 1; k < kWords; ++k) {
-        spin_until([&] { return ld_dev(wp + k); }, [](u64 x) { return (x >> 32) == 1ull; }, a.ctr, t0, &v);
+        spin_until([&] { return ld_dev(wp + k); }, [](u64 x) { return (x & kTag) != 0ull; }, a.ctr, t0, &v);
         wd[k] = v;
       }
+      hits += (int)(wd[0] >> 33);   // the wave's resident tokens above theta
 #pragma unroll
       for (int k = 0; k < kWords; ++k) {
         c += __popc((uint32_t)wd[k]);
@@ -425,31 +526,36 @@ __device__ void alloc_sequence(const FusedArgs& a, int b, int* s_list, int* scr,
     want += tot;
   }
   const int take = min(a.cap, want);
-  // this sequence's first rank: the takes of the early sequences before it
+  hits = ech::block_sum<kT>(hits, scr);
+  if (tid == 0) st_dev(&a.ws.lb[b], kAgg | (u64)take);   // later sequences need only this
+  const int base = first_rank(a, b, t0, scr, s_min);
   if (tid == 0) {
-    st_dev(&a.ws.lb[b], kAgg | (u64)take);
-    u64 base = 0;
-    for (int bb = b - 1; bb >= a.e0; --bb) {
-      u64 v;
-      spin_until([&] { return ld_dev(&a.ws.lb[bb]); }, [](u64 x) { return (x & (kAgg | kInc)) != 0ull; }, a.ctr,
-                 t0, &v);
-      base += v & 0xffffffffull;
-      if (v & kInc) break;
+    st_dev(&a.ws.lb[b], kInc | (u64)(base + take));
+    if (b == a.e1 - 1) {   // the last early sequence knows the list's length
+      const int total = base + take;
+      const int n_alloc = min(total, nfree);
+      st_dev(&a.ws.ctl->finished, kFin | (u64)n_alloc);
+      a.ctr[ECH_CTR_NWANT] = total;
+      a.ctr[ECH_CTR_NMISS_EARLY] = n_alloc;
+      if (n_alloc > 0) {
+        int pv;
+        spin_until([&] { return ld_dev(&a.ws.freelist[n_alloc - 1]); }, [](int x) { return x != 0; }, a.ctr, t0,
+                   &pv);
+        const int last = pv - 1;
+        a.ctr[ECH_CTR_HEAD] = (last + 1 == a.C) ? 0 : last + 1;
+      }
     }
-    st_dev(&a.ws.lb[b], kInc | (base + (u64)take));
-    *s_bcast = base;
   }
-  __syncthreads();   // s_list complete, base published in LDS
-  const int base = (int)*s_bcast;
-  const int nfree = a.ws.ctl->nfree;
   const int fetched = max(0, min(nfree - base, take));
   int ev = 0;
   for (int r = tid; r < fetched; r += kT) {
     const int m = base + r;
-    const int p = a.ws.freelist[m];
+    int pv;
+    spin_until([&] { return ld_dev(&a.ws.freelist[m]); }, [](int x) { return x != 0; }, a.ctr, t0, &pv);
+    const int p = pv - 1;
     const int g = s_list[r];
     if (p < 0 || p >= a.C || g < 0 || g >= a.P) {
-      set_status(a.ctr, ECH_ST_OVERFLOW);   // unreachable unless the rank phase and the masks disagree
+      set_status(a.ctr, ECH_ST_OVERFLOW);   // unreachable unless the rank workgroups and the masks disagree
       continue;
     }
     const int u = a.slot2tok[p];
@@ -464,129 +570,29 @@ __device__ void alloc_sequence(const FusedArgs& a, int b, int* s_list, int* scr,
   const int evs = ech::block_sum<kT>(ev, scr);
   if (tid == 0) {
     int32_t* st = a.stats + 4 * b;
+    st[0] = hits;
     st[1] = fetched;
     st[2] = want - fetched;   // wanted (before the cap) and not fetched
     st[3] = evs;
     if (evs) atomicAdd(&a.ctr[ECH_CTR_NEVICT], evs);
+    if (hits) atomicAdd(&a.ctr[ECH_CTR_NPINNED], hits);
   }
-  __syncthreads();   // s_list and s_bcast are reused by the next sequence
+  __syncthreads();   // s_list is reused by the next sequence
 }
 
 __device__ void alloc_role(const FusedArgs& a, int j, uint8_t* smem) {
   __shared__ int scr[kT / 64];
-  __shared__ u64 s_bcast;
+  __shared__ int s_min, s_nfree;
   int* s_list = reinterpret_cast<int*>(smem);
-  for (int b = a.e0 + j; b < a.e1; b += a.n_alloc_wg) alloc_sequence(a, b, s_list, scr, &s_bcast);
-  if (threadIdx.x == 0) {
-    const int prev = atomicAdd(&a.ws.ctl->a_done, 1);
-    if (prev == a.n_alloc_wg - 1) {   // the last alloc workgroup: totals, head, and the end mark
-      u64 v;
-      spin_until([&] { return ld_dev(&a.ws.lb[a.e1 - 1]); }, [](u64 x) { return (x & kInc) != 0ull; }, a.ctr,
-                 wall_clock64(), &v);
-      const int total = (int)(v & 0xffffffffull);
-      const int n_alloc = min(total, a.ws.ctl->nfree);
-      a.ctr[ECH_CTR_NWANT] = total;
-      a.ctr[ECH_CTR_NMISS_EARLY] = n_alloc;
-      if (n_alloc > 0) {
-        const int last = a.ws.freelist[n_alloc - 1];
-        a.ctr[ECH_CTR_HEAD] = (last + 1 == a.C) ? 0 : last + 1;
-      }
-      st_dev(&a.ws.ctl->finished, kFin | (u64)n_alloc);
-    }
+  if (threadIdx.x == 0) {   // the free count, published by the rank workgroups early in the launch
+    u64 nf;
+    spin_until([&] { return ld_dev(&a.ws.ctl->nfree); }, [](u64 x) { return (x & kFin) != 0ull; }, a.ctr,
+               wall_clock64(), &nf);
+    s_nfree = (int)(nf & 0xffffffffull);
   }
-}
-
-__device__ void copy_role(const FusedArgs& a, uint8_t* smem) {
-  __shared__ int s_g, s_stop;
-  u64* s_e = reinterpret_cast<u64*>(smem);
-  const int tid = threadIdx.x;
-  const int rg = max(1, (kT * kCopyUnroll) / a.row16);   // rows per group
-  const u64 t0 = wall_clock64();
-  u64* fin = &a.ws.ctl->finished;
-  const u64* ent = reinterpret_cast<const u64*>(a.miss);
-  for (;;) {
-    if (tid == 0) {
-      if (ld_dev(fin) & kFin) {
-        s_stop = 1;
-      } else {
-        s_stop = 0;
-        s_g = atomicAdd(&a.ws.ctl->next_group, 1);
-      }
-    }
-    __syncthreads();
-    if (s_stop) break;
-    const int m0 = s_g * rg;
-    // One thread waits for the group's last entry (entries are written in
-    // about rank order) or the end mark, then one thread per row reads its
-    // entry: few polls while the allocation runs.
-    if (tid == 0) {
-      const int m = min(m0 + rg, a.M_early) - 1;
-      for (;;) {
-        if (m < m0 || ld_dev(ent + m) != kNone) break;
-        const u64 f = ld_dev(fin);
-        if ((f & kFin) && m >= (int)(f & 0xffffffffull)) break;
-        if (wall_clock64() - t0 > kSpinTicks) {
-          set_status(a.ctr, ECH_ST_TIMEOUT);
-          break;
-        }
-        __builtin_amdgcn_s_sleep(16);
-      }
-    }
-    __syncthreads();
-    if (tid < rg) {   // one thread per row of the group reads its entry
-      const int m = m0 + tid;
-      u64 e = kNone;
-      if (m < a.M_early) {
-        for (;;) {
-          e = ld_dev(ent + m);
-          if (e != kNone) break;
-          const u64 f = ld_dev(fin);
-          if ((f & kFin) && m >= (int)(f & 0xffffffffull)) break;   // past the end: nothing to copy
-          if (wall_clock64() - t0 > kSpinTicks) {
-            set_status(a.ctr, ECH_ST_TIMEOUT);
-            break;
-          }
-          __builtin_amdgcn_s_sleep(16);
-        }
-      }
-      s_e[tid] = e;
-    }
-    __syncthreads();
-    v4u v[kCopyUnroll];
-    int64_t dst[kCopyUnroll];
-#pragma unroll
-    for (int u = 0; u < kCopyUnroll; ++u) {   // all host loads in flight, then the stores
-      const int i = tid + u * kT;
-      dst[u] = -1;
-      if (i < rg * a.row16) {
-        const int row = i / a.row16, c = i - row * a.row16;
-        const u64 e = s_e[row];
-        if (e != kNone) {
-          const int g = (int)(uint32_t)e, p = (int)(uint32_t)(e >> 32);
-          if (g >= 0 && g < a.P && p >= 0 && p < a.C) {
-            v[u] = __builtin_nontemporal_load(a.host + (int64_t)g * a.row16 + c);
-            dst[u] = (int64_t)p * a.row16 + c;
-          } else if (c == 0) {
-            set_status(a.ctr, ECH_ST_BADMISS);
-          }
-        }
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < kCopyUnroll; ++u)
-      if (dst[u] >= 0) __builtin_nontemporal_store(v[u], a.dev + dst[u]);
-    __syncthreads();   // s_g, s_e are rewritten by the next group
-  }
-  if (tid == 0) {
-    const int prev = atomicAdd(&a.ws.ctl->c_done, 1);
-    if (prev == a.n_copy_wg - 1) {   // the last copy workgroup: every claimed group is copied
-      const int n_alloc = (int)(ld_dev(fin) & 0xffffffffull);
-      const int claimed = ld_dev(&a.ws.ctl->next_group);
-      const int ncopied = (int)min((int64_t)claimed * rg, (int64_t)n_alloc);
-      a.ctr[ECH_CTR_NCOPIED_EARLY] = ncopied;
-      atomicAdd(&a.ctr[ECH_CTR_RECALLED], ncopied);
-    }
-  }
+  __syncthreads();
+  const int nfree = s_nfree;
+  for (int b = a.e0 + j; b < a.e1; b += a.n_alloc_wg) alloc_sequence(a, b, nfree, s_list, scr, &s_min);
 }
 
 __device__ void score_role(const FusedArgs& a, int fb, uint8_t* smem) {
@@ -616,27 +622,178 @@ __device__ void score_role(const FusedArgs& a, int fb, uint8_t* smem) {
     sl[j] = above[j] ? a.tok2slot[g0 + t] : 0;   // the lookups of the four tokens in flight together
   }
   u64 bal[kTPW / 4];
+  int hits = 0;
 #pragma unroll
-  for (int j = 0; j < kTPW / 4; ++j) bal[j] = __ballot(above[j] && !(sl[j] >= 0 && sl[j] < a.C));
+  for (int j = 0; j < kTPW / 4; ++j) {
+    const bool res = sl[j] >= 0 && sl[j] < a.C;
+    bal[j] = __ballot(above[j] && !res);
+    hits += __popcll(__ballot(above[j] && res));
+  }
   if (lane < kWords) {
     u64 m = bal[0];
 #pragma unroll
     for (int j = 1; j < kTPW / 4; ++j)
       if ((lane >> 1) == j) m = bal[j];
     const uint32_t half = (lane & 1) ? (uint32_t)(m >> 32) : (uint32_t)m;
-    st_dev(a.ws.masks + ((size_t)r * a.ws.wpr + wi) * kWords + lane, kTag | half);
+    // word 0 also carries the wave's hits (resident tokens above theta)
+    st_dev(a.ws.masks + ((size_t)r * a.ws.wpr + wi) * kWords + lane,
+           kTag | half | (lane == 0 ? (u64)hits << 33 : 0ull));
   }
 }
 
 __global__ __launch_bounds__(kT) void fused_kernel(FusedArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[kFusedLds];
   const int bid = blockIdx.x;
-  if (bid < a.n_alloc_wg) {
-    alloc_role(a, bid, smem);
-  } else if (bid < a.n_alloc_wg + a.n_copy_wg) {
-    copy_role(a, smem);
+  if (bid == 0 && threadIdx.x == 0) st_dev(&a.ctr[ECH_CTR_LIVE], 1);   // the live copier may start
+  if (bid < kRankWg) {
+    rank_role(a, bid, smem);
+  } else if (bid < kRankWg + a.n_alloc_wg) {
+    alloc_role(a, bid - kRankWg, smem);
   } else {
-    score_role(a, bid - a.n_alloc_wg - a.n_copy_wg, smem);
+    score_role(a, bid - kRankWg - a.n_alloc_wg, smem);
+  }
+}
+
+
+// ------------------------------------------------------------------ live copier
+// A separate launch on another stream, beside the fused launch: copies the
+// early rows over PCIe as the alloc workgroups write their miss-list entries.
+// It starts copying only once the fused launch has started this step's list
+// (ctr[ECH_CTR_LIVE] = 1; ech_recall(ECH_EARLY) clears it at the end of the
+// step), claims groups of consecutive ranks in order, waits for each group's
+// entries, and stops at the end of the list. Any wait without progress for
+// kPatienceTicks (the fused launch not running, e.g. queued behind this one)
+// makes it give up: the copied groups form a prefix of the list
+// (ctr[ECH_CTR_NCOPIED_EARLY]) and ech_recall(ECH_EARLY) copies the rest, so
+// the result never depends on how the two launches are scheduled.
+constexpr int kLive = 32;                     // copier workgroups (more slow the scoring beside them more than they gain)
+constexpr u64 kPatienceTicks = 100000ull;     // 1 ms at the 100 MHz constant-rate clock
+
+struct LiveArgs {
+  const v4u* host;                            // device view of the pinned pool
+  v4u* dev;
+  int row16;
+  int64_t P;
+  int32_t C;
+  const int32_t* miss;
+  int32_t M_early;
+  int32_t* ctr;
+  Ctl* ctl;
+};
+
+__global__ __launch_bounds__(kT) void early_live_copy_kernel(LiveArgs a) {
+  __shared__ u64 s_e[kT * kCopyUnroll];
+  __shared__ int s_g, s_state;                // state: 0 copy group s_g, 1 end of list, 2 gave up
+  const int tid = threadIdx.x;
+  const int rg = max(1, (kT * kCopyUnroll) / a.row16);   // rows per group
+  u64* fin = &a.ctl->finished;
+  const u64* ent = reinterpret_cast<const u64*>(a.miss);
+  if (tid == 0) {   // wait for the fused launch to start this step's list
+    const u64 t0 = wall_clock64();
+    s_state = 0;
+    while (ld_dev(&a.ctr[ECH_CTR_LIVE]) == 0) {
+      if (wall_clock64() - t0 > kPatienceTicks) {
+        s_state = 2;
+        break;
+      }
+      __builtin_amdgcn_s_sleep(16);
+    }
+  }
+  __syncthreads();
+  int gave_up_at = -1;
+  if (s_state == 0) {
+    for (;;) {
+      if (tid == 0) {
+        const int g = atomicAdd(&a.ctl->next_group, 1);
+        const int m0 = g * rg;
+        const u64 f0 = ld_dev(fin);
+        s_g = g;
+        s_state = ((f0 & kFin) && m0 >= (int)(f0 & 0xffffffffull)) || m0 >= a.M_early ? 1 : 0;
+        if (s_state == 0) {
+          // the group's last entry (entries are written in about rank order)
+          // or the end mark; patience restarts with every change seen
+          const int m = min(m0 + rg, a.M_early) - 1;
+          u64 t0 = wall_clock64();
+          for (;;) {
+            if (ld_dev(ent + m) != kNone) break;
+            const u64 f = ld_dev(fin);
+            if ((f & kFin) && m >= (int)(f & 0xffffffffull)) break;
+            if (wall_clock64() - t0 > kPatienceTicks) {
+              s_state = 2;
+              break;
+            }
+            __builtin_amdgcn_s_sleep(16);
+          }
+        }
+      }
+      __syncthreads();
+      if (s_state != 0) {
+        if (s_state == 2) gave_up_at = s_g;
+        break;
+      }
+      const int m0 = s_g * rg;
+      if (tid < rg) {   // one thread per row of the group reads its entry
+        const int m = m0 + tid;
+        u64 e = kNone;
+        if (m < a.M_early) {
+          const u64 t0 = wall_clock64();
+          for (;;) {
+            e = ld_dev(ent + m);
+            if (e != kNone) break;
+            const u64 f = ld_dev(fin);
+            if ((f & kFin) && m >= (int)(f & 0xffffffffull)) break;   // past the end: nothing to copy
+            if (wall_clock64() - t0 > kPatienceTicks) {
+              atomicOr(&s_state, 2);
+              break;
+            }
+            __builtin_amdgcn_s_sleep(16);
+          }
+        }
+        s_e[tid] = e;
+      }
+      __syncthreads();
+      if (s_state != 0) {   // a row of this group never came: the group is not copied
+        gave_up_at = s_g;
+        break;
+      }
+      v4u v[kCopyUnroll];
+      int64_t dst[kCopyUnroll];
+#pragma unroll
+      for (int u = 0; u < kCopyUnroll; ++u) {   // all host loads in flight, then the stores
+        const int i = tid + u * kT;
+        dst[u] = -1;
+        if (i < rg * a.row16) {
+          const int row = i / a.row16, c = i - row * a.row16;
+          const u64 e = s_e[row];
+          if (e != kNone) {
+            const int g = (int)(uint32_t)e, p = (int)(uint32_t)(e >> 32);
+            if (g >= 0 && g < a.P && p >= 0 && p < a.C) {
+              v[u] = __builtin_nontemporal_load(a.host + (int64_t)g * a.row16 + c);
+              dst[u] = (int64_t)p * a.row16 + c;
+            } else if (c == 0) {
+              set_status(a.ctr, ECH_ST_BADMISS);
+            }
+          }
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < kCopyUnroll; ++u)
+        if (dst[u] >= 0) __builtin_nontemporal_store(v[u], a.dev + dst[u]);
+      __syncthreads();   // s_g, s_e, s_state are rewritten by the next group
+    }
+  }
+  if (tid == 0) {
+    if (gave_up_at >= 0) atomicMin(&a.ctl->first_incomplete, gave_up_at);
+    const int prev = atomicAdd(&a.ctl->c_done, 1);
+    if (prev == kLive - 1) {   // the last copier workgroup: the copied prefix
+      const u64 f = ld_dev(fin);
+      int64_t groups = min(ld_dev(&a.ctl->next_group), ld_dev(&a.ctl->first_incomplete));
+      int64_t ncopied = groups * rg;
+      if (f & kFin) ncopied = min(ncopied, (int64_t)(f & 0xffffffffull));
+      ncopied = min(ncopied, (int64_t)a.M_early);
+      a.ctr[ECH_CTR_NCOPIED_EARLY] = (int)ncopied;
+      atomicAdd(&a.ctr[ECH_CTR_RECALLED], (int)ncopied);
+    }
   }
 }
 
@@ -644,9 +801,9 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 
 }  // namespace
 
-extern "C" size_t ech_index_logits_early_ws_bytes(int R, int max_len, int32_t M_early) {
-  if (R < 1 || max_len < 0 || M_early < 0) return 0;
-  return fused_layout(R, max_len, M_early, nullptr, nullptr);
+extern "C" size_t ech_index_logits_early_ws_bytes(int R, int max_len, int32_t C, int32_t M_early) {
+  if (R < 1 || max_len < 0 || C < 1 || M_early < 0) return 0;
+  return fused_layout(R, max_len, C, M_early, nullptr, nullptr);
 }
 
 extern "C" int ech_index_logits_early(const void* q, const float* w, const void* kcache, int kdtype,
@@ -654,35 +811,25 @@ extern "C" int ech_index_logits_early(const void* q, const float* w, const void*
                                       int H, int D, int max_len, float* logits, int64_t ld, int e0, int e1,
                                       const float* theta, int cap, int32_t* tok2slot, int64_t P, int32_t* slot2tok,
                                       int32_t* slot_pin, int32_t C, int32_t* miss_early, int32_t M_early,
-                                      int32_t* ctr, int32_t* stats, const void* host_pool, int64_t row_bytes,
-                                      void* dev_cache, void* ws, size_t ws_bytes, void* stream) {
+                                      int32_t* ctr, int32_t* stats, void* ws, size_t ws_bytes, void* stream) {
   if (!q || !w || !kcache || !row_tok0 || !row_len || !logits || !theta || !tok2slot || !slot2tok || !slot_pin ||
-      !miss_early || !ctr || !stats || !host_pool || !dev_cache || !ws)
+      !miss_early || !ctr || !stats || !ws)
     return ECH_EINVAL;
   if (kdtype != ECH_KEY_FP8) return ECH_EUNSUPPORTED;
   if (!kscale || H != kH || D != kD || R < 1 || R > kMaxB || max_len < 0 || ld < max_len) return ECH_EINVAL;
   if (e0 < 0 || e1 <= e0 || e1 > R || cap < 0 || cap > kMaxCap) return ECH_EINVAL;
   if (P < 1 || P >= INT32_MAX || C < 1 || C > (1 << 30) || M_early < 0) return ECH_EINVAL;
   if ((int64_t)M_early < (int64_t)(e1 - e0) * std::min(cap, max_len)) return ECH_EINVAL;
-  if (row_bytes < 16 || row_bytes % 16 != 0 || row_bytes > 16 * kT * kCopyUnroll) return ECH_EINVAL;
-  if (!aligned16(q) || !aligned16(kcache) || !aligned16(dev_cache) || !aligned16(host_pool)) return ECH_EINVAL;
+  if (!aligned16(q) || !aligned16(kcache)) return ECH_EINVAL;
   if ((reinterpret_cast<uintptr_t>(miss_early) & 7u) || (reinterpret_cast<uintptr_t>(ws) & 255u)) return ECH_EINVAL;
-  if (ws_bytes < ech_index_logits_early_ws_bytes(R, max_len, M_early)) return ECH_EINVAL;
-  void* hdev = nullptr;
-  if (hipHostGetDevicePointer(&hdev, const_cast<void*>(host_pool), 0) != hipSuccess || !hdev) {
-    (void)hipGetLastError();
-    return ECH_EINVAL;
-  }
+  if (ws_bytes < ech_index_logits_early_ws_bytes(R, max_len, C, M_early)) return ECH_EINVAL;
   FWs fw;
-  fused_layout(R, max_len, M_early, &fw, static_cast<char*>(ws));
+  fused_layout(R, max_len, C, M_early, &fw, static_cast<char*>(ws));
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   const uint16_t* qq = static_cast<const uint16_t*>(q);
   const uint8_t* kk = static_cast<const uint8_t*>(kcache);
-  hipLaunchKernelGGL(fused_pin_kernel, dim3(fw.nch, e1 - e0), dim3(kT), 0, s, qq, w, kk, kscale, row_tok0, row_len,
-                     theta, e0, tok2slot, P, C, slot_pin, ctr, fw);
-  ECH_LAUNCH_CHECK();
-  hipLaunchKernelGGL(fused_rank_kernel, dim3(1), dim3(kA), 0, s, slot_pin, C, e0, e1, miss_early, M_early, ctr,
-                     stats, fw);
+  hipLaunchKernelGGL(fused_pins_kernel, dim3(std::min(e1 - e0, kMaxPinWg)), dim3(kT), 0, s, qq, w, kk, kscale,
+                     row_tok0, row_len, theta, e0, e1, slot2tok, C, slot_pin, miss_early, M_early, ctr, fw);
   ECH_LAUNCH_CHECK();
   FusedArgs a;
   a.q = qq;
@@ -706,15 +853,42 @@ extern "C" int ech_index_logits_early(const void* q, const float* w, const void*
   a.M_early = M_early;
   a.ctr = ctr;
   a.stats = stats;
+  a.slot_pin = slot_pin;
+  a.n_alloc_wg = std::min(e1 - e0, kMaxAlloc);
+  a.ws = fw;
+  const int64_t blocks = kRankWg + (int64_t)a.n_alloc_wg + (int64_t)a.gx * R;
+  if (blocks > INT32_MAX) return ECH_EINVAL;
+  hipLaunchKernelGGL(fused_kernel, dim3((unsigned)blocks), dim3(kT), 0, s, a);
+  ECH_LAUNCH_CHECK();
+  return ECH_OK;
+}
+
+extern "C" int ech_recall_early_live(const void* host_pool, int64_t P, int64_t row_bytes, void* dev_cache, int32_t C,
+                                     const int32_t* miss_early, int32_t M_early, int32_t* ctr, void* ws,
+                                     void* stream) {
+  if (!host_pool || !dev_cache || !miss_early || !ctr || !ws || P < 1 || P >= INT32_MAX || C < 1 || M_early < 0)
+    return ECH_EINVAL;
+  if (row_bytes < 16 || row_bytes % 16 != 0 || row_bytes > 16 * kT * kCopyUnroll) return ECH_EINVAL;
+  if (!aligned16(dev_cache) || !aligned16(host_pool) || (reinterpret_cast<uintptr_t>(miss_early) & 7u) ||
+      (reinterpret_cast<uintptr_t>(ws) & 255u))
+    return ECH_EINVAL;
+  void* hdev = nullptr;
+  if (hipHostGetDevicePointer(&hdev, const_cast<void*>(host_pool), 0) != hipSuccess || !hdev) {
+    (void)hipGetLastError();
+    return ECH_EINVAL;
+  }
+  if (M_early == 0) return ECH_OK;
+  LiveArgs a;
   a.host = static_cast<const v4u*>(hdev);
   a.dev = static_cast<v4u*>(dev_cache);
   a.row16 = (int)(row_bytes / 16);
-  a.n_alloc_wg = std::min(e1 - e0, kMaxAlloc);
-  a.n_copy_wg = kCopy;
-  a.ws = fw;
-  const int64_t blocks = (int64_t)a.n_alloc_wg + a.n_copy_wg + (int64_t)a.gx * R;
-  if (blocks > INT32_MAX) return ECH_EINVAL;
-  hipLaunchKernelGGL(fused_kernel, dim3((unsigned)blocks), dim3(kT), 0, s, a);
+  a.P = P;
+  a.C = C;
+  a.miss = miss_early;
+  a.M_early = M_early;
+  a.ctr = ctr;
+  a.ctl = reinterpret_cast<Ctl*>(ws);   // the control words lead the fused launch's workspace
+  hipLaunchKernelGGL(early_live_copy_kernel, dim3(kLive), dim3(kT), 0, reinterpret_cast<hipStream_t>(stream), a);
   ECH_LAUNCH_CHECK();
   return ECH_OK;
 }

@@ -42,7 +42,8 @@ import torch
 
 from . import (ECH_EARLY, ECH_FINAL, ECH_PREFILL, LayerState, ech_cache_reset, ech_cache_step,
                ech_cache_step_ws_bytes, ech_index_logits, ech_index_logits_causal, ech_index_logits_early,
-               ech_index_logits_early_ws_bytes, ech_kv_append, ech_recall, ech_topk, ech_topk_ws_bytes)
+               ech_index_logits_early_ws_bytes, ech_kv_append, ech_recall, ech_recall_early_live, ech_topk,
+               ech_topk_ws_bytes)
 
 
 def round_up(x: int, m: int) -> int:
@@ -133,7 +134,7 @@ class DecodeLayer:
                              'cap <= 4096')
         if self.fused:
             # zero-filled once; every call leaves it ready for the next
-            self.ws_fused = torch.zeros(ech_index_logits_early_ws_bytes(self.B, self.max_len, m_early),
+            self.ws_fused = torch.zeros(ech_index_logits_early_ws_bytes(self.B, self.max_len, C, m_early),
                                         dtype=torch.uint8, **dev)
         self.host_pool = host_pool
         if host_pool is not None:
@@ -141,6 +142,7 @@ class DecodeLayer:
         else:
             self.dev_cache = None
         self.s1 = torch.cuda.Stream(device=device)
+        self.ev_fork = torch.cuda.Event()
         self.ev_logits = torch.cuda.Event()
         self.ev_early_maps = torch.cuda.Event()
         self.ev_early = torch.cuda.Event()
@@ -176,14 +178,19 @@ class DecodeLayer:
                          stream=stream)
 
     def scores_launch(self, q: torch.Tensor, stream=None) -> None:
-        """The first launch of a step: the scores, and with the fused path
-        also the first chunk's early fetch (its maps, and the rows of a
-        leading part of its misses copied over PCIe)."""
+        """The first launches of a step: the scores, and with the fused path
+        also the first chunk's early fetch (its maps, written while the
+        scoring runs) and, on S1, the live copy of its rows."""
         if self.fused:
+            s0 = torch.cuda.current_stream() if stream is None else stream
+            self.ev_fork.record(s0)
             b0, b1 = self.chunks[0]
             ech_index_logits_early(q, self.w, self.kcache, self.kscale, self.tok0, self.lens, self.max_len,
                                    self.logits, b0, b1, self.theta[self.parity], self.cap, self.state,
-                                   self.stats_early, self.host_pool, self.dev_cache, self.ws_fused, stream=stream)
+                                   self.stats_early, self.ws_fused, stream=s0)
+            # enqueued after the fused launch, waiting only for the step's start
+            self.s1.wait_event(self.ev_fork)
+            ech_recall_early_live(self.host_pool, self.dev_cache, self.state, self.ws_fused, stream=self.s1)
         else:
             self.logits_only(q, stream=stream)
 
@@ -256,9 +263,10 @@ class DecodeLayer:
         self.parity ^= 1
 
     def _after_fused(self, th, th_next, s0, mark) -> None:
-        """First chunk after the fused launch: the rest of the early rows on
-        S1, the top-k and the FINAL maps on S0; ends with S0 waiting for the
-        early rows (the FINAL recall may reuse a slot they fill)."""
+        """First chunk after the fused launch: on S1, after the live copy,
+        the early rows it left (once the fused launch is done); the top-k and
+        the FINAL maps on S0; ends with S0 waiting for the early rows (the
+        FINAL recall may reuse a slot they fill)."""
         first_b0, first_b1 = self.chunks[0]
         mark('topk', s0)
         ech_topk(self.logits, self.lens, self.max_len, self.k, th, th_next, self.idx, self.kth, self.ws_topk,

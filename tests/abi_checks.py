@@ -74,17 +74,16 @@ def check_recall_rejects_bad_args(lib):
 
 
 def check_index_logits_early_rejects_bad_args(lib):
-    assert lib.ech_index_logits_early_ws_bytes(0, 10, 10) == 0
-    a = lib.ech_index_logits_early_ws_bytes(4, 131072, 2048)
-    b = lib.ech_index_logits_early_ws_bytes(32, 131072, 16384)
+    assert lib.ech_index_logits_early_ws_bytes(0, 10, 10, 10) == 0
+    a = lib.ech_index_logits_early_ws_bytes(4, 131072, 260000, 2048)
+    b = lib.ech_index_logits_early_ws_bytes(32, 131072, 260000, 16384)
     assert 0 < a < b
-    ws = lib.ech_index_logits_early_ws_bytes(4, 1000, 64)
+    ws = lib.ech_index_logits_early_ws_bytes(4, 1000, 500, 64)
 
-    def call(q=FAKE, dt=1, sc=FAKE, R=4, ml=1000, ld=1000, e0=0, e1=4, cap=16, P=4000, C=500, M=64, rb=1152,
-             wsb=ws, wsp=FAKE, pool=FAKE, miss=FAKE):
+    def call(q=FAKE, dt=1, sc=FAKE, R=4, ml=1000, ld=1000, e0=0, e1=4, cap=16, P=4000, C=500, M=64, wsb=ws,
+             wsp=FAKE, miss=FAKE):
         return lib.ech_index_logits_early(q, FAKE, FAKE, dt, sc, FAKE, FAKE, R, 64, 128, ml, FAKE, ld, e0, e1, FAKE,
-                                          cap, FAKE, P, FAKE, FAKE, C, miss, M, FAKE, FAKE, pool, rb, FAKE, wsp, wsb,
-                                          None)
+                                          cap, FAKE, P, FAKE, FAKE, C, miss, M, FAKE, FAKE, wsp, wsb, None)
     assert call(q=None) == -1
     assert call(dt=0) == -3              # bf16 keys: not fused
     assert call(sc=None) == -1
@@ -95,13 +94,19 @@ def check_index_logits_early_rejects_bad_args(lib):
     assert call(cap=5000) == -1
     assert call(cap=17) == -1            # early miss list smaller than (e1 - e0) * cap
     assert call(P=1 << 31) == -1
-    assert call(rb=1150) == -1
-    assert call(rb=65536) == -1
     assert call(wsb=ws - 1) == -1
     assert call(wsp=FAKE + 64) == -1
     assert call(q=FAKE + 8) == -1
     assert call(miss=FAKE + 4) == -1
-    assert call(pool=None) == -1
+
+    def live(pool=FAKE, rb=1152, miss=FAKE, wsp=FAKE, M=64):
+        return lib.ech_recall_early_live(pool, 4000, rb, FAKE, 500, miss, M, FAKE, wsp, None)
+    assert live(pool=None) == -1
+    assert live(rb=1150) == -1
+    assert live(rb=65536) == -1
+    assert live(miss=FAKE + 4) == -1
+    assert live(wsp=FAKE + 64) == -1
+    assert live(M=-1) == -1
 
 
 def check_topk_noalloc_rejects_bad_args(lib):
