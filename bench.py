@@ -141,20 +141,24 @@ def bench_decode(args, wl):
     stats_final = layer.stats_final.cpu().numpy()
     stats_early = layer.stats_early.cpu().numpy()
 
-    # The roofline kernel, timed with HIP events on its launch stream: K
-    # launches back to back (the step's queries) between one pair of events,
-    # so no event sits between launches; the average launch is the span / K.
     s0 = torch.cuda.current_stream()
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    layer.logits_only(qd[args.warmup], stream=s0)
-    ev0.record(s0)
-    for s in range(args.steps):
-        layer.logits_only(qd[args.warmup + s], stream=s0)
-    ev1.record(s0)
-    torch.cuda.synchronize()
-    logits_runs = [ev0.elapsed_time(ev1) / args.steps]
+    if not layer.fused:
+        # The roofline kernel, timed with HIP events on its launch stream: K
+        # launches back to back (the step's queries) between one pair of
+        # events, so no event sits between launches; the average launch is the
+        # span / K.
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        layer.logits_only(qd[args.warmup], stream=s0)
+        ev0.record(s0)
+        for s in range(args.steps):
+            layer.logits_only(qd[args.warmup + s], stream=s0)
+        ev1.record(s0)
+        torch.cuda.synchronize()
+        logits_runs = [ev0.elapsed_time(ev1) / args.steps]
 
-    # Stage breakdown from a few eager steps with events on each stage's stream.
+    # Stage breakdown from eager steps with events on each stage's stream.
+    # With the fused launch these also time the roofline launch inside the
+    # step (beside the live copier), on its own stream.
     marks = {}
     for s in range(n_stage):
         layer.step(qd[args.warmup + args.steps + s], marks)
@@ -243,14 +247,15 @@ def bench_decode(args, wl):
     wall = t1 - t0
     tokens = int(wl.lens.astype(np.int64).sum())
     value = tokens * args.steps / wall
-    logits_ms = float(np.mean(logits_runs))
+    logits_ms = avg_ms('logits') if layer.fused else float(np.mean(logits_runs))
     kbytes = 128 + 4 if wl.kdtype == 'fp8' else 256
     per_token = kbytes + 4                                   # key (+scale) read, score written
     per_launch = tokens * per_token + wl.B * (64 * 128 * 2 + 64 * 4)
     achieved = per_launch / (logits_ms * 1e-3) / 1e9
     flops = tokens * 2 * 64 * 128
-    src = source_hash('logits.hip', 'score.hpp')
-    traffic = measured_traffic('logits_decode_' + wl.name, src)
+    src = source_hash('fused.hip', 'decode.hpp', 'score.hpp') if layer.fused else \
+        source_hash('logits.hip', 'decode.hpp', 'score.hpp')
+    traffic = measured_traffic(('fused_' if layer.fused else 'logits_decode_') + wl.name, src)
     out = {
         'metric': 'decode tokens scored/s (indexer logits + exact top-k + early/final slot-map step + recall), '
                   '1 layer',
@@ -270,15 +275,20 @@ def bench_decode(args, wl):
                    'early_fetch': not args.no_early, 'fused_scores_early_fetch': layer.fused, 'row_bytes': 1152,
                    'launch': 'eager' if args.eager else 'hipGraph replay per step',
                    'topk_first': layer.topk_first},
-        'roofline': {'bound': 'hbm', 'kernel': 'logits_decode_fp8_kernel' if wl.kdtype == 'fp8' else 'logits_decode_kernel',
+        'roofline': {'bound': 'hbm',
+                     'kernel': ('ech_index_logits_early (fused_pins_kernel + fused_kernel: scores, pins, EARLY '
+                                'allocation), inside the step beside the live copier') if layer.fused else
+                     ('logits_decode_fp8_kernel' if wl.kdtype == 'fp8' else 'logits_decode_kernel'),
                      'achieved': achieved,
                      'peak': PEAK_HBM_GBS, 'unit': 'GB/s', 'frac': achieved / PEAK_HBM_GBS,
                      'traffic': traffic, 'algorithmic_bytes_per_launch': per_launch,
                      'avg_launch_us': logits_ms * 1e3,
+                     'timing': ('HIP events on the scores stream around the fused launch in eager steps'
+                                if layer.fused else 'HIP events around K back-to-back launches on its stream'),
                      'mfma_bf16_frac': flops / (logits_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS},
         'stages_us_eager': {k: (avg_ms(k) or 0.0) * 1e3
-                            for k in ('logits', 'topk', 'early', 'early_maps', 'recall_early', 'final',
-                                      'final_maps', 'recall_final')},
+                            for k in ('logits', 'recall_live', 'topk', 'early', 'early_maps', 'recall_early',
+                                      'final', 'final_maps', 'recall_final')},
         'recall': {'rows_per_step': recalled / args.steps, 'bytes_per_step': recalled * 1152 / args.steps},
         'last_step': {'final_hits': int(stats_final[:, 0].sum()), 'final_misses': int(stats_final[:, 1].sum()),
                       'early_fetched': int(stats_early[:, 1].sum()), 'evictions':
@@ -287,7 +297,7 @@ def bench_decode(args, wl):
     }
     st = out['stages_us_eager']
     topk_bytes = tokens * 4 + wl.B * wl.k * 4
-    rec_us = st['recall_early'] + st['recall_final']
+    rec_us = st['recall_live'] + st['recall_early'] + st['recall_final']
     out['stage_rooflines'] = {
         'topk': {'bound': 'hbm', 'algorithmic_bytes': topk_bytes, 'us': st['topk'],
                  'achieved_GBs': topk_bytes / (st['topk'] * 1e-6) / 1e9 if st['topk'] else None,
@@ -296,7 +306,8 @@ def bench_decode(args, wl):
                  'note': 'one read of the scores plus the index output, over the five top-k launches'},
         'recall': {'bound': 'pcie', 'bytes_per_step': out['recall']['bytes_per_step'], 'us': rec_us,
                    'achieved_GBs': out['recall']['bytes_per_step'] / (rec_us * 1e-6) / 1e9 if rec_us else None,
-                   'note': 'EARLY + FINAL recall kernels of eager steps; denominator: pcie.h2d_memcpy_GBs'},
+                   'note': 'the recall kernels of eager steps (live copier beside the scoring, rest of EARLY, '
+                           'FINAL); denominator: pcie.h2d_memcpy_GBs'},
         'attention': {'kernel': 'ech_sparse_attn (span + merge launches)', 'heads': Ha, 'rows_attended': n_sel,
                       'us': attn_us,
                       'bound': 'hbm',

@@ -177,10 +177,11 @@ class DecodeLayer:
         ech_index_logits(q, self.w, self.kcache, self.kscale, self.tok0, self.lens, self.max_len, self.logits,
                          stream=stream)
 
-    def scores_launch(self, q: torch.Tensor, stream=None) -> None:
+    def scores_launch(self, q: torch.Tensor, stream=None, mark=None) -> None:
         """The first launches of a step: the scores, and with the fused path
         also the first chunk's early fetch (its maps, written while the
-        scoring runs) and, on S1, the live copy of its rows."""
+        scoring runs) and, on S1, the live copy of its rows. `mark(name,
+        stream)`, when given, records the copier's span as 'recall_live'."""
         if self.fused:
             s0 = torch.cuda.current_stream() if stream is None else stream
             self.ev_fork.record(s0)
@@ -190,7 +191,11 @@ class DecodeLayer:
                                    self.stats_early, self.ws_fused, stream=s0)
             # enqueued after the fused launch, waiting only for the step's start
             self.s1.wait_event(self.ev_fork)
+            if mark is not None:
+                mark('recall_live', self.s1)
             ech_recall_early_live(self.host_pool, self.dev_cache, self.state, self.ws_fused, stream=self.s1)
+            if mark is not None:
+                mark('recall_live', self.s1)
         else:
             self.logits_only(q, stream=stream)
 
@@ -232,7 +237,7 @@ class DecodeLayer:
         th, th_next = self.theta[self.parity], self.theta[1 - self.parity]
         if scores:
             mark('logits', s0)
-            self.scores_launch(q, stream=s0)
+            self.scores_launch(q, stream=s0, mark=mark if marks is not None else None)
             mark('logits', s0)
         if logits_done is not None:
             logits_done.record(s0)
