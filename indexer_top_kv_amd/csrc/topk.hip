@@ -2,12 +2,20 @@
 //
 // ECHO explainer, "Prefill: one-round histogram": a single 256-bin histogram
 // pass keyed by the high byte of the score minus the predicted threshold
-// theta; the selection must be exact (the explainer's opening summary). The k-th element (s*, t*) of the order
-// (score descending, token ascending) defines the set exactly:
+// theta; the selection must be exact (the explainer's opening summary). The
+// k-th element (s*, t*) of the order (score descending, token ascending)
+// defines the set exactly:
 //     t selected  <=>  s_t > s*  or  (s_t == s* and t among the first
 //                      need_eq tokens with score s*)
 // so the kernels find s* and need_eq, then compact in ascending t.
 //
+// Three launch shapes, by the call's rows:
+//   - a few rows of at most 16384 tokens: one workgroup per row holds the row
+//     in registers (topk_small_kernel, one launch);
+//   - a few long rows (decode): one pass over the scores (topk_one_kernel,
+//     after a one-block reset), each workgroup a 16384-token chunk; the last
+//     workgroup of a row selects from the chunks' band lists;
+//   - many rows (a prefill block), in five launches:
 //   T1 hist     grid (chunks, R): LDS histogram of bin(t) = high byte of
 //               the order key of fp16(fl32(s_t - theta)) per 4096-token chunk.
 //               Every step is monotone in s, so higher bins hold strictly
@@ -29,8 +37,8 @@
 //               whose boundary bin holds more than cap tokens (no or poor
 //               theta), for which T4 ran the radix rounds over the whole row
 //               and left per-chunk offsets.
-// A good theta puts only a few hundred tokens in b* (bins are logarithmic
-// around the threshold), so the row is read twice (T1, T3).
+//   A good theta puts only a few hundred tokens in b* (bins are logarithmic
+//   around the threshold), so the row is read twice (T1, T3).
 
 #include <algorithm>
 #include <mutex>
@@ -77,11 +85,12 @@ struct Ws {
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
-int cand_cap(int R) { return R <= 256 ? 16384 : 4096; }
+// Largest boundary bin the list serves (T4 selects it in LDS).
+constexpr int kListCap = 4096;
 
 size_t layout(int R, int max_len, int k, Ws* w, char* base) {
   const int nch = std::max(1, (max_len + kChunk - 1) / kChunk);
-  const int cap = cand_cap(R);
+  const int cap = kListCap;
   const int lcap = (k + cap + 7) & ~7;   // rows of the list stay 64-byte aligned
   size_t o = 0;
   auto take = [&](size_t bytes) {
@@ -209,129 +218,6 @@ __global__ __launch_bounds__(kT) void topk_hist_kernel(const float* __restrict__
 }
 
 // ------------------------------------------------------------------ T2
-// T2 for a few long rows, NT = 1024 threads. Wave w reads the
-// chunk histograms w, w + kW, ... with lane l holding bins 4l..4l+3 (one int4
-// per lane, a whole histogram per wave instruction, sixteen loads in flight).
-// Their sum is the row histogram, which fixes b*; the same registers then give
-// each chunk's count over bins >= b* (a row of at most 16 kW chunks is read
-// once).
-template <int NT>
-__global__ __launch_bounds__(NT) void topk_rowsel_kernel(const int32_t* __restrict__ lens, int k, Ws ws) {
-  constexpr int kW = NT / 64;
-  constexpr int kPass = 16 * kW;   // chunks per pass
-  const int r = blockIdx.x;
-  const int len = lens[r];
-  RowState& st = ws.rs[r];
-  if (len <= k) {
-    if (threadIdx.x == 0) {
-      st.mode = len == 0 ? kEmpty : kAll;
-      st.bstar = 0;
-      st.need = 0;
-      st.nlist = 0;
-      st.refine = 0;
-    }
-    return;
-  }
-  const int nch = (len + kChunk - 1) / kChunk;
-  __shared__ int4 part_sum[kW][64];
-  __shared__ int s_cnt[kMaxChunks];
-  __shared__ int scratch[NT / 64];
-  __shared__ int s_bstar, s_nbin;
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  const int4* h4 = reinterpret_cast<const int4*>(ws.hist + (size_t)r * ws.nch * 256) + lane;
-  int4 q[16];
-  auto load_pass = [&](int c0) {
-#pragma unroll
-    for (int u = 0; u < 16; ++u) {
-      const int cc = c0 + wv + kW * u;
-      q[u] = cc < nch ? h4[(size_t)cc * 64] : int4{0, 0, 0, 0};
-    }
-  };
-  {
-    int4 acc = {0, 0, 0, 0};
-    for (int c0 = 0; c0 < nch; c0 += kPass) {
-      load_pass(c0);
-#pragma unroll
-      for (int u = 0; u < 16; ++u) {
-        acc.x += q[u].x;
-        acc.y += q[u].y;
-        acc.z += q[u].z;
-        acc.w += q[u].w;
-      }
-    }
-    part_sum[wv][lane] = acc;
-  }
-  __syncthreads();
-  // threads 0..255 hold bins 255..0 in order; the rest add zeros after them
-  {
-    const int bin = 255 - (int)(threadIdx.x & 255);
-    int cnt = 0;
-    if (threadIdx.x < 256) {
-#pragma unroll
-      for (int w = 0; w < kW; ++w) cnt += reinterpret_cast<const int*>(part_sum[w])[bin];
-    }
-    int tot;
-    const int above = ech::block_excl_scan<NT>(cnt, scratch, &tot);
-    if (threadIdx.x < 256 && above < k && above + cnt >= k) {
-      s_bstar = bin;
-      s_nbin = cnt;
-      st.bstar = bin;
-      st.need = k - above;
-    }
-  }
-  __syncthreads();
-  const int bstar = s_bstar;
-  const bool wide = s_nbin > ws.cap;
-  if (threadIdx.x == 0) {
-    st.mode = wide ? kWide : kNormal;
-    st.refine = 0;
-  }
-  // Per chunk, the count over bins >= tb: list sizes for normal rows (their
-  // exclusive scan gives the list offsets); for wide rows the count of bins
-  // above b* (kept in take, for the refinement).
-  const int tb = wide ? bstar + 1 : bstar;
-  for (int c0 = 0; c0 < nch; c0 += kPass) {
-    if (nch > kPass) load_pass(c0);   // one pass: q still holds it
-    int p[16];
-    const int b0 = 4 * lane;
-#pragma unroll
-    for (int u = 0; u < 16; ++u)
-      p[u] = (b0 >= tb ? q[u].x : 0) + (b0 + 1 >= tb ? q[u].y : 0) + (b0 + 2 >= tb ? q[u].z : 0) +
-             (b0 + 3 >= tb ? q[u].w : 0);
-    // Sum each p[u] over the wave, halving the values per lane at each step:
-    // lane l ends with the total of u = (l >> 2) & 15.
-#pragma unroll
-    for (int m = 32, n = 16; m >= 4; m >>= 1, n >>= 1) {
-      const bool hi = (lane & m) != 0;
-#pragma unroll
-      for (int j = 0; j < n / 2; ++j) {
-        const int keep = hi ? p[j + n / 2] : p[j];
-        const int give = hi ? p[j] : p[j + n / 2];
-        p[j] = keep + __shfl_xor(give, m, 64);
-      }
-    }
-    int n = p[0];
-    n += __shfl_xor(n, 2, 64);
-    n += __shfl_xor(n, 1, 64);
-    const int cc = c0 + wv + kW * ((lane >> 2) & 15);
-    if ((lane & 3) == 0 && cc < nch) s_cnt[cc] = n;
-  }
-  __syncthreads();
-  int run = 0;
-  for (int c0 = 0; c0 < nch; c0 += NT) {
-    const int c = c0 + (int)threadIdx.x;
-    const int n = c < nch ? s_cnt[c] : 0;
-    int t;
-    const int pre = ech::block_excl_scan<NT>(n, scratch, &t);
-    if (c < nch) {
-      if (wide) ws.take[(size_t)r * ws.nch + c] = n;
-      else ws.off[(size_t)r * ws.nch + c] = run + pre;
-    }
-    run += t;
-  }
-  if (threadIdx.x == 0 && !wide) st.nlist = run;
-}
-
 // T2 for calls with many rows (a prefill block: rows of at most a few dozen
 // chunks), 256 threads: thread b sums bin (255 - b) over the row's chunks,
 // eight independent loads in flight; four adjacent threads then share a
@@ -989,9 +875,9 @@ __global__ __launch_bounds__(kT) void topk_compact_kernel(const float* __restric
 }
 
 // ------------------------------------------------------------------ short rows
-// A few rows of at most kSmallMax tokens: one launch, one workgroup per row,
-// each thread holding 16 consecutive scores of the row in registers for the
-// whole kernel. The same steps as the multi-kernel path: histogram of the
+// A few rows of at most kSmallMax tokens: one workgroup per row, each thread
+// holding 16 consecutive scores of the row in registers for the whole
+// selection. The same steps as the multi-kernel path: histogram of the
 // shifted bins, boundary bin b*, radix rounds on the exact order keys of the
 // b* tokens (listed in LDS and selected by one wave when there are at most
 // kSmallCand of them, else block-wide over the registers, so b* may be any
@@ -1001,33 +887,34 @@ constexpr int kSmallPer = 16;
 constexpr int kSmallMax = kSmallNT * kSmallPer;   // 16384 tokens
 constexpr int kSmallCand = 4096;                  // boundary tokens listed for the radix rounds
 
-__global__ __launch_bounds__(kSmallNT) void topk_small_kernel(const float* __restrict__ logits, int64_t ld,
-                                                              const int32_t* __restrict__ lens, int k,
-                                                              const float* theta_in,
-                                                              float* theta_out,
-                                                              float* __restrict__ kth, int32_t* __restrict__ idx) {
+// LDS of a 1024-thread selection workgroup (short rows and the one-pass path).
+struct SelLds {
+  int2 cand[kSmallCand + 64];   // (score bits, token): boundary tokens, or a chunk's list being
+                                // staged (+ a junk entry per lane)
+  int hist[256 + 64];           // + a junk word per lane
+  int sh[kSmallNT / 64];
+  int s_digit, s_need, s_nc, s_last;
+  uint32_t s_prefix;
+  float s_min;
+};
+
+// The whole selection of one row of at most kSmallMax tokens by one
+// workgroup of kSmallNT threads: idx (k entries, -1 padded), kth and the EMA
+// update of theta (theta_out may be null).
+__device__ void small_row(const float* __restrict__ row, int len, int k, float th_in, float* kth_out,
+                          float* theta_out, int32_t* __restrict__ orow, SelLds& L) {
   constexpr int NT = kSmallNT;
-  __shared__ int2 cand[kSmallCand];   // (score bits, token) of the boundary tokens
-  __shared__ int hist[256];
-  __shared__ int sh[NT / 64];
-  __shared__ int s_digit, s_need, s_nc;
-  __shared__ uint32_t s_prefix;
-  __shared__ float s_min;
-  const int r = blockIdx.x, tid = threadIdx.x;
-  const int len = min(lens[r], kSmallMax);
-  const float th_in = row_theta(theta_in, r);
-  int32_t* orow = idx + (size_t)r * k;
+  const int tid = threadIdx.x;
   for (int j = min(k, len) + tid; j < k; j += NT) orow[j] = -1;
   if (len == 0) {
     if (tid == 0) {
-      kth[r] = __builtin_nanf("");
-      if (theta_out) theta_out[r] = th_in;
+      *kth_out = __builtin_nanf("");
+      if (theta_out) *theta_out = th_in;
     }
     return;
   }
   // tokens t0 .. t0+15 of this thread (16-byte aligned rows: ld % 4 == 0)
   const int t0 = kSmallPer * tid;
-  const float* row = logits + (size_t)r * ld;
   float v[kSmallPer];
   if (t0 + kSmallPer <= len) {
 #pragma unroll
@@ -1054,7 +941,7 @@ __global__ __launch_bounds__(kSmallNT) void topk_small_kernel(const float* __res
     for (int e = 0; e < kSmallPer; ++e)
       if ((valid >> e) & 1u) m = fminf(m, v[e]);
     for (int d = 32; d > 0; d >>= 1) m = fminf(m, __shfl_xor(m, d, 64));
-    float* wmin = reinterpret_cast<float*>(hist);
+    float* wmin = reinterpret_cast<float*>(L.hist);
     if (ech::lane_id() == 0) wmin[tid / 64] = m;
 #pragma unroll
     for (int e = 0; e < kSmallPer; ++e)
@@ -1063,16 +950,16 @@ __global__ __launch_bounds__(kSmallNT) void topk_small_kernel(const float* __res
     if (tid == 0) {
       float mm = __builtin_inff();
       for (int i = 0; i < NT / 64; ++i) mm = fminf(mm, wmin[i]);
-      s_min = mm;
+      L.s_min = mm;
     }
     __syncthreads();
-    sstar = s_min;
+    sstar = L.s_min;
   } else {
     // 1. histogram of the shifted bins (lumped tokens counted per wave); the
     // thread keeps its bins
     const Shift shf = make_shift(th_in);
-    if (tid < 256) hist[tid] = 0;
-    if (tid == 0) s_nc = 0;
+    if (tid < 256) L.hist[tid] = 0;
+    if (tid == 0) L.s_nc = 0;
     __syncthreads();
     uint32_t bins[kSmallPer];
     int lumped = 0;
@@ -1082,15 +969,15 @@ __global__ __launch_bounds__(kSmallNT) void topk_small_kernel(const float* __res
       const bool ok = (valid >> e) & 1u;
       const bool lump = ok && shf.on && bins[e] == 0u;
       lumped += lump;
-      ech::lds_hist_add(hist, bins[e], ok && !lump);
+      ech::lds_hist_add(L.hist, bins[e], ok && !lump);
     }
     lumped = ech::wave_sum(lumped);
-    if (ech::lane_id() == 0 && lumped) atomicAdd(&hist[0], lumped);
+    if (ech::lane_id() == 0 && lumped) atomicAdd(&L.hist[0], lumped);
     __syncthreads();
     // 2. boundary bin and the rank of the k-th token within it
-    pick_digit(hist, sh, k, &s_digit, &s_need);
-    const uint32_t bstar = (uint32_t)s_digit;
-    int need = s_need;
+    pick_digit(L.hist, L.sh, k, &L.s_digit, &L.s_need);
+    const uint32_t bstar = (uint32_t)L.s_digit;
+    int need = L.s_need;
     // list the boundary tokens (one LDS atomic per wave)
     uint32_t bm = 0;
 #pragma unroll
@@ -1098,50 +985,50 @@ __global__ __launch_bounds__(kSmallNT) void topk_small_kernel(const float* __res
     const int cnt = __popc(bm);
     const int incl = ech::wave_incl_scan(cnt);
     int wbase = 0;
-    if (ech::lane_id() == 63 && incl > 0) wbase = atomicAdd(&s_nc, incl);
+    if (ech::lane_id() == 63 && incl > 0) wbase = atomicAdd(&L.s_nc, incl);
     wbase = __shfl(wbase, 63, 64);
     int p = wbase + incl - cnt;
 #pragma unroll
     for (int e = 0; e < kSmallPer; ++e) {
       if ((bm >> e) & 1u) {
-        if (p < kSmallCand) cand[p] = make_int2(__float_as_int(v[e]), t0 + e);
+        if (p < kSmallCand) L.cand[p] = make_int2(__float_as_int(v[e]), t0 + e);
         ++p;
       }
     }
     __syncthreads();
-    const int nc = s_nc;
+    const int nc = L.s_nc;
     // 3. the need-th largest boundary score: one wave over the list, or
     // block-wide rounds over the registers when the bin is wider than it
     uint32_t prefix = 0;
     if (nc <= kSmallCand) {   // block-uniform
       if (tid < 64) {
         int nq;
-        const uint32_t pf = wave_select(cand, nc, need, hist, &nq);
+        const uint32_t pf = wave_select(L.cand, nc, need, L.hist, &nq);
         if (tid == 0) {
-          s_prefix = pf;
-          s_need = nq;
+          L.s_prefix = pf;
+          L.s_need = nq;
         }
       }
       __syncthreads();
-      prefix = s_prefix;
-      need = s_need;
+      prefix = L.s_prefix;
+      need = L.s_need;
     } else {
       uint32_t mask = 0;
 #pragma unroll 1
       for (int round = 0; round < 4; ++round) {
         const int shift = 24 - 8 * round;
-        if (tid < 256) hist[tid] = 0;
+        if (tid < 256) L.hist[tid] = 0;
         __syncthreads();
 #pragma unroll
         for (int e = 0; e < kSmallPer; ++e) {
           const uint32_t key = ech::ord_key(v[e]);
-          ech::lds_hist_add(hist, (key >> shift) & 255u, ((bm >> e) & 1u) && (key & mask) == prefix);
+          ech::lds_hist_add(L.hist, (key >> shift) & 255u, ((bm >> e) & 1u) && (key & mask) == prefix);
         }
         __syncthreads();
-        pick_digit(hist, sh, need, &s_digit, &s_need);
-        prefix |= (uint32_t)s_digit << shift;
+        pick_digit(L.hist, L.sh, need, &L.s_digit, &L.s_need);
+        prefix |= (uint32_t)L.s_digit << shift;
         mask |= 255u << shift;
-        need = s_need;
+        need = L.s_need;
         __syncthreads();
       }
     }
@@ -1157,7 +1044,7 @@ __global__ __launch_bounds__(kSmallNT) void topk_small_kernel(const float* __res
       eqm |= (ok && v[e] == sstar) ? 1u << e : 0u;
     }
     int tot;
-    const int pre = ech::block_excl_scan<NT>(__popc(gtm) | (__popc(eqm) << 16), sh, &tot);
+    const int pre = ech::block_excl_scan<NT>(__popc(gtm) | (__popc(eqm) << 16), L.sh, &tot);
     int gt_b = pre & 0xffff, eq_b = pre >> 16;
 #pragma unroll
     for (int e = 0; e < kSmallPer; ++e) {
@@ -1169,6 +1056,507 @@ __global__ __launch_bounds__(kSmallNT) void topk_small_kernel(const float* __res
     }
   }
   if (tid == 0) {
+    *kth_out = sstar;
+    if (theta_out) *theta_out = (th_in == th_in) ? (sstar + th_in) * 0.5f : sstar;
+  }
+}
+
+__global__ __launch_bounds__(kSmallNT) void topk_small_kernel(const float* __restrict__ logits, int64_t ld,
+                                                              const int32_t* __restrict__ lens, int k,
+                                                              const float* theta_in, float* theta_out,
+                                                              float* __restrict__ kth, int32_t* __restrict__ idx) {
+  __shared__ SelLds L;
+  const int r = blockIdx.x;
+  small_row(logits + (size_t)r * ld, min(lens[r], kSmallMax), k, row_theta(theta_in, r), kth + r,
+            theta_out ? theta_out + r : nullptr, idx + (size_t)r * k, L);
+}
+
+// ------------------------------------------------------------------ few long rows: one pass
+// grid (chunks of kOneChunk tokens, R), kSmallNT threads, after a one-block
+// reset of the row counters and histograms. Each workgroup reads its chunk
+// once (16 scores per thread in registers) and
+//   - adds its histogram of shifted bins to the row's histogram (global
+//     atomics, only the bins it holds),
+//   - lists, in token order, its tokens in the bins at and above a floor
+//     into its slice of the row's pool (the pool split evenly over the row's
+//     chunks, at most kSmallCand entries each): the floor is the bin of
+//     theta - |theta|/8 (the band the prediction implies), raised where
+//     needed so that the chunk's tokens fit its slice,
+//   - counts itself done. The last workgroup of the row to finish takes b*
+//     from the row histogram. If b* is at or above every chunk's floor (every
+//     bin from b* up is listed), the selection comes from the lists alone:
+//     radix rounds on the b* entries give s* and need_eq, and one ordered
+//     pass over the lists writes the selection. Otherwise (a floor above b*)
+//     the same workgroup selects over the whole row: radix rounds restricted
+//     to b*, then an ordered pass.
+// The decode prediction moves by a few percent of the k-th score per step
+// (the EMA of the explainer's "Decode: fetch above a predicted threshold"),
+// so the band holds b* and each score is read once. Rows of a ragged call
+// no longer than kSmallMax are selected whole by their first workgroup.
+constexpr int kOneChunk = kSmallNT * kSmallPer;                  // 16384 tokens per workgroup
+constexpr int kOneMaxChunks = kMaxChunks * kChunk / kOneChunk;   // 256 (4M tokens)
+constexpr int kOneMaxRows = 256;
+constexpr int kPool = 32768;         // listed entries per row, at most
+constexpr float kBandFrac = 0.125f;  // band: scores down to about theta - |theta|/8
+
+struct OneWs {
+  int* ctl;      // [R] * 32: per row, one 128-byte line: [0] chunks done
+  int* hist;     // [R][256] row histograms
+  int2* meta;    // [R][nch] per chunk: entries listed, floor
+  int2* pool;    // [R][npool] (score bits, token): chunk c's slice at c * slice
+  int nch;       // chunks of the longest row
+  int npool;     // entries per row
+};
+
+// Pool entries per row for rows of at most nch chunks.
+int one_pool(int nch) { return std::min(kPool, nch * kSmallCand); }
+
+size_t one_layout(int R, int max_len, OneWs* w, char* base) {
+  const int nch = std::max(1, (max_len + kOneChunk - 1) / kOneChunk);
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    size_t at = o;
+    o = align256(o + bytes);
+    return at;
+  };
+  size_t o_ctl = take(sizeof(int) * 32 * (size_t)R);
+  size_t o_hist = take(sizeof(int) * 256 * (size_t)R);
+  size_t o_meta = take(sizeof(int2) * (size_t)R * nch);
+  size_t o_pool = take(sizeof(int2) * (size_t)R * one_pool(nch));
+  if (w && base) {
+    w->ctl = reinterpret_cast<int*>(base + o_ctl);
+    w->hist = reinterpret_cast<int*>(base + o_hist);
+    w->meta = reinterpret_cast<int2*>(base + o_meta);
+    w->pool = reinterpret_cast<int2*>(base + o_pool);
+    w->nch = nch;
+    w->npool = one_pool(nch);
+  }
+  return o;
+}
+
+// Bins of the one-pass path: the high byte of the order key of fp16(d), the
+// same four bins per binade as bin16, computed with fewer instructions: d + 0
+// folds -0 onto +0 (equal scores share a bin), and the key's high byte is
+// the fp16 high byte with the sign bit flipped (positive d) or all bits
+// flipped (negative d). A negative d that rounds to fp16 -0 takes bin 0x7f,
+// just below +0: still monotone in d.
+__device__ __forceinline__ uint32_t bin_one(float d) {
+  const _Float16 h = (_Float16)(d + 0.0f);
+  const uint32_t u = __builtin_bit_cast(uint16_t, h);
+  const uint32_t neg = (uint32_t)((int32_t)(u << 16) >> 31);   // ~0 for a negative d
+  return (u >> 8) ^ 0x80u ^ (neg & 0x7fu);
+}
+
+__device__ __forceinline__ uint32_t shifted_bin_one(float x, const Shift& sh) {
+  const float d = sh.on ? x - sh.th : x;
+  return d < sh.cut ? 0u : bin_one(d);
+}
+
+// Floor the prediction implies: the bin of d = -|theta|/8 (above the lumping
+// cut at -|theta|/4); 0 (no constraint) without a finite nonzero theta.
+__device__ __forceinline__ uint32_t band_lo(const Shift& sh) {
+  const float a = fabsf(sh.th);
+  if (!sh.on || !(a > 0.f) || !(a < __builtin_inff())) return 0u;
+  return bin_one(-kBandFrac * a);
+}
+
+// Wait until this wave's global stores and atomics have completed.
+__device__ __forceinline__ void wait_vm_zero() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// What a chunk workgroup hands to the last one goes through device-coherent
+// (agent-scope) stores, loads and atomics: once a wave's stores have
+// completed they are visible to such loads on every XCD, so the hand-over
+// needs no cache write-back or invalidation, only the wait before the count.
+__device__ __forceinline__ void st_agent(int2* p, int2 v) {
+  const uint64_t u = (uint64_t)(uint32_t)v.x | ((uint64_t)(uint32_t)v.y << 32);
+  __hip_atomic_store(reinterpret_cast<uint64_t*>(p), u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ int2 ld_agent(const int2* p) {
+  const uint64_t u = __hip_atomic_load(reinterpret_cast<const uint64_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return make_int2((int)(uint32_t)u, (int)(uint32_t)(u >> 32));
+}
+__device__ __forceinline__ int ld_agent(const int* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Inclusive scan over a wave through DPP row shifts (within rows of 16
+// lanes) and row broadcasts (rows 1, 3 take row 0, 2's total; rows 2, 3 take
+// lane 31's): a few cycles per step where a lane shuffle is an LDS round
+// trip. Every lane of the wave must be active.
+__device__ __forceinline__ int wave_scan_dpp(int v) {
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, false);   // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xf, 0xf, false);   // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xf, false);   // row_shr:4
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xf, false);   // row_shr:8
+  v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xa, 0xf, false);   // row_bcast:15
+  v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xc, 0xf, false);   // row_bcast:31
+  return v;
+}
+
+__device__ __forceinline__ int wave_sum_dpp(int v) { return __builtin_amdgcn_readlane(wave_scan_dpp(v), 63); }
+
+// Exclusive scan over a workgroup of NT threads (all active) with the DPP
+// wave scan; the total goes to *total.
+template <int NT>
+__device__ __forceinline__ int block_scan_dpp(int v, int* scratch, int* total) {
+  constexpr int NW = NT / 64;
+  const int lane = ech::lane_id(), wave = threadIdx.x / 64;
+  const int incl = wave_scan_dpp(v);
+  if (lane == 63) scratch[wave] = incl;
+  __syncthreads();
+  int wbase = 0, tot = 0;
+#pragma unroll
+  for (int i = 0; i < NW; ++i) {
+    const int x = scratch[i];
+    wbase += i < wave ? x : 0;
+    tot += x;
+  }
+  __syncthreads();
+  *total = tot;
+  return wbase + incl - v;
+}
+
+__global__ __launch_bounds__(256) void topk_one_reset_kernel(OneWs ws) {
+  const int r = blockIdx.x;
+  ws.hist[(size_t)r * 256 + threadIdx.x] = 0;
+  if (threadIdx.x < 32) ws.ctl[32 * r + threadIdx.x] = 0;
+}
+
+// Ordered pass over a whole row by one workgroup: every score above s* and
+// the first need_eq equal to it, in token order. Thread tid takes 16
+// consecutive tokens of each 16384-token block, so one block scan orders them.
+__device__ void row_compact(const float* __restrict__ row, int len, float sstar, int need_eq, int k,
+                            int32_t* __restrict__ orow, int* sh) {
+  constexpr int NT = kSmallNT;
+  int gt_run = 0, eq_run = 0;
+  for (int b0 = 0; b0 < len; b0 += kOneChunk) {
+    const int t0 = b0 + kSmallPer * (int)threadIdx.x;
+    float v[kSmallPer];
+    if (t0 + kSmallPer <= len) {
+#pragma unroll
+      for (int q = 0; q < kSmallPer / 4; ++q) {
+        const float4 x = reinterpret_cast<const float4*>(row + t0)[q];
+        v[4 * q] = x.x;
+        v[4 * q + 1] = x.y;
+        v[4 * q + 2] = x.z;
+        v[4 * q + 3] = x.w;
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < kSmallPer; ++e) v[e] = t0 + e < len ? row[t0 + e] : 0.f;
+    }
+    uint32_t gtm = 0, eqm = 0;
+#pragma unroll
+    for (int e = 0; e < kSmallPer; ++e) {
+      const bool ok = t0 + e < len;
+      gtm |= (ok && v[e] > sstar) ? 1u << e : 0u;
+      eqm |= (ok && v[e] == sstar) ? 1u << e : 0u;
+    }
+    int tot;
+    const int pre = ech::block_excl_scan<NT>(__popc(gtm) | (__popc(eqm) << 16), sh, &tot);
+    int gt_b = gt_run + (pre & 0xffff), eq_b = eq_run + (pre >> 16);
+#pragma unroll
+    for (int e = 0; e < kSmallPer; ++e) {
+      const bool gt = (gtm >> e) & 1u, eq = (eqm >> e) & 1u;
+      const int pos = gt_b + min(eq_b, need_eq);
+      if ((gt || (eq && eq_b < need_eq)) && pos < k) orow[pos] = t0 + e;
+      gt_b += gt;
+      eq_b += eq;
+    }
+    gt_run += tot & 0xffff;
+    eq_run += tot >> 16;
+  }
+}
+
+__global__ __launch_bounds__(kSmallNT) void topk_one_kernel(const float* __restrict__ logits, int64_t ld,
+                                                            const int32_t* __restrict__ lens, int max_len, int k,
+                                                            const float* theta_in, float* theta_out,
+                                                            float* __restrict__ kth, int32_t* __restrict__ idx,
+                                                            OneWs ws) {
+  constexpr int NT = kSmallNT;
+  __shared__ SelLds L;
+  __shared__ int s_off[kOneMaxChunks + 1];   // the last workgroup: chunk c's entries start at s_off[c]
+  __shared__ int s_fmax;
+  const int r = blockIdx.y, c = blockIdx.x, tid = threadIdx.x;
+  const int len = min(lens[r], max_len);   // the grid and workspace are sized by max_len
+  const float th_in = row_theta(theta_in, r);
+  const float* row = logits + (size_t)r * ld;
+  int32_t* orow = idx + (size_t)r * k;
+  if (len <= kSmallMax) {
+    if (c == 0) small_row(row, len, k, th_in, kth + r, theta_out ? theta_out + r : nullptr, orow, L);
+    return;
+  }
+  const int nch = (len + kOneChunk - 1) / kOneChunk;
+  if (c >= nch) return;
+  const Shift shf = make_shift(th_in);
+  int* ctl = ws.ctl + 32 * r;
+  int2* pool = ws.pool + (size_t)r * ws.npool;
+  const int slice = min(kSmallCand, ws.npool / nch);   // this row's entries per chunk
+
+  // ---- the chunk: histogram, floor, listed tokens
+  // Thread tid holds the 16 consecutive tokens from t0, so one scan of the
+  // per-thread counts orders the list. The per-token work is branch-free
+  // (the pass is bound by instruction issue, not by the read): lumped and
+  // absent tokens add to a junk word of their lane, unlisted ones stage into
+  // a junk entry of their lane.
+  const int lane = ech::lane_id();
+  const int lo = c * kOneChunk, hi = min(lo + kOneChunk, len);
+  const int t0 = lo + kSmallPer * tid;
+  const int nv = min(kSmallPer, max(0, hi - t0));   // this thread's tokens in the row
+  float v[kSmallPer];
+  if (nv == kSmallPer) {
+#pragma unroll
+    for (int q = 0; q < kSmallPer / 4; ++q) {
+      typedef float f4v __attribute__((ext_vector_type(4)));
+      const f4v x = __builtin_nontemporal_load(reinterpret_cast<const f4v*>(row + t0) + q);
+      v[4 * q] = x.x;
+      v[4 * q + 1] = x.y;
+      v[4 * q + 2] = x.z;
+      v[4 * q + 3] = x.w;
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < kSmallPer; ++e) v[e] = e < nv ? row[t0 + e] : 0.f;
+  }
+  const uint32_t blo = band_lo(shf);
+  if (tid < 256) L.hist[tid] = 0;
+  __syncthreads();
+  uint32_t in = 0;   // bit e: token t0 + e is listed
+  int lumped = 0;
+#pragma unroll
+  for (int e = 0; e < kSmallPer; ++e) {
+    const bool ok = e < nv;
+    const float d = shf.on ? v[e] - shf.th : v[e];
+    const bool lump = d < shf.cut;
+    const uint32_t b = bin_one(d);
+    atomicAdd(&L.hist[(ok && !lump) ? b : 256 + lane], 1);
+    lumped += (ok && lump) ? 1 : 0;
+    in |= (ok && !lump && b >= blo) ? 1u << e : 0u;
+  }
+  lumped = wave_sum_dpp(lumped);
+  if (lane == 0 && lumped) atomicAdd(&L.hist[0], lumped);
+  int total;
+  int pre = block_scan_dpp<NT>(__popc(in), L.sh, &total);   // its barriers also close the histogram
+  uint32_t floor_c = blo;
+  if (total > slice) {   // the band does not fit the slice (block-uniform): raise the floor
+    // to the lowest bin whose count from the top fits (threads 0..255 take bins 255..0)
+    const int hb = tid < 256 ? L.hist[255 - tid] : 0;
+    int hall;
+    const int hex = block_scan_dpp<NT>(hb, L.sh, &hall);
+    const int fit = __syncthreads_count(tid < 256 && hex + hb <= slice);
+    floor_c = max(blo, 256u - (uint32_t)fit);
+    in = 0;
+#pragma unroll
+    for (int e = 0; e < kSmallPer; ++e)
+      in |= (e < nv && shifted_bin_one(v[e], shf) >= floor_c) ? 1u << e : 0u;
+    pre = block_scan_dpp<NT>(__popc(in), L.sh, &total);
+  }
+  {
+    int pos = pre;
+#pragma unroll
+    for (int e = 0; e < kSmallPer; ++e) {
+      const bool listed = (in >> e) & 1u;
+      L.cand[(listed && pos < slice) ? pos : kSmallCand + lane] = make_int2(__float_as_int(v[e]), t0 + e);
+      pos += listed ? 1 : 0;
+    }
+  }
+  __syncthreads();
+  const int n_out = min(total, slice);   // the floor bounds total by slice; guard only
+  for (int i = tid; i < n_out; i += NT) st_agent(&pool[c * slice + i], L.cand[i]);
+  if (tid == 0) st_agent(&ws.meta[(size_t)r * ws.nch + c], make_int2(n_out, (int)floor_c));
+  if (tid < 256) {
+    const int hv = L.hist[tid];
+    if (hv) atomicAdd(&ws.hist[(size_t)r * 256 + tid], hv);
+  }
+  // Publish: every wave's coherent stores and atomics complete, then the
+  // count; the last workgroup reads with coherent loads.
+  wait_vm_zero();
+  __syncthreads();
+  if (tid == 0)
+    L.s_last = __hip_atomic_fetch_add(&ctl[0], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == nch - 1;
+  __syncthreads();
+  if (!L.s_last) return;
+
+  // ---- the last workgroup of the row: b* and the selection
+  if (tid < 256) L.hist[tid] = ld_agent(&ws.hist[(size_t)r * 256 + tid]);
+  const int2 m = tid < nch ? ld_agent(&ws.meta[(size_t)r * ws.nch + tid]) : make_int2(0, 0);
+  if (tid == 0) s_fmax = 0;
+  __syncthreads();
+  pick_digit(L.hist, L.sh, k, &L.s_digit, &L.s_need);
+  const uint32_t bstar = (uint32_t)L.s_digit;
+  int need = L.s_need;
+  const int nb = L.hist[bstar];
+  if (tid < nch) atomicMax(&s_fmax, m.y);
+  int nlist;
+  const int off = block_scan_dpp<NT>(m.x, L.sh, &nlist);
+  if (tid < nch) s_off[tid] = off;
+  if (tid == 0) s_off[nch] = nlist;
+  __syncthreads();
+  float sstar;
+  int need_eq;
+  if ((uint32_t)s_fmax <= bstar) {
+    // Entries 8 tid + u of each 8 NT-entry round of the chunks' lists in
+    // chunk order.
+    auto load8 = [&](int ib, int2 (&e)[8]) {
+      int a = 0, b = nch;   // s_off[a] <= ib < s_off[b]
+      if (ib < nlist) {
+        while (b - a > 1) {
+          const int mid = (a + b) >> 1;
+          if (s_off[mid] <= ib) a = mid;
+          else b = mid;
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int i = ib + u;
+        if (i < nlist) {
+          while (s_off[a + 1] <= i) ++a;
+          e[u] = ld_agent(&pool[a * slice + (i - s_off[a])]);
+        } else {
+          e[u] = make_int2(0, -1);
+        }
+      }
+    };
+    int2 first[8];   // the first round, kept for the ordered pass
+    load8(8 * tid, first);
+    uint32_t prefix = 0;
+    if (nb <= kSmallCand) {   // the b* entries into LDS
+      if (tid == 0) L.s_nc = 0;
+      __syncthreads();
+      for (int i0 = 0; i0 < nlist; i0 += 8 * NT) {
+        int2 e[8];
+        if (i0 == 0) {
+#pragma unroll
+          for (int u = 0; u < 8; ++u) e[u] = first[u];
+        } else {
+          load8(i0 + 8 * tid, e);
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          if (e[u].y >= 0 && shifted_bin_one(__int_as_float(e[u].x), shf) == bstar) {
+            const int p = atomicAdd(&L.s_nc, 1);
+            if (p < kSmallCand) L.cand[p] = e[u];   // the histogram bounds them by nb; guard only
+          }
+        }
+      }
+      __syncthreads();
+      const int nc = min(L.s_nc, kSmallCand);
+      if (tid < 64) {
+        uint32_t pf;
+        int nq;
+        if (nc <= 64) {
+          // A few: lane l takes entry l and counts the keys above and at or
+          // above its own; the lane where the count from the top reaches
+          // need holds s*.
+          const uint32_t key = tid < nc ? ech::ord_key(__int_as_float(L.cand[tid].x)) : 0u;
+          int gt = 0, ge = 0;
+          for (int j = 0; j < nc; ++j) {
+            const uint32_t kj = __builtin_amdgcn_readlane(key, j);
+            gt += kj > key;
+            ge += kj >= key;
+          }
+          const uint64_t hit = __ballot(tid < nc && gt < need && need <= ge);
+          const int src = __ffsll((unsigned long long)hit) - 1;
+          pf = __shfl(key, src, 64);
+          nq = need - __shfl(gt, src, 64);
+        } else {
+          pf = wave_select(L.cand, nc, need, L.hist, &nq);
+        }
+        if (tid == 0) {
+          L.s_prefix = pf;
+          L.s_need = nq;
+        }
+      }
+      __syncthreads();
+      prefix = L.s_prefix;
+      need = L.s_need;
+    } else {   // a wide b*: block-wide rounds over the lists
+      uint32_t mask = 0;
+#pragma unroll 1
+      for (int round = 0; round < 4; ++round) {
+        const int shift = 24 - 8 * round;
+        if (tid < 256) L.hist[tid] = 0;
+        __syncthreads();
+        for (int i0 = 0; i0 < nlist; i0 += 8 * NT) {
+          int2 e[8];
+          load8(i0 + 8 * tid, e);
+#pragma unroll
+          for (int u = 0; u < 8; ++u) {
+            const float x = __int_as_float(e[u].x);
+            const uint32_t key = ech::ord_key(x);
+            ech::lds_hist_add(L.hist, (key >> shift) & 255u,
+                              e[u].y >= 0 && shifted_bin_one(x, shf) == bstar && (key & mask) == prefix);
+          }
+        }
+        __syncthreads();
+        pick_digit(L.hist, L.sh, need, &L.s_digit, &L.s_need);
+        prefix |= (uint32_t)L.s_digit << shift;
+        mask |= 255u << shift;
+        need = L.s_need;
+        __syncthreads();
+      }
+    }
+    sstar = ech::ord_to_float(prefix);
+    need_eq = need;
+    // The selection in token order by one ordered pass over the lists: listed
+    // entries above b* score above s*, those below b* under it.
+    int gt_run = 0, eq_run = 0;
+    for (int i0 = 0; i0 < nlist; i0 += 8 * NT) {
+      int2 e[8];
+      if (i0 == 0) {
+#pragma unroll
+        for (int u = 0; u < 8; ++u) e[u] = first[u];
+      } else {
+        load8(i0 + 8 * tid, e);
+      }
+      uint32_t gtm = 0, eqm = 0;
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        if (e[u].y < 0) continue;
+        const float x = __int_as_float(e[u].x);
+        gtm |= x > sstar ? 1u << u : 0u;
+        eqm |= x == sstar ? 1u << u : 0u;
+      }
+      int tot;
+      const int pre = block_scan_dpp<NT>(__popc(gtm) | (__popc(eqm) << 16), L.sh, &tot);
+      int gt_b = gt_run + (pre & 0xffff), eq_b = eq_run + (pre >> 16);
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const bool gt = (gtm >> u) & 1u, eq = (eqm >> u) & 1u;
+        const int pos = gt_b + min(eq_b, need_eq);
+        if ((gt || (eq && eq_b < need_eq)) && pos < k) orow[pos] = e[u].y;
+        gt_b += gt;
+        eq_b += eq;
+      }
+      gt_run += tot & 0xffff;
+      eq_run += tot >> 16;
+    }
+  } else {
+    // The lists miss b*: radix rounds over the row's b* tokens, then an
+    // ordered pass over the row.
+    uint32_t prefix = 0, mask = 0;
+#pragma unroll 1
+    for (int round = 0; round < 4; ++round) {
+      const int shift = 24 - 8 * round;
+      if (tid < 256) L.hist[tid] = 0;
+      __syncthreads();
+      for_each_score<NT>(row, len, [&](int, float x) {
+        const uint32_t key = ech::ord_key(x);
+        ech::lds_hist_add(L.hist, (key >> shift) & 255u,
+                          shifted_bin_one(x, shf) == bstar && (key & mask) == prefix);
+      });
+      __syncthreads();
+      pick_digit(L.hist, L.sh, need, &L.s_digit, &L.s_need);
+      prefix |= (uint32_t)L.s_digit << shift;
+      mask |= 255u << shift;
+      need = L.s_need;
+      __syncthreads();
+    }
+    sstar = ech::ord_to_float(prefix);
+    need_eq = need;
+    row_compact(row, len, sstar, need_eq, k, orow, L.sh);
+  }
+  if (tid == 0) {
     kth[r] = sstar;
     if (theta_out) theta_out[r] = (th_in == th_in) ? (sstar + th_in) * 0.5f : sstar;
   }
@@ -1176,12 +1564,22 @@ __global__ __launch_bounds__(kSmallNT) void topk_small_kernel(const float* __res
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+// Which launches serve a call: a few short rows (one launch, no workspace
+// use), a few long rows (the one-pass launch), or many rows (T1..T5).
+enum class TopkPath { kSmall, kOne, kMany };
+
+TopkPath topk_path(int R, int max_len) {
+  if (R <= kOneMaxRows) return max_len <= kSmallMax ? TopkPath::kSmall : TopkPath::kOne;
+  return TopkPath::kMany;
+}
+
 }  // namespace
 
 extern "C" size_t ech_topk_ws_bytes(int R, int max_len, int k) {
   if (R < 1 || max_len < 0) return 0;
   if (k < 1 || k > kMaxK) return 0;
-  return layout(R, max_len, k, nullptr, nullptr);
+  if (topk_path(R, max_len) == TopkPath::kMany) return layout(R, max_len, k, nullptr, nullptr);
+  return std::max<size_t>(256, one_layout(R, max_len, nullptr, nullptr));
 }
 
 namespace {
@@ -1198,41 +1596,42 @@ bool topk_args_ok(const float* logits, int64_t ld, const int32_t* row_len, int R
 // The launches of one ech_topk call on a checked workspace.
 int topk_launch(const float* logits, int64_t ld, const int32_t* row_len, int R, int max_len, int k,
                 const float* theta_in, float* theta_out, int32_t* idx, float* kth, void* ws, void* stream) {
-  Ws w;
-  layout(R, max_len, k, &w, static_cast<char*>(ws));
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  if (R <= 256 && max_len <= kSmallMax) {   // a few short rows: one launch
+  const TopkPath path = topk_path(R, max_len);
+  if (path == TopkPath::kSmall) {
     hipLaunchKernelGGL(topk_small_kernel, dim3(R), dim3(kSmallNT), 0, s, logits, ld, row_len, k, theta_in,
                        theta_out, kth, idx);
     ECH_LAUNCH_CHECK();
     return ECH_OK;
   }
+  if (path == TopkPath::kOne) {
+    OneWs w;
+    one_layout(R, max_len, &w, static_cast<char*>(ws));
+    hipLaunchKernelGGL(topk_one_reset_kernel, dim3(R), dim3(256), 0, s, w);
+    ECH_LAUNCH_CHECK();
+    hipLaunchKernelGGL(topk_one_kernel, dim3(w.nch, R), dim3(kSmallNT), 0, s, logits, ld, row_len, max_len, k, theta_in,
+                       theta_out, kth, idx, w);
+    ECH_LAUNCH_CHECK();
+    return ECH_OK;
+  }
+  // Many rows (a prefill block): 256-thread per-row kernels, so they fit
+  // beside other work on a CU.
+  Ws w;
+  layout(R, max_len, k, &w, static_cast<char*>(ws));
   const dim3 gch(w.nch, R);
   hipLaunchKernelGGL(topk_hist_kernel, gch, dim3(kT), 0, s, logits, ld, row_len, k, theta_in, w);
   ECH_LAUNCH_CHECK();
-  // A few long rows (decode) get 1024 threads per row; many rows (a prefill
-  // block) get 256, so the per-row kernels fit beside other work on a CU.
-  const bool few_rows = R <= 256;
-  if (few_rows)
-    hipLaunchKernelGGL(topk_rowsel_kernel<1024>, dim3(R), dim3(1024), 0, s, row_len, k, w);
-  else
-    hipLaunchKernelGGL(topk_rowsel_many_kernel, dim3(R), dim3(256), 0, s, row_len, k, w);
+  hipLaunchKernelGGL(topk_rowsel_many_kernel, dim3(R), dim3(256), 0, s, row_len, k, w);
   ECH_LAUNCH_CHECK();
-  if (!few_rows) {
-    // many rows: refine rows with a lumped boundary in parallel over chunks
-    hipLaunchKernelGGL(topk_refine_hist_kernel, gch, dim3(kT), 0, s, logits, ld, row_len, theta_in, w);
-    ECH_LAUNCH_CHECK();
-    hipLaunchKernelGGL(topk_refine_sel_kernel<256>, dim3(R), dim3(256), 0, s, row_len, theta_in, w);
-    ECH_LAUNCH_CHECK();
-  }
+  // refine rows with a lumped boundary in parallel over chunks
+  hipLaunchKernelGGL(topk_refine_hist_kernel, gch, dim3(kT), 0, s, logits, ld, row_len, theta_in, w);
+  ECH_LAUNCH_CHECK();
+  hipLaunchKernelGGL(topk_refine_sel_kernel<256>, dim3(R), dim3(256), 0, s, row_len, theta_in, w);
+  ECH_LAUNCH_CHECK();
   hipLaunchKernelGGL(topk_list_kernel, gch, dim3(kT), 0, s, logits, ld, row_len, theta_in, w);
   ECH_LAUNCH_CHECK();
-  if (few_rows)
-    hipLaunchKernelGGL(topk_resolve_kernel<1024>, dim3(R), dim3(1024), sizeof(int2) * w.cap, s, logits, ld,
-                       row_len, k, theta_in, theta_out, kth, idx, w);
-  else
-    hipLaunchKernelGGL(topk_resolve_kernel<256>, dim3(R), dim3(256), sizeof(int2) * w.cap, s, logits, ld, row_len,
-                       k, theta_in, theta_out, kth, idx, w);
+  hipLaunchKernelGGL(topk_resolve_kernel<256>, dim3(R), dim3(256), sizeof(int2) * w.cap, s, logits, ld, row_len,
+                     k, theta_in, theta_out, kth, idx, w);
   ECH_LAUNCH_CHECK();
   const int gx = std::max(1, std::min(w.nch, std::max(8, 256 / R)));
   hipLaunchKernelGGL(topk_compact_kernel, dim3(gx, R), dim3(kT), 0, s, logits, ld, row_len, k, idx, w);

@@ -120,7 +120,7 @@ def check_topk_noalloc_rejects_bad_args(lib):
     # a 4096-row prefill block needs more than the static array: -5, before any HIP call
     assert lib.ech_topk_ws_bytes(4096, 110000, 2048) > (16 << 20)
     assert call(R=4096, ml=110000, k=2048, ld=110016) == -5
-    assert lib.ech_topk_ws_bytes(64, 131072, 2048) <= (16 << 20)
+    assert lib.ech_topk_ws_bytes(32, 131072, 2048) <= (16 << 20)
 
 
 CHECKS = [v for k, v in sorted(globals().items()) if k.startswith('check_')]

@@ -55,6 +55,7 @@ def run_topk(logits: np.ndarray, lens, k: int, theta=None):
     max_len = int(max(lens)) if len(lens) else 0
     L = dev(logits.astype(np.float32))
     ws = torch.empty(ech.ech_topk_ws_bytes(R, max_len, k), dtype=torch.uint8, device='cuda')
+    ws.fill_(0x5a)   # the workspace carries no state between calls: any contents will do
     idx = torch.full((R, k), -7, dtype=torch.int32, device='cuda')
     kth = torch.full((R,), 123.0, dtype=torch.float32, device='cuda')
     th_in = None if theta is None else dev(np.asarray(theta, np.float32))

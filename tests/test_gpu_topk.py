@@ -195,3 +195,72 @@ def test_short_rows_most_rows_and_many_rows():
     lens = [100 + (r * 977) % 16285 for r in range(300)]
     y = wk.random_logits(17, 300, 16384, 'ties')
     _check(y, lens, 2048)
+
+
+@pytest.mark.parametrize('kind', ['normal', 'signed', 'ties'])
+def test_one_pass_predictions_and_ragged_rows(kind):
+    """A few long rows (the one-pass launch: one read of the scores, the last
+    workgroup of a row selecting from the chunks' lists): predictions inside
+    the band (exact, 1% and 3% off), below it (the chunks' lists capped by
+    their slices), above it so far that the lists miss b* (the whole-row
+    selection), absent and mixed; rows of one chunk, empty rows and rows no
+    longer than k in the same call."""
+    need_gpu()
+    ld = 131076
+    lens = [131076, 131073, 100000, 16385, 16384, 5000, 0, 2048, 40000, 65536]
+    R = len(lens)
+    x = wk.random_logits(18, R, ld, kind)
+    kth = np.array([oracle.topk_row(x[r, :lens[r]], 2048)[1] if lens[r] else np.nan for r in range(R)],
+                   np.float32)
+    _check(x, lens, 2048)
+    for f in (1.0, 1.01, 0.97, 1.03, 0.5, 1.3):
+        _check(x, lens, 2048, (kth * np.float32(f)).astype(np.float32))
+    mixed = kth.copy()
+    mixed[::3] = np.nan
+    mixed[1::3] *= np.float32(2.0)
+    _check(x, lens, 2048, mixed)
+
+
+def test_one_pass_wide_boundary_bin_in_the_lists():
+    """More tokens tie at the k-th score than the LDS selection holds (5000
+    at one value, 1000 above it): the boundary is selected by rounds over the
+    listed entries, and the ties are taken in token order."""
+    need_gpu()
+    n = 131072
+    x = wk.random_logits(19, 2, n, 'normal')
+    r = np.random.default_rng(19)
+    for row in range(2):
+        order = np.argsort(-x[row], kind='stable')
+        v = x[row, order[1000]]
+        below = order[1001:]
+        x[row, r.choice(below, 5000, replace=False)] = v
+    kth = np.array([oracle.topk_row(x[row], 2048)[1] for row in range(2)], np.float32)
+    _check(x, [n, n - 4], 2048, kth)
+    _check(x, [n, n - 4], 4096, kth)
+
+
+def test_one_pass_workspace_reused_across_shapes():
+    """One workspace for calls of different shapes in a row: nothing a call
+    leaves behind steers the next."""
+    need_gpu()
+    import torch
+    from gpu_util import dev, host
+    import indexer_top_kv_amd as ech
+    # (rows, row stride, tokens per row, k)
+    shapes = [(6, 200000, 200000, 2048), (2, 40000, 39999, 7), (9, 131072, 131072, 4096), (1, 16388, 16385, 2048)]
+    ws = torch.empty(max(ech.ech_topk_ws_bytes(R, n, k) for R, _, n, k in shapes), dtype=torch.uint8,
+                     device='cuda')
+    for i, (R, ld, n, k) in enumerate(shapes):
+        x = wk.random_logits(20, R, ld, 'normal', seed_extra=i)
+        kth = np.array([oracle.topk_row(x[row, :n], k)[1] for row in range(R)], np.float32)
+        th = (kth * np.float32(1.01)).astype(np.float32)
+        idx = torch.full((R, k), -7, dtype=torch.int32, device='cuda')
+        kt = torch.empty(R, dtype=torch.float32, device='cuda')
+        to = torch.empty(R, dtype=torch.float32, device='cuda')
+        ech.ech_topk(dev(x), dev(np.full(R, n, np.int32)), n, k, dev(th), to, idx, kt, ws)
+        torch.cuda.synchronize()
+        for row in range(R):
+            ref_idx, ref_kth = oracle.topk_row(x[row, :n], k)
+            np.testing.assert_array_equal(host(idx)[row], ref_idx, err_msg=f'shape {i} row {row}')
+            assert host(kt)[row] == ref_kth
+            assert host(to)[row] == oracle.theta_next(th[row], ref_kth)
