@@ -142,19 +142,33 @@ def bench_decode(args, wl):
     stats_early = layer.stats_early.cpu().numpy()
 
     s0 = torch.cuda.current_stream()
-    if not layer.fused:
-        # The roofline kernel, timed with HIP events on its launch stream: K
-        # launches back to back (the step's queries) between one pair of
-        # events, so no event sits between launches; the average launch is the
-        # span / K.
-        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        layer.logits_only(qd[args.warmup], stream=s0)
-        ev0.record(s0)
-        for s in range(args.steps):
-            layer.logits_only(qd[args.warmup + s], stream=s0)
-        ev1.record(s0)
-        torch.cuda.synchronize()
-        logits_runs = [ev0.elapsed_time(ev1) / args.steps]
+    # The plain scores kernel, timed with HIP events on its launch stream: K
+    # launches back to back (the step's queries) between one pair of events,
+    # so no event sits between launches; the average launch is the span / K.
+    # Without the fused path this is the roofline kernel; with it, the same
+    # stream alone, for comparison with the fused launch inside the step.
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    layer.logits_only(qd[args.warmup], stream=s0)
+    ev0.record(s0)
+    for s in range(args.steps):
+        layer.logits_only(qd[args.warmup + s], stream=s0)
+    ev1.record(s0)
+    torch.cuda.synchronize()
+    logits_runs = [ev0.elapsed_time(ev1) / args.steps]
+
+    # The top-k alone: K calls back to back on the last step's scores with its
+    # prediction, into scratch outputs (the layer's state is left as it is).
+    th_a = layer.theta[layer.parity].clone()
+    th_b, idx_b = torch.empty_like(th_a), torch.empty_like(layer.idx)
+    kth_b, ws_b = torch.empty_like(layer.kth), torch.zeros_like(layer.ws_topk)
+    ech_topk_fn = __import__('indexer_top_kv_amd').ech_topk
+    ech_topk_fn(layer.logits, layer.lens, layer.max_len, layer.k, th_a, th_b, idx_b, kth_b, ws_b, stream=s0)
+    ev0.record(s0)
+    for s in range(args.steps):
+        ech_topk_fn(layer.logits, layer.lens, layer.max_len, layer.k, th_a, th_b, idx_b, kth_b, ws_b, stream=s0)
+    ev1.record(s0)
+    torch.cuda.synchronize()
+    topk_alone_us = ev0.elapsed_time(ev1) / args.steps * 1e3
 
     # Stage breakdown from eager steps with events on each stage's stream.
     # With the fused launch these also time the roofline launch inside the
@@ -180,7 +194,9 @@ def bench_decode(args, wl):
     qa = torch.randn((wl.B, Ha, 576), device='cuda').to(torch.bfloat16).view(torch.int16)
     out_a = torch.empty((wl.B, Ha, 512), dtype=torch.float32, device='cuda')
     lse_a = torch.empty((wl.B, Ha), dtype=torch.float32, device='cuda')
-    ws_a = torch.empty(ech.ech_sparse_attn_ws_bytes(wl.B, Ha, wl.k), dtype=torch.uint8, device='cuda')
+    # a chunk of fewer sequences splits each into more spans: size for the largest need
+    ws_a = torch.empty(max(ech.ech_sparse_attn_ws_bytes(b1 - b0, Ha, wl.k) for b0, b1 in [(0, wl.B)] + layer.chunks),
+                       dtype=torch.uint8, device='cuda')
     sm = 1.0 / float(np.sqrt(192.0))
     if len(layer.chunks) == 1:
         ech.ech_sparse_attn(qa, layer.dev_cache, layer.sel_slot, sm, out_a, lse_a, ws_a)
@@ -247,7 +263,8 @@ def bench_decode(args, wl):
     wall = t1 - t0
     tokens = int(wl.lens.astype(np.int64).sum())
     value = tokens * args.steps / wall
-    logits_ms = avg_ms('logits') if layer.fused else float(np.mean(logits_runs))
+    plain_ms = float(np.mean(logits_runs))
+    logits_ms = avg_ms('logits') if layer.fused else plain_ms
     kbytes = 128 + 4 if wl.kdtype == 'fp8' else 256
     per_token = kbytes + 4                                   # key (+scale) read, score written
     per_launch = tokens * per_token + wl.B * (64 * 128 * 2 + 64 * 4)
@@ -283,9 +300,18 @@ def bench_decode(args, wl):
                      'peak': PEAK_HBM_GBS, 'unit': 'GB/s', 'frac': achieved / PEAK_HBM_GBS,
                      'traffic': traffic, 'algorithmic_bytes_per_launch': per_launch,
                      'avg_launch_us': logits_ms * 1e3,
-                     'timing': ('HIP events on the scores stream around the fused launch in eager steps'
+                     'timing': ('HIP events on the scores stream around the fused launch in eager steps '
+                                '(the PCIe copier runs beside it on the other stream)'
                                 if layer.fused else 'HIP events around K back-to-back launches on its stream'),
-                     'mfma_bf16_frac': flops / (logits_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS},
+                     'mfma_bf16_frac': flops / (logits_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+                     'plain_scores_kernel_alone': {
+                         'kernel': 'logits_decode_fp8_kernel' if wl.kdtype == 'fp8' else 'logits_decode_kernel',
+                         'avg_launch_us': plain_ms * 1e3,
+                         'achieved': per_launch / (plain_ms * 1e-3) / 1e9,
+                         'frac': per_launch / (plain_ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
+                         'traffic': measured_traffic('logits_decode_' + wl.name,
+                                                     source_hash('logits.hip', 'decode.hpp', 'score.hpp')),
+                         'timing': 'HIP events around K back-to-back launches on its stream'}},
         'stages_us_eager': {k: (avg_ms(k) or 0.0) * 1e3
                             for k in ('logits', 'recall_live', 'topk', 'early', 'early_maps', 'recall_early',
                                       'final', 'final_maps', 'recall_final')},
@@ -298,12 +324,18 @@ def bench_decode(args, wl):
     st = out['stages_us_eager']
     topk_bytes = tokens * 4 + wl.B * wl.k * 4
     rec_us = st['recall_live'] + st['recall_early'] + st['recall_final']
+    one_pass = wl.B <= 256 and layer.max_len > 16384
     out['stage_rooflines'] = {
         'topk': {'bound': 'hbm', 'algorithmic_bytes': topk_bytes, 'us': st['topk'],
                  'achieved_GBs': topk_bytes / (st['topk'] * 1e-6) / 1e9 if st['topk'] else None,
                  'peak_GBs': PEAK_HBM_GBS,
                  'frac': topk_bytes / (st['topk'] * 1e-6) / 1e9 / PEAK_HBM_GBS if st['topk'] else None,
-                 'note': 'one read of the scores plus the index output, over the five top-k launches'},
+                 'alone_us': topk_alone_us,
+                 'alone_frac': topk_bytes / (topk_alone_us * 1e-6) / 1e9 / PEAK_HBM_GBS,
+                 'traffic': measured_traffic('topk_one_' + wl.name, source_hash('topk.hip')) if one_pass else None,
+                 'note': ('one read of the scores plus the index output; us: in eager steps, alone_us: K calls '
+                          'back to back; ' + ('one pass (a reset and the pass kernel)' if one_pass else
+                                              'one launch (rows of at most 16384 tokens)'))},
         'recall': {'bound': 'pcie', 'bytes_per_step': out['recall']['bytes_per_step'], 'us': rec_us,
                    'achieved_GBs': out['recall']['bytes_per_step'] / (rec_us * 1e-6) / 1e9 if rec_us else None,
                    'note': 'the recall kernels of eager steps (live copier beside the scoring, rest of EARLY, '

@@ -126,9 +126,14 @@ class DecodeLayer:
         self.ws_final = torch.empty(ech_cache_step_ws_bytes(ECH_FINAL, cb, cb, k, self.max_len, C, m_max),
                                     dtype=torch.uint8, **dev)
         # Scores fused with the first chunk's early fetch: fp8 keys, a host
-        # pool to copy from, and the early fetch on.
+        # pool to copy from, and the early fetch on. By default only for
+        # batches of more than 8 sequences: a sequence's early fetch starts
+        # once its whole row is scored, so with a few long rows the fused
+        # launch ends late (4 x 1M tokens: 261 us per step fused, 208 us
+        # not), while with many rows their early rows cross PCIe under the
+        # scoring (32 x 131072: 405 us vs 441 us; 64 x 110K: 2.06 vs 2.10 ms).
         can_fuse = early and host_pool is not None and kscale is not None and cap <= 4096
-        self.fused = can_fuse if fused is None else bool(fused)
+        self.fused = (can_fuse and self.B > 8) if fused is None else bool(fused)
         if self.fused and not can_fuse:
             raise ValueError('the fused scores + early fetch needs fp8 keys, a host pool, the early fetch and '
                              'cap <= 4096')
@@ -146,6 +151,8 @@ class DecodeLayer:
         self.ev_logits = torch.cuda.Event()
         self.ev_early_maps = torch.cuda.Event()
         self.ev_early = torch.cuda.Event()
+        self.ev_final_maps = torch.cuda.Event()
+        self.ev_final = torch.cuda.Event()
         ech_cache_reset(self.state)
 
     def reset(self) -> None:
@@ -245,12 +252,12 @@ class DecodeLayer:
         if self.early:
             self.ev_logits.record(s0)
         if self.fused:
-            self._after_fused(th, th_next, s0, mark)
+            self._after_fused(th, th_next, s0, mark)   # the first chunk's FINAL recall included
         else:
             self._after_scores(th, th_next, s0, mark)
-        mark('recall_final', s0)
-        self._recall(ECH_FINAL, s0)
-        mark('recall_final', s0)
+            mark('recall_final', s0)
+            self._recall(ECH_FINAL, s0)
+            mark('recall_final', s0)
         if on_chunk is not None:
             on_chunk(first_b0, first_b1, s0)
         for b0, b1 in self.chunks[1:]:
@@ -269,9 +276,11 @@ class DecodeLayer:
 
     def _after_fused(self, th, th_next, s0, mark) -> None:
         """First chunk after the fused launch: on S1, after the live copy,
-        the early rows it left (once the fused launch is done); the top-k and
-        the FINAL maps on S0; ends with S0 waiting for the early rows (the
-        FINAL recall may reuse a slot they fill)."""
+        the early rows it left (once the fused launch is done), then the
+        FINAL recall (it may reuse a slot they fill) once S0 has the FINAL
+        maps; the top-k and the FINAL maps on S0, which ends waiting for
+        S1. The FINAL rows follow the early ones on S1 with no hop back to
+        S0 in between."""
         first_b0, first_b1 = self.chunks[0]
         mark('topk', s0)
         ech_topk(self.logits, self.lens, self.max_len, self.k, th, th_next, self.idx, self.kth, self.ws_topk,
@@ -283,12 +292,17 @@ class DecodeLayer:
         self._recall(ECH_EARLY, self.s1)
         mark('recall_early', self.s1)
         mark('early', self.s1)
-        self.ev_early.record(self.s1)
         mark('final', s0)
         mark('final_maps', s0)
         self._maps(ECH_FINAL, first_b0, first_b1, th, s0)
         mark('final_maps', s0)
-        s0.wait_event(self.ev_early)
+        self.ev_final_maps.record(s0)
+        self.s1.wait_event(self.ev_final_maps)
+        mark('recall_final', self.s1)
+        self._recall(ECH_FINAL, self.s1)
+        mark('recall_final', self.s1)
+        self.ev_final.record(self.s1)
+        s0.wait_event(self.ev_final)
 
     def _after_scores(self, th, th_next, s0, mark) -> None:
         """First chunk after the plain scores: the EARLY maps and recall on
