@@ -378,18 +378,25 @@ def bench_stack(args, wl):
     C_m = wl.C // len(groups)
     total_steps = args.warmup + args.steps
     layers, qs, pools = [], [], []
+    ctx0 = None
     for l in range(L):
         t = time.time()
         wll = wl.scaled(layer=l)
         keys, scale = wk.keys(wll)
         pool = torch.empty((wll.P, wk.ROW_ELEMS), dtype=torch.int16, pin_memory=True)
         wk.host_rows(wll, out=pool.numpy().view(np.uint16))
-        kc, ks, wd = dev(keys), (dev(scale) if scale is not None else None), dev(wk.head_weights(wll))
-        del keys, scale
+        w_np = wk.head_weights(wll)
+        kc, ks, wd = dev(keys), (dev(scale) if scale is not None else None), dev(w_np)
         layers.append([DecodeLayer(kc, ks, wd[b0:b1], wll.tok0[b0:b1], wll.lens[b0:b1], C_m, k=wll.k,
-                                   cap=wll.cap, host_pool=pool) for b0, b1 in groups])
-        qs.append(dev(np.stack(list(wk.decode_queries(wll, total_steps)))))
+                                   cap=wll.cap, host_pool=pool, fused=False)
+                       for b0, b1 in groups])
+        q_np = np.stack(list(wk.decode_queries(wll, total_steps)))
+        qs.append(dev(q_np))
         pools.append(pool)
+        if l == 0:   # layer 0's inputs for the CPU oracle baseline
+            ctx0 = dict(keys=keys, scale=scale, w=w_np, pool=pool, qs=q_np)
+        else:
+            del keys, scale
         log(f'layer {l}: keys, {wll.P} host rows and queries in {time.time() - t:.1f}s')
     stack = DecodeStack(layers)
     step_q = lambda s: [[qs[l][s, b0:b1] for b0, b1 in groups] for l in range(L)]
@@ -413,6 +420,20 @@ def bench_stack(args, wl):
     tokens = int(wl.lens.astype(np.int64).sum())
     step_ms = wall / args.steps * 1e3
     rec_bytes = recalled * 1152 / args.steps
+    # Roofline: every (layer, micro-batch)'s plain scores kernel, K rounds of
+    # L x M launches back to back on one stream between one pair of HIP
+    # events (the step's own queries); per layer = span / (K x L).
+    s0 = torch.cuda.current_stream()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record(s0)
+    for s in range(args.steps):
+        for l in range(L):
+            for m, (b0, b1) in enumerate(groups):
+                layers[l][m].logits_only(qs[l][args.warmup + s, b0:b1], stream=s0)
+    ev1.record(s0)
+    torch.cuda.synchronize()
+    layer_ms = ev0.elapsed_time(ev1) / (args.steps * L)
+    per_layer = tokens * (128 + 4 + 4) + wl.B * (64 * 128 * 2 + 64 * 4)
     return {
         'metric': f'decode tokens scored/s over a {L}-layer step (indexer logits + exact top-k + early/final '
                   f'slot-map step + recall per layer)',
@@ -425,15 +446,21 @@ def bench_stack(args, wl):
         'data': 'synthetic, seeded per layer',
         'config': {'workload': wl.name, 'layers': L, 'micro_batches': len(groups),
                    'micro_batch_sequences': [b1 - b0 for b0, b1 in groups], 'cache_slots_per_micro_batch': C_m,
+                   'fused_scores_early_fetch': layers[0][0].fused,
                    'B': wl.B, 'context': wl.N, 'k': wl.k, 'early_fetch_cap': wl.cap,
                    'launch': launch},
         'us_per_layer': step_ms * 1e3 / L,
         'host_enqueue_ms_per_step': t_host / args.steps * 1e3,
         'recall': {'rows_per_step': recalled / args.steps, 'bytes_per_step': rec_bytes,
                    'GBs_over_step': rec_bytes / (step_ms * 1e-3) / 1e9},
-        'roofline': None,
+        'roofline': {'bound': 'hbm', 'kernel': 'logits_decode_fp8_kernel (every layer and micro-batch)',
+                     'achieved': per_layer / (layer_ms * 1e-3) / 1e9, 'peak': PEAK_HBM_GBS, 'unit': 'GB/s',
+                     'frac': per_layer / (layer_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 'traffic': None,
+                     'algorithmic_bytes_per_layer': per_layer, 'avg_us_per_layer': layer_ms * 1e3,
+                     'timing': 'HIP events around K rounds of the L x M scores launches back to back on one '
+                               'stream'},
         'cpu_baseline': None,
-    }, pools
+    }, pools, ctx0
 
 
 def pcie_check(pool, C, rows=16384, reps=5):
@@ -664,9 +691,14 @@ def main():
     wl = wk.CONFIGS[args.config]
     log(f'{wl.name} on {torch.cuda.get_device_name(0)}')
     if wl.mode == 'decode' and (args.layers > 1 or args.micro_batches > 1):
-        out, pools = bench_stack(args, wl)
+        out, pools, ctx0 = bench_stack(args, wl)
         out['pcie'] = pcie_check(pools[0], wl.C)
         out['recall']['frac_of_memcpy'] = out['recall']['GBs_over_step'] / out['pcie']['h2d_memcpy_GBs']
+        if not args.no_cpu_baseline:
+            log('timing the CPU oracle on a sample of layer 0')
+            cb = cpu_baseline_decode(args, wl, ctx0)
+            cb['sample'] += ' (layer 0; every layer costs the oracle the same, so the rate is per token-layer)'
+            out['cpu_baseline'] = cb
     elif wl.mode == 'decode':
         out, ctx = bench_decode(args, wl)
         out['pcie'] = pcie_check(ctx['pool'], wl.C)

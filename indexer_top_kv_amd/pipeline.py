@@ -357,7 +357,12 @@ class DecodeLayer:
         """Capture one decode step per threshold parity as a hipGraph that
         reads q from a static buffer (every tensor of the step has a fixed
         size and address, so the step replays unchanged). Nothing runs.
-        scores=False captures the step after the scores (replay_after_scores)."""
+        scores=False captures the step after the scores (replay_after_scores);
+        not with the fused path, whose live copier (launched with the scores)
+        must precede the early rest and FINAL recalls of the same step: a
+        graph of the rest alone would not wait for it."""
+        if self.fused and not scores:
+            raise ValueError('the fused path captures whole steps only (the scores launch starts the copier)')
         self.q_static = torch.zeros((self.B, 64, 128), dtype=torch.int16, device=self.logits.device)
         self.graphs = [None, None]
         self.graph_scores = scores
@@ -543,6 +548,12 @@ class DecodeStack:
         self.L, self.M = len(self.layers), (len(self.layers[0]) if self.layers else 0)
         if self.L == 0 or self.M == 0 or any(len(r) != self.M for r in self.layers):
             raise ValueError('layers must be a non-empty L x M list of DecodeLayer')
+        # The stack launches each pair's scores itself and replays graphs of
+        # the rest, which the fused path cannot split (see capture); it is
+        # also slower here (4 layers x 2 micro-batches of 16 sequences: 471
+        # us per layer fused, 408 us not).
+        if any(d.fused for r in self.layers for d in r):
+            raise ValueError('DecodeStack takes layers built with fused=False')
         # Two streams per micro-batch (scores and its chain; EARLY branch),
         # shared by its layers; micro-batch 0's chain is the caller's stream.
         # With two micro-batches these are four streams, one per hardware

@@ -57,7 +57,7 @@ def _build(base, L, M, C_m, steps):
         pool.numpy()[:] = wk.host_rows(wl).view(np.int16)
         kc, ks, wd = dev(keys), dev(scale), dev(w)
         layers.append([DecodeLayer(kc, ks, wd[b0:b1], wl.tok0[b0:b1], wl.lens[b0:b1], C_m, k=wl.k, cap=wl.cap,
-                                   host_pool=pool) for b0, b1 in groups])
+                                   host_pool=pool, fused=False) for b0, b1 in groups])
         refs.append([OracleMicro(wl, keys, scale, w, pool.numpy().copy(), b0, b1, C_m) for b0, b1 in groups])
         qs.append([q for q in wk.decode_queries(wl, steps)])
     return groups, layers, refs, qs
@@ -114,3 +114,12 @@ def test_stack_rejects_bad_shapes():
     mk = lambda: DecodeLayer(dev(keys), dev(scale), w, base.tok0, base.lens, base.C, k=base.k, cap=base.cap)
     with pytest.raises(ValueError):
         DecodeStack([[mk(), mk()], [mk()]])
+    # the fused path: its scores launch starts the live copier, which a graph
+    # of the rest of the step would not wait for
+    pool = torch.zeros((base.P, 576), dtype=torch.int16, pin_memory=True)
+    fused = DecodeLayer(dev(keys), dev(scale), w, base.tok0, base.lens, base.C, k=base.k, cap=base.cap,
+                        host_pool=pool, fused=True)
+    with pytest.raises(ValueError):
+        DecodeStack([[fused]])
+    with pytest.raises(ValueError):
+        fused.capture(scores=False)
