@@ -7,11 +7,9 @@
 //
 // Work split. A workgroup takes one (sequence, token span) and every head
 // (or half of 128 heads when there are fewer workgroups than CUs): each of
-// its waves owns 16 heads. The span's rows are gathered 32
-// tokens at a time from HBM into LDS once for all heads, token-major for the
-// scores and transposed (value column-major) for the output product, so each
-// row crosses HBM once. Per 32-token tile and wave, on the matrix cores
-// (v_mfma_f32_16x16x32_bf16):
+// its waves owns 16 heads. The span's rows are gathered 32 tokens at a time
+// from HBM into LDS once for all heads, so each row crosses HBM once. Per
+// 32-token tile and wave, on the matrix cores (v_mfma_f32_16x16x32_bf16):
 //   S^T[token][head] = K . Q^T      2 token tiles x 18 contraction steps
 //   O^T[col][head]  += V^T . P^T    32 column tiles, contraction = 32 tokens
 // S^T leaves each lane one head (lane % 16) and 4+4 tokens, which are exactly
@@ -37,11 +35,11 @@ constexpr int kTile = 32;                  // tokens per LDS tile
 constexpr int kKs = kRowV / 32;            // contraction steps of the scores (18)
 constexpr int kCt = kValV / 16;            // column tiles of the output (32)
 constexpr int kKPitch = kRowV * 2 + 16;    // bytes per token row in LDS (bank spread)
-constexpr int kVPitch = 72;                // bytes per value column in LDS (32 tokens + pad)
 constexpr int kChunks = kRowV * 2 / 16;    // 16-byte pieces per row (72)
-constexpr int kVChunks = kValV * 2 / 16;   // of which value (64)
 constexpr int kMaxWaves = 8;               // heads <= 128
-constexpr size_t kLdsBytes = (size_t)kTile * kKPitch + (size_t)kValV * kVPitch + kTile * 4;
+
+#define ECH_ATTN_LDS(p) ((__attribute__((address_space(3))) void*)(p))
+
 
 __device__ __forceinline__ float lane_group_max(float x) {
   const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
@@ -50,163 +48,193 @@ __device__ __forceinline__ float lane_group_max(float x) {
   return fmaxf(__uint_as_float(q[0]), __uint_as_float(q[1]));
 }
 
-// Gather the rows of tile tokens [t0, t0 + 32) of this span into registers.
-// Each thread takes pieces i = tid + j*NT, token fastest: neighbouring lanes
-// then write neighbouring tokens of one value column in the transposed tile
-// (2-byte stores without bank conflicts; token-major pieces would put 16
-// lanes on 4 banks), and 16-byte row pieces of neighbouring tokens, whose LDS
-// rows the pitch spreads over all banks. Every slot id is read first with a
-// clamped index and every row piece after, with no branch around a load, so
-// a tile costs two memory round trips (a guarded load waits for all loads in
-// flight before the next one issues). Invalid tokens read slot 0; the
-// result says whether piece 0's token is valid.
-template <int NT>
-__device__ __forceinline__ uint32_t tile_load(const uint4* __restrict__ cache, const int32_t* __restrict__ sel,
-                                              int C, int t0, int t1,
-                                              uint4 (&reg)[(kTile * kChunks + NT - 1) / NT]) {
-  constexpr int kP = (kTile * kChunks + NT - 1) / NT;
-  int slot[kP];
-#pragma unroll
-  for (int j = 0; j < kP; ++j) {
-    const int i = threadIdx.x + j * NT;
-    const int t = i % kTile;
-    slot[j] = sel[min(t0 + t, t1 - 1)];
-  }
-  uint32_t ok0 = 0;
-#pragma unroll
-  for (int j = 0; j < kP; ++j) {
-    const int i = threadIdx.x + j * NT;
-    const int ch = min(i / kTile, kChunks - 1), t = i % kTile;
-    const bool valid = (t0 + t < t1) && slot[j] >= 0 && slot[j] < C;
-    if (j == 0) ok0 = valid;
-    reg[j] = cache[(size_t)(valid ? slot[j] : 0) * kChunks + ch];
-  }
-  return ok0;
+// ------------------------------------------------------------------ span kernel
+// NW waves of NS x 16 heads (NS = 1: 16 heads per wave, two waves per SIMD;
+// two sets per wave would share every key fragment read but need 2 x 144
+// fragment and 256 accumulator registers, past what a wave can hold without
+// spilling). The tile stays token-major in LDS for both products: the value
+// operand V^T of O^T += V^T.P^T comes from ds_read_b64_tr_b16 (within each
+// 16-lane group, lane i receives element i%4 of the 8-byte pieces addressed
+// by lanes 4e + i/4, e = 0..3: with lanes 4j..4j+3 pointing at token j's
+// columns c, c+4, c+8, c+12, lane i gets column c+i of 4 tokens), so no
+// transposed copy is stored. Rows arrive by direct-to-LDS loads into two tile
+// buffers: tile i+1's loads are issued right after the barrier that opens
+// tile i and run under its products. They are issued from inline asm, so
+// that the compiler, which cannot tell the two buffers apart, does not wait
+// for them before every LDS read; they write no register, and each tile opens
+// with an explicit wait for all of them and a barrier. Slot ids go through a
+// 3-deep LDS ring, loaded one tile further ahead and used only after that
+// wait. Measured at 32 x 128 x 2048: each tile's loads have landed when its
+// products start (0.3 us of wait and barrier per tile), the products take
+// ~3 us per 32-token tile (LDS reads of every wave's operands: ~1.8 us at
+// 128 B per clock).
+constexpr int kP2 = kKPitch / 16;            // 73 chunks per token row in LDS (one spare: banks)
+constexpr int kPos2 = kTile * kP2;           // 2336 chunk positions per tile
+constexpr int kBuf2 = kPos2 * 16;            // 37376 bytes per tile buffer
+constexpr int kInstr2 = (kPos2 + 63) / 64;   // 37 load instructions per tile
+
+typedef short v4s_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ bf16x8_t tr_pair(const uint8_t* p0, const uint8_t* p1) {
+  const v4s_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s_t*)(p0));
+  const v4s_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s_t*)(p1));
+  typedef short v8s_t __attribute__((ext_vector_type(8)));
+  const v8s_t v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  return __builtin_bit_cast(bf16x8_t, v);
 }
 
-// Pieces beyond the tile (i >= 32 * 72) were loaded from a clamped address
-// and are dropped here. Threads 0..31 hold piece 0 of token tid (chunk 0).
-template <int NT>
-__device__ __forceinline__ void tile_store(uint8_t* __restrict__ lds_k, uint8_t* __restrict__ lds_v,
-                                           int* __restrict__ lds_ok, uint32_t ok,
-                                           const uint4 (&reg)[(kTile * kChunks + NT - 1) / NT]) {
-  constexpr int kP = (kTile * kChunks + NT - 1) / NT;
-#pragma unroll
-  for (int j = 0; j < kP; ++j) {
-    const int i = threadIdx.x + j * NT;
-    if (i >= kTile * kChunks) break;
-    const int ch = i / kTile, t = i - ch * kTile;
-    *reinterpret_cast<uint4*>(lds_k + t * kKPitch + ch * 16) = reg[j];
-    if (ch < kVChunks) {
-      const uint32_t w[4] = {reg[j].x, reg[j].y, reg[j].z, reg[j].w};
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const uint16_t v = (uint16_t)(w[e >> 1] >> ((e & 1) * 16));
-        *reinterpret_cast<uint16_t*>(lds_v + (ch * 8 + e) * kVPitch + t * 2) = v;
-      }
-    }
-  }
-  if (threadIdx.x < kTile) lds_ok[threadIdx.x] = (int)ok;
-}
-
-// grid (spans, B), block 64 * H/16 threads (NT fixed at compile time).
-template <int NT>
-__global__ void __launch_bounds__(NT, 1)
+// grid (spans x head groups, B), block 64 * NW threads; NS sets of 16 heads per wave.
+template <int NW, int NS>
+__global__ void __launch_bounds__(64 * NW, 1)
     attn_span_kernel(const uint16_t* __restrict__ q, const uint4* __restrict__ cache, int C,
-                     const int32_t* __restrict__ sel_slot, int H, int k, int span, float scale2,
-                     float* __restrict__ part_o, float2* __restrict__ part_ml) {
-  extern __shared__ __align__(16) uint8_t smem[];
-  uint8_t* lds_k = smem;
-  uint8_t* lds_v = smem + kTile * kKPitch;
-  int* lds_ok = reinterpret_cast<int*>(lds_v + kValV * kVPitch);
-  constexpr int kP = (kTile * kChunks + NT - 1) / NT;
-
-  // blockIdx.x = span * hsplit + head group (hsplit = H / heads per workgroup)
-  const int hsplit = H / (NT / 4);
+                       const int32_t* __restrict__ sel_slot, int H, int k, int span, float scale2,
+                       float* __restrict__ part_o, float2* __restrict__ part_ml) {
+  __shared__ __align__(16) uint8_t tiles[2][kBuf2];
+  __shared__ int slots[3][kTile];   // slot id of each token of a tile, -1: nothing to attend
+  constexpr int kJ = (kInstr2 + NW - 1) / NW;   // load instructions per wave per tile
+  const int hsplit = H / (16 * NS * NW);
   const int b = blockIdx.y, sp = blockIdx.x / hsplit, nsp = gridDim.x / hsplit;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, col = lane & 15, grp = lane >> 4;
-  const int h = (blockIdx.x % hsplit) * (NT / 4) + wave * 16 + col;   // this lane's head (S^T, O^T column)
+  const int h0 = (blockIdx.x % hsplit) * (16 * NS * NW) + wave * 16 * NS + col;   // head set hs: h0 + 16 hs
   const int32_t* sel = sel_slot + (size_t)b * k;
   const int t_begin = sp * span, t_end = min(k, t_begin + span);
+  const int ntiles = t_end > t_begin ? (t_end - t_begin + kTile - 1) / kTile : 0;
+  const bool slot_lane = wave == 0 && lane < kTile;   // the lanes that fetch slot ids
 
-  // Q^T fragments (B operand of the scores): head h, dims 32 s + 8 grp .. +8.
-  bf16x8_t qf[kKs];
-  const uint8_t* qrow = reinterpret_cast<const uint8_t*>(q + ((size_t)b * H + h) * kRowV);
-#pragma unroll
-  for (int s = 0; s < kKs; ++s) qf[s] = as_bf16x8(*reinterpret_cast<const uint4*>(qrow + s * 64 + grp * 16));
+  bf16x8_t qf[NS][kKs];   // Q^T fragments: head h0 + 16 hs, dims 32 s + 8 grp .. +8
+  f32x4_t acc[NS][kCt];
+  float m[NS], l[NS];
 
-  f32x4_t acc[kCt];
+  // slot id of token t0 + lane: a clamped load, then validity in arithmetic
+  auto slot_raw = [&](int t0) -> int { return sel[min(t0 + lane, t_end - 1)]; };
+  auto slot_ok = [&](int t0, int sl) -> int { return (t0 + lane < t_end && sl >= 0 && sl < C) ? sl : -1; };
+  // direct-to-LDS loads of the tile whose slot ids are in slots[si]; the
+  // pad chunk of each LDS row and positions past the tile are not loaded
+  auto issue = [&](int si, uint8_t* dst) {
 #pragma unroll
-  for (int c = 0; c < kCt; ++c) acc[c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  float m = -__builtin_inff(), l = 0.f;
-
-  for (int t0 = t_begin; t0 < t_end; t0 += kTile) {
-    {
-      uint4 reg[kP];
-      const uint32_t ok = tile_load<NT>(cache, sel, C, t0, t_end, reg);
-      __syncthreads();                                       // the previous tile is consumed
-      tile_store<NT>(lds_k, lds_v, lds_ok, ok, reg);
-      __syncthreads();
-    }
-
-    // scores of the 32 tokens for this wave's 16 heads
-    f32x4_t st[2];
-#pragma unroll
-    for (int sub = 0; sub < 2; ++sub) {
-      st[sub] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-      const uint8_t* kr = lds_k + (sub * 16 + col) * kKPitch + grp * 16;
-#pragma unroll
-      for (int s = 0; s < kKs; ++s)
-        st[sub] = mfma(as_bf16x8(*reinterpret_cast<const uint4*>(kr + s * 64)), qf[s], st[sub]);
-    }
-    float sv[8];
-    float tmax = -__builtin_inff();
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int t = (j < 4) ? (4 * grp + j) : (16 + 4 * grp + j - 4);
-      sv[j] = lds_ok[t] ? st[j >> 2][j & 3] * scale2 : -__builtin_inff();
-      tmax = fmaxf(tmax, sv[j]);
-    }
-    tmax = lane_group_max(tmax);
-    // The running max moves only when some head's tile max exceeds it by more
-    // than 8 (base 2): weights up to 2^8 stay exact enough in fp32 sums and
-    // in bf16, and most tiles then skip the rescale of the accumulators.
-    const bool grow = __any(tmax > m + 8.f);
-    const float mn = grow ? fmaxf(m, tmax) : m;
-    const bool none = (mn == -__builtin_inff());
-    const float alpha = none ? 1.f : exp2f(m - mn);
-    float psum = 0.f;
-    bf16x8_t pb;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const float p = none ? 0.f : exp2f(sv[j] - mn);
-      psum += p;
-      pb[j] = (__bf16)p;
-    }
-    l = l * alpha + lane_group_sum(psum);
-    m = mn;
-    if (grow) {
-#pragma unroll
-      for (int c = 0; c < kCt; ++c) {
-#pragma unroll
-        for (int v = 0; v < 4; ++v) acc[c][v] *= alpha;
+    for (int j = 0; j < kJ; ++j) {
+      const int ins = j * NW + wave;
+      const int p = ins * 64 + lane;
+      const int t = p / kP2, c = p - t * kP2;
+      if (ins < kInstr2 && p < kPos2 && c < kChunks) {
+        const int sl = slots[si][t];
+        const uint4* src = cache + (size_t)max(sl, 0) * kChunks + c;
+        const uint32_t lds = __builtin_amdgcn_readfirstlane(
+            static_cast<uint32_t>(reinterpret_cast<uintptr_t>(ECH_ATTN_LDS(dst + ins * 1024))));
+        asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off nt" ::"s"(lds), "v"(src) : "memory", "m0");
       }
     }
-    // O^T += V^T . P^T: A = value column (ct*16 + col) at this lane group's tokens
+  };
+  // the scores, online softmax and value product of the tile in cur
+  auto compute = [&](int si, const uint8_t* cur) {
+    f32x4_t st[2][NS];   // [16-token half][head set]
+#pragma unroll
+    for (int sub = 0; sub < 2; ++sub) {
+#pragma unroll
+      for (int hs = 0; hs < NS; ++hs) st[sub][hs] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      const uint8_t* kr = cur + (sub * 16 + col) * kKPitch + grp * 16;
+#pragma unroll
+      for (int s = 0; s < kKs; ++s) {
+        const bf16x8_t kf = as_bf16x8(*reinterpret_cast<const uint4*>(kr + s * 64));
+#pragma unroll
+        for (int hs = 0; hs < NS; ++hs) st[sub][hs] = mfma(kf, qf[hs][s], st[sub][hs]);
+      }
+    }
+    bool ok[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) ok[j] = slots[si][(j < 4) ? (4 * grp + j) : (16 + 4 * grp + j - 4)] >= 0;
+    bf16x8_t pb[NS];
+    float alpha[NS];
+    bool grow[NS];
+#pragma unroll
+    for (int hs = 0; hs < NS; ++hs) {
+      float sv[8];
+      float tmax = -__builtin_inff();
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        sv[j] = ok[j] ? st[j >> 2][hs][j & 3] * scale2 : -__builtin_inff();
+        tmax = fmaxf(tmax, sv[j]);
+      }
+      tmax = lane_group_max(tmax);
+      // the running max moves only when a head's tile max exceeds it by more
+      // than 8 (base 2), as in the 16-head form
+      grow[hs] = __any(tmax > m[hs] + 8.f);
+      const float mn = grow[hs] ? fmaxf(m[hs], tmax) : m[hs];
+      const bool none = (mn == -__builtin_inff());
+      alpha[hs] = none ? 1.f : exp2f(m[hs] - mn);
+      float psum = 0.f;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const float p = none ? 0.f : exp2f(sv[j] - mn);
+        psum += p;
+        pb[hs][j] = (__bf16)p;
+      }
+      l[hs] = l[hs] * alpha[hs] + lane_group_sum(psum);
+      m[hs] = mn;
+    }
+#pragma unroll
+    for (int hs = 0; hs < NS; ++hs) {
+      if (grow[hs]) {
+#pragma unroll
+        for (int c = 0; c < kCt; ++c)
+#pragma unroll
+          for (int v = 0; v < 4; ++v) acc[hs][c][v] *= alpha[hs];
+      }
+    }
+    // O^T += V^T . P^T: the value operand of tokens {4 grp .. +3, 16 + 4 grp .. +3}
+    // (the order of this lane's probabilities) at column c*16 + col
+    const uint8_t* vb = cur + (4 * grp + (col >> 2)) * kKPitch + 8 * (col & 3);
 #pragma unroll
     for (int c = 0; c < kCt; ++c) {
-      const uint8_t* vr = lds_v + (c * 16 + col) * kVPitch;
-      const uint2 lo = *reinterpret_cast<const uint2*>(vr + 8 * grp);
-      const uint2 hi = *reinterpret_cast<const uint2*>(vr + 32 + 8 * grp);
-      acc[c] = mfma(as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y)), pb, acc[c]);
+      const bf16x8_t vf = tr_pair(vb + c * 32, vb + 16 * kKPitch + c * 32);
+#pragma unroll
+      for (int hs = 0; hs < NS; ++hs) acc[hs][c] = mfma(vf, pb[hs], acc[hs][c]);
+    }
+  };
+
+  // The first tile's slot ids, then its loads, go out before the query
+  // fragments (a wait for the slot ids would otherwise wait for them too).
+  if (ntiles > 0) {
+    if (slot_lane) slots[0][lane] = slot_ok(t_begin, slot_raw(t_begin));
+    __syncthreads();
+    issue(0, tiles[0]);
+  }
+  int nxt = slot_lane && ntiles > 1 ? slot_raw(t_begin + kTile) : -1;
+#pragma unroll
+  for (int hs = 0; hs < NS; ++hs) {
+    const uint8_t* qrow = reinterpret_cast<const uint8_t*>(q + ((size_t)b * H + h0 + 16 * hs) * kRowV);
+#pragma unroll
+    for (int s = 0; s < kKs; ++s) qf[hs][s] = as_bf16x8(*reinterpret_cast<const uint4*>(qrow + s * 64 + grp * 16));
+#pragma unroll
+    for (int c = 0; c < kCt; ++c) acc[hs][c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    m[hs] = -__builtin_inff();
+    l[hs] = 0.f;
+  }
+  if (ntiles > 0) {
+    // one tile: its loads have landed (every wave waited, then the barrier),
+    // the next tile's slot ids are published and its loads issued, then the
+    // products of this tile run over them
+    for (int i = 0; i < ntiles; ++i) {
+      // every load of this wave (the builtin form, so that the compiler knows
+      // the query fragments and slot ids are in as well)
+      __builtin_amdgcn_s_waitcnt(0x70 | 0xF00);   // vmcnt(0)
+      if (slot_lane && i + 1 < ntiles) slots[(i + 1) % 3][lane] = slot_ok(t_begin + (i + 1) * kTile, nxt);
+      __syncthreads();
+      if (i + 1 < ntiles) issue((i + 1) % 3, tiles[(i + 1) & 1]);
+      if (slot_lane && i + 2 < ntiles) nxt = slot_raw(t_begin + (i + 2) * kTile);
+      compute(i % 3, tiles[i & 1]);
     }
   }
 
-  // partials: O^T column c = ct*16 + 4 grp + v of head h
-  float* po = part_o + (((size_t)b * nsp + sp) * H + h) * kValV;
+  // partials: O^T column c*16 + 4 grp + v of heads h0 + 16 hs
 #pragma unroll
-  for (int c = 0; c < kCt; ++c) *reinterpret_cast<f32x4_t*>(po + c * 16 + 4 * grp) = acc[c];
-  if (grp == 0) part_ml[((size_t)b * nsp + sp) * H + h] = make_float2(m, l);
+  for (int hs = 0; hs < NS; ++hs) {
+    const int h = h0 + 16 * hs;
+    float* po = part_o + (((size_t)b * nsp + sp) * H + h) * kValV;
+#pragma unroll
+    for (int c = 0; c < kCt; ++c) *reinterpret_cast<f32x4_t*>(po + c * 16 + 4 * grp) = acc[hs][c];
+    if (grp == 0) part_ml[((size_t)b * nsp + sp) * H + h] = make_float2(m[hs], l[hs]);
+  }
 }
 
 // out[b, h, :] and lse[b, h] from the spans' partials. grid (H, B), 128 threads.
@@ -298,19 +326,19 @@ extern "C" int ech_sparse_attn(const void* q, const void* dev_cache, int32_t C, 
   float2* part_ml = reinterpret_cast<float2*>(static_cast<char*>(ws) + ((o + 255) & ~(size_t)255));
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   const float scale2 = sm_scale * 1.4426950408889634f;
+  const auto* qq = static_cast<const uint16_t*>(q);
+  const auto* cc = static_cast<const uint4*>(dev_cache);
   // With fewer workgroups than CUs (a few sequences), 128 heads go to two
   // workgroups of 64 per span: twice the workgroups, rows read twice (one
   // sequence: 36 -> 29 us). With more, one workgroup of 128 reads each row
-  // once and its 8 waves fill a CU.
+  // once.
   const int hsplit = (H == 16 * kMaxWaves && B * nsp < 256) ? 2 : 1;
   const dim3 grid(nsp * hsplit, B);
-  const auto* qq = static_cast<const uint16_t*>(q);
-  const auto* cc = static_cast<const uint4*>(dev_cache);
   switch (H / 16 / hsplit) {
-#define ECH_ATTN_CASE(W)                                                                                      \
-  case W:                                                                                                     \
-    hipLaunchKernelGGL(attn_span_kernel<64 * W>, grid, dim3(64 * W), kLdsBytes, s, qq, cc, C, sel_slot, H, k, \
-                       span, scale2, part_o, part_ml);                                                        \
+#define ECH_ATTN_CASE(W)                                                                                        \
+  case W:                                                                                                       \
+    hipLaunchKernelGGL((attn_span_kernel<W, 1>), grid, dim3(64 * W), 0, s, qq, cc, C, sel_slot, H, k, span,     \
+                       scale2, part_o, part_ml);                                                                \
     break;
     ECH_ATTN_CASE(1)
     ECH_ATTN_CASE(2)
