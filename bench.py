@@ -120,12 +120,15 @@ def bench_decode(args, wl):
                         fused=False if (args.no_fused or args.no_early) else None)
     torch.cuda.synchronize()
     log(f'chunks {layer.chunks}; warm-up {args.warmup} steps')
-    for s in range(args.warmup):
-        layer.step(qd[s])
-    torch.cuda.synchronize()
     if not args.eager:
-        layer.capture()
+        layer.capture()          # nothing runs; the warm-up steps are replays of the timed path
         torch.cuda.synchronize()
+    for s in range(args.warmup):
+        if args.eager:
+            layer.step(qd[s])
+        else:
+            layer.replay(qd[s])
+    torch.cuda.synchronize()
     recalled0 = int(layer.state.ctr[4].item())
     log(f'timing {args.steps} steps ({"eager launches" if args.eager else "hipGraph replay per step"})')
     torch.cuda.synchronize()
@@ -338,8 +341,10 @@ def bench_decode(args, wl):
                                               'one launch (rows of at most 16384 tokens)'))},
         'recall': {'bound': 'pcie', 'bytes_per_step': out['recall']['bytes_per_step'], 'us': rec_us,
                    'achieved_GBs': out['recall']['bytes_per_step'] / (rec_us * 1e-6) / 1e9 if rec_us else None,
-                   'note': 'the recall kernels of eager steps (live copier beside the scoring, rest of EARLY, '
-                           'FINAL); denominator: pcie.h2d_memcpy_GBs'},
+                   'note': ('the recall kernels of eager steps: the live copier (early rows beside the scoring, '
+                            'then the FINAL rows) and the rest of both lists (ech_recall_rest); denominator: '
+                            'pcie.h2d_memcpy_GBs' if layer.fused else
+                            'the recall kernels of eager steps (EARLY, FINAL); denominator: pcie.h2d_memcpy_GBs')},
         'attention': {'kernel': 'ech_sparse_attn (span + merge launches)', 'heads': Ha, 'rows_attended': n_sel,
                       'us': attn_us,
                       'bound': 'hbm',
@@ -355,8 +360,10 @@ def bench_decode(args, wl):
                    'note': 'one decoded token per sequence: its row written over PCIe into the pinned pool, '
                            'its fp8 key and scale into the key cache; latency-bound'},
         'allocator': {'early_maps_us': st['early_maps'], 'final_maps_us': st['final_maps'],
-                      'note': 'slot-map phases in eager steps (count, place), run beside '
-                              'the top-k (EARLY) and beside the EARLY recall (FINAL)'},
+                      'note': ('FINAL maps (count, place) in eager steps, beside the live copier; the EARLY maps '
+                               'are part of the fused launch' if layer.fused else
+                               'slot-map phases in eager steps (count, place), run beside '
+                               'the top-k (EARLY) and beside the EARLY recall (FINAL)')},
     }
     return out, dict(wl=wl, pool=pool, qs=qs, w=w, keys=keys, scale=scale)
 
@@ -400,11 +407,11 @@ def bench_stack(args, wl):
         log(f'layer {l}: keys, {wll.P} host rows and queries in {time.time() - t:.1f}s')
     stack = DecodeStack(layers)
     step_q = lambda s: [[qs[l][s, b0:b1] for b0, b1 in groups] for l in range(L)]
-    for s in range(args.warmup):
-        stack.step(step_q(s))
-    torch.cuda.synchronize()
     if not args.eager:
-        stack.capture()
+        stack.capture()          # nothing runs; the warm-up steps are replays of the timed path
+    torch.cuda.synchronize()
+    for s in range(args.warmup):
+        (stack.step if args.eager else stack.replay)(step_q(s))
     torch.cuda.synchronize()
     rec0 = sum(int(d.state.ctr[4].item()) for r in layers for d in r)
     launch = ('eager launches' if args.eager

@@ -84,6 +84,12 @@ extern "C" {
 #define ECH_CTR_TICKET    9   /* reserved: stays 0 */
 #define ECH_CTR_NCOPIED_EARLY 10 /* leading EARLY miss-list entries already copied (by ech_recall_early_live) */
 #define ECH_CTR_LIVE     11   /* 1 while ech_index_logits_early is writing the early list; ech_recall(EARLY) clears it */
+#define ECH_CTR_NCOPIED_FINAL 12 /* leading FINAL miss-list entries already copied (by ech_recall_early_live) */
+#define ECH_CTR_FINAL_READY 13 /* bit 0: the FINAL phase's miss list is complete; bit 1: its allocation walked
+                                  onto slots the EARLY phase before it allocated (cleared by each FINAL phase
+                                  and by ech_index_logits_early) */
+#define ECH_CTR_FINAL_DONE 14 /* internal: FINAL placing workgroups finished */
+#define ECH_CTR_EARLY_WALK 15 /* ring positions the last EARLY phase walked, head to last slot it allocated (0: none) */
 #define ECH_CTR_LEN      16
 
 /* ---- sticky status bits in ctr[ECH_CTR_STATUS] */
@@ -97,7 +103,8 @@ extern "C" {
 const char* ech_status_str(int code);
 
 /* Library ABI version (major*100 + minor); 200: the grouped early-fetch calls gave way to
-   ech_index_logits_early; ech_topk_noalloc. */
+   ech_index_logits_early; ech_topk_noalloc. 300: ech_recall_early_live also takes the FINAL list;
+   ech_recall_rest. */
 int ech_version(void);
 
 /*
@@ -258,7 +265,9 @@ int ech_cache_step(int phase, int32_t* tok2slot, int64_t P, int32_t* slot2tok, i
  * otherwise; `miss` is the list that phase wrote. Phase ECH_EARLY starts at
  * m = ctr[ECH_CTR_NCOPIED_EARLY] (rows ech_index_logits_early already
  * copied; 0 after ech_cache_step). Rows are read directly over
- * PCIe by a gather kernel (zero-copy). A FINAL recall must be ordered after
+ * PCIe by a gather kernel (zero-copy). Phase ECH_FINAL starts at
+ * m = ctr[ECH_CTR_NCOPIED_FINAL] (rows ech_recall_early_live already copied;
+ * 0 after ech_cache_step(ECH_FINAL)). A FINAL recall must be ordered after
  * the EARLY recall of the same step (it may reuse a slot the EARLY phase
  * filled).
  *  host_pool  [P, row_bytes] pinned host memory (hipHostMalloc / torch
@@ -323,12 +332,45 @@ int ech_index_logits_early(const void* q, const float* w, const void* kcache, in
  * The copier never depends on being scheduled beside the scoring: it waits
  * for the list to start and for each entry with a bounded patience (1 ms
  * without progress) and otherwise leaves the rows to ech_recall(ECH_EARLY).
+ *
+ * With miss_final (the list of the ech_cache_step(ECH_FINAL) call that
+ * follows in the same step, on another stream, for the same sequences), the
+ * copier goes on to the FINAL rows once it has copied the whole early list:
+ * it waits, with the same patience, for that phase to complete its list
+ * (ctr[ECH_CTR_FINAL_READY] bit 0) and copies its entries in order, leaving
+ * ctr[ECH_CTR_NCOPIED_FINAL] = the copied prefix; ech_recall(ECH_FINAL) or
+ * ech_recall_rest, ordered after both, copies the rest. It copies no FINAL
+ * row when the FINAL allocation walked onto slots the early phase allocated
+ * (bit 1): those rows must land after the early ones.
  *  host_pool [P, row_bytes] pinned, device-mapped (host pointer); dev_cache
  *  [C, row_bytes]; row_bytes a multiple of 16, at most 32768; miss_early,
  *  M_early, ctr and ws: those of the ech_index_logits_early call.
+ *  miss_final [M_final, 2], 8-byte aligned, or NULL (early rows only).
  */
 int ech_recall_early_live(const void* host_pool, int64_t P, int64_t row_bytes, void* dev_cache, int32_t C,
-                          const int32_t* miss_early, int32_t M_early, int32_t* ctr, void* ws, void* stream);
+                          const int32_t* miss_early, int32_t M_early, const int32_t* miss_final, int32_t M_final,
+                          int32_t* ctr, void* ws, void* stream);
+
+/*
+ * ech_recall_rest - what ech_recall_early_live left of a step's two lists, in
+ * one launch (ECHO explainer, "One layer, one step: free -> allocate ->
+ * recall"): the early entries m >= ctr[ECH_CTR_NCOPIED_EARLY] (m <
+ * ctr[ECH_CTR_NMISS_EARLY]) whose slot still holds their token
+ * (slot2tok[slot] == g: a slot the FINAL phase gave to another token gets
+ * that token's row from the FINAL list instead), and the FINAL entries
+ * m >= ctr[ECH_CTR_NCOPIED_FINAL] (m < ctr[ECH_CTR_NMISS]); so no two rows of
+ * the launch go to one slot. The same rows as ech_recall(ECH_EARLY) followed
+ * by ech_recall(ECH_FINAL). Enqueue it after the FINAL phase and after the
+ * copier; it ends the step's early list (ctr[ECH_CTR_LIVE] = 0) and adds the
+ * rows it copies to ctr[ECH_CTR_RECALLED].
+ *  host_pool [P, row_bytes] pinned, device-mapped (host pointer); dev_cache
+ *  [C, row_bytes]; row_bytes a multiple of 16; both 16-byte aligned.
+ *  miss_early [M_early, 2], miss [M_max, 2]: the lists of the step's EARLY
+ *  and FINAL phases; slot2tok [C] the layer's map after the FINAL phase.
+ */
+int ech_recall_rest(const void* host_pool, int64_t P, int64_t row_bytes, void* dev_cache, int32_t C,
+                    const int32_t* miss_early, int32_t M_early, const int32_t* miss, int32_t M_max,
+                    const int32_t* slot2tok, int32_t* ctr, void* stream);
 
 /*
  * ech_sparse_attn - the consumer of sel_slot: softmax attention of each head

@@ -17,12 +17,14 @@ import torch
 from . import _native
 from ._native import (ECH_EARLY, ECH_FINAL, ECH_PREFILL, ECH_KEY_BF16, ECH_KEY_FP8,  # noqa: F401
                       CTR_HEAD, CTR_EPOCH, CTR_NMISS, CTR_NEVICT, CTR_RECALLED, CTR_STATUS, CTR_NWANT,
-                      CTR_NPINNED, CTR_NMISS_EARLY, CTR_TICKET, CTR_NCOPIED_EARLY, CTR_LIVE, CTR_LEN, ST_OVERFLOW, ST_BADTOK,
+                      CTR_NPINNED, CTR_NMISS_EARLY, CTR_TICKET, CTR_NCOPIED_EARLY, CTR_LIVE,
+                      CTR_NCOPIED_FINAL, CTR_FINAL_READY, CTR_FINAL_DONE, CTR_EARLY_WALK, CTR_LEN, ST_OVERFLOW, ST_BADTOK,
                       ST_BADMISS, ST_FULL, ST_TIMEOUT)
 
 __all__ = ['ech_kv_append', 'ech_sparse_attn', 'ech_sparse_attn_ws_bytes', 'ech_index_logits', 'ech_index_logits_causal', 'ech_topk', 'ech_topk_noalloc', 'ech_topk_ws_bytes', 'ech_cache_reset',
            'ech_cache_step', 'ech_cache_step_ws_bytes', 'ech_recall', 'ech_index_logits_early',
-           'ech_index_logits_early_ws_bytes', 'ech_recall_early_live', 'EchError', 'LayerState', 'lib']
+           'ech_index_logits_early_ws_bytes', 'ech_recall_early_live', 'ech_recall_rest', 'EchError', 'LayerState',
+           'lib']
 
 
 class EchError(RuntimeError):
@@ -198,14 +200,27 @@ def ech_index_logits_early(q, w, kcache, kscale, row_tok0, row_len, max_len: int
         ws.numel() * ws.element_size(), _stream(stream)))
 
 
-def ech_recall_early_live(host_pool, dev_cache, state: 'LayerState', ws, stream=None) -> None:
+def ech_recall_early_live(host_pool, dev_cache, state: 'LayerState', ws, stream=None, final: bool = False) -> None:
     """Copy early rows as ech_index_logits_early allocates them (enqueue on a
     second stream right after it; ech_recall(ECH_EARLY) afterwards copies the
-    rest)."""
+    rest). final=True: then the rows of the FINAL phase that follows in the
+    same step (state.miss), once that phase has completed its list;
+    ech_recall(ECH_FINAL) afterwards copies what it left."""
     row_bytes = host_pool.shape[1] * host_pool.element_size()
     _check('ech_recall_early_live', lib().ech_recall_early_live(
         _ptr(host_pool), host_pool.shape[0], row_bytes, _ptr(dev_cache), dev_cache.shape[0], _ptr(state.miss_early),
-        state.miss_early.shape[0], _ptr(state.ctr), _ptr(ws), _stream(stream)))
+        state.miss_early.shape[0], _ptr(state.miss) if final else None, state.miss.shape[0] if final else 0,
+        _ptr(state.ctr), _ptr(ws), _stream(stream)))
+
+
+def ech_recall_rest(host_pool, dev_cache, state: 'LayerState', stream=None) -> None:
+    """What ech_recall_early_live left of the step's early and FINAL lists, in
+    one launch (after the FINAL phase and the copier)."""
+    row_bytes = host_pool.shape[1] * host_pool.element_size()
+    _check('ech_recall_rest', lib().ech_recall_rest(
+        _ptr(host_pool), host_pool.shape[0], row_bytes, _ptr(dev_cache), dev_cache.shape[0], _ptr(state.miss_early),
+        state.miss_early.shape[0], _ptr(state.miss), state.miss.shape[0], _ptr(state.slot2tok), _ptr(state.ctr),
+        _stream(stream)))
 
 
 # ------------------------------------------------------------------ consumer

@@ -25,7 +25,8 @@ ECH_FINAL = 1
 ECH_PREFILL = 2
 
 (CTR_HEAD, CTR_EPOCH, CTR_NMISS, CTR_NEVICT, CTR_RECALLED, CTR_STATUS, CTR_NWANT, CTR_NPINNED,
- CTR_NMISS_EARLY, CTR_TICKET, CTR_NCOPIED_EARLY, CTR_LIVE) = range(12)
+ CTR_NMISS_EARLY, CTR_TICKET, CTR_NCOPIED_EARLY, CTR_LIVE, CTR_NCOPIED_FINAL, CTR_FINAL_READY, CTR_FINAL_DONE,
+ CTR_EARLY_WALK) = range(16)
 CTR_LEN = 16
 
 ST_OVERFLOW = 1
@@ -62,7 +63,8 @@ SIGNATURES = {
     'ech_index_logits_early': (ctypes.c_int, [_p, _p, _p, ctypes.c_int, _p, _p, _p, ctypes.c_int, ctypes.c_int,
                                               ctypes.c_int, ctypes.c_int, _p, _i64, ctypes.c_int, ctypes.c_int, _p,
                                               ctypes.c_int, _p, _i64, _p, _p, _i32, _p, _i32, _p, _p, _p, _sz, _p]),
-    'ech_recall_early_live': (ctypes.c_int, [_p, _i64, _i64, _p, _i32, _p, _i32, _p, _p, _p]),
+    'ech_recall_early_live': (ctypes.c_int, [_p, _i64, _i64, _p, _i32, _p, _i32, _p, _i32, _p, _p, _p]),
+    'ech_recall_rest': (ctypes.c_int, [_p, _i64, _i64, _p, _i32, _p, _i32, _p, _i32, _p, _p, _p]),
     'ech_kv_append': (ctypes.c_int, [_p, _i64, _i64, _p, ctypes.c_int, _p, _p, _p, _p, _p, ctypes.c_int, _p, _p, _p,
                                      _p, _p]),
     'ech_sparse_attn_ws_bytes': (_sz, [ctypes.c_int, ctypes.c_int, ctypes.c_int]),

@@ -91,6 +91,14 @@ size_t layout(int phase, int B, int k, int max_len, CWs* w, char* base) {
 
 __device__ __forceinline__ void set_status(int32_t* ctr, int bit) { atomicOr(&ctr[ECH_CTR_STATUS], bit); }
 
+// Relaxed device-scope stores and loads: coherent across the XCDs' L2s, so a
+// word written in a launch is seen by a workgroup of a launch running beside
+// it (the live copier) without a release fence.
+__device__ __forceinline__ void st_dev(int32_t* p, int32_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void wait_vm_zero() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
 // Start of a phase, by one thread of its counting kernel: publish the epoch
 // and the head (the placing kernel's blocks read them while its bookkeeping
 // block rewrites ctr) and clear the eviction count.
@@ -210,7 +218,12 @@ __global__ __launch_bounds__(kT) void pin_final_kernel(const int32_t* __restrict
     w.want[blk] = nm;
     if (blockIdx.x == 0) {
       stats[4 * b + 3] = 0;   // evictions, counted by the placing kernel
-      if (b == 0) publish_phase(ctr, ep, w);
+      if (b == 0) {
+        publish_phase(ctr, ep, w);
+        ctr[ECH_CTR_NCOPIED_FINAL] = 0;   // nothing of this list is copied yet
+        ctr[ECH_CTR_FINAL_READY] = 0;     // the placing kernel's last workgroup sets it
+        ctr[ECH_CTR_FINAL_DONE] = 0;
+      }
     }
   }
 }
@@ -454,24 +467,38 @@ __device__ void bookkeep(int phase, int nseq, int cap, const int32_t* __restrict
     st[2] = s_want[b] - fetched;   // wanted (before the cap) and not fetched
   }
   if (tid == 0) {
-    ctr[phase == ECH_EARLY ? ECH_CTR_NMISS_EARLY : ECH_CTR_NMISS] = n_alloc;
-    if (phase == ECH_EARLY) ctr[ECH_CTR_NCOPIED_EARLY] = 0;   // nothing of this list is copied yet
+    if (phase == ECH_EARLY) {
+      ctr[ECH_CTR_NMISS_EARLY] = n_alloc;
+      ctr[ECH_CTR_NCOPIED_EARLY] = 0;   // nothing of this list is copied yet
+    } else if (phase == ECH_FINAL) {
+      st_dev(&ctr[ECH_CTR_NMISS], n_alloc);   // read beside this launch once the list is complete
+    } else {
+      ctr[ECH_CTR_NMISS] = n_alloc;
+    }
     ctr[ECH_CTR_NWANT] = n_want;
     ctr[ECH_CTR_NPINNED] = hit_all;
     ctr[ECH_CTR_EPOCH] = ep;
+    int walk = 0;   // ring positions from the head to the last slot allocated
     if (n_alloc > 0) {
       const int last = (n_alloc == n_want) ? s_last : s_lastw;
       ctr[ECH_CTR_HEAD] = (last + 1 == w.C) ? 0 : last + 1;
+      walk = (last - head + w.C) % w.C + 1;
+    }
+    if (phase == ECH_EARLY) ctr[ECH_CTR_EARLY_WALK] = walk;
+    // The FINAL walk starts where the EARLY one ended; together longer than
+    // the ring, it reached slots the EARLY phase allocated.
+    if (phase == ECH_FINAL && walk > 0) {
+      const int we = ctr[ECH_CTR_EARLY_WALK];
+      if (we > 0 && (int64_t)we + walk > w.C) atomicOr(&ctr[ECH_CTR_FINAL_READY], 2);
     }
     if ((phase != ECH_EARLY && n_want > found) || clamped) ctr[ECH_CTR_STATUS] |= ECH_ST_OVERFLOW;
   }
 }
 
-__global__ __launch_bounds__(kT) void place_kernel(int phase, int nseq, int cap, int32_t* __restrict__ tok2slot,
-                                                   int32_t* __restrict__ slot2tok,
-                                                   const int32_t* __restrict__ slot_pin, int32_t* __restrict__ miss,
-                                                   int32_t* ctr, int32_t* __restrict__ sel_slot,
-                                                   int32_t* __restrict__ stats, CWs w) {
+__device__ __forceinline__ void place_block(int phase, int nseq, int cap, int32_t* __restrict__ tok2slot,
+                                            int32_t* __restrict__ slot2tok, const int32_t* __restrict__ slot_pin,
+                                            int32_t* __restrict__ miss, int32_t* ctr, int32_t* __restrict__ sel_slot,
+                                            int32_t* __restrict__ stats, CWs w) {
   // placing blocks: s_slot [kBlk ints] | s_fr [kWin bytes] | s_tot [kMaxB ints];
   // the bookkeeping block: 4 x [kMaxB ints] | s_fr [kWin bytes]
   __shared__ __align__(16) uint8_t smem[4 * kBlk + kWin + 4 * kMaxB];
@@ -530,14 +557,37 @@ __global__ __launch_bounds__(kT) void place_kernel(int phase, int nseq, int cap,
       }
       slot2tok[p] = g;
       tok2slot[g] = p;
-      miss[2 * m] = g;
-      miss[2 * m + 1] = p;
-      if (phase == ECH_FINAL) sel_slot[mc.y] = p;
+      if (phase == ECH_FINAL) {   // read beside this launch once the list is complete
+        st_dev(&miss[2 * m], g);
+        st_dev(&miss[2 * m + 1], p);
+        sel_slot[mc.y] = p;
+      } else {
+        miss[2 * m] = g;
+        miss[2 * m + 1] = p;
+      }
     } else if (phase == ECH_PREFILL) {
       tok2slot[g] = -1;     // release the claim of a miss that got no slot
     }
     ech::wave_count(&ctr[ECH_CTR_NEVICT], evicted);
     ech::wave_count(&stats[4 * owner + 3], evicted);
+  }
+}
+
+__global__ __launch_bounds__(kT) void place_kernel(int phase, int nseq, int cap, int32_t* __restrict__ tok2slot,
+                                                   int32_t* __restrict__ slot2tok,
+                                                   const int32_t* __restrict__ slot_pin, int32_t* __restrict__ miss,
+                                                   int32_t* ctr, int32_t* __restrict__ sel_slot,
+                                                   int32_t* __restrict__ stats, CWs w) {
+  place_block(phase, nseq, cap, tok2slot, slot2tok, slot_pin, miss, ctr, sel_slot, stats, w);
+  if (phase == ECH_FINAL) {
+    // The last workgroup to finish marks the list complete (bit 0) for a
+    // copier running beside this launch: every workgroup's coherent stores
+    // (entries, count, bit 1) have completed before it arrives.
+    wait_vm_zero();
+    __syncthreads();
+    if (threadIdx.x == 0 &&
+        atomicAdd(&ctr[ECH_CTR_FINAL_DONE], 1) == (int)(gridDim.x * gridDim.y) - 1)
+      atomicOr(&ctr[ECH_CTR_FINAL_READY], 1);
   }
 }
 
@@ -575,10 +625,10 @@ typedef uint32_t v4u __attribute__((ext_vector_type(4)));
 __global__ __launch_bounds__(kT) void recall_kernel(const v4u* __restrict__ host, int64_t P, int row16,
                                                     v4u* __restrict__ dev, int32_t C,
                                                     const int32_t* __restrict__ miss, int32_t* ctr, int cidx,
-                                                    int32_t M_max) {
+                                                    int ccopied, int32_t M_max) {
   const int n = min(ctr[cidx], M_max);
-  // EARLY: entries the fused scores + early-fetch launch already copied are skipped
-  const int n0 = (cidx == ECH_CTR_NMISS_EARLY) ? min(max(ctr[ECH_CTR_NCOPIED_EARLY], 0), n) : 0;
+  // EARLY, FINAL: entries the live copier already copied are skipped
+  const int n0 = (ccopied >= 0) ? min(max(ctr[ccopied], 0), n) : 0;
   const int64_t total = (int64_t)(n - n0) * row16;
   const int64_t stride = (int64_t)gridDim.x * kT * kRecallUnroll;
   for (int64_t base = (int64_t)blockIdx.x * kT * kRecallUnroll + threadIdx.x; base < total; base += stride) {
@@ -608,6 +658,55 @@ __global__ __launch_bounds__(kT) void recall_kernel(const v4u* __restrict__ host
     atomicAdd(&ctr[ECH_CTR_RECALLED], n - n0);
     if (cidx == ECH_CTR_NMISS_EARLY) ctr[ECH_CTR_LIVE] = 0;   // this step's early list is complete
   }
+}
+
+// The rows the live copier left of both lists of a step, in one launch,
+// after the FINAL phase: early entries from ctr[NCOPIED_EARLY] on whose slot
+// still holds their token (a slot the FINAL phase gave to another token
+// gets that token's row from the FINAL list instead, so no two rows of the
+// launch go to one slot), then FINAL entries from ctr[NCOPIED_FINAL] on.
+__global__ __launch_bounds__(kT) void recall_rest_kernel(const v4u* __restrict__ host, int64_t P, int row16,
+                                                         v4u* __restrict__ dev, int32_t C,
+                                                         const int32_t* __restrict__ miss_e, int32_t M_early,
+                                                         const int32_t* __restrict__ miss_f, int32_t M_max,
+                                                         const int32_t* __restrict__ slot2tok, int32_t* ctr) {
+  const int ne = min(ctr[ECH_CTR_NMISS_EARLY], M_early), nf = min(ctr[ECH_CTR_NMISS], M_max);
+  const int n0e = min(max(ctr[ECH_CTR_NCOPIED_EARLY], 0), ne), n0f = min(max(ctr[ECH_CTR_NCOPIED_FINAL], 0), nf);
+  const int re = ne - n0e;   // early rows, then FINAL rows
+  const int64_t total = (int64_t)(re + nf - n0f) * row16;
+  const int64_t stride = (int64_t)gridDim.x * kT * kRecallUnroll;
+  int copied = 0;
+  for (int64_t base = (int64_t)blockIdx.x * kT * kRecallUnroll + threadIdx.x; base < total; base += stride) {
+    v4u v[kRecallUnroll];
+    int64_t dst[kRecallUnroll];
+#pragma unroll
+    for (int u = 0; u < kRecallUnroll; ++u) {
+      const int64_t i = base + (int64_t)u * kT;
+      dst[u] = -1;
+      if (i < total) {
+        const int r = (int)(i / row16);
+        const int c = (int)(i % row16);
+        const bool early = r < re;
+        const int32_t* e = early ? miss_e + 2 * (n0e + r) : miss_f + 2 * (n0f + r - re);
+        const int g = e[0], p = e[1];
+        if (g >= 0 && g < P && p >= 0 && p < C) {
+          if (!early || slot2tok[p] == g) {
+            v[u] = __builtin_nontemporal_load(host + (int64_t)g * row16 + c);
+            dst[u] = (int64_t)p * row16 + c;
+            copied += (c == 0);
+          }
+        } else if (c == 0) {
+          set_status(ctr, ECH_ST_BADMISS);
+        }
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kRecallUnroll; ++u)
+      if (dst[u] >= 0) __builtin_nontemporal_store(v[u], dev + dst[u]);
+  }
+  copied = ech::wave_sum(copied);
+  if ((threadIdx.x & 63) == 0 && copied) atomicAdd(&ctr[ECH_CTR_RECALLED], copied);
+  if (blockIdx.x == 0 && threadIdx.x == 0) ctr[ECH_CTR_LIVE] = 0;   // this step's early list is complete
 }
 
 }  // namespace
@@ -713,7 +812,34 @@ extern "C" int ech_recall(int phase, const void* host_pool, int64_t P, int64_t r
                                                                                     (kT * kRecallUnroll)));
   hipLaunchKernelGGL(recall_kernel, dim3(blocks), dim3(kT), 0, s, static_cast<const v4u*>(dptr), P, row16,
                      static_cast<v4u*>(dev_cache), C, miss, ctr,
-                     phase == ECH_EARLY ? ECH_CTR_NMISS_EARLY : ECH_CTR_NMISS, M_max);
+                     phase == ECH_EARLY ? ECH_CTR_NMISS_EARLY : ECH_CTR_NMISS,
+                     phase == ECH_EARLY ? ECH_CTR_NCOPIED_EARLY : phase == ECH_FINAL ? ECH_CTR_NCOPIED_FINAL : -1,
+                     M_max);
+  ECH_LAUNCH_CHECK();
+  return ECH_OK;
+}
+
+extern "C" int ech_recall_rest(const void* host_pool, int64_t P, int64_t row_bytes, void* dev_cache, int32_t C,
+                               const int32_t* miss_early, int32_t M_early, const int32_t* miss, int32_t M_max,
+                               const int32_t* slot2tok, int32_t* ctr, void* stream) {
+  if (!host_pool || !dev_cache || !miss_early || !miss || !slot2tok || !ctr || P < 1 || C < 1 || M_early < 0 ||
+      M_max < 0)
+    return ECH_EINVAL;
+  if (row_bytes <= 0 || row_bytes % 16 != 0 || row_bytes / 16 > INT32_MAX) return ECH_EINVAL;
+  if ((reinterpret_cast<uintptr_t>(host_pool) & 15u) || (reinterpret_cast<uintptr_t>(dev_cache) & 15u))
+    return ECH_EINVAL;
+  void* dptr = nullptr;
+  if (hipHostGetDevicePointer(&dptr, const_cast<void*>(host_pool), 0) != hipSuccess || !dptr) {
+    (void)hipGetLastError();
+    return ECH_EINVAL;
+  }
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const int row16 = (int)(row_bytes / 16);
+  const int64_t work = ((int64_t)M_early + M_max) * row16;
+  const int blocks = (int)std::max<int64_t>(1, std::min<int64_t>(kRecallBlocks, (work + kT * kRecallUnroll - 1) /
+                                                                                    (kT * kRecallUnroll)));
+  hipLaunchKernelGGL(recall_rest_kernel, dim3(blocks), dim3(kT), 0, s, static_cast<const v4u*>(dptr), P, row16,
+                     static_cast<v4u*>(dev_cache), C, miss_early, M_early, miss, M_max, slot2tok, ctr);
   ECH_LAUNCH_CHECK();
   return ECH_OK;
 }

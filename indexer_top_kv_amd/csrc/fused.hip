@@ -100,6 +100,7 @@ struct Ctl {                             // control words at the start of the wo
   int pin_done;                          // pins kernel: window arrivals (all workgroups, all windows)
   int pin_total;                         // pins kernel: slots pinned so far
   int first_incomplete;                  // live copier: the first group it gave up on
+  int next_fgroup;                       // live copier: FINAL copy groups claimed
   u64 finished;                          // kFin | n_alloc
   u64 nfree;                             // kFin | free slots ranked (<= M_early)
 };
@@ -297,6 +298,9 @@ __global__ __launch_bounds__(kT) void fused_pins_kernel(const uint16_t* __restri
     cl->finished = 0;
     cl->nfree = 0;
     cl->first_incomplete = INT32_MAX;
+    cl->next_fgroup = 0;
+    ctr[ECH_CTR_FINAL_READY] = 0;   // the FINAL phase after this launch sets it again
+    ctr[ECH_CTR_EARLY_WALK] = 0;
     ctr[ECH_CTR_NEVICT] = 0;
     ctr[ECH_CTR_NWANT] = 0;
     ctr[ECH_CTR_NMISS_EARLY] = 0;
@@ -543,6 +547,7 @@ __device__ void alloc_sequence(const FusedArgs& a, int b, int nfree, int* s_list
                    &pv);
         const int last = pv - 1;
         a.ctr[ECH_CTR_HEAD] = (last + 1 == a.C) ? 0 : last + 1;
+        a.ctr[ECH_CTR_EARLY_WALK] = (last - a.ws.ctl->head + a.C) % a.C + 1;
       }
     }
   }
@@ -666,6 +671,18 @@ __global__ __launch_bounds__(kT) void fused_kernel(FusedArgs a) {
 // makes it give up: the copied groups form a prefix of the list
 // (ctr[ECH_CTR_NCOPIED_EARLY]) and ech_recall(ECH_EARLY) copies the rest, so
 // the result never depends on how the two launches are scheduled.
+//
+// Given the FINAL list, a workgroup that reached the end of the early list
+// then waits (same patience) for the FINAL phase of the step to complete its
+// list (ctr[ECH_CTR_FINAL_READY] bit 0, set by that phase's last placing
+// workgroup after every entry and ctr[ECH_CTR_NMISS] went out with coherent
+// stores) and copies it group by group; every claimed group is copied whole,
+// so the copied groups are again a prefix (ctr[ECH_CTR_NCOPIED_FINAL]). The
+// FINAL rows go to slots no early row is written to: the FINAL allocation
+// walks the ring on from where the early one stopped, and if it walked onto
+// the early one's slots (bit 1) no FINAL row is copied here. The PCIe link
+// thus stays busy from the first early row to the last FINAL one, with no
+// launch boundary and no cross-stream wait between the two lists.
 constexpr int kLive = 32;                     // copier workgroups (more slow the scoring beside them more than they gain)
 constexpr u64 kPatienceTicks = 100000ull;     // 1 ms at the 100 MHz constant-rate clock
 
@@ -677,13 +694,45 @@ struct LiveArgs {
   int32_t C;
   const int32_t* miss;
   int32_t M_early;
+  const int32_t* missf;                       // the FINAL list, or null
+  int32_t M_final;
   int32_t* ctr;
   Ctl* ctl;
 };
 
+// Copies the rows of the group's entries s_e[0..rg) (kNone: nothing), all
+// host loads in flight before the stores.
+__device__ __forceinline__ void copy_group(const LiveArgs& a, const u64* s_e, int rg) {
+  const int tid = threadIdx.x;
+  v4u v[kCopyUnroll];
+  int64_t dst[kCopyUnroll];
+#pragma unroll
+  for (int u = 0; u < kCopyUnroll; ++u) {
+    const int i = tid + u * kT;
+    dst[u] = -1;
+    if (i < rg * a.row16) {
+      const int row = i / a.row16, c = i - row * a.row16;
+      const u64 e = s_e[row];
+      if (e != kNone) {
+        const int g = (int)(uint32_t)e, p = (int)(uint32_t)(e >> 32);
+        if (g >= 0 && g < a.P && p >= 0 && p < a.C) {
+          v[u] = __builtin_nontemporal_load(a.host + (int64_t)g * a.row16 + c);
+          dst[u] = (int64_t)p * a.row16 + c;
+        } else if (c == 0) {
+          set_status(a.ctr, ECH_ST_BADMISS);
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < kCopyUnroll; ++u)
+    if (dst[u] >= 0) __builtin_nontemporal_store(v[u], a.dev + dst[u]);
+}
+
 __global__ __launch_bounds__(kT) void early_live_copy_kernel(LiveArgs a) {
   __shared__ u64 s_e[kT * kCopyUnroll];
   __shared__ int s_g, s_state;                // state: 0 copy group s_g, 1 end of list, 2 gave up
+  __shared__ int s_nf;
   const int tid = threadIdx.x;
   const int rg = max(1, (kT * kCopyUnroll) / a.row16);   // rows per group
   u64* fin = &a.ctl->finished;
@@ -756,43 +805,61 @@ __global__ __launch_bounds__(kT) void early_live_copy_kernel(LiveArgs a) {
         gave_up_at = s_g;
         break;
       }
-      v4u v[kCopyUnroll];
-      int64_t dst[kCopyUnroll];
-#pragma unroll
-      for (int u = 0; u < kCopyUnroll; ++u) {   // all host loads in flight, then the stores
-        const int i = tid + u * kT;
-        dst[u] = -1;
-        if (i < rg * a.row16) {
-          const int row = i / a.row16, c = i - row * a.row16;
-          const u64 e = s_e[row];
-          if (e != kNone) {
-            const int g = (int)(uint32_t)e, p = (int)(uint32_t)(e >> 32);
-            if (g >= 0 && g < a.P && p >= 0 && p < a.C) {
-              v[u] = __builtin_nontemporal_load(a.host + (int64_t)g * a.row16 + c);
-              dst[u] = (int64_t)p * a.row16 + c;
-            } else if (c == 0) {
-              set_status(a.ctr, ECH_ST_BADMISS);
-            }
-          }
-        }
-      }
-#pragma unroll
-      for (int u = 0; u < kCopyUnroll; ++u)
-        if (dst[u] >= 0) __builtin_nontemporal_store(v[u], a.dev + dst[u]);
+      copy_group(a, s_e, rg);
       __syncthreads();   // s_g, s_e, s_state are rewritten by the next group
+    }
+  }
+  // the FINAL rows, by the workgroups that reached the end of the early list
+  const bool final_rows = a.missf != nullptr && s_state == 1;
+  __syncthreads();   // every thread has read s_state
+  if (final_rows) {
+    if (tid == 0) {
+      const u64 t0 = wall_clock64();
+      int r;
+      for (;;) {
+        r = ld_dev(&a.ctr[ECH_CTR_FINAL_READY]);
+        if ((r & 1) || wall_clock64() - t0 > kPatienceTicks) break;
+        __builtin_amdgcn_s_sleep(16);
+      }
+      s_state = (r & 3) == 1 ? 0 : 2;
+      s_nf = min(max(ld_dev(&a.ctr[ECH_CTR_NMISS]), 0), a.M_final);
+    }
+    __syncthreads();
+    const u64* entf = reinterpret_cast<const u64*>(a.missf);
+    for (;;) {
+      if (tid == 0 && s_state == 0) {
+        const int g = atomicAdd(&a.ctl->next_fgroup, 1);
+        s_g = g;
+        if ((int64_t)g * rg >= s_nf) s_state = 1;
+      }
+      __syncthreads();
+      if (s_state != 0) break;
+      if (tid < rg) {
+        const int m = s_g * rg + tid;
+        s_e[tid] = m < s_nf ? ld_dev(entf + m) : kNone;
+      }
+      __syncthreads();
+      copy_group(a, s_e, rg);
+      __syncthreads();
     }
   }
   if (tid == 0) {
     if (gave_up_at >= 0) atomicMin(&a.ctl->first_incomplete, gave_up_at);
     const int prev = atomicAdd(&a.ctl->c_done, 1);
-    if (prev == kLive - 1) {   // the last copier workgroup: the copied prefix
+    if (prev == kLive - 1) {   // the last copier workgroup: the copied prefixes
       const u64 f = ld_dev(fin);
       int64_t groups = min(ld_dev(&a.ctl->next_group), ld_dev(&a.ctl->first_incomplete));
       int64_t ncopied = groups * rg;
       if (f & kFin) ncopied = min(ncopied, (int64_t)(f & 0xffffffffull));
       ncopied = min(ncopied, (int64_t)a.M_early);
       a.ctr[ECH_CTR_NCOPIED_EARLY] = (int)ncopied;
-      atomicAdd(&a.ctr[ECH_CTR_RECALLED], (int)ncopied);
+      int64_t nfin = 0;
+      const int fg = ld_dev(&a.ctl->next_fgroup);
+      if (fg > 0) {   // some workgroup saw the FINAL list complete: its length is final
+        nfin = min((int64_t)fg * rg, (int64_t)min(max(ld_dev(&a.ctr[ECH_CTR_NMISS]), 0), a.M_final));
+        a.ctr[ECH_CTR_NCOPIED_FINAL] = (int)nfin;
+      }
+      atomicAdd(&a.ctr[ECH_CTR_RECALLED], (int)(ncopied + nfin));
     }
   }
 }
@@ -864,10 +931,11 @@ extern "C" int ech_index_logits_early(const void* q, const float* w, const void*
 }
 
 extern "C" int ech_recall_early_live(const void* host_pool, int64_t P, int64_t row_bytes, void* dev_cache, int32_t C,
-                                     const int32_t* miss_early, int32_t M_early, int32_t* ctr, void* ws,
-                                     void* stream) {
+                                     const int32_t* miss_early, int32_t M_early, const int32_t* miss_final,
+                                     int32_t M_final, int32_t* ctr, void* ws, void* stream) {
   if (!host_pool || !dev_cache || !miss_early || !ctr || !ws || P < 1 || P >= INT32_MAX || C < 1 || M_early < 0)
     return ECH_EINVAL;
+  if (miss_final && (M_final < 0 || (reinterpret_cast<uintptr_t>(miss_final) & 7u))) return ECH_EINVAL;
   if (row_bytes < 16 || row_bytes % 16 != 0 || row_bytes > 16 * kT * kCopyUnroll) return ECH_EINVAL;
   if (!aligned16(dev_cache) || !aligned16(host_pool) || (reinterpret_cast<uintptr_t>(miss_early) & 7u) ||
       (reinterpret_cast<uintptr_t>(ws) & 255u))
@@ -886,6 +954,8 @@ extern "C" int ech_recall_early_live(const void* host_pool, int64_t P, int64_t r
   a.C = C;
   a.miss = miss_early;
   a.M_early = M_early;
+  a.missf = miss_final;
+  a.M_final = miss_final ? M_final : 0;
   a.ctr = ctr;
   a.ctl = reinterpret_cast<Ctl*>(ws);   // the control words lead the fused launch's workspace
   hipLaunchKernelGGL(early_live_copy_kernel, dim3(kLive), dim3(kT), 0, reinterpret_cast<hipStream_t>(stream), a);

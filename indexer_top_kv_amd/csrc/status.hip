@@ -13,4 +13,4 @@ extern "C" const char* ech_status_str(int code) {
   }
 }
 
-extern "C" int ech_version(void) { return 200; }   // 2.0: ech_index_logits_early replaces the grouped early fetch
+extern "C" int ech_version(void) { return 300; }   // 3.0: the live copier takes the FINAL list too

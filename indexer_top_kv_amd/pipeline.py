@@ -10,11 +10,11 @@ fetch of tokens scoring above the predicted threshold starts before it:
 With fp8 keys the scores and the early fetch are one launch
 (ech_index_logits_early): the early misses of a sequence get their slots, and
 their rows start crossing PCIe, while later sequences are still being scored;
-the rows not yet copied when the scoring ends are copied on S1 beside the
-top-k:
+a copier on S1 takes them as they appear and, once S0 has the FINAL maps,
+goes on to the FINAL rows with the link still busy:
 
-    S0: scores + EARLY maps + early rows (one launch) --> ech_topk --> FINAL maps --+--> FINAL recall
-         \-> S1: rest of the early rows (PCIe) ------------------------------------/
+    S0: scores + EARLY maps (one launch) --> ech_topk --> FINAL maps ........--> rest of both lists
+    S1: live copier: early rows as allocated, then the FINAL rows ------------/
 
 theta is double-buffered (the early fetch reads the prediction while the
 top-k writes its update). When the batch's
@@ -42,8 +42,8 @@ import torch
 
 from . import (ECH_EARLY, ECH_FINAL, ECH_PREFILL, LayerState, ech_cache_reset, ech_cache_step,
                ech_cache_step_ws_bytes, ech_index_logits, ech_index_logits_causal, ech_index_logits_early,
-               ech_index_logits_early_ws_bytes, ech_kv_append, ech_recall, ech_recall_early_live, ech_topk,
-               ech_topk_ws_bytes)
+               ech_index_logits_early_ws_bytes, ech_kv_append, ech_recall, ech_recall_early_live, ech_recall_rest,
+               ech_topk, ech_topk_ws_bytes)
 
 
 def round_up(x: int, m: int) -> int:
@@ -151,8 +151,6 @@ class DecodeLayer:
         self.ev_logits = torch.cuda.Event()
         self.ev_early_maps = torch.cuda.Event()
         self.ev_early = torch.cuda.Event()
-        self.ev_final_maps = torch.cuda.Event()
-        self.ev_final = torch.cuda.Event()
         ech_cache_reset(self.state)
 
     def reset(self) -> None:
@@ -200,7 +198,8 @@ class DecodeLayer:
             self.s1.wait_event(self.ev_fork)
             if mark is not None:
                 mark('recall_live', self.s1)
-            ech_recall_early_live(self.host_pool, self.dev_cache, self.state, self.ws_fused, stream=self.s1)
+            ech_recall_early_live(self.host_pool, self.dev_cache, self.state, self.ws_fused, stream=self.s1,
+                                  final=True)
             if mark is not None:
                 mark('recall_live', self.s1)
         else:
@@ -275,34 +274,25 @@ class DecodeLayer:
         self.parity ^= 1
 
     def _after_fused(self, th, th_next, s0, mark) -> None:
-        """First chunk after the fused launch: on S1, after the live copy,
-        the early rows it left (once the fused launch is done), then the
-        FINAL recall (it may reuse a slot they fill) once S0 has the FINAL
-        maps; the top-k and the FINAL maps on S0, which ends waiting for
-        S1. The FINAL rows follow the early ones on S1 with no hop back to
-        S0 in between."""
+        """First chunk after the fused launch: the top-k and the FINAL maps
+        on S0, while on S1 the live copier goes on from the early rows to the
+        FINAL ones as soon as S0 has completed the FINAL list. S0 then waits
+        for the copier and copies what it left of both lists in one launch
+        (ech_recall_rest)."""
         first_b0, first_b1 = self.chunks[0]
         mark('topk', s0)
         ech_topk(self.logits, self.lens, self.max_len, self.k, th, th_next, self.idx, self.kth, self.ws_topk,
                  stream=s0)
         mark('topk', s0)
-        self.s1.wait_event(self.ev_logits)
-        mark('early', self.s1)
-        mark('recall_early', self.s1)
-        self._recall(ECH_EARLY, self.s1)
-        mark('recall_early', self.s1)
-        mark('early', self.s1)
+        self.ev_early.record(self.s1)              # the copier is done
         mark('final', s0)
         mark('final_maps', s0)
         self._maps(ECH_FINAL, first_b0, first_b1, th, s0)
         mark('final_maps', s0)
-        self.ev_final_maps.record(s0)
-        self.s1.wait_event(self.ev_final_maps)
-        mark('recall_final', self.s1)
-        self._recall(ECH_FINAL, self.s1)
-        mark('recall_final', self.s1)
-        self.ev_final.record(self.s1)
-        s0.wait_event(self.ev_final)
+        s0.wait_event(self.ev_early)
+        mark('recall_final', s0)
+        ech_recall_rest(self.host_pool, self.dev_cache, self.state, stream=s0)
+        mark('recall_final', s0)
 
     def _after_scores(self, th, th_next, s0, mark) -> None:
         """First chunk after the plain scores: the EARLY maps and recall on

@@ -99,14 +99,26 @@ def check_index_logits_early_rejects_bad_args(lib):
     assert call(q=FAKE + 8) == -1
     assert call(miss=FAKE + 4) == -1
 
-    def live(pool=FAKE, rb=1152, miss=FAKE, wsp=FAKE, M=64):
-        return lib.ech_recall_early_live(pool, 4000, rb, FAKE, 500, miss, M, FAKE, wsp, None)
+    def live(pool=FAKE, rb=1152, miss=FAKE, wsp=FAKE, M=64, mf=None, Mf=0):
+        return lib.ech_recall_early_live(pool, 4000, rb, FAKE, 500, miss, M, mf, Mf, FAKE, wsp, None)
     assert live(pool=None) == -1
     assert live(rb=1150) == -1
     assert live(rb=65536) == -1
     assert live(miss=FAKE + 4) == -1
     assert live(wsp=FAKE + 64) == -1
     assert live(M=-1) == -1
+    assert live(mf=FAKE + 4) == -1       # FINAL list not 8-byte aligned
+    assert live(mf=FAKE, Mf=-1) == -1
+
+    def rest(pool=FAKE, rb=1152, me=FAKE, mf=FAKE, s2t=FAKE, Me=64, Mf=64):
+        return lib.ech_recall_rest(pool, 4000, rb, FAKE, 500, me, Me, mf, Mf, s2t, FAKE, None)
+    assert rest(pool=None) == -1
+    assert rest(rb=1150) == -1
+    assert rest(me=None) == -1
+    assert rest(mf=None) == -1
+    assert rest(s2t=None) == -1
+    assert rest(Me=-1) == -1
+    assert rest(pool=FAKE + 8) == -1
 
 
 def check_topk_noalloc_rejects_bad_args(lib):
@@ -121,6 +133,7 @@ def check_topk_noalloc_rejects_bad_args(lib):
     assert lib.ech_topk_ws_bytes(4096, 110000, 2048) > (16 << 20)
     assert call(R=4096, ml=110000, k=2048, ld=110016) == -5
     assert lib.ech_topk_ws_bytes(32, 131072, 2048) <= (16 << 20)
+
 
 
 CHECKS = [v for k, v in sorted(globals().items()) if k.startswith('check_')]

@@ -27,7 +27,7 @@ def test_header_declares_entry_points():
     for name in ['ech_index_logits', 'ech_index_logits_causal', 'ech_topk', 'ech_topk_ws_bytes',
                  'ech_cache_step', 'ech_cache_step_ws_bytes', 'ech_cache_reset', 'ech_recall',
                  'ech_index_logits_early', 'ech_index_logits_early_ws_bytes', 'ech_recall_early_live',
-                 'ech_topk_noalloc',
+                 'ech_recall_rest', 'ech_topk_noalloc',
                  'ech_status_str', 'ech_version']:
         assert name in syms
 
@@ -41,7 +41,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_status_strings_and_version():
     lib = ech.lib()
-    assert lib.ech_version() == 200
+    assert lib.ech_version() == 300
     assert lib.ech_status_str(0) == b'ok'
     for code in (-1, -2, -3, -4, -5):
         assert b'unknown' not in lib.ech_status_str(code)

@@ -7,8 +7,11 @@ thresholds fall between real scores). The copier is run in three schedules:
 on a second stream beside the scoring (the normal one), on the same stream
 before the fused launch (it finds no list, gives up after its patience and
 leaves every row to ech_recall(ECH_EARLY)), and on the same stream after it
-(the whole list is there). ECHO explainer, "Decode: fetch above a predicted
-threshold" and "One layer, one step: free -> allocate -> recall"."""
+(the whole list is there). In the decode step's own schedule the copier
+also takes the FINAL list (ech_cache_step(ECH_FINAL) on the first stream),
+unless the FINAL allocation walked onto the early phase's slots. ECHO
+explainer, "Decode: fetch above a predicted threshold" and "One layer, one
+step: free -> allocate -> recall"."""
 import numpy as np
 import pytest
 import torch
@@ -21,7 +24,15 @@ from gpu_util import TOL_FP8, dev, host, need_gpu, rel_err
 pytestmark = pytest.mark.gpu
 
 
-def _run(wl, schedule, steps=4, e=None):
+def _walk(h0, h1, n, C):
+    """Ring positions a phase walked from head h0 to its last allocated slot,
+    h1 - 1 (0 if it allocated nothing; C if it went all the way round)."""
+    if n == 0:
+        return 0
+    return (h1 - h0) % C or C
+
+
+def _run(wl, schedule, steps=4, e=None, final_live=False):
     keys, scale = wk.keys(wl)
     w = wk.head_weights(wl)
     rows = wk.host_rows(wl)
@@ -45,7 +56,7 @@ def _run(wl, schedule, steps=4, e=None):
     sm = oracle.SlotMap(wl.P, C)
     ref_cache = np.zeros((C, 576), np.int16)
     s1 = torch.cuda.Stream()
-    copied_live = 0
+    copied_live = copied_final = reached = 0
     for s, q in enumerate(wk.decode_queries(wl, steps)):
         qd = dev(q)
         logits = torch.zeros((B, ld), dtype=torch.float32, device='cuda')
@@ -53,7 +64,43 @@ def _run(wl, schedule, steps=4, e=None):
         s0 = torch.cuda.current_stream()
         fused = lambda: ech.ech_index_logits_early(qd, wd, kd, sd, t0d, lnd, max_len, logits, e0, e1, theta, cap, st,
                                                    stats, ws, stream=s0)
-        if schedule == 'beside':
+        idx = torch.empty((B, k), dtype=torch.int32, device='cuda')
+        kth = torch.empty(B, dtype=torch.float32, device='cuda')
+        th_next = torch.empty(B, dtype=torch.float32, device='cuda')
+        sel = torch.empty((B, k), dtype=torch.int32, device='cuda')
+        st_f = torch.empty((B, 4), dtype=torch.int32, device='cuda')
+
+        def topk_and_final(stream):
+            ech.ech_topk(logits, lnd, max_len, k, theta, th_next, idx, kth, ws_t, stream=stream)
+            ech.ech_cache_step(ech.ECH_FINAL, st, t0d, lnd, max_len, idx=idx, k=k, sel_slot=sel, stats=st_f,
+                               ws=ws_f, stream=stream)
+
+        head0 = sm.head
+        if final_live and schedule == 'beside':
+            # the decode step's schedule: the copier takes the FINAL rows too,
+            # then one launch copies what it left of both lists
+            ev = torch.cuda.Event()
+            ev.record(s0)
+            fused()
+            s1.wait_event(ev)
+            ech.ech_recall_early_live(pool, cache, st, ws, stream=s1, final=True)
+            copier_done = torch.cuda.Event()
+            copier_done.record(s1)
+            topk_and_final(s0)
+            s0.wait_event(copier_done)
+            ech.ech_recall_rest(pool, cache, st, stream=s0)
+            torch.cuda.synchronize()
+        elif final_live:
+            # the copier finds no list and gives up: every row of both lists,
+            # but no early row whose slot the FINAL phase gave away, comes
+            # from ech_recall_rest
+            assert schedule == 'copier_first'
+            ech.ech_recall_early_live(pool, cache, st, ws, stream=s0, final=True)
+            fused()
+            topk_and_final(s0)
+            ech.ech_recall_rest(pool, cache, st, stream=s0)
+            torch.cuda.synchronize()
+        elif schedule == 'beside':
             ev = torch.cuda.Event()
             ev.record(s0)
             fused()
@@ -91,38 +138,55 @@ def _run(wl, schedule, steps=4, e=None):
         n = int(ctr[ech.CTR_NMISS_EARLY])
         assert [tuple(x) for x in host(st.miss_early)[:n].tolist()] == a_o, f'step {s}'
         np.testing.assert_array_equal(host(stats)[e0:e1], st_o, err_msg=f'step {s}')
-        np.testing.assert_array_equal(host(st.tok2slot), sm.tok2slot, err_msg=f'step {s}')
-        np.testing.assert_array_equal(host(st.slot2tok), sm.slot2tok, err_msg=f'step {s}')
-        assert ctr[ech.CTR_HEAD] == sm.head
-        oracle.recall_rows(rows.view(np.int16), ref_cache, a_o)
-        np.testing.assert_array_equal(host(cache), ref_cache, err_msg=f'step {s}')
-        # the top-k and FINAL phase advance the state as a decode step does
-        idx = torch.empty((B, k), dtype=torch.int32, device='cuda')
-        kth = torch.empty(B, dtype=torch.float32, device='cuda')
-        th_next = torch.empty(B, dtype=torch.float32, device='cuda')
-        ech.ech_topk(logits, lnd, max_len, k, theta, th_next, idx, kth, ws_t)
-        sel = torch.empty((B, k), dtype=torch.int32, device='cuda')
-        st_f = torch.empty((B, 4), dtype=torch.int32, device='cuda')
-        ech.ech_cache_step(ech.ECH_FINAL, st, t0d, lnd, max_len, idx=idx, k=k, sel_slot=sel, stats=st_f, ws=ws_f)
-        ech.ech_recall(pool, cache, st, phase=ech.ECH_FINAL)
-        torch.cuda.synchronize()
+        head1 = sm.head
+        if not final_live:
+            np.testing.assert_array_equal(host(st.tok2slot), sm.tok2slot, err_msg=f'step {s}')
+            np.testing.assert_array_equal(host(st.slot2tok), sm.slot2tok, err_msg=f'step {s}')
+            assert ctr[ech.CTR_HEAD] == sm.head
+            oracle.recall_rows(rows.view(np.int16), ref_cache, a_o)
+            np.testing.assert_array_equal(host(cache), ref_cache, err_msg=f'step {s}')
+            # the top-k and FINAL phase advance the state as a decode step does
+            topk_and_final(s0)
+            ech.ech_recall(pool, cache, st, phase=ech.ECH_FINAL)
+            torch.cuda.synchronize()
+        else:
+            oracle.recall_rows(rows.view(np.int16), ref_cache, a_o)
+        ctr = host(st.ctr)
+        assert ctr[ech.CTR_STATUS] == 0, ctr[ech.CTR_STATUS]
         idx_o, kth_o = oracle.topk_rows(rows_l, k)
         np.testing.assert_array_equal(host(idx), idx_o)
         a_f, sel_o, stf_o = sm.final(wl.tok0, idx_o)
         oracle.recall_rows(rows.view(np.int16), ref_cache, a_f)
+        n_f = int(ctr[ech.CTR_NMISS])
+        assert [tuple(x) for x in host(st.miss)[:n_f].tolist()] == a_f, f'step {s}'
         np.testing.assert_array_equal(host(sel), sel_o)
-        np.testing.assert_array_equal(host(cache), ref_cache)
+        np.testing.assert_array_equal(host(st.tok2slot), sm.tok2slot, err_msg=f'step {s}')
+        np.testing.assert_array_equal(host(st.slot2tok), sm.slot2tok, err_msg=f'step {s}')
+        assert ctr[ech.CTR_HEAD] == sm.head
+        np.testing.assert_array_equal(host(cache), ref_cache, err_msg=f'step {s}')
+        # the FINAL phase's flags: its list complete, and whether its ring walk
+        # (from where the early one ended) reached the early phase's slots
+        w_e = _walk(head0, head1, n, C)
+        w_f = _walk(head1, sm.head, n_f, C)
+        assert ctr[ech.CTR_EARLY_WALK] == w_e
+        reach = w_e > 0 and w_f > 0 and w_e + w_f > C
+        assert ctr[ech.CTR_FINAL_READY] == (3 if reach else 1), (ctr[ech.CTR_FINAL_READY], w_e, w_f)
+        if reach:
+            assert ctr[ech.CTR_NCOPIED_FINAL] == 0
+            reached += 1
+        copied_final += int(ctr[ech.CTR_NCOPIED_FINAL])
         theta.copy_(th_next)
         np.testing.assert_array_equal(host(theta), oracle.theta_rows(th, kth_o))
     np.testing.assert_array_equal(pool.numpy(), rows.view(np.int16))   # no write-back
-    return copied_live
+    return copied_live, copied_final, reached
 
 
 @pytest.mark.parametrize('schedule', ['beside', 'copier_first', 'copier_after'])
 def test_fused_early_fetch_schedules(schedule):
     need_gpu()
     wl = wk.CONFIGS['decode-32x128k-fp8'].scaled(B=6, N=20000, C=30000, k=1024, cap=300, variant='normal')
-    copied = _run(wl, schedule)
+    copied, copied_final, _ = _run(wl, schedule)
+    assert copied_final == 0          # the copier was not given the FINAL list
     if schedule == 'copier_first':
         assert copied == 0            # it gave up: ech_recall(ECH_EARLY) copied every row
     if schedule == 'copier_after':
@@ -145,3 +209,40 @@ def test_fused_early_fetch_ring_of_several_pin_windows():
     need_gpu()
     wl = wk.CONFIGS['decode-32x128k-fp8'].scaled(B=8, N=40000, C=70000, k=4096, cap=2000, variant='normal')
     _run(wl, 'beside', steps=5)
+
+
+def test_fused_copier_takes_the_final_rows():
+    """The decode step's schedule: the copier goes on from the early rows to
+    the FINAL ones once the FINAL phase on the other stream has completed its
+    list; the maps, both lists and the cache match the oracle, and the
+    FINAL rows were copied by the copier."""
+    need_gpu()
+    wl = wk.CONFIGS['decode-32x128k-fp8'].scaled(B=6, N=20000, C=30000, k=1024, cap=300, variant='normal')
+    copied, copied_final, reached = _run(wl, 'beside', final_live=True)
+    assert copied > 0 and copied_final > 0 and reached == 0
+
+
+def test_fused_copier_final_rows_small_ring():
+    """A ring barely larger than the FINAL demand (4 x 1024 of 4200 slots),
+    so that in the second step the FINAL allocation walks round onto the
+    slots the early phase filled: then the copier leaves every FINAL row to
+    ech_recall(ECH_FINAL) (the flag checked against the oracle's ring walks
+    in every step)."""
+    need_gpu()
+    wl = wk.CONFIGS['decode-64x110k-fp8-capacity'].scaled(B=4, N=6000, len_lo=2500, C=4200, k=1024, cap=800,
+                                                          resample_p=0.5, variant='normal')
+    _, _, reached = _run(wl, 'beside', steps=5, final_live=True)
+    assert reached >= 1
+
+
+def test_recall_rest_after_a_copier_that_gave_up_small_ring():
+    """The copier gives up (it runs before the fused launch), so
+    ech_recall_rest copies both whole lists in one launch; in the step whose
+    FINAL allocation reaches the early slots, the early rows of the slots the
+    FINAL phase gave away are skipped, so each slot ends with its own
+    token's row (checked against the oracle's cache)."""
+    need_gpu()
+    wl = wk.CONFIGS['decode-64x110k-fp8-capacity'].scaled(B=4, N=6000, len_lo=2500, C=4200, k=1024, cap=800,
+                                                          resample_p=0.5, variant='normal')
+    copied, copied_final, reached = _run(wl, 'copier_first', steps=3, final_live=True)
+    assert copied == 0 and copied_final == 0 and reached >= 1
