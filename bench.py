@@ -161,14 +161,23 @@ def bench_decode(args, wl):
 
     # The top-k alone: K calls back to back on the last step's scores with its
     # prediction, into scratch outputs (the layer's state is left as it is).
-    th_a = layer.theta[layer.parity].clone()
+    # With the fused path the step's top-k selects from the band lists the
+    # last scores launch wrote with the theta it took (theta[1 - parity] once
+    # the step is over).
+    import indexer_top_kv_amd as ech_m
+    th_a = layer.theta[1 - layer.parity if layer.fused else layer.parity].clone()
     th_b, idx_b = torch.empty_like(th_a), torch.empty_like(layer.idx)
     kth_b, ws_b = torch.empty_like(layer.kth), torch.zeros_like(layer.ws_topk)
-    ech_topk_fn = __import__('indexer_top_kv_amd').ech_topk
-    ech_topk_fn(layer.logits, layer.lens, layer.max_len, layer.k, th_a, th_b, idx_b, kth_b, ws_b, stream=s0)
+    if layer.fused:
+        topk_call = lambda: ech_m.ech_topk_early(layer.logits, layer.lens, layer.max_len, layer.k, th_a, th_b, idx_b,
+                                                 kth_b, layer.state, layer.ws_fused, stream=s0)
+    else:
+        topk_call = lambda: ech_m.ech_topk(layer.logits, layer.lens, layer.max_len, layer.k, th_a, th_b, idx_b,
+                                           kth_b, ws_b, stream=s0)
+    topk_call()
     ev0.record(s0)
     for s in range(args.steps):
-        ech_topk_fn(layer.logits, layer.lens, layer.max_len, layer.k, th_a, th_b, idx_b, kth_b, ws_b, stream=s0)
+        topk_call()
     ev1.record(s0)
     torch.cuda.synchronize()
     topk_alone_us = ev0.elapsed_time(ev1) / args.steps * 1e3
@@ -328,8 +337,15 @@ def bench_decode(args, wl):
     topk_bytes = tokens * 4 + wl.B * wl.k * 4
     rec_us = st['recall_live'] + st['recall_early'] + st['recall_final']
     one_pass = wl.B <= 256 and layer.max_len > 16384
+    if layer.fused:
+        topk_stage = {'kernel': 'ech_topk_early (topk_lists_kernel: the selection from the band lists the scores '
+                                'launch wrote as it scored)',
+                      'bound': 'latency', 'us': st['topk'], 'alone_us': topk_alone_us,
+                      'note': 'one workgroup per row reads its band lists (a few thousand entries) and writes its k '
+                              'indices; the scores are not read again (rows the lists cannot decide take one pass '
+                              'over the row). us: in eager steps, alone_us: K calls back to back'}
     out['stage_rooflines'] = {
-        'topk': {'bound': 'hbm', 'algorithmic_bytes': topk_bytes, 'us': st['topk'],
+        'topk': topk_stage if layer.fused else {'bound': 'hbm', 'algorithmic_bytes': topk_bytes, 'us': st['topk'],
                  'achieved_GBs': topk_bytes / (st['topk'] * 1e-6) / 1e9 if st['topk'] else None,
                  'peak_GBs': PEAK_HBM_GBS,
                  'frac': topk_bytes / (st['topk'] * 1e-6) / 1e9 / PEAK_HBM_GBS if st['topk'] else None,

@@ -104,7 +104,7 @@ const char* ech_status_str(int code);
 
 /* Library ABI version (major*100 + minor); 200: the grouped early-fetch calls gave way to
    ech_index_logits_early; ech_topk_noalloc. 300: ech_recall_early_live also takes the FINAL list;
-   ech_recall_rest. */
+   ech_recall_rest; ech_topk_early. */
 int ech_version(void);
 
 /*
@@ -318,6 +318,30 @@ int ech_index_logits_early(const void* q, const float* w, const void* kcache, in
                            int32_t* tok2slot, int64_t P, int32_t* slot2tok, int32_t* slot_pin, int32_t C,
                            int32_t* miss_early, int32_t M_early, int32_t* ctr, int32_t* stats, void* ws,
                            size_t ws_bytes, void* stream);
+
+/*
+ * ech_topk_early - ech_topk for the rows of the last ech_index_logits_early
+ * call on ws (ECHO explainer, "Fused indexer kernel (extends DeepGEMM)" and
+ * "Prefill: one-round histogram": the scores kernel also emits what the
+ * selection needs). Each scoring wave of that launch listed, as it scored,
+ * its tokens in the band its row's theta implies (the bins from the bin of
+ * theta - |theta|/8 up); this selects from those lists, one workgroup per
+ * row, without reading the scores again, and takes the whole row where the
+ * lists cannot decide (NaN theta, a wave whose band did not fit its 64
+ * entries, or a band holding fewer than k tokens). Results exactly those of
+ * ech_topk(logits, ld, row_len, R, max_len, k, theta_in, ...).
+ *  logits, ld, row_len, R, max_len: those of the ech_index_logits_early call
+ *            (its output scores, unchanged since).
+ *  theta_in  [R]: the theta that call took (not NULL; a row whose theta_in
+ *            differs from it bit for bit is selected from the whole row:
+ *            slower, same result); theta_out, idx, kth, k (<= 4096) as
+ *            ech_topk.
+ *  ws, ws_bytes, C, M_early: that call's workspace and sizes; read only.
+ *  max_len at most 1048576.
+ */
+int ech_topk_early(const float* logits, int64_t ld, const int32_t* row_len, int R, int max_len, int k,
+                   const float* theta_in, float* theta_out, int32_t* idx, float* kth, const void* ws,
+                   size_t ws_bytes, int32_t C, int32_t M_early, void* stream);
 
 /*
  * ech_recall_early_live - copy the early rows while ech_index_logits_early

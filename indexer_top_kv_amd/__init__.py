@@ -23,7 +23,7 @@ from ._native import (ECH_EARLY, ECH_FINAL, ECH_PREFILL, ECH_KEY_BF16, ECH_KEY_F
 
 __all__ = ['ech_kv_append', 'ech_sparse_attn', 'ech_sparse_attn_ws_bytes', 'ech_index_logits', 'ech_index_logits_causal', 'ech_topk', 'ech_topk_noalloc', 'ech_topk_ws_bytes', 'ech_cache_reset',
            'ech_cache_step', 'ech_cache_step_ws_bytes', 'ech_recall', 'ech_index_logits_early',
-           'ech_index_logits_early_ws_bytes', 'ech_recall_early_live', 'ech_recall_rest', 'EchError', 'LayerState',
+           'ech_index_logits_early_ws_bytes', 'ech_recall_early_live', 'ech_recall_rest', 'ech_topk_early', 'EchError', 'LayerState',
            'lib']
 
 
@@ -211,6 +211,17 @@ def ech_recall_early_live(host_pool, dev_cache, state: 'LayerState', ws, stream=
         _ptr(host_pool), host_pool.shape[0], row_bytes, _ptr(dev_cache), dev_cache.shape[0], _ptr(state.miss_early),
         state.miss_early.shape[0], _ptr(state.miss) if final else None, state.miss.shape[0] if final else 0,
         _ptr(state.ctr), _ptr(ws), _stream(stream)))
+
+
+def ech_topk_early(logits, row_len, max_len: int, k: int, theta_in, theta_out, idx, kth, state: 'LayerState', ws,
+                   stream=None) -> None:
+    """ech_topk for the rows of the last ech_index_logits_early call on ws,
+    from the band lists its scoring waves wrote (theta_in: that call's)."""
+    R = logits.shape[0]
+    _check('ech_topk_early', lib().ech_topk_early(
+        _ptr(logits), logits.stride(0), _ptr(row_len), R, int(max_len), int(k), _ptr(theta_in), _ptr(theta_out),
+        _ptr(idx), _ptr(kth), _ptr(ws), ws.numel() * ws.element_size(), state.C, state.miss_early.shape[0],
+        _stream(stream)))
 
 
 def ech_recall_rest(host_pool, dev_cache, state: 'LayerState', stream=None) -> None:

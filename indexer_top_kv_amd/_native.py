@@ -65,6 +65,8 @@ SIGNATURES = {
                                               ctypes.c_int, _p, _i64, _p, _p, _i32, _p, _i32, _p, _p, _p, _sz, _p]),
     'ech_recall_early_live': (ctypes.c_int, [_p, _i64, _i64, _p, _i32, _p, _i32, _p, _i32, _p, _p, _p]),
     'ech_recall_rest': (ctypes.c_int, [_p, _i64, _i64, _p, _i32, _p, _i32, _p, _i32, _p, _p, _p]),
+    'ech_topk_early': (ctypes.c_int, [_p, _i64, _p, ctypes.c_int, ctypes.c_int, ctypes.c_int, _p, _p, _p, _p, _p, _sz,
+                                      _i32, _i32, _p]),
     'ech_kv_append': (ctypes.c_int, [_p, _i64, _i64, _p, ctypes.c_int, _p, _p, _p, _p, _p, ctypes.c_int, _p, _p, _p,
                                      _p, _p]),
     'ech_sparse_attn_ws_bytes': (_sz, [ctypes.c_int, ctypes.c_int, ctypes.c_int]),

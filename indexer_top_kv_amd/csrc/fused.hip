@@ -64,7 +64,9 @@
 
 #include <algorithm>
 
+#include "bins.hpp"
 #include "decode.hpp"
+#include "lists.hpp"
 
 namespace {
 
@@ -74,6 +76,7 @@ constexpr int kNS = 4;                   // ring slots per scoring wave
 constexpr int kWavesF = 4;               // waves per scoring workgroup
 constexpr int kWaveTok = kTPW * 16;      // 256 tokens per scoring wave
 constexpr int kWords = kWaveTok / 32;    // mask words per wave
+constexpr int kListSlice = 64;           // band entries a scoring wave lists for the top-k, at most
 constexpr int kMaxCap = 4096;
 constexpr int kMaxB = 1024;
 constexpr int kMaxAlloc = 64;            // alloc workgroups at most
@@ -111,6 +114,9 @@ struct FWs {
   u64* rlb;                              // [ceil(C / kRankSlice)] look-back word per ring slice
   int* freelist;                         // [M_early] slot + 1 of the free slot of each rank (0: not yet)
   u64* masks;                            // [R * wpr * kWords] published miss masks
+  int2* lmeta;                           // [R * wpr] per scoring wave: (band tokens listed, floor bin)
+  int2* lpool;                           // [R * wpr * kListSlice] listed (score bits, token), per wave
+  float* lth;                            // [R] the theta each row's band was listed against
   int wpr;
 };
 
@@ -127,13 +133,17 @@ size_t fused_layout(int R, int max_len, int32_t C, int32_t M_early, FWs* w, char
   const size_t o_ctl = take(sizeof(Ctl)), o_lb = take(8 * (size_t)R),
                o_rlb = take(8 * (size_t)((std::max(C, 1) + kRankSlice - 1) / kRankSlice)),
                o_fl = take(4 * (size_t)std::max(M_early, 1)),
-               o_m = take(8 * (size_t)R * wpr * kWords);
+               o_m = take(8 * (size_t)R * wpr * kWords), o_lm = take(8 * (size_t)R * wpr),
+               o_lp = take(8 * (size_t)R * wpr * kListSlice), o_lt = take(4 * (size_t)R);
   if (w && base) {
     w->ctl = reinterpret_cast<Ctl*>(base + o_ctl);
     w->lb = reinterpret_cast<u64*>(base + o_lb);
     w->rlb = reinterpret_cast<u64*>(base + o_rlb);
     w->freelist = reinterpret_cast<int*>(base + o_fl);
     w->masks = reinterpret_cast<u64*>(base + o_m);
+    w->lmeta = reinterpret_cast<int2*>(base + o_lm);
+    w->lpool = reinterpret_cast<int2*>(base + o_lp);
+    w->lth = reinterpret_cast<float*>(base + o_lt);
     w->wpr = wpr;
   }
   return o;
@@ -600,6 +610,45 @@ __device__ void alloc_role(const FusedArgs& a, int j, uint8_t* smem) {
   for (int b = a.e0 + j; b < a.e1; b += a.n_alloc_wg) alloc_sequence(a, b, nfree, s_list, scr, &s_min);
 }
 
+// For the top-k (ech_topk_early): the wave's tokens in the row's band, the
+// bins at and above the floor theta implies (the one-pass top-k's band), in
+// token order into the wave's slice, and the wave's (count, floor). A NaN
+// theta, or more band tokens than the slice holds, leaves (0, 256): no bin
+// is known to be complete there, and the selection takes the whole row.
+__device__ __forceinline__ void list_band(const FusedArgs& a, int r, int wi, int wt0, int len,
+                                          const float (&keep)[kTPW / 4]) {
+  const Shift shf = make_shift(a.theta[r]);
+  const uint32_t blo = band_lo(shf);
+  const int lane = threadIdx.x & 63;
+  u64 bal[kTPW / 4];
+  int cnt = 0;
+#pragma unroll
+  for (int j = 0; j < kTPW / 4; ++j) {
+    const int t = wt0 + 64 * j + lane;
+    bal[j] = __ballot(t < len && shifted_bin_one(keep[j], shf) >= blo);
+    cnt += __popcll(bal[j]);
+  }
+  const bool ok = shf.on && cnt <= kListSlice;
+  const size_t wslot = (size_t)r * a.ws.wpr + wi;
+  if (ok) {
+    int2* lp = a.ws.lpool + wslot * kListSlice;
+    int base = 0;
+#pragma unroll
+    for (int j = 0; j < kTPW / 4; ++j) {
+      if ((bal[j] >> lane) & 1ull) {
+        const int pos = base + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(bal[j] >> 32),
+                                                              __builtin_amdgcn_mbcnt_lo((uint32_t)bal[j], 0u));
+        lp[pos] = make_int2(__float_as_int(keep[j]), wt0 + 64 * j + lane);
+      }
+      base += __popcll(bal[j]);
+    }
+  }
+  if (lane == 0) {
+    a.ws.lmeta[wslot] = ok ? make_int2(cnt, (int)blo) : make_int2(0, 256);
+    if (wi == 0) a.ws.lth[r] = shf.th;
+  }
+}
+
 __device__ void score_role(const FusedArgs& a, int fb, uint8_t* smem) {
   const int r = fb / a.gx, bx = fb - r * a.gx;
   const int len = a.lens[r];
@@ -613,6 +662,7 @@ __device__ void score_role(const FusedArgs& a, int fb, uint8_t* smem) {
   const int64_t g0 = a.tok0[r];
   fp8_wave_scores<kTPW, kNS>(a.q, a.w, a.kc, a.ksc, r, g0, len, wt0, ring, sring, keep);
   fp8_wave_store<kTPW>(keep, &ring[0][0], a.out + (size_t)r * a.ld + wt0, min(kWaveTok, len - wt0));
+  list_band(a, r, wi, wt0, len, keep);
   if (r < a.e0 || r >= a.e1) return;
   const float th = a.theta[r];
   if (th != th) return;
@@ -928,6 +978,21 @@ extern "C" int ech_index_logits_early(const void* q, const float* w, const void*
   hipLaunchKernelGGL(fused_kernel, dim3((unsigned)blocks), dim3(kT), 0, s, a);
   ECH_LAUNCH_CHECK();
   return ECH_OK;
+}
+
+extern "C" int ech_topk_early(const float* logits, int64_t ld, const int32_t* row_len, int R, int max_len, int k,
+                              const float* theta_in, float* theta_out, int32_t* idx, float* kth, const void* ws,
+                              size_t ws_bytes, int32_t C, int32_t M_early, void* stream) {
+  if (!logits || !row_len || !idx || !kth || !ws || !theta_in) return ECH_EINVAL;
+  if (R < 1 || R > kMaxB || k < 1 || k > ech::kListMaxK || max_len < 0 || ld < max_len || C < 1 || M_early < 0)
+    return ECH_EINVAL;
+  if (ld % 4 != 0 || !aligned16(logits) || (reinterpret_cast<uintptr_t>(ws) & 255u)) return ECH_EINVAL;
+  if ((max_len + kWaveTok - 1) / kWaveTok > ech::kListMaxChunks) return ECH_EINVAL;
+  if (ws_bytes < ech_index_logits_early_ws_bytes(R, max_len, C, M_early)) return ECH_EINVAL;
+  FWs fw;
+  fused_layout(R, max_len, C, M_early, &fw, static_cast<char*>(const_cast<void*>(ws)));
+  return ech::topk_lists_launch(logits, ld, row_len, R, max_len, k, theta_in, theta_out, idx, kth, fw.lmeta, fw.lpool,
+                                fw.lth, fw.wpr, kListSlice, kWaveTok, reinterpret_cast<hipStream_t>(stream));
 }
 
 extern "C" int ech_recall_early_live(const void* host_pool, int64_t P, int64_t row_bytes, void* dev_cache, int32_t C,

@@ -43,7 +43,8 @@
 #include <algorithm>
 #include <mutex>
 
-#include "common.hpp"
+#include "bins.hpp"
+#include "lists.hpp"
 
 namespace {
 
@@ -114,25 +115,6 @@ size_t layout(int R, int max_len, int k, Ws* w, char* base) {
     w->nch = nch;
   }
   return o;
-}
-
-// Binning of a score relative to the prediction theta. Scores more than
-// |theta|/4 below theta all share bin 0: only the bins around and above the
-// boundary are needed, and lumping the bulk lets the histogram skip the
-// per-bin work for most tokens. Bin 0 is below every real bin, so the binning
-// stays monotone in s. A NaN theta means no shift and no lumping.
-struct Shift {
-  float th, cut;
-  bool on;
-};
-
-__device__ __forceinline__ Shift make_shift(float th) {
-  Shift sh;
-  sh.on = th == th;
-  sh.th = th;
-  const float a = fabsf(th);
-  sh.cut = (sh.on && a > 0.f && a < __builtin_inff()) ? -0.25f * a : -__builtin_inff();
-  return sh;
 }
 
 // The 256 bins are the high byte of the order key of fp16(d): sign, 5
@@ -1097,7 +1079,6 @@ constexpr int kOneChunk = kSmallNT * kSmallPer;                  // 16384 tokens
 constexpr int kOneMaxChunks = kMaxChunks * kChunk / kOneChunk;   // 256 (4M tokens)
 constexpr int kOneMaxRows = 256;
 constexpr int kPool = 32768;         // listed entries per row, at most
-constexpr float kBandFrac = 0.125f;  // band: scores down to about theta - |theta|/8
 
 struct OneWs {
   int* ctl;      // [R] * 32: per row, one 128-byte line: [0] chunks done
@@ -1132,32 +1113,6 @@ size_t one_layout(int R, int max_len, OneWs* w, char* base) {
     w->npool = one_pool(nch);
   }
   return o;
-}
-
-// Bins of the one-pass path: the high byte of the order key of fp16(d), the
-// same four bins per binade as bin16, computed with fewer instructions: d + 0
-// folds -0 onto +0 (equal scores share a bin), and the key's high byte is
-// the fp16 high byte with the sign bit flipped (positive d) or all bits
-// flipped (negative d). A negative d that rounds to fp16 -0 takes bin 0x7f,
-// just below +0: still monotone in d.
-__device__ __forceinline__ uint32_t bin_one(float d) {
-  const _Float16 h = (_Float16)(d + 0.0f);
-  const uint32_t u = __builtin_bit_cast(uint16_t, h);
-  const uint32_t neg = (uint32_t)((int32_t)(u << 16) >> 31);   // ~0 for a negative d
-  return (u >> 8) ^ 0x80u ^ (neg & 0x7fu);
-}
-
-__device__ __forceinline__ uint32_t shifted_bin_one(float x, const Shift& sh) {
-  const float d = sh.on ? x - sh.th : x;
-  return d < sh.cut ? 0u : bin_one(d);
-}
-
-// Floor the prediction implies: the bin of d = -|theta|/8 (above the lumping
-// cut at -|theta|/4); 0 (no constraint) without a finite nonzero theta.
-__device__ __forceinline__ uint32_t band_lo(const Shift& sh) {
-  const float a = fabsf(sh.th);
-  if (!sh.on || !(a > 0.f) || !(a < __builtin_inff())) return 0u;
-  return bin_one(-kBandFrac * a);
 }
 
 // Wait until this wave's global stores and atomics have completed.
@@ -1268,157 +1223,54 @@ __device__ void row_compact(const float* __restrict__ row, int len, float sstar,
   }
 }
 
-__global__ __launch_bounds__(kSmallNT) void topk_one_kernel(const float* __restrict__ logits, int64_t ld,
-                                                            const int32_t* __restrict__ lens, int max_len, int k,
-                                                            const float* theta_in, float* theta_out,
-                                                            float* __restrict__ kth, int32_t* __restrict__ idx,
-                                                            OneWs ws) {
+// A row's chunk lists: chunk c's n_out entries (score bits, token) start at
+// pool[c * slice], entry i of the concatenation is in chunk a with
+// off[a] <= i < off[a + 1] (off in LDS, nch + 1 entries).
+struct ListView {
+  const int2* pool;
+  const int* off;
+  int nch, slice, nlist;
+  bool coherent;   // written by workgroups of this launch: device-coherent loads
+  // Entries ib .. ib + 7 (token -1 past the end).
+  __device__ __forceinline__ void load8(int ib, int2 (&e)[8]) const {
+    int a = 0, b = nch;   // off[a] <= ib < off[b]
+    if (ib < nlist) {
+      while (b - a > 1) {
+        const int mid = (a + b) >> 1;
+        if (off[mid] <= ib) a = mid;
+        else b = mid;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int i = ib + u;
+      if (i < nlist) {
+        while (off[a + 1] <= i) ++a;
+        const int2* p = &pool[a * slice + (i - off[a])];
+        e[u] = coherent ? ld_agent(p) : *p;
+      } else {
+        e[u] = make_int2(0, -1);
+      }
+    }
+  }
+};
+
+// The selection of one row once its boundary bin b* and need (the rank of s*
+// among the b* tokens) are known, by a whole workgroup of kSmallNT threads:
+// from the lists when `lists` (every token of the row in b* and above is
+// listed; `first` holds list entries 8 tid .. 8 tid + 7), else from the whole
+// row (radix rounds restricted to b*, then an ordered pass). Writes the
+// row's indices, kth and the EMA update of theta.
+__device__ void select_bstar(bool lists, uint32_t bstar, int need, int nb, const float* __restrict__ row, int len,
+                             int k, const Shift& shf, float th_in, const ListView& lv, const int2 (&first)[8],
+                             int32_t* __restrict__ orow, float* kth_r, float* theta_out_r, SelLds& L) {
   constexpr int NT = kSmallNT;
-  __shared__ SelLds L;
-  __shared__ int s_off[kOneMaxChunks + 1];   // the last workgroup: chunk c's entries start at s_off[c]
-  __shared__ int s_fmax;
-  const int r = blockIdx.y, c = blockIdx.x, tid = threadIdx.x;
-  const int len = min(lens[r], max_len);   // the grid and workspace are sized by max_len
-  const float th_in = row_theta(theta_in, r);
-  const float* row = logits + (size_t)r * ld;
-  int32_t* orow = idx + (size_t)r * k;
-  if (len <= kSmallMax) {
-    if (c == 0) small_row(row, len, k, th_in, kth + r, theta_out ? theta_out + r : nullptr, orow, L);
-    return;
-  }
-  const int nch = (len + kOneChunk - 1) / kOneChunk;
-  if (c >= nch) return;
-  const Shift shf = make_shift(th_in);
-  int* ctl = ws.ctl + 32 * r;
-  int2* pool = ws.pool + (size_t)r * ws.npool;
-  const int slice = min(kSmallCand, ws.npool / nch);   // this row's entries per chunk
-
-  // ---- the chunk: histogram, floor, listed tokens
-  // Thread tid holds the 16 consecutive tokens from t0, so one scan of the
-  // per-thread counts orders the list. The per-token work is branch-free
-  // (the pass is bound by instruction issue, not by the read): lumped and
-  // absent tokens add to a junk word of their lane, unlisted ones stage into
-  // a junk entry of their lane.
-  const int lane = ech::lane_id();
-  const int lo = c * kOneChunk, hi = min(lo + kOneChunk, len);
-  const int t0 = lo + kSmallPer * tid;
-  const int nv = min(kSmallPer, max(0, hi - t0));   // this thread's tokens in the row
-  float v[kSmallPer];
-  if (nv == kSmallPer) {
-#pragma unroll
-    for (int q = 0; q < kSmallPer / 4; ++q) {
-      typedef float f4v __attribute__((ext_vector_type(4)));
-      const f4v x = __builtin_nontemporal_load(reinterpret_cast<const f4v*>(row + t0) + q);
-      v[4 * q] = x.x;
-      v[4 * q + 1] = x.y;
-      v[4 * q + 2] = x.z;
-      v[4 * q + 3] = x.w;
-    }
-  } else {
-#pragma unroll
-    for (int e = 0; e < kSmallPer; ++e) v[e] = e < nv ? row[t0 + e] : 0.f;
-  }
-  const uint32_t blo = band_lo(shf);
-  if (tid < 256) L.hist[tid] = 0;
-  __syncthreads();
-  uint32_t in = 0;   // bit e: token t0 + e is listed
-  int lumped = 0;
-#pragma unroll
-  for (int e = 0; e < kSmallPer; ++e) {
-    const bool ok = e < nv;
-    const float d = shf.on ? v[e] - shf.th : v[e];
-    const bool lump = d < shf.cut;
-    const uint32_t b = bin_one(d);
-    atomicAdd(&L.hist[(ok && !lump) ? b : 256 + lane], 1);
-    lumped += (ok && lump) ? 1 : 0;
-    in |= (ok && !lump && b >= blo) ? 1u << e : 0u;
-  }
-  lumped = wave_sum_dpp(lumped);
-  if (lane == 0 && lumped) atomicAdd(&L.hist[0], lumped);
-  int total;
-  int pre = block_scan_dpp<NT>(__popc(in), L.sh, &total);   // its barriers also close the histogram
-  uint32_t floor_c = blo;
-  if (total > slice) {   // the band does not fit the slice (block-uniform): raise the floor
-    // to the lowest bin whose count from the top fits (threads 0..255 take bins 255..0)
-    const int hb = tid < 256 ? L.hist[255 - tid] : 0;
-    int hall;
-    const int hex = block_scan_dpp<NT>(hb, L.sh, &hall);
-    const int fit = __syncthreads_count(tid < 256 && hex + hb <= slice);
-    floor_c = max(blo, 256u - (uint32_t)fit);
-    in = 0;
-#pragma unroll
-    for (int e = 0; e < kSmallPer; ++e)
-      in |= (e < nv && shifted_bin_one(v[e], shf) >= floor_c) ? 1u << e : 0u;
-    pre = block_scan_dpp<NT>(__popc(in), L.sh, &total);
-  }
-  {
-    int pos = pre;
-#pragma unroll
-    for (int e = 0; e < kSmallPer; ++e) {
-      const bool listed = (in >> e) & 1u;
-      L.cand[(listed && pos < slice) ? pos : kSmallCand + lane] = make_int2(__float_as_int(v[e]), t0 + e);
-      pos += listed ? 1 : 0;
-    }
-  }
-  __syncthreads();
-  const int n_out = min(total, slice);   // the floor bounds total by slice; guard only
-  for (int i = tid; i < n_out; i += NT) st_agent(&pool[c * slice + i], L.cand[i]);
-  if (tid == 0) st_agent(&ws.meta[(size_t)r * ws.nch + c], make_int2(n_out, (int)floor_c));
-  if (tid < 256) {
-    const int hv = L.hist[tid];
-    if (hv) atomicAdd(&ws.hist[(size_t)r * 256 + tid], hv);
-  }
-  // Publish: every wave's coherent stores and atomics complete, then the
-  // count; the last workgroup reads with coherent loads.
-  wait_vm_zero();
-  __syncthreads();
-  if (tid == 0)
-    L.s_last = __hip_atomic_fetch_add(&ctl[0], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == nch - 1;
-  __syncthreads();
-  if (!L.s_last) return;
-
-  // ---- the last workgroup of the row: b* and the selection
-  if (tid < 256) L.hist[tid] = ld_agent(&ws.hist[(size_t)r * 256 + tid]);
-  const int2 m = tid < nch ? ld_agent(&ws.meta[(size_t)r * ws.nch + tid]) : make_int2(0, 0);
-  if (tid == 0) s_fmax = 0;
-  __syncthreads();
-  pick_digit(L.hist, L.sh, k, &L.s_digit, &L.s_need);
-  const uint32_t bstar = (uint32_t)L.s_digit;
-  int need = L.s_need;
-  const int nb = L.hist[bstar];
-  if (tid < nch) atomicMax(&s_fmax, m.y);
-  int nlist;
-  const int off = block_scan_dpp<NT>(m.x, L.sh, &nlist);
-  if (tid < nch) s_off[tid] = off;
-  if (tid == 0) s_off[nch] = nlist;
-  __syncthreads();
+  const int tid = threadIdx.x;
+  const int nlist = lv.nlist;
+  auto load8 = [&](int ib, int2 (&e)[8]) { lv.load8(ib, e); };
   float sstar;
   int need_eq;
-  if ((uint32_t)s_fmax <= bstar) {
-    // Entries 8 tid + u of each 8 NT-entry round of the chunks' lists in
-    // chunk order.
-    auto load8 = [&](int ib, int2 (&e)[8]) {
-      int a = 0, b = nch;   // s_off[a] <= ib < s_off[b]
-      if (ib < nlist) {
-        while (b - a > 1) {
-          const int mid = (a + b) >> 1;
-          if (s_off[mid] <= ib) a = mid;
-          else b = mid;
-        }
-      }
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int i = ib + u;
-        if (i < nlist) {
-          while (s_off[a + 1] <= i) ++a;
-          e[u] = ld_agent(&pool[a * slice + (i - s_off[a])]);
-        } else {
-          e[u] = make_int2(0, -1);
-        }
-      }
-    };
-    int2 first[8];   // the first round, kept for the ordered pass
-    load8(8 * tid, first);
+  if (lists) {
     uint32_t prefix = 0;
     if (nb <= kSmallCand) {   // the b* entries into LDS
       if (tid == 0) L.s_nc = 0;
@@ -1557,9 +1409,240 @@ __global__ __launch_bounds__(kSmallNT) void topk_one_kernel(const float* __restr
     row_compact(row, len, sstar, need_eq, k, orow, L.sh);
   }
   if (tid == 0) {
-    kth[r] = sstar;
-    if (theta_out) theta_out[r] = (th_in == th_in) ? (sstar + th_in) * 0.5f : sstar;
+    *kth_r = sstar;
+    if (theta_out_r) *theta_out_r = (th_in == th_in) ? (sstar + th_in) * 0.5f : sstar;
   }
+}
+
+
+__global__ __launch_bounds__(kSmallNT) void topk_one_kernel(const float* __restrict__ logits, int64_t ld,
+                                                            const int32_t* __restrict__ lens, int max_len, int k,
+                                                            const float* theta_in, float* theta_out,
+                                                            float* __restrict__ kth, int32_t* __restrict__ idx,
+                                                            OneWs ws) {
+  constexpr int NT = kSmallNT;
+  __shared__ SelLds L;
+  __shared__ int s_off[kOneMaxChunks + 1];   // the last workgroup: chunk c's entries start at s_off[c]
+  __shared__ int s_fmax;
+  const int r = blockIdx.y, c = blockIdx.x, tid = threadIdx.x;
+  const int len = min(lens[r], max_len);   // the grid and workspace are sized by max_len
+  const float th_in = row_theta(theta_in, r);
+  const float* row = logits + (size_t)r * ld;
+  int32_t* orow = idx + (size_t)r * k;
+  if (len <= kSmallMax) {
+    if (c == 0) small_row(row, len, k, th_in, kth + r, theta_out ? theta_out + r : nullptr, orow, L);
+    return;
+  }
+  const int nch = (len + kOneChunk - 1) / kOneChunk;
+  if (c >= nch) return;
+  const Shift shf = make_shift(th_in);
+  int* ctl = ws.ctl + 32 * r;
+  int2* pool = ws.pool + (size_t)r * ws.npool;
+  const int slice = min(kSmallCand, ws.npool / nch);   // this row's entries per chunk
+
+  // ---- the chunk: histogram, floor, listed tokens
+  // Thread tid holds the 16 consecutive tokens from t0, so one scan of the
+  // per-thread counts orders the list. The per-token work is branch-free
+  // (the pass is bound by instruction issue, not by the read): lumped and
+  // absent tokens add to a junk word of their lane, unlisted ones stage into
+  // a junk entry of their lane.
+  const int lane = ech::lane_id();
+  const int lo = c * kOneChunk, hi = min(lo + kOneChunk, len);
+  const int t0 = lo + kSmallPer * tid;
+  const int nv = min(kSmallPer, max(0, hi - t0));   // this thread's tokens in the row
+  float v[kSmallPer];
+  if (nv == kSmallPer) {
+#pragma unroll
+    for (int q = 0; q < kSmallPer / 4; ++q) {
+      typedef float f4v __attribute__((ext_vector_type(4)));
+      const f4v x = __builtin_nontemporal_load(reinterpret_cast<const f4v*>(row + t0) + q);
+      v[4 * q] = x.x;
+      v[4 * q + 1] = x.y;
+      v[4 * q + 2] = x.z;
+      v[4 * q + 3] = x.w;
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < kSmallPer; ++e) v[e] = e < nv ? row[t0 + e] : 0.f;
+  }
+  const uint32_t blo = band_lo(shf);
+  if (tid < 256) L.hist[tid] = 0;
+  __syncthreads();
+  uint32_t in = 0;   // bit e: token t0 + e is listed
+  int lumped = 0;
+#pragma unroll
+  for (int e = 0; e < kSmallPer; ++e) {
+    const bool ok = e < nv;
+    const float d = shf.on ? v[e] - shf.th : v[e];
+    const bool lump = d < shf.cut;
+    const uint32_t b = bin_one(d);
+    atomicAdd(&L.hist[(ok && !lump) ? b : 256 + lane], 1);
+    lumped += (ok && lump) ? 1 : 0;
+    in |= (ok && !lump && b >= blo) ? 1u << e : 0u;
+  }
+  lumped = wave_sum_dpp(lumped);
+  if (lane == 0 && lumped) atomicAdd(&L.hist[0], lumped);
+  int total;
+  int pre = block_scan_dpp<NT>(__popc(in), L.sh, &total);   // its barriers also close the histogram
+  uint32_t floor_c = blo;
+  if (total > slice) {   // the band does not fit the slice (block-uniform): raise the floor
+    // to the lowest bin whose count from the top fits (threads 0..255 take bins 255..0)
+    const int hb = tid < 256 ? L.hist[255 - tid] : 0;
+    int hall;
+    const int hex = block_scan_dpp<NT>(hb, L.sh, &hall);
+    const int fit = __syncthreads_count(tid < 256 && hex + hb <= slice);
+    floor_c = max(blo, 256u - (uint32_t)fit);
+    in = 0;
+#pragma unroll
+    for (int e = 0; e < kSmallPer; ++e)
+      in |= (e < nv && shifted_bin_one(v[e], shf) >= floor_c) ? 1u << e : 0u;
+    pre = block_scan_dpp<NT>(__popc(in), L.sh, &total);
+  }
+  {
+    int pos = pre;
+#pragma unroll
+    for (int e = 0; e < kSmallPer; ++e) {
+      const bool listed = (in >> e) & 1u;
+      L.cand[(listed && pos < slice) ? pos : kSmallCand + lane] = make_int2(__float_as_int(v[e]), t0 + e);
+      pos += listed ? 1 : 0;
+    }
+  }
+  __syncthreads();
+  const int n_out = min(total, slice);   // the floor bounds total by slice; guard only
+  for (int i = tid; i < n_out; i += NT) st_agent(&pool[c * slice + i], L.cand[i]);
+  if (tid == 0) st_agent(&ws.meta[(size_t)r * ws.nch + c], make_int2(n_out, (int)floor_c));
+  if (tid < 256) {
+    const int hv = L.hist[tid];
+    if (hv) atomicAdd(&ws.hist[(size_t)r * 256 + tid], hv);
+  }
+  // Publish: every wave's coherent stores and atomics complete, then the
+  // count; the last workgroup reads with coherent loads.
+  wait_vm_zero();
+  __syncthreads();
+  if (tid == 0)
+    L.s_last = __hip_atomic_fetch_add(&ctl[0], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == nch - 1;
+  __syncthreads();
+  if (!L.s_last) return;
+
+  // ---- the last workgroup of the row: b* and the selection
+  if (tid < 256) L.hist[tid] = ld_agent(&ws.hist[(size_t)r * 256 + tid]);
+  const int2 m = tid < nch ? ld_agent(&ws.meta[(size_t)r * ws.nch + tid]) : make_int2(0, 0);
+  if (tid == 0) s_fmax = 0;
+  __syncthreads();
+  pick_digit(L.hist, L.sh, k, &L.s_digit, &L.s_need);
+  const uint32_t bstar = (uint32_t)L.s_digit;
+  const int need = L.s_need;
+  const int nb = L.hist[bstar];
+  if (tid < nch) atomicMax(&s_fmax, m.y);
+  int nlist;
+  const int off = block_scan_dpp<NT>(m.x, L.sh, &nlist);
+  if (tid < nch) s_off[tid] = off;
+  if (tid == 0) s_off[nch] = nlist;
+  __syncthreads();
+  ListView lv{pool, s_off, nch, slice, nlist, true};
+  int2 first[8];
+  const bool lists = (uint32_t)s_fmax <= bstar;
+  if (lists) lv.load8(8 * tid, first);
+  select_bstar(lists, bstar, need, nb, row, len, k, shf, th_in, lv, first, orow, kth + r,
+               theta_out ? theta_out + r : nullptr, L);
+}
+
+// ------------------------------------------------------------------ rows listed while scored
+// grid (R), kSmallNT threads: the selection of rows whose band the scoring
+// kernel listed as it scored them, in the one-pass layout with its scoring
+// waves as the chunks. Every token of the row at or above the highest floor
+// is listed, so the histogram of those entries is the row's histogram there:
+// if they are at least k, b* is among them and the selection comes from the
+// lists; otherwise (a NaN theta, an overflowing wave, or a band that holds
+// fewer than k tokens) one pass over the row gives its whole histogram and
+// the row path selects. Rows no longer than kSmallMax are selected whole.
+__global__ __launch_bounds__(kSmallNT) void topk_lists_kernel(const float* __restrict__ logits, int64_t ld,
+                                                              const int32_t* __restrict__ lens, int max_len, int k,
+                                                              const float* theta_in, float* theta_out,
+                                                              float* __restrict__ kth, int32_t* __restrict__ idx,
+                                                              const int2* __restrict__ meta,
+                                                              const int2* __restrict__ pool,
+                                                              const float* __restrict__ list_theta, int cpr,
+                                                              int slice, int chunk_tok) {
+  constexpr int NT = kSmallNT;
+  constexpr int kPerT = ech::kListMaxChunks / NT;   // chunks per thread
+  __shared__ SelLds L;
+  __shared__ int s_off[ech::kListMaxChunks + 1];
+  __shared__ int s_fmax;
+  const int r = blockIdx.x, tid = threadIdx.x;
+  const int len = min(lens[r], max_len);
+  const float th_in = row_theta(theta_in, r);
+  const float* row = logits + (size_t)r * ld;
+  int32_t* orow = idx + (size_t)r * k;
+  if (len <= kSmallMax) {
+    small_row(row, len, k, th_in, kth + r, theta_out ? theta_out + r : nullptr, orow, L);
+    return;
+  }
+  const int nch = min((len + chunk_tok - 1) / chunk_tok, cpr);
+  const Shift shf = make_shift(th_in);
+  // lists made against another theta prove nothing here: the whole row then
+  const bool same_theta = __float_as_uint(list_theta[r]) == __float_as_uint(th_in);
+  // chunk offsets (thread tid sums chunks kPerT tid .. +kPerT) and the highest floor
+  int cnt[kPerT];
+  int mine = 0, fl = 0;
+#pragma unroll
+  for (int u = 0; u < kPerT; ++u) {
+    const int c = kPerT * tid + u;
+    const int2 m = c < nch ? (same_theta ? meta[(size_t)r * cpr + c] : make_int2(0, 256)) : make_int2(0, 0);
+    cnt[u] = m.x;
+    mine += m.x;
+    fl = max(fl, m.y);
+  }
+  if (tid == 0) s_fmax = 0;
+  if (tid < 256) L.hist[tid] = 0;
+  __syncthreads();
+  if (fl) atomicMax(&s_fmax, fl);
+  int nlist;
+  int off = block_scan_dpp<NT>(mine, L.sh, &nlist);
+#pragma unroll
+  for (int u = 0; u < kPerT; ++u) {
+    const int c = kPerT * tid + u;
+    if (c < nch) s_off[c] = off;
+    off += cnt[u];
+  }
+  if (tid == 0) s_off[nch] = nlist;
+  __syncthreads();
+  const uint32_t fmax = (uint32_t)s_fmax;
+  const ListView lv{pool + (size_t)r * cpr * slice, s_off, nch, slice, nlist, false};
+  int2 first[8];
+  lv.load8(8 * tid, first);
+  int above = 0;
+  for (int i0 = 0; i0 < nlist; i0 += 8 * NT) {
+    int2 e[8];
+    if (i0 == 0) {
+#pragma unroll
+      for (int u = 0; u < 8; ++u) e[u] = first[u];
+    } else {
+      lv.load8(i0 + 8 * tid, e);
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const uint32_t b = e[u].y >= 0 ? shifted_bin_one(__int_as_float(e[u].x), shf) : 0u;
+      const bool at = e[u].y >= 0 && b >= fmax;
+      ech::lds_hist_add(L.hist, b, at);
+      above += at ? 1 : 0;
+    }
+  }
+  int n_above;
+  (void)block_scan_dpp<NT>(above, L.sh, &n_above);   // its barriers also close the histogram
+  const bool lists = n_above >= k;
+  if (!lists) {   // the row's whole histogram, by one pass over the row
+    if (tid < 256) L.hist[tid] = 0;
+    __syncthreads();
+    for_each_score<NT>(row, len, [&](int, float x) { ech::lds_hist_add(L.hist, shifted_bin_one(x, shf), true); });
+    __syncthreads();
+  }
+  pick_digit(L.hist, L.sh, k, &L.s_digit, &L.s_need);
+  const uint32_t bstar = (uint32_t)L.s_digit;
+  const int need = L.s_need;
+  const int nb = L.hist[bstar];
+  select_bstar(lists, bstar, need, nb, row, len, k, shf, th_in, lv, first, orow, kth + r,
+               theta_out ? theta_out + r : nullptr, L);
 }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -1696,4 +1779,14 @@ extern "C" int ech_topk_noalloc(const float* logits, int64_t ld, const int32_t* 
   const int rc = scratch_of_current_device(&ws);
   if (rc != ECH_OK) return rc;
   return topk_launch(logits, ld, row_len, R, max_len, k, theta_in, theta_out, idx, kth, ws, stream);
+}
+
+int ech::topk_lists_launch(const float* logits, int64_t ld, const int32_t* row_len, int R, int max_len, int k,
+                           const float* theta_in, float* theta_out, int32_t* idx, float* kth, const int2* meta,
+                           const int2* pool, const float* list_theta, int cpr, int slice, int chunk_tok,
+                           hipStream_t stream) {
+  hipLaunchKernelGGL(topk_lists_kernel, dim3(R), dim3(kSmallNT), 0, stream, logits, ld, row_len, max_len, k,
+                     theta_in, theta_out, kth, idx, meta, pool, list_theta, cpr, slice, chunk_tok);
+  ECH_LAUNCH_CHECK();
+  return ECH_OK;
 }

@@ -13,8 +13,8 @@ their rows start crossing PCIe, while later sequences are still being scored;
 a copier on S1 takes them as they appear and, once S0 has the FINAL maps,
 goes on to the FINAL rows with the link still busy:
 
-    S0: scores + EARLY maps (one launch) --> ech_topk --> FINAL maps ........--> rest of both lists
-    S1: live copier: early rows as allocated, then the FINAL rows ------------/
+    S0: scores + EARLY maps + band lists (one launch) --> ech_topk_early --> FINAL maps --> rest of both lists
+    S1: live copier: early rows as allocated, then the FINAL rows ---------------------------/
 
 theta is double-buffered (the early fetch reads the prediction while the
 top-k writes its update). When the batch's
@@ -43,7 +43,7 @@ import torch
 from . import (ECH_EARLY, ECH_FINAL, ECH_PREFILL, LayerState, ech_cache_reset, ech_cache_step,
                ech_cache_step_ws_bytes, ech_index_logits, ech_index_logits_causal, ech_index_logits_early,
                ech_index_logits_early_ws_bytes, ech_kv_append, ech_recall, ech_recall_early_live, ech_recall_rest,
-               ech_topk, ech_topk_ws_bytes)
+               ech_topk, ech_topk_early, ech_topk_ws_bytes)
 
 
 def round_up(x: int, m: int) -> int:
@@ -281,8 +281,9 @@ class DecodeLayer:
         (ech_recall_rest)."""
         first_b0, first_b1 = self.chunks[0]
         mark('topk', s0)
-        ech_topk(self.logits, self.lens, self.max_len, self.k, th, th_next, self.idx, self.kth, self.ws_topk,
-                 stream=s0)
+        # from the band lists the scoring waves wrote (the scores are not read again)
+        ech_topk_early(self.logits, self.lens, self.max_len, self.k, th, th_next, self.idx, self.kth, self.state,
+                       self.ws_fused, stream=s0)
         mark('topk', s0)
         self.ev_early.record(self.s1)              # the copier is done
         mark('final', s0)

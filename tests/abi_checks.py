@@ -120,6 +120,20 @@ def check_index_logits_early_rejects_bad_args(lib):
     assert rest(Me=-1) == -1
     assert rest(pool=FAKE + 8) == -1
 
+    wse = lib.ech_index_logits_early_ws_bytes(8, 20000, 500, 64)
+
+    def early_topk(k=64, ld=20032, ml=20000, th=FAKE, wsp=FAKE, wsb=wse, R=8):
+        return lib.ech_topk_early(FAKE, ld, FAKE, R, ml, k, th, None, FAKE, FAKE, wsp, wsb, 500, 64, None)
+    assert early_topk(th=None) == -1          # the theta the scores call took is required
+    assert early_topk(k=0) == -1
+    assert early_topk(k=4097) == -1
+    assert early_topk(ld=19999) == -1
+    assert early_topk(ld=20002) == -1         # rows 16-byte aligned
+    assert early_topk(wsp=FAKE + 128) == -1
+    assert early_topk(wsb=wse - 1) == -1
+    assert early_topk(R=0) == -1
+    assert early_topk(ml=(1 << 20) + 1, ld=(1 << 20) + 64, wsb=1 << 40) == -1   # more than 4096 waves per row
+
 
 def check_topk_noalloc_rejects_bad_args(lib):
     def call(R=4, ml=1000, k=64, ld=1000, ptr=FAKE):

@@ -27,7 +27,7 @@ def test_header_declares_entry_points():
     for name in ['ech_index_logits', 'ech_index_logits_causal', 'ech_topk', 'ech_topk_ws_bytes',
                  'ech_cache_step', 'ech_cache_step_ws_bytes', 'ech_cache_reset', 'ech_recall',
                  'ech_index_logits_early', 'ech_index_logits_early_ws_bytes', 'ech_recall_early_live',
-                 'ech_recall_rest', 'ech_topk_noalloc',
+                 'ech_recall_rest', 'ech_topk_early', 'ech_topk_noalloc',
                  'ech_status_str', 'ech_version']:
         assert name in syms
 

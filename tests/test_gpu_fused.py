@@ -32,7 +32,7 @@ def _walk(h0, h1, n, C):
     return (h1 - h0) % C or C
 
 
-def _run(wl, schedule, steps=4, e=None, final_live=False):
+def _run(wl, schedule, steps=4, e=None, final_live=False, topk_early=False):
     keys, scale = wk.keys(wl)
     w = wk.head_weights(wl)
     rows = wk.host_rows(wl)
@@ -71,7 +71,10 @@ def _run(wl, schedule, steps=4, e=None, final_live=False):
         st_f = torch.empty((B, 4), dtype=torch.int32, device='cuda')
 
         def topk_and_final(stream):
-            ech.ech_topk(logits, lnd, max_len, k, theta, th_next, idx, kth, ws_t, stream=stream)
+            if topk_early:   # from the band lists the fused launch wrote
+                ech.ech_topk_early(logits, lnd, max_len, k, theta, th_next, idx, kth, st, ws, stream=stream)
+            else:
+                ech.ech_topk(logits, lnd, max_len, k, theta, th_next, idx, kth, ws_t, stream=stream)
             ech.ech_cache_step(ech.ECH_FINAL, st, t0d, lnd, max_len, idx=idx, k=k, sel_slot=sel, stats=st_f,
                                ws=ws_f, stream=stream)
 
@@ -218,7 +221,7 @@ def test_fused_copier_takes_the_final_rows():
     FINAL rows were copied by the copier."""
     need_gpu()
     wl = wk.CONFIGS['decode-32x128k-fp8'].scaled(B=6, N=20000, C=30000, k=1024, cap=300, variant='normal')
-    copied, copied_final, reached = _run(wl, 'beside', final_live=True)
+    copied, copied_final, reached = _run(wl, 'beside', final_live=True, topk_early=True)
     assert copied > 0 and copied_final > 0 and reached == 0
 
 
@@ -231,7 +234,7 @@ def test_fused_copier_final_rows_small_ring():
     need_gpu()
     wl = wk.CONFIGS['decode-64x110k-fp8-capacity'].scaled(B=4, N=6000, len_lo=2500, C=4200, k=1024, cap=800,
                                                           resample_p=0.5, variant='normal')
-    _, _, reached = _run(wl, 'beside', steps=5, final_live=True)
+    _, _, reached = _run(wl, 'beside', steps=5, final_live=True, topk_early=True)
     assert reached >= 1
 
 
@@ -244,5 +247,71 @@ def test_recall_rest_after_a_copier_that_gave_up_small_ring():
     need_gpu()
     wl = wk.CONFIGS['decode-64x110k-fp8-capacity'].scaled(B=4, N=6000, len_lo=2500, C=4200, k=1024, cap=800,
                                                           resample_p=0.5, variant='normal')
-    copied, copied_final, reached = _run(wl, 'copier_first', steps=3, final_live=True)
+    copied, copied_final, reached = _run(wl, 'copier_first', steps=3, final_live=True, topk_early=True)
     assert copied == 0 and copied_final == 0 and reached >= 1
+
+
+@pytest.mark.parametrize('pred', ['near', 'high', 'low', 'nan', 'mixed', 'other'])
+def test_topk_early_matches_the_oracle(pred):
+    """ech_topk_early selects from the band lists the scoring waves wrote. The
+    predictions steer which way it goes: near the k-th score (the lists
+    decide), far above it (the band holds fewer than k tokens), far below it
+    (the waves' bands overflow their slices), NaN, a mix over the rows, and a
+    call with a theta other than the one the lists were made against (the
+    whole row is selected). Each must give exactly the oracle's selection,
+    kth and EMA update, and ech_topk's bits on the same scores.
+    ECHO explainer, "Prefill: one-round histogram" and "Fused indexer kernel
+    (extends DeepGEMM)"."""
+    need_gpu()
+    wl = wk.CONFIGS['decode-32x128k-fp8'].scaled(B=6, N=40000, C=30000, k=1024, cap=300, variant='normal')
+    keys, scale = wk.keys(wl)
+    w = wk.head_weights(wl)
+    B, C, k, cap = wl.B, wl.C, wl.k, wl.cap
+    max_len = int(wl.lens.max())
+    ld = (max_len + 63) // 64 * 64
+    m_early = B * min(cap, max_len)
+    st = ech.LayerState.allocate(wl.P, C, B * min(k, max_len), M_early=m_early)
+    ws = torch.zeros(ech.ech_index_logits_early_ws_bytes(B, max_len, C, m_early), dtype=torch.uint8, device='cuda')
+    kd, sd, wd = dev(keys), dev(scale), dev(w)
+    t0d, lnd = dev(wl.tok0), dev(wl.lens)
+    q = next(iter(wk.decode_queries(wl, 1)))
+    qd = dev(q)
+    logits = torch.zeros((B, ld), dtype=torch.float32, device='cuda')
+    stats = torch.zeros((B, 4), dtype=torch.int32, device='cuda')
+
+    def fused(theta):
+        ech.ech_cache_reset(st)
+        ech.ech_index_logits_early(qd, wd, kd, sd, t0d, lnd, max_len, logits, 0, B, theta, cap, st, stats, ws)
+
+    fused(torch.full((B,), float('nan'), device='cuda'))
+    torch.cuda.synchronize()
+    rows_l = [host(logits)[b, :wl.lens[b]] for b in range(B)]
+    idx_o, kth_o = oracle.topk_rows(rows_l, k)
+    kth_o = np.asarray(kth_o, np.float32)
+    scale_by = {'near': 1.01, 'high': 1.6, 'low': -1.0, 'other': 1.01}
+    if pred in scale_by:
+        th = (kth_o * np.float32(scale_by[pred])).astype(np.float32)
+    elif pred == 'nan':
+        th = np.full(B, np.nan, np.float32)
+    else:
+        th = np.array([kth_o[b] * f for b, f in enumerate([1.0, 1.6, -1.0, np.nan, 0.99, 1.02])], np.float32)
+    thd = dev(th)
+    fused(thd)
+    if pred == 'other':   # the selection is asked with another theta than the lists were made against
+        th = (th * np.float32(1.001)).astype(np.float32)
+        thd = dev(th)
+    idx = torch.full((B, k), -7, dtype=torch.int32, device='cuda')
+    kth = torch.empty(B, dtype=torch.float32, device='cuda')
+    th_next = torch.empty(B, dtype=torch.float32, device='cuda')
+    ech.ech_topk_early(logits, lnd, max_len, k, thd, th_next, idx, kth, st, ws)
+    ws_t = torch.empty(ech.ech_topk_ws_bytes(B, max_len, k), dtype=torch.uint8, device='cuda')
+    idx2 = torch.full((B, k), -7, dtype=torch.int32, device='cuda')
+    kth2, th2 = torch.empty_like(kth), torch.empty_like(th_next)
+    ech.ech_topk(logits, lnd, max_len, k, thd, th2, idx2, kth2, ws_t)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(host(idx), idx_o)
+    np.testing.assert_array_equal(host(kth), kth_o)
+    np.testing.assert_array_equal(host(th_next), oracle.theta_rows(th, kth_o))
+    np.testing.assert_array_equal(host(idx), host(idx2))
+    np.testing.assert_array_equal(host(kth).view(np.int32), host(kth2).view(np.int32))
+    np.testing.assert_array_equal(host(th_next).view(np.int32), host(th2).view(np.int32))
