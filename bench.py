@@ -282,7 +282,7 @@ def bench_decode(args, wl):
     per_launch = tokens * per_token + wl.B * (64 * 128 * 2 + 64 * 4)
     achieved = per_launch / (logits_ms * 1e-3) / 1e9
     flops = tokens * 2 * 64 * 128
-    src = source_hash('fused.hip', 'decode.hpp', 'score.hpp') if layer.fused else \
+    src = source_hash('fused.hip', 'decode.hpp', 'score.hpp', 'bins.hpp') if layer.fused else \
         source_hash('logits.hip', 'decode.hpp', 'score.hpp')
     traffic = measured_traffic(('fused_' if layer.fused else 'logits_decode_') + wl.name, src)
     out = {
@@ -341,6 +341,7 @@ def bench_decode(args, wl):
         topk_stage = {'kernel': 'ech_topk_early (topk_lists_kernel: the selection from the band lists the scores '
                                 'launch wrote as it scored)',
                       'bound': 'latency', 'us': st['topk'], 'alone_us': topk_alone_us,
+                      'traffic': measured_traffic('topk_lists_' + wl.name, source_hash('topk.hip', 'bins.hpp')),
                       'note': 'one workgroup per row reads its band lists (a few thousand entries) and writes its k '
                               'indices; the scores are not read again (rows the lists cannot decide take one pass '
                               'over the row). us: in eager steps, alone_us: K calls back to back'}
@@ -351,7 +352,8 @@ def bench_decode(args, wl):
                  'frac': topk_bytes / (st['topk'] * 1e-6) / 1e9 / PEAK_HBM_GBS if st['topk'] else None,
                  'alone_us': topk_alone_us,
                  'alone_frac': topk_bytes / (topk_alone_us * 1e-6) / 1e9 / PEAK_HBM_GBS,
-                 'traffic': measured_traffic('topk_one_' + wl.name, source_hash('topk.hip')) if one_pass else None,
+                 'traffic': (measured_traffic('topk_one_' + wl.name, source_hash('topk.hip', 'bins.hpp'))
+                             if one_pass else None),
                  'note': ('one read of the scores plus the index output; us: in eager steps, alone_us: K calls '
                           'back to back; ' + ('one pass (a reset and the pass kernel)' if one_pass else
                                               'one launch (rows of at most 16384 tokens)'))},
