@@ -34,9 +34,11 @@ constexpr int kValV = 512;                 // value width
 constexpr int kTile = 32;                  // tokens per LDS tile
 constexpr int kKs = kRowV / 32;            // contraction steps of the scores (18)
 constexpr int kCt = kValV / 16;            // column tiles of the output (32)
-constexpr int kKPitch = kRowV * 2 + 16;    // bytes per token row in LDS (bank spread)
+constexpr int kKPitch = kRowV * 2 + 32;    // bytes per token row in LDS (bank spread)
 constexpr int kChunks = kRowV * 2 / 16;    // 16-byte pieces per row (72)
 constexpr int kMaxWaves = 8;               // heads <= 128
+constexpr int kKD = 4;                     // key fragments in flight per wave
+constexpr int kVD = 3;                     // value fragments in flight per wave
 
 #define ECH_ATTN_LDS(p) ((__attribute__((address_space(3))) void*)(p))
 
@@ -64,13 +66,18 @@ __device__ __forceinline__ float lane_group_max(float x) {
 // for them before every LDS read; they write no register, and each tile opens
 // with an explicit wait for all of them and a barrier. Slot ids go through a
 // 3-deep LDS ring, loaded one tile further ahead and used only after that
-// wait. Measured at 32 x 128 x 2048: each tile's loads have landed when its
-// products start (0.3 us of wait and barrier per tile), the products take
-// ~3 us per 32-token tile (LDS reads of every wave's operands: ~1.8 us at
-// 128 B per clock).
-constexpr int kP2 = kKPitch / 16;            // 73 chunks per token row in LDS (one spare: banks)
-constexpr int kPos2 = kTile * kP2;           // 2336 chunk positions per tile
-constexpr int kBuf2 = kPos2 * 16;            // 37376 bytes per tile buffer
+// wait.
+//
+// LDS reads are software-pipelined: kKD key and kVD value fragments are in
+// flight per wave (the scheduler is held to one read per product), where the
+// compiler alone would wait for each read before its product. The row pitch
+// is 74 chunks: the key reads (16 rows x 64 B per read) then hit every bank
+// once per pass; measured on gfx950 with a read probe, 216 B per clock per CU
+// at pitch 74 against 125 at 73 and 63 at 72; the transposed value reads
+// give ~89 B per clock at any of these pitches.
+constexpr int kP2 = kKPitch / 16;            // 74 chunks per token row in LDS (two spare: banks)
+constexpr int kPos2 = kTile * kP2;           // 2368 chunk positions per tile
+constexpr int kBuf2 = kPos2 * 16;            // 37888 bytes per tile buffer
 constexpr int kInstr2 = (kPos2 + 63) / 64;   // 37 load instructions per tile
 
 typedef short v4s_t __attribute__((ext_vector_type(4)));
@@ -93,9 +100,16 @@ __global__ void __launch_bounds__(64 * NW, 1)
   __shared__ int slots[3][kTile];   // slot id of each token of a tile, -1: nothing to attend
   constexpr int kJ = (kInstr2 + NW - 1) / NW;   // load instructions per wave per tile
   const int hsplit = H / (16 * NS * NW);
-  const int b = blockIdx.y, sp = blockIdx.x / hsplit, nsp = gridDim.x / hsplit;
+  const int nsp = gridDim.x / hsplit;
+  // The head groups of one span run on one XCD, next to each other in
+  // dispatch order (workgroups go to the XCDs round robin), so that the
+  // rows they all read come from that XCD's L2 after the first read.
+  int wg = blockIdx.x + blockIdx.y * gridDim.x;
+  const int nwg = gridDim.x * gridDim.y;
+  if (hsplit > 1 && nwg % (8 * hsplit) == 0) wg = (wg % 8) * (nwg / 8) + wg / 8;
+  const int hh = wg % hsplit, b = wg / (hsplit * nsp), sp = (wg / hsplit) % nsp;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, col = lane & 15, grp = lane >> 4;
-  const int h0 = (blockIdx.x % hsplit) * (16 * NS * NW) + wave * 16 * NS + col;   // head set hs: h0 + 16 hs
+  const int h0 = hh * (16 * NS * NW) + wave * 16 * NS + col;   // head set hs: h0 + 16 hs
   const int32_t* sel = sel_slot + (size_t)b * k;
   const int t_begin = sp * span, t_end = min(k, t_begin + span);
   const int ntiles = t_end > t_begin ? (t_end - t_begin + kTile - 1) / kTile : 0;
@@ -110,17 +124,24 @@ __global__ void __launch_bounds__(64 * NW, 1)
   auto slot_ok = [&](int t0, int sl) -> int { return (t0 + lane < t_end && sl >= 0 && sl < C) ? sl : -1; };
   // direct-to-LDS loads of the tile whose slot ids are in slots[si]; the
   // pad chunk of each LDS row and positions past the tile are not loaded
-  auto issue = [&](int si, uint8_t* dst) {
+  // The lane's positions are recomputed per tile (a few integer operations)
+  // and the LDS addresses are scalar: held across the loop they would take
+  // registers the products need.
+  auto issue = [&](int si, int buf) {
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+    const int wv = __builtin_amdgcn_readfirstlane(wave);
+    const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(ECH_ATTN_LDS(&tiles[0][0]))) +
+                          static_cast<uint32_t>(buf * kBuf2);
 #pragma unroll
     for (int j = 0; j < kJ; ++j) {
-      const int ins = j * NW + wave;
-      const int p = ins * 64 + lane;
+      const int ins = j * NW + wv;
+      const int p = ins * 64 + ln;
       const int t = p / kP2, c = p - t * kP2;
       if (ins < kInstr2 && p < kPos2 && c < kChunks) {
         const int sl = slots[si][t];
         const uint4* src = cache + (size_t)max(sl, 0) * kChunks + c;
-        const uint32_t lds = __builtin_amdgcn_readfirstlane(
-            static_cast<uint32_t>(reinterpret_cast<uintptr_t>(ECH_ATTN_LDS(dst + ins * 1024))));
+        const uint32_t lds = lds0 + static_cast<uint32_t>(ins * 1024);
         asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off nt" ::"s"(lds), "v"(src) : "memory", "m0");
       }
     }
@@ -129,16 +150,33 @@ __global__ void __launch_bounds__(64 * NW, 1)
   auto compute = [&](int si, const uint8_t* cur) {
     f32x4_t st[2][NS];   // [16-token half][head set]
 #pragma unroll
-    for (int sub = 0; sub < 2; ++sub) {
+    for (int sub = 0; sub < 2; ++sub)
 #pragma unroll
       for (int hs = 0; hs < NS; ++hs) st[sub][hs] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-      const uint8_t* kr = cur + (sub * 16 + col) * kKPitch + grp * 16;
+    {
+      // 36 key fragments, x = 2 s + half, kKD of them in flight
+      const uint8_t* kr = cur + col * kKPitch + grp * 16;
+      auto kload = [&](int x) {
+        return as_bf16x8(*reinterpret_cast<const uint4*>(kr + (x & 1) * 16 * kKPitch + (x >> 1) * 64));
+      };
+      bf16x8_t kb[kKD];
 #pragma unroll
-      for (int s = 0; s < kKs; ++s) {
-        const bf16x8_t kf = as_bf16x8(*reinterpret_cast<const uint4*>(kr + s * 64));
+      for (int x = 0; x < kKD; ++x) kb[x] = kload(x);
 #pragma unroll
-        for (int hs = 0; hs < NS; ++hs) st[sub][hs] = mfma(kf, qf[hs][s], st[sub][hs]);
+      for (int x = 0; x < 2 * kKs; ++x) {
+        const bf16x8_t kf = kb[x % kKD];
+        if (x + kKD < 2 * kKs) kb[x % kKD] = kload(x + kKD);
+#pragma unroll
+        for (int hs = 0; hs < NS; ++hs) st[x & 1][hs] = mfma(kf, qf[hs][x >> 1], st[x & 1][hs]);
       }
+      __builtin_amdgcn_sched_group_barrier(0x100, kKD, 0);   // DS reads
+#pragma unroll
+      for (int x = 0; x < 2 * kKs - kKD; ++x) {
+        __builtin_amdgcn_sched_group_barrier(0x008, NS, 0);  // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, NS * kKD, 0);
+      __builtin_amdgcn_sched_barrier(0);
     }
     bool ok[8];
 #pragma unroll
@@ -184,11 +222,26 @@ __global__ void __launch_bounds__(64 * NW, 1)
     // O^T += V^T . P^T: the value operand of tokens {4 grp .. +3, 16 + 4 grp .. +3}
     // (the order of this lane's probabilities) at column c*16 + col
     const uint8_t* vb = cur + (4 * grp + (col >> 2)) * kKPitch + 8 * (col & 3);
+    __builtin_amdgcn_sched_barrier(0);
+    {
+      bf16x8_t vbuf[kVD];
 #pragma unroll
-    for (int c = 0; c < kCt; ++c) {
-      const bf16x8_t vf = tr_pair(vb + c * 32, vb + 16 * kKPitch + c * 32);
+      for (int c = 0; c < kVD; ++c) vbuf[c] = tr_pair(vb + c * 32, vb + 16 * kKPitch + c * 32);
 #pragma unroll
-      for (int hs = 0; hs < NS; ++hs) acc[hs][c] = mfma(vf, pb[hs], acc[hs][c]);
+      for (int c = 0; c < kCt; ++c) {
+        const bf16x8_t vf = vbuf[c % kVD];
+        if (c + kVD < kCt) vbuf[c % kVD] = tr_pair(vb + (c + kVD) * 32, vb + 16 * kKPitch + (c + kVD) * 32);
+#pragma unroll
+        for (int hs = 0; hs < NS; ++hs) acc[hs][c] = mfma(vf, pb[hs], acc[hs][c]);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x100, 2 * kVD, 0);
+#pragma unroll
+      for (int c = 0; c < kCt - kVD; ++c) {
+        __builtin_amdgcn_sched_group_barrier(0x008, NS, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, NS * kVD, 0);
+      __builtin_amdgcn_sched_barrier(0);
     }
   };
 
@@ -197,7 +250,7 @@ __global__ void __launch_bounds__(64 * NW, 1)
   if (ntiles > 0) {
     if (slot_lane) slots[0][lane] = slot_ok(t_begin, slot_raw(t_begin));
     __syncthreads();
-    issue(0, tiles[0]);
+    issue(0, 0);
   }
   int nxt = slot_lane && ntiles > 1 ? slot_raw(t_begin + kTile) : -1;
 #pragma unroll
@@ -220,7 +273,7 @@ __global__ void __launch_bounds__(64 * NW, 1)
       __builtin_amdgcn_s_waitcnt(0x70 | 0xF00);   // vmcnt(0)
       if (slot_lane && i + 1 < ntiles) slots[(i + 1) % 3][lane] = slot_ok(t_begin + (i + 1) * kTile, nxt);
       __syncthreads();
-      if (i + 1 < ntiles) issue((i + 1) % 3, tiles[(i + 1) & 1]);
+      if (i + 1 < ntiles) issue((i + 1) % 3, (i + 1) & 1);
       if (slot_lane && i + 2 < ntiles) nxt = slot_raw(t_begin + (i + 2) * kTile);
       compute(i % 3, tiles[i & 1]);
     }
@@ -239,41 +292,42 @@ __global__ void __launch_bounds__(64 * NW, 1)
 
 // out[b, h, :] and lse[b, h] from the spans' partials. grid (H, B), 128 threads.
 // KG = spans whose loads are in flight together (8 for up to 8 spans, else 32).
+// One pass: a group's maxima, sums and outputs are loaded together, and the
+// running sums are rescaled when a group raises the maximum.
 template <int kG>
 __global__ void __launch_bounds__(128)
     attn_merge_kernel(const float* __restrict__ part_o, const float2* __restrict__ part_ml, int H, int nsp,
                       float* __restrict__ out, float* __restrict__ lse) {
   const int h = blockIdx.x, b = blockIdx.y;
-  // Every load below is clamped and unguarded, so a group's loads all issue
-  // before the first wait; spans past the end are masked in arithmetic.
-  float mx = -__builtin_inff();
+  float mx = -__builtin_inff(), den = 0.f;
+  f32x4_t o = f32x4_t{0.f, 0.f, 0.f, 0.f};
   for (int s0 = 0; s0 < nsp; s0 += kG) {
+    // every load is clamped and unguarded, so all of a group's loads issue
+    // before the first wait; spans past the end are masked in arithmetic
+    f32x4_t v[kG];
     float2 ml[kG];
 #pragma unroll
-    for (int j = 0; j < kG; ++j) ml[j] = part_ml[((size_t)b * nsp + min(s0 + j, nsp - 1)) * H + h];
-#pragma unroll
-    for (int j = 0; j < kG; ++j) mx = fmaxf(mx, ml[j].x);          // clamped repeats change nothing
-  }
-  float den = 0.f;
-  f32x4_t o = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  if (mx != -__builtin_inff()) {
-    for (int s0 = 0; s0 < nsp; s0 += kG) {
-      f32x4_t v[kG];
-      float2 ml[kG];
-#pragma unroll
-      for (int j = 0; j < kG; ++j) {
-        const size_t sj = (size_t)b * nsp + min(s0 + j, nsp - 1);
-        v[j] = *reinterpret_cast<const f32x4_t*>(part_o + (sj * H + h) * kValV + 4 * threadIdx.x);
-        ml[j] = part_ml[sj * H + h];
-      }
-#pragma unroll
-      for (int j = 0; j < kG; ++j) {
-        const float wgt = (s0 + j < nsp) ? exp2f(ml[j].x - mx) : 0.f;   // 0 also for a span that saw nothing
-        den += wgt * ml[j].y;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) o[e] += wgt * v[j][e];
-      }
+    for (int j = 0; j < kG; ++j) {
+      const size_t sj = (size_t)b * nsp + min(s0 + j, nsp - 1);
+      v[j] = *reinterpret_cast<const f32x4_t*>(part_o + (sj * H + h) * kValV + 4 * threadIdx.x);
+      ml[j] = part_ml[sj * H + h];
     }
+    float gmx = mx;
+#pragma unroll
+    for (int j = 0; j < kG; ++j) gmx = fmaxf(gmx, ml[j].x);   // clamped repeats change nothing
+    if (gmx == -__builtin_inff()) continue;                  // nothing attended so far
+    const float r = exp2f(mx - gmx);                          // 0 while mx is -inf (den, o are 0)
+    den *= r;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) o[e] *= r;
+#pragma unroll
+    for (int j = 0; j < kG; ++j) {
+      const float wgt = (s0 + j < nsp) ? exp2f(ml[j].x - gmx) : 0.f;   // 0 also for a span that saw nothing
+      den += wgt * ml[j].y;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) o[e] += wgt * v[j][e];
+    }
+    mx = gmx;
   }
   const float inv = den > 0.f ? 1.f / den : 0.f;
 #pragma unroll
@@ -285,11 +339,13 @@ __global__ void __launch_bounds__(128)
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+// Spans of whole 32-token tiles, about 256 workgroups: one span per CU's
+// worth of sequences (ceil(256 / B) per sequence), but at least two tiles
+// per span, so that few sequences do not end up with one-tile spans whose
+// partials cost more than their rows.
 int spans_for(int B, int k) {
-  // about one workgroup per CU over 256 CUs (a workgroup of 8 waves holds a
-  // CU's registers), spans of whole 32-token tiles
   const int tiles = (k + kTile - 1) / kTile;
-  int nsp = (256 + B - 1) / B;
+  int nsp = std::min((256 + B - 1) / B, std::max(1, tiles / 2));
   nsp = std::max(1, std::min(nsp, tiles));
   const int per = (tiles + nsp - 1) / nsp;
   return (tiles + per - 1) / per;
@@ -299,6 +355,18 @@ int span_tokens(int B, int k) {
   const int tiles = (k + kTile - 1) / kTile;
   const int nsp = spans_for(B, k);
   return ((tiles + nsp - 1) / nsp) * kTile;
+}
+
+// Head groups per span: when spans x sequences leave CUs without a
+// workgroup, the heads of a span are split over up to 4 workgroups (a
+// divisor of H / 16), which read the span's rows from one XCD's L2. Measured
+// at 128 heads x 2048 rows: one sequence 22.9 us with 32 spans x 4 groups
+// against 27.5 with 64 x 2; four sequences 33.8 with 32 x 2 against 40.
+int head_groups_for(int B, int H, int nsp) {
+  const int groups = H / 16, want = std::max(1, 256 / (B * nsp));
+  for (int d = std::min(4, groups); d > 1; --d)
+    if (groups % d == 0 && d <= want) return d;
+  return 1;
 }
 
 }  // namespace
@@ -328,11 +396,7 @@ extern "C" int ech_sparse_attn(const void* q, const void* dev_cache, int32_t C, 
   const float scale2 = sm_scale * 1.4426950408889634f;
   const auto* qq = static_cast<const uint16_t*>(q);
   const auto* cc = static_cast<const uint4*>(dev_cache);
-  // With fewer workgroups than CUs (a few sequences), 128 heads go to two
-  // workgroups of 64 per span: twice the workgroups, rows read twice (one
-  // sequence: 36 -> 29 us). With more, one workgroup of 128 reads each row
-  // once.
-  const int hsplit = (H == 16 * kMaxWaves && B * nsp < 256) ? 2 : 1;
+  const int hsplit = head_groups_for(B, H, nsp);
   const dim3 grid(nsp * hsplit, B);
   switch (H / 16 / hsplit) {
 #define ECH_ATTN_CASE(W)                                                                                        \

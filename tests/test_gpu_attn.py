@@ -57,9 +57,9 @@ def _case(seed, B, H, C, k, pad_max, q_scale=1.0):
 
 @pytest.mark.parametrize('B,H,k,pad', [(3, 16, 37, 10), (2, 48, 64, 64), (4, 128, 2048, 1500), (1, 128, 5, 0),
                                        (5, 64, 300, 299),
-                                       # two workgroups of 64 heads per span (fewer workgroups than CUs),
-                                       # several spans and tiles each
-                                       (1, 128, 2048, 0), (2, 128, 1024, 100)])
+                                       # few sequences: the heads of a span split over 2-4 workgroups
+                                       # (3 for 48 heads above), several spans and tiles each
+                                       (1, 128, 2048, 0), (2, 128, 1024, 100), (4, 128, 2048, 7), (1, 64, 999, 3)])
 def test_random_against_oracle(B, H, k, pad):
     need_gpu()
     q, cache, sel = _case(B * 100 + H + k, B, H, 4000, k, pad)
