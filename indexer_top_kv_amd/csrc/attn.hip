@@ -6,9 +6,10 @@
 // bf16 values, all of them the key and the first 512 the value.
 //
 // Work split. A workgroup takes one (sequence, token span) and every head
-// (or half of 128 heads when there are fewer workgroups than CUs): each of
-// its waves owns 16 heads. The span's rows are gathered 32 tokens at a time
-// from HBM into LDS once for all heads, so each row crosses HBM once. Per
+// (or a quarter or half of them when there are fewer workgroups than CUs, the
+// head groups of a span on one XCD): each of its waves owns 16 heads. The
+// span's rows are gathered 32 tokens at a time from HBM into LDS once for all
+// of the workgroup's heads, so each row crosses HBM once. Per
 // 32-token tile and wave, on the matrix cores (v_mfma_f32_16x16x32_bf16):
 //   S^T[token][head] = K . Q^T      2 token tiles x 18 contraction steps
 //   O^T[col][head]  += V^T . P^T    32 column tiles, contraction = 32 tokens
