@@ -14,10 +14,11 @@
 // and appear in the early miss list, while later sequences are still being
 // scored, and a copier launch on another stream moves their rows meanwhile.
 //
-//   pins    (min(e1-e0, 64) workgroups) only slots the allocation can reach
-//           need their pin status, so the ring is taken in windows of 16384
-//           positions from the head: each workgroup finds its sequence's
-//           tokens in the window (slot2tok), scores them with the scores
+//   pins    (min(e1-e0, 64) x 4 workgroups) only slots the allocation can
+//           reach need their pin status, so the ring is taken in windows of
+//           32768 positions from the head, a quarter per workgroup: each
+//           workgroup finds its sequence's tokens in its quarter (slot2tok),
+//           scores them with the scores
 //           kernel's own tile arithmetic (decode.hpp / score.hpp: the same bit
 //           patterns) and pins those above theta (slot_pin = epoch); the
 //           workgroups then agree, through two counters, whether the windows
@@ -81,8 +82,10 @@ constexpr int kMaxCap = 4096;
 constexpr int kMaxB = 1024;
 constexpr int kMaxAlloc = 64;            // alloc workgroups at most
 constexpr int kCopyUnroll = 8;           // 16-byte pieces per thread per copied group
-constexpr int kPinWin = 16384;           // ring positions per window of the pins kernel
-constexpr int kMaxPinWg = 64;            // pins workgroups at most
+constexpr int kPinPart = 8192;           // ring positions per pins workgroup and window
+constexpr int kPinParts = 4;             // pins workgroups per early sequence (parts of a window)
+constexpr int kPinWin = kPinPart * kPinParts;   // ring positions per window of the pins kernel
+constexpr int kMaxPinWg = 64;            // early sequences the pins grid covers at once
 constexpr int kRankSlice = kT * 16;      // ring positions per slice of a rank workgroup
 constexpr int kRankWg = 16;              // rank workgroups
 
@@ -184,11 +187,13 @@ __device__ __forceinline__ bool spin_until(Load load, Pred pred, int32_t* ctr, u
 }
 
 // ------------------------------------------------------------------ pins
-// grid (min(e1 - e0, kMaxPinWg)); workgroup j handles the early sequences
-// e0 + j, e0 + j + grid, ... Every workgroup takes part in every window's
-// count (two counters that only grow, so nothing is cleared between
-// windows); every workgroup reads the same totals after a window and so takes
-// the same decision.
+// grid (min(e1 - e0, kMaxPinWg), kPinParts); workgroup (j, part) handles
+// part `part` (kPinPart positions) of every window for the early sequences
+// e0 + j, e0 + j + gridDim.x, ... A window covers twice the early demand
+// bound of a full batch, so one window normally suffices. Every workgroup
+// takes part in every window's count (two counters that only grow, so
+// nothing is cleared between windows); every workgroup reads the same totals
+// after a window and so takes the same decision.
 constexpr int kPinBatch = 4;
 
 __device__ int pin_sequence_window(const uint16_t* __restrict__ q, const float* __restrict__ w,
@@ -196,8 +201,9 @@ __device__ int pin_sequence_window(const uint16_t* __restrict__ q, const float* 
                                    int len, float th, const int32_t* __restrict__ slot2tok, int32_t C, int head, int p0,
                                    int wsz, int ep, int32_t* __restrict__ slot_pin, int* s_pos, int* scr) {
   const int tid = threadIdx.x;
-  // the window's slots holding a token of sequence b
-  constexpr int kU = kPinWin / kT;
+  // the part's slots holding a token of sequence b
+  constexpr int kU = kPinPart / kT;
+  static_assert(kU % 32 == 0, "whole mask words");
   int n = 0;
   uint32_t mine[kU / 32];
 #pragma unroll
@@ -287,19 +293,20 @@ __global__ __launch_bounds__(kT) void fused_pins_kernel(const uint16_t* __restri
                                                         const int32_t* __restrict__ slot2tok, int32_t C,
                                                         int32_t* __restrict__ slot_pin, int32_t* __restrict__ miss_early,
                                                         int32_t M_early, int32_t* ctr, FWs ws) {
-  __shared__ int s_pos[kPinWin];
+  __shared__ int s_pos[kPinPart];
   __shared__ int scr[kT / 64];
   __shared__ int s_tot;
-  const int tid = threadIdx.x, j = blockIdx.x, nwg = gridDim.x;
+  const int tid = threadIdx.x, j = blockIdx.x, part = blockIdx.y;
+  const int lid = blockIdx.y * gridDim.x + blockIdx.x, nwg = gridDim.x * gridDim.y;
   const int ep = ctr[ECH_CTR_EPOCH] + 1;
   int head = ctr[ECH_CTR_HEAD];
   if (head < 0 || head >= C) head = 0;   // only a corrupted state; keeps every slot index in range
   // the launch starts from empty lists and cleared control words
-  for (int i = j * kT + tid; i < 2 * M_early; i += nwg * kT) miss_early[i] = -1;
-  for (int i = j * kT + tid; i < M_early; i += nwg * kT) ws.freelist[i] = 0;
-  for (int b = e0 + j * kT + tid; b < e1; b += nwg * kT) ws.lb[b] = 0;
-  for (int i = j * kT + tid; i < (C + kRankSlice - 1) / kRankSlice; i += nwg * kT) ws.rlb[i] = 0;
-  if (j == 0 && tid == 0) {
+  for (int i = lid * kT + tid; i < 2 * M_early; i += nwg * kT) miss_early[i] = -1;
+  for (int i = lid * kT + tid; i < M_early; i += nwg * kT) ws.freelist[i] = 0;
+  for (int b = e0 + lid * kT + tid; b < e1; b += nwg * kT) ws.lb[b] = 0;
+  for (int i = lid * kT + tid; i < (C + kRankSlice - 1) / kRankSlice; i += nwg * kT) ws.rlb[i] = 0;
+  if (lid == 0 && tid == 0) {
     Ctl* cl = ws.ctl;
     cl->next_group = 0;
     cl->c_done = 0;
@@ -320,11 +327,12 @@ __global__ __launch_bounds__(kT) void fused_pins_kernel(const uint16_t* __restri
   const u64 t0 = wall_clock64();
   int covered = 0;
   for (int win = 0;; ++win) {   // block-uniform
-    const int p0 = win * kPinWin;
-    if (p0 >= C) break;
-    const int wsz = min(kPinWin, C - p0);
+    const int w0 = win * kPinWin;
+    if (w0 >= C) break;
+    const int p0 = w0 + part * kPinPart;
+    const int wsz = max(0, min(kPinPart, C - p0));
     int pinned = 0;
-    for (int b = e0 + j; b < e1; b += nwg) {
+    for (int b = e0 + j; b < e1 && wsz > 0; b += gridDim.x) {
       const float th = theta[b];
       if (th != th) continue;
       pinned += pin_sequence_window(q, w, kc, ksc, b, tok0[b], lens[b], th, slot2tok, C, head, p0, wsz, ep, slot_pin,
@@ -345,7 +353,7 @@ __global__ __launch_bounds__(kT) void fused_pins_kernel(const uint16_t* __restri
       s_tot = ld_dev(&ws.ctl->pin_total);
     }
     __syncthreads();
-    covered += wsz;
+    covered += min(kPinWin, C - w0);
     const int enough = covered - s_tot >= M_early;
     __syncthreads();   // s_tot is rewritten after the next window
     if (enough) break;
@@ -945,7 +953,7 @@ extern "C" int ech_index_logits_early(const void* q, const float* w, const void*
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   const uint16_t* qq = static_cast<const uint16_t*>(q);
   const uint8_t* kk = static_cast<const uint8_t*>(kcache);
-  hipLaunchKernelGGL(fused_pins_kernel, dim3(std::min(e1 - e0, kMaxPinWg)), dim3(kT), 0, s, qq, w, kk, kscale,
+  hipLaunchKernelGGL(fused_pins_kernel, dim3(std::min(e1 - e0, kMaxPinWg), kPinParts), dim3(kT), 0, s, qq, w, kk, kscale,
                      row_tok0, row_len, theta, e0, e1, slot2tok, C, slot_pin, miss_early, M_early, ctr, fw);
   ECH_LAUNCH_CHECK();
   FusedArgs a;
