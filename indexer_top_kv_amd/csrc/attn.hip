@@ -7,9 +7,10 @@
 //
 // Work split. A workgroup takes one (sequence, token span) and every head
 // (or a quarter or half of them when there are fewer workgroups than CUs, the
-// head groups of a span on one XCD): each of its waves owns 16 heads. The
-// span's rows are gathered 32 tokens at a time from HBM into LDS once for all
-// of the workgroup's heads, so each row crosses HBM once. Per
+// head groups of a span on one XCD): each of its waves owns 16 heads of one
+// token lane. The span's rows are gathered 32 tokens (one tile per lane) at a
+// time from HBM into LDS once for all of the workgroup's heads, so each row
+// crosses HBM once. Per
 // 32-token tile and wave, on the matrix cores (v_mfma_f32_16x16x32_bf16):
 //   S^T[token][head] = K . Q^T      2 token tiles x 18 contraction steps
 //   O^T[col][head]  += V^T . P^T    32 column tiles, contraction = 32 tokens
@@ -22,7 +23,8 @@
 // belongs to its head). Scores are kept in the base-2 domain.
 //
 // Spans are merged by a second kernel from per-span (max, sum, unnormalised
-// output) partials in the workspace.
+// output) partials in the workspace; two token lanes of a workgroup are
+// merged in LDS before their span's partial is written.
 #include <algorithm>
 
 #include "common.hpp"
@@ -91,16 +93,25 @@ __device__ __forceinline__ bf16x8_t tr_pair(const uint8_t* p0, const uint8_t* p1
   return __builtin_bit_cast(bf16x8_t, v);
 }
 
-// grid (spans x head groups, B), block 64 * NW threads; NS sets of 16 heads per wave.
-template <int NW, int NS>
-__global__ void __launch_bounds__(64 * NW, 1)
+// grid (spans x head groups, B), block 64 * NH * TL threads: NH waves of 16
+// heads for each of TL token lanes. With TL = 2 a step brings two tiles into
+// LDS and the two waves of a head set take one tile each, with a softmax
+// state of their own, merged in LDS at the end: half the spans (and the
+// partials the merge reads) for the same waves per CU.
+template <int NH, int TL>
+__global__ void __launch_bounds__(64 * NH * TL, 1)
     attn_span_kernel(const uint16_t* __restrict__ q, const uint4* __restrict__ cache, int C,
                        const int32_t* __restrict__ sel_slot, int H, int k, int span, float scale2,
                        float* __restrict__ part_o, float2* __restrict__ part_ml) {
-  __shared__ __align__(16) uint8_t tiles[2][kBuf2];
-  __shared__ int slots[3][kTile];   // slot id of each token of a tile, -1: nothing to attend
-  constexpr int kJ = (kInstr2 + NW - 1) / NW;   // load instructions per wave per tile
-  const int hsplit = H / (16 * NS * NW);
+  constexpr int NS = 1;
+  constexpr int NW = NH * TL;
+  constexpr int kStep = TL * kTile;                    // tokens per step
+  constexpr int kInstrS = (TL * kPos2 + 63) / 64;      // load instructions per step
+  static_assert(kStep <= 64, "one slot id per lane of wave 0");
+  __shared__ __align__(16) uint8_t tiles[2][TL * kBuf2];
+  __shared__ int slots[3][kStep];   // slot id of each token of a step, -1: nothing to attend
+  constexpr int kJ = (kInstrS + NW - 1) / NW;   // load instructions per wave per step
+  const int hsplit = H / (16 * NH);
   const int nsp = gridDim.x / hsplit;
   // The head groups of one span run on one XCD, next to each other in
   // dispatch order (workgroups go to the XCDs round robin), so that the
@@ -110,11 +121,13 @@ __global__ void __launch_bounds__(64 * NW, 1)
   if (hsplit > 1 && nwg % (8 * hsplit) == 0) wg = (wg % 8) * (nwg / 8) + wg / 8;
   const int hh = wg % hsplit, b = wg / (hsplit * nsp), sp = (wg / hsplit) % nsp;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, col = lane & 15, grp = lane >> 4;
-  const int h0 = hh * (16 * NS * NW) + wave * 16 * NS + col;   // head set hs: h0 + 16 hs
+  const int wvu = __builtin_amdgcn_readfirstlane(wave);
+  const int hw = wvu % NH, tl = wvu / NH;             // head set and token lane of this wave
+  const int h0 = hh * (16 * NH) + hw * 16 + col;
   const int32_t* sel = sel_slot + (size_t)b * k;
   const int t_begin = sp * span, t_end = min(k, t_begin + span);
-  const int ntiles = t_end > t_begin ? (t_end - t_begin + kTile - 1) / kTile : 0;
-  const bool slot_lane = wave == 0 && lane < kTile;   // the lanes that fetch slot ids
+  const int nsteps = t_end > t_begin ? (t_end - t_begin + kStep - 1) / kStep : 0;
+  const bool slot_lane = wave == 0 && lane < kStep;   // the lanes that fetch slot ids
 
   bf16x8_t qf[NS][kKs];   // Q^T fragments: head h0 + 16 hs, dims 32 s + 8 grp .. +8
   f32x4_t acc[NS][kCt];
@@ -133,13 +146,13 @@ __global__ void __launch_bounds__(64 * NW, 1)
     asm volatile("" : "+v"(ln));
     const int wv = __builtin_amdgcn_readfirstlane(wave);
     const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(ECH_ATTN_LDS(&tiles[0][0]))) +
-                          static_cast<uint32_t>(buf * kBuf2);
+                          static_cast<uint32_t>(buf * TL * kBuf2);
 #pragma unroll
     for (int j = 0; j < kJ; ++j) {
       const int ins = j * NW + wv;
       const int p = ins * 64 + ln;
       const int t = p / kP2, c = p - t * kP2;
-      if (ins < kInstr2 && p < kPos2 && c < kChunks) {
+      if (ins < kInstrS && p < TL * kPos2 && c < kChunks) {
         const int sl = slots[si][t];
         const uint4* src = cache + (size_t)max(sl, 0) * kChunks + c;
         const uint32_t lds = lds0 + static_cast<uint32_t>(ins * 1024);
@@ -148,7 +161,7 @@ __global__ void __launch_bounds__(64 * NW, 1)
     }
   };
   // the scores, online softmax and value product of the tile in cur
-  auto compute = [&](int si, const uint8_t* cur) {
+  auto compute = [&](const int* sid, const uint8_t* cur) {
     f32x4_t st[2][NS];   // [16-token half][head set]
 #pragma unroll
     for (int sub = 0; sub < 2; ++sub)
@@ -181,7 +194,7 @@ __global__ void __launch_bounds__(64 * NW, 1)
     }
     bool ok[8];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) ok[j] = slots[si][(j < 4) ? (4 * grp + j) : (16 + 4 * grp + j - 4)] >= 0;
+    for (int j = 0; j < 8; ++j) ok[j] = sid[(j < 4) ? (4 * grp + j) : (16 + 4 * grp + j - 4)] >= 0;
     bf16x8_t pb[NS];
     float alpha[NS];
     bool grow[NS];
@@ -246,14 +259,14 @@ __global__ void __launch_bounds__(64 * NW, 1)
     }
   };
 
-  // The first tile's slot ids, then its loads, go out before the query
+  // The first step's slot ids, then its loads, go out before the query
   // fragments (a wait for the slot ids would otherwise wait for them too).
-  if (ntiles > 0) {
+  if (nsteps > 0) {
     if (slot_lane) slots[0][lane] = slot_ok(t_begin, slot_raw(t_begin));
     __syncthreads();
     issue(0, 0);
   }
-  int nxt = slot_lane && ntiles > 1 ? slot_raw(t_begin + kTile) : -1;
+  int nxt = slot_lane && nsteps > 1 ? slot_raw(t_begin + kStep) : -1;
 #pragma unroll
   for (int hs = 0; hs < NS; ++hs) {
     const uint8_t* qrow = reinterpret_cast<const uint8_t*>(q + ((size_t)b * H + h0 + 16 * hs) * kRowV);
@@ -264,19 +277,50 @@ __global__ void __launch_bounds__(64 * NW, 1)
     m[hs] = -__builtin_inff();
     l[hs] = 0.f;
   }
-  if (ntiles > 0) {
-    // one tile: its loads have landed (every wave waited, then the barrier),
-    // the next tile's slot ids are published and its loads issued, then the
-    // products of this tile run over them
-    for (int i = 0; i < ntiles; ++i) {
+  if (nsteps > 0) {
+    // one step: its loads have landed (every wave waited, then the barrier),
+    // the next step's slot ids are published and its loads issued, then the
+    // products of this wave's tile run over them
+    for (int i = 0; i < nsteps; ++i) {
       // every load of this wave (the builtin form, so that the compiler knows
       // the query fragments and slot ids are in as well)
       __builtin_amdgcn_s_waitcnt(0x70 | 0xF00);   // vmcnt(0)
-      if (slot_lane && i + 1 < ntiles) slots[(i + 1) % 3][lane] = slot_ok(t_begin + (i + 1) * kTile, nxt);
+      if (slot_lane && i + 1 < nsteps) slots[(i + 1) % 3][lane] = slot_ok(t_begin + (i + 1) * kStep, nxt);
       __syncthreads();
-      if (i + 1 < ntiles) issue((i + 1) % 3, (i + 1) & 1);
-      if (slot_lane && i + 2 < ntiles) nxt = slot_raw(t_begin + (i + 2) * kTile);
-      compute(i % 3, tiles[i & 1]);
+      if (i + 1 < nsteps) issue((i + 1) % 3, (i + 1) & 1);
+      if (slot_lane && i + 2 < nsteps) nxt = slot_raw(t_begin + (i + 2) * kStep);
+      // a token lane past the span's end has nothing to add (a wave-uniform test)
+      if (TL == 1 || t_begin + i * kStep + tl * kTile < t_end)
+        compute(&slots[i % 3][tl * kTile], &tiles[i & 1][tl * kBuf2]);
+    }
+  }
+
+  if constexpr (TL == 2) {
+    // The second token lane's state goes through LDS (the tile buffers, free
+    // once every wave has left the loop) to the first, which merges it.
+    static_assert(NH * (kCt * 64 * 16 + 64 * 8) <= 2 * TL * kBuf2, "merge state fits the tile buffers");
+    f32x4_t* xo = reinterpret_cast<f32x4_t*>(&tiles[0][0]) + hw * kCt * 64 + lane;
+    float2* xml = reinterpret_cast<float2*>(&tiles[0][0] + NH * kCt * 64 * 16) + hw * 64 + lane;
+    __syncthreads();
+    if (tl == 1) {
+#pragma unroll
+      for (int c = 0; c < kCt; ++c) xo[c * 64] = acc[0][c];
+      *xml = make_float2(m[0], l[0]);
+    }
+    __syncthreads();
+    if (tl == 1) return;
+    const float2 o = *xml;
+    const float mn = fmaxf(m[0], o.x);
+    if (mn != -__builtin_inff()) {
+      const float ra = exp2f(m[0] - mn), rb = exp2f(o.x - mn);   // 0 for a lane that saw nothing
+      l[0] = l[0] * ra + o.y * rb;
+      m[0] = mn;
+#pragma unroll
+      for (int c = 0; c < kCt; ++c) {
+        const f32x4_t x = xo[c * 64];
+#pragma unroll
+        for (int v = 0; v < 4; ++v) acc[0][c][v] = acc[0][c][v] * ra + x[v] * rb;
+      }
     }
   }
 
@@ -292,7 +336,8 @@ __global__ void __launch_bounds__(64 * NW, 1)
 }
 
 // out[b, h, :] and lse[b, h] from the spans' partials. grid (H, B), 128 threads.
-// KG = spans whose loads are in flight together (8 for up to 8 spans, else 32).
+// KG = spans whose loads are in flight together (8 for up to 8 spans, 16 for up
+// to 16, else 32).
 // One pass: a group's maxima, sums and outputs are loaded together, and the
 // running sums are rescaled when a group raises the maximum.
 template <int kG>
@@ -340,41 +385,62 @@ __global__ void __launch_bounds__(128)
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+// The launch's shape: spans per sequence, tokens per span, head groups per
+// span, token lanes per workgroup.
+struct Plan {
+  int nsp, span, hsplit, tl;
+};
+
 // Spans of whole 32-token tiles, about 256 workgroups: one span per CU's
 // worth of sequences (ceil(256 / B) per sequence), but at least two tiles
 // per span, so that few sequences do not end up with one-tile spans whose
-// partials cost more than their rows.
-int spans_for(int B, int k) {
-  const int tiles = (k + kTile - 1) / kTile;
+// partials cost more than their rows. When spans x sequences leave CUs
+// without a workgroup, the heads of a span are split over up to 4
+// workgroups (a divisor of H / 16), which read the span's rows from one
+// XCD's L2. Then two token lanes where a workgroup has room for them: eight
+// waves of 16 heads become two head groups of four waves with two lanes each
+// (as many workgroups, half the spans and partials), and four waves or fewer
+// take a second lane (half the spans when that still leaves a workgroup per
+// CU, else twice the waves). Measured at 128 heads x 2048 rows (span + merge,
+// rocprofv3): 32 sequences 39.8 + 12.2 -> 41.0 + 7.7 us, 16 sequences 29.0 +
+// 15.6 -> 30.8 + 6.8 us; one sequence 23.8 -> 22.9 us, four 34.4 -> 33.4 us.
+Plan plan_for(int B, int H, int k) {
+  const int tiles = (k + kTile - 1) / kTile, groups = H / 16;
   int nsp = std::min((256 + B - 1) / B, std::max(1, tiles / 2));
   nsp = std::max(1, std::min(nsp, tiles));
-  const int per = (tiles + nsp - 1) / nsp;
-  return (tiles + per - 1) / per;
-}
-
-int span_tokens(int B, int k) {
-  const int tiles = (k + kTile - 1) / kTile;
-  const int nsp = spans_for(B, k);
-  return ((tiles + nsp - 1) / nsp) * kTile;
-}
-
-// Head groups per span: when spans x sequences leave CUs without a
-// workgroup, the heads of a span are split over up to 4 workgroups (a
-// divisor of H / 16), which read the span's rows from one XCD's L2. Measured
-// at 128 heads x 2048 rows: one sequence 22.9 us with 32 spans x 4 groups
-// against 27.5 with 64 x 2; four sequences 33.8 with 32 x 2 against 40.
-int head_groups_for(int B, int H, int nsp) {
-  const int groups = H / 16, want = std::max(1, 256 / (B * nsp));
+  int per = (tiles + nsp - 1) / nsp;
+  nsp = (tiles + per - 1) / per;
+  int hsplit = 1;
+  const int want = std::max(1, 256 / (B * nsp));
   for (int d = std::min(4, groups); d > 1; --d)
-    if (groups % d == 0 && d <= want) return d;
-  return 1;
+    if (groups % d == 0 && d <= want) {
+      hsplit = d;
+      break;
+    }
+  int tl = 1;
+  const int nh = groups / hsplit;
+  if (per >= 2 && nh == kMaxWaves) {
+    tl = 2;
+    hsplit *= 2;
+    nsp = (nsp + 1) / 2;
+  } else if (per >= 2 && 2 * nh <= kMaxWaves) {
+    tl = 2;
+    if (B * nsp * hsplit >= 256) nsp = (nsp + 1) / 2;
+  }
+  if (tl == 2) {
+    // whole steps of two tiles per span
+    per = (tiles + nsp - 1) / nsp;
+    per += per & 1;
+    nsp = (tiles + per - 1) / per;
+  }
+  return Plan{nsp, per * kTile, hsplit, tl};
 }
 
 }  // namespace
 
 extern "C" size_t ech_sparse_attn_ws_bytes(int B, int H, int k) {
   if (B < 1 || H < 16 || H > 16 * kMaxWaves || H % 16 || k < 1 || k > 65536) return 0;
-  const size_t nsp = (size_t)spans_for(B, k);
+  const size_t nsp = (size_t)plan_for(B, H, k).nsp;
   const size_t o = nsp * B * H * kValV * sizeof(float);
   return ((o + 255) & ~(size_t)255) + nsp * B * H * sizeof(float2);
 }
@@ -389,7 +455,9 @@ extern "C" int ech_sparse_attn(const void* q, const void* dev_cache, int32_t C, 
       (reinterpret_cast<uintptr_t>(ws) & 255u))
     return ECH_EINVAL;
   if (ws_bytes < ech_sparse_attn_ws_bytes(B, H, k)) return ECH_EINVAL;
-  const int nsp = spans_for(B, k), span = span_tokens(B, k);
+  const Plan pl = plan_for(B, H, k);
+  const int nsp = pl.nsp, span = pl.span, hsplit = pl.hsplit;
+  if (H % (16 * hsplit) || (H / 16 / hsplit) * pl.tl > kMaxWaves) return ECH_EINVAL;
   const size_t o = (size_t)nsp * B * H * kValV * sizeof(float);
   float* part_o = static_cast<float*>(ws);
   float2* part_ml = reinterpret_cast<float2*>(static_cast<char*>(ws) + ((o + 255) & ~(size_t)255));
@@ -397,22 +465,25 @@ extern "C" int ech_sparse_attn(const void* q, const void* dev_cache, int32_t C, 
   const float scale2 = sm_scale * 1.4426950408889634f;
   const auto* qq = static_cast<const uint16_t*>(q);
   const auto* cc = static_cast<const uint4*>(dev_cache);
-  const int hsplit = head_groups_for(B, H, nsp);
   const dim3 grid(nsp * hsplit, B);
-  switch (H / 16 / hsplit) {
-#define ECH_ATTN_CASE(W)                                                                                        \
-  case W:                                                                                                       \
-    hipLaunchKernelGGL((attn_span_kernel<W, 1>), grid, dim3(64 * W), 0, s, qq, cc, C, sel_slot, H, k, span,     \
+  switch ((H / 16 / hsplit) * 16 + pl.tl) {
+#define ECH_ATTN_CASE(W, T)                                                                                     \
+  case W * 16 + T:                                                                                              \
+    hipLaunchKernelGGL((attn_span_kernel<W, T>), grid, dim3(64 * W * T), 0, s, qq, cc, C, sel_slot, H, k, span, \
                        scale2, part_o, part_ml);                                                                \
     break;
-    ECH_ATTN_CASE(1)
-    ECH_ATTN_CASE(2)
-    ECH_ATTN_CASE(3)
-    ECH_ATTN_CASE(4)
-    ECH_ATTN_CASE(5)
-    ECH_ATTN_CASE(6)
-    ECH_ATTN_CASE(7)
-    ECH_ATTN_CASE(8)
+    ECH_ATTN_CASE(1, 1)
+    ECH_ATTN_CASE(2, 1)
+    ECH_ATTN_CASE(3, 1)
+    ECH_ATTN_CASE(4, 1)
+    ECH_ATTN_CASE(5, 1)
+    ECH_ATTN_CASE(6, 1)
+    ECH_ATTN_CASE(7, 1)
+    ECH_ATTN_CASE(8, 1)
+    ECH_ATTN_CASE(1, 2)
+    ECH_ATTN_CASE(2, 2)
+    ECH_ATTN_CASE(3, 2)
+    ECH_ATTN_CASE(4, 2)
 #undef ECH_ATTN_CASE
     default:
       return ECH_EINVAL;
@@ -420,6 +491,8 @@ extern "C" int ech_sparse_attn(const void* q, const void* dev_cache, int32_t C, 
   ECH_LAUNCH_CHECK();
   if (nsp <= 8)
     hipLaunchKernelGGL(attn_merge_kernel<8>, dim3(H, B), dim3(kValV / 4), 0, s, part_o, part_ml, H, nsp, out, lse);
+  else if (nsp <= 16)
+    hipLaunchKernelGGL(attn_merge_kernel<16>, dim3(H, B), dim3(kValV / 4), 0, s, part_o, part_ml, H, nsp, out, lse);
   else
     hipLaunchKernelGGL(attn_merge_kernel<32>, dim3(H, B), dim3(kValV / 4), 0, s, part_o, part_ml, H, nsp, out, lse);
   ECH_LAUNCH_CHECK();

@@ -59,7 +59,12 @@ def _case(seed, B, H, C, k, pad_max, q_scale=1.0):
                                        (5, 64, 300, 299),
                                        # few sequences: the heads of a span split over 2-4 workgroups
                                        # (3 for 48 heads above), several spans and tiles each
-                                       (1, 128, 2048, 0), (2, 128, 1024, 100), (4, 128, 2048, 7), (1, 64, 999, 3)])
+                                       (1, 128, 2048, 0), (2, 128, 1024, 100), (4, 128, 2048, 7), (1, 64, 999, 3),
+                                       # two token lanes per workgroup: 8 waves as 4 x 2 (16, 8 sequences),
+                                       # spans ending on one tile of a step (33 tiles), 7 waves (112 heads)
+                                       # with one lane
+                                       (16, 128, 2048, 40), (8, 128, 1056, 0), (32, 128, 1056, 31),
+                                       (3, 112, 700, 20)])
 def test_random_against_oracle(B, H, k, pad):
     need_gpu()
     q, cache, sel = _case(B * 100 + H + k, B, H, 4000, k, pad)
