@@ -336,8 +336,8 @@ __global__ void __launch_bounds__(64 * NH * TL, 1)
 }
 
 // out[b, h, :] and lse[b, h] from the spans' partials. grid (H, B), 128 threads.
-// KG = spans whose loads are in flight together (8 for up to 8 spans, 16 for up
-// to 16, else 32).
+// KG = spans whose loads are in flight together (the power of two from 2 to 32
+// that covers the spans, 32 beyond).
 // One pass: a group's maxima, sums and outputs are loaded together, and the
 // running sums are rescaled when a group raises the maximum.
 template <int kG>
@@ -489,12 +489,19 @@ extern "C" int ech_sparse_attn(const void* q, const void* dev_cache, int32_t C, 
       return ECH_EINVAL;
   }
   ECH_LAUNCH_CHECK();
-  if (nsp <= 8)
-    hipLaunchKernelGGL(attn_merge_kernel<8>, dim3(H, B), dim3(kValV / 4), 0, s, part_o, part_ml, H, nsp, out, lse);
+  // the merge loads up to kG spans at once: the power of two that covers nsp
+  // (clamped repeats past nsp would cost requests), at most 32
+  const dim3 mgrid(H, B), mblock(kValV / 4);
+  if (nsp <= 2)
+    hipLaunchKernelGGL(attn_merge_kernel<2>, mgrid, mblock, 0, s, part_o, part_ml, H, nsp, out, lse);
+  else if (nsp <= 4)
+    hipLaunchKernelGGL(attn_merge_kernel<4>, mgrid, mblock, 0, s, part_o, part_ml, H, nsp, out, lse);
+  else if (nsp <= 8)
+    hipLaunchKernelGGL(attn_merge_kernel<8>, mgrid, mblock, 0, s, part_o, part_ml, H, nsp, out, lse);
   else if (nsp <= 16)
-    hipLaunchKernelGGL(attn_merge_kernel<16>, dim3(H, B), dim3(kValV / 4), 0, s, part_o, part_ml, H, nsp, out, lse);
+    hipLaunchKernelGGL(attn_merge_kernel<16>, mgrid, mblock, 0, s, part_o, part_ml, H, nsp, out, lse);
   else
-    hipLaunchKernelGGL(attn_merge_kernel<32>, dim3(H, B), dim3(kValV / 4), 0, s, part_o, part_ml, H, nsp, out, lse);
+    hipLaunchKernelGGL(attn_merge_kernel<32>, mgrid, mblock, 0, s, part_o, part_ml, H, nsp, out, lse);
   ECH_LAUNCH_CHECK();
   return ECH_OK;
 }
