@@ -8,13 +8,14 @@ cache 260000 slots, host pool of 4.19M rows x 1152 B in pinned memory, q from
 an AR(1) process (rho 0.9). A step is one full pass of the path for the
 batch: indexer scores, exact top-k + threshold update, early fetch (second
 stream), final slot-map step and recall. Inputs are resident in HBM (and the
-pinned pool) before the timed region; W warm-up steps (the cold first step
-included) are untimed, then exactly K steps are timed between two device
-synchronisations.
+pinned pool) before the timed region; F fill steps (from the cold device
+cache: the first step misses every selected row, and the resident set takes
+about ten steps to settle) and W warm-up steps are untimed, then exactly K
+steps are timed between two device synchronisations.
 
 Prints one JSON line (stdout). Progress goes to stderr.
 
-  python bench.py [--steps K] [--warmup W] [--config NAME] [--no-cpu-baseline]
+  python bench.py [--steps K] [--warmup W] [--fill F] [--config NAME] [--no-cpu-baseline]
 """
 import argparse
 import hashlib
@@ -39,6 +40,9 @@ def parse():
     p.add_argument('--gpus', type=int, default=1)
     p.add_argument('--steps', type=int, default=30)
     p.add_argument('--warmup', type=int, default=2)
+    p.add_argument('--fill', type=int, default=8,
+                   help='decode: untimed steps before the warm-up ones, from the cold device cache until the '
+                        'resident set has converged (the steady state of a serving layer)')
     p.add_argument('--config', default='decode-32x128k-fp8')
     p.add_argument('--no-cpu-baseline', action='store_true')
     p.add_argument('--no-early', action='store_true', help='disable the early fetch (ablation)')
@@ -110,7 +114,8 @@ def bench_decode(args, wl):
     wk.host_rows(wl, out=pool.numpy().view(np.uint16))
     log(f'host pool {wl.P} rows x {wk.ROW_BYTES} B pinned in {time.time() - t:.1f}s')
     n_stage = 4                                       # extra eager steps for the stage breakdown
-    total_steps = args.warmup + args.steps + n_stage
+    pre = args.fill + args.warmup                # untimed steps before the timed ones
+    total_steps = pre + args.steps + n_stage
     qs = np.stack(list(wk.decode_queries(wl, total_steps)))
     kc, ks, wd = dev(keys), (dev(scale) if scale is not None else None), dev(w)
     qd = dev(qs)
@@ -119,11 +124,11 @@ def bench_decode(args, wl):
                         topk_first={'auto': None, 'on': True, 'off': False}[args.topk_first],
                         fused=False if (args.no_fused or args.no_early) else None)
     torch.cuda.synchronize()
-    log(f'chunks {layer.chunks}; warm-up {args.warmup} steps')
+    log(f'chunks {layer.chunks}; {args.fill} fill + {args.warmup} warm-up steps')
     if not args.eager:
         layer.capture()          # nothing runs; the warm-up steps are replays of the timed path
         torch.cuda.synchronize()
-    for s in range(args.warmup):
+    for s in range(pre):
         if args.eager:
             layer.step(qd[s])
         else:
@@ -135,9 +140,9 @@ def bench_decode(args, wl):
     t0 = time.perf_counter()
     for s in range(args.steps):
         if args.eager:
-            layer.step(qd[args.warmup + s])
+            layer.step(qd[pre + s])
         else:
-            layer.replay(qd[args.warmup + s])
+            layer.replay(qd[pre + s])
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     recalled = int(layer.state.ctr[4].item()) - recalled0
@@ -151,10 +156,10 @@ def bench_decode(args, wl):
     # Without the fused path this is the roofline kernel; with it, the same
     # stream alone, for comparison with the fused launch inside the step.
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    layer.logits_only(qd[args.warmup], stream=s0)
+    layer.logits_only(qd[pre], stream=s0)
     ev0.record(s0)
     for s in range(args.steps):
-        layer.logits_only(qd[args.warmup + s], stream=s0)
+        layer.logits_only(qd[pre + s], stream=s0)
     ev1.record(s0)
     torch.cuda.synchronize()
     logits_runs = [ev0.elapsed_time(ev1) / args.steps]
@@ -187,7 +192,7 @@ def bench_decode(args, wl):
     # step (beside the live copier), on its own stream.
     marks = {}
     for s in range(n_stage):
-        layer.step(qd[args.warmup + args.steps + s], marks)
+        layer.step(qd[pre + args.steps + s], marks)
     torch.cuda.synchronize()
 
     def avg_ms(name):
@@ -238,7 +243,7 @@ def bench_decode(args, wl):
 
         n_att = 2
         for s in range(n_att):
-            layer.step(qd[args.warmup + args.steps + s], on_chunk=consume)
+            layer.step(qd[pre + args.steps + s], on_chunk=consume)
         torch.cuda.synchronize()
         attn_us = sum(a.elapsed_time(b) for a, b in att_ev) / n_att * 1e3
         n_sel = int(sum(int(x.item()) for x in n_sel_c) / n_att)
@@ -293,6 +298,7 @@ def bench_decode(args, wl):
         'n_gpus': 1,
         'steps': args.steps,
         'warmup': args.warmup,
+        'fill_steps': args.fill,
         'ms_per_step': wall / args.steps * 1e3,
         'higher_is_better': True,
         'scaling': 'weak',
@@ -401,7 +407,8 @@ def bench_stack(args, wl):
     L, M = args.layers, args.micro_batches
     groups = sequence_groups(wl.B, M)
     C_m = wl.C // len(groups)
-    total_steps = args.warmup + args.steps
+    pre = args.fill + args.warmup                # untimed steps before the timed ones
+    total_steps = pre + args.steps
     layers, qs, pools = [], [], []
     ctx0 = None
     for l in range(L):
@@ -428,7 +435,7 @@ def bench_stack(args, wl):
     if not args.eager:
         stack.capture()          # nothing runs; the warm-up steps are replays of the timed path
     torch.cuda.synchronize()
-    for s in range(args.warmup):
+    for s in range(pre):
         (stack.step if args.eager else stack.replay)(step_q(s))
     torch.cuda.synchronize()
     rec0 = sum(int(d.state.ctr[4].item()) for r in layers for d in r)
@@ -437,7 +444,7 @@ def bench_stack(args, wl):
     log(f'timing {args.steps} steps of {L} layers x {len(groups)} micro-batches ({launch})')
     t0 = time.perf_counter()
     for s in range(args.steps):
-        (stack.step if args.eager else stack.replay)(step_q(args.warmup + s))
+        (stack.step if args.eager else stack.replay)(step_q(pre + s))
     t_host = time.perf_counter() - t0                  # host time to enqueue the K steps
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -454,7 +461,7 @@ def bench_stack(args, wl):
     for s in range(args.steps):
         for l in range(L):
             for m, (b0, b1) in enumerate(groups):
-                layers[l][m].logits_only(qs[l][args.warmup + s, b0:b1], stream=s0)
+                layers[l][m].logits_only(qs[l][pre + s, b0:b1], stream=s0)
     ev1.record(s0)
     torch.cuda.synchronize()
     layer_ms = ev0.elapsed_time(ev1) / (args.steps * L)
@@ -464,7 +471,7 @@ def bench_stack(args, wl):
                   f'slot-map step + recall per layer)',
         'value': tokens * L * args.steps / wall,
         'unit': 'tokens/s',
-        'n_gpus': 1, 'steps': args.steps, 'warmup': args.warmup,
+        'n_gpus': 1, 'steps': args.steps, 'warmup': args.warmup, 'fill_steps': args.fill,
         'ms_per_step': step_ms,
         'higher_is_better': True, 'scaling': 'weak', 'vs_baseline': None,
         'dtype': 'fp8-e4m3 keys, bf16 q, bf16 MFMA with fp32 accumulation' if wl.kdtype == 'fp8' else 'bf16',
