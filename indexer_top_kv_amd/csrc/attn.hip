@@ -81,7 +81,6 @@ __device__ __forceinline__ float lane_group_max(float x) {
 constexpr int kP2 = kKPitch / 16;            // 74 chunks per token row in LDS (two spare: banks)
 constexpr int kPos2 = kTile * kP2;           // 2368 chunk positions per tile
 constexpr int kBuf2 = kPos2 * 16;            // 37888 bytes per tile buffer
-constexpr int kInstr2 = (kPos2 + 63) / 64;   // 37 load instructions per tile
 
 typedef short v4s_t __attribute__((ext_vector_type(4)));
 
