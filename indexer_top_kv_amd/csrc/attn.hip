@@ -399,10 +399,12 @@ struct Plan {
 // XCD's L2. Then two token lanes where a workgroup has room for them: eight
 // waves of 16 heads become two head groups of four waves with two lanes each
 // (as many workgroups, half the spans and partials), and four waves or fewer
-// take a second lane (half the spans when that still leaves a workgroup per
-// CU, else twice the waves). Measured at 128 heads x 2048 rows (span + merge,
+// take a second lane: with a workgroup per CU already, half the spans and
+// twice the head groups (as many workgroups and waves, half the partials),
+// else twice the waves. Measured at 128 heads x 2048 rows (span + merge,
 // rocprofv3): 32 sequences 39.8 + 12.2 -> 41.0 + 7.7 us, 16 sequences 29.0 +
-// 15.6 -> 30.8 + 6.8 us; one sequence 23.8 -> 22.9 us, four 34.4 -> 33.4 us.
+// 15.6 -> 30.8 + 6.8 us; one sequence 23.8 -> 22.9 us; four 34.4 us one lane,
+// 30.8 with 2 head groups x 2 lanes, 28.5 with 4 x 2 (16 spans).
 Plan plan_for(int B, int H, int k) {
   const int tiles = (k + kTile - 1) / kTile, groups = H / 16;
   int nsp = std::min((256 + B - 1) / B, std::max(1, tiles / 2));
@@ -424,7 +426,10 @@ Plan plan_for(int B, int H, int k) {
     nsp = (nsp + 1) / 2;
   } else if (per >= 2 && 2 * nh <= kMaxWaves) {
     tl = 2;
-    if (B * nsp * hsplit >= 256) nsp = (nsp + 1) / 2;
+    if (B * nsp * hsplit >= 256) {
+      nsp = (nsp + 1) / 2;
+      if (nh % 2 == 0) hsplit *= 2;   // as many workgroups as before, as many waves each
+    }
   }
   if (tl == 2) {
     // whole steps of two tiles per span
