@@ -382,6 +382,71 @@ __global__ void __launch_bounds__(128)
     lse[(size_t)b * H + h] = den > 0.f ? (mx + log2f(den)) * 0.69314718055994531f : -__builtin_inff();
 }
 
+// The merge for many spans (a few sequences): grid (H, B, 4), 128 threads.
+// Workgroup z takes the value columns 128 z .. +127 of one (sequence, head);
+// thread t the four columns 4 (t % 32) .. +3 of them over the spans
+// t / 32, t / 32 + 4, ... (kPer of them, loads all in flight); the four span
+// subsets are combined through LDS. Four times the workgroups of the
+// one-group form, a quarter of the loads per thread.
+template <int kPer>
+__global__ void __launch_bounds__(128)
+    attn_merge_split_kernel(const float* __restrict__ part_o, const float2* __restrict__ part_ml, int H, int nsp,
+                            float* __restrict__ out, float* __restrict__ lse) {
+  __shared__ float s_mx[128], s_den[128];
+  __shared__ f32x4_t s_o[128];
+  const int h = blockIdx.x, b = blockIdx.y, quarter = blockIdx.z;
+  const int tid = threadIdx.x, quad = tid & 31, sub = tid >> 5;
+  const int c0 = quarter * 128 + 4 * quad;
+  f32x4_t v[kPer];
+  float2 ml[kPer];
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {   // clamped and unguarded: every load issues before the first wait
+    const size_t sj = (size_t)b * nsp + min(sub + 4 * j, nsp - 1);
+    v[j] = *reinterpret_cast<const f32x4_t*>(part_o + (sj * H + h) * kValV + c0);
+    ml[j] = part_ml[sj * H + h];
+  }
+  float mx = -__builtin_inff(), den = 0.f;
+  f32x4_t o = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int j = 0; j < kPer; ++j)
+    if (sub + 4 * j < nsp) mx = fmaxf(mx, ml[j].x);
+  if (mx != -__builtin_inff()) {
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+      const float wgt = (sub + 4 * j < nsp) ? exp2f(ml[j].x - mx) : 0.f;   // 0 also for a span that saw nothing
+      den += wgt * ml[j].y;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) o[e] += wgt * v[j][e];
+    }
+  }
+  s_mx[tid] = mx;
+  s_den[tid] = den;
+  s_o[tid] = o;
+  __syncthreads();
+  if (sub != 0) return;
+  float gmx = -__builtin_inff();
+#pragma unroll
+  for (int u = 0; u < 4; ++u) gmx = fmaxf(gmx, s_mx[quad + 32 * u]);
+  float gden = 0.f;
+  f32x4_t go = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  if (gmx != -__builtin_inff()) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const float r = exp2f(s_mx[quad + 32 * u] - gmx);   // 0 for a subset that saw nothing
+      gden += r * s_den[quad + 32 * u];
+      const f32x4_t x = s_o[quad + 32 * u];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) go[e] += r * x[e];
+    }
+  }
+  const float inv = gden > 0.f ? 1.f / gden : 0.f;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) go[e] *= inv;
+  *reinterpret_cast<f32x4_t*>(out + ((size_t)b * H + h) * kValV + c0) = go;
+  if (lse && quarter == 0 && quad == 0)
+    lse[(size_t)b * H + h] = gden > 0.f ? (gmx + log2f(gden)) * 0.69314718055994531f : -__builtin_inff();
+}
+
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 // The launch's shape: spans per sequence, tokens per span, head groups per
@@ -503,7 +568,9 @@ extern "C" int ech_sparse_attn(const void* q, const void* dev_cache, int32_t C, 
   else if (nsp <= 8)
     hipLaunchKernelGGL(attn_merge_kernel<8>, mgrid, mblock, 0, s, part_o, part_ml, H, nsp, out, lse);
   else if (nsp <= 16)
-    hipLaunchKernelGGL(attn_merge_kernel<16>, mgrid, mblock, 0, s, part_o, part_ml, H, nsp, out, lse);
+    hipLaunchKernelGGL(attn_merge_split_kernel<4>, dim3(H, B, 4), mblock, 0, s, part_o, part_ml, H, nsp, out, lse);
+  else if (nsp <= 32)
+    hipLaunchKernelGGL(attn_merge_split_kernel<8>, dim3(H, B, 4), mblock, 0, s, part_o, part_ml, H, nsp, out, lse);
   else
     hipLaunchKernelGGL(attn_merge_kernel<32>, mgrid, mblock, 0, s, part_o, part_ml, H, nsp, out, lse);
   ECH_LAUNCH_CHECK();
