@@ -335,8 +335,8 @@ __global__ void __launch_bounds__(64 * NH * TL, 1)
 }
 
 // out[b, h, :] and lse[b, h] from the spans' partials. grid (H, B), 128 threads.
-// KG = spans whose loads are in flight together (the power of two from 2 to 32
-// that covers the spans, 32 beyond).
+// KG = spans whose loads are in flight together (2, 4 or 8: the power of two
+// that covers the spans; 32 beyond 32 spans, whose merge loops over groups).
 // One pass: a group's maxima, sums and outputs are loaded together, and the
 // running sums are rescaled when a group raises the maximum.
 template <int kG>
