@@ -74,6 +74,17 @@ def test_random_against_oracle(B, H, k, pad):
     _check(o, l, ro, rl, f'B{B} H{H} k{k}')
 
 
+def test_many_spans_merged_in_groups():
+    """One sequence of 8192 selected rows: 64 spans, more than one merge group
+    of 32 (the other merge forms cover up to 32 spans)."""
+    need_gpu()
+    q, cache, sel = _case(7, 1, 32, 10000, 8192, 50)
+    scale = 1.0 / np.sqrt(192.0)
+    o, l = _run(dev(q), dev(cache), dev(sel), scale)
+    ro, rl = oracle.sparse_attention(q, cache, sel, scale)
+    _check(o, l, ro, rl, 'k8192')
+
+
 def test_peaked_and_flat_softmax():
     """Large scores (one token dominates) and a zero query (uniform weights)."""
     need_gpu()
