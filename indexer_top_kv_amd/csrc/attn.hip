@@ -335,8 +335,8 @@ __global__ void __launch_bounds__(64 * NH * TL, 1)
 }
 
 // out[b, h, :] and lse[b, h] from the spans' partials. grid (H, B), 128 threads.
-// KG = spans whose loads are in flight together (2, 4 or 8: the power of two
-// that covers the spans; 32 beyond 32 spans, whose merge loops over groups).
+// KG = spans whose loads are in flight together (2 or 4: the power of two that
+// covers the spans; 32 beyond 32 spans, whose merge loops over groups).
 // One pass: a group's maxima, sums and outputs are loaded together, and the
 // running sums are rescaled when a group raises the maximum.
 template <int kG>
@@ -382,7 +382,7 @@ __global__ void __launch_bounds__(128)
     lse[(size_t)b * H + h] = den > 0.f ? (mx + log2f(den)) * 0.69314718055994531f : -__builtin_inff();
 }
 
-// The merge for many spans (a few sequences): grid (H, B, 4), 128 threads.
+// The merge for 5 to 32 spans: grid (H, B, 4), 128 threads.
 // Workgroup z takes the value columns 128 z .. +127 of one (sequence, head);
 // thread t the four columns 4 (t % 32) .. +3 of them over the spans
 // t / 32, t / 32 + 4, ... (kPer of them, loads all in flight); the four span
@@ -566,7 +566,7 @@ extern "C" int ech_sparse_attn(const void* q, const void* dev_cache, int32_t C, 
   else if (nsp <= 4)
     hipLaunchKernelGGL(attn_merge_kernel<4>, mgrid, mblock, 0, s, part_o, part_ml, H, nsp, out, lse);
   else if (nsp <= 8)
-    hipLaunchKernelGGL(attn_merge_kernel<8>, mgrid, mblock, 0, s, part_o, part_ml, H, nsp, out, lse);
+    hipLaunchKernelGGL(attn_merge_split_kernel<2>, dim3(H, B, 4), mblock, 0, s, part_o, part_ml, H, nsp, out, lse);
   else if (nsp <= 16)
     hipLaunchKernelGGL(attn_merge_split_kernel<4>, dim3(H, B, 4), mblock, 0, s, part_o, part_ml, H, nsp, out, lse);
   else if (nsp <= 32)
